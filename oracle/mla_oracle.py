@@ -1,0 +1,240 @@
+"""Plain float64 CPU oracle for MLA over a latent KV cache (non-absorbed form).
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the package smoke check and the
+benchmark's CPU-baseline leg may import this module. The product path (the HIP
+library and its Python binding) never calls it, and it shares no code with it.
+
+What it computes, step by step, and the passage each step follows.  Pages are
+named by their title / subject; equation numbers are the pages' own.
+
+* Page "MLA 原理 / 关于矩阵吸收十倍提速" (dtcms.com, the DeepSeek-V2 MLA walkthrough):
+  - §"对KV张量的降维、分裂K、拆分KV且升维": the latent c = x·W_DKV is what the
+    cache holds (kv_a_proj_with_mqa, the report's eq. (41)); the up-projection
+    kv_b_proj (eq. (42)) is viewed as [H, d_nope + d_v, r] and split into
+    W_UK = [:, :d_nope, :] and W_UV = [:, d_nope:, :].
+  - §"将查询和键张量 q_pe 和 k_pe 进行旋转": only q_pe / k_pe are rotated
+    (apply_rotary_pos_emb with cos/sin and position ids); the query is
+    [q_nope ; q_pe] with the no-position part first.
+  - §"升维之后计算注意力": after the up-projection, standard attention.
+  - "原始顺序" eq. (1)-(2): v = einsum('hdc,blc->blhd', W_UV, c),
+    o = attn_weights · v.  This oracle follows that original order: it EXPANDS
+    k_nope = W_UK·c and v = W_UV·c for every cached row, and never uses the
+    absorbed rewrite except in ``absorbed_query`` (the per-token W_UK absorption
+    the page writes as einsum('hdc,bhqd->bhqc'), kept to localise errors in a GPU
+    intermediate, never used to produce the attention output).
+* Page "Qwen2.5-7B-base-mla-topk8-rank128 MLAfication" (wzjinhao.cn),
+  §"MLAfication 如何改写注意力结构": X → down_kv → c_kv (the only thing cached);
+  c_kv → up_kc / up_v; RoPE only on a small rotary subspace per KV head
+  (k_r_proj, q_r_proj); the query is split into a content part (q_c_proj) and a
+  rotary part (q_r_proj).  With several KV groups, each query head uses its
+  group's rotary key.
+* Page "Qwen3-30B-A3B-base-mla-topk8-rank512" (kwkr.cn): config field
+  ``variant: disrms``; read here as RMSNorm over the latent before it is stored
+  (unit gain), matching the nanowhale page's kv_norm (DeepseekV4RMSNorm on the
+  KV projection).
+* Page "MLA 在 nanowhale-100m 中的实现原理", §"高效注意力计算实现": causal
+  scaled-dot-product attention with an explicit scale (SDPA with is_causal).
+
+Readings taken where the pages are silent (each is listed in the design doc):
+rotate-half RoPE pairing (j, j + d_r/2) with θ_j = θ^(-2j/d_r) and the angle
+p·θ_j formed in float64; softmax over keys after the causal mask; causal rule
+p[key] <= p[query] within one sequence; head h uses rotary-key group
+h // (H/G); no biases; unit-gain RMSNorm with eps inside the square root.
+
+Parity pins: see tests/test_oracle_pins.py (brute force, associativity, torch
+SDPA in float64, RoPE invariants, closed forms, consistency, page facts).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=F64)
+
+
+# ----------------------------------------------------------------------------
+# rotary embedding on the rotary sub-dims only
+# ----------------------------------------------------------------------------
+
+
+def rope_angles(pos, d_rope: int, theta: float) -> np.ndarray:
+    """Angles p·θ_j, θ_j = θ^(-2j/d_rope), j < d_rope/2, in float64; shape [..., d_rope/2]."""
+    if d_rope % 2:
+        raise ValueError("rotary width must be even")
+    half = d_rope // 2
+    j = np.arange(half, dtype=F64)
+    inv_freq = float(theta) ** (-2.0 * j / d_rope)
+    return _f64(pos)[..., None] * inv_freq
+
+
+def rope(y, pos, theta: float) -> np.ndarray:
+    """Rotate-half RoPE of the last axis of ``y`` (width d_r) by position ``pos``.
+
+    Dims j and j + d_r/2 form a pair rotated by angle p·θ_j:
+      y'[j]        = y[j]·cos − y[j+half]·sin
+      y'[j+half]   = y[j+half]·cos + y[j]·sin
+    ``pos`` broadcasts against y's leading axes.
+    """
+    y = _f64(y)
+    d = y.shape[-1]
+    half = d // 2
+    ang = rope_angles(pos, d, theta)
+    # broadcast angles over any middle axes (e.g. heads) of y
+    while ang.ndim < y.ndim:
+        ang = np.expand_dims(ang, axis=-2)
+    cos, sin = np.cos(ang), np.sin(ang)
+    a, b = y[..., :half], y[..., half:]
+    return np.concatenate([a * cos - b * sin, b * cos + a * sin], axis=-1)
+
+
+# ----------------------------------------------------------------------------
+# cache side: latent + rotary key
+# ----------------------------------------------------------------------------
+
+
+def rmsnorm(v, eps: float) -> np.ndarray:
+    """Unit-gain RMSNorm over the last axis: v / sqrt(mean(v^2) + eps)."""
+    v = _f64(v)
+    return v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps)
+
+
+def latent(x, w_dkv, latent_rmsnorm: bool = False, eps: float = 1e-6) -> np.ndarray:
+    """c = x · W_DKVᵀ  (W_DKV stored [r, d_model]); optional RMSNorm. Shape [T, r]."""
+    c = _f64(x) @ _f64(w_dkv).T
+    return rmsnorm(c, eps) if latent_rmsnorm else c
+
+
+def rotary_key(x, w_kr, pos, n_groups: int, d_rope: int, theta: float) -> np.ndarray:
+    """kr[t, g] = RoPE(x[t] · W_KR[g·d_r:(g+1)·d_r]ᵀ, p[t]). Shape [T, G, d_r]."""
+    raw = (_f64(x) @ _f64(w_kr).T).reshape(-1, n_groups, d_rope)
+    return rope(raw, pos, theta)
+
+
+def cache_rows(x, w_dkv, w_kr, pos, *, n_groups, d_rope, theta, latent_rmsnorm=False,
+               eps=1e-6) -> np.ndarray:
+    """One cache row per token: [c (r) ; kr_0 ; ... ; kr_{G-1}] (width r + G·d_r)."""
+    c = latent(x, w_dkv, latent_rmsnorm, eps)
+    kr = rotary_key(x, w_kr, pos, n_groups, d_rope, theta)
+    return np.concatenate([c, kr.reshape(kr.shape[0], -1)], axis=1)
+
+
+def split_rows(rows, rank: int, n_groups: int, d_rope: int):
+    """Split cache rows into (c [S, r], kr [S, G, d_r])."""
+    rows = _f64(rows)
+    return rows[:, :rank], rows[:, rank:rank + n_groups * d_rope].reshape(-1, n_groups, d_rope)
+
+
+# ----------------------------------------------------------------------------
+# query side
+# ----------------------------------------------------------------------------
+
+
+def query(x, w_qc, w_qr, pos, *, n_heads, d_nope, d_rope, theta):
+    """qn[t,h] = x[t]·W_QC[h·d_nope:(h+1)·d_nope]ᵀ; qr[t,h] = RoPE(x[t]·W_QR[h·d_r:…]ᵀ, p[t])."""
+    x = _f64(x)
+    qn = (x @ _f64(w_qc).T).reshape(-1, n_heads, d_nope)
+    qr = rope((x @ _f64(w_qr).T).reshape(-1, n_heads, d_rope), pos, theta)
+    return qn, qr
+
+
+def absorbed_query(qn, w_uk) -> np.ndarray:
+    """q_lat[t,h,:] = Σ_d qn[t,h,d]·W_UK[h,d,:] — W_UK folded into the query (A6).
+
+    Used only to check a GPU intermediate; the attention output of this oracle
+    never goes through it.
+    """
+    return np.einsum("hdc,thd->thc", _f64(w_uk), _f64(qn))
+
+
+# ----------------------------------------------------------------------------
+# non-absorbed attention
+# ----------------------------------------------------------------------------
+
+
+def expand_kv(c, w_uk, w_uv):
+    """Decompress every cached latent: kn[s,h,:] = W_UK[h]·c[s], v[s,h,:] = W_UV[h]·c[s]."""
+    c = _f64(c)
+    kn = np.einsum("hdc,sc->shd", _f64(w_uk), c)
+    v = np.einsum("hdc,sc->shd", _f64(w_uv), c)
+    return kn, v
+
+
+def head_groups(n_heads: int, n_groups: int) -> np.ndarray:
+    """g(h) = h // (H/G): contiguous blocks of query heads share a rotary key."""
+    if n_heads % n_groups:
+        raise ValueError("heads must divide evenly into rotary-key groups")
+    return np.arange(n_heads) // (n_heads // n_groups)
+
+
+def softmax_attention(q, k, v, allowed, scale: float) -> np.ndarray:
+    """Standard attention for one query set: q [Tq, H, d], k [S, H, d], v [S, H, e],
+    ``allowed`` [Tq, S] bool.  a = scale·q·k; P = softmax over allowed keys
+    (max subtracted); out = P·v.  Every query must allow at least one key."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    a = scale * np.einsum("thd,shd->hts", q, k)
+    a = np.where(allowed[None, :, :], a, -np.inf)
+    m = a.max(axis=-1, keepdims=True)
+    e = np.exp(a - m)
+    p = e / e.sum(axis=-1, keepdims=True)
+    return np.einsum("hts,she->the", p, v)
+
+
+def mla_attention(qn, qr, c, kr, w_uk, w_uv, q_pos, k_pos, q_seg, k_seg, scale, *,
+                  head_chunk: int | None = None, query_chunk: int = 64) -> np.ndarray:
+    """Non-absorbed MLA attention output [Tq, H, d_v] (before W_o).
+
+    K[s,h] = [kn[s,h] ; kr[s, g(h)]], Q[t,h] = [qn[t,h] ; qr[t,h]]; query t may
+    attend key s iff they are in the same sequence and p[s] <= p[t].
+    """
+    qn, qr = _f64(qn), _f64(qr)
+    c, kr = _f64(c), _f64(kr)
+    q_pos, k_pos = np.asarray(q_pos), np.asarray(k_pos)
+    q_seg, k_seg = np.asarray(q_seg), np.asarray(k_seg)
+    Tq, H, _ = qn.shape
+    G = kr.shape[1]
+    d_v = w_uv.shape[1]
+    g_of_h = head_groups(H, G)
+    out = np.zeros((Tq, H, d_v), F64)
+    hc = head_chunk or H
+    for h0 in range(0, H, hc):
+        h1 = min(H, h0 + hc)
+        kn, v = expand_kv(c, w_uk[h0:h1], w_uv[h0:h1])
+        K = np.concatenate([kn, kr[:, g_of_h[h0:h1], :]], axis=-1)
+        Q = np.concatenate([qn[:, h0:h1], qr[:, h0:h1]], axis=-1)
+        for t0 in range(0, Tq, query_chunk):
+            t1 = min(Tq, t0 + query_chunk)
+            allowed = (q_seg[t0:t1, None] == k_seg[None, :]) & (k_pos[None, :] <= q_pos[t0:t1, None])
+            keys = np.nonzero(allowed.any(axis=0))[0]
+            if keys.size == 0:
+                raise ValueError("a query has no key to attend")
+            out[t0:t1, h0:h1] = softmax_attention(Q[t0:t1], K[keys], v[keys],
+                                                  allowed[:, keys], scale)
+    return out
+
+
+def mla_layer(x_keys, x_queries, w, *, k_pos, q_pos, k_seg, q_seg, n_heads, n_groups,
+              d_nope, d_rope, theta, scale, latent_rmsnorm=False, eps=1e-6,
+              head_chunk=None) -> np.ndarray:
+    """End-to-end chain: cache rows from x_keys, queries from x_queries, attention output.
+
+    ``w`` holds w_dkv, w_kr, w_qc, w_qr, w_uk, w_uv (float arrays)."""
+    r = w["w_dkv"].shape[0]
+    rows = cache_rows(x_keys, w["w_dkv"], w["w_kr"], k_pos, n_groups=n_groups, d_rope=d_rope,
+                      theta=theta, latent_rmsnorm=latent_rmsnorm, eps=eps)
+    c, kr = split_rows(rows, r, n_groups, d_rope)
+    qn, qr = query(x_queries, w["w_qc"], w["w_qr"], q_pos, n_heads=n_heads, d_nope=d_nope,
+                   d_rope=d_rope, theta=theta)
+    return mla_attention(qn, qr, c, kr, w["w_uk"], w["w_uv"], q_pos, k_pos, q_seg, k_seg,
+                         scale, head_chunk=head_chunk)
+
+
+def max_rel_err(got, ref) -> float:
+    """max over (token, head) of ‖got − ref‖∞ / ‖ref‖∞ over the last axis."""
+    got, ref = _f64(got), _f64(ref)
+    num = np.abs(got - ref).max(axis=-1)
+    den = np.abs(ref).max(axis=-1)
+    den = np.where(den == 0, 1.0, den)
+    return float((num / den).max()) if num.size else 0.0

@@ -1,0 +1,426 @@
+"""Pins for the float64 oracle: each test ties it to something other than itself.
+
+- brute force: explicit scalar loops on tiny ragged inputs (no numpy matmul);
+- associativity: the absorbed order the MLA principle page gives (W_UK folded
+  into the query, W_UV applied after P·c, its eqs. (4)-(5)) equals the oracle's
+  original order (eqs. (1)-(2));
+- library routines: torch's scaled_dot_product_attention and rms_norm in
+  float64 on the CPU;
+- RoPE: hand-evaluated textbook rotations, complex-number form, and the
+  invariants of rotating only the rotary sub-dims;
+- closed forms and consistency properties of causal softmax attention;
+- page facts: the shape numbers the pages print (tests/golden/page_facts.json).
+"""
+import cmath
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla_oracle as O
+
+
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_layer(rng, d_model, H, G, r, d_r, d_nope, d_v):
+    return {
+        "w_dkv": rng.standard_normal((r, d_model)) / math.sqrt(d_model),
+        "w_kr": rng.standard_normal((G * d_r, d_model)) / math.sqrt(d_model),
+        "w_qc": rng.standard_normal((H * d_nope, d_model)) / math.sqrt(d_model),
+        "w_qr": rng.standard_normal((H * d_r, d_model)) / math.sqrt(d_model),
+        "w_uk": rng.standard_normal((H, d_nope, r)) / math.sqrt(r),
+        "w_uv": rng.standard_normal((H, d_v, r)) / math.sqrt(r),
+    }
+
+
+def _ragged(lengths):
+    seg = np.concatenate([np.full(n, b) for b, n in enumerate(lengths)])
+    pos = np.concatenate([np.arange(n) for n in lengths])
+    return seg, pos
+
+
+def _run(x, w, seg, pos, *, H, G, d_nope, d_r, theta, scale, norm=False, eps=1e-6):
+    return O.mla_layer(x, x, w, k_pos=pos, q_pos=pos, k_seg=seg, q_seg=seg, n_heads=H,
+                       n_groups=G, d_nope=d_nope, d_rope=d_r, theta=theta, scale=scale,
+                       latent_rmsnorm=norm, eps=eps)
+
+
+# ----------------------------------------------------------------------------
+# P1: brute force with scalar loops
+# ----------------------------------------------------------------------------
+
+
+def _brute(x, w, seg, pos, *, H, G, d_nope, d_r, theta, scale, norm, eps):
+    T, D = x.shape
+    r = w["w_dkv"].shape[0]
+    d_v = w["w_uv"].shape[1]
+    half = d_r // 2
+
+    def dot(a, b):
+        s = 0.0
+        for i in range(len(a)):
+            s += float(a[i]) * float(b[i])
+        return s
+
+    def rot(vec, p):
+        out = [0.0] * d_r
+        for j in range(half):
+            ang = p * theta ** (-2.0 * j / d_r)
+            cs, sn = math.cos(ang), math.sin(ang)
+            out[j] = vec[j] * cs - vec[j + half] * sn
+            out[j + half] = vec[j + half] * cs + vec[j] * sn
+        return out
+
+    c = [[dot(x[t], w["w_dkv"][i]) for i in range(r)] for t in range(T)]
+    if norm:
+        for t in range(T):
+            ms = sum(v * v for v in c[t]) / r
+            c[t] = [v / math.sqrt(ms + eps) for v in c[t]]
+    kr = [[rot([dot(x[t], w["w_kr"][g * d_r + j]) for j in range(d_r)], pos[t]) for g in range(G)]
+          for t in range(T)]
+    qn = [[[dot(x[t], w["w_qc"][h * d_nope + j]) for j in range(d_nope)] for h in range(H)]
+          for t in range(T)]
+    qr = [[rot([dot(x[t], w["w_qr"][h * d_r + j]) for j in range(d_r)], pos[t]) for h in range(H)]
+          for t in range(T)]
+    kn = [[[dot(w["w_uk"][h][j], c[s]) for j in range(d_nope)] for h in range(H)] for s in range(T)]
+    v = [[[dot(w["w_uv"][h][j], c[s]) for j in range(d_v)] for h in range(H)] for s in range(T)]
+    per = H // G
+    out = np.zeros((T, H, d_v))
+    for t in range(T):
+        for h in range(H):
+            keys = [s for s in range(T) if seg[s] == seg[t] and pos[s] <= pos[t]]
+            logits = [scale * (dot(qn[t][h], kn[s][h]) + dot(qr[t][h], kr[s][h // per])) for s in keys]
+            mx = max(logits)
+            ex = [math.exp(a - mx) for a in logits]
+            den = sum(ex)
+            for e in range(d_v):
+                out[t, h, e] = sum(ex[i] / den * v[keys[i]][h][e] for i in range(len(keys)))
+    return out
+
+
+@pytest.mark.parametrize("G,norm", [(1, False), (2, False), (2, True), (1, True)])
+def test_p1_brute_force_ragged(G, norm):
+    rng = np.random.default_rng(7 + G + 10 * norm)
+    H, r, d_r, d_nope, d_v, D = 4, 6, 4, 3, 5, 8
+    w = _rand_layer(rng, D, H, G, r, d_r, d_nope, d_v)
+    lengths = [7, 4]
+    seg, pos = _ragged(lengths)
+    pos = pos + np.array([3] * 7 + [0] * 4)  # sequence 0 starts at position 3
+    x = rng.standard_normal((sum(lengths), D))
+    kw = dict(H=H, G=G, d_nope=d_nope, d_r=d_r, theta=10000.0, scale=0.37, norm=norm, eps=1e-6)
+    got = _run(x, w, seg, pos, **kw)
+    ref = _brute(x, w, seg, pos, **kw)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# P2: associativity — absorbed order equals the original order
+# ----------------------------------------------------------------------------
+
+
+def _absorbed(x, w, seg, pos, *, H, G, d_nope, d_r, theta, scale, norm=False, eps=1e-6):
+    """Eqs. (4)-(5) of the MLA principle page, with W_UK absorbed into the query."""
+    r = w["w_dkv"].shape[0]
+    rows = O.cache_rows(x, w["w_dkv"], w["w_kr"], pos, n_groups=G, d_rope=d_r, theta=theta,
+                        latent_rmsnorm=norm, eps=eps)
+    c, kr = O.split_rows(rows, r, G, d_r)
+    qn, qr = O.query(x, w["w_qc"], w["w_qr"], pos, n_heads=H, d_nope=d_nope, d_rope=d_r, theta=theta)
+    q_lat = np.einsum("hdc,bhqd->bhqc", w["w_uk"], qn.transpose(1, 0, 2)[None])[0]  # [H, T, r]
+    g = np.arange(H) // (H // G)
+    s_lat = np.einsum("hqc,lc->hql", q_lat, c)
+    s_pe = np.einsum("qhd,lhd->hql", qr, kr[:, g, :])
+    a = scale * (s_lat + s_pe)
+    allowed = (seg[:, None] == seg[None, :]) & (pos[None, :] <= pos[:, None])
+    a = np.where(allowed[None], a, -np.inf)
+    p = np.exp(a - a.max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    o_ = np.einsum("bhql,blc->bhqc", p[None], c[None])  # eq. (4)
+    o = np.einsum("bhqc,hdc->bhqd", o_, w["w_uv"])       # eq. (5)
+    return o[0].transpose(1, 0, 2)
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_p2_associativity(G):
+    rng = np.random.default_rng(11 + G)
+    H, r, d_r, d_nope, d_v, D = 8, 24, 6, 5, 7, 16  # d_nope != r != d_v catches transposes
+    w = _rand_layer(rng, D, H, G, r, d_r, d_nope, d_v)
+    seg, pos = _ragged([9, 1, 5])
+    x = rng.standard_normal((15, D))
+    kw = dict(H=H, G=G, d_nope=d_nope, d_r=d_r, theta=500.0, scale=0.21)
+    np.testing.assert_allclose(_run(x, w, seg, pos, **kw), _absorbed(x, w, seg, pos, **kw),
+                               rtol=1e-11, atol=1e-12)
+
+
+def test_absorbed_query_matches_page_einsum():
+    rng = np.random.default_rng(3)
+    qn = rng.standard_normal((5, 4, 3))
+    w_uk = rng.standard_normal((4, 3, 7))
+    ref = np.einsum("hdc,bhqd->bhqc", w_uk, qn.transpose(1, 0, 2)[None])[0].transpose(1, 0, 2)
+    np.testing.assert_allclose(O.absorbed_query(qn, w_uk), ref, rtol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# P3: library routines in float64
+# ----------------------------------------------------------------------------
+
+
+def test_p3_sdpa_library_masked():
+    rng = np.random.default_rng(5)
+    Tq, S, H, d, e = 6, 9, 3, 8, 5
+    q, k, v = rng.standard_normal((Tq, H, d)), rng.standard_normal((S, H, d)), rng.standard_normal((S, H, e))
+    allowed = rng.random((Tq, S)) < 0.6
+    allowed[:, 0] = True
+    got = O.softmax_attention(q, k, v, allowed, 0.3)
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(k).permute(1, 0, 2)[None]
+    vt = torch.from_numpy(v).permute(1, 0, 2)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, attn_mask=torch.from_numpy(allowed), scale=0.3)[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_p3_sdpa_is_causal_pins_mask_direction():
+    """Single sequence, positions 0..n-1: the oracle's causal rule equals SDPA's is_causal."""
+    rng = np.random.default_rng(8)
+    H, r, d_r, d_nope, d_v, D, n = 2, 10, 4, 6, 3, 12, 11
+    w = _rand_layer(rng, D, H, 1, r, d_r, d_nope, d_v)
+    x = rng.standard_normal((n, D))
+    pos, seg = np.arange(n), np.zeros(n, int)
+    scale = 0.4
+    got = _run(x, w, seg, pos, H=H, G=1, d_nope=d_nope, d_r=d_r, theta=10000.0, scale=scale)
+    rows = O.cache_rows(x, w["w_dkv"], w["w_kr"], pos, n_groups=1, d_rope=d_r, theta=10000.0)
+    c, kr = O.split_rows(rows, r, 1, d_r)
+    qn, qr = O.query(x, w["w_qc"], w["w_qr"], pos, n_heads=H, d_nope=d_nope, d_rope=d_r, theta=10000.0)
+    kn, v = O.expand_kv(c, w["w_uk"], w["w_uv"])
+    Q = torch.from_numpy(np.concatenate([qn, qr], -1)).permute(1, 0, 2)[None]
+    K = torch.from_numpy(np.concatenate([kn, np.repeat(kr, H, axis=1)], -1)).permute(1, 0, 2)[None]
+    V = torch.from_numpy(v).permute(1, 0, 2)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=True, scale=scale)
+    np.testing.assert_allclose(got, ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_p3_rmsnorm_library():
+    rng = np.random.default_rng(2)
+    v = rng.standard_normal((7, 33)) * 3.0
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(v), (33,), eps=1e-6).numpy()
+    np.testing.assert_allclose(O.rmsnorm(v, 1e-6), ref, rtol=1e-13)
+    # closed form: ±a alternating has mean square a^2
+    a = 2.5
+    alt = np.array([a, -a] * 4)
+    np.testing.assert_allclose(O.rmsnorm(alt, 1e-6), alt / math.sqrt(a * a + 1e-6), rtol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# P4: RoPE — textbook values and invariants
+# ----------------------------------------------------------------------------
+
+
+def test_p4_rope_hand_values():
+    """d_r = 4, θ = 10000, p = 1: pairs (0,2) turn by 1 rad, pairs (1,3) by 10000^(-1/2) = 0.01 rad."""
+    y = np.array([1.0, 2.0, 3.0, 4.0])
+    got = O.rope(y, 1, 10000.0)
+    c1, s1, c2, s2 = math.cos(1.0), math.sin(1.0), math.cos(0.01), math.sin(0.01)
+    ref = [1 * c1 - 3 * s1, 2 * c2 - 4 * s2, 3 * c1 + 1 * s1, 4 * c2 + 2 * s2]
+    np.testing.assert_allclose(got, ref, rtol=1e-15)
+
+
+def test_p4_rope_complex_form():
+    """Pair (y_j, y_{j+half}) as a complex number, multiplied by e^{i·p·θ_j}."""
+    rng = np.random.default_rng(4)
+    d, theta = 16, 10000.0
+    y = rng.standard_normal(d)
+    for p in [0, 1, 17, 4095, 131071]:
+        got = O.rope(y, p, theta)
+        for j in range(d // 2):
+            z = complex(y[j], y[j + d // 2]) * cmath.exp(1j * p * theta ** (-2 * j / d))
+            assert abs(got[j] - z.real) < 1e-12 and abs(got[j + d // 2] - z.imag) < 1e-12
+
+
+def test_p4_rope_invariants():
+    rng = np.random.default_rng(9)
+    y = rng.standard_normal((5, 3, 8))
+    # (a) p = 0 is the identity
+    np.testing.assert_array_equal(O.rope(y, np.zeros(5), 10000.0), y)
+    # (b) norm preserved
+    yr = O.rope(y, np.arange(5) * 1000, 10000.0)
+    np.testing.assert_allclose(np.linalg.norm(yr, axis=-1), np.linalg.norm(y, axis=-1), rtol=1e-13)
+    # (f) composition
+    p1, p2 = np.array([3, 5, 7, 11, 13]), np.array([100, 0, 2, 9, 4096])
+    np.testing.assert_allclose(O.rope(O.rope(y, p1, 10000.0), p2, 10000.0), O.rope(y, p1 + p2, 10000.0),
+                               rtol=1e-11, atol=1e-12)
+
+
+def _layer_parts(x, w, pos, H, G, d_nope, d_r, theta):
+    r = w["w_dkv"].shape[0]
+    rows = O.cache_rows(x, w["w_dkv"], w["w_kr"], pos, n_groups=G, d_rope=d_r, theta=theta)
+    c, kr = O.split_rows(rows, r, G, d_r)
+    qn, qr = O.query(x, w["w_qc"], w["w_qr"], pos, n_heads=H, d_nope=d_nope, d_rope=d_r, theta=theta)
+    return c, kr, qn, qr
+
+
+def test_p4_rotation_only_on_rotary_dims_and_relative():
+    rng = np.random.default_rng(12)
+    H, G, r, d_r, d_nope, d_v, D, n = 4, 2, 8, 6, 5, 3, 10, 6
+    w = _rand_layer(rng, D, H, G, r, d_r, d_nope, d_v)
+    x = rng.standard_normal((n, D))
+    seg = np.zeros(n, int)
+    kw = dict(H=H, G=G, d_nope=d_nope, d_r=d_r, theta=10000.0, scale=0.5)
+    pos = np.arange(n)
+    base = _run(x, w, seg, pos, **kw)
+    # (c) shifting every position by Δ leaves the output unchanged (relative property)
+    np.testing.assert_allclose(_run(x, w, seg, pos + 777, **kw), base, rtol=1e-10, atol=1e-12)
+    # (e) positions change only the rotary parts: c and qn bit-identical, kr/qr not
+    a = _layer_parts(x, w, pos, H, G, d_nope, d_r, 10000.0)
+    b = _layer_parts(x, w, pos + 5, H, G, d_nope, d_r, 10000.0)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[2], b[2])
+    assert not np.allclose(a[1], b[1]) and not np.allclose(a[3], b[3])
+    # (d) with W_QR = W_KR = 0 the output does not depend on positions at all
+    w0 = dict(w, w_qr=np.zeros_like(w["w_qr"]), w_kr=np.zeros_like(w["w_kr"]))
+    np.testing.assert_array_equal(_run(x, w0, seg, pos, **kw), _run(x, w0, seg, pos * 3 + 1, **kw))
+
+
+# ----------------------------------------------------------------------------
+# P5: closed forms
+# ----------------------------------------------------------------------------
+
+
+def test_p5_hand_example_quarter_three_quarters():
+    """Hand-built layer: scores 0 and ln 3 give P = (1/4, 3/4) and o = (v0 + 3·v1)/4 = 5."""
+    scale = 1.0 / math.sqrt(3.0)  # d_nope = 1, d_r = 2
+    b = math.sqrt(3.0) * math.log(3.0)
+    w = {
+        "w_dkv": np.eye(2),                      # c0 = [1,0], c1 = [0,1]
+        "w_kr": np.zeros((2, 2)),
+        "w_qc": np.array([[0.0, 1.0]]),          # qn(token1) = 1, qn(token0) = 0
+        "w_qr": np.zeros((2, 2)),
+        "w_uk": np.array([[[0.0, b]]]),          # kn0 = 0, kn1 = b
+        "w_uv": np.array([[[2.0, 6.0]]]),        # v0 = 2, v1 = 6
+    }
+    x = np.eye(2)
+    out = _run(x, w, np.zeros(2, int), np.arange(2), H=1, G=1, d_nope=1, d_r=2, theta=10000.0,
+               scale=scale)
+    assert abs(out[0, 0, 0] - 2.0) < 1e-14          # token 0 sees only itself
+    assert abs(out[1, 0, 0] - 5.0) < 1e-13
+
+
+def test_p5_hand_example_rotary_cosine():
+    """Only the rotary part scores: with d_r = 2 and θ_0 = 1, q·k = cos(p_q − p_k)."""
+    w = {
+        "w_dkv": np.eye(2), "w_kr": np.array([[1.0, 0.0], [0.0, 0.0]]),
+        "w_qc": np.zeros((1, 2)), "w_qr": np.array([[1.0, 0.0], [0.0, 0.0]]),
+        "w_uk": np.zeros((1, 1, 2)), "w_uv": np.array([[[1.0, -1.0]]]),
+    }
+    x = np.array([[1.0, 3.0], [1.0, 5.0]])  # c = x; v0 = -2, v1 = -4; rotary inputs [1, 0]
+    scale = 0.8
+    out = _run(x, w, np.zeros(2, int), np.arange(2), H=1, G=1, d_nope=1, d_r=2, theta=10000.0,
+               scale=scale)
+    e0, e1 = math.exp(scale * math.cos(1.0)), math.exp(scale * 1.0)
+    assert abs(out[1, 0, 0] - (e0 * -2.0 + e1 * -4.0) / (e0 + e1)) < 1e-13
+
+
+def test_p5_closed_forms():
+    rng = np.random.default_rng(21)
+    H, G, r, d_r, d_nope, d_v, D, n = 3, 1, 7, 4, 5, 6, 9, 8
+    w = _rand_layer(rng, D, H, G, r, d_r, d_nope, d_v)
+    x = rng.standard_normal((n, D))
+    seg, pos = np.zeros(n, int), np.arange(n)
+    kw = dict(H=H, G=G, d_nope=d_nope, d_r=d_r, theta=10000.0, scale=0.3)
+    c = x @ w["w_dkv"].T
+    v = np.einsum("hdc,sc->shd", w["w_uv"], c)
+    # (a) first token attends only itself: o = v0
+    out = _run(x, w, seg, pos, **kw)
+    np.testing.assert_allclose(out[0], v[0], rtol=1e-13)
+    # (b) zero queries: uniform weights, o = prefix mean of v
+    wz = dict(w, w_qc=np.zeros_like(w["w_qc"]), w_qr=np.zeros_like(w["w_qr"]))
+    outz = _run(x, wz, seg, pos, **kw)
+    for t in range(n):
+        np.testing.assert_allclose(outz[t], v[:t + 1].mean(axis=0), rtol=1e-12, atol=1e-14)
+    # (c) all keys identical (same x at every position, no rotary): o = that v
+    xs = np.repeat(x[:1], n, axis=0)
+    w0 = dict(w, w_qr=np.zeros_like(w["w_qr"]), w_kr=np.zeros_like(w["w_kr"]))
+    outs = _run(xs, w0, seg, pos, **kw)
+    np.testing.assert_allclose(outs[-1], np.broadcast_to(v[0], outs[-1].shape), rtol=1e-12)
+    # (d) a huge scale makes the top-scoring key dominate
+    outd = _run(x, w, seg, pos, **dict(kw, scale=1e4))
+    rows = O.cache_rows(x, w["w_dkv"], w["w_kr"], pos, n_groups=G, d_rope=d_r, theta=10000.0)
+    cc, kr = O.split_rows(rows, r, G, d_r)
+    qn, qr = O.query(x, w["w_qc"], w["w_qr"], pos, n_heads=H, d_nope=d_nope, d_rope=d_r, theta=10000.0)
+    kn, _ = O.expand_kv(cc, w["w_uk"], w["w_uv"])
+    t = n - 1
+    for h in range(H):
+        s = [qn[t, h] @ kn[j, h] + qr[t, h] @ kr[j, 0] for j in range(n)]
+        np.testing.assert_allclose(outd[t, h], v[int(np.argmax(s)), h], rtol=1e-6, atol=1e-9)
+
+
+# ----------------------------------------------------------------------------
+# P6: consistency of the causal, segmented computation
+# ----------------------------------------------------------------------------
+
+
+def test_p6_consistency():
+    rng = np.random.default_rng(31)
+    H, G, r, d_r, d_nope, d_v, D = 4, 2, 8, 4, 3, 5, 12
+    w = _rand_layer(rng, D, H, G, r, d_r, d_nope, d_v)
+    kw = dict(H=H, G=G, d_nope=d_nope, d_r=d_r, theta=10000.0, scale=0.45)
+    lengths = [6, 3, 8]
+    seg, pos = _ragged(lengths)
+    x = rng.standard_normal((sum(lengths), D))
+    full = _run(x, w, seg, pos, **kw)
+    # ragged batch == independent runs; decode of the last token == prefill row
+    off = 0
+    for b, n in enumerate(lengths):
+        xb = x[off:off + n]
+        one = _run(xb, w, np.zeros(n, int), np.arange(n), **kw)
+        np.testing.assert_allclose(full[off:off + n], one, rtol=1e-12, atol=1e-14)
+        dec = O.mla_layer(xb, xb[-1:], w, k_pos=np.arange(n), q_pos=np.array([n - 1]),
+                          k_seg=np.zeros(n, int), q_seg=np.zeros(1, int), n_heads=H, n_groups=G,
+                          d_nope=d_nope, d_rope=d_r, theta=10000.0, scale=0.45)
+        np.testing.assert_allclose(dec[0], one[-1], rtol=1e-12, atol=1e-14)
+        # prefix stability: a shorter prefix gives the same earlier rows
+        pre = _run(xb[:n - 1], w, np.zeros(n - 1, int), np.arange(n - 1), **kw)
+        np.testing.assert_allclose(pre, one[:n - 1], rtol=1e-12, atol=1e-14)
+        off += n
+    # permuting sequences permutes outputs
+    order = [2, 0, 1]
+    offs = np.cumsum([0] + lengths)
+    xp = np.concatenate([x[offs[b]:offs[b + 1]] for b in order])
+    segp, posp = _ragged([lengths[b] for b in order])
+    outp = _run(xp, w, segp, posp, **kw)
+    np.testing.assert_allclose(outp, np.concatenate([full[offs[b]:offs[b + 1]] for b in order]),
+                               rtol=1e-12, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# P7: page facts fix the workload shapes
+# ----------------------------------------------------------------------------
+
+
+def test_p7_page_facts_and_workload_shapes():
+    from mla_inputs import CONFIGS
+    facts = json.load(open(os.path.join(GOLDEN, "page_facts.json")))
+    f = lambda k: facts[k]["value"]  # noqa: E731
+    # Qwen2.5-7B MLAfication: 4 KV heads x 128 x 2 = 1024 values -> 128 + 4x8 = 160, >= 6x smaller
+    assert 4 * 128 * 2 == f("qwen25_gqa_kv_values_per_token")
+    c2 = CONFIGS["qwen25_7b_decode"]
+    assert c2.rank == f("qwen25_latent_rank") and c2.d_rope == f("qwen25_rope_dims_per_kv_head")
+    assert c2.row_width == f("qwen25_mla_values_per_token")
+    assert f("qwen25_gqa_kv_values_per_token") / c2.row_width >= f("qwen25_compression_at_least")
+    # DeepSeek-V2: 24576 = H * (d_nope + d_r); o_proj input H * d_v = 16384; hidden 5120
+    c3 = CONFIGS["deepseek_v2_decode"]
+    assert c3.n_heads * (c3.d_nope + c3.d_rope) == f("deepseek_v2_q_b_proj_out")
+    assert c3.n_heads * c3.d_v == f("deepseek_v2_o_proj_in")
+    assert c3.d_model == f("deepseek_v2_hidden")
+    # Qwen3-30B-A3B delta: rank 512, 8 rotary dims per KV head
+    c4 = CONFIGS["qwen3_30b_ragged_decode"]
+    assert c4.rank == f("qwen3_30b_latent_rank") and c4.d_rope == f("qwen3_30b_rope_dims_per_kv_head")
+    # Zebra MLA layers: rank 256, hidden 2048, 16 heads
+    c5 = CONFIGS["long_prefill_131k"]
+    assert (c5.rank, c5.d_model, c5.n_heads) == (f("zebra_kv_lora_rank"), f("zebra_hidden"), f("zebra_heads"))
+    nw = f("nanowhale_head_dim_split")
+    assert nw["head_dim"] == nw["qk_rope_head_dim"] + nw["nope_head_dim"]
