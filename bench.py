@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of the absorbed-MLA decode hot path on one MI355X.
+
+Workload: DeepSeek-V2-shaped decode, H=128 heads, latent rank r=512, 64 rotary
+dims (one shared rotary key), d_model=5120, batch 64, context 8192, bf16.
+One step = the whole hot path for one new token per sequence:
+  mla_write_cache (append the token's [c ; kr] row)  ->  mla_absorb (q_lat, q_pe)
+  ->  mla_decode (attention over the 8192 cached rows, W_UV).
+The cache (rows 0..8190 of every sequence) is built once with mla_write_cache
+from seeded x ~ N(0,1) before timing; inputs are resident in HBM when the timed
+region starts.  Two copies of the cache alternate between steps so no step reads
+rows the 256 MB Infinity Cache still holds from the step before.
+
+Prints one JSON line: tokens/s of whole steps, the roofline of the dominant
+kernel (the decode attention), and the float64 CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MLA absorbed decode tokens/s + % of HBM/MFMA roofline, H=128 r=512 ctx 8K"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16, published
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="deepseek_v2_decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--threads", type=int, default=0, help="host threads for input generation (0: all)")
+    return ap.parse_args()
+
+
+def host_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def decode_alg_bytes(cfg, lengths) -> int:
+    """Bytes the decode call must move: cache rows read, queries, W_UV, outputs."""
+    e = cfg.elem_bytes
+    rows = int(sum(lengths))
+    B = len(lengths)
+    return (rows * cfg.row_width * e + B * cfg.n_heads * (cfg.rank + cfg.d_rope) * e
+            + cfg.n_heads * cfg.d_v * cfg.rank * e + B * cfg.n_heads * cfg.d_v * e)
+
+
+def decode_alg_flops(cfg, lengths) -> int:
+    rows = int(sum(lengths))
+    B = len(lengths)
+    H, r, dr = cfg.n_heads, cfg.rank, cfg.d_rope
+    return rows * H * (2 * (r + dr) + 2 * r) + B * H * 2 * r * cfg.d_v
+
+
+def build_cache(torch, M, I, layer, cfg, lengths, starts, threads):
+    """Rows 0..n-2 of every sequence, written by mla_write_cache from x ~ N(0,1)."""
+    rows = int(sum(lengths))
+    cache = torch.empty((rows, cfg.row_width), dtype=torch.bfloat16, device="cuda")
+    chunk = max(int(n) - 1 for n in lengths)
+    ws = torch.empty(M.mla_workspace_size(layer.dims, M.MLA_OP_WRITE_CACHE, 0, chunk, 0),
+                     dtype=torch.uint8, device="cuda")
+    import numpy as np
+
+    def gen(b):
+        n = int(lengths[b])
+        return b, I.x_rows(cfg, b, 0, n - 1, quantized=False)
+
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        for b, xb in ex.map(gen, range(len(lengths))):
+            n = int(lengths[b])
+            xd = torch.from_numpy(xb).cuda().to(torch.bfloat16)  # RNE on device
+            pos = torch.arange(n - 1, dtype=torch.int32, device="cuda")
+            slots = torch.arange(n - 1, dtype=torch.int64, device="cuda") + int(starts[b])
+            M.mla_write_cache(layer.dims, xd, layer.w_dev["w_dkv"], layer.w_dev["w_kr"], pos, slots,
+                              cache, workspace=ws)
+            del xd
+    torch.cuda.synchronize()
+    return cache
+
+
+def cpu_baseline(cfg, I, lengths):
+    """float64 oracle on one sequence's decode: query, K/V expansion, attention over
+    its whole context (cache rows precomputed by the oracle outside the timing)."""
+    import numpy as np
+
+    from oracle import mla_oracle as O
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_info = None
+        threadpool_limits = None
+    cores = host_threads()
+    n = int(lengths[0])
+    w = I.weights(cfg)
+    x = I.x_rows(cfg, 0, 0, n)
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    try:
+        rows = O.cache_rows(x, w["w_dkv"], w["w_kr"], np.arange(n), n_groups=cfg.n_groups,
+                            d_rope=cfg.d_rope, theta=cfg.rope_theta,
+                            latent_rmsnorm=cfg.latent_rmsnorm, eps=cfg.rms_eps)
+        c, kr = O.split_rows(rows, cfg.rank, cfg.n_groups, cfg.d_rope)
+        t0 = time.perf_counter()
+        qn, qr = O.query(x[-1:], w["w_qc"], w["w_qr"], np.array([n - 1]), n_heads=cfg.n_heads,
+                         d_nope=cfg.d_nope, d_rope=cfg.d_rope, theta=cfg.rope_theta)
+        O.mla_attention(qn, qr, c, kr, w["w_uk"], w["w_uv"], np.array([n - 1]), np.arange(n),
+                        np.zeros(1, int), np.zeros(n, int), cfg.softmax_scale, head_chunk=16)
+        dt = time.perf_counter() - t0
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    used = cores
+    if threadpool_info:
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if info:
+            used = min(cores, int(info[0].get("num_threads", cores)))
+    return {"value": 1.0 / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"1 of {len(lengths)} sequences: float64 non-absorbed oracle (query, "
+                      f"K/V expansion of {n} cached rows for {cfg.n_heads} heads, softmax "
+                      f"attention) = 1 decode token, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); the decode "
+              "path is measured on one GPU's share only.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import head_latent_attention_kv_amd as M
+    import mla_inputs as I
+    from tests import harness as Hh
+
+    M.load()
+    torch.cuda.set_device(0)
+    cfg = I.CONFIGS[args.workload]
+    if cfg.mode != "decode":
+        raise SystemExit("bench.py times decode workloads")
+    threads = args.threads or min(16, host_threads())
+    lengths = I.context_lengths(cfg)
+    starts = np.concatenate([[0], np.cumsum(lengths)[:-1]]).astype(np.int64)
+    B = len(lengths)
+    t_setup = time.perf_counter()
+    layer = Hh.make_layer(cfg)
+    cache0 = build_cache(torch, M, I, layer, cfg, lengths, starts, threads)
+    cache_bytes = cache0.numel() * cache0.element_size()
+    n_copies = max(2, math.ceil(512e6 / cache_bytes) + 1)
+    caches = [cache0] + [cache0.clone() for _ in range(n_copies - 1)]
+    # the new token of each sequence (position n-1): its x, position and slot
+    x_new = np.stack([I.x_rows(cfg, b, int(n) - 1, int(n)) [0] for b, n in enumerate(lengths)])
+    x_new_d = Hh.to_dev(x_new, cfg.dtype)
+    pos_new = torch.from_numpy((lengths - 1).astype(np.int32)).cuda()
+    slots_new = torch.from_numpy(starts + lengths - 1).cuda()
+    seq_start = torch.from_numpy(starts).cuda()
+    seq_len = torch.from_numpy(lengths.astype(np.int32)).cuda()
+    max_len = int(lengths.max())
+    et = torch.bfloat16
+    q_lat = torch.empty((B, cfg.n_heads, cfg.rank), dtype=et, device="cuda")
+    q_pe = torch.empty((B, cfg.n_heads, cfg.d_rope), dtype=et, device="cuda")
+    out = torch.empty((B, cfg.n_heads, cfg.d_v), dtype=et, device="cuda")
+    dims = layer.dims
+    ws_w = torch.empty(M.mla_workspace_size(dims, M.MLA_OP_WRITE_CACHE, 0, B, 0), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(M.mla_workspace_size(dims, M.MLA_OP_ABSORB, 0, B, 0), dtype=torch.uint8, device="cuda")
+    ws_d = torch.empty(M.mla_workspace_size(dims, M.MLA_OP_DECODE, B, 0, max_len), dtype=torch.uint8, device="cuda")
+    wd = layer.w_dev
+    setup_s = time.perf_counter() - t_setup
+
+    def step(i):
+        c = caches[i % n_copies]
+        M.mla_write_cache(dims, x_new_d, wd["w_dkv"], wd["w_kr"], pos_new, slots_new, c, workspace=ws_w)
+        M.mla_absorb(dims, x_new_d, wd["w_qc"], wd["w_qr"], wd["w_uk"], pos_new, q_lat, q_pe, workspace=ws_a)
+        M.mla_decode(dims, q_lat, q_pe, c, seq_start, seq_len, max_len, wd["w_uv"], out, workspace=ws_d)
+
+    def decode_only(i):
+        M.mla_decode(dims, q_lat, q_pe, caches[i % n_copies], seq_start, seq_len, max_len, wd["w_uv"],
+                     out, workspace=ws_d)
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (setup {setup_s:.1f} s)",
+          file=sys.stderr, flush=True)
+
+    # the dominant kernel group, timed on its own stream with HIP events
+    for i in range(args.warmup):
+        decode_only(i)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        decode_only(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_dec = e0.elapsed_time(e1) / args.steps
+    alg_bytes = decode_alg_bytes(cfg, lengths)
+    achieved = alg_bytes / (ms_dec * 1e-3) / 1e9
+    print(f"[bench] decode call: {ms_dec * 1e3:.1f} us, {achieved:.0f} GB/s algorithmic",
+          file=sys.stderr, flush=True)
+
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all(), "non-finite decode output"
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, I, lengths)
+        print(f"[bench] cpu oracle: {cpu['sample']}", file=sys.stderr, flush=True)
+
+    tokens_per_s = B / (ms_step * 1e-3)
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded x ~ N(0,1), weights ~ N(0,1/fan_in)",
+        "config": {"workload": cfg.name, "batch": B, "context": int(max_len), "heads": cfg.n_heads,
+                   "rank": cfg.rank, "d_rope": cfg.d_rope, "d_model": cfg.d_model,
+                   "step": "mla_write_cache + mla_absorb + mla_decode"},
+        "roofline": {"bound": "hbm", "kernel": "mla_decode (attention + merge + W_UV)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes": alg_bytes, "alg_flops": decode_alg_flops(cfg, lengths),
+                     "us_per_launch": round(ms_dec * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

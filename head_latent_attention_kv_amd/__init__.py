@@ -1,0 +1,23 @@
+"""MLA over a compressed latent KV cache for AMD Instinct MI355X (gfx950).
+
+The computation lives in libmla_amd.so (hand-written HIP kernels behind the C ABI
+of include/mla.h); this package only loads it and marshals torch tensors into
+its calls:
+
+    mla_write_cache  — c = x·W_DKVᵀ (+RMSNorm), kr = RoPE(x·W_KRᵀ), store [c ; kr]
+    mla_absorb       — q_lat = (x·W_QCᵀ)·W_UK per head, q_pe = RoPE(x·W_QRᵀ)
+    mla_decode       — one query per sequence against its cached rows
+    mla_prefill      — causal attention over packed sequences
+
+Build the library with ``python -m head_latent_attention_kv_amd.build``.
+"""
+from ._abi import (  # noqa: F401
+    MLA_BF16, MLA_EHIP, MLA_EINVAL, MLA_ENOTSUP, MLA_EWORKSPACE, MLA_F32, MLA_OK, MLA_OP_ABSORB,
+    MLA_OP_DECODE, MLA_OP_PREFILL, MLA_OP_WRITE_CACHE, MlaDims, MlaError, dims_of, load, make_dims,
+    mla_absorb, mla_decode, mla_prefill, mla_workspace_size, mla_write_cache, strerror,
+)
+
+__all__ = [
+    "MlaDims", "MlaError", "dims_of", "load", "make_dims", "mla_absorb", "mla_decode", "mla_prefill",
+    "mla_workspace_size", "mla_write_cache", "strerror",
+]

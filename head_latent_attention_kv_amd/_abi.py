@@ -1,0 +1,193 @@
+"""ctypes binding of libmla_amd.so (include/mla.h).  Argument marshalling only:
+every step of the computation runs in the library's HIP kernels.  Torch tensors
+provide device memory; the current torch stream is passed as the hipStream_t."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmla_amd.so")
+
+MLA_OK, MLA_EINVAL, MLA_ENOTSUP, MLA_EWORKSPACE, MLA_EHIP = 0, -1, -2, -3, -4
+MLA_F32, MLA_BF16 = 0, 1
+MLA_OP_WRITE_CACHE, MLA_OP_ABSORB, MLA_OP_DECODE, MLA_OP_PREFILL = 0, 1, 2, 3
+
+# Functions declared in include/mla.h, with their ctypes signatures.
+_vp, _sz, _i32, _i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+
+
+class MlaDims(ctypes.Structure):
+    _fields_ = [
+        ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+        ("rank", ctypes.c_int32), ("d_rope", ctypes.c_int32), ("d_nope", ctypes.c_int32),
+        ("d_v", ctypes.c_int32), ("dtype", ctypes.c_int32), ("latent_rmsnorm", ctypes.c_int32),
+        ("rms_eps", ctypes.c_float), ("softmax_scale", ctypes.c_float),
+        ("rope_theta", ctypes.c_double),
+    ]
+
+
+_PD = ctypes.POINTER(MlaDims)
+SIGNATURES = {
+    "mla_workspace_size": (_sz, [_PD, ctypes.c_int, _i32, _i64, _i32]),
+    "mla_check_dims": (ctypes.c_int, [_PD]),
+    "mla_write_cache": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
+    "mla_absorb": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "mla_decode": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "mla_prefill": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "mla_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "mla_version": (ctypes.c_int, []),
+}
+
+_lib = None
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({strerror(status)})")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the built library; raises if it has not been built (no fallback path)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m head_latent_attention_kv_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    try:
+        return load().mla_strerror(status).decode()
+    except ImportError:
+        return "library not loaded"
+
+
+def make_dims(*, d_model, n_heads, n_groups, rank, d_rope, d_nope, d_v, dtype, latent_rmsnorm=False,
+              rms_eps=1e-6, softmax_scale=0.0, rope_theta=10000.0) -> MlaDims:
+    dt = {"f32": MLA_F32, "bf16": MLA_BF16}.get(dtype, dtype)
+    return MlaDims(d_model, n_heads, n_groups, rank, d_rope, d_nope, d_v, int(dt), int(bool(latent_rmsnorm)),
+                   float(rms_eps), float(softmax_scale), float(rope_theta))
+
+
+def dims_of(cfg) -> MlaDims:
+    """mla_dims for a workload description with the usual field names."""
+    return make_dims(d_model=cfg.d_model, n_heads=cfg.n_heads, n_groups=cfg.n_groups, rank=cfg.rank,
+                     d_rope=cfg.d_rope, d_nope=cfg.d_nope, d_v=cfg.d_v, dtype=cfg.dtype,
+                     latent_rmsnorm=cfg.latent_rmsnorm, rms_eps=cfg.rms_eps,
+                     softmax_scale=cfg.softmax_scale, rope_theta=cfg.rope_theta)
+
+
+# ----------------------------------------------------------------------------
+# torch-tensor wrappers
+# ----------------------------------------------------------------------------
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _elem_dtype(dims: MlaDims):
+    torch = _torch()
+    return torch.float32 if dims.dtype == MLA_F32 else torch.bfloat16
+
+
+def _ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _check(fn, status):
+    if status != MLA_OK:
+        raise MlaError(fn, status)
+
+
+def mla_workspace_size(dims: MlaDims, op: int, batch: int = 0, n_tokens: int = 0, max_len: int = 0) -> int:
+    return int(load().mla_workspace_size(ctypes.byref(dims), op, batch, n_tokens, max_len))
+
+
+def _workspace(dims, op, batch, n_tokens, max_len, workspace, device):
+    need = mla_workspace_size(dims, op, batch, n_tokens, max_len)
+    if workspace is None:
+        torch = _torch()
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def mla_write_cache(dims, x, w_dkv, w_kr, positions, slots, cache, workspace=None, stream=None):
+    torch = _torch()
+    et = _elem_dtype(dims)
+    T = x.shape[0]
+    ws, nbytes = _workspace(dims, MLA_OP_WRITE_CACHE, 0, T, 0, workspace, x.device)
+    _check("mla_write_cache", load().mla_write_cache(
+        ctypes.byref(dims), _ptr(x, "x", et), _ptr(w_dkv, "w_dkv", et), _ptr(w_kr, "w_kr", et),
+        _ptr(positions, "positions", torch.int32), _ptr(slots, "slots", torch.int64), T,
+        _ptr(cache, "cache", et), cache.shape[0], _ptr(ws, "workspace"), nbytes, _stream(stream)))
+    return cache
+
+
+def mla_absorb(dims, x, w_qc, w_qr, w_uk, positions, q_lat, q_pe, workspace=None, stream=None):
+    torch = _torch()
+    et = _elem_dtype(dims)
+    T = x.shape[0]
+    ws, nbytes = _workspace(dims, MLA_OP_ABSORB, 0, T, 0, workspace, x.device)
+    _check("mla_absorb", load().mla_absorb(
+        ctypes.byref(dims), _ptr(x, "x", et), _ptr(w_qc, "w_qc", et), _ptr(w_qr, "w_qr", et),
+        _ptr(w_uk, "w_uk", et), _ptr(positions, "positions", torch.int32), T,
+        _ptr(q_lat, "q_lat", et), _ptr(q_pe, "q_pe", et), _ptr(ws, "workspace"), nbytes,
+        _stream(stream)))
+    return q_lat, q_pe
+
+
+def mla_decode(dims, q_lat, q_pe, cache, seq_start, seq_len, max_len, w_uv, out, workspace=None,
+               stream=None):
+    torch = _torch()
+    et = _elem_dtype(dims)
+    B = q_lat.shape[0]
+    ws, nbytes = _workspace(dims, MLA_OP_DECODE, B, 0, max_len, workspace, q_lat.device)
+    _check("mla_decode", load().mla_decode(
+        ctypes.byref(dims), _ptr(q_lat, "q_lat", et), _ptr(q_pe, "q_pe", et), _ptr(cache, "cache", et),
+        _ptr(seq_start, "seq_start", torch.int64), _ptr(seq_len, "seq_len", torch.int32), B,
+        int(max_len), _ptr(w_uv, "w_uv", et), _ptr(out, "out", et), _ptr(ws, "workspace"), nbytes,
+        _stream(stream)))
+    return out
+
+
+def mla_prefill(dims, q_lat, q_pe, cache, cu_seqlens, max_len, w_uv, out, workspace=None, stream=None):
+    torch = _torch()
+    et = _elem_dtype(dims)
+    T = q_lat.shape[0]
+    B = cu_seqlens.shape[0] - 1
+    ws, nbytes = _workspace(dims, MLA_OP_PREFILL, B, T, max_len, workspace, q_lat.device)
+    _check("mla_prefill", load().mla_prefill(
+        ctypes.byref(dims), _ptr(q_lat, "q_lat", et), _ptr(q_pe, "q_pe", et), _ptr(cache, "cache", et),
+        _ptr(cu_seqlens, "cu_seqlens", torch.int64), B, T, int(max_len), _ptr(w_uv, "w_uv", et),
+        _ptr(out, "out", et), _ptr(ws, "workspace"), nbytes, _stream(stream)))
+    return out
+
+
+def default_scale(d_nope: int, d_rope: int) -> float:
+    return 1.0 / math.sqrt(d_nope + d_rope)

@@ -1,0 +1,219 @@
+// Generic absorbed attention over latent-cache rows (VALU; any dtype/shape up to r = 512).
+//
+// Per query q, head h and cache row l of its key range:
+//   s = scale·(q_lat[q,h]·c[l] + q_pe[q,h]·kr[l, g(h)])
+// computed as one dot product of the whole cache row [c ; kr_0 ; ... ; kr_{G-1}]
+// with a query row that is zero outside [q_lat ; q_pe at group g(h)].
+// Online softmax over l (base-2: scale·log2(e) folded into the query), then
+// o_[q,h,:] = Σ_l P[h,l]·c[l,:] in latent space; W_UV is applied afterwards.
+//
+// Block = 256 threads, a block of kHB heads x one query x one split of the key
+// range; tiles of kLT rows staged through LDS and shared by the kHB heads.
+// This kernel serves the fp32 layer and any shape the MFMA kernels do not take.
+#include <math.h>
+
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kHB = 8;    // heads per block
+constexpr int kLT = 32;   // cache rows per tile
+constexpr int kRJ = 16;   // latent columns per thread (r <= 32 * kRJ = 512)
+
+// LDS row pitch (elements) of a staged cache tile: an odd number of 32-bit words,
+// so the per-row and per-column reads of the score and PV loops hit distinct banks.
+__host__ __device__ inline int lds_pitch(int row_w, int elem_bytes) {
+  if (elem_bytes == 4) return row_w | 1;
+  int p = (row_w + 1) & ~1;
+  return ((p / 2) & 1) ? p : p + 2;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void attend_generic_kernel(
+    const T* __restrict__ q_lat, const T* __restrict__ q_pe, const T* __restrict__ cache,
+    const int64_t* __restrict__ seq_start, const int32_t* __restrict__ seq_len,
+    const int64_t* __restrict__ cu, int batch, AttnShape sh, int n_split, int split_len,
+    float* __restrict__ part_o, float* __restrict__ part_ml, float* __restrict__ o_out) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int row_w = sh.row_w;
+  const int pitch = lds_pitch(row_w, sizeof(T));
+  float* sq = reinterpret_cast<float*>(smem);                        // [kHB][row_w]
+  float* sp = sq + kHB * row_w;                                      // [kHB][kLT]
+  T* sc = reinterpret_cast<T*>(sp + kHB * kLT);                      // [kLT][pitch]
+
+  const int64_t q = blockIdx.x;
+  const int h0 = blockIdx.y * kHB;
+  const int split = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int hl = tid >> 5;        // local head of this thread (score and PV)
+  const int lane32 = tid & 31;
+  const int head = h0 + hl;
+  const int per_group = sh.H / sh.G;
+
+  int64_t start;
+  int len;
+  if (cu == nullptr) {
+    start = seq_start[q];
+    len = seq_len[q];
+  } else {
+    int lo = 0, hi = batch - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (cu[mid] <= q) lo = mid; else hi = mid - 1;
+    }
+    start = cu[lo];
+    len = static_cast<int>(q - cu[lo] + 1);
+  }
+  const int l_begin = split * split_len;
+  const int l_end = min(len, l_begin + split_len);
+
+  // extended query rows, pre-scaled by scale*log2(e)
+  const float qscale = sh.scale * 1.4426950408889634f;
+  for (int i = tid; i < kHB * row_w; i += 256) {
+    int hh = i / row_w, k = i % row_w, hd = h0 + hh;
+    float v = 0.f;
+    if (hd < sh.H) {
+      if (k < sh.r) {
+        v = Elem<T>::load(q_lat, (q * sh.H + hd) * sh.r + k);
+      } else {
+        int g = (k - sh.r) / sh.d_rope, j = (k - sh.r) % sh.d_rope;
+        if (g == hd / per_group) v = Elem<T>::load(q_pe, (q * sh.H + hd) * sh.d_rope + j);
+      }
+    }
+    sq[i] = v * qscale;
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  float acc[kRJ];
+#pragma unroll
+  for (int j = 0; j < kRJ; ++j) acc[j] = 0.f;
+
+  for (int l0 = l_begin; l0 < l_end; l0 += kLT) {
+    __syncthreads();
+    const int rows = min(kLT, l_end - l0);
+    for (int i = tid; i < rows * row_w; i += 256) {
+      int l = i / row_w, k = i % row_w;
+      sc[l * pitch + k] = cache[(start + l0 + l) * row_w + k];
+    }
+    __syncthreads();
+    float s = -INFINITY;
+    if (lane32 < rows) {
+      const float* qr = sq + hl * row_w;
+      const T* cr = sc + lane32 * pitch;
+      float a = 0.f;
+      for (int k = 0; k < row_w; ++k) a = fmaf(qr[k], Elem<T>::load(cr, k), a);
+      s = a;
+    }
+    float tmax = s;
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    const float p = exp2f(s - m_new);
+    float psum = p;
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) psum += __shfl_xor(psum, o, 64);
+    const float alpha = exp2f(m_run - m_new);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    sp[hl * kLT + lane32] = p;
+    __syncthreads();
+    const float* pr = sp + hl * kLT;
+#pragma unroll
+    for (int j = 0; j < kRJ; ++j) {
+      int c = lane32 + 32 * j;
+      if (c < sh.r) {
+        float a = acc[j] * alpha;
+        for (int l = 0; l < rows; ++l) a = fmaf(pr[l], Elem<T>::load(sc + l * pitch, c), a);
+        acc[j] = a;
+      }
+    }
+  }
+
+  if (head >= sh.H) return;
+  if (n_split == 1) {
+    const float inv = 1.f / l_run;
+#pragma unroll
+    for (int j = 0; j < kRJ; ++j) {
+      int c = lane32 + 32 * j;
+      if (c < sh.r) o_out[(q * sh.H + head) * sh.r + c] = acc[j] * inv;
+    }
+  } else {
+    const int64_t pidx = (q * n_split + split) * sh.H + head;
+#pragma unroll
+    for (int j = 0; j < kRJ; ++j) {
+      int c = lane32 + 32 * j;
+      if (c < sh.r) part_o[pidx * sh.r + c] = acc[j];
+    }
+    if (lane32 == 0) {
+      part_ml[pidx * 2 + 0] = m_run;
+      part_ml[pidx * 2 + 1] = l_run;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void merge_kernel(AttnShape sh, int n_split,
+                                                    const float* __restrict__ part_o,
+                                                    const float* __restrict__ part_ml,
+                                                    float* __restrict__ o_out) {
+  const int64_t q = blockIdx.x;
+  const int h = blockIdx.y;
+  float mx = -INFINITY;
+  for (int j = 0; j < n_split; ++j) mx = fmaxf(mx, part_ml[((q * n_split + j) * sh.H + h) * 2]);
+  float den = 0.f;
+  for (int j = 0; j < n_split; ++j) {
+    const float* ml = part_ml + ((q * n_split + j) * sh.H + h) * 2;
+    den += exp2f(ml[0] - mx) * ml[1];
+  }
+  const float inv = 1.f / den;
+  for (int c = threadIdx.x; c < sh.r; c += blockDim.x) {
+    float num = 0.f;
+    for (int j = 0; j < n_split; ++j) {
+      const int64_t pidx = (q * n_split + j) * sh.H + h;
+      num += exp2f(part_ml[pidx * 2] - mx) * part_o[pidx * sh.r + c];
+    }
+    o_out[(q * sh.H + h) * sh.r + c] = num * inv;
+  }
+}
+
+template <typename T>
+size_t smem_bytes(const AttnShape& sh) {
+  return sizeof(float) * (kHB * sh.row_w + kHB * kLT) +
+         sizeof(T) * kLT * lds_pitch(sh.row_w, sizeof(T));
+}
+
+}  // namespace
+
+int generic_head_block() { return kHB; }
+
+void attend_generic(int dtype, const AttnShape& sh, const void* q_lat, const void* q_pe,
+                    const void* cache, const int64_t* seq_start, const int32_t* seq_len,
+                    const int64_t* cu, int batch, int64_t n_q, int n_split, int split_len,
+                    float* part_o, float* part_ml, float* o_out, hipStream_t s) {
+  if (n_q <= 0) return;
+  dim3 grid(static_cast<unsigned>(n_q), (sh.H + kHB - 1) / kHB, n_split);
+  if (dtype == kF32) {
+    size_t smem = smem_bytes<float>(sh);
+    hipLaunchKernelGGL(attend_generic_kernel<float>, grid, dim3(256), smem, s,
+                       static_cast<const float*>(q_lat), static_cast<const float*>(q_pe),
+                       static_cast<const float*>(cache), seq_start, seq_len, cu, batch, sh, n_split,
+                       split_len, part_o, part_ml, o_out);
+  } else {
+    size_t smem = smem_bytes<bf16_t>(sh);
+    hipLaunchKernelGGL(attend_generic_kernel<bf16_t>, grid, dim3(256), smem, s,
+                       static_cast<const bf16_t*>(q_lat), static_cast<const bf16_t*>(q_pe),
+                       static_cast<const bf16_t*>(cache), seq_start, seq_len, cu, batch, sh,
+                       n_split, split_len, part_o, part_ml, o_out);
+  }
+}
+
+void merge_splits(const AttnShape& sh, int64_t n_q, int n_split, const float* part_o,
+                  const float* part_ml, float* o_out, hipStream_t s) {
+  if (n_q <= 0) return;
+  hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>(n_q), sh.H), dim3(256), 0, s, sh,
+                     n_split, part_o, part_ml, o_out);
+}
+
+}  // namespace mla

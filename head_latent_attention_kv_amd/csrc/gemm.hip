@@ -1,0 +1,247 @@
+// Batched strided GEMM used by the projection steps of the MLA path:
+//   C[z][m][n] = Σ_k A[z][m][k] · B[z][k][n]
+// A is k-contiguous (bf16, or fp32 split into a hi + lo pair of bf16 operands),
+// B is either [n][k] (k-contiguous: the [out, in] projection weights, W_UV) or
+// [k][n] (n-contiguous: W_UK, whose reduction dim is d_nope), C is fp32 or bf16.
+//
+// bf16 path: 256 threads = 4 wave64s in a 2x2 grid, each wave owning a
+// (BM/2)x(BN/2) block of v_mfma_f32_16x16x32_bf16 tiles; A and B tiles are
+// staged through LDS (k-contiguous, padded rows) with the next tile's global
+// loads in flight while the current one is multiplied.
+// fp32 path: plain LDS-tiled VALU kernel (small fp32 layers only).
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kBK = 64;        // k per LDS tile (two MFMA k-steps of 32)
+constexpr int kPitch = kBK + 8;  // LDS row pitch in bf16 (16 B pad against bank conflicts)
+
+// A chunk of 8 consecutive k.  bf16 A: the raw bits.  fp32 A: split into
+// hi = bf16(a) and lo = bf16(a - hi), so hi·b + lo·b keeps ~16 mantissa bits of a.
+template <bool A_F32>
+__device__ __forceinline__ void load_a_chunk(const void* A, int64_t off, bool ok, uint4& hi,
+                                             uint4& lo) {
+  if (!ok) {
+    hi = make_uint4(0, 0, 0, 0);
+    lo = hi;
+    return;
+  }
+  if constexpr (A_F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(A) + off);
+    float4 a = p[0], b = p[1];
+    float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float h0 = bf16_to_f32(f32_to_bf16(v[2 * i])), h1 = bf16_to_f32(f32_to_bf16(v[2 * i + 1]));
+      h[i] = pack_bf16x2(h0, h1);
+      l[i] = pack_bf16x2(v[2 * i] - h0, v[2 * i + 1] - h1);
+    }
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
+  } else {
+    hi = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(A) + off);
+  }
+}
+
+template <int BM, int BN, bool A_F32, bool B_KN, typename OutT>
+__global__ __launch_bounds__(256) void gemm_bf16_mfma(GemmArgs g) {
+  constexpr int WM = BM / 2, WN = BN / 2;     // per-wave block
+  constexpr int TM = WM / 16, TN = WN / 16;   // MFMA tiles per wave
+  constexpr int A_CHUNKS = BM * kBK / 8 / 256;  // 16-byte chunks per thread
+  constexpr int B_CHUNKS = BN * kBK / 8 / 256;
+  static_assert(A_CHUNKS >= 1 && B_CHUNKS >= 1, "tile too small");
+
+  __shared__ __attribute__((aligned(16))) bf16_t sA[BM * kPitch];
+  __shared__ __attribute__((aligned(16))) bf16_t sAlo[A_F32 ? BM * kPitch : 8];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[BN * kPitch];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int z = blockIdx.z;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+
+  const int64_t a_base = static_cast<int64_t>(z) * g.sAz;
+  const int64_t b_base = static_cast<int64_t>(z) * g.sBz;
+
+  uint4 ra[A_CHUNKS], ralo[A_CHUNKS], rb[B_CHUNKS];
+
+  auto load_tiles = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) {
+      int c = tid + i * 256;
+      int row = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
+      int m = m0 + row, k = k0 + kc;
+      bool ok = (m < g.M) && (k < g.K);
+      load_a_chunk<A_F32>(g.A, a_base + static_cast<int64_t>(m) * g.sAm + k, ok, ra[i], ralo[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < B_CHUNKS; ++i) {
+      int c = tid + i * 256;
+      if constexpr (!B_KN) {
+        int row = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
+        int n = n0 + row, k = k0 + kc;
+        bool ok = (n < g.N) && (k < g.K);
+        rb[i] = ok ? *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(g.B) + b_base +
+                                                      static_cast<int64_t>(n) * g.sBo + k)
+                   : make_uint4(0, 0, 0, 0);
+      } else {
+        // chunk = 8 consecutive n at one k
+        int krow = c / (BN / 8), nc = (c % (BN / 8)) * 8;
+        int n = n0 + nc, k = k0 + krow;
+        bool ok = (n < g.N) && (k < g.K);  // N % 8 == 0 is checked by the host
+        rb[i] = ok ? *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(g.B) + b_base +
+                                                      static_cast<int64_t>(k) * g.sBo + n)
+                   : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  auto store_tiles = [&]() {
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) {
+      int c = tid + i * 256;
+      int row = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
+      *reinterpret_cast<uint4*>(&sA[row * kPitch + kc]) = ra[i];
+      if constexpr (A_F32) *reinterpret_cast<uint4*>(&sAlo[row * kPitch + kc]) = ralo[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_CHUNKS; ++i) {
+      int c = tid + i * 256;
+      if constexpr (!B_KN) {
+        int row = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
+        *reinterpret_cast<uint4*>(&sB[row * kPitch + kc]) = rb[i];
+      } else {
+        int krow = c / (BN / 8), nc = (c % (BN / 8)) * 8;
+        const bf16_t* v = reinterpret_cast<const bf16_t*>(&rb[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sB[(nc + e) * kPitch + krow] = v[e];
+      }
+    }
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load_tiles(0);
+  for (int k0 = 0; k0 < g.K; k0 += kBK) {
+    __syncthreads();
+    store_tiles();
+    __syncthreads();
+    if (k0 + kBK < g.K) load_tiles(k0 + kBK);
+#pragma unroll
+    for (int ks = 0; ks < kBK / 32; ++ks) {
+      const int kof = ks * 32 + 8 * (lane >> 4);
+      bf16x8 af[TM], aflo[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int a_off = (wm * WM + i * 16 + (lane & 15)) * kPitch + kof;
+        af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sA[a_off]));
+        if constexpr (A_F32) aflo[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sAlo[a_off]));
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        uint4 v = *reinterpret_cast<const uint4*>(&sB[(wn * WN + j * 16 + (lane & 15)) * kPitch + kof]);
+        bfr[j] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          if constexpr (A_F32)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aflo[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+    }
+  }
+
+  OutT* C = static_cast<OutT*>(g.C) + static_cast<int64_t>(z) * g.sCz;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      int n = n0 + wn * WN + j * 16 + (lane & 15);
+      if (n >= g.N) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        int m = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + e;
+        if (m < g.M) Elem<OutT>::store(C, static_cast<int64_t>(m) * g.sCm + n, acc[i][j][e]);
+      }
+    }
+}
+
+// fp32 VALU GEMM: 16x16 outputs per 256-thread block, k staged by 16.
+template <bool B_KN>
+__global__ __launch_bounds__(256) void gemm_f32_valu(GemmArgs g) {
+  __shared__ float sA[16][17];
+  __shared__ float sB[16][17];  // sB[n][k]
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int z = blockIdx.z;
+  const int m = blockIdx.y * 16 + ty, n = blockIdx.x * 16 + tx;
+  const float* A = static_cast<const float*>(g.A) + static_cast<int64_t>(z) * g.sAz;
+  const float* B = static_cast<const float*>(g.B) + static_cast<int64_t>(z) * g.sBz;
+  float acc = 0.f;
+  for (int k0 = 0; k0 < g.K; k0 += 16) {
+    int am = blockIdx.y * 16 + ty, ak = k0 + tx;
+    sA[ty][tx] = (am < g.M && ak < g.K) ? A[static_cast<int64_t>(am) * g.sAm + ak] : 0.f;
+    int bn = blockIdx.x * 16 + ty, bk = k0 + tx;
+    float bv = 0.f;
+    if (bn < g.N && bk < g.K)
+      bv = B_KN ? B[static_cast<int64_t>(bk) * g.sBo + bn] : B[static_cast<int64_t>(bn) * g.sBo + bk];
+    sB[ty][tx] = bv;
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) acc = fmaf(sA[ty][kk], sB[tx][kk], acc);
+    __syncthreads();
+  }
+  if (m < g.M && n < g.N)
+    static_cast<float*>(g.C)[static_cast<int64_t>(z) * g.sCz + static_cast<int64_t>(m) * g.sCm + n] = acc;
+}
+
+template <int BM, int BN, bool A_F32, bool B_KN>
+void launch_bf16(const GemmArgs& g, bool out_bf16, hipStream_t s) {
+  dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, g.Z);
+  if (out_bf16)
+    hipLaunchKernelGGL((gemm_bf16_mfma<BM, BN, A_F32, B_KN, bf16_t>), grid, dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_bf16_mfma<BM, BN, A_F32, B_KN, float>), grid, dim3(256), 0, s, g);
+}
+
+template <int BM, int BN>
+void dispatch_bf16(const GemmArgs& g, bool a_f32, bool b_kn, bool out_bf16, hipStream_t s) {
+  if (a_f32) {
+    if (b_kn) launch_bf16<BM, BN, true, true>(g, out_bf16, s);
+    else launch_bf16<BM, BN, true, false>(g, out_bf16, s);
+  } else {
+    if (b_kn) launch_bf16<BM, BN, false, true>(g, out_bf16, s);
+    else launch_bf16<BM, BN, false, false>(g, out_bf16, s);
+  }
+}
+
+}  // namespace
+
+void gemm(const GemmArgs& g, int dtype, bool a_f32, bool b_kn, bool out_bf16, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0 || g.Z <= 0) return;
+  if (dtype == kF32) {
+    dim3 grid((g.N + 15) / 16, (g.M + 15) / 16, g.Z);
+    if (b_kn) hipLaunchKernelGGL(gemm_f32_valu<true>, grid, dim3(256), 0, s, g);
+    else hipLaunchKernelGGL(gemm_f32_valu<false>, grid, dim3(256), 0, s, g);
+    return;
+  }
+  // Large problems: 128x128 tiles; otherwise 64x64 for more blocks.
+  int64_t tiles128 = static_cast<int64_t>((g.M + 127) / 128) * ((g.N + 127) / 128) * g.Z;
+  if (g.M >= 256 && tiles128 >= 512)
+    dispatch_bf16<128, 128>(g, a_f32, b_kn, out_bf16, s);
+  else
+    dispatch_bf16<64, 64>(g, a_f32, b_kn, out_bf16, s);
+}
+
+}  // namespace mla

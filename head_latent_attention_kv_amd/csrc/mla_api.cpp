@@ -1,0 +1,325 @@
+// C ABI of the MLA latent-cache hot path: argument validation, workspace
+// planning and kernel launches.  The declarations and their contracts are in
+// include/mla.h.  Nothing here allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/mla.h"
+#include "mla_internal.h"
+
+namespace {
+
+using mla::AttnShape;
+using mla::GemmArgs;
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxRank = 512;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
+
+int check_dims(const mla_dims* d) {
+  if (!d) return MLA_EINVAL;
+  if (d->d_model <= 0 || d->n_heads <= 0 || d->n_groups <= 0 || d->rank <= 0 || d->d_rope <= 0 ||
+      d->d_nope <= 0 || d->d_v <= 0)
+    return MLA_EINVAL;
+  if (d->n_heads % d->n_groups != 0) return MLA_EINVAL;
+  if (d->d_rope % 2 != 0) return MLA_EINVAL;
+  if (d->dtype != MLA_F32 && d->dtype != MLA_BF16) return MLA_EINVAL;
+  if (d->latent_rmsnorm != 0 && d->latent_rmsnorm != 1) return MLA_EINVAL;
+  if (!(d->rms_eps >= 0.f) || !isfinite(d->rms_eps)) return MLA_EINVAL;
+  if (isnan(d->softmax_scale) || isinf(d->softmax_scale)) return MLA_EINVAL;
+  if (!(d->rope_theta > 0.0) || !isfinite(d->rope_theta)) return MLA_EINVAL;
+  // limits of the compiled kernels
+  if (d->rank > kMaxRank || d->rank % 16 != 0) return MLA_ENOTSUP;
+  if (d->dtype == MLA_BF16 && (d->d_model % 8 != 0 || d->d_nope % 8 != 0)) return MLA_ENOTSUP;
+  return MLA_OK;
+}
+
+float eff_scale(const mla_dims* d) {
+  if (d->softmax_scale > 0.f) return d->softmax_scale;
+  return 1.0f / sqrtf(static_cast<float>(d->d_nope + d->d_rope));
+}
+
+AttnShape shape_of(const mla_dims* d) {
+  AttnShape s;
+  s.H = d->n_heads;
+  s.G = d->n_groups;
+  s.r = d->rank;
+  s.d_rope = d->d_rope;
+  s.row_w = d->rank + d->n_groups * d->d_rope;
+  s.scale = eff_scale(d);
+  return s;
+}
+
+// How a decode call is split.  Shared by mla_workspace_size and mla_decode so the
+// two always agree.
+struct DecodePlan {
+  bool mfma;
+  int n_split;
+  int split_len;
+  size_t part_o_bytes, part_ml_bytes, o_bytes;
+  size_t total() const { return part_o_bytes + part_ml_bytes + o_bytes; }
+};
+
+DecodePlan decode_plan(const mla_dims* d, int32_t batch, int32_t max_len) {
+  DecodePlan p{};
+  AttnShape sh = shape_of(d);
+  p.mfma = d->dtype == MLA_BF16 && mla::decode_mfma_supported(sh);
+  const int64_t B = std::max<int32_t>(batch, 0);
+  const int L = std::max<int32_t>(max_len, 1);
+  // blocks per split: the generic kernel splits heads into blocks, the MFMA
+  // kernel keeps all heads of a sequence in one block.
+  const int64_t per_split = p.mfma ? B : B * ((sh.H + mla::generic_head_block() - 1) / mla::generic_head_block());
+  // aim for ~2 blocks per compute unit (256 CUs) and >= 256 rows per split
+  const int64_t target = 512;
+  int64_t ns = per_split > 0 ? (target + per_split - 1) / per_split : 1;
+  const int64_t max_ns = std::max<int64_t>(1, (L + 255) / 256);
+  ns = std::max<int64_t>(1, std::min<int64_t>(ns, max_ns));
+  int split_len = static_cast<int>((L + ns - 1) / ns);
+  split_len = (split_len + 63) / 64 * 64;
+  ns = (L + split_len - 1) / split_len;
+  p.n_split = static_cast<int>(ns);
+  p.split_len = split_len;
+  p.o_bytes = align_up(static_cast<size_t>(B) * sh.H * sh.r * sizeof(float));
+  if (p.n_split > 1) {
+    p.part_o_bytes = align_up(static_cast<size_t>(B) * p.n_split * sh.H * sh.r * sizeof(float));
+    p.part_ml_bytes = align_up(static_cast<size_t>(B) * p.n_split * sh.H * 2 * sizeof(float));
+  }
+  return p;
+}
+
+size_t prefill_ws(const mla_dims* d, int64_t n_tokens) {
+  return align_up(static_cast<size_t>(std::max<int64_t>(n_tokens, 0)) * d->n_heads * d->rank *
+                  sizeof(float));
+}
+
+size_t write_ws(const mla_dims* d, int64_t n_tokens) {
+  return align_up(static_cast<size_t>(std::max<int64_t>(n_tokens, 0)) *
+                  (d->rank + d->n_groups * d->d_rope) * sizeof(float));
+}
+
+size_t absorb_ws(const mla_dims* d, int64_t n_tokens) {
+  const size_t T = static_cast<size_t>(std::max<int64_t>(n_tokens, 0));
+  return align_up(T * d->n_heads * d->d_nope * sizeof(float)) +
+         align_up(T * d->n_heads * d->d_rope * sizeof(float));
+}
+
+int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MLA_OK : MLA_EHIP;
+}
+
+// out[q, h, :] = W_UV[h] · o_[q, h, :]   (o_ fp32 [n_q, H, r]; W_UV [H, d_v, r])
+void apply_w_uv(const mla_dims* d, const float* o_lat, int64_t n_q, const void* w_uv, void* out,
+                hipStream_t s) {
+  GemmArgs g{};
+  g.A = o_lat;
+  g.sAz = d->rank;
+  g.sAm = static_cast<int64_t>(d->n_heads) * d->rank;
+  g.B = w_uv;
+  g.sBz = static_cast<int64_t>(d->d_v) * d->rank;
+  g.sBo = d->rank;
+  g.C = out;
+  g.sCz = d->d_v;
+  g.sCm = static_cast<int64_t>(d->n_heads) * d->d_v;
+  g.M = static_cast<int>(n_q);
+  g.N = d->d_v;
+  g.K = d->rank;
+  g.Z = d->n_heads;
+  mla::gemm(g, d->dtype, /*a_f32=*/true, /*b_kn=*/false, /*out_bf16=*/d->dtype == MLA_BF16, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_version(void) { return 100; }
+
+const char* mla_strerror(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_EINVAL: return "invalid argument";
+    case MLA_ENOTSUP: return "unsupported dimensions";
+    case MLA_EWORKSPACE: return "workspace too small";
+    case MLA_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int mla_check_dims(const mla_dims* dims) { return check_dims(dims); }
+
+size_t mla_workspace_size(const mla_dims* dims, int op, int32_t batch, int64_t n_tokens,
+                          int32_t max_len) {
+  if (check_dims(dims) != MLA_OK) return 0;
+  switch (op) {
+    case MLA_OP_WRITE_CACHE: return write_ws(dims, n_tokens);
+    case MLA_OP_ABSORB: return absorb_ws(dims, n_tokens);
+    case MLA_OP_DECODE: return decode_plan(dims, batch, max_len).total();
+    case MLA_OP_PREFILL: return prefill_ws(dims, n_tokens);
+    default: return 0;
+  }
+}
+
+int mla_write_cache(const mla_dims* dims, const void* x, const void* w_dkv, const void* w_kr,
+                    const int32_t* positions, const int64_t* slots, int64_t n_tokens, void* cache,
+                    int64_t cache_rows, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_tokens < 0 || cache_rows < 0) return MLA_EINVAL;
+  if (n_tokens == 0) return MLA_OK;
+  if (n_tokens > INT32_MAX) return MLA_ENOTSUP;
+  if (!ptr_ok(x) || !ptr_ok(w_dkv) || !ptr_ok(w_kr) || !ptr_ok(positions) || !ptr_ok(slots) ||
+      !ptr_ok(cache) || !ptr_ok(workspace))
+    return MLA_EINVAL;
+  if (workspace_bytes < write_ws(dims, n_tokens)) return MLA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int row_w = dims->rank + dims->n_groups * dims->d_rope;
+  float* proj = static_cast<float*>(workspace);
+
+  GemmArgs g{};
+  g.A = x;
+  g.sAz = 0;
+  g.sAm = dims->d_model;
+  g.B = w_dkv;
+  g.sBz = 0;
+  g.sBo = dims->d_model;
+  g.C = proj;
+  g.sCz = 0;
+  g.sCm = row_w;
+  g.M = static_cast<int>(n_tokens);
+  g.N = dims->rank;
+  g.K = dims->d_model;
+  g.Z = 1;
+  mla::gemm(g, dims->dtype, false, false, false, s);
+  g.B = w_kr;
+  g.C = proj + dims->rank;
+  g.N = dims->n_groups * dims->d_rope;
+  mla::gemm(g, dims->dtype, false, false, false, s);
+  mla::finalize_cache_rows(dims->dtype, proj, row_w, cache, slots, positions, n_tokens,
+                           dims->rank, dims->n_groups, dims->d_rope, dims->latent_rmsnorm,
+                           dims->rms_eps, dims->rope_theta, s);
+  return launch_status();
+}
+
+int mla_absorb(const mla_dims* dims, const void* x, const void* w_qc, const void* w_qr,
+               const void* w_uk, const int32_t* positions, int64_t n_tokens, void* q_lat,
+               void* q_pe, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_tokens < 0) return MLA_EINVAL;
+  if (n_tokens == 0) return MLA_OK;
+  if (n_tokens > INT32_MAX) return MLA_ENOTSUP;
+  if (!ptr_ok(x) || !ptr_ok(w_qc) || !ptr_ok(w_qr) || !ptr_ok(w_uk) || !ptr_ok(positions) ||
+      !ptr_ok(q_lat) || !ptr_ok(q_pe) || !ptr_ok(workspace))
+    return MLA_EINVAL;
+  if (workspace_bytes < absorb_ws(dims, n_tokens)) return MLA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int H = dims->n_heads;
+  const size_t T = static_cast<size_t>(n_tokens);
+  float* qn = static_cast<float*>(workspace);
+  float* qr = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       align_up(T * H * dims->d_nope * sizeof(float)));
+
+  GemmArgs g{};
+  g.A = x;
+  g.sAm = dims->d_model;
+  g.B = w_qc;
+  g.sBo = dims->d_model;
+  g.C = qn;
+  g.sCm = static_cast<int64_t>(H) * dims->d_nope;
+  g.M = static_cast<int>(n_tokens);
+  g.N = H * dims->d_nope;
+  g.K = dims->d_model;
+  g.Z = 1;
+  mla::gemm(g, dims->dtype, false, false, false, s);
+  g.B = w_qr;
+  g.C = qr;
+  g.sCm = static_cast<int64_t>(H) * dims->d_rope;
+  g.N = H * dims->d_rope;
+  mla::gemm(g, dims->dtype, false, false, false, s);
+  mla::finalize_query_rope(dims->dtype, qr, q_pe, positions, n_tokens, H, dims->d_rope,
+                           dims->rope_theta, s);
+  // q_lat[t,h,:] = Σ_d qn[t,h,d] W_UK[h,d,:]   (batched over heads)
+  GemmArgs a{};
+  a.A = qn;
+  a.sAz = dims->d_nope;
+  a.sAm = static_cast<int64_t>(H) * dims->d_nope;
+  a.B = w_uk;
+  a.sBz = static_cast<int64_t>(dims->d_nope) * dims->rank;
+  a.sBo = dims->rank;
+  a.C = q_lat;
+  a.sCz = dims->rank;
+  a.sCm = static_cast<int64_t>(H) * dims->rank;
+  a.M = static_cast<int>(n_tokens);
+  a.N = dims->rank;
+  a.K = dims->d_nope;
+  a.Z = H;
+  mla::gemm(a, dims->dtype, /*a_f32=*/true, /*b_kn=*/true, dims->dtype == MLA_BF16, s);
+  return launch_status();
+}
+
+int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_pe, const void* cache,
+               const int64_t* seq_start, const int32_t* seq_len, int32_t batch, int32_t max_len,
+               const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0) return MLA_EINVAL;
+  if (batch == 0) return MLA_OK;
+  if (max_len <= 0) return MLA_EINVAL;
+  if (!ptr_ok(q_lat) || !ptr_ok(q_pe) || !ptr_ok(cache) || !ptr_ok(seq_start) ||
+      !ptr_ok(seq_len) || !ptr_ok(w_uv) || !ptr_ok(out) || !ptr_ok(workspace))
+    return MLA_EINVAL;
+  DecodePlan p = decode_plan(dims, batch, max_len);
+  if (workspace_bytes < p.total()) return MLA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AttnShape sh = shape_of(dims);
+  char* ws = static_cast<char*>(workspace);
+  float* o_lat = reinterpret_cast<float*>(ws);
+  float* part_o = p.n_split > 1 ? reinterpret_cast<float*>(ws + p.o_bytes) : nullptr;
+  float* part_ml = p.n_split > 1 ? reinterpret_cast<float*>(ws + p.o_bytes + p.part_o_bytes) : nullptr;
+  if (p.mfma)
+    mla::decode_mfma(sh, q_lat, q_pe, cache, seq_start, seq_len, batch, p.n_split, p.split_len,
+                     part_o, part_ml, o_lat, s);
+  else
+    mla::attend_generic(dims->dtype, sh, q_lat, q_pe, cache, seq_start, seq_len, nullptr, batch,
+                        batch, p.n_split, p.split_len, part_o, part_ml, o_lat, s);
+  if (p.n_split > 1) mla::merge_splits(sh, batch, p.n_split, part_o, part_ml, o_lat, s);
+  apply_w_uv(dims, o_lat, batch, w_uv, out, s);
+  return launch_status();
+}
+
+int mla_prefill(const mla_dims* dims, const void* q_lat, const void* q_pe, const void* cache,
+                const int64_t* cu_seqlens, int32_t batch, int64_t n_tokens, int32_t max_len,
+                const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || n_tokens < 0) return MLA_EINVAL;
+  if (batch == 0 || n_tokens == 0) return MLA_OK;
+  if (max_len <= 0) return MLA_EINVAL;
+  if (n_tokens > INT32_MAX) return MLA_ENOTSUP;
+  if (!ptr_ok(q_lat) || !ptr_ok(q_pe) || !ptr_ok(cache) || !ptr_ok(cu_seqlens) || !ptr_ok(w_uv) ||
+      !ptr_ok(out) || !ptr_ok(workspace))
+    return MLA_EINVAL;
+  if (workspace_bytes < prefill_ws(dims, n_tokens)) return MLA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AttnShape sh = shape_of(dims);
+  float* o_lat = static_cast<float*>(workspace);
+  if (dims->dtype == MLA_BF16 && mla::prefill_mfma_supported(sh))
+    mla::prefill_mfma(sh, q_lat, q_pe, cache, cu_seqlens, batch, n_tokens, max_len, o_lat, s);
+  else
+    mla::attend_generic(dims->dtype, sh, q_lat, q_pe, cache, nullptr, nullptr, cu_seqlens, batch,
+                        n_tokens, 1, max_len, nullptr, nullptr, o_lat, s);
+  apply_w_uv(dims, o_lat, n_tokens, w_uv, out, s);
+  return launch_status();
+}
+
+}  // extern "C"

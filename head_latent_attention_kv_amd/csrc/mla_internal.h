@@ -1,0 +1,72 @@
+// Internal launcher interface between the C ABI (mla_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+// C[z][m][n] = Σ_k A[z][m][k] · B[z][k][n]; strides in elements.
+struct GemmArgs {
+  const void* A;
+  int64_t sAz, sAm;  // A[z][m][k]: k contiguous
+  const void* B;
+  int64_t sBz, sBo;  // b_kn: B[z][k][n] (sBo = k stride); else B[z][n][k] (sBo = n stride)
+  void* C;
+  int64_t sCz, sCm;  // C[z][m][n]: n contiguous
+  int M, N, K, Z;
+};
+
+// dtype == kF32: fp32 in/out VALU path.  dtype == kBF16: A bf16 (or fp32 if a_f32),
+// B bf16, fp32 accumulate, C fp32 or bf16 (out_bf16).
+void gemm(const GemmArgs& g, int dtype, bool a_f32, bool b_kn, bool out_bf16, hipStream_t s);
+
+// Cache rows from the fp32 projections in `proj` ([T, r + G*d_rope], row stride ld):
+// optional RMSNorm over the latent, RoPE on each rotary-key group, cast, scatter to slots.
+void finalize_cache_rows(int dtype, const float* proj, int64_t ld, void* cache,
+                         const int64_t* slots, const int32_t* positions, int64_t n_tokens, int r,
+                         int n_groups, int d_rope, int latent_rmsnorm, float eps, double theta,
+                         hipStream_t s);
+
+// q_pe[t,h,:] = RoPE(proj[t, h*d_rope : +d_rope], positions[t]), cast to dtype.
+void finalize_query_rope(int dtype, const float* proj, void* q_pe, const int32_t* positions,
+                         int64_t n_tokens, int n_heads, int d_rope, double theta, hipStream_t s);
+
+// Shape of one attention call, as the kernels see it.
+struct AttnShape {
+  int H, G, r, d_rope, row_w;  // row_w = r + G*d_rope
+  float scale;
+};
+
+// Generic split-K attention over cache rows (any dtype/shape within limits).
+// Query q (0..n_q-1) attends rows: decode (cu == nullptr): seq_start[q] + [0, seq_len[q]);
+// prefill: rows cu[b] .. q, where cu[b] <= q < cu[b+1].
+// n_split == 1: writes normalised o_ (fp32 [n_q, H, r]) to o_out.
+// n_split > 1: writes partials part_o [n_q, n_split, H, r] and part_ml [n_q, n_split, H, 2].
+void attend_generic(int dtype, const AttnShape& sh, const void* q_lat, const void* q_pe,
+                    const void* cache, const int64_t* seq_start, const int32_t* seq_len,
+                    const int64_t* cu, int batch, int64_t n_q, int n_split, int split_len,
+                    float* part_o, float* part_ml, float* o_out, hipStream_t s);
+int generic_head_block();
+
+// Log-sum-exp merge of split partials into normalised o_ (fp32 [n_q, H, r]).
+void merge_splits(const AttnShape& sh, int64_t n_q, int n_split, const float* part_o,
+                  const float* part_ml, float* o_out, hipStream_t s);
+
+// bf16 MFMA decode kernel for the shapes it supports (see decode_mfma.hip).
+bool decode_mfma_supported(const AttnShape& sh);
+void decode_mfma(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
+                 const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split,
+                 int split_len, float* part_o, float* part_ml, float* o_out, hipStream_t s);
+
+// bf16 MFMA causal prefill kernel for the shapes it supports (see prefill_mfma.hip).
+bool prefill_mfma_supported(const AttnShape& sh);
+void prefill_mfma(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
+                  const int64_t* cu, int batch, int64_t n_tokens, int max_len, float* o_out,
+                  hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,103 @@
+// Row epilogues of the projection GEMMs:
+//  - cache rows: optional unit-gain RMSNorm over the latent, rotate-half RoPE of
+//    each rotary-key group at the token's position, cast, store to its slot;
+//  - query rotary part: RoPE of q_pe per head.
+// RoPE pairs dims (j, j + d/2), angle p·θ^(-2j/d) formed in double.
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+
+namespace {
+
+template <typename T>
+__global__ __launch_bounds__(256) void cache_rows_kernel(const float* __restrict__ proj, int64_t ld,
+                                                         T* __restrict__ cache,
+                                                         const int64_t* __restrict__ slots,
+                                                         const int32_t* __restrict__ positions,
+                                                         int r, int n_groups, int d_rope,
+                                                         int latent_rmsnorm, float eps,
+                                                         double theta) {
+  const int64_t t = blockIdx.x;
+  const float* row = proj + t * ld;
+  const int row_w = r + n_groups * d_rope;
+  T* dst = cache + slots[t] * static_cast<int64_t>(row_w);
+  const int32_t pos = positions[t];
+
+  float inv = 1.f;
+  if (latent_rmsnorm) {
+    __shared__ float red[4];
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < r; i += blockDim.x) ss = fmaf(row[i], row[i], ss);
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int w = 0; w < static_cast<int>(blockDim.x) / 64; ++w) tot += red[w];
+    inv = 1.0f / sqrtf(tot / static_cast<float>(r) + eps);
+  }
+  for (int i = threadIdx.x; i < r; i += blockDim.x) Elem<T>::store(dst, i, row[i] * inv);
+
+  const int half = d_rope / 2;
+  for (int i = threadIdx.x; i < n_groups * half; i += blockDim.x) {
+    int g = i / half, j = i % half;
+    float cs, sn;
+    rope_cos_sin(pos, j, d_rope, theta, &cs, &sn);
+    const float* src = row + r + g * d_rope;
+    float a = src[j], b = src[j + half];
+    Elem<T>::store(dst, r + g * d_rope + j, a * cs - b * sn);
+    Elem<T>::store(dst, r + g * d_rope + j + half, b * cs + a * sn);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void query_rope_kernel(const float* __restrict__ proj,
+                                                         T* __restrict__ q_pe,
+                                                         const int32_t* __restrict__ positions,
+                                                         int n_heads, int d_rope, double theta) {
+  const int64_t t = blockIdx.x;
+  const int half = d_rope / 2;
+  const int32_t pos = positions[t];
+  const float* src = proj + t * static_cast<int64_t>(n_heads) * d_rope;
+  T* dst = q_pe + t * static_cast<int64_t>(n_heads) * d_rope;
+  for (int i = threadIdx.x; i < n_heads * half; i += blockDim.x) {
+    int h = i / half, j = i % half;
+    float cs, sn;
+    rope_cos_sin(pos, j, d_rope, theta, &cs, &sn);
+    float a = src[h * d_rope + j], b = src[h * d_rope + j + half];
+    Elem<T>::store(dst, h * d_rope + j, a * cs - b * sn);
+    Elem<T>::store(dst, h * d_rope + j + half, b * cs + a * sn);
+  }
+}
+
+}  // namespace
+
+void finalize_cache_rows(int dtype, const float* proj, int64_t ld, void* cache,
+                         const int64_t* slots, const int32_t* positions, int64_t n_tokens, int r,
+                         int n_groups, int d_rope, int latent_rmsnorm, float eps, double theta,
+                         hipStream_t s) {
+  if (n_tokens <= 0) return;
+  dim3 grid(static_cast<unsigned>(n_tokens));
+  if (dtype == kF32)
+    hipLaunchKernelGGL(cache_rows_kernel<float>, grid, dim3(256), 0, s, proj, ld,
+                       static_cast<float*>(cache), slots, positions, r, n_groups, d_rope,
+                       latent_rmsnorm, eps, theta);
+  else
+    hipLaunchKernelGGL(cache_rows_kernel<bf16_t>, grid, dim3(256), 0, s, proj, ld,
+                       static_cast<bf16_t*>(cache), slots, positions, r, n_groups, d_rope,
+                       latent_rmsnorm, eps, theta);
+}
+
+void finalize_query_rope(int dtype, const float* proj, void* q_pe, const int32_t* positions,
+                         int64_t n_tokens, int n_heads, int d_rope, double theta, hipStream_t s) {
+  if (n_tokens <= 0) return;
+  dim3 grid(static_cast<unsigned>(n_tokens));
+  if (dtype == kF32)
+    hipLaunchKernelGGL(query_rope_kernel<float>, grid, dim3(256), 0, s, proj,
+                       static_cast<float*>(q_pe), positions, n_heads, d_rope, theta);
+  else
+    hipLaunchKernelGGL(query_rope_kernel<bf16_t>, grid, dim3(256), 0, s, proj,
+                       static_cast<bf16_t*>(q_pe), positions, n_heads, d_rope, theta);
+}
+
+}  // namespace mla

@@ -1,0 +1,172 @@
+/*
+ * mla.h — C ABI of the MLA latent-cache hot path for AMD Instinct MI355X (gfx950).
+ *
+ * Multi-head Latent Attention keeps one row per token in the KV cache:
+ *   row = [ c (r values) ; kr_0 (d_rope) ; ... ; kr_{G-1} (d_rope) ]
+ * where c = x·W_DKVᵀ is the low-rank latent and kr_g the rotary key of group g,
+ * already rotated by the token's position.  Attention is computed in the
+ * "absorbed" order: W_UK is folded into the query (q_lat = q_nope·W_UK), scores
+ * are taken against the latent directly, P·c is formed in latent space and W_UV
+ * is applied last.
+ *
+ * Sources (pages on MLA; equations are the pages' own numbers):
+ *  - MLA principle page (dtcms.com, DeepSeek-V2 walkthrough), section on the
+ *    KV down-projection and up-projection (kv_a_proj_with_mqa / kv_b_proj), the
+ *    section on rotating q_pe and k_pe, and section "矩阵吸收" with the absorbed
+ *    score q_pe·k_peᵀ + q_lat·cᵀ and eqs. (4)-(5) (o_ = P·c, o = o_·W_UV).
+ *  - Qwen2.5-7B MLAfication page (wzjinhao.cn), section on how MLAfication
+ *    rewrites attention: only the latent is cached, RoPE only on a small
+ *    rotary subspace per KV head, the query split into content and rotary parts.
+ *  - nanowhale-100m MLA page (cnnetsun.cn), section on attention: causal
+ *    scaled-dot-product attention with an explicit scale.
+ *
+ * Conventions for every entry point
+ *  - Pointers named "device" are device (HBM) addresses on the current HIP
+ *    device; the caller allocates and owns every buffer, including workspaces.
+ *    The library allocates nothing, frees nothing and never synchronises: all
+ *    work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *  - Tensors are dense row-major.  Element type of x, weights, cache, q_lat,
+ *    q_pe and out is dims->dtype (MLA_F32 or MLA_BF16); positions are int32,
+ *    cache slots / sequence starts are int64, lengths are int32.
+ *    Base pointers must be 16-byte aligned.
+ *  - Projection weights use the [out_features, in_features] layout:
+ *      W_DKV [r, d_model]   W_KR [G*d_rope, d_model]
+ *      W_QC  [H*d_nope, d_model]   W_QR [H*d_rope, d_model]
+ *    and the up-projection is split per head: W_UK [H, d_nope, r], W_UV [H, d_v, r].
+ *  - Return value: MLA_OK or a negative mla_status.  Argument errors are
+ *    detected on the host before anything is enqueued, and outputs are then
+ *    untouched.  Contents of device index arrays (positions, slots, lengths)
+ *    are trusted: out-of-range values are undefined behaviour.
+ *  - Calls on one stream are ordered; calls on different streams that share a
+ *    workspace or an output race.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_EINVAL = -1,     /* null/misaligned pointer, bad dimension, H % G != 0, ... */
+  MLA_ENOTSUP = -2,    /* a dimension combination the compiled kernels do not cover */
+  MLA_EWORKSPACE = -3, /* workspace smaller than mla_workspace_size() */
+  MLA_EHIP = -4        /* the HIP runtime reported an error at launch */
+} mla_status;
+
+typedef enum mla_dtype { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+typedef enum mla_op {
+  MLA_OP_WRITE_CACHE = 0,
+  MLA_OP_ABSORB = 1,
+  MLA_OP_DECODE = 2,
+  MLA_OP_PREFILL = 3
+} mla_op;
+
+/* Layer dimensions and hyper-parameters shared by all calls. */
+typedef struct mla_dims {
+  int32_t d_model;        /* hidden size of x */
+  int32_t n_heads;        /* H, query heads */
+  int32_t n_groups;       /* G, rotary-key groups; head h uses group h / (H/G) */
+  int32_t rank;           /* r, latent width (multiple of 16) */
+  int32_t d_rope;         /* rotary dims per query head and per key group (even) */
+  int32_t d_nope;         /* non-rotary query/key dims per head */
+  int32_t d_v;            /* value dims per head */
+  int32_t dtype;          /* mla_dtype */
+  int32_t latent_rmsnorm; /* 1: c <- c / sqrt(mean(c^2) + rms_eps) before storage */
+  float rms_eps;          /* RMSNorm epsilon (unit gain) */
+  float softmax_scale;    /* applied to the whole score; <= 0 selects 1/sqrt(d_nope + d_rope) */
+  double rope_theta;      /* RoPE base; pair (j, j + d_rope/2) turns by p * theta^(-2j/d_rope) */
+} mla_dims;
+
+/* Bytes of scratch an operation needs for the given sizes (0 if none).
+ * op: mla_op.  batch: sequences (decode/prefill).  n_tokens: tokens in the call.
+ * max_len: the largest per-sequence context in the call (decode/prefill).
+ * Returns 0 also for invalid dims; mla_check_dims() tells them apart. */
+size_t mla_workspace_size(const mla_dims* dims, int op, int32_t batch, int64_t n_tokens,
+                          int32_t max_len);
+
+/* Validate dims on the host only (no HIP call).  MLA_OK, MLA_EINVAL or MLA_ENOTSUP. */
+int mla_check_dims(const mla_dims* dims);
+
+/* Cache write (latent down-projection + partial RoPE key), for n_tokens tokens.
+ *   cache[slots[t], 0:r]                = c[t] = x[t]·W_DKVᵀ   (RMSNorm'd if latent_rmsnorm)
+ *   cache[slots[t], r+g*d_rope : +d_rope] = RoPE(x[t]·W_KR[g*d_rope : +d_rope]ᵀ, positions[t])
+ * Source: MLA principle page, KV down-projection section (kv_a_proj_with_mqa) and
+ * the q_pe/k_pe rotation section; MLAfication page, "X → down_kv → c_kv, only it is
+ * cached"; Qwen3-30B delta page, variant "disrms" (read as RMSNorm on c).
+ *   x         device [n_tokens, d_model]
+ *   w_dkv     device [r, d_model];  w_kr device [G*d_rope, d_model]
+ *   positions device int32 [n_tokens] (>= 0)
+ *   slots     device int64 [n_tokens], each in [0, cache_rows); distinct
+ *   cache     device [cache_rows, r + G*d_rope] (written rows only)
+ *   workspace device, >= mla_workspace_size(dims, MLA_OP_WRITE_CACHE, 0, n_tokens, 0) bytes
+ * n_tokens == 0 is a no-op. */
+int mla_write_cache(const mla_dims* dims, const void* x, const void* w_dkv, const void* w_kr,
+                    const int32_t* positions, const int64_t* slots, int64_t n_tokens,
+                    void* cache, int64_t cache_rows, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Query side with W_UK absorption, for n_tokens query tokens.
+ *   q_nope[t,h] = x[t]·W_QC[h*d_nope : +d_nope]ᵀ
+ *   q_pe[t,h]   = RoPE(x[t]·W_QR[h*d_rope : +d_rope]ᵀ, positions[t])
+ *   q_lat[t,h,:] = Σ_d q_nope[t,h,d]·W_UK[h,d,:]
+ * Source: MLA principle page, split of q into q_nope/q_pe and section "矩阵吸收"
+ * (einsum 'hdc,bhqd->bhqc' of W_UK with q_nope); MLAfication page, q_c_proj / q_r_proj.
+ *   x device [n_tokens, d_model]; w_qc device [H*d_nope, d_model];
+ *   w_qr device [H*d_rope, d_model]; w_uk device [H, d_nope, r]
+ *   positions device int32 [n_tokens]
+ *   q_lat device out [n_tokens, H, r];  q_pe device out [n_tokens, H, d_rope]
+ *   workspace device, >= mla_workspace_size(dims, MLA_OP_ABSORB, 0, n_tokens, 0) bytes */
+int mla_absorb(const mla_dims* dims, const void* x, const void* w_qc, const void* w_qr,
+               const void* w_uk, const int32_t* positions, int64_t n_tokens, void* q_lat,
+               void* q_pe, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Batched decode: one query token per sequence, attending to all of its cached rows.
+ * For sequence b with n = seq_len[b] >= 1 rows starting at cache row seq_start[b]
+ * (the query's own row, at position n-1, is the last one):
+ *   s[h,l] = scale·(q_lat[b,h]·c[l] + q_pe[b,h]·kr[l, g(h)])
+ *   P = softmax_l(s);  o_[h,:] = Σ_l P[h,l]·c[l,:];  out[b,h,:] = W_UV[h]·o_[h,:]
+ * Source: MLA principle page, section "矩阵吸收" (absorbed score on compressed_kv,
+ * softmax_scale on the sum) and eqs. (4)-(5) (P·c first, then W_UV).
+ *   q_lat device [batch, H, r]; q_pe device [batch, H, d_rope]
+ *   cache device [*, r + G*d_rope]; seq_start device int64 [batch]; seq_len device int32 [batch]
+ *   max_len: host upper bound on seq_len (sizes the split of each context)
+ *   w_uv device [H, d_v, r];  out device out [batch, H, d_v]
+ *   workspace device, >= mla_workspace_size(dims, MLA_OP_DECODE, batch, 0, max_len) bytes
+ * batch == 0 is a no-op; seq_len[b] must be in [1, max_len]. */
+int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_pe, const void* cache,
+               const int64_t* seq_start, const int32_t* seq_len, int32_t batch, int32_t max_len,
+               const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/* Causal prefill over packed sequences.  Tokens cu_seqlens[b] .. cu_seqlens[b+1]-1
+ * form sequence b at positions 0..n_b-1; token t's own cache row is row t, and it
+ * attends to rows cu_seqlens[b] .. t (same formula as mla_decode per token).
+ * Source: as mla_decode, plus the causal SDPA of the nanowhale MLA page.
+ *   q_lat device [n_tokens, H, r]; q_pe device [n_tokens, H, d_rope]
+ *   cache device [>= n_tokens, r + G*d_rope]
+ *   cu_seqlens device int64 [batch+1], cu_seqlens[0] = 0, cu_seqlens[batch] = n_tokens
+ *   max_len: host upper bound on n_b
+ *   w_uv device [H, d_v, r];  out device out [n_tokens, H, d_v]
+ *   workspace device, >= mla_workspace_size(dims, MLA_OP_PREFILL, batch, n_tokens, max_len) */
+int mla_prefill(const mla_dims* dims, const void* q_lat, const void* q_pe, const void* cache,
+                const int64_t* cu_seqlens, int32_t batch, int64_t n_tokens, int32_t max_len,
+                const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* Human-readable text for a status code (static storage). */
+const char* mla_strerror(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

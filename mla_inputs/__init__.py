@@ -5,7 +5,7 @@ It holds only workload definitions (shapes, hyper-parameters) and seeded random
 number streams; it contains none of the attention arithmetic.
 
 Every tensor is drawn in float32 from
-``np.random.Generator(PCG64(SeedSequence([seed, tensor_id, *stream])))``
+``np.random.Generator(Philox(SeedSequence([seed, tensor_id, *stream])))``
 and, for bf16 workloads, rounded to bfloat16 with round-to-nearest-even, so the
 oracle (which upcasts the stored values exactly to float64) and the GPU (which
 receives the bf16 bit patterns) see identical values.
@@ -37,9 +37,11 @@ def rne_bf16_bits(a: np.ndarray) -> np.ndarray:
     """
     f = np.ascontiguousarray(a, dtype=np.float32)
     u = f.view(np.uint32)
-    lsb = (u >> np.uint32(16)) & np.uint32(1)
-    rounded = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
-    out = rounded.astype(np.uint16)
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += u
+    r += np.uint32(0x7FFF)
+    r >>= np.uint32(16)
+    out = r.astype(np.uint16)
     nan = np.isnan(f)
     if nan.any():
         out[nan] = np.uint16(0x7FC0)
@@ -165,7 +167,7 @@ def small_variant(cfg: MLAConfig, **changes) -> MLAConfig:
 
 def _rng(seed: int, tensor_id: int, *stream: int) -> np.random.Generator:
     ss = np.random.SeedSequence([int(seed), int(tensor_id), *[int(s) for s in stream]])
-    return np.random.Generator(np.random.PCG64(ss))
+    return np.random.Generator(np.random.Philox(ss))
 
 
 def draw_normal(seed: int, tensor_id: int, stream: Tuple[int, ...], shape, std: float,
@@ -191,11 +193,14 @@ def weights(cfg: MLAConfig) -> Dict[str, np.ndarray]:
     return out
 
 
-def x_rows(cfg: MLAConfig, seq: int, start: int, stop: int, scale: float = 1.0) -> np.ndarray:
+def x_rows(cfg: MLAConfig, seq: int, start: int, stop: int, scale: float = 1.0,
+           quantized: bool = True) -> np.ndarray:
     """Hidden states x ~ N(0, 1) for tokens [start, stop) of sequence ``seq``.
 
     Rows are drawn in independent blocks of X_BLOCK tokens, so any slice can be
-    regenerated without drawing the whole sequence.
+    regenerated without drawing the whole sequence.  ``quantized=False`` returns
+    the raw float32 draw; rounding it to bf16 with round-to-nearest-even (on the
+    host or on the device) gives exactly the quantized values.
     """
     if stop <= start:
         return np.zeros((0, cfg.d_model), np.float32)
@@ -207,10 +212,10 @@ def x_rows(cfg: MLAConfig, seq: int, start: int, stop: int, scale: float = 1.0) 
         lo = max(start, blk * X_BLOCK) - blk * X_BLOCK
         hi = min(stop, (blk + 1) * X_BLOCK) - blk * X_BLOCK
         parts.append(a[lo:hi])
-    a = np.concatenate(parts, axis=0)
+    a = parts[0] if len(parts) == 1 else np.concatenate(parts, axis=0)
     if scale != 1.0:
-        a *= np.float32(scale)
-    return quantize(a, cfg.dtype)
+        a = a * np.float32(scale)
+    return quantize(a, cfg.dtype) if quantized else np.ascontiguousarray(a)
 
 
 def context_lengths(cfg: MLAConfig) -> np.ndarray:

@@ -1,0 +1,147 @@
+"""Shared test/bench plumbing: seeded inputs to device tensors, the GPU chain through
+the C ABI, and the oracle on the same inputs.  Test infrastructure only."""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional
+
+import numpy as np
+
+import mla_inputs as I
+
+TOL = {"bf16": 1e-2, "f32": 1e-4}  # max relative error per (token, head), over d_v
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def to_dev(a: np.ndarray, dtype: str, device="cuda"):
+    """float32 array of representable values -> device tensor of the workload dtype."""
+    torch = torch_mod()
+    if dtype == "bf16":
+        bits = I.rne_bf16_bits(a).view(np.int16)
+        return torch.from_numpy(bits).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+
+
+def to_host(t) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def elem_dtype(cfg):
+    torch = torch_mod()
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+@dataclasses.dataclass
+class DeviceLayer:
+    cfg: I.MLAConfig
+    w_host: Dict[str, np.ndarray]
+    w_dev: Dict[str, object]
+    dims: object
+
+
+def make_layer(cfg: I.MLAConfig, device="cuda") -> DeviceLayer:
+    import head_latent_attention_kv_amd as M
+    w = I.weights(cfg)
+    return DeviceLayer(cfg, w, {k: to_dev(v, cfg.dtype, device) for k, v in w.items()}, M.dims_of(cfg))
+
+
+def write_cache(layer: DeviceLayer, x_dev, positions: np.ndarray, slots: np.ndarray, cache,
+                workspace=None):
+    import head_latent_attention_kv_amd as M
+    torch = torch_mod()
+    pos = torch.from_numpy(positions.astype(np.int32)).to(cache.device)
+    sl = torch.from_numpy(slots.astype(np.int64)).to(cache.device)
+    M.mla_write_cache(layer.dims, x_dev, layer.w_dev["w_dkv"], layer.w_dev["w_kr"], pos, sl, cache,
+                      workspace=workspace)
+
+
+def absorb(layer: DeviceLayer, x_dev, positions: np.ndarray):
+    import head_latent_attention_kv_amd as M
+    torch = torch_mod()
+    cfg = layer.cfg
+    T = x_dev.shape[0]
+    q_lat = torch.empty((T, cfg.n_heads, cfg.rank), dtype=elem_dtype(cfg), device=x_dev.device)
+    q_pe = torch.empty((T, cfg.n_heads, cfg.d_rope), dtype=elem_dtype(cfg), device=x_dev.device)
+    pos = torch.from_numpy(positions.astype(np.int32)).to(x_dev.device)
+    M.mla_absorb(layer.dims, x_dev, layer.w_dev["w_qc"], layer.w_dev["w_qr"], layer.w_dev["w_uk"],
+                 pos, q_lat, q_pe)
+    return q_lat, q_pe
+
+
+@dataclasses.dataclass
+class DecodeRun:
+    lengths: np.ndarray
+    starts: np.ndarray
+    cache: object
+    q_lat: object
+    q_pe: object
+    out: object
+    x_query: np.ndarray  # [B, d_model] float32 (representable values)
+
+
+def build_decode(layer: DeviceLayer, lengths: np.ndarray, x_scale: float = 1.0,
+                 chunk: int = 8192) -> DecodeRun:
+    """Fill a packed cache for sequences of the given lengths with mla_write_cache,
+    absorb each sequence's last token, run mla_decode."""
+    import head_latent_attention_kv_amd as M
+    torch = torch_mod()
+    cfg = layer.cfg
+    lengths = np.asarray(lengths, np.int64)
+    starts = np.concatenate([[0], np.cumsum(lengths)[:-1]]).astype(np.int64)
+    rows = int(lengths.sum())
+    cache = torch.empty((rows, cfg.row_width), dtype=elem_dtype(cfg), device="cuda")
+    ws = torch.empty(max(256, M.mla_workspace_size(layer.dims, M.MLA_OP_WRITE_CACHE, 0, chunk, 0)),
+                     dtype=torch.uint8, device="cuda")
+    xq = np.zeros((len(lengths), cfg.d_model), np.float32)
+    for b, n in enumerate(lengths):
+        for c0 in range(0, int(n), chunk):
+            c1 = min(int(n), c0 + chunk)
+            xb = I.x_rows(cfg, b, c0, c1, scale=x_scale)
+            if c1 == n:
+                xq[b] = xb[-1]
+            write_cache(layer, to_dev(xb, cfg.dtype), np.arange(c0, c1), starts[b] + np.arange(c0, c1),
+                        cache, workspace=ws)
+    q_lat, q_pe = absorb(layer, to_dev(xq, cfg.dtype), lengths - 1)
+    out = torch.empty((len(lengths), cfg.n_heads, cfg.d_v), dtype=elem_dtype(cfg), device="cuda")
+    seq_start = torch.from_numpy(starts).cuda()
+    seq_len = torch.from_numpy(lengths.astype(np.int32)).cuda()
+    M.mla_decode(layer.dims, q_lat, q_pe, cache, seq_start, seq_len, int(lengths.max()),
+                 layer.w_dev["w_uv"], out)
+    torch.cuda.synchronize()
+    return DecodeRun(lengths, starts, cache, q_lat, q_pe, out, xq)
+
+
+def oracle_decode_rows(cfg, w, x_keys: np.ndarray, x_query: np.ndarray, n: int,
+                       cache_rows: Optional[np.ndarray] = None, heads: Optional[List[int]] = None):
+    """Oracle output [H or len(heads), d_v] for one decode query at position n-1.
+    cache_rows given: attention parity on those (GPU-written) rows; else the oracle
+    builds its own rows from x_keys (chain parity)."""
+    from oracle import mla_oracle as O
+    pos = np.arange(n)
+    if cache_rows is None:
+        cache_rows = O.cache_rows(x_keys, w["w_dkv"], w["w_kr"], pos, n_groups=cfg.n_groups,
+                                  d_rope=cfg.d_rope, theta=cfg.rope_theta,
+                                  latent_rmsnorm=cfg.latent_rmsnorm, eps=cfg.rms_eps)
+    c, kr = O.split_rows(cache_rows, cfg.rank, cfg.n_groups, cfg.d_rope)
+    qn, qr = O.query(x_query[None], w["w_qc"], w["w_qr"], np.array([n - 1]), n_heads=cfg.n_heads,
+                     d_nope=cfg.d_nope, d_rope=cfg.d_rope, theta=cfg.rope_theta)
+    heads = list(range(cfg.n_heads)) if heads is None else list(heads)
+    g_of_h = O.head_groups(cfg.n_heads, cfg.n_groups)
+    out = []
+    for h in heads:
+        o = O.mla_attention(qn[:, h:h + 1], qr[:, h:h + 1], c, kr[:, g_of_h[h]:g_of_h[h] + 1],
+                            w["w_uk"][h:h + 1], w["w_uv"][h:h + 1], np.array([n - 1]), pos,
+                            np.zeros(1, int), np.zeros(n, int), cfg.softmax_scale)
+        out.append(o[0, 0])
+    return np.stack(out)
+
+
+def rel_err_rows(got: np.ndarray, ref: np.ndarray) -> float:
+    num = np.abs(got - ref).max(axis=-1)
+    den = np.abs(ref).max(axis=-1)
+    den = np.where(den == 0, 1.0, den)
+    return float((num / den).max())

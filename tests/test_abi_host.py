@@ -1,0 +1,101 @@
+"""Host-only checks of the C ABI: the header compiles as C and C++, the library
+loads and exports every function the header declares, and argument validation
+(which runs before any HIP call) returns the documented status codes."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mla_inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+def _lib():
+    from head_latent_attention_kv_amd import _abi
+    if not os.path.exists(_abi.LIB_PATH):
+        from head_latent_attention_kv_amd import build
+        build.build()
+    return _abi, _abi.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_header_compiles_as_c_and_cpp(tmp_path):
+    for lang, comp in (("c", "gcc"), ("c++", "g++")):
+        src = tmp_path / ("t." + ("c" if lang == "c" else "cpp"))
+        src.write_text('#include "mla.h"\nint main(void){ return (int)sizeof(mla_dims); }\n')
+        r = subprocess.run([comp, "-Wall", "-Werror", "-I", os.path.dirname(HEADER), "-c", str(src),
+                            "-o", str(tmp_path / "t.o")], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+
+
+def test_library_exports_every_declared_symbol():
+    abi, lib = _lib()
+    names = _declared()
+    assert {"mla_write_cache", "mla_absorb", "mla_decode", "mla_prefill"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in abi.SIGNATURES, n
+    assert lib.mla_version() >= 100
+    assert ctypes.sizeof(abi.MlaDims) == 56
+
+
+def test_dims_validation_codes():
+    abi, lib = _lib()
+    for cfg in I.CONFIGS.values():
+        assert lib.mla_check_dims(ctypes.byref(abi.dims_of(cfg))) == abi.MLA_OK, cfg.name
+    base = dict(d_model=256, n_heads=8, n_groups=2, rank=64, d_rope=16, d_nope=32, d_v=32, dtype="bf16")
+    cases = [
+        (dict(n_groups=3), abi.MLA_EINVAL),       # H % G != 0
+        (dict(d_rope=15), abi.MLA_EINVAL),        # odd rotary width
+        (dict(d_model=0), abi.MLA_EINVAL),
+        (dict(dtype=7), abi.MLA_EINVAL),
+        (dict(rank=1024), abi.MLA_ENOTSUP),       # above the kernels' latent limit
+        (dict(rank=40), abi.MLA_ENOTSUP),         # not a multiple of 16
+        (dict(d_model=260), abi.MLA_ENOTSUP),     # bf16 rows must be 16-byte multiples
+        (dict(softmax_scale=float("nan")), abi.MLA_EINVAL),
+        (dict(rope_theta=-1.0), abi.MLA_EINVAL),
+    ]
+    for change, want in cases:
+        d = abi.make_dims(**{**base, **change})
+        assert lib.mla_check_dims(ctypes.byref(d)) == want, change
+        assert lib.mla_workspace_size(ctypes.byref(d), abi.MLA_OP_DECODE, 4, 0, 100) == 0
+
+
+def test_calls_reject_bad_arguments_before_any_launch():
+    abi, lib = _lib()
+    d = abi.dims_of(I.CONFIGS["deepseek_v2_decode"])
+    null = None
+    # null pointers
+    assert lib.mla_decode(ctypes.byref(d), null, null, null, null, null, 4, 100, null, null, null, 0, null) == abi.MLA_EINVAL
+    assert lib.mla_prefill(ctypes.byref(d), null, null, null, null, 1, 10, 10, null, null, null, 0, null) == abi.MLA_EINVAL
+    assert lib.mla_write_cache(ctypes.byref(d), null, null, null, null, null, 3, null, 3, null, 0, null) == abi.MLA_EINVAL
+    assert lib.mla_absorb(ctypes.byref(d), null, null, null, null, null, 3, null, null, null, 0, null) == abi.MLA_EINVAL
+    # misaligned (never dereferenced: validation fails first)
+    odd = 0x1001
+    assert lib.mla_decode(ctypes.byref(d), odd, odd, odd, odd, odd, 4, 100, odd, odd, odd, 1 << 30, null) == abi.MLA_EINVAL
+    # negative sizes, empty calls
+    assert lib.mla_decode(ctypes.byref(d), null, null, null, null, null, -1, 100, null, null, null, 0, null) == abi.MLA_EINVAL
+    assert lib.mla_decode(ctypes.byref(d), null, null, null, null, null, 0, 100, null, null, null, 0, null) == abi.MLA_OK
+    assert lib.mla_write_cache(ctypes.byref(d), null, null, null, null, null, 0, null, 0, null, 0, null) == abi.MLA_OK
+    assert lib.mla_decode(None, null, null, null, null, null, 4, 100, null, null, null, 0, null) == abi.MLA_EINVAL
+    assert lib.mla_strerror(abi.MLA_EWORKSPACE) == b"workspace too small"
+
+
+def test_workspace_sizes_cover_the_plan():
+    abi, lib = _lib()
+    d = abi.dims_of(I.CONFIGS["deepseek_v2_decode"])
+    B, L = 64, 8192
+    ws = lib.mla_workspace_size(ctypes.byref(d), abi.MLA_OP_DECODE, B, 0, L)
+    assert ws >= B * 128 * 512 * 4  # at least the merged latent outputs
+    assert lib.mla_workspace_size(ctypes.byref(d), abi.MLA_OP_WRITE_CACHE, 0, 1000, 0) >= 1000 * 576 * 4
+    assert lib.mla_workspace_size(ctypes.byref(d), abi.MLA_OP_ABSORB, 0, 64, 0) >= 64 * 128 * 192 * 4
+    assert lib.mla_workspace_size(ctypes.byref(d), 99, 1, 1, 1) == 0

@@ -1,0 +1,194 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle on the same
+seeded inputs.  Tolerance: max over (token, head) of ‖gpu − oracle‖∞ / ‖oracle‖∞
+over the d_v outputs <= 1e-2 for bf16 workloads and 1e-4 for the fp32 one.
+
+Three levels for decode workloads: (i) cache rows written by mla_write_cache vs
+the oracle's rows; (ii) attention on the GPU-written cache (oracle reads the same
+rows); (iii) the whole chain from x."""
+import numpy as np
+import pytest
+
+import mla_inputs as I
+from tests import harness as Hh
+
+pytestmark = pytest.mark.gpu
+
+
+def _print_case(name, **kw):
+    print(f"[case] {name} {kw}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch
+    import head_latent_attention_kv_amd as M
+    M.load()
+    assert torch.cuda.is_available()
+    return torch
+
+
+# ----------------------------------------------------------------------------
+# fp32 tiny layer: prefill 256 then 16 decode steps, full size
+# ----------------------------------------------------------------------------
+
+
+def test_tiny_f32_prefill_then_decode(torch):
+    import head_latent_attention_kv_amd as M
+    from oracle import mla_oracle as O
+    cfg = I.CONFIGS["tiny_f32"]
+    _print_case("tiny_f32", L=cfg.prefill_len, steps=cfg.decode_steps)
+    layer = Hh.make_layer(cfg)
+    n_all = cfg.prefill_len + cfg.decode_steps
+    x = I.x_rows(cfg, 0, 0, n_all)
+    cache = torch.zeros((n_all, cfg.row_width), dtype=torch.float32, device="cuda")
+    # prefill
+    L = cfg.prefill_len
+    xd = Hh.to_dev(x[:L], cfg.dtype)
+    Hh.write_cache(layer, xd, np.arange(L), np.arange(L), cache)
+    q_lat, q_pe = Hh.absorb(layer, xd, np.arange(L))
+    out_pre = torch.empty((L, cfg.n_heads, cfg.d_v), dtype=torch.float32, device="cuda")
+    cu = torch.tensor([0, L], dtype=torch.int64, device="cuda")
+    M.mla_prefill(layer.dims, q_lat, q_pe, cache, cu, L, layer.w_dev["w_uv"], out_pre)
+    # decode steps: write the new row, then attend over all rows so far
+    outs = []
+    for i in range(cfg.decode_steps):
+        p = L + i
+        xi = Hh.to_dev(x[p:p + 1], cfg.dtype)
+        Hh.write_cache(layer, xi, np.array([p]), np.array([p]), cache)
+        ql, qp = Hh.absorb(layer, xi, np.array([p]))
+        o = torch.empty((1, cfg.n_heads, cfg.d_v), dtype=torch.float32, device="cuda")
+        M.mla_decode(layer.dims, ql, qp, cache, torch.zeros(1, dtype=torch.int64, device="cuda"),
+                     torch.tensor([p + 1], dtype=torch.int32, device="cuda"), p + 1,
+                     layer.w_dev["w_uv"], o)
+        outs.append(o)
+    torch.cuda.synchronize()
+    got = np.concatenate([Hh.to_host(out_pre)] + [Hh.to_host(o) for o in outs])
+    pos = np.arange(n_all)
+    ref = O.mla_layer(x, x, layer.w_host, k_pos=pos, q_pos=pos, k_seg=np.zeros(n_all, int),
+                      q_seg=np.zeros(n_all, int), n_heads=cfg.n_heads, n_groups=cfg.n_groups,
+                      d_nope=cfg.d_nope, d_rope=cfg.d_rope, theta=cfg.rope_theta,
+                      scale=cfg.softmax_scale)
+    err = Hh.rel_err_rows(got, ref)
+    print(f"tiny_f32 chain max rel err {err:.3e}")
+    assert err <= Hh.TOL["f32"]
+    # cache rows (i)
+    rows_ref = O.cache_rows(x, layer.w_host["w_dkv"], layer.w_host["w_kr"], pos, n_groups=cfg.n_groups,
+                            d_rope=cfg.d_rope, theta=cfg.rope_theta)
+    assert Hh.rel_err_rows(Hh.to_host(cache), rows_ref) <= 1e-5
+
+
+# ----------------------------------------------------------------------------
+# bf16 decode workloads at their full layer dims, reduced batch / lengths
+# ----------------------------------------------------------------------------
+
+DECODE_CASES = [
+    ("qwen25_7b_decode", [1, 65, 511, 1000]),
+    ("deepseek_v2_decode", [1, 300, 2048]),
+    ("qwen3_30b_ragged_decode", [1024, 1537]),
+]
+
+
+@pytest.mark.parametrize("name,lengths", DECODE_CASES)
+def test_decode_reduced(torch, name, lengths):
+    from oracle import mla_oracle as O
+    cfg = I.CONFIGS[name]
+    _print_case("decode_reduced", cfg=name, lengths=lengths)
+    layer = Hh.make_layer(cfg)
+    run = Hh.build_decode(layer, np.array(lengths))
+    got = Hh.to_host(run.out)
+    cache_h = Hh.to_host(run.cache)
+    w = layer.w_host
+    errs = {"write": 0.0, "attn": 0.0, "chain": 0.0, "q_lat": 0.0, "q_pe": 0.0}
+    for b, n in enumerate(run.lengths):
+        n = int(n)
+        xb = I.x_rows(cfg, b, 0, n)
+        rows_ref = O.cache_rows(xb, w["w_dkv"], w["w_kr"], np.arange(n), n_groups=cfg.n_groups,
+                                d_rope=cfg.d_rope, theta=cfg.rope_theta,
+                                latent_rmsnorm=cfg.latent_rmsnorm, eps=cfg.rms_eps)
+        rows_gpu = cache_h[run.starts[b]:run.starts[b] + n]
+        errs["write"] = max(errs["write"], Hh.rel_err_rows(rows_gpu[:, :cfg.rank], rows_ref[:, :cfg.rank]))
+        attn = Hh.oracle_decode_rows(cfg, w, None, run.x_query[b], n, cache_rows=rows_gpu)
+        chain = Hh.oracle_decode_rows(cfg, w, xb, run.x_query[b], n, cache_rows=rows_ref)
+        errs["attn"] = max(errs["attn"], Hh.rel_err_rows(got[b], attn))
+        errs["chain"] = max(errs["chain"], Hh.rel_err_rows(got[b], chain))
+        qn, qr = O.query(run.x_query[b:b + 1], w["w_qc"], w["w_qr"], np.array([n - 1]),
+                         n_heads=cfg.n_heads, d_nope=cfg.d_nope, d_rope=cfg.d_rope, theta=cfg.rope_theta)
+        errs["q_lat"] = max(errs["q_lat"], Hh.rel_err_rows(Hh.to_host(run.q_lat[b]), O.absorbed_query(qn, w["w_uk"])[0]))
+        errs["q_pe"] = max(errs["q_pe"], Hh.rel_err_rows(Hh.to_host(run.q_pe[b]), qr[0]))
+    print(f"{name} {lengths}: " + " ".join(f"{k}={v:.3e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= Hh.TOL[cfg.dtype], (k, v)
+
+
+def test_decode_deterministic(torch):
+    cfg = I.small_variant(I.CONFIGS["deepseek_v2_decode"], d_model=512)
+    _print_case("decode_deterministic")
+    layer = Hh.make_layer(cfg)
+    a = Hh.build_decode(layer, np.array([777, 3000, 64]))
+    b = Hh.build_decode(layer, np.array([777, 3000, 64]))
+    assert torch.equal(a.out, b.out) and torch.equal(a.cache, b.cache)
+
+
+# ----------------------------------------------------------------------------
+# prefill (bf16) at the long-prefill layer dims, reduced length, ragged batch
+# ----------------------------------------------------------------------------
+
+
+def test_prefill_reduced_ragged(torch):
+    import head_latent_attention_kv_amd as M
+    from oracle import mla_oracle as O
+    cfg = I.CONFIGS["long_prefill_131k"]
+    lengths = [700, 1, 333]
+    _print_case("prefill_reduced", lengths=lengths)
+    layer = Hh.make_layer(cfg)
+    T = sum(lengths)
+    xs = [I.x_rows(cfg, b, 0, n) for b, n in enumerate(lengths)]
+    x = np.concatenate(xs)
+    pos = np.concatenate([np.arange(n) for n in lengths])
+    seg = np.concatenate([np.full(n, b) for b, n in enumerate(lengths)])
+    cache = torch.empty((T, cfg.row_width), dtype=torch.bfloat16, device="cuda")
+    xd = Hh.to_dev(x, cfg.dtype)
+    Hh.write_cache(layer, xd, pos, np.arange(T), cache)
+    q_lat, q_pe = Hh.absorb(layer, xd, pos)
+    out = torch.empty((T, cfg.n_heads, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int64, device="cuda")
+    M.mla_prefill(layer.dims, q_lat, q_pe, cache, cu, max(lengths), layer.w_dev["w_uv"], out)
+    torch.cuda.synchronize()
+    got = Hh.to_host(out)
+    w = layer.w_host
+    ref = O.mla_layer(x, x, w, k_pos=pos, q_pos=pos, k_seg=seg, q_seg=seg, n_heads=cfg.n_heads,
+                      n_groups=cfg.n_groups, d_nope=cfg.d_nope, d_rope=cfg.d_rope,
+                      theta=cfg.rope_theta, scale=cfg.softmax_scale, head_chunk=4)
+    err = Hh.rel_err_rows(got, ref)
+    print(f"prefill ragged {lengths}: chain max rel err {err:.3e}")
+    assert err <= Hh.TOL["bf16"]
+
+
+# ----------------------------------------------------------------------------
+# ABI behaviour on the device
+# ----------------------------------------------------------------------------
+
+
+def test_abi_errors_leave_outputs_untouched(torch):
+    import head_latent_attention_kv_amd as M
+    cfg = I.small_variant(I.CONFIGS["deepseek_v2_decode"], d_model=256)
+    layer = Hh.make_layer(cfg)
+    B, L = 2, 100
+    q_lat = torch.zeros((B, cfg.n_heads, cfg.rank), dtype=torch.bfloat16, device="cuda")
+    q_pe = torch.zeros((B, cfg.n_heads, cfg.d_rope), dtype=torch.bfloat16, device="cuda")
+    cache = torch.zeros((B * L, cfg.row_width), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((B, cfg.n_heads, cfg.d_v), 7.0, dtype=torch.bfloat16, device="cuda")
+    ss = torch.tensor([0, L], dtype=torch.int64, device="cuda")
+    sl = torch.tensor([L, L], dtype=torch.int32, device="cuda")
+    need = M.mla_workspace_size(layer.dims, M.MLA_OP_DECODE, B, 0, L)
+    small = torch.empty(max(0, need - 256), dtype=torch.uint8, device="cuda")
+    with pytest.raises(M.MlaError) as e:
+        M.mla_decode(layer.dims, q_lat, q_pe, cache, ss, sl, L, layer.w_dev["w_uv"], out, workspace=small)
+    assert e.value.status == M.MLA_EWORKSPACE
+    bad = M.make_dims(d_model=256, n_heads=128, n_groups=3, rank=512, d_rope=64, d_nope=128, d_v=128,
+                      dtype="bf16")
+    with pytest.raises(M.MlaError) as e:
+        M.mla_decode(bad, q_lat, q_pe, cache, ss, sl, L, layer.w_dev["w_uv"], out)
+    assert e.value.status == M.MLA_EINVAL
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
