@@ -17,6 +17,7 @@ using mla::GemmArgs;
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxRank = 512;
+constexpr int kCUs = 256;  // compute units of an MI355X (sizes the split of decode contexts)
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -74,13 +75,16 @@ DecodePlan decode_plan(const mla_dims* d, int32_t batch, int32_t max_len) {
   p.mfma = d->dtype == MLA_BF16 && mla::decode_mfma_supported(sh);
   const int64_t B = std::max<int32_t>(batch, 0);
   const int L = std::max<int32_t>(max_len, 1);
-  // blocks per split: the generic kernel splits heads into blocks, the MFMA
-  // kernel keeps all heads of a sequence in one block.
-  const int64_t per_split = p.mfma ? B : B * ((sh.H + mla::generic_head_block() - 1) / mla::generic_head_block());
-  // aim for ~2 blocks per compute unit (256 CUs) and >= 256 rows per split
-  const int64_t target = 512;
+  // Workgroups per split: the MFMA kernel keeps all heads of a sequence in one
+  // workgroup; the generic kernel splits heads into blocks.
+  const int64_t per_split =
+      p.mfma ? B : B * ((sh.H + mla::generic_head_block() - 1) / mla::generic_head_block());
+  // Fill the 256 compute units of an MI355X once (the MFMA kernel's LDS
+  // footprint allows one workgroup per CU at the large shapes), keeping
+  // splits >= 256 rows.
+  const int64_t target = p.mfma ? mla::decode_mfma_blocks_per_cu(sh) * kCUs : 2 * kCUs;
   int64_t ns = per_split > 0 ? (target + per_split - 1) / per_split : 1;
-  const int64_t max_ns = std::max<int64_t>(1, (L + 255) / 256);
+  const int64_t max_ns = std::max<int64_t>(1, L / 256);
   ns = std::max<int64_t>(1, std::min<int64_t>(ns, max_ns));
   int split_len = static_cast<int>((L + ns - 1) / ns);
   split_len = (split_len + 63) / 64 * 64;

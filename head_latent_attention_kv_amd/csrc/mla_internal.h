@@ -59,6 +59,7 @@ void merge_splits(const AttnShape& sh, int64_t n_q, int n_split, const float* pa
 
 // bf16 MFMA decode kernel for the shapes it supports (see decode_mfma.hip).
 bool decode_mfma_supported(const AttnShape& sh);
+int decode_mfma_blocks_per_cu(const AttnShape& sh);  // workgroups one CU holds (LDS-limited)
 void decode_mfma(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
                  const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split,
                  int split_len, float* part_o, float* part_ml, float* o_out, hipStream_t s);

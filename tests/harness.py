@@ -83,10 +83,20 @@ class DecodeRun:
     x_query: np.ndarray  # [B, d_model] float32 (representable values)
 
 
+def raw_to_dev(a: np.ndarray, dtype: str, device="cuda"):
+    """Unrounded float32 draw -> device tensor; bf16 rounding (RNE) happens on the
+    device and gives the same values as mla_inputs.quantize on the host."""
+    torch = torch_mod()
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
 def build_decode(layer: DeviceLayer, lengths: np.ndarray, x_scale: float = 1.0,
-                 chunk: int = 8192) -> DecodeRun:
+                 chunk: int = 8192, threads: int = 8) -> DecodeRun:
     """Fill a packed cache for sequences of the given lengths with mla_write_cache,
     absorb each sequence's last token, run mla_decode."""
+    import concurrent.futures as cf
+
     import head_latent_attention_kv_amd as M
     torch = torch_mod()
     cfg = layer.cfg
@@ -97,14 +107,18 @@ def build_decode(layer: DeviceLayer, lengths: np.ndarray, x_scale: float = 1.0,
     ws = torch.empty(max(256, M.mla_workspace_size(layer.dims, M.MLA_OP_WRITE_CACHE, 0, chunk, 0)),
                      dtype=torch.uint8, device="cuda")
     xq = np.zeros((len(lengths), cfg.d_model), np.float32)
-    for b, n in enumerate(lengths):
-        for c0 in range(0, int(n), chunk):
-            c1 = min(int(n), c0 + chunk)
-            xb = I.x_rows(cfg, b, c0, c1, scale=x_scale)
-            if c1 == n:
-                xq[b] = xb[-1]
-            write_cache(layer, to_dev(xb, cfg.dtype), np.arange(c0, c1), starts[b] + np.arange(c0, c1),
-                        cache, workspace=ws)
+    jobs = [(b, c0, min(int(n), c0 + chunk)) for b, n in enumerate(lengths) for c0 in range(0, int(n), chunk)]
+
+    def gen(job):
+        b, c0, c1 = job
+        return job, I.x_rows(cfg, b, c0, c1, scale=x_scale, quantized=False)
+
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        for (b, c0, c1), xb in ex.map(gen, jobs):
+            if c1 == lengths[b]:
+                xq[b] = I.quantize(xb[-1:], cfg.dtype)[0]
+            write_cache(layer, raw_to_dev(xb, cfg.dtype), np.arange(c0, c1),
+                        starts[b] + np.arange(c0, c1), cache, workspace=ws)
     q_lat, q_pe = absorb(layer, to_dev(xq, cfg.dtype), lengths - 1)
     out = torch.empty((len(lengths), cfg.n_heads, cfg.d_v), dtype=elem_dtype(cfg), device="cuda")
     seq_start = torch.from_numpy(starts).cuda()

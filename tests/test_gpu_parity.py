@@ -192,3 +192,43 @@ def test_abi_errors_leave_outputs_untouched(torch):
     assert e.value.status == M.MLA_EINVAL
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
+
+
+# ----------------------------------------------------------------------------
+# full workload sizes, the launch configuration the benchmark times:
+# sampled (sequence, head) outputs against the oracle, all outputs finite
+# ----------------------------------------------------------------------------
+
+FULL_DECODE = [
+    # name, sampled sequences, sampled heads per sequence, sequences also checked end to end
+    ("qwen25_7b_decode", [0, 13, 31], None, [13]),
+    ("deepseek_v2_decode", [0, 21, 42, 63], [0, 37, 64, 127], [42]),
+    ("qwen3_30b_ragged_decode", list(range(8)), [0, 9, 31], [int(np.argmax(I.context_lengths(I.CONFIGS["qwen3_30b_ragged_decode"])))]),
+]
+
+
+@pytest.mark.parametrize("name,seqs,heads,chain_seqs", FULL_DECODE)
+def test_decode_full_size_sampled(torch, name, seqs, heads, chain_seqs):
+    from oracle import mla_oracle as O
+    cfg = I.CONFIGS[name]
+    lengths = I.context_lengths(cfg)
+    _print_case("decode_full", cfg=name, batch=len(lengths), max_len=int(lengths.max()))
+    layer = Hh.make_layer(cfg)
+    run = Hh.build_decode(layer, lengths)
+    assert bool(torch.isfinite(run.out.float()).all())
+    got = Hh.to_host(run.out)
+    w = layer.w_host
+    worst = {"attn": 0.0, "chain": 0.0}
+    hs = list(range(cfg.n_heads)) if heads is None else heads
+    for b in seqs:
+        n = int(lengths[b])
+        rows_gpu = Hh.to_host(run.cache[int(run.starts[b]):int(run.starts[b]) + n])
+        ref = Hh.oracle_decode_rows(cfg, w, None, run.x_query[b], n, cache_rows=rows_gpu, heads=hs)
+        worst["attn"] = max(worst["attn"], Hh.rel_err_rows(got[b, hs], ref))
+        if b in chain_seqs:
+            xb = I.x_rows(cfg, b, 0, n)
+            ref_c = Hh.oracle_decode_rows(cfg, w, xb, run.x_query[b], n, heads=hs)
+            worst["chain"] = max(worst["chain"], Hh.rel_err_rows(got[b, hs], ref_c))
+    print(f"{name} full size: " + " ".join(f"{k}={v:.3e}" for k, v in worst.items()))
+    for k, v in worst.items():
+        assert v <= Hh.TOL[cfg.dtype], (k, v)
