@@ -1,22 +1,30 @@
-// bf16 MFMA decode over the latent cache: one query token per sequence, all
-// heads of that sequence in one workgroup, so every cache row is read from HBM
-// once and used by all heads (the property that makes MLA decode cheap: the
-// absorbed score q_lat·c + q_pe·kr and the latent-space P·c both read only the
-// cached [c ; kr] rows).
+// bf16 MFMA decode over the latent cache: one query token per sequence.
 //
-// Workgroup = 8 wave64s, one (sequence, split of its rows).  Per 32-row tile:
+// The heads of a sequence share every cache row (the absorbed score
+// q_lat·c + q_pe·kr and the latent-space P·c both read only the cached [c ; kr]
+// rows), so a workgroup takes a block of heads of one sequence and streams the
+// rows of one split of its context through LDS once for all of them.  When the
+// heads are split over several workgroups (NHH > 1) those workgroups are placed
+// on the same XCD (workgroups are dealt to the 8 XCDs round-robin) so the
+// second read of a tile is served by that XCD's L2.
+//
+// Workgroup = 8 wave64s.  Per 32-row tile (software-pipelined: the iteration
+// that accumulates tile t also scores tile t+1, one barrier per tile):
 //  1. the tile is copied HBM -> LDS with global_load_lds_dwordx4 (no register
-//     staging), three tiles in flight;
-//  2. score: wave w < H/16 computes Sᵀ[32 rows x 16 heads] = C·Qᵀ with
-//     v_mfma_f32_16x16x32_bf16; C (the cache tile) is the A operand read from
-//     LDS, Qᵀ the B operand held in registers (q_lat and the group's q_pe,
-//     zero elsewhere, so one K loop covers the whole cache row);
-//  3. online softmax per head in registers (base 2, max/sum across the four
-//     lane groups that hold a head), P written to LDS as bf16, the rescale
-//     factor of each head to LDS;
-//  4. PV: wave w owns latent columns [w·R/8, (w+1)·R/8) for every head;
-//     O += P·C with P (A operand) from LDS and C (B operand) read transposed
-//     from the same tile with ds_read_b64_tr_b16.
+//     staging), STAGES-2 tiles in flight beyond the two being used;
+//  2. score: wave w (< 2·NHB) computes Sᵀ[16 rows x 16 heads] = C·Qᵀ for head
+//     block w % NHB and row block w / NHB with v_mfma_f32_16x16x32_bf16; C (the
+//     tile) is the A operand read from LDS, fetched a few k-steps ahead; Qᵀ is
+//     the B operand held in registers (q_lat and the group's q_pe, zero
+//     elsewhere, so one K loop covers the whole cache row);
+//  3. softmax in registers against a per-split reference max (base 2): the
+//     first tile's max, with 2^64 of headroom; a split whose later scores
+//     exceed that finishes as a max-only scan and is redone with its true max,
+//     so the accumulators are never rescaled; row sums stay per lane until the
+//     end; P is written to LDS as bf16 (double-buffered);
+//  4. PV: wave w owns latent columns [w·R/8, (w+1)·R/8) for all heads of the
+//     workgroup; O += P·C with P (A operand) from LDS and C (B operand) read
+//     transposed from the same tile with ds_read_b64_tr_b16.
 // Output: normalised o_ (one split) or (m, l, unnormalised o_) partials.
 #include <math.h>
 
@@ -29,39 +37,51 @@ namespace mla {
 
 namespace {
 
+constexpr int kTL = 32;          // cache rows per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kTL = 32;      // cache rows per tile
-constexpr int kStages = 3;   // tiles in flight
-constexpr int kPP = 80;      // LDS bytes per head row of P (32 bf16 + pad: conflict-free reads)
+constexpr int kPP = 80;          // LDS bytes per head row of P (32 bf16 + pad: conflict-free reads)
+constexpr int kPF = 3;           // score k-steps fetched ahead
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSlack = 64.f;   // base-2 headroom above the softmax reference (P <= 2^64)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-template <int R, int RW, int NHB>
+// R: latent width; RW: cache row width; NHB: 16-head blocks per workgroup;
+// NHH: workgroups sharing one (sequence, split); STAGES: LDS tile buffers.
+template <int R, int RW, int NHB, int NHH, int STAGES>
 struct Shape {
+  static constexpr int kUnits = 2 * NHB;                        // (head block, row block) per tile
+  static_assert(kUnits <= kWaves, "one score unit per wave at most");
   static_assert(R % (16 * kWaves) == 0, "latent width must split into 16-column blocks per wave");
   static_assert(RW % 32 == 0, "row width must be a multiple of 32");
-  static constexpr int kSteps = RW / 32;                         // score k-steps
-  static constexpr int kPitch = (((RW * 2 + 31) / 32) | 1) * 32;  // LDS row bytes: odd multiple of 32
+  static constexpr int kHeads = NHB * 16;
+  static constexpr int kSteps = RW / 32;                        // score k-steps
+  // LDS row bytes: an odd multiple of 16, so the 16 rows one score read touches
+  // start in 16 distinct 4-bank groups
+  static constexpr int kPitch = ((RW * 2 / 16) | 1) * 16;
   static constexpr int kTileBytes = kTL * kPitch;
-  static constexpr int kChunks = (kTileBytes + 1023) / 1024;     // 1 KB direct-load chunks per tile
-  static constexpr int kCPW = (kChunks + kWaves - 1) / kWaves;   // chunks per wave (padded)
-  static constexpr int kNC = R / kWaves;                         // PV columns per wave
+  static constexpr int kChunks = (kTileBytes + 1023) / 1024;    // 1 KB direct-load chunks per tile
+  static constexpr int kCPW = (kChunks + kWaves - 1) / kWaves;  // chunks per wave (padded)
+  static constexpr int kBufBytes = kChunks * 1024;
+  static constexpr int kNC = R / kWaves;                        // PV columns per wave
   static constexpr int kNB = kNC / 16;
-  static constexpr int kLdsBytes = kStages * ((kTileBytes + 1023) / 1024) * 1024 + NHB * 16 * kPP +
-                                   NHB * 16 * 4 + NHB * 16 * 8;
+  static constexpr int kPBytes = kHeads * kPP;                  // one P buffer
+  static constexpr int kRedBytes = 2 * kHeads * 4 + 2 * kWaves * 4;  // exchange array + flags
+  static constexpr int kLdsBytes = STAGES * kBufBytes + 2 * kPBytes + kRedBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+  static_assert(STAGES >= 3 && STAGES <= 4, "tiles t, t+1 resident and 1-2 copies in flight");
+  static_assert(2 * kCPW < 64, "vmcnt range");
 };
 
-// s_waitcnt with vmcnt = N (expcnt, lgkmcnt left at their maximum), gfx9 encoding.
+// s_waitcnt with vmcnt = N (expcnt, lgkmcnt left at their maximum), gfx9
+// encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0xF70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0xF70);
 }
 
 // 16 bytes per lane, global -> LDS (global_load_lds_dwordx4): lane i's bytes land
@@ -69,13 +89,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 // every later LDS read as aliasing the in-flight copy (which makes it wait for
 // all outstanding loads, prefetches included); the kernel waits with explicit
 // vmcnt counts instead.  No register is written, so nothing is live in flight.
-__device__ __forceinline__ void global_to_lds16(const void* gptr, uint32_t lds_base) {
+__device__ __forceinline__ void global_to_lds16(const void* sbase, uint32_t voff, uint32_t lds_base) {
   __asm__ __volatile__(
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
+      "global_load_lds_dwordx4 %0, %1"
       :
-      : "v"(gptr), "s"(lds_base)
+      : "v"(voff), "s"(sbase), "s"(lds_base)
       : "memory", "m0");
 }
 
@@ -88,72 +108,100 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ __volatile__("" ::: "memory");
 }
 
-template <int R, int RW, int NHB>
+__device__ __forceinline__ bf16x8 lds_frag(const unsigned char* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+template <int R, int RW, int NHB, int NHH, int STAGES>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
     const bf16_t* __restrict__ q_lat, const bf16_t* __restrict__ q_pe,
     const bf16_t* __restrict__ cache, const int64_t* __restrict__ seq_start,
-    const int32_t* __restrict__ seq_len, int H, int G, int d_rope, float scale, int n_split,
-    int split_len, float* __restrict__ part_o, float* __restrict__ part_ml,
+    const int32_t* __restrict__ seq_len, int batch, int H, int G, int d_rope, float scale,
+    int n_split, int split_len, float* __restrict__ part_o, float* __restrict__ part_ml,
     float* __restrict__ o_out) {
-  using S = Shape<R, RW, NHB>;
+  using S = Shape<R, RW, NHB, NHH, STAGES>;
+  constexpr int kBufBytes = S::kBufBytes;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  constexpr int kBufBytes = S::kChunks * 1024;
-  unsigned char* pbuf = smem + kStages * kBufBytes;               // P: [NHB*16 heads][kPP bytes]
-  float* alpha_lds = reinterpret_cast<float*>(pbuf + NHB * 16 * kPP);  // [NHB*16]
-  float* ml_lds = alpha_lds + NHB * 16;                             // [NHB*16][2]
+  unsigned char* pbuf = smem + STAGES * kBufBytes;                        // P [2][kHeads][kPP]
+  float* xch = reinterpret_cast<float*>(pbuf + 2 * S::kPBytes);           // [2][kHeads]
+  int* flag_lds = reinterpret_cast<int*>(xch + 2 * S::kHeads);            // [2][kWaves]
+
+  // ---- which (sequence, split, head group) this workgroup computes
+  int pair, hh;
+  if (NHH == 1) {
+    pair = blockIdx.x;
+    hh = 0;
+  } else {
+    // the NHH workgroups of a pair are 8 apart: same XCD, dispatched together
+    const int q = blockIdx.x / (8 * NHH), rem = blockIdx.x % (8 * NHH);
+    hh = rem / 8;
+    pair = q * 8 + rem % 8;
+  }
+  if (pair >= batch * n_split) return;
+  const int split = pair % n_split;
+  const int b = pair / n_split;
+  const int head0 = hh * S::kHeads;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
 
-  const int split = blockIdx.x % n_split;
-  const int b = blockIdx.x / n_split;
   const int64_t row0 = seq_start[b];
   const int len = seq_len[b];
   const int l_begin = split * split_len;
   const int l_end = min(len, l_begin + split_len);
   const int n_tiles = l_end > l_begin ? (l_end - l_begin + kTL - 1) / kTL : 0;
-
   const char* cache_b = reinterpret_cast<const char*>(cache + row0 * RW);
 
   // ---- tile loader: chunk j of the padded tile image -> LDS [j*1 KB + lane*16]
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)smem));
   auto issue_tile = [&](int t) {
     const int tile_row = l_begin + t * kTL;
-    const uint32_t dst_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)smem)) +
-                              (t % kStages) * kBufBytes;
+    const int valid = min(kTL, l_end - tile_row);
+    const char* tbase = cache_b + static_cast<int64_t>(tile_row) * (RW * 2);
+    const uint32_t dst = lds0 + (t % STAGES) * kBufBytes;
 #pragma unroll
     for (int i = 0; i < S::kCPW; ++i) {
-      int j = wave + kWaves * i;
-      if (j >= S::kChunks) j = S::kChunks - 1;  // duplicate of the last chunk: same bytes, benign
+      const int j = min(wave + kWaves * i, S::kChunks - 1);  // duplicates of the last chunk are benign
       const int off = j * 1024 + lane * 16;
-      const int r = off / S::kPitch;
-      int cb = off - r * S::kPitch;
-      int row = tile_row + r;
-      if (row >= l_end || r >= kTL) row = l_end - 1;   // masked rows / tail: read a valid row
-      if (cb >= RW * 2) cb = 0;                        // pad bytes: any valid 16 B
-      const char* src = cache_b + static_cast<uint32_t>(row * (RW * 2) + cb);
-      global_to_lds16(src, __builtin_amdgcn_readfirstlane(dst_base + j * 1024));
+      const int r = off / S::kPitch;          // tile row this lane's 16 bytes belong to
+      int cb = off - r * S::kPitch;           // byte within the padded LDS row
+      if (cb >= RW * 2) cb = 0;               // pad bytes: any valid 16 B of the row
+      // rows past the sequence (last tile) or past the tile read the last valid row
+      const uint32_t voff = r < valid ? static_cast<uint32_t>(r * (RW * 2) + cb)
+                                      : static_cast<uint32_t>((valid - 1) * (RW * 2));
+      global_to_lds16(tbase, voff, __builtin_amdgcn_readfirstlane(dst + j * 1024));
     }
   };
+  // wait until tile t has landed, given that the copies of tiles up to `last_issued` were issued
+  auto wait_tile = [&](int t, int last_issued) {
+    const int later = last_issued - t;
+    if (later >= 2) wait_vmcnt<2 * S::kCPW>();
+    else if (later == 1) wait_vmcnt<S::kCPW>();
+    else wait_vmcnt<0>();
+  };
 
-  // ---- query fragments (score waves): Qᵀ B operand, lane: head = 16w + l16, k = 32ks + 8lg + e
-  const bool score_wave = wave < NHB;
-  const int head_s = wave * 16 + l16;
-  bf16x8 qf[S::kSteps];
-  if (score_wave) {
+  // ---- score unit of this wave: head block hb, row block mb
+  constexpr bool kAllUnits = S::kUnits == kWaves;
+  const bool unit = kAllUnits || wave < S::kUnits;
+  const int hb_s = wave % NHB, mb_s = wave / NHB;
+  const int hloc = hb_s * 16 + l16;          // head (within the workgroup) of this lane's scores
+  const int head = head0 + hloc;
+  bf16x8 qf[S::kSteps];                      // Qᵀ B operand: lane k = 32ks + 8lg + e
+  if (unit) {
     const int per_group = H / G;
 #pragma unroll
     for (int ks = 0; ks < S::kSteps; ++ks) {
       const int k0 = ks * 32 + lg * 8;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (head_s < H) {
+      if (head < H) {
         if (k0 < R) {
-          v = *reinterpret_cast<const uint4*>(q_lat + (static_cast<int64_t>(b) * H + head_s) * R + k0);
+          v = *reinterpret_cast<const uint4*>(q_lat + (static_cast<int64_t>(b) * H + head) * R + k0);
         } else {
           const int g = (k0 - R) / d_rope, j0 = (k0 - R) - g * d_rope;
-          if (g == head_s / per_group)
-            v = *reinterpret_cast<const uint4*>(q_pe + (static_cast<int64_t>(b) * H + head_s) * d_rope + j0);
+          if (g == head / per_group)
+            v = *reinterpret_cast<const uint4*>(q_pe + (static_cast<int64_t>(b) * H + head) * d_rope + j0);
         }
       }
       qf[ks] = __builtin_bit_cast(bf16x8, v);
@@ -165,121 +213,213 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
   // also drain the tile copies in flight.
   wait_vmcnt<0>();
 
-  float m_run = -INFINITY, l_run = 0.f;  // per head (score waves), replicated over lane groups
-  f32x4 o[NHB][S::kNB];
+  // Scaled, masked scores Sᵀ of tile t for this unit: lane holds rows 16mb+4lg+i of head hloc.
+  auto score = [&](int t) -> f32x4 {
+    const unsigned char* arow = smem + (t % STAGES) * kBufBytes + (mb_s * 16 + l16) * S::kPitch + lg * 16;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 f[kPF];
 #pragma unroll
-  for (int hb = 0; hb < NHB; ++hb)
+    for (int p = 0; p < kPF; ++p) f[p] = lds_frag(arow + p * 64);
 #pragma unroll
-    for (int nb = 0; nb < S::kNB; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < S::kSteps; ++ks) {
+      const bf16x8 x = f[ks % kPF];
+      if (ks + kPF < S::kSteps) f[ks % kPF] = lds_frag(arow + (ks + kPF) * 64);
+      if (ks & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, qf[ks], acc1, 0, 0, 0);
+      else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, qf[ks], acc0, 0, 0, 0);
+    }
+    f32x4 sv = (acc0 + acc1) * qk_scale;
+    const int valid = min(kTL, l_end - (l_begin + t * kTL));  // rows past the split take no weight
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = (mb_s * 16 + lg * 4 + i < valid) ? sv[i] : -INFINITY;
+    return sv;
+  };
 
+  float m_ref = -INFINITY;   // reference max of head `hloc` (same in both row blocks)
+  float m_lane = -INFINITY;  // max of the scores this lane has seen in the pass
+  float l_lane = 0.f;        // sum of P over the rows this lane holds
+  f32x4 o[NHB][S::kNB];
   const int c0 = wave * S::kNC;  // PV column slice of this wave
 
-  if (n_tiles > 0) issue_tile(0);
-  if (n_tiles > 1) issue_tile(1);
+  // P of tile t (relative to m_ref) -> LDS buffer t&1; returns whether a score
+  // exceeds the reference by more than the slack.
+  auto emit_p = [&](int t, const f32x4& sv) -> bool {
+    m_lane = fmaxf(m_lane, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+    const float lim = m_ref + kSlack;
+    const bool over = (sv[0] > lim) || (sv[1] > lim) || (sv[2] > lim) || (sv[3] > lim);
+    const float p0 = __builtin_amdgcn_exp2f(sv[0] - m_ref);
+    const float p1 = __builtin_amdgcn_exp2f(sv[1] - m_ref);
+    const float p2 = __builtin_amdgcn_exp2f(sv[2] - m_ref);
+    const float p3 = __builtin_amdgcn_exp2f(sv[3] - m_ref);
+    l_lane += (p0 + p1) + (p2 + p3);
+    *reinterpret_cast<uint2*>(pbuf + (t & 1) * S::kPBytes + hloc * kPP + (mb_s * 16 + lg * 4) * 2) =
+        make_uint2(pack_bf16x2(p0, p1), pack_bf16x2(p2, p3));
+    return over;
+  };
 
-  for (int t = 0; t < n_tiles; ++t) {
-    if (t + 1 < n_tiles) wait_vmcnt<S::kCPW>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-    if (t + 2 < n_tiles) issue_tile(t + 2);
-    const unsigned char* tile = smem + (t % kStages) * kBufBytes;
-    const int valid = min(kTL, l_end - (l_begin + t * kTL));
-
-    if (score_wave) {
-      f32x4 sacc[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const unsigned char* arow = tile + (mb * 16 + l16) * S::kPitch + lg * 16;
-#pragma unroll
-        for (int ks = 0; ks < S::kSteps; ++ks) {
-          bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(arow + ks * 64));
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc, 0, 0, 0);
-        }
-        sacc[mb] = acc;
-      }
-      // rows of this lane: 16mb + 4lg + i ; head: l16
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = mb * 16 + lg * 4 + i;
-          float s = sacc[mb][i] * qk_scale;
-          s = row < valid ? s : -INFINITY;
-          sacc[mb][i] = s;
-          tmax = fmaxf(tmax, s);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = exp2f(m_run - m_new);
-      float psum = 0.f;
-      unsigned char* prow = pbuf + head_s * kPP;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        float p0 = exp2f(sacc[mb][0] - m_new), p1 = exp2f(sacc[mb][1] - m_new);
-        float p2 = exp2f(sacc[mb][2] - m_new), p3 = exp2f(sacc[mb][3] - m_new);
-        psum += (p0 + p1) + (p2 + p3);
-        uint2 pk = make_uint2(pack_bf16x2(p0, p1), pack_bf16x2(p2, p3));
-        *reinterpret_cast<uint2*>(prow + (mb * 16 + lg * 4) * 2) = pk;
-      }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      if (lg == 0) alpha_lds[head_s] = alpha;
-    }
-    lds_barrier();
-
-    // ---- PV: O[heads][c0 : c0+kNC] += P[heads][rows] · C[rows][cols]
+  // O[heads][c0 : c0+kNC] += P(t)[heads][rows] · C(t)[rows][cols]
+  auto pv = [&](int t) {
+    const unsigned char* tile = smem + (t % STAGES) * kBufBytes;
+    const unsigned char* pb = pbuf + (t & 1) * S::kPBytes;
     bf16x8 bfrag[S::kNB];
 #pragma unroll
     for (int nb = 0; nb < S::kNB; ++nb) {
       const int col = c0 + nb * 16 + 4 * (l16 & 3);
       const unsigned char* base = tile + (lg * 8 + (l16 >> 2)) * S::kPitch + col * 2;
-      s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
-      s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 4 * S::kPitch));
-      typedef short s16x8 __attribute__((ext_vector_type(8)));
-      s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      bfrag[nb] = __builtin_bit_cast(bf16x8, v);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 4 * S::kPitch));
+      bfrag[nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
+    bf16x8 pf[NHB];
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) {
-      const float4 al = *reinterpret_cast<const float4*>(alpha_lds + hb * 16 + lg * 4);
-      const bf16x8 pa = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const uint4*>(pbuf + (hb * 16 + l16) * kPP + lg * 16));
+    for (int hb = 0; hb < NHB; ++hb) pf[hb] = lds_frag(pb + (hb * 16 + l16) * kPP + lg * 16);
 #pragma unroll
-      for (int nb = 0; nb < S::kNB; ++nb) {
-        f32x4 acc = o[hb][nb];
-        acc[0] *= al.x;
-        acc[1] *= al.y;
-        acc[2] *= al.z;
-        acc[3] *= al.w;
-        o[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bfrag[nb], acc, 0, 0, 0);
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int nb = 0; nb < S::kNB; ++nb)
+        o[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[hb], bfrag[nb], o[hb][nb], 0, 0, 0);
+  };
+
+  // score(ts) and pv(tp) in one instruction stream: the operands of both are
+  // fetched first, then score and PV MFMAs alternate, so the MFMA pipe has
+  // independent work while LDS reads are outstanding.
+  auto score_and_pv = [&](int ts, int tp) -> f32x4 {
+    const unsigned char* tile = smem + (tp % STAGES) * kBufBytes;
+    const unsigned char* pb = pbuf + (tp & 1) * S::kPBytes;
+    bf16x8 bfrag[S::kNB];
+#pragma unroll
+    for (int nb = 0; nb < S::kNB; ++nb) {
+      const int col = c0 + nb * 16 + 4 * (l16 & 3);
+      const unsigned char* base = tile + (lg * 8 + (l16 >> 2)) * S::kPitch + col * 2;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 4 * S::kPitch));
+      bfrag[nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    bf16x8 pf[NHB];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) pf[hb] = lds_frag(pb + (hb * 16 + l16) * kPP + lg * 16);
+    const unsigned char* arow = smem + (ts % STAGES) * kBufBytes + (mb_s * 16 + l16) * S::kPitch + lg * 16;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 f[kPF];
+#pragma unroll
+    for (int p = 0; p < kPF; ++p) f[p] = lds_frag(arow + p * 64);
+    constexpr int kPV = NHB * S::kNB;
+#pragma unroll
+    for (int ks = 0; ks < (S::kSteps > kPV ? S::kSteps : kPV); ++ks) {
+      if (ks < S::kSteps) {
+        const bf16x8 x = f[ks % kPF];
+        if (ks + kPF < S::kSteps) f[ks % kPF] = lds_frag(arow + (ks + kPF) * 64);
+        if (ks & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, qf[ks], acc1, 0, 0, 0);
+        else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, qf[ks], acc0, 0, 0, 0);
+      }
+      if (ks < kPV) {
+        const int hb = ks / S::kNB, nb = ks % S::kNB;
+        o[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[hb], bfrag[nb], o[hb][nb], 0, 0, 0);
       }
     }
+    f32x4 sv = (acc0 + acc1) * qk_scale;
+    const int valid = min(kTL, l_end - (l_begin + ts * kTL));  // rows past the split take no weight
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = (mb_s * 16 + lg * 4 + i < valid) ? sv[i] : -INFINITY;
+    return sv;
+  };
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int nb = 0; nb < S::kNB; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_lane = 0.f;
+    m_lane = -INFINITY;
+    bool scan = false;  // workgroup-uniform: some score exceeded the reference's slack
+
+#pragma unroll
+    for (int t = 0; t < STAGES - 1; ++t)
+      if (t < n_tiles) issue_tile(t);
+    int issued = min(STAGES - 1, n_tiles) - 1;  // last tile whose copy is in flight or done
+
+    if (n_tiles > 0) {
+      // prologue: score tile 0; in the first pass its max sets the reference
+      wait_tile(0, issued);
+      lds_barrier();
+      f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+      if (unit) sv = score(0);
+      if (pass == 0) {
+        if (unit) {
+          float tmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+          if (lg == 0) xch[mb_s * S::kHeads + hloc] = tmax;
+        }
+        lds_barrier();
+        if (unit) m_ref = fmaxf(xch[hloc], xch[S::kHeads + hloc]);
+      }
+      if (unit) {
+        const bool over = emit_p(0, sv);
+        if (lane == 0) flag_lds[wave] = __ballot(over) != 0 ? 1 : 0;
+      }
+    }
+
+    // steady state: iteration t scores tile t+1 and accumulates tile t
+    for (int t = 0; t < n_tiles; ++t) {
+      if (t + 1 < n_tiles) wait_tile(t + 1, issued);
+      lds_barrier();  // tile t+1, P(t) and the flags of tile t are visible; tile t-1's buffer is free
+      {
+        int any = 0;
+#pragma unroll
+        for (int w = 0; w < S::kUnits; ++w) any |= flag_lds[(t & 1) * kWaves + w];
+        scan = scan || (any != 0);
+      }
+      if (t + STAGES - 1 < n_tiles) {
+        issue_tile(t + STAGES - 1);
+        issued = t + STAGES - 1;
+      }
+      // Tile t+1 is scored even past the last tile: its rows are then all masked
+      // (P = 0, no effect), which keeps this loop body free of branches.  In a
+      // scan, P may be out of range; the accumulators are then discarded.
+      if constexpr (kAllUnits) {
+        const f32x4 sv = score_and_pv(t + 1, t);
+        const bool over = emit_p(t + 1, sv);
+        if (lane == 0) flag_lds[((t + 1) & 1) * kWaves + wave] = __ballot(over) != 0 ? 1 : 0;
+      } else {
+        if (unit) {
+          const f32x4 sv = score(t + 1);
+          const bool over = emit_p(t + 1, sv);
+          if (lane == 0) flag_lds[((t + 1) & 1) * kWaves + wave] = __ballot(over) != 0 ? 1 : 0;
+        }
+        pv(t);
+      }
+    }
+    if (!scan) break;
+    // second pass with the split's true max (over all rows of both row blocks) as the reference
+    float mx = m_lane;
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (unit && lg == 0) xch[mb_s * S::kHeads + hloc] = mx;
+    lds_barrier();
+    if (unit) m_ref = fmaxf(xch[hloc], xch[S::kHeads + hloc]);
+    lds_barrier();
   }
 
-  // ---- epilogue
-  if (score_wave && lg == 0) {
-    ml_lds[head_s * 2 + 0] = m_run;
-    ml_lds[head_s * 2 + 1] = l_run;
-    if (n_split > 1 && head_s < H) {
-      const int64_t pidx = (static_cast<int64_t>(b) * n_split + split) * H + head_s;
-      part_ml[pidx * 2 + 0] = m_run;
-      part_ml[pidx * 2 + 1] = l_run;
-    }
+  // ---- epilogue: l = sum over the lanes and both row blocks; O normalised or as a partial
+  float l = l_lane;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (unit && lg == 0) xch[mb_s * S::kHeads + hloc] = l;
+  lds_barrier();
+  if (unit && mb_s == 0 && lg == 0 && n_split > 1 && head < H) {
+    const int64_t pidx = (static_cast<int64_t>(b) * n_split + split) * H + head;
+    part_ml[pidx * 2 + 0] = m_ref;
+    part_ml[pidx * 2 + 1] = xch[hloc] + xch[S::kHeads + hloc];
   }
-  __syncthreads();
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int h = hb * 16 + lg * 4 + i;
+      const int hl = hb * 16 + lg * 4 + i;
+      const int h = head0 + hl;
       if (h >= H) continue;
       if (n_split == 1) {
-        const float inv = 1.f / ml_lds[h * 2 + 1];
+        const float inv = 1.f / (xch[hl] + xch[S::kHeads + hl]);
         float* dst = o_out + (static_cast<int64_t>(b) * H + h) * R + c0 + l16;
 #pragma unroll
         for (int nb = 0; nb < S::kNB; ++nb) dst[nb * 16] = o[hb][nb][i] * inv;
@@ -291,37 +431,55 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
     }
 }
 
-template <int R, int RW, int NHB>
+template <int R, int RW, int NHB, int NHH, int STAGES>
 void launch(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
             const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split, int split_len,
             float* part_o, float* part_ml, float* o_out, hipStream_t s) {
-  using S = Shape<R, RW, NHB>;
-  auto kern = decode_mfma_kernel<R, RW, NHB>;
+  using S = Shape<R, RW, NHB, NHH, STAGES>;
+  auto kern = decode_mfma_kernel<R, RW, NHB, NHH, STAGES>;
   hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                       S::kLdsBytes);
-  hipLaunchKernelGGL(kern, dim3(batch * n_split), dim3(kThreads), S::kLdsBytes, s,
+  const int pairs = batch * n_split;
+  const int grid = NHH == 1 ? pairs : (pairs + 7) / 8 * 8 * NHH;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), S::kLdsBytes, s,
                      static_cast<const bf16_t*>(q_lat), static_cast<const bf16_t*>(q_pe),
-                     static_cast<const bf16_t*>(cache), seq_start, seq_len, sh.H, sh.G, sh.d_rope,
-                     sh.scale, n_split, split_len, part_o, part_ml, o_out);
+                     static_cast<const bf16_t*>(cache), seq_start, seq_len, batch, sh.H, sh.G,
+                     sh.d_rope, sh.scale, n_split, split_len, part_o, part_ml, o_out);
 }
+
+// Compiled shapes: (latent r, row width r + G*d_rope, 16-head blocks per workgroup,
+// workgroups per sequence split, LDS stages, head count range served).
+#define MLA_DECODE_SHAPES(X)                                                                  \
+  X(512, 576, 4, 2, 4, 113, 128) /* H = 128, G = 1, d_rope = 64 (DeepSeek-V2)          */ \
+  X(512, 544, 2, 1, 4, 17, 32)   /* H = 32, G = 4, d_rope = 8 (Qwen3-30B-A3B MLA delta) */ \
+  X(128, 160, 2, 1, 3, 17, 32)   /* H = 28, G = 4, d_rope = 8 (Qwen2.5-7B MLA delta)    */
 
 }  // namespace
 
 bool decode_mfma_supported(const AttnShape& sh) {
-  const int nhb = (sh.H + 15) / 16;
   if (sh.d_rope % 8 != 0) return false;
-  if (sh.r == 512 && sh.row_w == 576 && nhb == 8) return true;   // DeepSeek-V2 shape
-  if (sh.r == 512 && sh.row_w == 544 && nhb == 2) return true;   // Qwen3-30B-A3B shape
-  if (sh.r == 128 && sh.row_w == 160 && nhb == 2) return true;   // Qwen2.5-7B shape
+#define MLA_MATCH(R_, RW_, NHB_, NHH_, ST_, HLO_, HHI_) \
+  if (sh.r == R_ && sh.row_w == RW_ && sh.H >= HLO_ && sh.H <= HHI_) return true;
+  MLA_DECODE_SHAPES(MLA_MATCH)
+#undef MLA_MATCH
   return false;
 }
 
+int decode_mfma_head_groups(const AttnShape& sh) {
+#define MLA_NHH(R_, RW_, NHB_, NHH_, ST_, HLO_, HHI_) \
+  if (sh.r == R_ && sh.row_w == RW_ && sh.H >= HLO_ && sh.H <= HHI_) return NHH_;
+  MLA_DECODE_SHAPES(MLA_NHH)
+#undef MLA_NHH
+  return 1;
+}
+
 int decode_mfma_blocks_per_cu(const AttnShape& sh) {
-  const int nhb = (sh.H + 15) / 16;
   int lds = 0;
-  if (sh.r == 512 && sh.row_w == 576 && nhb == 8) lds = Shape<512, 576, 8>::kLdsBytes;
-  else if (sh.r == 512 && sh.row_w == 544 && nhb == 2) lds = Shape<512, 544, 2>::kLdsBytes;
-  else if (sh.r == 128 && sh.row_w == 160 && nhb == 2) lds = Shape<128, 160, 2>::kLdsBytes;
+#define MLA_LDS(R_, RW_, NHB_, NHH_, ST_, HLO_, HHI_)              \
+  if (sh.r == R_ && sh.row_w == RW_ && sh.H >= HLO_ && sh.H <= HHI_) \
+    lds = Shape<R_, RW_, NHB_, NHH_, ST_>::kLdsBytes;
+  MLA_DECODE_SHAPES(MLA_LDS)
+#undef MLA_LDS
   if (lds == 0) return 1;
   return std::max(1, std::min(4, (160 * 1024) / lds));
 }
@@ -330,16 +488,14 @@ void decode_mfma(const AttnShape& sh, const void* q_lat, const void* q_pe, const
                  const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split,
                  int split_len, float* part_o, float* part_ml, float* o_out, hipStream_t s) {
   if (batch <= 0) return;
-  const int nhb = (sh.H + 15) / 16;
-  if (sh.r == 512 && sh.row_w == 576 && nhb == 8)
-    launch<512, 576, 8>(sh, q_lat, q_pe, cache, seq_start, seq_len, batch, n_split, split_len,
-                        part_o, part_ml, o_out, s);
-  else if (sh.r == 512 && sh.row_w == 544 && nhb == 2)
-    launch<512, 544, 2>(sh, q_lat, q_pe, cache, seq_start, seq_len, batch, n_split, split_len,
-                        part_o, part_ml, o_out, s);
-  else if (sh.r == 128 && sh.row_w == 160 && nhb == 2)
-    launch<128, 160, 2>(sh, q_lat, q_pe, cache, seq_start, seq_len, batch, n_split, split_len,
-                        part_o, part_ml, o_out, s);
+#define MLA_LAUNCH(R_, RW_, NHB_, NHH_, ST_, HLO_, HHI_)                                          \
+  if (sh.r == R_ && sh.row_w == RW_ && sh.H >= HLO_ && sh.H <= HHI_) {                           \
+    launch<R_, RW_, NHB_, NHH_, ST_>(sh, q_lat, q_pe, cache, seq_start, seq_len, batch, n_split, \
+                                     split_len, part_o, part_ml, o_out, s);                      \
+    return;                                                                                      \
+  }
+  MLA_DECODE_SHAPES(MLA_LAUNCH)
+#undef MLA_LAUNCH
 }
 
 }  // namespace mla

@@ -40,6 +40,9 @@ int check_dims(const mla_dims* d) {
   // limits of the compiled kernels
   if (d->rank > kMaxRank || d->rank % 16 != 0) return MLA_ENOTSUP;
   if (d->dtype == MLA_BF16 && (d->d_model % 8 != 0 || d->d_nope % 8 != 0)) return MLA_ENOTSUP;
+  // the cache-row epilogue holds one projected row (<= 1024 floats) and one
+  // cos/sin table (<= 256 pairs) in LDS
+  if (d->rank + static_cast<int64_t>(d->n_groups) * d->d_rope > 1024 || d->d_rope > 512) return MLA_ENOTSUP;
   return MLA_OK;
 }
 
@@ -75,10 +78,11 @@ DecodePlan decode_plan(const mla_dims* d, int32_t batch, int32_t max_len) {
   p.mfma = d->dtype == MLA_BF16 && mla::decode_mfma_supported(sh);
   const int64_t B = std::max<int32_t>(batch, 0);
   const int L = std::max<int32_t>(max_len, 1);
-  // Workgroups per split: the MFMA kernel keeps all heads of a sequence in one
-  // workgroup; the generic kernel splits heads into blocks.
+  // Workgroups per split: the MFMA kernel splits the heads of a sequence over
+  // decode_mfma_head_groups() workgroups; the generic kernel into 8-head blocks.
   const int64_t per_split =
-      p.mfma ? B : B * ((sh.H + mla::generic_head_block() - 1) / mla::generic_head_block());
+      p.mfma ? B * mla::decode_mfma_head_groups(sh)
+             : B * ((sh.H + mla::generic_head_block() - 1) / mla::generic_head_block());
   // Fill the 256 compute units of an MI355X once (the MFMA kernel's LDS
   // footprint allows one workgroup per CU at the large shapes), keeping
   // splits >= 256 rows.
@@ -99,20 +103,94 @@ DecodePlan decode_plan(const mla_dims* d, int32_t batch, int32_t max_len) {
   return p;
 }
 
+// Few-token bf16 projections stream their weights with the skinny kernel.
+bool skinny_ok(const mla_dims* d, int64_t m) { return d->dtype == MLA_BF16 && m > 0 && m <= 64; }
+
+// x [T, d_model] · [W0; W1]ᵀ -> fp32 C (row stride ldc), W0 giving columns [0, n0)
+// and W1 columns [n0, n0 + n1).  The skinny kernel runs both weights in one
+// launch and leaves `splits` K-slices (slice stride sps floats) for the consumer
+// to sum; the tiled kernel runs once per weight and leaves one slice.
+struct Proj {
+  int splits;
+  int64_t sps;
+};
+
+Proj proj_plan(const mla_dims* d, int n, int64_t n_tokens, int64_t ldc) {
+  Proj p{1, 0};
+  if (skinny_ok(d, n_tokens)) {
+    p.splits = mla::skinny_splits(n, 1, d->d_model);
+    p.sps = static_cast<int64_t>(align_up(static_cast<size_t>(n_tokens) * ldc * sizeof(float)) / sizeof(float));
+  }
+  return p;
+}
+
+size_t proj_bytes(const mla_dims* d, int n, int64_t n_tokens, int64_t ldc) {
+  const Proj p = proj_plan(d, n, n_tokens, ldc);
+  return static_cast<size_t>(p.splits) * align_up(static_cast<size_t>(n_tokens) * ldc * sizeof(float));
+}
+
+GemmArgs proj_args(const mla_dims* d, const void* x, const void* w, int n, float* c, int64_t ldc,
+                   int64_t n_tokens) {
+  GemmArgs g{};
+  g.A = x;
+  g.sAm = d->d_model;
+  g.B = w;
+  g.sBo = d->d_model;
+  g.C = c;
+  g.sCm = ldc;
+  g.M = static_cast<int>(n_tokens);
+  g.N = n;
+  g.K = d->d_model;
+  g.Z = 1;
+  return g;
+}
+
+Proj proj_two(const mla_dims* d, const void* x, const void* w0, int n0, const void* w1, int n1,
+              float* c, int64_t ldc, int64_t n_tokens, hipStream_t s) {
+  const Proj p = proj_plan(d, n0 + n1, n_tokens, ldc);
+  if (skinny_ok(d, n_tokens)) {
+    mla::SkinnyArgs sa{};
+    sa.A = x;
+    sa.sAm = d->d_model;
+    sa.B0 = static_cast<const uint16_t*>(w0);
+    sa.B1 = static_cast<const uint16_t*>(w1);
+    sa.N0 = n0;
+    sa.sBo = d->d_model;
+    sa.C = c;
+    sa.sCm = ldc;
+    sa.sPs = p.sps;
+    sa.M = static_cast<int>(n_tokens);
+    sa.N = n0 + n1;
+    sa.K = d->d_model;
+    sa.Z = 1;
+    sa.splits = p.splits;
+    mla::gemm_skinny(sa, /*a_f32=*/false, /*out_bf16=*/false, s);
+  } else {
+    mla::gemm(proj_args(d, x, w0, n0, c, ldc, n_tokens), d->dtype, false, false, false, s);
+    mla::gemm(proj_args(d, x, w1, n1, c + n0, ldc, n_tokens), d->dtype, false, false, false, s);
+  }
+  return p;
+}
+
 size_t prefill_ws(const mla_dims* d, int64_t n_tokens) {
   return align_up(static_cast<size_t>(std::max<int64_t>(n_tokens, 0)) * d->n_heads * d->rank *
                   sizeof(float));
 }
 
+int row_width(const mla_dims* d) { return d->rank + d->n_groups * d->d_rope; }
+// fp32 query projection row: [q_nope (H x d_nope) | q_rope (H x d_rope)], padded to
+// 8 floats so every row starts 32-byte aligned for the W_UK GEMM's vector loads.
+int q_cols(const mla_dims* d) { return d->n_heads * (d->d_nope + d->d_rope); }
+int64_t q_width(const mla_dims* d) { return (static_cast<int64_t>(q_cols(d)) + 7) / 8 * 8; }
+
 size_t write_ws(const mla_dims* d, int64_t n_tokens) {
-  return align_up(static_cast<size_t>(std::max<int64_t>(n_tokens, 0)) *
-                  (d->rank + d->n_groups * d->d_rope) * sizeof(float));
+  const int64_t T = std::max<int64_t>(n_tokens, 0);
+  return proj_bytes(d, row_width(d), T, row_width(d));
 }
 
 size_t absorb_ws(const mla_dims* d, int64_t n_tokens) {
-  const size_t T = static_cast<size_t>(std::max<int64_t>(n_tokens, 0));
-  return align_up(T * d->n_heads * d->d_nope * sizeof(float)) +
-         align_up(T * d->n_heads * d->d_rope * sizeof(float));
+  const int64_t T = std::max<int64_t>(n_tokens, 0);
+  return proj_bytes(d, q_cols(d), T, q_width(d));
 }
 
 int launch_status() {
@@ -123,6 +201,26 @@ int launch_status() {
 // out[q, h, :] = W_UV[h] · o_[q, h, :]   (o_ fp32 [n_q, H, r]; W_UV [H, d_v, r])
 void apply_w_uv(const mla_dims* d, const float* o_lat, int64_t n_q, const void* w_uv, void* out,
                 hipStream_t s) {
+  if (skinny_ok(d, n_q)) {
+    mla::SkinnyArgs sa{};
+    sa.A = o_lat;
+    sa.sAz = d->rank;
+    sa.sAm = static_cast<int64_t>(d->n_heads) * d->rank;
+    sa.B0 = sa.B1 = static_cast<const uint16_t*>(w_uv);
+    sa.N0 = d->d_v;
+    sa.sBz = static_cast<int64_t>(d->d_v) * d->rank;
+    sa.sBo = d->rank;
+    sa.C = out;
+    sa.sCz = d->d_v;
+    sa.sCm = static_cast<int64_t>(d->n_heads) * d->d_v;
+    sa.M = static_cast<int>(n_q);
+    sa.N = d->d_v;
+    sa.K = d->rank;
+    sa.Z = d->n_heads;
+    sa.splits = 1;
+    mla::gemm_skinny(sa, /*a_f32=*/true, /*out_bf16=*/true, s);
+    return;
+  }
   GemmArgs g{};
   g.A = o_lat;
   g.sAz = d->rank;
@@ -184,30 +282,12 @@ int mla_write_cache(const mla_dims* dims, const void* x, const void* w_dkv, cons
     return MLA_EINVAL;
   if (workspace_bytes < write_ws(dims, n_tokens)) return MLA_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int row_w = dims->rank + dims->n_groups * dims->d_rope;
+  const int row_w = row_width(dims);
   float* proj = static_cast<float*>(workspace);
-
-  GemmArgs g{};
-  g.A = x;
-  g.sAz = 0;
-  g.sAm = dims->d_model;
-  g.B = w_dkv;
-  g.sBz = 0;
-  g.sBo = dims->d_model;
-  g.C = proj;
-  g.sCz = 0;
-  g.sCm = row_w;
-  g.M = static_cast<int>(n_tokens);
-  g.N = dims->rank;
-  g.K = dims->d_model;
-  g.Z = 1;
-  mla::gemm(g, dims->dtype, false, false, false, s);
-  g.B = w_kr;
-  g.C = proj + dims->rank;
-  g.N = dims->n_groups * dims->d_rope;
-  mla::gemm(g, dims->dtype, false, false, false, s);
-  mla::finalize_cache_rows(dims->dtype, proj, row_w, cache, slots, positions, n_tokens,
-                           dims->rank, dims->n_groups, dims->d_rope, dims->latent_rmsnorm,
+  const Proj p = proj_two(dims, x, w_dkv, dims->rank, w_kr, dims->n_groups * dims->d_rope, proj,
+                          row_w, n_tokens, s);
+  mla::finalize_cache_rows(dims->dtype, proj, row_w, p.splits, p.sps, cache, slots, positions,
+                           n_tokens, dims->rank, dims->n_groups, dims->d_rope, dims->latent_rmsnorm,
                            dims->rms_eps, dims->rope_theta, s);
   return launch_status();
 }
@@ -226,35 +306,18 @@ int mla_absorb(const mla_dims* dims, const void* x, const void* w_qc, const void
   if (workspace_bytes < absorb_ws(dims, n_tokens)) return MLA_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int H = dims->n_heads;
-  const size_t T = static_cast<size_t>(n_tokens);
-  float* qn = static_cast<float*>(workspace);
-  float* qr = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                       align_up(T * H * dims->d_nope * sizeof(float)));
-
-  GemmArgs g{};
-  g.A = x;
-  g.sAm = dims->d_model;
-  g.B = w_qc;
-  g.sBo = dims->d_model;
-  g.C = qn;
-  g.sCm = static_cast<int64_t>(H) * dims->d_nope;
-  g.M = static_cast<int>(n_tokens);
-  g.N = H * dims->d_nope;
-  g.K = dims->d_model;
-  g.Z = 1;
-  mla::gemm(g, dims->dtype, false, false, false, s);
-  g.B = w_qr;
-  g.C = qr;
-  g.sCm = static_cast<int64_t>(H) * dims->d_rope;
-  g.N = H * dims->d_rope;
-  mla::gemm(g, dims->dtype, false, false, false, s);
-  mla::finalize_query_rope(dims->dtype, qr, q_pe, positions, n_tokens, H, dims->d_rope,
-                           dims->rope_theta, s);
-  // q_lat[t,h,:] = Σ_d qn[t,h,d] W_UK[h,d,:]   (batched over heads)
+  const int64_t ld = q_width(dims);
+  // one fp32 row per token: [q_nope (H x d_nope) | q_rope (H x d_rope)]
+  float* q = static_cast<float*>(workspace);
+  const Proj p = proj_two(dims, x, w_qc, H * dims->d_nope, w_qr, H * dims->d_rope, q, ld, n_tokens, s);
+  mla::sum_split_slices(q, p.splits, p.sps, static_cast<int>(n_tokens), q_cols(dims), ld, s);
+  mla::finalize_query_rope(dims->dtype, q + static_cast<int64_t>(H) * dims->d_nope, ld, q_pe, positions,
+                           n_tokens, H, dims->d_rope, dims->rope_theta, s);
+  // q_lat[t,h,:] = Σ_d q_nope[t,h,d] W_UK[h,d,:]   (batched over heads)
   GemmArgs a{};
-  a.A = qn;
+  a.A = q;
   a.sAz = dims->d_nope;
-  a.sAm = static_cast<int64_t>(H) * dims->d_nope;
+  a.sAm = ld;
   a.B = w_uk;
   a.sBz = static_cast<int64_t>(dims->d_nope) * dims->rank;
   a.sBo = dims->rank;

@@ -25,16 +25,36 @@ struct GemmArgs {
 // B bf16, fp32 accumulate, C fp32 or bf16 (out_bf16).
 void gemm(const GemmArgs& g, int dtype, bool a_f32, bool b_kn, bool out_bf16, hipStream_t s);
 
+// Weight-streaming GEMM for M <= 64 rows: C[z][m][n] = Σ_k A[z][m][k]·W[z][n][k]
+// with W rows n < N0 from B0 and n >= N0 from B1 (row n - N0), bf16 weights.
+// splits > 1: K pieces write fp32 slices C + s*sPs that the consumer sums.
+struct SkinnyArgs {
+  const void* A;
+  int64_t sAz, sAm;          // A[z][m][k]: bf16, or fp32 (split hi/lo)
+  const uint16_t* B0;  // bf16 bit patterns
+  const uint16_t* B1;
+  int N0;
+  int64_t sBz, sBo;          // W[z][n][k]
+  void* C;
+  int64_t sCz, sCm, sPs;     // C[s][z][m][n]
+  int M, N, K, Z, splits, k_per_split;
+};
+int skinny_splits(int N, int Z, int K);
+void gemm_skinny(SkinnyArgs sa, bool a_f32, bool out_bf16, hipStream_t s);
+void sum_split_slices(float* c, int splits, int64_t sps, int M, int N, int64_t ldc, hipStream_t s);
+
 // Cache rows from the fp32 projections in `proj` ([T, r + G*d_rope], row stride ld):
 // optional RMSNorm over the latent, RoPE on each rotary-key group, cast, scatter to slots.
-void finalize_cache_rows(int dtype, const float* proj, int64_t ld, void* cache,
-                         const int64_t* slots, const int32_t* positions, int64_t n_tokens, int r,
-                         int n_groups, int d_rope, int latent_rmsnorm, float eps, double theta,
-                         hipStream_t s);
+// `proj` holds `splits` partial slices (slice stride `sps` floats) that are summed first.
+void finalize_cache_rows(int dtype, const float* proj, int64_t ld, int splits, int64_t sps,
+                         void* cache, const int64_t* slots, const int32_t* positions,
+                         int64_t n_tokens, int r, int n_groups, int d_rope, int latent_rmsnorm,
+                         float eps, double theta, hipStream_t s);
 
-// q_pe[t,h,:] = RoPE(proj[t, h*d_rope : +d_rope], positions[t]), cast to dtype.
-void finalize_query_rope(int dtype, const float* proj, void* q_pe, const int32_t* positions,
-                         int64_t n_tokens, int n_heads, int d_rope, double theta, hipStream_t s);
+// q_pe[t,h,:] = RoPE(proj[t*ld + h*d_rope : +d_rope], positions[t]), cast to dtype.
+void finalize_query_rope(int dtype, const float* proj, int64_t ld, void* q_pe,
+                         const int32_t* positions, int64_t n_tokens, int n_heads, int d_rope,
+                         double theta, hipStream_t s);
 
 // Shape of one attention call, as the kernels see it.
 struct AttnShape {
@@ -60,6 +80,7 @@ void merge_splits(const AttnShape& sh, int64_t n_q, int n_split, const float* pa
 // bf16 MFMA decode kernel for the shapes it supports (see decode_mfma.hip).
 bool decode_mfma_supported(const AttnShape& sh);
 int decode_mfma_blocks_per_cu(const AttnShape& sh);  // workgroups one CU holds (LDS-limited)
+int decode_mfma_head_groups(const AttnShape& sh);    // workgroups that share one sequence split
 void decode_mfma(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
                  const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split,
                  int split_len, float* part_o, float* part_ml, float* o_out, hipStream_t s);

@@ -10,23 +10,35 @@ namespace mla {
 
 namespace {
 
+constexpr int kMaxHalf = 256;  // rotary pairs per group supported by the shared cos/sin table
+
 template <typename T>
 __global__ __launch_bounds__(256) void cache_rows_kernel(const float* __restrict__ proj, int64_t ld,
+                                                         int splits, int64_t sps,
                                                          T* __restrict__ cache,
                                                          const int64_t* __restrict__ slots,
                                                          const int32_t* __restrict__ positions,
                                                          int r, int n_groups, int d_rope,
                                                          int latent_rmsnorm, float eps,
                                                          double theta) {
+  __shared__ float row[1024];  // summed projection row (r + G*d_rope <= 1024)
+  __shared__ float cs[kMaxHalf], sn[kMaxHalf];
+  __shared__ float red[4];
   const int64_t t = blockIdx.x;
-  const float* row = proj + t * ld;
   const int row_w = r + n_groups * d_rope;
-  T* dst = cache + slots[t] * static_cast<int64_t>(row_w);
+  const int half = d_rope / 2;
+  for (int i = threadIdx.x; i < row_w; i += blockDim.x) {
+    float v = 0.f;
+    for (int p = 0; p < splits; ++p) v += proj[p * sps + t * ld + i];
+    row[i] = v;
+  }
   const int32_t pos = positions[t];
+  for (int j = threadIdx.x; j < half; j += blockDim.x) rope_cos_sin(pos, j, d_rope, theta, &cs[j], &sn[j]);
+  __syncthreads();
+  T* dst = cache + slots[t] * static_cast<int64_t>(row_w);
 
   float inv = 1.f;
   if (latent_rmsnorm) {
-    __shared__ float red[4];
     float ss = 0.f;
     for (int i = threadIdx.x; i < r; i += blockDim.x) ss = fmaf(row[i], row[i], ss);
     ss = wave_sum(ss);
@@ -37,66 +49,64 @@ __global__ __launch_bounds__(256) void cache_rows_kernel(const float* __restrict
     inv = 1.0f / sqrtf(tot / static_cast<float>(r) + eps);
   }
   for (int i = threadIdx.x; i < r; i += blockDim.x) Elem<T>::store(dst, i, row[i] * inv);
-
-  const int half = d_rope / 2;
   for (int i = threadIdx.x; i < n_groups * half; i += blockDim.x) {
-    int g = i / half, j = i % half;
-    float cs, sn;
-    rope_cos_sin(pos, j, d_rope, theta, &cs, &sn);
+    const int g = i / half, j = i % half;
     const float* src = row + r + g * d_rope;
-    float a = src[j], b = src[j + half];
-    Elem<T>::store(dst, r + g * d_rope + j, a * cs - b * sn);
-    Elem<T>::store(dst, r + g * d_rope + j + half, b * cs + a * sn);
+    const float a = src[j], b = src[j + half];
+    Elem<T>::store(dst, r + g * d_rope + j, a * cs[j] - b * sn[j]);
+    Elem<T>::store(dst, r + g * d_rope + j + half, b * cs[j] + a * sn[j]);
   }
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void query_rope_kernel(const float* __restrict__ proj,
+__global__ __launch_bounds__(256) void query_rope_kernel(const float* __restrict__ proj, int64_t ld,
                                                          T* __restrict__ q_pe,
                                                          const int32_t* __restrict__ positions,
                                                          int n_heads, int d_rope, double theta) {
+  __shared__ float cs[kMaxHalf], sn[kMaxHalf];
   const int64_t t = blockIdx.x;
   const int half = d_rope / 2;
   const int32_t pos = positions[t];
-  const float* src = proj + t * static_cast<int64_t>(n_heads) * d_rope;
+  for (int j = threadIdx.x; j < half; j += blockDim.x) rope_cos_sin(pos, j, d_rope, theta, &cs[j], &sn[j]);
+  __syncthreads();
+  const float* src = proj + t * ld;
   T* dst = q_pe + t * static_cast<int64_t>(n_heads) * d_rope;
   for (int i = threadIdx.x; i < n_heads * half; i += blockDim.x) {
-    int h = i / half, j = i % half;
-    float cs, sn;
-    rope_cos_sin(pos, j, d_rope, theta, &cs, &sn);
-    float a = src[h * d_rope + j], b = src[h * d_rope + j + half];
-    Elem<T>::store(dst, h * d_rope + j, a * cs - b * sn);
-    Elem<T>::store(dst, h * d_rope + j + half, b * cs + a * sn);
+    const int h = i / half, j = i % half;
+    const float a = src[h * d_rope + j], b = src[h * d_rope + j + half];
+    Elem<T>::store(dst, h * d_rope + j, a * cs[j] - b * sn[j]);
+    Elem<T>::store(dst, h * d_rope + j + half, b * cs[j] + a * sn[j]);
   }
 }
 
 }  // namespace
 
-void finalize_cache_rows(int dtype, const float* proj, int64_t ld, void* cache,
-                         const int64_t* slots, const int32_t* positions, int64_t n_tokens, int r,
-                         int n_groups, int d_rope, int latent_rmsnorm, float eps, double theta,
-                         hipStream_t s) {
+void finalize_cache_rows(int dtype, const float* proj, int64_t ld, int splits, int64_t sps,
+                         void* cache, const int64_t* slots, const int32_t* positions,
+                         int64_t n_tokens, int r, int n_groups, int d_rope, int latent_rmsnorm,
+                         float eps, double theta, hipStream_t s) {
   if (n_tokens <= 0) return;
   dim3 grid(static_cast<unsigned>(n_tokens));
   if (dtype == kF32)
-    hipLaunchKernelGGL(cache_rows_kernel<float>, grid, dim3(256), 0, s, proj, ld,
+    hipLaunchKernelGGL(cache_rows_kernel<float>, grid, dim3(256), 0, s, proj, ld, splits, sps,
                        static_cast<float*>(cache), slots, positions, r, n_groups, d_rope,
                        latent_rmsnorm, eps, theta);
   else
-    hipLaunchKernelGGL(cache_rows_kernel<bf16_t>, grid, dim3(256), 0, s, proj, ld,
+    hipLaunchKernelGGL(cache_rows_kernel<bf16_t>, grid, dim3(256), 0, s, proj, ld, splits, sps,
                        static_cast<bf16_t*>(cache), slots, positions, r, n_groups, d_rope,
                        latent_rmsnorm, eps, theta);
 }
 
-void finalize_query_rope(int dtype, const float* proj, void* q_pe, const int32_t* positions,
-                         int64_t n_tokens, int n_heads, int d_rope, double theta, hipStream_t s) {
+void finalize_query_rope(int dtype, const float* proj, int64_t ld, void* q_pe,
+                         const int32_t* positions, int64_t n_tokens, int n_heads, int d_rope,
+                         double theta, hipStream_t s) {
   if (n_tokens <= 0) return;
   dim3 grid(static_cast<unsigned>(n_tokens));
   if (dtype == kF32)
-    hipLaunchKernelGGL(query_rope_kernel<float>, grid, dim3(256), 0, s, proj,
+    hipLaunchKernelGGL(query_rope_kernel<float>, grid, dim3(256), 0, s, proj, ld,
                        static_cast<float*>(q_pe), positions, n_heads, d_rope, theta);
   else
-    hipLaunchKernelGGL(query_rope_kernel<bf16_t>, grid, dim3(256), 0, s, proj,
+    hipLaunchKernelGGL(query_rope_kernel<bf16_t>, grid, dim3(256), 0, s, proj, ld,
                        static_cast<bf16_t*>(q_pe), positions, n_heads, d_rope, theta);
 }
 
