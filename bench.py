@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--workload", default="deepseek_v2_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--threads", type=int, default=0, help="host threads for input generation (0: all)")
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="finish with one plain device copy of this many MB (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
@@ -59,6 +61,38 @@ def decode_alg_bytes(cfg, lengths) -> int:
     B = len(lengths)
     return (rows * cfg.row_width * e + B * cfg.n_heads * (cfg.rank + cfg.d_rope) * e
             + cfg.n_heads * cfg.d_v * cfg.rank * e + B * cfg.n_heads * cfg.d_v * e)
+
+
+def attention_alg_bytes(cfg, lengths) -> int:
+    """Bytes the split attention kernel must move: cache rows read and the queries
+    (the split partials it writes are overhead of the split, not counted)."""
+    e = cfg.elem_bytes
+    rows = int(sum(lengths))
+    return rows * cfg.row_width * e + len(lengths) * cfg.n_heads * (cfg.rank + cfg.d_rope) * e
+
+
+def attention_alg_flops(cfg, lengths) -> int:
+    rows = int(sum(lengths))
+    return rows * cfg.n_heads * (2 * (cfg.rank + cfg.d_rope) + 2 * cfg.rank)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attention_deepseek_v2_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "head_latent_attention_kv_amd", "csrc", "decode_mfma.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the attention kernel from the committed rocprofv3
+    counter summary, or None when the kernel source has changed since."""
+    import hashlib
+    try:
+        kv = dict(line.split("=", 1) for line in open(TRAFFIC_FILE).read().split("\n")
+                  if "=" in line and not line.startswith("#"))
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if kv.get("kernel_source_sha256", "").strip() != src:
+        return None
+    return int(float(kv["hbm_bytes_per_launch"]))
 
 
 def decode_alg_flops(cfg, lengths) -> int:
@@ -206,7 +240,7 @@ def main():
     print(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (setup {setup_s:.1f} s)",
           file=sys.stderr, flush=True)
 
-    # the dominant kernel group, timed on its own stream with HIP events
+    # the whole decode call (attention, then the split merge folded into W_UV)
     for i in range(args.warmup):
         decode_only(i)
     torch.cuda.synchronize()
@@ -216,10 +250,31 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     ms_dec = e0.elapsed_time(e1) / args.steps
-    alg_bytes = decode_alg_bytes(cfg, lengths)
-    achieved = alg_bytes / (ms_dec * 1e-3) / 1e9
-    print(f"[bench] decode call: {ms_dec * 1e3:.1f} us, {achieved:.0f} GB/s algorithmic",
-          file=sys.stderr, flush=True)
+
+    # the dominant kernel alone: the split attention (mla_decode_partials launches
+    # exactly that kernel, with mla_decode's split plan), HIP events on its stream
+    n_split = M.mla_decode_splits(dims, B, max_len)
+    part_o = torch.empty((B, n_split, cfg.n_heads, cfg.rank), dtype=torch.float32, device="cuda")
+    part_ml = torch.empty((B, n_split, cfg.n_heads, 2), dtype=torch.float32, device="cuda")
+
+    def attention_only(i):
+        M.mla_decode_partials(dims, q_lat, q_pe, caches[i % n_copies], seq_start, seq_len, max_len, n_split,
+                              part_o, part_ml)
+
+    for i in range(args.warmup):
+        attention_only(i)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        attention_only(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_att = e0.elapsed_time(e1) / args.steps
+    alg_bytes = attention_alg_bytes(cfg, lengths)
+    achieved = alg_bytes / (ms_att * 1e-3) / 1e9
+    traffic = measured_traffic()
+    print(f"[bench] decode call: {ms_dec * 1e3:.1f} us; attention kernel ({n_split} splits): "
+          f"{ms_att * 1e3:.1f} us, {achieved:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
 
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all(), "non-finite decode output"
@@ -246,14 +301,33 @@ def main():
         "config": {"workload": cfg.name, "batch": B, "context": int(max_len), "heads": cfg.n_heads,
                    "rank": cfg.rank, "d_rope": cfg.d_rope, "d_model": cfg.d_model,
                    "step": "mla_write_cache + mla_absorb + mla_decode"},
-        "roofline": {"bound": "hbm", "kernel": "mla_decode (attention + merge + W_UV)",
+        "roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel (split attention over the latent cache)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "alg_bytes": alg_bytes, "alg_flops": decode_alg_flops(cfg, lengths),
-                     "us_per_launch": round(ms_dec * 1e3, 2)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": (round(traffic / (ms_att * 1e-3) / 1e9, 1) if traffic else None),
+                     "traffic_bytes_per_launch": traffic,
+                     "alg_bytes_per_launch": alg_bytes,
+                     "alg_flops_per_launch": attention_alg_flops(cfg, lengths),
+                     "mfma_frac": round(attention_alg_flops(cfg, lengths) / (ms_att * 1e-3) / 1e12
+                                        / MFMA_BF16_PEAK_TFS, 4),
+                     "us_per_launch": round(ms_att * 1e3, 2)},
+        "decode_call": {"us": round(ms_dec * 1e3, 2), "alg_bytes": decode_alg_bytes(cfg, lengths),
+                        "alg_flops": decode_alg_flops(cfg, lengths),
+                        "hbm_frac": round(decode_alg_bytes(cfg, lengths) / (ms_dec * 1e-3) / 1e9
+                                          / HBM_PEAK_GBS, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+    if args.copy_calib_mb > 0:
+        # one plain copy of known size: its FETCH_SIZE / WRITE_SIZE calibrate the counters
+        n = args.copy_calib_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy: {n * 4} bytes read, {n * 4} bytes written", file=sys.stderr)
 
 
 if __name__ == "__main__":

@@ -8,16 +8,19 @@ its calls:
     mla_absorb       — q_lat = (x·W_QCᵀ)·W_UK per head, q_pe = RoPE(x·W_QRᵀ)
     mla_decode       — one query per sequence against its cached rows
     mla_prefill      — causal attention over packed sequences
+    mla_decode_partials — the decode attention's per-split softmax partials
 
 Build the library with ``python -m head_latent_attention_kv_amd.build``.
 """
 from ._abi import (  # noqa: F401
     MLA_BF16, MLA_EHIP, MLA_EINVAL, MLA_ENOTSUP, MLA_EWORKSPACE, MLA_F32, MLA_OK, MLA_OP_ABSORB,
     MLA_OP_DECODE, MLA_OP_PREFILL, MLA_OP_WRITE_CACHE, MlaDims, MlaError, dims_of, load, make_dims,
-    mla_absorb, mla_decode, mla_prefill, mla_workspace_size, mla_write_cache, strerror,
+    mla_absorb, mla_decode, mla_decode_partials, mla_decode_split_rows, mla_decode_splits, mla_prefill,
+    mla_workspace_size, mla_write_cache, strerror,
 )
 
 __all__ = [
-    "MlaDims", "MlaError", "dims_of", "load", "make_dims", "mla_absorb", "mla_decode", "mla_prefill",
+    "MlaDims", "MlaError", "dims_of", "load", "make_dims", "mla_absorb", "mla_decode",
+    "mla_decode_partials", "mla_decode_split_rows", "mla_decode_splits", "mla_prefill",
     "mla_workspace_size", "mla_write_cache", "strerror",
 ]

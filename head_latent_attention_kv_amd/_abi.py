@@ -36,6 +36,9 @@ SIGNATURES = {
     "mla_absorb": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "mla_decode": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "mla_prefill": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "mla_decode_splits": (_i32, [_PD, _i32, _i32]),
+    "mla_decode_split_rows": (_i32, [_PD, _i32, _i32]),
+    "mla_decode_partials": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "mla_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_version": (ctypes.c_int, []),
 }
@@ -174,6 +177,33 @@ def mla_decode(dims, q_lat, q_pe, cache, seq_start, seq_len, max_len, w_uv, out,
         int(max_len), _ptr(w_uv, "w_uv", et), _ptr(out, "out", et), _ptr(ws, "workspace"), nbytes,
         _stream(stream)))
     return out
+
+
+def mla_decode_splits(dims, batch: int, max_len: int) -> int:
+    n = int(load().mla_decode_splits(ctypes.byref(dims), int(batch), int(max_len)))
+    if n < 0:
+        raise MlaError("mla_decode_splits", n)
+    return n
+
+
+def mla_decode_split_rows(dims, batch: int, max_len: int) -> int:
+    n = int(load().mla_decode_split_rows(ctypes.byref(dims), int(batch), int(max_len)))
+    if n < 0:
+        raise MlaError("mla_decode_split_rows", n)
+    return n
+
+
+def mla_decode_partials(dims, q_lat, q_pe, cache, seq_start, seq_len, max_len, n_split, part_o, part_ml,
+                        stream=None):
+    torch = _torch()
+    et = _elem_dtype(dims)
+    B = q_lat.shape[0]
+    _check("mla_decode_partials", load().mla_decode_partials(
+        ctypes.byref(dims), _ptr(q_lat, "q_lat", et), _ptr(q_pe, "q_pe", et), _ptr(cache, "cache", et),
+        _ptr(seq_start, "seq_start", torch.int64), _ptr(seq_len, "seq_len", torch.int32), B,
+        int(max_len), int(n_split), _ptr(part_o, "part_o", torch.float32),
+        _ptr(part_ml, "part_ml", torch.float32), _stream(stream)))
+    return part_o, part_ml
 
 
 def mla_prefill(dims, q_lat, q_pe, cache, cu_seqlens, max_len, w_uv, out, workspace=None, stream=None):

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(
   }
 
   if (head >= sh.H) return;
-  if (n_split == 1) {
+  if (part_o == nullptr) {  // normalised o_ (one split)
     const float inv = 1.f / l_run;
 #pragma unroll
     for (int j = 0; j < kRJ; ++j) {

@@ -25,7 +25,7 @@
 //  4. PV: wave w owns latent columns [w·R/8, (w+1)·R/8) for all heads of the
 //     workgroup; O += P·C with P (A operand) from LDS and C (B operand) read
 //     transposed from the same tile with ds_read_b64_tr_b16.
-// Output: normalised o_ (one split) or (m, l, unnormalised o_) partials.
+// Output: normalised o_ (part_o null, one split) or (m, l, unnormalised o_) partials.
 #include <math.h>
 
 #include <algorithm>
@@ -406,7 +406,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
   l += __shfl_xor(l, 32, 64);
   if (unit && lg == 0) xch[mb_s * S::kHeads + hloc] = l;
   lds_barrier();
-  if (unit && mb_s == 0 && lg == 0 && n_split > 1 && head < H) {
+  const bool partials = part_o != nullptr;
+  if (unit && mb_s == 0 && lg == 0 && partials && head < H) {
     const int64_t pidx = (static_cast<int64_t>(b) * n_split + split) * H + head;
     part_ml[pidx * 2 + 0] = m_ref;
     part_ml[pidx * 2 + 1] = xch[hloc] + xch[S::kHeads + hloc];
@@ -418,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
       const int hl = hb * 16 + lg * 4 + i;
       const int h = head0 + hl;
       if (h >= H) continue;
-      if (n_split == 1) {
+      if (!partials) {
         const float inv = 1.f / (xch[hl] + xch[S::kHeads + hl]);
         float* dst = o_out + (static_cast<int64_t>(b) * H + h) * R + c0 + l16;
 #pragma unroll

@@ -72,12 +72,22 @@ struct DecodePlan {
   size_t total() const { return part_o_bytes + part_ml_bytes + o_bytes; }
 };
 
-DecodePlan decode_plan(const mla_dims* d, int32_t batch, int32_t max_len) {
+int split_rows(int L, int64_t ns) {
+  int split_len = static_cast<int>((L + ns - 1) / ns);
+  return (split_len + 63) / 64 * 64;
+}
+
+DecodePlan decode_plan(const mla_dims* d, int32_t batch, int32_t max_len, int32_t force_splits = 0) {
   DecodePlan p{};
   AttnShape sh = shape_of(d);
   p.mfma = d->dtype == MLA_BF16 && mla::decode_mfma_supported(sh);
   const int64_t B = std::max<int32_t>(batch, 0);
   const int L = std::max<int32_t>(max_len, 1);
+  if (force_splits > 0) {
+    p.split_len = split_rows(L, force_splits);
+    p.n_split = force_splits;
+    return p;
+  }
   // Workgroups per split: the MFMA kernel splits the heads of a sequence over
   // decode_mfma_head_groups() workgroups; the generic kernel into 8-head blocks.
   const int64_t per_split =
@@ -90,8 +100,7 @@ DecodePlan decode_plan(const mla_dims* d, int32_t batch, int32_t max_len) {
   int64_t ns = per_split > 0 ? (target + per_split - 1) / per_split : 1;
   const int64_t max_ns = std::max<int64_t>(1, L / 256);
   ns = std::max<int64_t>(1, std::min<int64_t>(ns, max_ns));
-  int split_len = static_cast<int>((L + ns - 1) / ns);
-  split_len = (split_len + 63) / 64 * 64;
+  const int split_len = split_rows(L, ns);
   ns = (L + split_len - 1) / split_len;
   p.n_split = static_cast<int>(ns);
   p.split_len = split_len;
@@ -118,7 +127,7 @@ struct Proj {
 Proj proj_plan(const mla_dims* d, int n, int64_t n_tokens, int64_t ldc) {
   Proj p{1, 0};
   if (skinny_ok(d, n_tokens)) {
-    p.splits = mla::skinny_splits(n, 1, d->d_model);
+    p.splits = mla::skinny_splits(static_cast<int>(n_tokens), n, 1, d->d_model);
     p.sps = static_cast<int64_t>(align_up(static_cast<size_t>(n_tokens) * ldc * sizeof(float)) / sizeof(float));
   }
   return p;
@@ -358,8 +367,70 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_pe, const 
   else
     mla::attend_generic(dims->dtype, sh, q_lat, q_pe, cache, seq_start, seq_len, nullptr, batch,
                         batch, p.n_split, p.split_len, part_o, part_ml, o_lat, s);
+  if (p.n_split > 1 && skinny_ok(dims, batch) && p.n_split <= mla::skinny_max_merge()) {
+    // split merge folded into the W_UV operand load:
+    //   out[b,h,:] = W_UV[h] · Σ_j w_j(b,h) part_o[b,j,h,:]
+    mla::SkinnyArgs sa{};
+    sa.A = part_o;
+    sa.sAz = dims->rank;
+    sa.sAm = static_cast<int64_t>(p.n_split) * dims->n_heads * dims->rank;
+    sa.sAs = static_cast<int64_t>(dims->n_heads) * dims->rank;
+    sa.ml = part_ml;
+    sa.ml_heads = dims->n_heads;
+    sa.B0 = sa.B1 = static_cast<const uint16_t*>(w_uv);
+    sa.N0 = dims->d_v;
+    sa.sBz = static_cast<int64_t>(dims->d_v) * dims->rank;
+    sa.sBo = dims->rank;
+    sa.C = out;
+    sa.sCz = dims->d_v;
+    sa.sCm = static_cast<int64_t>(dims->n_heads) * dims->d_v;
+    sa.M = batch;
+    sa.N = dims->d_v;
+    sa.K = dims->rank;
+    sa.Z = dims->n_heads;
+    mla::gemm_skinny_merged(sa, p.n_split, /*out_bf16=*/true, s);
+    return launch_status();
+  }
   if (p.n_split > 1) mla::merge_splits(sh, batch, p.n_split, part_o, part_ml, o_lat, s);
   apply_w_uv(dims, o_lat, batch, w_uv, out, s);
+  return launch_status();
+}
+
+int32_t mla_decode_splits(const mla_dims* dims, int32_t batch, int32_t max_len) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || max_len <= 0) return MLA_EINVAL;
+  return decode_plan(dims, batch, max_len).n_split;
+}
+
+int32_t mla_decode_split_rows(const mla_dims* dims, int32_t batch, int32_t max_len) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || max_len <= 0) return MLA_EINVAL;
+  return decode_plan(dims, batch, max_len).split_len;
+}
+
+int mla_decode_partials(const mla_dims* dims, const void* q_lat, const void* q_pe,
+                        const void* cache, const int64_t* seq_start, const int32_t* seq_len,
+                        int32_t batch, int32_t max_len, int32_t n_split, float* part_o,
+                        float* part_ml, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || n_split < 1) return MLA_EINVAL;
+  if (batch == 0) return MLA_OK;
+  if (max_len <= 0) return MLA_EINVAL;
+  if (!ptr_ok(q_lat) || !ptr_ok(q_pe) || !ptr_ok(cache) || !ptr_ok(seq_start) ||
+      !ptr_ok(seq_len) || !ptr_ok(part_o) || !ptr_ok(part_ml))
+    return MLA_EINVAL;
+  const DecodePlan p = decode_plan(dims, batch, max_len, n_split);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AttnShape sh = shape_of(dims);
+  if (p.mfma)
+    mla::decode_mfma(sh, q_lat, q_pe, cache, seq_start, seq_len, batch, p.n_split, p.split_len,
+                     part_o, part_ml, nullptr, s);
+  else
+    mla::attend_generic(dims->dtype, sh, q_lat, q_pe, cache, seq_start, seq_len, nullptr, batch,
+                        batch, p.n_split, p.split_len, part_o, part_ml, nullptr, s);
   return launch_status();
 }
 

@@ -38,10 +38,18 @@ struct SkinnyArgs {
   void* C;
   int64_t sCz, sCm, sPs;     // C[s][z][m][n]
   int M, N, K, Z, splits, k_per_split;
+  // merged A (gemm_skinny_merged): A[z][m][k] = Σ_j w_j · A[z][m][k + j*sAs] with
+  // softmax-merge weights from ml[(m*n_merge + j)*ml_heads + z] = (max, sum)
+  int64_t sAs;
+  const float* ml;
+  int ml_heads, n_merge;
 };
-int skinny_splits(int N, int Z, int K);
+int skinny_splits(int M, int N, int Z, int K);
 void gemm_skinny(SkinnyArgs sa, bool a_f32, bool out_bf16, hipStream_t s);
 void sum_split_slices(float* c, int splits, int64_t sps, int M, int N, int64_t ldc, hipStream_t s);
+// fp32 A merged from n_merge <= skinny_max_merge() split-softmax partials, one K piece
+int skinny_max_merge();
+void gemm_skinny_merged(SkinnyArgs sa, int n_merge, bool out_bf16, hipStream_t s);
 
 // Cache rows from the fp32 projections in `proj` ([T, r + G*d_rope], row stride ld):
 // optional RMSNorm over the latent, RoPE on each rotary-key group, cast, scatter to slots.

@@ -3,6 +3,8 @@
 //    each rotary-key group at the token's position, cast, store to its slot;
 //  - query rotary part: RoPE of q_pe per head.
 // RoPE pairs dims (j, j + d/2), angle p·θ^(-2j/d) formed in double.
+#include <algorithm>
+
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -28,8 +30,13 @@ __global__ __launch_bounds__(256) void cache_rows_kernel(const float* __restrict
   const int row_w = r + n_groups * d_rope;
   const int half = d_rope / 2;
   for (int i = threadIdx.x; i < row_w; i += blockDim.x) {
+    // all slices' loads issued before the sum (splits <= 16)
+    float part[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) part[p] = p < splits ? proj[p * sps + t * ld + i] : 0.f;
     float v = 0.f;
-    for (int p = 0; p < splits; ++p) v += proj[p * sps + t * ld + i];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) v += part[p];
     row[i] = v;
   }
   const int32_t pos = positions[t];
@@ -71,7 +78,12 @@ __global__ __launch_bounds__(256) void query_rope_kernel(const float* __restrict
   __syncthreads();
   const float* src = proj + t * ld;
   T* dst = q_pe + t * static_cast<int64_t>(n_heads) * d_rope;
-  for (int i = threadIdx.x; i < n_heads * half; i += blockDim.x) {
+  // blockIdx.y picks a slice of the (head, pair) items so one token's heads
+  // spread over several workgroups
+  const int items = n_heads * half;
+  const int per = (items + gridDim.y - 1) / gridDim.y;
+  const int lo = blockIdx.y * per, hi = min(items, lo + per);
+  for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) {
     const int h = i / half, j = i % half;
     const float a = src[h * d_rope + j], b = src[h * d_rope + j + half];
     Elem<T>::store(dst, h * d_rope + j, a * cs[j] - b * sn[j]);
@@ -101,7 +113,8 @@ void finalize_query_rope(int dtype, const float* proj, int64_t ld, void* q_pe,
                          const int32_t* positions, int64_t n_tokens, int n_heads, int d_rope,
                          double theta, hipStream_t s) {
   if (n_tokens <= 0) return;
-  dim3 grid(static_cast<unsigned>(n_tokens));
+  const int items = n_heads * (d_rope / 2);
+  dim3 grid(static_cast<unsigned>(n_tokens), static_cast<unsigned>(std::max(1, std::min(16, items / 256))));
   if (dtype == kF32)
     hipLaunchKernelGGL(query_rope_kernel<float>, grid, dim3(256), 0, s, proj, ld,
                        static_cast<float*>(q_pe), positions, n_heads, d_rope, theta);

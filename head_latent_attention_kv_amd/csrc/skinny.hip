@@ -22,42 +22,53 @@ namespace mla {
 
 namespace {
 
-constexpr int kBN = 64;     // output columns per workgroup
+constexpr int kWideNB = 6;  // 16-column blocks per workgroup of the wide bf16 variant
 constexpr int kKS = 32;     // k per MFMA step
-constexpr int kDepth = 2;   // k-steps of loads in flight per wave
+constexpr int kMaxMerge = 8;
 
-template <bool A_F32>
-__device__ __forceinline__ void load_a(const void* A, int64_t off, bool ok, bf16x8& hi, bf16x8& lo) {
-  if (!ok) {
-    hi = lo = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-    return;
-  }
-  if constexpr (A_F32) {
-    // fp32 operand as hi = bf16(a) and lo = bf16(a - hi): hi·w + lo·w keeps ~16 bits of a
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(A) + off);
-    const float4 a = p[0], b = p[1];
-    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t h[4], l[4];
+// A operand kinds
+constexpr int kABf16 = 0;   // bf16 rows
+constexpr int kAF32 = 1;    // fp32 rows, split hi/lo into two bf16 MFMA operands
+constexpr int kAMerge = 2;  // fp32 rows formed as Σ_s w[m][s]·A_s (split-softmax merge)
+
+// Raw A data of one lane for one k-step and one 16-row block: 8 consecutive k.
+template <int AK, int NS>
+struct ARaw;
+template <int NS>
+struct ARaw<kABf16, NS> {
+  uint4 v;
+};
+template <int NS>
+struct ARaw<kAF32, NS> {
+  float4 v[2];
+};
+template <int NS>
+struct ARaw<kAMerge, NS> {
+  float4 v[NS][2];
+};
+
+__device__ __forceinline__ void split_hi_lo(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  // hi = bf16(x), lo = bf16(x - hi): hi·w + lo·w carries ~16 bits of x
+  uint32_t h[4], l[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-      const float h0 = bf16_to_f32(static_cast<bf16_t>(h[i] & 0xFFFF));
-      const float h1 = bf16_to_f32(static_cast<bf16_t>(h[i] >> 16));
-      l[i] = pack_bf16x2(v[2 * i] - h0, v[2 * i + 1] - h1);
-    }
-    hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
-    lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
-  } else {
-    hi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(A) + off));
+  for (int i = 0; i < 4; ++i) {
+    h[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    const float h0 = __uint_as_float(h[i] << 16);
+    const float h1 = __uint_as_float(h[i] & 0xFFFF0000u);
+    l[i] = pack_bf16x2(x[2 * i] - h0, x[2 * i + 1] - h1);
   }
+  hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
 }
 
-template <int MB, bool A_F32, typename OutT>
-__global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs sa) {
-  __shared__ float red[3][MB * 4][4][64];  // partial tiles of waves 1..3
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int MB, int NB, int AK, int NS, int DEPTH, int MINB, typename OutT>
+__global__ __launch_bounds__(256, MINB) void skinny_kernel(SkinnyArgs sa) {
+  __shared__ float red[3][MB * NB][4][64];  // partial tiles of waves 1..3
+  __shared__ float wmerge[AK == kAMerge ? 64 * NS : 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * kBN;
+  const int n0 = blockIdx.x * 16 * NB;
   const int z = blockIdx.y;
   const int split = blockIdx.z;
   const int k_lo = split * sa.k_per_split;
@@ -65,11 +76,33 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs sa) {
   const int64_t a_base = static_cast<int64_t>(z) * sa.sAz;
   const int64_t b_base = static_cast<int64_t>(z) * sa.sBz;
 
-  f32x4 acc[MB][4];
+  if constexpr (AK == kAMerge) {
+    // w[m][s] = 2^(m_s - max_s m_s) / Σ_s 2^(m_s - max) l_s   for this workgroup's head z
+    if (tid < sa.M) {
+      const int ns = min(sa.n_merge, NS);
+      const float* ml = sa.ml + (static_cast<int64_t>(tid) * ns * sa.ml_heads + z) * 2;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+        if (j < ns) mx = fmaxf(mx, ml[j * sa.ml_heads * 2]);
+      float den = 0.f, e[NS];
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        e[j] = j < ns ? exp2f(ml[j * sa.ml_heads * 2] - mx) : 0.f;
+        if (j < ns) den += e[j] * ml[j * sa.ml_heads * 2 + 1];
+      }
+      const float inv = 1.f / den;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) wmerge[tid * NS + j] = e[j] * inv;
+    }
+    __syncthreads();
+  }
+
+  f32x4 acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // contiguous k-steps of this wave
   const int n_steps = max(0, (k_hi - k_lo + kKS - 1) / kKS);  // 0 for an empty trailing piece
@@ -77,59 +110,114 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs sa) {
   const int s_lo = wave * per + min(wave, extra);
   const int my_steps = per + (wave < extra ? 1 : 0);
 
-  // weight row pointer of each n-block this lane feeds
-  const bf16_t* wrow[4];
-  bool nok[4];
+  // Loads are unconditional: rows m >= M and columns n >= N read a clamped
+  // (valid) row and only feed outputs that are never stored; k-groups past the
+  // end of the K piece (only in a wave's last step) are zeroed at use.
+  const bf16_t* wrow[NB];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + 16 * j + l16;
-    nok[j] = n < sa.N;
-    const bf16_t* base = n < sa.N0 ? sa.B0 + static_cast<int64_t>(n) * sa.sBo
-                                   : sa.B1 + static_cast<int64_t>(n - sa.N0) * sa.sBo;
+  for (int j = 0; j < NB; ++j) {
+    const int n = min(n0 + 16 * j + l16, sa.N - 1);
+    const uint16_t* base = n < sa.N0 ? sa.B0 + static_cast<int64_t>(n) * sa.sBo
+                                     : sa.B1 + static_cast<int64_t>(n - sa.N0) * sa.sBo;
     wrow[j] = base + b_base;
   }
+  int64_t arow[MB];
+  float wm[MB][AK == kAMerge ? NS : 1];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int m = min(16 * i + l16, sa.M - 1);
+    arow[i] = a_base + static_cast<int64_t>(m) * sa.sAm;
+    if constexpr (AK == kAMerge) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) wm[i][j] = wmerge[m * NS + j];
+    }
+  }
 
-  bf16x8 ah[kDepth][MB], al[kDepth][MB], bw[kDepth][4];
+  // loads in flight: DEPTH k-steps of raw A and B fragments
+  ARaw<AK, NS> ar[DEPTH][MB];
+  uint4 bw[DEPTH][NB];
+  bool kin[DEPTH];
+  // step s of this wave; steps past its range re-read its last step's
+  // addresses (cache hits) and are zeroed at use, so the loop has no branches
   auto fetch = [&](int s, int slot) {
-    const int k = k_lo + kKS * (s_lo + s) + 8 * lg;
-    const bool kok = k < k_hi;  // K is a multiple of 8
+    const int s_eff = max(0, min(s, my_steps - 1));
+    const int k_raw = k_lo + kKS * (s_lo + s_eff) + 8 * lg;
+    kin[slot] = s < my_steps && k_raw < k_hi;  // K is a multiple of 8
+    const int k = min(kin[slot] ? k_raw : k_lo + kKS * (s_lo + s_eff), sa.K - 8);
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
-      const int m = 16 * i + l16;
-      load_a<A_F32>(sa.A, a_base + static_cast<int64_t>(m) * sa.sAm + k, kok && m < sa.M, ah[slot][i],
-                    al[slot][i]);
+      const int64_t off = arow[i] + k;
+      if constexpr (AK == kABf16) {
+        ar[slot][i].v = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(sa.A) + off);
+      } else if constexpr (AK == kAF32) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(sa.A) + off);
+        ar[slot][i].v[0] = p[0];
+        ar[slot][i].v[1] = p[1];
+      } else {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          const int jj = j < sa.n_merge ? j : 0;
+          const float4* p =
+              reinterpret_cast<const float4*>(static_cast<const float*>(sa.A) + off + jj * sa.sAs);
+          ar[slot][i].v[j][0] = p[0];
+          ar[slot][i].v[j][1] = p[1];
+        }
+      }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      bw[slot][j] = (kok && nok[j]) ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(wrow[j] + k))
-                                    : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    for (int j = 0; j < NB; ++j) bw[slot][j] = *reinterpret_cast<const uint4*>(wrow[j] + k);
+  };
+
+  auto consume = [&](int slot) {
+    bf16x8 ah[MB], al[MB], bf[NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      if constexpr (AK == kABf16) {
+        const uint4 v = ar[slot][i].v;
+        ah[i] = __builtin_bit_cast(bf16x8, kin[slot] ? v : make_uint4(0, 0, 0, 0));
+      } else {
+        float x[8];
+        if constexpr (AK == kAF32) {
+          const float4 a = ar[slot][i].v[0], b = ar[slot][i].v[1];
+          x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = 0.f;
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            const float4 a = ar[slot][i].v[j][0], b = ar[slot][i].v[j][1];
+            const float w = wm[i][j];
+            x[0] = fmaf(w, a.x, x[0]); x[1] = fmaf(w, a.y, x[1]); x[2] = fmaf(w, a.z, x[2]);
+            x[3] = fmaf(w, a.w, x[3]); x[4] = fmaf(w, b.x, x[4]); x[5] = fmaf(w, b.y, x[5]);
+            x[6] = fmaf(w, b.z, x[6]); x[7] = fmaf(w, b.w, x[7]);
+          }
+        }
+        if (!kin[slot]) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        }
+        split_hi_lo(x, ah[i], al[i]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bf[j] = __builtin_bit_cast(bf16x8, bw[slot][j]);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bf[j], acc[i][j], 0, 0, 0);
+        if constexpr (AK != kABf16)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], bf[j], acc[i][j], 0, 0, 0);
+      }
   };
 
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d)
-    if (d < my_steps) fetch(d, d);
-  for (int s = 0; s < my_steps; s += kDepth) {
+  for (int d = 0; d < DEPTH; ++d) fetch(d, d);
+  for (int s = 0; s < my_steps; s += DEPTH) {
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      if (s + d < my_steps) {
-        bf16x8 a_h[MB], a_l[MB], b_w[4];
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-          a_h[i] = ah[d][i];
-          a_l[i] = al[d][i];
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) b_w[j] = bw[d][j];
-        if (s + d + kDepth < my_steps) fetch(s + d + kDepth, d);
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_h[i], b_w[j], acc[i][j], 0, 0, 0);
-            if constexpr (A_F32)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_l[i], b_w[j], acc[i][j], 0, 0, 0);
-          }
-      }
+    for (int d = 0; d < DEPTH; ++d) {
+      consume(d);
+      fetch(s + d + DEPTH, d);
     }
   }
 
@@ -138,26 +226,26 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs sa) {
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[wave - 1][i * 4 + j][e][lane] = acc[i][j][e];
+        for (int e = 0; e < 4; ++e) red[wave - 1][i * NB + j][e][lane] = acc[i][j][e];
   }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        acc[i][j][e] += red[0][i * 4 + j][e][lane] + red[1][i * 4 + j][e][lane] + red[2][i * 4 + j][e][lane];
+        acc[i][j][e] += red[0][i * NB + j][e][lane] + red[1][i * NB + j][e][lane] + red[2][i * NB + j][e][lane];
 
   // lane holds C[m = 16i + 4lg + e][n = n0 + 16j + l16]
   OutT* C = static_cast<OutT*>(sa.C) + static_cast<int64_t>(split) * sa.sPs + static_cast<int64_t>(z) * sa.sCz;
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NB; ++j) {
       const int n = n0 + 16 * j + l16;
       if (n >= sa.N) continue;
 #pragma unroll
@@ -166,24 +254,6 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs sa) {
         if (m < sa.M) Elem<OutT>::store(C, static_cast<int64_t>(m) * sa.sCm + n, acc[i][j][e]);
       }
     }
-}
-
-template <int MB, bool A_F32>
-void launch_mb(const SkinnyArgs& sa, dim3 grid, bool out_bf16, hipStream_t s) {
-  if (out_bf16)
-    hipLaunchKernelGGL((skinny_kernel<MB, A_F32, bf16_t>), grid, dim3(256), 0, s, sa);
-  else
-    hipLaunchKernelGGL((skinny_kernel<MB, A_F32, float>), grid, dim3(256), 0, s, sa);
-}
-
-template <bool A_F32>
-void launch_a(const SkinnyArgs& sa, dim3 grid, int mb, bool out_bf16, hipStream_t s) {
-  switch (mb) {
-    case 1: launch_mb<1, A_F32>(sa, grid, out_bf16, s); break;
-    case 2: launch_mb<2, A_F32>(sa, grid, out_bf16, s); break;
-    case 3: launch_mb<3, A_F32>(sa, grid, out_bf16, s); break;
-    default: launch_mb<4, A_F32>(sa, grid, out_bf16, s); break;
-  }
 }
 
 }  // namespace
@@ -199,19 +269,41 @@ __global__ __launch_bounds__(256) void sum_slices_kernel(float* __restrict__ c, 
   const int64_t total = static_cast<int64_t>(M) * N;
   for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < total; i += gridDim.x * 256LL) {
     const int64_t off = (i / N) * ldc + i % N;
-    float v = c[off];
-    for (int p = 1; p < splits; ++p) v += c[p * sps + off];
+    float part[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) part[p] = p < splits ? c[p * sps + off] : 0.f;
+    float v = 0.f;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) v += part[p];
     c[off] = v;
   }
 }
 }  // namespace
 
-int skinny_splits(int N, int Z, int K) {
-  // enough workgroups for 256 compute units, at least 512 k per split; the value
-  // returned is the number of K pieces the kernel actually uses
-  const int tiles = (N + kBN - 1) / kBN * Z;
-  int splits = (256 + tiles - 1) / tiles;
-  splits = std::max(1, std::min(splits, std::max(1, K / 512)));
+namespace {
+// bf16 variant choice, shared by the split planner and the launcher:
+//  wide   = 96 columns per workgroup, one workgroup per CU (many column tiles,
+//           A re-read per tile 2/3 of the weight bytes);
+//  narrow = 32 columns, two per CU, deeper prefetch (few column tiles, where
+//           K splits supply the parallelism);
+//  else   = 64 columns, two per CU (up to 32 token rows).
+enum class Bf16Variant { kWide, kNarrow, kBase };
+Bf16Variant bf16_variant(int M, int N, int Z) {
+  if (M <= 32) return Bf16Variant::kBase;
+  return (N + 16 * kWideNB - 1) / (16 * kWideNB) * Z >= 128 ? Bf16Variant::kWide : Bf16Variant::kNarrow;
+}
+}  // namespace
+
+int skinny_splits(int M, int N, int Z, int K) {
+  // enough workgroups to fill every slot (one or two per compute unit, as the
+  // bf16 launch picks), at least 256 k per split and at most 16 slices; the
+  // value returned is the number of K pieces the kernel uses
+  const Bf16Variant v = bf16_variant(M, N, Z);
+  const int cols = v == Bf16Variant::kWide ? 16 * kWideNB : v == Bf16Variant::kNarrow ? 32 : 64;
+  const int slots = v == Bf16Variant::kWide ? 256 : 512;
+  const int tiles = (N + cols - 1) / cols * Z;
+  int splits = (slots + tiles - 1) / tiles;
+  splits = std::max(1, std::min({splits, std::max(1, K / 256), 16}));
   const int kps = k_per_split(K, splits);
   return (K + kps - 1) / kps;
 }
@@ -219,19 +311,69 @@ int skinny_splits(int N, int Z, int K) {
 void sum_split_slices(float* c, int splits, int64_t sps, int M, int N, int64_t ldc, hipStream_t s) {
   if (splits <= 1 || M <= 0 || N <= 0) return;
   const int64_t total = static_cast<int64_t>(M) * N;
-  const int blocks = static_cast<int>(std::min<int64_t>(1024, (total + 255) / 256));
+  const int blocks = static_cast<int>(std::min<int64_t>(2048, (total + 255) / 256));
   hipLaunchKernelGGL(sum_slices_kernel, dim3(blocks), dim3(256), 0, s, c, splits, sps, M, N, ldc);
 }
 
-void gemm_skinny(SkinnyArgs sa, bool a_f32, bool out_bf16, hipStream_t s) {
+namespace {
+
+template <int MB, int NB, int AK, int NS, int DEPTH, int MINB>
+void launch_out(const SkinnyArgs& sa, bool out_bf16, hipStream_t s) {
+  // every one of the `splits` slices is written (an empty K piece writes zeros)
+  dim3 grid((sa.N + 16 * NB - 1) / (16 * NB), sa.Z, sa.splits);
+  if (out_bf16)
+    hipLaunchKernelGGL((skinny_kernel<MB, NB, AK, NS, DEPTH, MINB, bf16_t>), grid, dim3(256), 0, s, sa);
+  else
+    hipLaunchKernelGGL((skinny_kernel<MB, NB, AK, NS, DEPTH, MINB, float>), grid, dim3(256), 0, s, sa);
+}
+
+template <int MB>
+void launch_kind(const SkinnyArgs& sa, int kind, int ns, bool out_bf16, hipStream_t s) {
+  if (kind == kABf16) {
+    const Bf16Variant v = bf16_variant(sa.M, sa.N, sa.Z);
+    if constexpr (MB >= 3) {
+      if (v == Bf16Variant::kWide) launch_out<MB, kWideNB, kABf16, 1, 3, 1>(sa, out_bf16, s);
+      else launch_out<MB, 2, kABf16, 1, 4, 2>(sa, out_bf16, s);
+    } else {
+      launch_out<MB, 4, kABf16, 1, 3, 2>(sa, out_bf16, s);
+    }
+  } else if (kind == kAF32 || ns <= 1) {
+    launch_out<MB, 4, kAF32, 1, 2, 1>(sa, out_bf16, s);
+  } else {
+    switch (ns) {
+      case 2: launch_out<MB, 4, kAMerge, 2, 2, 1>(sa, out_bf16, s); break;
+      case 3: launch_out<MB, 4, kAMerge, 3, 1, 1>(sa, out_bf16, s); break;
+      case 4: launch_out<MB, 4, kAMerge, 4, 1, 1>(sa, out_bf16, s); break;
+      default: launch_out<MB, 4, kAMerge, kMaxMerge, 1, 1>(sa, out_bf16, s); break;
+    }
+  }
+}
+
+void launch(const SkinnyArgs& sa, int kind, int ns, bool out_bf16, hipStream_t s) {
   if (sa.M <= 0 || sa.N <= 0 || sa.Z <= 0) return;
+  switch ((sa.M + 15) / 16) {
+    case 1: launch_kind<1>(sa, kind, ns, out_bf16, s); break;
+    case 2: launch_kind<2>(sa, kind, ns, out_bf16, s); break;
+    case 3: launch_kind<3>(sa, kind, ns, out_bf16, s); break;
+    default: launch_kind<4>(sa, kind, ns, out_bf16, s); break;
+  }
+}
+
+}  // namespace
+
+void gemm_skinny(SkinnyArgs sa, bool a_f32, bool out_bf16, hipStream_t s) {
   if (sa.splits < 1) sa.splits = 1;
   sa.k_per_split = k_per_split(sa.K, sa.splits);
-  const int mb = (sa.M + 15) / 16;
-  // every one of the `splits` slices is written (an empty K piece writes zeros)
-  dim3 grid((sa.N + kBN - 1) / kBN, sa.Z, sa.splits);
-  if (a_f32) launch_a<true>(sa, grid, mb, out_bf16, s);
-  else launch_a<false>(sa, grid, mb, out_bf16, s);
+  launch(sa, a_f32 ? kAF32 : kABf16, 1, out_bf16, s);
+}
+
+int skinny_max_merge() { return kMaxMerge; }
+
+void gemm_skinny_merged(SkinnyArgs sa, int n_merge, bool out_bf16, hipStream_t s) {
+  sa.n_merge = n_merge;
+  sa.splits = 1;
+  sa.k_per_split = k_per_split(sa.K, 1);
+  launch(sa, n_merge <= 1 ? kAF32 : kAMerge, n_merge, out_bf16, s);
 }
 
 }  // namespace mla

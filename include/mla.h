@@ -144,6 +144,33 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_pe, const 
                const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
                void* stream);
 
+/* Number of context splits mla_decode uses for this batch (>= 1), or a negative
+ * mla_status.  Split j of a sequence covers its rows [j*L, min(n, (j+1)*L)) with
+ * L = mla_decode_split_rows(dims, batch, max_len); trailing splits may be empty. */
+int32_t mla_decode_splits(const mla_dims* dims, int32_t batch, int32_t max_len);
+int32_t mla_decode_split_rows(const mla_dims* dims, int32_t batch, int32_t max_len);
+
+/* The attention of mla_decode without its merge and W_UV: per (sequence, split,
+ * head) the partial softmax state of the split's rows, for callers that combine
+ * partial results themselves (one sequence's rows spread over several devices,
+ * or a projection fused downstream).  With s_l the score of row l (as in
+ * mla_decode) and u_l = s_l·log2(e):
+ *   part_ml[b,j,h] = (m, Σ_l 2^(u_l - m))      m: a per-split reference, base 2
+ *   part_o[b,j,h,:] = Σ_l 2^(u_l - m)·c[l,:]
+ * so o_ = Σ_j 2^(m_j - M)·part_o_j / Σ_j 2^(m_j - M)·l_j for any M.  An empty
+ * split gives m = -inf, l = 0, part_o = 0.  m is not necessarily the true max:
+ * the kernels may use any reference that keeps 2^(u_l - m) finite.
+ * Source: split softmax merge of the MLA principle page's attention (eq. (4)
+ * computed per split of the context), the exchange a multi-device split needs.
+ *   q_lat, q_pe, cache, seq_start, seq_len, max_len: as mla_decode
+ *   n_split: >= 1; splits of L = ceil(max_len / n_split) rounded up to 64 rows
+ *   part_o device fp32 out [batch, n_split, H, r]; part_ml device fp32 out [batch, n_split, H, 2]
+ * Needs no workspace; batch == 0 is a no-op. */
+int mla_decode_partials(const mla_dims* dims, const void* q_lat, const void* q_pe,
+                        const void* cache, const int64_t* seq_start, const int32_t* seq_len,
+                        int32_t batch, int32_t max_len, int32_t n_split, float* part_o,
+                        float* part_ml, void* stream);
+
 /* Causal prefill over packed sequences.  Tokens cu_seqlens[b] .. cu_seqlens[b+1]-1
  * form sequence b at positions 0..n_b-1; token t's own cache row is row t, and it
  * attends to rows cu_seqlens[b] .. t (same formula as mla_decode per token).

@@ -87,7 +87,20 @@ def test_calls_reject_bad_arguments_before_any_launch():
     assert lib.mla_decode(ctypes.byref(d), null, null, null, null, null, 0, 100, null, null, null, 0, null) == abi.MLA_OK
     assert lib.mla_write_cache(ctypes.byref(d), null, null, null, null, null, 0, null, 0, null, 0, null) == abi.MLA_OK
     assert lib.mla_decode(None, null, null, null, null, null, 4, 100, null, null, null, 0, null) == abi.MLA_EINVAL
+    assert lib.mla_decode_partials(ctypes.byref(d), null, null, null, null, null, 4, 100, 2, null, null, null) == abi.MLA_EINVAL
+    assert lib.mla_decode_partials(ctypes.byref(d), null, null, null, null, null, 4, 100, 0, null, null, null) == abi.MLA_EINVAL
+    assert lib.mla_decode_partials(ctypes.byref(d), null, null, null, null, null, 0, 100, 2, null, null, null) == abi.MLA_OK
     assert lib.mla_strerror(abi.MLA_EWORKSPACE) == b"workspace too small"
+
+
+def test_decode_split_queries():
+    abi, lib = _lib()
+    d = abi.dims_of(I.CONFIGS["deepseek_v2_decode"])
+    ns = lib.mla_decode_splits(ctypes.byref(d), 64, 8192)
+    rows = lib.mla_decode_split_rows(ctypes.byref(d), 64, 8192)
+    assert ns >= 1 and rows % 64 == 0 and ns * rows >= 8192 and (ns - 1) * rows < 8192
+    assert lib.mla_decode_splits(ctypes.byref(d), 64, 0) == abi.MLA_EINVAL
+    assert lib.mla_decode_splits(None, 64, 10) == abi.MLA_EINVAL
 
 
 def test_workspace_sizes_cover_the_plan():

@@ -120,6 +120,52 @@ def test_decode_reduced(torch, name, lengths):
         assert v <= Hh.TOL[cfg.dtype], (k, v)
 
 
+@pytest.mark.parametrize("n_split", [1, 3, None])
+def test_decode_partials_merge(torch, n_split):
+    """mla_decode_partials: the host merges the per-split partials by their stated
+    definition (float64), applies W_UV, and must match the oracle's attention on the
+    GPU-written rows; splits past a short sequence must come back empty."""
+    import head_latent_attention_kv_amd as M
+    cfg = I.CONFIGS["deepseek_v2_decode"]
+    lengths = [1, 300, 2048]
+    _print_case("decode_partials", cfg=cfg.name, lengths=lengths, n_split=n_split)
+    layer = Hh.make_layer(cfg)
+    run = Hh.build_decode(layer, np.array(lengths))
+    B, H, r = len(lengths), cfg.n_heads, cfg.rank
+    max_len = int(max(lengths))
+    ns = M.mla_decode_splits(layer.dims, B, max_len) if n_split is None else n_split
+    split_rows = (-(-max_len // ns) + 63) // 64 * 64
+    part_o = torch.full((B, ns, H, r), float("nan"), dtype=torch.float32, device="cuda")
+    part_ml = torch.full((B, ns, H, 2), float("nan"), dtype=torch.float32, device="cuda")
+    seq_start = torch.from_numpy(run.starts).cuda()
+    seq_len = torch.from_numpy(run.lengths.astype(np.int32)).cuda()
+    M.mla_decode_partials(layer.dims, run.q_lat, run.q_pe, run.cache, seq_start, seq_len, max_len, ns,
+                          part_o, part_ml)
+    torch.cuda.synchronize()
+    po = Hh.to_host(part_o).astype(np.float64)
+    pml = Hh.to_host(part_ml).astype(np.float64)
+    assert np.isfinite(po).all() and not np.isnan(pml).any()
+    cache_h = Hh.to_host(run.cache)
+    w = layer.w_host
+    err = 0.0
+    for b, n in enumerate(run.lengths):
+        n = int(n)
+        empty = [j for j in range(ns) if j * split_rows >= n]
+        for j in empty:
+            assert np.all(pml[b, j, :, 0] == -np.inf) and np.all(pml[b, j, :, 1] == 0), (b, j)
+            assert np.all(po[b, j] == 0), (b, j)
+        m = pml[b, :, :, 0]                                   # [ns, H]
+        mx = m.max(axis=0)
+        wj = np.where(np.isneginf(m), 0.0, np.exp2(m - mx))
+        o_lat = (wj[:, :, None] * po[b]).sum(0) / (wj * pml[b, :, :, 1]).sum(0)[:, None]
+        out = np.einsum("hdc,hc->hd", w["w_uv"].astype(np.float64), o_lat)
+        ref = Hh.oracle_decode_rows(cfg, w, None, run.x_query[b], n,
+                                    cache_rows=cache_h[run.starts[b]:run.starts[b] + n])
+        err = max(err, Hh.rel_err_rows(out, ref))
+    print(f"partials n_split={ns}: merged attention max rel err {err:.3e}")
+    assert err <= Hh.TOL[cfg.dtype]
+
+
 def test_decode_deterministic(torch):
     cfg = I.small_variant(I.CONFIGS["deepseek_v2_decode"], d_model=512)
     _print_case("decode_deterministic")
