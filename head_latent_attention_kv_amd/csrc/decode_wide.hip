@@ -1,0 +1,400 @@
+// bf16 MFMA decode for the wide-head shape: H = 128 query heads sharing one
+// latent cache row of r = 512 latent + 64 rotary dims (one rotary key).
+//
+// The absorbed score of every head reads the same cached row [c ; kr] and the
+// latent-space PV reads the same c (MLA principle page, section on matrix
+// absorption, eqs. (4)-(5)), so one workgroup takes ALL heads of one
+// (sequence, context split): each cache tile crosses HBM -> LDS once per CU.
+//
+// Workgroup = 4 wave64s, one per SIMD, each with the whole 512-entry register
+// file.  Wave w owns heads [32w, 32w+32): their Qᵀ for the split (144 registers
+// of bf16 MFMA operands) and their fp32 accumulators O over all 512 latent
+// columns (256 AGPRs), so a wave's softmax weights never leave its registers.
+// Tiles of 32 rows:
+//   - copies HBM -> LDS by global_load_lds_dwordx4 into 4 buffers (tiles t and
+//     t+1 in use, t+2 and t+3 in flight), stored without padding; the 16-byte
+//     chunks of a row are XOR-swizzled by (row / 2) within groups of eight, so
+//     the 16 rows one fragment read touches fall on distinct bank groups;
+//   - score: Sᵀ[32 rows x 32 heads], four 16x16 blocks of
+//     v_mfma_f32_16x16x32_bf16 over the whole row (K = 576), tile rows as the A
+//     operand from LDS, Qᵀ as the B operand from registers;
+//   - softmax against a per-head reference max of the split (the first tile's
+//     max, base 2, with 2^64 of headroom); a split whose later scores pass the
+//     headroom is redone with its true max, so O is never rescaled;
+//   - PV: O[32 heads x 512] += P[32 x 32]·C[32 x 512].  P is the A operand
+//     straight from the softmax registers: a lane holds rows 4lg..4lg+3 and
+//     16+4lg..16+4lg+3 of its head, and the K order of the product is taken to
+//     be exactly that, so the transposed C fragments (ds_read_b64_tr_b16) are
+//     read at those row bases.
+// Iteration t (one barrier, for the tile ring): score of tile t+1, then PV of
+// tile t with the softmax of tile t+1 issued between its MFMAs.
+// Output: normalised o_ (part_o null, one split) or the split's (m, l) and
+// unnormalised o_.
+#include <math.h>
+
+#include "lds_dma.h"
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kR = 512;              // latent width
+constexpr int kRW = 576;             // cache row width (r + d_rope, one rotary group)
+constexpr int kHeads = 128;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTL = 32;              // rows per tile
+constexpr int kStages = 4;
+constexpr int kRowBytes = kRW * 2;   // 1152
+constexpr int kRowChunks = kRowBytes / 16;           // 72
+constexpr int kTileBytes = kTL * kRowBytes;          // 36864
+constexpr int kDmaOps = kTileBytes / 1024;           // 36 one-KB copies per tile
+constexpr int kDmaPerWave = kDmaOps / kWaves;        // 9
+constexpr int kSteps = kRW / 32;                     // 18 score k-steps
+constexpr int kHW = kHeads / kWaves;                 // 32 heads per wave
+constexpr int kNB = kR / 16;                         // 32 PV column blocks
+constexpr int kLdsBytes = kStages * kTileBytes + kHeads * 4 + 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSlack = 64.f;
+#ifndef MLA_WIDE_SCORE_LA
+#define MLA_WIDE_SCORE_LA 2  // score k-steps of LDS fragments in flight
+#endif
+#ifndef MLA_WIDE_PV_LA
+#define MLA_WIDE_PV_LA 3     // PV column blocks of LDS fragments in flight
+#endif
+
+static_assert(kDmaOps % kWaves == 0, "tile copies split evenly over the waves");
+static_assert(kRowChunks % 8 == 0, "swizzle groups of eight chunks");
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+static_assert(3 * kDmaPerWave < 64, "vmcnt range");
+static_assert(kTL * kRowChunks <= 2304, "row-of-chunk division by multiplication is exact below 2304");
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// LDS chunk slot of 16-byte chunk c of tile row r (an involution for fixed r).
+__device__ __forceinline__ int swz(int c, int r) { return (c & ~7) | ((c ^ (r >> 1)) & 7); }
+
+
+template <int N>
+__device__ __forceinline__ void wait_tiles_after() {
+  wait_vmcnt<N * kDmaPerWave>();
+}
+
+__global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
+    const bf16_t* __restrict__ q_lat, const bf16_t* __restrict__ q_pe,
+    const bf16_t* __restrict__ cache, const int64_t* __restrict__ seq_start,
+    const int32_t* __restrict__ seq_len, int batch, float scale, int n_split, int split_len,
+    float* __restrict__ part_o, float* __restrict__ part_ml, float* __restrict__ o_out) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  float* xch = reinterpret_cast<float*>(smem + kStages * kTileBytes);  // [kHeads]
+  int* flags = reinterpret_cast<int*>(xch + kHeads);                   // [kWaves]
+
+  const int pair = blockIdx.x;
+  if (pair >= batch * n_split) return;
+  const int split = pair % n_split;
+  const int b = pair / n_split;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, lg = lane >> 4;
+
+  const int64_t row0 = seq_start[b];
+  const int len = seq_len[b];
+  const int l_begin = split * split_len;
+  const int l_end = min(len, l_begin + split_len);
+  const int n_tiles = l_end > l_begin ? (l_end - l_begin + kTL - 1) / kTL : 0;
+  const char* cache_b = reinterpret_cast<const char*>(cache + row0 * kRW);
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)smem));
+
+  // ---- tile copy: wave w issues 1 KB copies j = w + 4i; copy j fills LDS chunks
+  // [64j, 64j + 64) of the tile image.  LDS chunk L (row L / 72, slot L % 72)
+  // holds global chunk swz(slot, row) of the same row, which is L ^ ((row / 2) & 7)
+  // since rows are whole groups of eight chunks.  Rows past the split read a
+  // chunk of its last valid row instead.  The lane index is made opaque so the
+  // few offset instructions are redone per tile rather than held in registers.
+  auto issue_tile = [&](int t) {
+    const int tile_row = l_begin + t * kTL;
+    const int valid = min(kTL, l_end - tile_row);
+    const char* tbase = cache_b + static_cast<int64_t>(tile_row) * kRowBytes;
+    const uint32_t dst = lds0 + (t % kStages) * kTileBytes;
+    int ln = lane;
+    __asm__ volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      const int j = wave + kWaves * i;
+      const int L = j * 64 + ln;
+      const int r = (L * 1821) >> 17;  // L / 72 for L < 2304
+      const int g = r < valid ? (L ^ ((r >> 1) & 7)) : (valid - 1) * kRowChunks + (L & 63);
+      global_to_lds16(tbase, static_cast<uint32_t>(g * 16), __builtin_amdgcn_readfirstlane(dst + j * 1024));
+    }
+  };
+  auto wait_tile = [&](int t, int last_issued) {
+    switch (last_issued - t) {
+      case 0: wait_tiles_after<0>(); break;
+      case 1: wait_tiles_after<1>(); break;
+      case 2: wait_tiles_after<2>(); break;
+      default: wait_tiles_after<3>(); break;
+    }
+  };
+
+  // ---- Qᵀ of this wave's heads: B operand, lane = head 16hb + l16, k = 32ks + 8lg + e
+  bf16x8 qf[2][kSteps];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int head = wave * kHW + hb * 16 + l16;
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) {
+      const int k0 = ks * 32 + lg * 8;
+      const uint4 v = k0 < kR
+          ? *reinterpret_cast<const uint4*>(q_lat + (static_cast<int64_t>(b) * kHeads + head) * kR + k0)
+          : *reinterpret_cast<const uint4*>(q_pe + (static_cast<int64_t>(b) * kHeads + head) * (kRW - kR) +
+                                            (k0 - kR));
+      qf[hb][ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  const float qk_scale = scale * kLog2e;
+  // the Q loads must land before any tile copy is issued: the compiler's wait at
+  // their first use would otherwise also drain the copies in flight
+  wait_vmcnt<0>();
+
+  // score fragment addresses: row r = 16rb + l16, chunk 4ks + lg, whose slot in
+  // its group of eight is (4(ks & 1) + lg) ^ (r >> 1 & 7), the same for both rb
+  const int a_off0 = l16 * kRowBytes, a_off1 = (16 + l16) * kRowBytes;
+  const int x_even = (lg ^ (l16 >> 1)) & 7;
+  const int x_odd = ((4 + lg) ^ (l16 >> 1)) & 7;
+
+  float m_ref[2] = {-INFINITY, -INFINITY};   // reference max of heads 32w + 16hb + l16 (base 2)
+  float m_lane[2], l_lane[2];
+  bool over = false;                         // some score passed the reference's headroom
+  f32x4 o[2][kNB];                           // O[head block][column block]
+
+  // Scaled, masked scores of tile tt: s[rb][hb] = rows 16rb + 4lg + i, head
+  // 16hb + l16.  Fragments of k-step ks + 2 are read while the MFMAs of ks run;
+  // the scheduling barriers keep the compiler from hoisting more reads.
+  auto score = [&](int tt, f32x4 (&s)[2][2]) {
+    const unsigned char* tb = smem + (tt % kStages) * kTileBytes;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) s[rb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto frag = [&](int ks, int off) {
+      const int coff = (ks >> 1) * 128 + ((ks & 1) ? x_odd : x_even) * 16;
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tb + off + coff));
+    };
+    constexpr int kLA = MLA_WIDE_SCORE_LA;  // k-steps of fragments in flight
+    bf16x8 fa[kLA][2];
+#pragma unroll
+    for (int p = 0; p < kLA; ++p) {
+      fa[p][0] = frag(p, a_off0);
+      fa[p][1] = frag(p, a_off1);
+    }
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) {
+      const bf16x8 a0 = fa[ks % kLA][0], a1 = fa[ks % kLA][1];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        s[0][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[hb][ks], s[0][hb], 0, 0, 0);
+        s[1][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[hb][ks], s[1][hb], 0, 0, 0);
+      }
+      if (ks + kLA < kSteps) {
+        fa[ks % kLA][0] = frag(ks + kLA, a_off0);
+        fa[ks % kLA][1] = frag(ks + kLA, a_off1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int valid = min(kTL, l_end - (l_begin + tt * kTL));  // <= 0 past the last tile
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = s[rb][hb][i] * qk_scale;
+          s[rb][hb][i] = (rb * 16 + lg * 4 + i < valid) ? v : -INFINITY;
+        }
+  };
+
+  // softmax weights of head block hb: P = 2^(s - m_ref) as the bf16 A operand
+  // of the PV product, K order = [rows 4lg + i, then 16 + 4lg + i]
+  auto softmax = [&](const f32x4 (&s)[2][2], int hb) -> bf16x8 {
+    const float lim = m_ref[hb] + kSlack;
+    uint32_t w[4];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const f32x4 v = s[rb][hb];
+      m_lane[hb] = fmaxf(m_lane[hb], fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+      over = over || (v[0] > lim) || (v[1] > lim) || (v[2] > lim) || (v[3] > lim);
+      const float p0 = __builtin_amdgcn_exp2f(v[0] - m_ref[hb]);
+      const float p1 = __builtin_amdgcn_exp2f(v[1] - m_ref[hb]);
+      const float p2 = __builtin_amdgcn_exp2f(v[2] - m_ref[hb]);
+      const float p3 = __builtin_amdgcn_exp2f(v[3] - m_ref[hb]);
+      l_lane[hb] += (p0 + p1) + (p2 + p3);
+      w[2 * rb] = pack_bf16x2(p0, p1);
+      w[2 * rb + 1] = pack_bf16x2(p2, p3);
+    }
+    return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+  };
+
+  // transposed C fragment of column block nb: lane (l16, lg) gets column
+  // 16nb + l16 at rows 4lg + (0..3) (lo) and 16 + 4lg + (0..3) (hi); lane s of a
+  // 16-lane group supplies the address of row base + s/4, columns 4(s % 4)..+3
+  const int r_lo = lg * 4 + (l16 >> 2), r_hi = 16 + r_lo;
+  const int c_sub = (l16 & 1) * 8, c_half = (l16 & 3) >> 1;
+  auto cfrag = [&](const unsigned char* tb, int nb) {
+    const int chunk = nb * 2 + c_half;
+    const unsigned char* plo = tb + r_lo * kRowBytes + swz(chunk, r_lo) * 16 + c_sub;
+    const unsigned char* phi = tb + r_hi * kRowBytes + swz(chunk, r_hi) * 16 + c_sub;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(plo));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(phi));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // PV of tile tt with weights pa; the softmax of the next tile's scores s_next
+  // is issued between the products (into pn)
+  auto pv_softmax = [&](int tt, const bf16x8 (&pa)[2], const f32x4 (&s_next)[2][2], bf16x8 (&pn)[2]) {
+    const unsigned char* tb = smem + (tt % kStages) * kTileBytes;
+    constexpr int kLA = MLA_WIDE_PV_LA;
+    bf16x8 cf[kLA];
+#pragma unroll
+    for (int p = 0; p < kLA; ++p) cf[p] = cfrag(tb, p);
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      const bf16x8 b = cf[nb % kLA];
+      o[0][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0], b, o[0][nb], 0, 0, 0);
+      o[1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1], b, o[1][nb], 0, 0, 0);
+      if (nb + kLA < kNB) cf[nb % kLA] = cfrag(tb, nb + kLA);
+      if (nb == 8) pn[0] = softmax(s_next, 0);
+      if (nb == 20) pn[1] = softmax(s_next, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_lane[0] = m_lane[1] = -INFINITY;
+    l_lane[0] = l_lane[1] = 0.f;
+    over = false;
+
+#pragma unroll
+    for (int t = 0; t < kStages - 1; ++t)
+      if (t < n_tiles) issue_tile(t);
+    int issued = min(kStages - 1, n_tiles) - 1;
+
+    bf16x8 pa[2];  // softmax weights of tile t
+    if (n_tiles > 0) {
+      // prologue: tile 0; in the first pass its max sets the reference
+      wait_tile(0, issued);
+      lds_barrier();
+      f32x4 s0[2][2];
+      score(0, s0);
+      if (pass == 0) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          float mx = fmaxf(fmaxf(fmaxf(s0[0][hb][0], s0[0][hb][1]), fmaxf(s0[0][hb][2], s0[0][hb][3])),
+                           fmaxf(fmaxf(s0[1][hb][0], s0[1][hb][1]), fmaxf(s0[1][hb][2], s0[1][hb][3])));
+          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          m_ref[hb] = mx;
+        }
+      }
+      pa[0] = softmax(s0, 0);
+      pa[1] = softmax(s0, 1);
+    }
+
+    // iteration t: scores of tile t+1 (masked to nothing past the last tile),
+    // then PV of tile t with the softmax of tile t+1 between its MFMAs
+    for (int t = 0; t < n_tiles; ++t) {
+      if (t + 1 < n_tiles) wait_tile(t + 1, issued);
+      lds_barrier();  // tile t+1 visible; PV(t-1) done everywhere: buffer (t-1)%4 is free
+      if (t + kStages - 1 < n_tiles) {
+        issue_tile(t + kStages - 1);
+        issued = t + kStages - 1;
+      }
+      f32x4 s_next[2][2];
+      score(t + 1, s_next);
+      bf16x8 pn[2];
+      pv_softmax(t, pa, s_next, pn);
+      pa[0] = pn[0];
+      pa[1] = pn[1];
+    }
+    lds_barrier();
+    if (lane == 0) flags[wave] = __ballot(over) != 0 ? 1 : 0;
+    lds_barrier();
+    const bool scan = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
+    if (!scan) break;
+    // second pass with the split's true max per head
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      float mx = m_lane[hb];
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      m_ref[hb] = mx;
+    }
+    lds_barrier();  // every wave has read the flags before they are rewritten
+  }
+
+  // ---- epilogue: l per head -> LDS (the wave's own heads); O normalised or as a partial
+  const bool partials = part_o != nullptr;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    float l = l_lane[hb];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int head = wave * kHW + hb * 16 + l16;
+    if (lg == 0) {
+      xch[head] = l;
+      if (partials) {
+        const int64_t pidx = (static_cast<int64_t>(b) * n_split + split) * kHeads + head;
+        part_ml[pidx * 2 + 0] = m_ref[hb];
+        part_ml[pidx * 2 + 1] = l;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's row sums are in LDS (read back by the same wave)
+  __builtin_amdgcn_wave_barrier();
+  // lane holds O[head 32w + 16hb + 4lg + i][column 16nb + l16]
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = wave * kHW + hb * 16 + lg * 4 + i;
+      if (!partials) {
+        const float inv = 1.f / xch[h];
+        float* dst = o_out + (static_cast<int64_t>(b) * kHeads + h) * kR + l16;
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) dst[nb * 16] = o[hb][nb][i] * inv;
+      } else {
+        float* dst = part_o + ((static_cast<int64_t>(b) * n_split + split) * kHeads + h) * kR + l16;
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) dst[nb * 16] = o[hb][nb][i];
+      }
+    }
+}
+
+}  // namespace
+
+bool decode_wide_supported(const AttnShape& sh) {
+  return sh.H == kHeads && sh.G == 1 && sh.r == kR && sh.row_w == kRW;
+}
+
+void decode_wide(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
+                 const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split,
+                 int split_len, float* part_o, float* part_ml, float* o_out, hipStream_t s) {
+  if (batch <= 0) return;
+  hipFuncSetAttribute(reinterpret_cast<const void*>(decode_wide_kernel),
+                      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  hipLaunchKernelGGL(decode_wide_kernel, dim3(batch * n_split), dim3(kThreads), kLdsBytes, s,
+                     static_cast<const bf16_t*>(q_lat), static_cast<const bf16_t*>(q_pe),
+                     static_cast<const bf16_t*>(cache), seq_start, seq_len, batch, sh.scale, n_split,
+                     split_len, part_o, part_ml, o_out);
+}
+
+}  // namespace mla

@@ -65,6 +65,7 @@ AttnShape shape_of(const mla_dims* d) {
 // How a decode call is split.  Shared by mla_workspace_size and mla_decode so the
 // two always agree.
 struct DecodePlan {
+  bool wide;  // all heads per workgroup (decode_wide)
   bool mfma;
   int n_split;
   int split_len;
@@ -80,7 +81,8 @@ int split_rows(int L, int64_t ns) {
 DecodePlan decode_plan(const mla_dims* d, int32_t batch, int32_t max_len, int32_t force_splits = 0) {
   DecodePlan p{};
   AttnShape sh = shape_of(d);
-  p.mfma = d->dtype == MLA_BF16 && mla::decode_mfma_supported(sh);
+  p.wide = d->dtype == MLA_BF16 && mla::decode_wide_supported(sh);
+  p.mfma = !p.wide && d->dtype == MLA_BF16 && mla::decode_mfma_supported(sh);
   const int64_t B = std::max<int32_t>(batch, 0);
   const int L = std::max<int32_t>(max_len, 1);
   if (force_splits > 0) {
@@ -91,12 +93,14 @@ DecodePlan decode_plan(const mla_dims* d, int32_t batch, int32_t max_len, int32_
   // Workgroups per split: the MFMA kernel splits the heads of a sequence over
   // decode_mfma_head_groups() workgroups; the generic kernel into 8-head blocks.
   const int64_t per_split =
-      p.mfma ? B * mla::decode_mfma_head_groups(sh)
-             : B * ((sh.H + mla::generic_head_block() - 1) / mla::generic_head_block());
+      p.wide ? B
+      : p.mfma ? B * mla::decode_mfma_head_groups(sh)
+               : B * ((sh.H + mla::generic_head_block() - 1) / mla::generic_head_block());
   // Fill the 256 compute units of an MI355X once (the MFMA kernel's LDS
   // footprint allows one workgroup per CU at the large shapes), keeping
   // splits >= 256 rows.
-  const int64_t target = p.mfma ? mla::decode_mfma_blocks_per_cu(sh) * kCUs : 2 * kCUs;
+  const int64_t target =
+      p.wide ? kCUs : p.mfma ? mla::decode_mfma_blocks_per_cu(sh) * kCUs : 2 * kCUs;
   int64_t ns = per_split > 0 ? (target + per_split - 1) / per_split : 1;
   const int64_t max_ns = std::max<int64_t>(1, L / 256);
   ns = std::max<int64_t>(1, std::min<int64_t>(ns, max_ns));
@@ -361,7 +365,10 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_pe, const 
   float* o_lat = reinterpret_cast<float*>(ws);
   float* part_o = p.n_split > 1 ? reinterpret_cast<float*>(ws + p.o_bytes) : nullptr;
   float* part_ml = p.n_split > 1 ? reinterpret_cast<float*>(ws + p.o_bytes + p.part_o_bytes) : nullptr;
-  if (p.mfma)
+  if (p.wide)
+    mla::decode_wide(sh, q_lat, q_pe, cache, seq_start, seq_len, batch, p.n_split, p.split_len,
+                     part_o, part_ml, o_lat, s);
+  else if (p.mfma)
     mla::decode_mfma(sh, q_lat, q_pe, cache, seq_start, seq_len, batch, p.n_split, p.split_len,
                      part_o, part_ml, o_lat, s);
   else
@@ -425,7 +432,10 @@ int mla_decode_partials(const mla_dims* dims, const void* q_lat, const void* q_p
   const DecodePlan p = decode_plan(dims, batch, max_len, n_split);
   hipStream_t s = static_cast<hipStream_t>(stream);
   AttnShape sh = shape_of(dims);
-  if (p.mfma)
+  if (p.wide)
+    mla::decode_wide(sh, q_lat, q_pe, cache, seq_start, seq_len, batch, p.n_split, p.split_len,
+                     part_o, part_ml, nullptr, s);
+  else if (p.mfma)
     mla::decode_mfma(sh, q_lat, q_pe, cache, seq_start, seq_len, batch, p.n_split, p.split_len,
                      part_o, part_ml, nullptr, s);
   else

@@ -86,6 +86,13 @@ void merge_splits(const AttnShape& sh, int64_t n_q, int n_split, const float* pa
                   const float* part_ml, float* o_out, hipStream_t s);
 
 // bf16 MFMA decode kernel for the shapes it supports (see decode_mfma.hip).
+// All 128 heads of a (sequence, split) per workgroup, for H = 128, G = 1,
+// r = 512, d_rope = 64 (decode_wide.hip).
+bool decode_wide_supported(const AttnShape& sh);
+void decode_wide(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
+                 const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split,
+                 int split_len, float* part_o, float* part_ml, float* o_out, hipStream_t s);
+
 bool decode_mfma_supported(const AttnShape& sh);
 int decode_mfma_blocks_per_cu(const AttnShape& sh);  // workgroups one CU holds (LDS-limited)
 int decode_mfma_head_groups(const AttnShape& sh);    // workgroups that share one sequence split
