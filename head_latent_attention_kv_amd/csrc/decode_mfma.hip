@@ -219,9 +219,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
     const float p1 = __builtin_amdgcn_exp2f(sv[1] - m_ref);
     const float p2 = __builtin_amdgcn_exp2f(sv[2] - m_ref);
     const float p3 = __builtin_amdgcn_exp2f(sv[3] - m_ref);
-    l_lane += (p0 + p1) + (p2 + p3);
+    // the row sum takes the bf16 weights the PV product uses, so o_ is their exact average
+    const uint32_t w01 = pack_bf16x2(p0, p1), w23 = pack_bf16x2(p2, p3);
+    l_lane += bf16x2_sum(w01) + bf16x2_sum(w23);
     *reinterpret_cast<uint2*>(pbuf + (t & 1) * S::kPBytes + hloc * kPP + (mb_s * 16 + lg * 4) * 2) =
-        make_uint2(pack_bf16x2(p0, p1), pack_bf16x2(p2, p3));
+        make_uint2(w01, w23);
     return over;
   };
 

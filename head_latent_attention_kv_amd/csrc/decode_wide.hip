@@ -233,9 +233,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
       const float p1 = __builtin_amdgcn_exp2f(v[1] - m_ref[hb]);
       const float p2 = __builtin_amdgcn_exp2f(v[2] - m_ref[hb]);
       const float p3 = __builtin_amdgcn_exp2f(v[3] - m_ref[hb]);
-      l_lane[hb] += (p0 + p1) + (p2 + p3);
       w[2 * rb] = pack_bf16x2(p0, p1);
       w[2 * rb + 1] = pack_bf16x2(p2, p3);
+      // the row sum takes the bf16 weights the PV product uses
+      l_lane[hb] += bf16x2_sum(w[2 * rb]) + bf16x2_sum(w[2 * rb + 1]);
     }
     return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
   };

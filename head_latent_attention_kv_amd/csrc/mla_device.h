@@ -30,6 +30,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
+// Sum of the two bf16 values of a packed pair, as float.
+__device__ __forceinline__ float bf16x2_sum(uint32_t w) {
+  return __uint_as_float(w << 16) + __uint_as_float(w & 0xFFFF0000u);
+}
+
 // float -> bfloat16, round to nearest even.
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return static_cast<bf16_t>(pack_bf16x2(f, 0.f) & 0xFFFFu);

@@ -1,12 +1,346 @@
-// bf16 MFMA causal prefill kernel.
+// bf16 MFMA causal prefill over the latent cache (absorbed form).
+//
+// Every query head of a token reads the same cached rows [c ; kr] (MLA
+// principle page, section on matrix absorption: the score is q_lat·c + q_pe·kr,
+// eq. (4) accumulates P·c), so attention over the latent cache is multi-query
+// attention with K = [c ; kr] and V = c.  Causal rule (nanowhale page, SDPA
+// with is_causal): token t attends to the rows cu[b] .. t of its sequence.
+//
+// Workgroup = 8 wave64s on 8 consecutive query tokens; wave w takes token
+// 8k + w with its H = 16 heads as the MFMA N dimension.  The workgroup streams
+// the union of its tokens' key ranges in 32-row tiles through a 4-buffer LDS
+// ring (global_load_lds_dwordx4; 16-byte chunks XOR-swizzled by row / 2 within
+// groups of eight so fragment reads spread over the banks).  Per tile and wave:
+//   - score Sᵀ[32 keys x 16 heads]: two 16x16 blocks of
+//     v_mfma_f32_16x16x32_bf16 over the whole row (K = r + G·d_rope), key rows
+//     as the A operand from LDS, the token's Qᵀ as the B operand in registers
+//     (q_lat, the head's rotary-group q_pe, zero elsewhere);
+//   - causal / sequence mask, softmax against a per-head reference: the max of
+//     the first tile where the head has a valid key, base 2, 2^64 of headroom; a
+//     pass in which some later score passes the headroom is redone with the
+//     true max, so O is never rescaled;
+//   - PV: O[16 heads x r] += P[16 x 32]·C[32 x r], P straight from the softmax
+//     registers as the A operand (the product's K order is the order in which
+//     a lane holds its keys), C read transposed from the tile with
+//     ds_read_b64_tr_b16 at the matching row bases.
+// Blocks of later tokens (longer key ranges) are dispatched first.
+// Output: normalised o_ [n_tokens, H, r] fp32.
+#include <math.h>
+
+#include <algorithm>
+
+#include "lds_dma.h"
 #include "mla_device.h"
 #include "mla_internal.h"
 
 namespace mla {
 
-bool prefill_mfma_supported(const AttnShape&) { return false; }
+namespace {
 
-void prefill_mfma(const AttnShape&, const void*, const void*, const void*, const int64_t*, int,
-                  int64_t, int, float*, hipStream_t) {}
+constexpr int kHeads = 16;          // query heads per token (one MFMA N block)
+constexpr int kWaves = 8;           // query tokens per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTL = 32;             // key rows per tile
+constexpr int kStages = 4;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSlack = 64.f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// LDS chunk slot of 16-byte chunk c of tile row r (an involution for fixed r).
+__device__ __forceinline__ int swz(int c, int r) { return (c & ~7) | ((c ^ (r >> 1)) & 7); }
+
+template <int R, int RW>
+struct PShape {
+  static_assert(R % 16 == 0 && RW % 32 == 0 && RW > R, "row layout");
+  static constexpr int kRowBytes = RW * 2;
+  static constexpr int kRowChunks = kRowBytes / 16;
+  static_assert(kRowChunks % 8 == 0, "swizzle groups of eight chunks");
+  static constexpr int kTileBytes = kTL * kRowBytes;
+  static_assert(kTileBytes % 1024 == 0, "whole 1 KB copies");
+  static constexpr int kDmaOps = kTileBytes / 1024;
+  static constexpr int kDmaPerWave = (kDmaOps + kWaves - 1) / kWaves;
+  static_assert(3 * kDmaPerWave < 64, "vmcnt range");
+  static constexpr int kSteps = RW / 32;     // score k-steps
+  static constexpr int kNB = R / 16;         // PV column blocks
+  static constexpr int kLdsBytes = kStages * kTileBytes + 64;
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+};
+
+template <int N, int PerWave>
+__device__ __forceinline__ void wait_tiles_after() {
+  wait_vmcnt<N * PerWave>();
+}
+
+template <int R, int RW>
+__global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
+    const bf16_t* __restrict__ q_lat, const bf16_t* __restrict__ q_pe,
+    const bf16_t* __restrict__ cache, const int64_t* __restrict__ cu, int batch, int64_t n_tokens,
+    int n_groups, int d_rope, float scale, float* __restrict__ o_out) {
+  using S = PShape<R, RW>;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  int64_t* range = reinterpret_cast<int64_t*>(smem + kStages * S::kTileBytes);  // [2][kWaves/2] scratch
+  int* flags = reinterpret_cast<int*>(range);                                    // reused after setup
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, lg = lane >> 4;
+
+  // ---- this wave's token and its key rows [seq_lo, t]
+  const int64_t n_blocks = (n_tokens + kWaves - 1) / kWaves;
+  const int64_t block = n_blocks - 1 - blockIdx.x;  // longest key ranges first
+  const int64_t t = block * kWaves + wave;
+  const bool active = t < n_tokens;
+  int64_t seq_lo = 0;
+  if (active) {
+    int lo = 0, hi = batch;  // largest b with cu[b] <= t
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cu[mid] <= t) lo = mid;
+      else hi = mid;
+    }
+    seq_lo = cu[lo];
+  }
+  // the workgroup's key range: union of its tokens' ranges
+  const int64_t last_t = min(block * kWaves + kWaves - 1, n_tokens - 1);
+  if (lane == 0) range[wave] = active ? seq_lo : last_t;
+  __syncthreads();
+  int64_t k_lo = range[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) k_lo = min(k_lo, range[w]);
+  const int64_t k_hi = last_t;
+  const int n_tiles = static_cast<int>((k_hi - k_lo + kTL) / kTL);
+  __syncthreads();  // range[] read everywhere before it is reused as flags
+
+  const char* cache_c = reinterpret_cast<const char*>(cache);
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)smem));
+
+  // ---- tile copy: copy j fills LDS chunks [64j, 64j + 64); chunk L holds global
+  // chunk L ^ ((row / 2) & 7) of row L / kRowChunks; rows past k_hi read row k_hi
+  auto issue_tile = [&](int tt) {
+    const int64_t tile_row = k_lo + static_cast<int64_t>(tt) * kTL;
+    const int valid = static_cast<int>(min<int64_t>(kTL, k_hi + 1 - tile_row));
+    const char* tbase = cache_c + tile_row * S::kRowBytes;
+    const uint32_t dst = lds0 + (tt % kStages) * S::kTileBytes;
+    int ln = lane;
+    __asm__ volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < S::kDmaPerWave; ++i) {
+      const int j = min(wave + kWaves * i, S::kDmaOps - 1);  // duplicates of the last copy are benign
+      const int L = j * 64 + ln;
+      const int r = L / S::kRowChunks;
+      const int g = r < valid ? (L ^ ((r >> 1) & 7)) : (valid - 1) * S::kRowChunks + (L & 7);
+      global_to_lds16(tbase, static_cast<uint32_t>(g * 16), __builtin_amdgcn_readfirstlane(dst + j * 1024));
+    }
+  };
+  auto wait_tile = [&](int tt, int last_issued) {
+    switch (last_issued - tt) {
+      case 0: wait_tiles_after<0, S::kDmaPerWave>(); break;
+      case 1: wait_tiles_after<1, S::kDmaPerWave>(); break;
+      default: wait_tiles_after<2, S::kDmaPerWave>(); break;
+    }
+  };
+
+  // ---- Qᵀ of the token: B operand, lane = head l16, k = 32ks + 8lg + e
+  const int tq = active ? static_cast<int>(t) : 0;
+  const int per_group = kHeads / n_groups;
+  bf16x8 qf[S::kSteps];
+#pragma unroll
+  for (int ks = 0; ks < S::kSteps; ++ks) {
+    const int k0 = ks * 32 + lg * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (k0 < R) {
+      v = *reinterpret_cast<const uint4*>(q_lat + (static_cast<int64_t>(tq) * kHeads + l16) * R + k0);
+    } else {
+      const int g = (k0 - R) / d_rope, j0 = (k0 - R) - g * d_rope;
+      if (g == l16 / per_group)
+        v = *reinterpret_cast<const uint4*>(q_pe + (static_cast<int64_t>(tq) * kHeads + l16) * d_rope + j0);
+    }
+    qf[ks] = __builtin_bit_cast(bf16x8, v);
+  }
+  const float qk_scale = scale * kLog2e;
+  wait_vmcnt<0>();  // Q landed before any tile copy is in flight
+
+  const int a_off0 = l16 * S::kRowBytes, a_off1 = (16 + l16) * S::kRowBytes;
+  const int x_even = (lg ^ (l16 >> 1)) & 7;
+  const int x_odd = ((4 + lg) ^ (l16 >> 1)) & 7;
+  const int r_lo = lg * 4 + (l16 >> 2), r_hi = 16 + r_lo;
+  const int c_sub = (l16 & 1) * 8, c_half = (l16 & 3) >> 1;
+
+  float m_ref = -INFINITY;   // reference max of head l16 (base 2); set at its first valid key
+  float m_lane = -INFINITY, l_lane = 0.f;
+  bool over = false;
+  f32x4 o[S::kNB];
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int nb = 0; nb < S::kNB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_lane = -INFINITY;
+    l_lane = 0.f;
+    over = false;
+
+#pragma unroll
+    for (int tt = 0; tt < kStages - 1; ++tt)
+      if (tt < n_tiles) issue_tile(tt);
+    int issued = min(kStages - 1, n_tiles) - 1;
+
+    for (int tt = 0; tt < n_tiles; ++tt) {
+      wait_tile(tt, issued);
+      lds_barrier();  // tile tt landed everywhere; tile tt-1's buffer is free
+      if (tt + kStages - 1 < n_tiles) {
+        issue_tile(tt + kStages - 1);
+        issued = tt + kStages - 1;
+      }
+      const unsigned char* tb = smem + (tt % kStages) * S::kTileBytes;
+
+      // score: s[rb] = keys 16rb + 4lg + i of head l16
+      f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      auto frag = [&](int ks, int off) {
+        const int coff = (ks >> 1) * 128 + ((ks & 1) ? x_odd : x_even) * 16;
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tb + off + coff));
+      };
+      bf16x8 fa[2][2];
+      fa[0][0] = frag(0, a_off0);
+      fa[0][1] = frag(0, a_off1);
+      fa[1][0] = frag(1, a_off0);
+      fa[1][1] = frag(1, a_off1);
+#pragma unroll
+      for (int ks = 0; ks < S::kSteps; ++ks) {
+        s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ks & 1][0], qf[ks], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ks & 1][1], qf[ks], s[1], 0, 0, 0);
+        if (ks + 2 < S::kSteps) {
+          fa[ks & 1][0] = frag(ks + 2, a_off0);
+          fa[ks & 1][1] = frag(ks + 2, a_off1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // mask (this token's sequence rows up to itself), reference, weights
+      const int64_t row0 = k_lo + static_cast<int64_t>(tt) * kTL;
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t kr = row0 + rb * 16 + lg * 4 + i;
+          const float v = s[rb][i] * qk_scale;
+          s[rb][i] = (active && kr >= seq_lo && kr <= t) ? v : -INFINITY;
+          tmax = fmaxf(tmax, s[rb][i]);
+        }
+      if (pass == 0) {
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        if (m_ref == -INFINITY) m_ref = tmax;  // first tile with a valid key of this head
+      }
+      const float lim = m_ref + kSlack;
+      uint32_t w[4];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const f32x4 v = s[rb];
+        m_lane = fmaxf(m_lane, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+        over = over || (v[0] > lim) || (v[1] > lim) || (v[2] > lim) || (v[3] > lim);
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = v[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(v[i] - m_ref);
+        w[2 * rb] = pack_bf16x2(p[0], p[1]);
+        w[2 * rb + 1] = pack_bf16x2(p[2], p[3]);
+        // the row sum takes the bf16 weights the PV product uses
+        l_lane += bf16x2_sum(w[2 * rb]) + bf16x2_sum(w[2 * rb + 1]);
+      }
+      const bf16x8 pa = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+
+      // PV: O[head][16nb + col] += P[head][keys]·C[keys][cols], K order as held
+      auto cfrag = [&](int nb) {
+        const int chunk = nb * 2 + c_half;
+        const unsigned char* plo = tb + r_lo * S::kRowBytes + swz(chunk, r_lo) * 16 + c_sub;
+        const unsigned char* phi = tb + r_hi * S::kRowBytes + swz(chunk, r_hi) * 16 + c_sub;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(plo));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(phi));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      constexpr int kLA = 3;
+      bf16x8 cf[kLA];
+#pragma unroll
+      for (int q = 0; q < kLA; ++q) cf[q] = cfrag(q);
+#pragma unroll
+      for (int nb = 0; nb < S::kNB; ++nb) {
+        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, cf[nb % kLA], o[nb], 0, 0, 0);
+        if (nb + kLA < S::kNB) cf[nb % kLA] = cfrag(nb + kLA);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    lds_barrier();
+    if (lane == 0) flags[wave] = __ballot(over) != 0 ? 1 : 0;
+    lds_barrier();
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) any |= flags[w];
+    if (any == 0) break;
+    // second pass with each head's true max
+    float mx = fmaxf(m_lane, __shfl_xor(m_lane, 16, 64));
+    m_ref = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    lds_barrier();  // flags read everywhere before they are rewritten
+  }
+
+  // ---- epilogue: l per head (lanes with l16 = head), O[head 4lg + i][16nb + l16]
+  float l = l_lane;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (!active) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = lg * 4 + i;
+    const float inv = 1.f / __shfl(l, h, 64);
+    float* dst = o_out + (t * kHeads + h) * R + l16;
+#pragma unroll
+    for (int nb = 0; nb < S::kNB; ++nb) dst[nb * 16] = o[nb][i] * inv;
+  }
+}
+
+template <int R, int RW>
+void launch(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
+            const int64_t* cu, int batch, int64_t n_tokens, float* o_out, hipStream_t s) {
+  using S = PShape<R, RW>;
+  auto kern = prefill_mfma_kernel<R, RW>;
+  hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                      S::kLdsBytes);
+  const int64_t n_blocks = (n_tokens + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(n_blocks)), dim3(kThreads), S::kLdsBytes, s,
+                     static_cast<const bf16_t*>(q_lat), static_cast<const bf16_t*>(q_pe),
+                     static_cast<const bf16_t*>(cache), cu, batch, n_tokens, sh.G, sh.d_rope, sh.scale,
+                     o_out);
+}
+
+// Compiled shapes: (latent r, row width r + G*d_rope) with H = 16 query heads.
+#define MLA_PREFILL_SHAPES(X) \
+  X(256, 320) /* r = 256, one 64-wide rotary key (Zebra MLA layers) */
+
+}  // namespace
+
+bool prefill_mfma_supported(const AttnShape& sh) {
+  if (sh.H != kHeads || sh.d_rope % 8 != 0 || sh.H % sh.G != 0) return false;
+#define MLA_MATCH(R_, RW_) \
+  if (sh.r == R_ && sh.row_w == RW_) return true;
+  MLA_PREFILL_SHAPES(MLA_MATCH)
+#undef MLA_MATCH
+  return false;
+}
+
+void prefill_mfma(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
+                  const int64_t* cu, int batch, int64_t n_tokens, int max_len, float* o_out,
+                  hipStream_t s) {
+  (void)max_len;
+  if (n_tokens <= 0 || batch <= 0) return;
+#define MLA_LAUNCH(R_, RW_)                                                          \
+  if (sh.r == R_ && sh.row_w == RW_) {                                               \
+    launch<R_, RW_>(sh, q_lat, q_pe, cache, cu, batch, n_tokens, o_out, s);          \
+    return;                                                                          \
+  }
+  MLA_PREFILL_SHAPES(MLA_LAUNCH)
+#undef MLA_LAUNCH
+}
 
 }  // namespace mla

@@ -174,12 +174,14 @@ def softmax_attention(q, k, v, allowed, scale: float) -> np.ndarray:
     ``allowed`` [Tq, S] bool.  a = scale·q·k; P = softmax over allowed keys
     (max subtracted); out = P·v.  Every query must allow at least one key."""
     q, k, v = _f64(q), _f64(k), _f64(v)
-    a = scale * np.einsum("thd,shd->hts", q, k)
+    # a[h,t,s] = scale·Σ_d q[t,h,d]·k[s,h,d]  (a matrix product per head)
+    a = scale * np.matmul(q.transpose(1, 0, 2), k.transpose(1, 2, 0))
     a = np.where(allowed[None, :, :], a, -np.inf)
     m = a.max(axis=-1, keepdims=True)
     e = np.exp(a - m)
     p = e / e.sum(axis=-1, keepdims=True)
-    return np.einsum("hts,she->the", p, v)
+    # out[t,h,e] = Σ_s p[h,t,s]·v[s,h,e]
+    return np.matmul(p, v.transpose(1, 0, 2)).transpose(1, 0, 2)
 
 
 def mla_attention(qn, qr, c, kr, w_uk, w_uv, q_pos, k_pos, q_seg, k_seg, scale, *,

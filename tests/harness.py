@@ -129,6 +129,54 @@ def build_decode(layer: DeviceLayer, lengths: np.ndarray, x_scale: float = 1.0,
     return DecodeRun(lengths, starts, cache, q_lat, q_pe, out, xq)
 
 
+@dataclasses.dataclass
+class PrefillRun:
+    x_q: np.ndarray        # the bf16-exact hidden states (float32) the GPU received
+    cache: object          # device [L, row_width]
+    q_lat: object          # device [L, H, r]
+    q_pe: object           # device [L, H, d_rope]
+    out: object            # device [L, H, d_v]
+
+
+def build_prefill(layer: DeviceLayer, L: int, chunk: int = 8192, threads: int = 8) -> PrefillRun:
+    """One sequence of L tokens: cache rows and queries from seeded x (written and
+    absorbed in chunks of ``chunk`` tokens), then one causal mla_prefill call."""
+    import concurrent.futures as cf
+
+    import head_latent_attention_kv_amd as M
+    torch = torch_mod()
+    cfg = layer.cfg
+    et = elem_dtype(cfg)
+    cache = torch.empty((L, cfg.row_width), dtype=et, device="cuda")
+    q_lat = torch.empty((L, cfg.n_heads, cfg.rank), dtype=et, device="cuda")
+    q_pe = torch.empty((L, cfg.n_heads, cfg.d_rope), dtype=et, device="cuda")
+    x_q = np.empty((L, cfg.d_model), np.float32)
+    ws_w = torch.empty(max(256, M.mla_workspace_size(layer.dims, M.MLA_OP_WRITE_CACHE, 0, chunk, 0)),
+                       dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(max(256, M.mla_workspace_size(layer.dims, M.MLA_OP_ABSORB, 0, chunk, 0)),
+                       dtype=torch.uint8, device="cuda")
+    jobs = [(c0, min(L, c0 + chunk)) for c0 in range(0, L, chunk)]
+
+    def gen(job):
+        c0, c1 = job
+        return job, I.x_rows(cfg, 0, c0, c1, quantized=False)
+
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        for (c0, c1), xb in ex.map(gen, jobs):
+            x_q[c0:c1] = I.quantize(xb, cfg.dtype)
+            xd = raw_to_dev(xb, cfg.dtype)
+            pos = np.arange(c0, c1)
+            write_cache(layer, xd, pos, pos, cache, workspace=ws_w)
+            M.mla_absorb(layer.dims, xd, layer.w_dev["w_qc"], layer.w_dev["w_qr"], layer.w_dev["w_uk"],
+                         torch.from_numpy(pos.astype(np.int32)).cuda(), q_lat[c0:c1], q_pe[c0:c1],
+                         workspace=ws_a)
+    out = torch.empty((L, cfg.n_heads, cfg.d_v), dtype=et, device="cuda")
+    cu = torch.tensor([0, L], dtype=torch.int64, device="cuda")
+    M.mla_prefill(layer.dims, q_lat, q_pe, cache, cu, L, layer.w_dev["w_uv"], out)
+    torch.cuda.synchronize()
+    return PrefillRun(x_q, cache, q_lat, q_pe, out)
+
+
 def oracle_decode_rows(cfg, w, x_keys: np.ndarray, x_query: np.ndarray, n: int,
                        cache_rows: Optional[np.ndarray] = None, heads: Optional[List[int]] = None):
     """Oracle output [H or len(heads), d_v] for one decode query at position n-1.

@@ -210,6 +210,50 @@ def test_prefill_reduced_ragged(torch):
     assert err <= Hh.TOL["bf16"]
 
 
+def test_prefill_full_size_sampled(torch):
+    """The 131072-token causal prefill at full size: the whole chain runs on the
+    GPU; 512 seeded rows spread over the sequence (row 0 and the last row
+    included) are checked against the oracle on the GPU-written cache (attention
+    parity), every eighth of them also against the oracle's own cache (chain
+    parity), and their q_lat / q_pe against the oracle's queries."""
+    from oracle import mla_oracle as O
+    cfg = I.CONFIGS["long_prefill_131k"]
+    L = cfg.prefill_len
+    _print_case("prefill_full_size", cfg=cfg.name, L=L)
+    layer = Hh.make_layer(cfg)
+    run = Hh.build_prefill(layer, L)
+    rows = I.sample_rows(cfg)
+    print("  gpu chain done; oracle attention on the gpu cache", flush=True)
+    got = Hh.to_host(run.out[torch.from_numpy(rows).cuda()])
+    cache_h = Hh.to_host(run.cache)
+    w = layer.w_host
+    c, kr = O.split_rows(cache_h, cfg.rank, cfg.n_groups, cfg.d_rope)
+    qn, qr = O.query(run.x_q[rows], w["w_qc"], w["w_qr"], rows, n_heads=cfg.n_heads, d_nope=cfg.d_nope,
+                     d_rope=cfg.d_rope, theta=cfg.rope_theta)
+    zeros_q, zeros_k = np.zeros(len(rows), int), np.zeros(L, int)
+    ref = O.mla_attention(qn, qr, c, kr, w["w_uk"], w["w_uv"], rows, np.arange(L), zeros_q, zeros_k,
+                          cfg.softmax_scale, head_chunk=1)
+    err_attn = Hh.rel_err_rows(got, ref)
+    err_qlat = Hh.rel_err_rows(Hh.to_host(run.q_lat[torch.from_numpy(rows).cuda()]), O.absorbed_query(qn, w["w_uk"]))
+    err_qpe = Hh.rel_err_rows(Hh.to_host(run.q_pe[torch.from_numpy(rows).cuda()]), qr)
+    print(f"  attention parity {err_attn:.3e}, q_lat {err_qlat:.3e}, q_pe {err_qpe:.3e}; oracle chain", flush=True)
+    sub = rows[::8].copy()
+    sub[-1] = rows[-1]
+    rows_ref = O.cache_rows(run.x_q, w["w_dkv"], w["w_kr"], np.arange(L), n_groups=cfg.n_groups,
+                            d_rope=cfg.d_rope, theta=cfg.rope_theta)
+    err_write = Hh.rel_err_rows(cache_h[:, :cfg.rank], rows_ref[:, :cfg.rank])
+    c_o, kr_o = O.split_rows(rows_ref, cfg.rank, cfg.n_groups, cfg.d_rope)
+    sel = np.searchsorted(rows, sub)
+    ref_chain = O.mla_attention(qn[sel], qr[sel], c_o, kr_o, w["w_uk"], w["w_uv"], sub, np.arange(L),
+                                np.zeros(len(sub), int), zeros_k, cfg.softmax_scale, head_chunk=1)
+    err_chain = Hh.rel_err_rows(got[sel], ref_chain)
+    print(f"prefill {L}: attn={err_attn:.3e} chain={err_chain:.3e} write={err_write:.3e} "
+          f"q_lat={err_qlat:.3e} q_pe={err_qpe:.3e}")
+    for name, v in (("attn", err_attn), ("chain", err_chain), ("write", err_write), ("q_lat", err_qlat),
+                    ("q_pe", err_qpe)):
+        assert v <= Hh.TOL[cfg.dtype], (name, v)
+
+
 # ----------------------------------------------------------------------------
 # ABI behaviour on the device
 # ----------------------------------------------------------------------------
