@@ -169,6 +169,95 @@ def cpu_baseline(cfg, I, lengths):
                       f"attention) = 1 decode token, {dt:.2f} s"}
 
 
+def prefill_alg_flops(cfg, L: int) -> int:
+    """Causal absorbed attention over one sequence of L tokens: every (query,
+    key <= query, head) pair costs 2(r + G·d_rope) for the score and 2r for P·c."""
+    pairs = L * (L + 1) // 2
+    return pairs * cfg.n_heads * (2 * cfg.row_width + 2 * cfg.rank)
+
+
+def bench_prefill(args, torch, M, I, Hh, cfg):
+    """Long causal prefill: one step = mla_write_cache + mla_absorb + mla_prefill over
+    the whole sequence (x resident in HBM); the attention kernel is timed alone
+    for the MFMA roofline."""
+    L = cfg.prefill_len
+    layer = Hh.make_layer(cfg)
+    dims = layer.dims
+    et = torch.bfloat16
+    t_setup = time.perf_counter()
+    x = torch.empty((L, cfg.d_model), dtype=et, device="cuda")
+    for c0 in range(0, L, 8192):
+        c1 = min(L, c0 + 8192)
+        x[c0:c1] = Hh.raw_to_dev(I.x_rows(cfg, 0, c0, c1, quantized=False), cfg.dtype)
+    pos = torch.arange(L, dtype=torch.int32, device="cuda")
+    slots = torch.arange(L, dtype=torch.int64, device="cuda")
+    cu = torch.tensor([0, L], dtype=torch.int64, device="cuda")
+    cache = torch.empty((L, cfg.row_width), dtype=et, device="cuda")
+    q_lat = torch.empty((L, cfg.n_heads, cfg.rank), dtype=et, device="cuda")
+    q_pe = torch.empty((L, cfg.n_heads, cfg.d_rope), dtype=et, device="cuda")
+    out = torch.empty((L, cfg.n_heads, cfg.d_v), dtype=et, device="cuda")
+    ws_w = torch.empty(M.mla_workspace_size(dims, M.MLA_OP_WRITE_CACHE, 0, L, 0), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(M.mla_workspace_size(dims, M.MLA_OP_ABSORB, 0, L, 0), dtype=torch.uint8, device="cuda")
+    ws_p = torch.empty(M.mla_workspace_size(dims, M.MLA_OP_PREFILL, 1, L, L), dtype=torch.uint8, device="cuda")
+    wd = layer.w_dev
+    setup_s = time.perf_counter() - t_setup
+
+    def step():
+        M.mla_write_cache(dims, x, wd["w_dkv"], wd["w_kr"], pos, slots, cache, workspace=ws_w)
+        M.mla_absorb(dims, x, wd["w_qc"], wd["w_qr"], wd["w_uk"], pos, q_lat, q_pe, workspace=ws_a)
+        M.mla_prefill(dims, q_lat, q_pe, cache, cu, L, wd["w_uv"], out, workspace=ws_p)
+
+    def attention():
+        M.mla_prefill(dims, q_lat, q_pe, cache, cu, L, wd["w_uv"], out, workspace=ws_p)
+
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n, w):
+        for _ in range(w):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    steps = min(args.steps, 5)
+    warm = min(args.warmup, 1)
+    ms_step = timed(step, steps, warm)
+    ms_attn = timed(attention, steps, warm)
+    flops = prefill_alg_flops(cfg, L)
+    tflops = flops / (ms_attn * 1e-3) / 1e12
+    print(f"[bench] prefill {L}: step {ms_step:.2f} ms, mla_prefill {ms_attn:.2f} ms "
+          f"({tflops:.0f} TFLOP/s on the attention) (setup {setup_s:.1f} s)", file=sys.stderr, flush=True)
+    assert torch.isfinite(out.float()).all(), "non-finite prefill output"
+    line = {
+        "metric": "MLA absorbed causal prefill tokens/s + % of MFMA roofline, H=16 r=256 L=131072",
+        "value": round(L / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded x ~ N(0,1), weights ~ N(0,1/fan_in)",
+        "config": {"workload": cfg.name, "tokens": L, "heads": cfg.n_heads, "rank": cfg.rank,
+                   "d_rope": cfg.d_rope, "d_model": cfg.d_model,
+                   "step": "mla_write_cache + mla_absorb + mla_prefill"},
+        "roofline": {"bound": "mfma", "kernel": "mla_prefill (attention + W_UV)",
+                     "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                     "alg_flops_per_launch": flops, "ms_per_launch": round(ms_attn, 3)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -185,8 +274,10 @@ def main():
     M.load()
     torch.cuda.set_device(0)
     cfg = I.CONFIGS[args.workload]
+    if cfg.mode == "prefill":
+        return bench_prefill(args, torch, M, I, Hh, cfg)
     if cfg.mode != "decode":
-        raise SystemExit("bench.py times decode workloads")
+        raise SystemExit(f"no benchmark for workload mode {cfg.mode!r}")
     threads = args.threads or min(16, host_threads())
     lengths = I.context_lengths(cfg)
     starts = np.concatenate([[0], np.cumsum(lengths)[:-1]]).astype(np.int64)
