@@ -65,7 +65,7 @@ def decode_alg_bytes(cfg, lengths) -> int:
 
 def attention_alg_bytes(cfg, lengths) -> int:
     """Bytes the split attention kernel must move: cache rows read and the queries
-    (the split partials it writes are overhead of the split, not counted)."""
+    (the per-split partials it writes are overhead of the split, not counted)."""
     e = cfg.elem_bytes
     rows = int(sum(lengths))
     return rows * cfg.row_width * e + len(lengths) * cfg.n_heads * (cfg.rank + cfg.d_rope) * e
@@ -77,7 +77,7 @@ def attention_alg_flops(cfg, lengths) -> int:
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attention_deepseek_v2_traffic.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "head_latent_attention_kv_amd", "csrc", "decode_mfma.hip")
+KERNEL_SOURCE = os.path.join(ROOT, "head_latent_attention_kv_amd", "csrc", "decode_wide.hip")
 
 
 def measured_traffic():
@@ -345,7 +345,7 @@ def main():
     # the dominant kernel alone: the split attention (mla_decode_partials launches
     # exactly that kernel, with mla_decode's split plan), HIP events on its stream
     n_split = M.mla_decode_splits(dims, B, max_len)
-    part_o = torch.empty((B, n_split, cfg.n_heads, cfg.rank), dtype=torch.float32, device="cuda")
+    part_o = torch.empty((B, n_split, cfg.n_heads, cfg.rank), dtype=et, device="cuda")
     part_ml = torch.empty((B, n_split, cfg.n_heads, 2), dtype=torch.float32, device="cuda")
 
     def attention_only(i):
@@ -392,7 +392,7 @@ def main():
         "config": {"workload": cfg.name, "batch": B, "context": int(max_len), "heads": cfg.n_heads,
                    "rank": cfg.rank, "d_rope": cfg.d_rope, "d_model": cfg.d_model,
                    "step": "mla_write_cache + mla_absorb + mla_decode"},
-        "roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel (split attention over the latent cache)",
+        "roofline": {"bound": "hbm", "kernel": "decode_wide_kernel (split attention over the latent cache)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (round(traffic / (ms_att * 1e-3) / 1e9, 1) if traffic else None),

@@ -201,7 +201,7 @@ def mla_decode_partials(dims, q_lat, q_pe, cache, seq_start, seq_len, max_len, n
     _check("mla_decode_partials", load().mla_decode_partials(
         ctypes.byref(dims), _ptr(q_lat, "q_lat", et), _ptr(q_pe, "q_pe", et), _ptr(cache, "cache", et),
         _ptr(seq_start, "seq_start", torch.int64), _ptr(seq_len, "seq_len", torch.int32), B,
-        int(max_len), int(n_split), _ptr(part_o, "part_o", torch.float32),
+        int(max_len), int(n_split), _ptr(part_o, "part_o", et),
         _ptr(part_ml, "part_ml", torch.float32), _stream(stream)))
     return part_o, part_ml
 

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(
     const T* __restrict__ q_lat, const T* __restrict__ q_pe, const T* __restrict__ cache,
     const int64_t* __restrict__ seq_start, const int32_t* __restrict__ seq_len,
     const int64_t* __restrict__ cu, int batch, AttnShape sh, int n_split, int split_len,
-    float* __restrict__ part_o, float* __restrict__ part_ml, float* __restrict__ o_out) {
+    T* __restrict__ part_o, float* __restrict__ part_ml, float* __restrict__ o_out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int row_w = sh.row_w;
   const int pitch = lds_pitch(row_w, sizeof(T));
@@ -141,11 +141,13 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(
       if (c < sh.r) o_out[(q * sh.H + head) * sh.r + c] = acc[j] * inv;
     }
   } else {
+    // the split's normalised o_ in the layer's element type (an empty split: 0)
     const int64_t pidx = (q * n_split + split) * sh.H + head;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
     for (int j = 0; j < kRJ; ++j) {
       int c = lane32 + 32 * j;
-      if (c < sh.r) part_o[pidx * sh.r + c] = acc[j];
+      if (c < sh.r) Elem<T>::store(part_o, pidx * sh.r + c, acc[j] * inv);
     }
     if (lane32 == 0) {
       part_ml[pidx * 2 + 0] = m_run;
@@ -154,8 +156,9 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(
   }
 }
 
-__global__ __launch_bounds__(256) void merge_kernel(AttnShape sh, int n_split,
-                                                    const float* __restrict__ part_o,
+// o_ = Σ_j 2^(m_j - M) l_j o_j / Σ_j 2^(m_j - M) l_j over the splits j of (query, head)
+template <typename T>
+__global__ __launch_bounds__(256) void merge_kernel(AttnShape sh, int n_split, const T* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     float* __restrict__ o_out) {
   const int64_t q = blockIdx.x;
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnShape sh, int n_split,
     float num = 0.f;
     for (int j = 0; j < n_split; ++j) {
       const int64_t pidx = (q * n_split + j) * sh.H + h;
-      num += exp2f(part_ml[pidx * 2] - mx) * part_o[pidx * sh.r + c];
+      num += exp2f(part_ml[pidx * 2] - mx) * part_ml[pidx * 2 + 1] * Elem<T>::load(part_o, pidx * sh.r + c);
     }
     o_out[(q * sh.H + h) * sh.r + c] = num * inv;
   }
@@ -191,7 +194,7 @@ int generic_head_block() { return kHB; }
 void attend_generic(int dtype, const AttnShape& sh, const void* q_lat, const void* q_pe,
                     const void* cache, const int64_t* seq_start, const int32_t* seq_len,
                     const int64_t* cu, int batch, int64_t n_q, int n_split, int split_len,
-                    float* part_o, float* part_ml, float* o_out, hipStream_t s) {
+                    void* part_o, float* part_ml, float* o_out, hipStream_t s) {
   if (n_q <= 0) return;
   dim3 grid(static_cast<unsigned>(n_q), (sh.H + kHB - 1) / kHB, n_split);
   if (dtype == kF32) {
@@ -199,21 +202,26 @@ void attend_generic(int dtype, const AttnShape& sh, const void* q_lat, const voi
     hipLaunchKernelGGL(attend_generic_kernel<float>, grid, dim3(256), smem, s,
                        static_cast<const float*>(q_lat), static_cast<const float*>(q_pe),
                        static_cast<const float*>(cache), seq_start, seq_len, cu, batch, sh, n_split,
-                       split_len, part_o, part_ml, o_out);
+                       split_len, static_cast<float*>(part_o), part_ml, o_out);
   } else {
     size_t smem = smem_bytes<bf16_t>(sh);
     hipLaunchKernelGGL(attend_generic_kernel<bf16_t>, grid, dim3(256), smem, s,
                        static_cast<const bf16_t*>(q_lat), static_cast<const bf16_t*>(q_pe),
                        static_cast<const bf16_t*>(cache), seq_start, seq_len, cu, batch, sh,
-                       n_split, split_len, part_o, part_ml, o_out);
+                       n_split, split_len, static_cast<bf16_t*>(part_o), part_ml, o_out);
   }
 }
 
-void merge_splits(const AttnShape& sh, int64_t n_q, int n_split, const float* part_o,
+void merge_splits(int dtype, const AttnShape& sh, int64_t n_q, int n_split, const void* part_o,
                   const float* part_ml, float* o_out, hipStream_t s) {
   if (n_q <= 0) return;
-  hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>(n_q), sh.H), dim3(256), 0, s, sh,
-                     n_split, part_o, part_ml, o_out);
+  const dim3 grid(static_cast<unsigned>(n_q), sh.H);
+  if (dtype == kF32)
+    hipLaunchKernelGGL(merge_kernel<float>, grid, dim3(256), 0, s, sh, n_split,
+                       static_cast<const float*>(part_o), part_ml, o_out);
+  else
+    hipLaunchKernelGGL(merge_kernel<bf16_t>, grid, dim3(256), 0, s, sh, n_split,
+                       static_cast<const bf16_t*>(part_o), part_ml, o_out);
 }
 
 }  // namespace mla

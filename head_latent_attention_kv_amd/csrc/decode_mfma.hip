@@ -25,7 +25,8 @@
 //  4. PV: wave w owns latent columns [w·R/8, (w+1)·R/8) for all heads of the
 //     workgroup; O += P·C with P (A operand) from LDS and C (B operand) read
 //     transposed from the same tile with ds_read_b64_tr_b16.
-// Output: normalised o_ (part_o null, one split) or (m, l, unnormalised o_) partials.
+// Output: normalised o_ (part_o null, one split) or the split's (m, l) and its
+// normalised o_ in bf16.
 #include <math.h>
 
 #include <algorithm>
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
     const bf16_t* __restrict__ q_lat, const bf16_t* __restrict__ q_pe,
     const bf16_t* __restrict__ cache, const int64_t* __restrict__ seq_start,
     const int32_t* __restrict__ seq_len, int batch, int H, int G, int d_rope, float scale,
-    int n_split, int split_len, float* __restrict__ part_o, float* __restrict__ part_ml,
+    int n_split, int split_len, bf16_t* __restrict__ part_o, float* __restrict__ part_ml,
     float* __restrict__ o_out) {
   using S = Shape<R, RW, NHB, NHH, STAGES>;
   constexpr int kBufBytes = S::kBufBytes;
@@ -390,15 +391,16 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
       const int hl = hb * 16 + lg * 4 + i;
       const int h = head0 + hl;
       if (h >= H) continue;
+      const float lh = xch[hl] + xch[S::kHeads + hl];
+      const float inv = lh > 0.f ? 1.f / lh : 0.f;  // an empty split has l = 0 and o_ = 0
       if (!partials) {
-        const float inv = 1.f / (xch[hl] + xch[S::kHeads + hl]);
         float* dst = o_out + (static_cast<int64_t>(b) * H + h) * R + c0 + l16;
 #pragma unroll
         for (int nb = 0; nb < S::kNB; ++nb) dst[nb * 16] = o[hb][nb][i] * inv;
       } else {
-        float* dst = part_o + ((static_cast<int64_t>(b) * n_split + split) * H + h) * R + c0 + l16;
+        bf16_t* dst = part_o + ((static_cast<int64_t>(b) * n_split + split) * H + h) * R + c0 + l16;
 #pragma unroll
-        for (int nb = 0; nb < S::kNB; ++nb) dst[nb * 16] = o[hb][nb][i];
+        for (int nb = 0; nb < S::kNB; ++nb) dst[nb * 16] = f32_to_bf16(o[hb][nb][i] * inv);
       }
     }
 }
@@ -406,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
 template <int R, int RW, int NHB, int NHH, int STAGES>
 void launch(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
             const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split, int split_len,
-            float* part_o, float* part_ml, float* o_out, hipStream_t s) {
+            void* part_o, float* part_ml, float* o_out, hipStream_t s) {
   using S = Shape<R, RW, NHB, NHH, STAGES>;
   auto kern = decode_mfma_kernel<R, RW, NHB, NHH, STAGES>;
   hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -416,7 +418,8 @@ void launch(const AttnShape& sh, const void* q_lat, const void* q_pe, const void
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), S::kLdsBytes, s,
                      static_cast<const bf16_t*>(q_lat), static_cast<const bf16_t*>(q_pe),
                      static_cast<const bf16_t*>(cache), seq_start, seq_len, batch, sh.H, sh.G,
-                     sh.d_rope, sh.scale, n_split, split_len, part_o, part_ml, o_out);
+                     sh.d_rope, sh.scale, n_split, split_len, static_cast<bf16_t*>(part_o), part_ml,
+                     o_out);
 }
 
 // Compiled shapes: (latent r, row width r + G*d_rope, 16-head blocks per workgroup,
@@ -458,7 +461,7 @@ int decode_mfma_blocks_per_cu(const AttnShape& sh) {
 
 void decode_mfma(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
                  const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split,
-                 int split_len, float* part_o, float* part_ml, float* o_out, hipStream_t s) {
+                 int split_len, void* part_o, float* part_ml, float* o_out, hipStream_t s) {
   if (batch <= 0) return;
 #define MLA_LAUNCH(R_, RW_, NHB_, NHH_, ST_, HLO_, HHI_)                                          \
   if (sh.r == R_ && sh.row_w == RW_ && sh.H >= HLO_ && sh.H <= HHI_) {                           \

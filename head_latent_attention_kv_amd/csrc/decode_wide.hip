@@ -29,7 +29,7 @@
 // Iteration t (one barrier, for the tile ring): score of tile t+1, then PV of
 // tile t with the softmax of tile t+1 issued between its MFMAs.
 // Output: normalised o_ (part_o null, one split) or the split's (m, l) and
-// unnormalised o_.
+// its normalised o_ in bf16.
 #include <math.h>
 
 #include "lds_dma.h"
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
     const bf16_t* __restrict__ q_lat, const bf16_t* __restrict__ q_pe,
     const bf16_t* __restrict__ cache, const int64_t* __restrict__ seq_start,
     const int32_t* __restrict__ seq_len, int batch, float scale, int n_split, int split_len,
-    float* __restrict__ part_o, float* __restrict__ part_ml, float* __restrict__ o_out) {
+    bf16_t* __restrict__ part_o, float* __restrict__ part_ml, float* __restrict__ o_out) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   float* xch = reinterpret_cast<float*>(smem + kStages * kTileBytes);  // [kHeads]
   int* flags = reinterpret_cast<int*>(xch + kHeads);                   // [kWaves]
@@ -367,15 +367,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = wave * kHW + hb * 16 + lg * 4 + i;
+      const float lh = xch[h];
+      const float inv = lh > 0.f ? 1.f / lh : 0.f;  // an empty split has l = 0 and o_ = 0
       if (!partials) {
-        const float inv = 1.f / xch[h];
         float* dst = o_out + (static_cast<int64_t>(b) * kHeads + h) * kR + l16;
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) dst[nb * 16] = o[hb][nb][i] * inv;
       } else {
-        float* dst = part_o + ((static_cast<int64_t>(b) * n_split + split) * kHeads + h) * kR + l16;
+        bf16_t* dst = part_o + ((static_cast<int64_t>(b) * n_split + split) * kHeads + h) * kR + l16;
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) dst[nb * 16] = o[hb][nb][i];
+        for (int nb = 0; nb < kNB; ++nb) dst[nb * 16] = f32_to_bf16(o[hb][nb][i] * inv);
       }
     }
 }
@@ -388,14 +389,14 @@ bool decode_wide_supported(const AttnShape& sh) {
 
 void decode_wide(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
                  const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split,
-                 int split_len, float* part_o, float* part_ml, float* o_out, hipStream_t s) {
+                 int split_len, void* part_o, float* part_ml, float* o_out, hipStream_t s) {
   if (batch <= 0) return;
   hipFuncSetAttribute(reinterpret_cast<const void*>(decode_wide_kernel),
                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   hipLaunchKernelGGL(decode_wide_kernel, dim3(batch * n_split), dim3(kThreads), kLdsBytes, s,
                      static_cast<const bf16_t*>(q_lat), static_cast<const bf16_t*>(q_pe),
                      static_cast<const bf16_t*>(cache), seq_start, seq_len, batch, sh.scale, n_split,
-                     split_len, part_o, part_ml, o_out);
+                     split_len, static_cast<bf16_t*>(part_o), part_ml, o_out);
 }
 
 }  // namespace mla

@@ -110,7 +110,8 @@ DecodePlan decode_plan(const mla_dims* d, int32_t batch, int32_t max_len, int32_
   p.split_len = split_len;
   p.o_bytes = align_up(static_cast<size_t>(B) * sh.H * sh.r * sizeof(float));
   if (p.n_split > 1) {
-    p.part_o_bytes = align_up(static_cast<size_t>(B) * p.n_split * sh.H * sh.r * sizeof(float));
+    const size_t elem = d->dtype == MLA_F32 ? sizeof(float) : 2;  // partials in the layer's type
+    p.part_o_bytes = align_up(static_cast<size_t>(B) * p.n_split * sh.H * sh.r * elem);
     p.part_ml_bytes = align_up(static_cast<size_t>(B) * p.n_split * sh.H * 2 * sizeof(float));
   }
   return p;
@@ -363,7 +364,7 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_pe, const 
   AttnShape sh = shape_of(dims);
   char* ws = static_cast<char*>(workspace);
   float* o_lat = reinterpret_cast<float*>(ws);
-  float* part_o = p.n_split > 1 ? reinterpret_cast<float*>(ws + p.o_bytes) : nullptr;
+  void* part_o = p.n_split > 1 ? static_cast<void*>(ws + p.o_bytes) : nullptr;
   float* part_ml = p.n_split > 1 ? reinterpret_cast<float*>(ws + p.o_bytes + p.part_o_bytes) : nullptr;
   if (p.wide)
     mla::decode_wide(sh, q_lat, q_pe, cache, seq_start, seq_len, batch, p.n_split, p.split_len,
@@ -398,7 +399,7 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_pe, const 
     mla::gemm_skinny_merged(sa, p.n_split, /*out_bf16=*/true, s);
     return launch_status();
   }
-  if (p.n_split > 1) mla::merge_splits(sh, batch, p.n_split, part_o, part_ml, o_lat, s);
+  if (p.n_split > 1) mla::merge_splits(dims->dtype, sh, batch, p.n_split, part_o, part_ml, o_lat, s);
   apply_w_uv(dims, o_lat, batch, w_uv, out, s);
   return launch_status();
 }
@@ -419,7 +420,7 @@ int32_t mla_decode_split_rows(const mla_dims* dims, int32_t batch, int32_t max_l
 
 int mla_decode_partials(const mla_dims* dims, const void* q_lat, const void* q_pe,
                         const void* cache, const int64_t* seq_start, const int32_t* seq_len,
-                        int32_t batch, int32_t max_len, int32_t n_split, float* part_o,
+                        int32_t batch, int32_t max_len, int32_t n_split, void* part_o,
                         float* part_ml, void* stream) {
   int st = check_dims(dims);
   if (st != MLA_OK) return st;

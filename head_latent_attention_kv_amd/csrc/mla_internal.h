@@ -38,8 +38,9 @@ struct SkinnyArgs {
   void* C;
   int64_t sCz, sCm, sPs;     // C[s][z][m][n]
   int M, N, K, Z, splits, k_per_split;
-  // merged A (gemm_skinny_merged): A[z][m][k] = Σ_j w_j · A[z][m][k + j*sAs] with
-  // softmax-merge weights from ml[(m*n_merge + j)*ml_heads + z] = (max, sum)
+  // merged A (gemm_skinny_merged): A[z][m][k] = Σ_j w_j · A[z][m][k + j*sAs] over
+  // bf16 split partials (each normalised) with softmax-merge weights
+  // w_j ∝ 2^(max_j) sum_j from ml[(m*n_merge + j)*ml_heads + z] = (max, sum)
   int64_t sAs;
   const float* ml;
   int ml_heads, n_merge;
@@ -78,11 +79,12 @@ struct AttnShape {
 void attend_generic(int dtype, const AttnShape& sh, const void* q_lat, const void* q_pe,
                     const void* cache, const int64_t* seq_start, const int32_t* seq_len,
                     const int64_t* cu, int batch, int64_t n_q, int n_split, int split_len,
-                    float* part_o, float* part_ml, float* o_out, hipStream_t s);
+                    void* part_o, float* part_ml, float* o_out, hipStream_t s);
 int generic_head_block();
 
 // Log-sum-exp merge of split partials into normalised o_ (fp32 [n_q, H, r]).
-void merge_splits(const AttnShape& sh, int64_t n_q, int n_split, const float* part_o,
+// part_o holds each split's normalised o_ in the layer's element type.
+void merge_splits(int dtype, const AttnShape& sh, int64_t n_q, int n_split, const void* part_o,
                   const float* part_ml, float* o_out, hipStream_t s);
 
 // bf16 MFMA decode kernel for the shapes it supports (see decode_mfma.hip).
@@ -91,14 +93,14 @@ void merge_splits(const AttnShape& sh, int64_t n_q, int n_split, const float* pa
 bool decode_wide_supported(const AttnShape& sh);
 void decode_wide(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
                  const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split,
-                 int split_len, float* part_o, float* part_ml, float* o_out, hipStream_t s);
+                 int split_len, void* part_o, float* part_ml, float* o_out, hipStream_t s);
 
 bool decode_mfma_supported(const AttnShape& sh);
 int decode_mfma_blocks_per_cu(const AttnShape& sh);  // workgroups one CU holds (LDS-limited)
 int decode_mfma_head_groups(const AttnShape& sh);    // workgroups that share one sequence split
 void decode_mfma(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
                  const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split,
-                 int split_len, float* part_o, float* part_ml, float* o_out, hipStream_t s);
+                 int split_len, void* part_o, float* part_ml, float* o_out, hipStream_t s);
 
 // bf16 MFMA causal prefill kernel for the shapes it supports (see prefill_mfma.hip).
 bool prefill_mfma_supported(const AttnShape& sh);

@@ -29,7 +29,7 @@ constexpr int kMaxMerge = 8;
 // A operand kinds
 constexpr int kABf16 = 0;   // bf16 rows
 constexpr int kAF32 = 1;    // fp32 rows, split hi/lo into two bf16 MFMA operands
-constexpr int kAMerge = 2;  // fp32 rows formed as Σ_s w[m][s]·A_s (split-softmax merge)
+constexpr int kAMerge = 2;  // rows formed as Σ_s w[m][s]·A_s from bf16 split partials (softmax merge)
 
 // Raw A data of one lane for one k-step and one 16-row block: 8 consecutive k.
 template <int AK, int NS>
@@ -44,7 +44,7 @@ struct ARaw<kAF32, NS> {
 };
 template <int NS>
 struct ARaw<kAMerge, NS> {
-  float4 v[NS][2];
+  uint4 v[NS];  // 8 bf16 of each split
 };
 
 __device__ __forceinline__ void split_hi_lo(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
@@ -77,7 +77,8 @@ __global__ __launch_bounds__(256, MINB) void skinny_kernel(SkinnyArgs sa) {
   const int64_t b_base = static_cast<int64_t>(z) * sa.sBz;
 
   if constexpr (AK == kAMerge) {
-    // w[m][s] = 2^(m_s - max_s m_s) / Σ_s 2^(m_s - max) l_s   for this workgroup's head z
+    // w[m][s] = 2^(m_s - M) l_s / Σ_s 2^(m_s - M) l_s, M = max_s m_s, for this
+    // workgroup's head z (each split's partial is its normalised o_)
     if (tid < sa.M) {
       const int ns = min(sa.n_merge, NS);
       const float* ml = sa.ml + (static_cast<int64_t>(tid) * ns * sa.ml_heads + z) * 2;
@@ -88,8 +89,8 @@ __global__ __launch_bounds__(256, MINB) void skinny_kernel(SkinnyArgs sa) {
       float den = 0.f, e[NS];
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
-        e[j] = j < ns ? exp2f(ml[j * sa.ml_heads * 2] - mx) : 0.f;
-        if (j < ns) den += e[j] * ml[j * sa.ml_heads * 2 + 1];
+        e[j] = j < ns ? exp2f(ml[j * sa.ml_heads * 2] - mx) * ml[j * sa.ml_heads * 2 + 1] : 0.f;
+        den += e[j];
       }
       const float inv = 1.f / den;
 #pragma unroll
@@ -157,10 +158,7 @@ __global__ __launch_bounds__(256, MINB) void skinny_kernel(SkinnyArgs sa) {
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
           const int jj = j < sa.n_merge ? j : 0;
-          const float4* p =
-              reinterpret_cast<const float4*>(static_cast<const float*>(sa.A) + off + jj * sa.sAs);
-          ar[slot][i].v[j][0] = p[0];
-          ar[slot][i].v[j][1] = p[1];
+          ar[slot][i].v[j] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(sa.A) + off + jj * sa.sAs);
         }
       }
     }
@@ -185,11 +183,14 @@ __global__ __launch_bounds__(256, MINB) void skinny_kernel(SkinnyArgs sa) {
           for (int e = 0; e < 8; ++e) x[e] = 0.f;
 #pragma unroll
           for (int j = 0; j < NS; ++j) {
-            const float4 a = ar[slot][i].v[j][0], b = ar[slot][i].v[j][1];
+            const uint4 a = ar[slot][i].v[j];
             const float w = wm[i][j];
-            x[0] = fmaf(w, a.x, x[0]); x[1] = fmaf(w, a.y, x[1]); x[2] = fmaf(w, a.z, x[2]);
-            x[3] = fmaf(w, a.w, x[3]); x[4] = fmaf(w, b.x, x[4]); x[5] = fmaf(w, b.y, x[5]);
-            x[6] = fmaf(w, b.z, x[6]); x[7] = fmaf(w, b.w, x[7]);
+            const uint32_t u[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              x[2 * q] = fmaf(w, __uint_as_float(u[q] << 16), x[2 * q]);
+              x[2 * q + 1] = fmaf(w, __uint_as_float(u[q] & 0xFFFF0000u), x[2 * q + 1]);
+            }
           }
         }
         if (!kin[slot]) {

@@ -151,24 +151,25 @@ int32_t mla_decode_splits(const mla_dims* dims, int32_t batch, int32_t max_len);
 int32_t mla_decode_split_rows(const mla_dims* dims, int32_t batch, int32_t max_len);
 
 /* The attention of mla_decode without its merge and W_UV: per (sequence, split,
- * head) the partial softmax state of the split's rows, for callers that combine
- * partial results themselves (one sequence's rows spread over several devices,
- * or a projection fused downstream).  With s_l the score of row l (as in
- * mla_decode) and u_l = s_l·log2(e):
- *   part_ml[b,j,h] = (m, Σ_l 2^(u_l - m))      m: a per-split reference, base 2
- *   part_o[b,j,h,:] = Σ_l 2^(u_l - m)·c[l,:]
- * so o_ = Σ_j 2^(m_j - M)·part_o_j / Σ_j 2^(m_j - M)·l_j for any M.  An empty
- * split gives m = -inf, l = 0, part_o = 0.  m is not necessarily the true max:
- * the kernels may use any reference that keeps 2^(u_l - m) finite.
+ * head) the softmax state of the split's rows, for callers that combine partial
+ * results themselves (one sequence's rows spread over several devices, or a
+ * projection fused downstream).  With s_l the score of row l (as in mla_decode)
+ * and u_l = s_l·log2(e):
+ *   part_ml[b,j,h] = (m, l = Σ_l 2^(u_l - m))   m: a per-split reference, base 2
+ *   part_o[b,j,h,:] = Σ_l 2^(u_l - m)·c[l,:] / l  (the split's own o_)
+ * so o_ = Σ_j 2^(m_j - M)·l_j·part_o_j / Σ_j 2^(m_j - M)·l_j for any M.  An empty
+ * split gives m = -inf, l = 0, part_o = 0.  m need not be the true max: the
+ * kernels may use any reference that keeps 2^(u_l - m) finite.
  * Source: split softmax merge of the MLA principle page's attention (eq. (4)
  * computed per split of the context), the exchange a multi-device split needs.
  *   q_lat, q_pe, cache, seq_start, seq_len, max_len: as mla_decode
  *   n_split: >= 1; splits of L = ceil(max_len / n_split) rounded up to 64 rows
- *   part_o device fp32 out [batch, n_split, H, r]; part_ml device fp32 out [batch, n_split, H, 2]
+ *   part_o device out [batch, n_split, H, r] in the layer's element type (dims->dtype)
+ *   part_ml device fp32 out [batch, n_split, H, 2]
  * Needs no workspace; batch == 0 is a no-op. */
 int mla_decode_partials(const mla_dims* dims, const void* q_lat, const void* q_pe,
                         const void* cache, const int64_t* seq_start, const int32_t* seq_len,
-                        int32_t batch, int32_t max_len, int32_t n_split, float* part_o,
+                        int32_t batch, int32_t max_len, int32_t n_split, void* part_o,
                         float* part_ml, void* stream);
 
 /* Causal prefill over packed sequences.  Tokens cu_seqlens[b] .. cu_seqlens[b+1]-1

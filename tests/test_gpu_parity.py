@@ -122,9 +122,10 @@ def test_decode_reduced(torch, name, lengths):
 
 @pytest.mark.parametrize("n_split", [1, 3, None])
 def test_decode_partials_merge(torch, n_split):
-    """mla_decode_partials: the host merges the per-split partials by their stated
-    definition (float64), applies W_UV, and must match the oracle's attention on the
-    GPU-written rows; splits past a short sequence must come back empty."""
+    """mla_decode_partials: the host merges the per-split partials (each split's
+    normalised o_ and its (m, l)) by their stated definition in float64, applies
+    W_UV, and must match the oracle's attention on the GPU-written rows; splits
+    past a short sequence must come back empty."""
     import head_latent_attention_kv_amd as M
     cfg = I.CONFIGS["deepseek_v2_decode"]
     lengths = [1, 300, 2048]
@@ -135,7 +136,7 @@ def test_decode_partials_merge(torch, n_split):
     max_len = int(max(lengths))
     ns = M.mla_decode_splits(layer.dims, B, max_len) if n_split is None else n_split
     split_rows = (-(-max_len // ns) + 63) // 64 * 64
-    part_o = torch.full((B, ns, H, r), float("nan"), dtype=torch.float32, device="cuda")
+    part_o = torch.full((B, ns, H, r), float("nan"), dtype=torch.bfloat16, device="cuda")
     part_ml = torch.full((B, ns, H, 2), float("nan"), dtype=torch.float32, device="cuda")
     seq_start = torch.from_numpy(run.starts).cuda()
     seq_len = torch.from_numpy(run.lengths.astype(np.int32)).cuda()
@@ -154,10 +155,10 @@ def test_decode_partials_merge(torch, n_split):
         for j in empty:
             assert np.all(pml[b, j, :, 0] == -np.inf) and np.all(pml[b, j, :, 1] == 0), (b, j)
             assert np.all(po[b, j] == 0), (b, j)
-        m = pml[b, :, :, 0]                                   # [ns, H]
+        m, lsum = pml[b, :, :, 0], pml[b, :, :, 1]           # [ns, H]
         mx = m.max(axis=0)
-        wj = np.where(np.isneginf(m), 0.0, np.exp2(m - mx))
-        o_lat = (wj[:, :, None] * po[b]).sum(0) / (wj * pml[b, :, :, 1]).sum(0)[:, None]
+        wj = np.where(np.isneginf(m), 0.0, np.exp2(m - mx)) * lsum
+        o_lat = (wj[:, :, None] * po[b]).sum(0) / wj.sum(0)[:, None]
         out = np.einsum("hdc,hc->hd", w["w_uv"].astype(np.float64), o_lat)
         ref = Hh.oracle_decode_rows(cfg, w, None, run.x_query[b], n,
                                     cache_rows=cache_h[run.starts[b]:run.starts[b] + n])
