@@ -7,9 +7,12 @@
 // (sequence, context split): each cache tile crosses HBM -> LDS once per CU.
 //
 // Workgroup = 4 wave64s, one per SIMD, each with the whole 512-entry register
-// file.  Wave w owns heads [32w, 32w+32): their Qᵀ for the split (144 registers
-// of bf16 MFMA operands) and their fp32 accumulators O over all 512 latent
-// columns (256 AGPRs), so a wave's softmax weights never leave its registers.
+// file.  Wave w scores heads [32w, 32w+32) (their Qᵀ for the split: 144
+// registers of bf16 MFMA operands) and accumulates latent columns
+// [128w, 128w+128) of O for all 128 heads (256 fp32 registers).  Splitting the
+// PV by columns makes each wave read only its quarter of the transposed C
+// fragments, whose LDS path runs at about half the rate of plain reads; the
+// softmax weights cross between waves through a small LDS buffer instead.
 // Tiles of 32 rows:
 //   - copies HBM -> LDS by global_load_lds_dwordx4 into 4 buffers (tiles t and
 //     t+1 in use, t+2 and t+3 in flight), stored without padding; the 16-byte
@@ -21,13 +24,15 @@
 //   - softmax against a per-head reference max of the split (the first tile's
 //     max, base 2, with 2^64 of headroom); a split whose later scores pass the
 //     headroom is redone with its true max, so O is never rescaled;
-//   - PV: O[32 heads x 512] += P[32 x 32]·C[32 x 512].  P is the A operand
-//     straight from the softmax registers: a lane holds rows 4lg..4lg+3 and
-//     16+4lg..16+4lg+3 of its head, and the K order of the product is taken to
-//     be exactly that, so the transposed C fragments (ds_read_b64_tr_b16) are
-//     read at those row bases.
-// Iteration t (one barrier, for the tile ring): score of tile t+1, then PV of
-// tile t with the softmax of tile t+1 issued between its MFMAs.
+//   - softmax weights P as bf16 MFMA A fragments into a double-buffered LDS
+//     exchange [head block][lane] (8 KB a tile): a score lane holds rows
+//     4lg..4lg+3 and 16+4lg..16+4lg+3 of its head, and the K order of the PV
+//     product is taken to be exactly that;
+//   - PV: O[128 heads x 128 columns of wave w] += P[128 x 32]·C[32 x 128], the
+//     transposed C fragments (ds_read_b64_tr_b16) read at those row bases.
+// Iteration t (one barrier, for the tile ring and the P exchange): score of
+// tile t+1, then PV of tile t with the softmax of tile t+1 (and its store to
+// the exchange) issued between its MFMAs.
 // Output: normalised o_ (part_o null, one split) or the split's (m, l) and
 // its normalised o_ in bf16.
 #include <math.h>
@@ -46,7 +51,10 @@ constexpr int kHeads = 128;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTL = 32;              // rows per tile
-constexpr int kStages = 4;
+#ifndef MLA_WIDE_STAGES
+#define MLA_WIDE_STAGES 4
+#endif
+constexpr int kStages = MLA_WIDE_STAGES;
 constexpr int kRowBytes = kRW * 2;   // 1152
 constexpr int kRowChunks = kRowBytes / 16;           // 72
 constexpr int kTileBytes = kTL * kRowBytes;          // 36864
@@ -54,12 +62,21 @@ constexpr int kDmaOps = kTileBytes / 1024;           // 36 one-KB copies per til
 constexpr int kDmaPerWave = kDmaOps / kWaves;        // 9
 constexpr int kSteps = kRW / 32;                     // 18 score k-steps
 constexpr int kHW = kHeads / kWaves;                 // 32 heads per wave
-constexpr int kNB = kR / 16;                         // 32 PV column blocks
-constexpr int kLdsBytes = kStages * kTileBytes + kHeads * 4 + 64;
+constexpr int kHB = kHeads / 16;                     // 8 head blocks of the PV
+constexpr int kCB = kR / 16 / kWaves;                // 8 column blocks of 16 per wave
+constexpr int kPBytes = kHB * 64 * 16;               // one tile's softmax weights: 8 KB
+constexpr int kPOff = kStages * kTileBytes;          // P exchange, two buffers
+constexpr int kLdsBytes = kPOff + 2 * kPBytes;       // 160 KB
+// after a pass's tile loop the ring is idle: its first bytes hold the row sums
+// per head (xch) and the restart flags
+constexpr int kFlagsOff = 1024;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSlack = 64.f;
 #ifndef MLA_WIDE_SCORE_LA
 #define MLA_WIDE_SCORE_LA 2  // score k-steps of LDS fragments in flight
+#endif
+#ifndef MLA_WIDE_DMA_SPREAD
+#define MLA_WIDE_DMA_SPREAD 0  // 1: a tile's copies spread over the score k-steps
 #endif
 #ifndef MLA_WIDE_PV_LA
 #define MLA_WIDE_PV_LA 3     // PV column blocks of LDS fragments in flight
@@ -68,7 +85,9 @@ constexpr float kSlack = 64.f;
 static_assert(kDmaOps % kWaves == 0, "tile copies split evenly over the waves");
 static_assert(kRowChunks % 8 == 0, "swizzle groups of eight chunks");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+static_assert(kHeads * 4 <= kFlagsOff && kFlagsOff + 64 <= kTileBytes, "xch and flags inside tile slot 0");
 static_assert(3 * kDmaPerWave < 64, "vmcnt range");
+static_assert(2 * kDmaPerWave <= kSteps, "one tile copy per odd score k-step");
 static_assert(kTL * kRowChunks <= 2304, "row-of-chunk division by multiplication is exact below 2304");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -90,8 +109,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
     const int32_t* __restrict__ seq_len, int batch, float scale, int n_split, int split_len,
     bf16_t* __restrict__ part_o, float* __restrict__ part_ml, float* __restrict__ o_out) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  float* xch = reinterpret_cast<float*>(smem + kStages * kTileBytes);  // [kHeads]
-  int* flags = reinterpret_cast<int*>(xch + kHeads);                   // [kWaves]
+  float* xch = reinterpret_cast<float*>(smem);               // [kHeads], after the tile loop
+  int* flags = reinterpret_cast<int*>(smem + kFlagsOff);      // [kWaves], after the tile loop
 
   const int pair = blockIdx.x;
   if (pair >= batch * n_split) return;
@@ -117,21 +136,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
   // since rows are whole groups of eight chunks.  Rows past the split read a
   // chunk of its last valid row instead.  The lane index is made opaque so the
   // few offset instructions are redone per tile rather than held in registers.
-  auto issue_tile = [&](int t) {
+  auto issue_op = [&](int t, int i) {
     const int tile_row = l_begin + t * kTL;
     const int valid = min(kTL, l_end - tile_row);
     const char* tbase = cache_b + static_cast<int64_t>(tile_row) * kRowBytes;
     const uint32_t dst = lds0 + (t % kStages) * kTileBytes;
+    const int j = wave + kWaves * i;
     int ln = lane;
     __asm__ volatile("" : "+v"(ln));
-#pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) {
-      const int j = wave + kWaves * i;
+    if (valid == kTL) {
+      // whole tile: the copy's 64 chunks span rows r0 and r0 + 1 (lanes from
+      // bnd on), each with a uniform swizzle key, so a lane's offset within the
+      // copy's kilobyte is 16·lane ^ key (the key only touches bits 4..6)
+      const int r0 = (j * 64) / kRowChunks;
+      const int bnd = (r0 + 1) * kRowChunks - j * 64;
+      const int k0 = ((r0 >> 1) & 7) << 4, k1 = (((r0 + 1) >> 1) & 7) << 4;
+      const uint32_t voff = static_cast<uint32_t>((ln * 16) ^ (ln < bnd ? k0 : k1));
+      global_to_lds16(tbase + j * 1024, voff, __builtin_amdgcn_readfirstlane(dst + j * 1024));
+    } else {
+      // last tile of the split: rows past it read a chunk of its last valid row
       const int L = j * 64 + ln;
       const int r = (L * 1821) >> 17;  // L / 72 for L < 2304
       const int g = r < valid ? (L ^ ((r >> 1) & 7)) : (valid - 1) * kRowChunks + (L & 63);
       global_to_lds16(tbase, static_cast<uint32_t>(g * 16), __builtin_amdgcn_readfirstlane(dst + j * 1024));
     }
+  };
+  auto issue_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) issue_op(t, i);
   };
   auto wait_tile = [&](int t, int last_issued) {
     switch (last_issued - t) {
@@ -171,12 +203,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
   float m_ref[2] = {-INFINITY, -INFINITY};   // reference max of heads 32w + 16hb + l16 (base 2)
   float m_lane[2], l_lane[2];
   bool over = false;                         // some score passed the reference's headroom
-  f32x4 o[2][kNB];                           // O[head block][column block]
+  f32x4 o[kHB][kCB];  // O[heads 16HB + 4lg + i][columns 128w + 16j + l16]
 
   // Scaled, masked scores of tile tt: s[rb][hb] = rows 16rb + 4lg + i, head
   // 16hb + l16.  Fragments of k-step ks + 2 are read while the MFMAs of ks run;
-  // the scheduling barriers keep the compiler from hoisting more reads.
-  auto score = [&](int tt, f32x4 (&s)[2][2]) {
+  // the scheduling barriers keep the compiler from hoisting more reads.  The
+  // copies of tile t_issue (if >= 0) go out one per odd k-step, so the memory
+  // pipeline's back-pressure on their issue is spent under the MFMAs.
+  auto score = [&](int tt, f32x4 (&s)[2][2], int t_issue) {
     const unsigned char* tb = smem + (tt % kStages) * kTileBytes;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
@@ -205,6 +239,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
         fa[ks % kLA][0] = frag(ks + kLA, a_off0);
         fa[ks % kLA][1] = frag(ks + kLA, a_off1);
       }
+#if MLA_WIDE_DMA_SPREAD
+      if ((ks & 1) && (ks >> 1) < kDmaPerWave && t_issue >= 0) issue_op(t_issue, ks >> 1);
+#endif
       __builtin_amdgcn_sched_barrier(0);
     }
     const int valid = min(kTL, l_end - (l_begin + tt * kTL));  // <= 0 past the last tile
@@ -220,8 +257,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
   };
 
   // softmax weights of head block hb: P = 2^(s - m_ref) as the bf16 A operand
-  // of the PV product, K order = [rows 4lg + i, then 16 + 4lg + i]
-  auto softmax = [&](const f32x4 (&s)[2][2], int hb) -> bf16x8 {
+  // of the PV product, K order = [rows 4lg + i, then 16 + 4lg + i], stored to
+  // slot [2w + hb][lane] of P exchange buffer pbuf
+  auto softmax = [&](const f32x4 (&s)[2][2], int hb, unsigned char* pbuf) {
     const float lim = m_ref[hb] + kSlack;
     uint32_t w[4];
 #pragma unroll
@@ -238,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
       // the row sum takes the bf16 weights the PV product uses
       l_lane[hb] += bf16x2_sum(w[2 * rb]) + bf16x2_sum(w[2 * rb + 1]);
     }
-    return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+    *reinterpret_cast<uint4*>(pbuf + ((wave * 2 + hb) * 64 + lane) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   };
 
   // transposed C fragment of column block nb: lane (l16, lg) gets column
@@ -255,31 +293,39 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  // PV of tile tt with weights pa; the softmax of the next tile's scores s_next
-  // is issued between the products (into pn)
-  auto pv_softmax = [&](int tt, const bf16x8 (&pa)[2], const f32x4 (&s_next)[2][2], bf16x8 (&pn)[2]) {
+  // PV of tile tt over this wave's columns, P of all heads from exchange buffer
+  // tt % 2; the softmax of the next tile's scores s_next is issued between the
+  // products, into buffer (tt + 1) % 2
+  auto pv_softmax = [&](int tt, const f32x4 (&s_next)[2][2]) {
     const unsigned char* tb = smem + (tt % kStages) * kTileBytes;
+    const unsigned char* pb = smem + kPOff + (tt & 1) * kPBytes;
+    unsigned char* pn = smem + kPOff + ((tt + 1) & 1) * kPBytes;
     constexpr int kLA = MLA_WIDE_PV_LA;
+    bf16x8 pf[kHB];
+#pragma unroll
+    for (int hb = 0; hb < kHB; ++hb)
+      pf[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pb + (hb * 64 + lane) * 16));
     bf16x8 cf[kLA];
 #pragma unroll
-    for (int p = 0; p < kLA; ++p) cf[p] = cfrag(tb, p);
+    for (int p = 0; p < kLA; ++p) cf[p] = cfrag(tb, wave * kCB + p);
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      const bf16x8 b = cf[nb % kLA];
-      o[0][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0], b, o[0][nb], 0, 0, 0);
-      o[1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1], b, o[1][nb], 0, 0, 0);
-      if (nb + kLA < kNB) cf[nb % kLA] = cfrag(tb, nb + kLA);
-      if (nb == 8) pn[0] = softmax(s_next, 0);
-      if (nb == 20) pn[1] = softmax(s_next, 1);
+    for (int j = 0; j < kCB; ++j) {
+      const bf16x8 b = cf[j % kLA];
+#pragma unroll
+      for (int hb = 0; hb < kHB; ++hb)
+        o[hb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[hb], b, o[hb][j], 0, 0, 0);
+      if (j + kLA < kCB) cf[j % kLA] = cfrag(tb, wave * kCB + j + kLA);
+      if (j == 1) softmax(s_next, 0, pn);
+      if (j == 4) softmax(s_next, 1, pn);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int hb = 0; hb < kHB; ++hb)
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < kCB; ++j) o[hb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_lane[0] = m_lane[1] = -INFINITY;
     l_lane[0] = l_lane[1] = 0.f;
     over = false;
@@ -289,13 +335,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
       if (t < n_tiles) issue_tile(t);
     int issued = min(kStages - 1, n_tiles) - 1;
 
-    bf16x8 pa[2];  // softmax weights of tile t
     if (n_tiles > 0) {
       // prologue: tile 0; in the first pass its max sets the reference
       wait_tile(0, issued);
       lds_barrier();
       f32x4 s0[2][2];
-      score(0, s0);
+      score(0, s0, -1);
       if (pass == 0) {
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
@@ -306,25 +351,26 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
           m_ref[hb] = mx;
         }
       }
-      pa[0] = softmax(s0, 0);
-      pa[1] = softmax(s0, 1);
+      softmax(s0, 0, smem + kPOff);
+      softmax(s0, 1, smem + kPOff);
     }
 
     // iteration t: scores of tile t+1 (masked to nothing past the last tile),
     // then PV of tile t with the softmax of tile t+1 between its MFMAs
     for (int t = 0; t < n_tiles; ++t) {
       if (t + 1 < n_tiles) wait_tile(t + 1, issued);
-      lds_barrier();  // tile t+1 visible; PV(t-1) done everywhere: buffer (t-1)%4 is free
-      if (t + kStages - 1 < n_tiles) {
-        issue_tile(t + kStages - 1);
-        issued = t + kStages - 1;
-      }
+      // tile t+1 and the P of tile t visible; PV(t-1) done everywhere: ring
+      // buffer (t-1) % 4 and P buffer (t+1) % 2 are free
+      lds_barrier();
+      // tile t+3 goes to buffer (t-1) % 4, its copies spread over the score of t+1
+      const int t_issue = t + kStages - 1 < n_tiles ? t + kStages - 1 : -1;
+#if !MLA_WIDE_DMA_SPREAD
+      if (t_issue >= 0) issue_tile(t_issue);
+#endif
       f32x4 s_next[2][2];
-      score(t + 1, s_next);
-      bf16x8 pn[2];
-      pv_softmax(t, pa, s_next, pn);
-      pa[0] = pn[0];
-      pa[1] = pn[1];
+      score(t + 1, s_next, t_issue);
+      if (t_issue >= 0) issued = t_issue;
+      pv_softmax(t, s_next);
     }
     lds_barrier();
     if (lane == 0) flags[wave] = __ballot(over) != 0 ? 1 : 0;
@@ -359,24 +405,24 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
       }
     }
   }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's row sums are in LDS (read back by the same wave)
-  __builtin_amdgcn_wave_barrier();
-  // lane holds O[head 32w + 16hb + 4lg + i][column 16nb + l16]
+  lds_barrier();  // the row sums of every head are in LDS
+  // lane holds O[head 16hb + 4lg + i][column 128w + 16j + l16]
+  const int col0 = wave * kCB * 16 + l16;
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb)
+  for (int hb = 0; hb < kHB; ++hb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int h = wave * kHW + hb * 16 + lg * 4 + i;
+      const int h = hb * 16 + lg * 4 + i;
       const float lh = xch[h];
       const float inv = lh > 0.f ? 1.f / lh : 0.f;  // an empty split has l = 0 and o_ = 0
       if (!partials) {
-        float* dst = o_out + (static_cast<int64_t>(b) * kHeads + h) * kR + l16;
+        float* dst = o_out + (static_cast<int64_t>(b) * kHeads + h) * kR + col0;
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) dst[nb * 16] = o[hb][nb][i] * inv;
+        for (int j = 0; j < kCB; ++j) dst[j * 16] = o[hb][j][i] * inv;
       } else {
-        bf16_t* dst = part_o + ((static_cast<int64_t>(b) * n_split + split) * kHeads + h) * kR + l16;
+        bf16_t* dst = part_o + ((static_cast<int64_t>(b) * n_split + split) * kHeads + h) * kR + col0;
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) dst[nb * 16] = f32_to_bf16(o[hb][nb][i] * inv);
+        for (int j = 0; j < kCB; ++j) dst[j * 16] = f32_to_bf16(o[hb][j][i] * inv);
       }
     }
 }

@@ -15,6 +15,7 @@
 // tiles go to C + s*sPs; the consumer of the output sums them.
 #include <algorithm>
 
+#include "lds_dma.h"
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -257,6 +258,176 @@ __global__ __launch_bounds__(256, MINB) void skinny_kernel(SkinnyArgs sa) {
     }
 }
 
+// ---- DMA-staged variant for many column tiles, bf16 A (M <= 64) ----
+// Per-lane fragment loads read 64 bytes of each of 16 weight rows per
+// instruction, which leaves DRAM pages mostly idle (measured: ~4.9 TB/s at
+// best for that pattern against ~6.2 TB/s for runs of 512 bytes and more).
+// Here a workgroup of four waves owns 96 output columns and copies, per stage
+// of 128 k, the tile's 96 weight rows and the 64 token rows (256-byte runs of
+// each row) HBM/L2 -> LDS with global_load_lds_dwordx4, four stages in flight
+// (160 KB; two stages of 256 k measured slower).  16-byte chunk
+// p of LDS row r holds global chunk p ^ (r & 15), so the 16 rows of one MFMA
+// fragment read fall on distinct banks.  Inside a stage wave w takes k-step w
+// (32 k) for all 64 x 96 outputs; the four partial tiles are summed through LDS
+// at the end.  k past the K piece is read from a clamped address and its A
+// fragments are zeroed.
+constexpr int kDmaCols = 96;                         // 6 column blocks
+constexpr int kDmaNB = kDmaCols / 16;
+constexpr int kDmaLdsMax = 160 * 1024;
+
+// stage geometry for KC k per stage (KC = 128: four stages; 256: two)
+template <int KC>
+struct DmaStage {
+  static constexpr int kRun = KC * 2;                    // bytes of a row per stage
+  static constexpr int kRowsPerOp = 1024 / kRun;         // rows per 1 KB copy
+  static constexpr int kWOps = kDmaCols * kRun / 1024;   // weight copies per stage
+  static constexpr int kAOps = 64 * kRun / 1024;         // token-row copies per stage
+  static constexpr int kOps = kWOps + kAOps;
+  static constexpr int kOpsPerWave = kOps / 4;
+  static constexpr int kBytes = kOps * 1024;
+  static constexpr int kStages = kDmaLdsMax / kBytes;
+  static constexpr int kLds = kStages * kBytes;
+  static constexpr int kStepsPerWave = KC / 4 / kKS;     // k-steps of one wave per stage
+  static_assert(kOps % 4 == 0, "copies split evenly over the waves");
+  static_assert(kOpsPerWave * (kStages - 1) < 64, "vmcnt range");
+  static_assert(kStepsPerWave >= 1 && kRun / 16 <= 16 * 2, "swizzle covers a row's chunks");
+};
+
+template <int MB, int KC, typename OutT>
+__global__ __launch_bounds__(256, 1) void skinny_dma_kernel(SkinnyArgs sa) {
+  using G = DmaStage<KC>;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * kDmaCols;
+  const int z = blockIdx.y;
+  const int split = blockIdx.z;
+  const int k_lo = split * sa.k_per_split;
+  const int k_hi = min(sa.K, k_lo + sa.k_per_split);
+  const int n_st = k_hi > k_lo ? (k_hi - k_lo + KC - 1) / KC : 0;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)smem));
+  const bf16_t* a_mat = static_cast<const bf16_t*>(sa.A) + static_cast<int64_t>(z) * sa.sAz;
+  const int64_t b_off = static_cast<int64_t>(z) * sa.sBz;
+
+  // copy o of stage st (1 KB, R = 1024 / run rows): rows R·o' .. R·o'+R-1 of the
+  // weight tile (o < kWOps, o' = o) or of the token rows (o' = o - kWOps); the
+  // lanes of row R·o'+q fill its LDS chunks p in order.  The rows of a weight
+  // copy come from one matrix (B0 rows [0, N0), B1 the rest; N0 is a multiple
+  // of 4 and of R).
+  auto issue = [&](int st) {
+    const int kb = k_lo + st * KC;
+    const uint32_t dst = lds0 + (st % G::kStages) * G::kBytes;
+    int ln = lane;
+    __asm__ volatile("" : "+v"(ln));
+    constexpr int kLanesPerRow = G::kRun / 16;
+    const int q = ln / kLanesPerRow, p = ln % kLanesPerRow;
+#pragma unroll
+    for (int i = 0; i < G::kOpsPerWave; ++i) {
+      const int o = wave + 4 * i;
+      const bool w_op = o < G::kWOps;
+      const int o2 = w_op ? o : o - G::kWOps;
+      const int key = (o2 * G::kRowsPerOp + q) & 15;
+      int kc = kb + 8 * (p ^ key);
+      kc = kc < k_hi ? kc : k_hi - 8;
+      const char* sbase;
+      uint32_t voff;
+      if (w_op) {
+        // rows past N read row N - 1; the base row keeps every lane offset >= 0
+        const int r_base = min(n0 + o2 * G::kRowsPerOp, sa.N - 1);
+        const int r = min(n0 + o2 * G::kRowsPerOp + q, sa.N - 1);
+        const uint16_t* mat = r_base < sa.N0 ? sa.B0 + static_cast<int64_t>(r_base) * sa.sBo
+                                             : sa.B1 + static_cast<int64_t>(r_base - sa.N0) * sa.sBo;
+        sbase = reinterpret_cast<const char*>(mat + b_off);
+        voff = static_cast<uint32_t>((r - r_base) * sa.sBo + kc) * 2u;
+      } else {
+        const int m_base = min(o2 * G::kRowsPerOp, sa.M - 1);
+        const int m = min(o2 * G::kRowsPerOp + q, sa.M - 1);
+        sbase = reinterpret_cast<const char*>(a_mat + static_cast<int64_t>(m_base) * sa.sAm);
+        voff = static_cast<uint32_t>((m - m_base) * sa.sAm + kc) * 2u;
+      }
+      global_to_lds16(sbase, voff, __builtin_amdgcn_readfirstlane(dst + o * 1024));
+    }
+  };
+
+  f32x4 acc[MB][kDmaNB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < kDmaNB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // fragment reads: row t of a region, logical chunk c -> LDS chunk c ^ (t & 15);
+  // wave w takes k-steps [w S, w S + S) of the stage, S = kStepsPerWave
+#pragma unroll
+  for (int st = 0; st < G::kStages - 1; ++st)
+    if (st < n_st) issue(st);
+  int issued = min(G::kStages - 1, n_st) - 1;
+
+  for (int st = 0; st < n_st; ++st) {
+    switch (issued - st) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<G::kOpsPerWave>(); break;
+      default: wait_vmcnt<2 * G::kOpsPerWave>(); break;
+    }
+    lds_barrier();  // stage st visible; stage st-1 read everywhere: its buffer is free
+    if (st + G::kStages - 1 < n_st) {
+      issue(st + G::kStages - 1);
+      issued = st + G::kStages - 1;
+    }
+    const unsigned char* sb = smem + (st % G::kStages) * G::kBytes;
+#pragma unroll
+    for (int q = 0; q < G::kStepsPerWave; ++q) {
+      const int c_log = (wave * G::kStepsPerWave + q) * 4 + lg;
+      const int frag_off = l16 * G::kRun + ((c_log ^ l16) << 4);
+      const bool k_in = k_lo + st * KC + 8 * c_log < k_hi;
+      bf16x8 af[MB], bf[kDmaNB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(sb + G::kWOps * 1024 + i * 16 * G::kRun + frag_off);
+        af[i] = __builtin_bit_cast(bf16x8, k_in ? v : make_uint4(0, 0, 0, 0));
+      }
+#pragma unroll
+      for (int j = 0; j < kDmaNB; ++j)
+        bf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sb + j * 16 * G::kRun + frag_off));
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < kDmaNB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // sum the four waves' tiles: each wave writes its partial tile, then sums a
+  // quarter of the tile over the four copies and stores it
+  lds_barrier();  // every stage read; no copy in flight
+  float* red = reinterpret_cast<float*>(smem);  // [4 waves][MB * kDmaNB][4][64]
+  constexpr int kTile = MB * kDmaNB * 4 * 64;
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < kDmaNB; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[wave * kTile + ((i * kDmaNB + j) * 4 + e) * 64 + lane] = acc[i][j][e];
+  lds_barrier();
+  OutT* C = static_cast<OutT*>(sa.C) + static_cast<int64_t>(split) * sa.sPs + static_cast<int64_t>(z) * sa.sCz;
+  // blocks (i, j) = b handled by wave b % 4; lane holds C[m = 16i + 4lg + e][n = n0 + 16j + l16]
+#pragma unroll
+  for (int b = 0; b < MB * kDmaNB; ++b) {
+    if (b % 4 != wave) continue;
+    const int i = b / kDmaNB, j = b % kDmaNB;
+    const int n = n0 + 16 * j + l16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = (b * 4 + e) * 64 + lane;
+      const float v = red[idx] + red[kTile + idx] + red[2 * kTile + idx] + red[3 * kTile + idx];
+      const int m = 16 * i + 4 * lg + e;
+      if (n < sa.N && m < sa.M) Elem<OutT>::store(C, static_cast<int64_t>(m) * sa.sCm + n, v);
+    }
+  }
+}
+static_assert(4 * 4 * kDmaNB * 4 * 64 * 4 <= DmaStage<256>::kLds && 4 * 4 * kDmaNB * 4 * 64 * 4 <= DmaStage<128>::kLds,
+              "reduction buffer inside the ring");
+
 }  // namespace
 
 namespace {
@@ -328,12 +499,31 @@ void launch_out(const SkinnyArgs& sa, bool out_bf16, hipStream_t s) {
     hipLaunchKernelGGL((skinny_kernel<MB, NB, AK, NS, DEPTH, MINB, float>), grid, dim3(256), 0, s, sa);
 }
 
+#ifndef MLA_SKINNY_DMA_KC
+#define MLA_SKINNY_DMA_KC 128
+#endif
+template <int MB, int KC = MLA_SKINNY_DMA_KC>
+void launch_dma(const SkinnyArgs& sa, bool out_bf16, hipStream_t s) {
+  dim3 grid((sa.N + kDmaCols - 1) / kDmaCols, sa.Z, sa.splits);
+  constexpr int lds = DmaStage<KC>::kLds;
+  if (out_bf16) {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_dma_kernel<MB, KC, bf16_t>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    hipLaunchKernelGGL((skinny_dma_kernel<MB, KC, bf16_t>), grid, dim3(256), lds, s, sa);
+  } else {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_dma_kernel<MB, KC, float>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    hipLaunchKernelGGL((skinny_dma_kernel<MB, KC, float>), grid, dim3(256), lds, s, sa);
+  }
+}
+
 template <int MB>
 void launch_kind(const SkinnyArgs& sa, int kind, int ns, bool out_bf16, hipStream_t s) {
   if (kind == kABf16) {
     const Bf16Variant v = bf16_variant(sa.M, sa.N, sa.Z);
     if constexpr (MB >= 3) {
-      if (v == Bf16Variant::kWide) launch_out<MB, kWideNB, kABf16, 1, 3, 1>(sa, out_bf16, s);
+      if (v == Bf16Variant::kWide && sa.N0 % 4 == 0) launch_dma<MB>(sa, out_bf16, s);
+      else if (v == Bf16Variant::kWide) launch_out<MB, kWideNB, kABf16, 1, 3, 1>(sa, out_bf16, s);
       else launch_out<MB, 2, kABf16, 1, 4, 2>(sa, out_bf16, s);
     } else {
       launch_out<MB, 4, kABf16, 1, 3, 2>(sa, out_bf16, s);

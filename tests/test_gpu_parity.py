@@ -120,6 +120,28 @@ def test_decode_reduced(torch, name, lengths):
         assert v <= Hh.TOL[cfg.dtype], (k, v)
 
 
+@pytest.mark.parametrize("tokens", [37, 64])
+def test_absorb_wide_ragged_k(torch, tokens):
+    """mla_absorb at H=128 (24576 projection columns, the column-tiled weight
+    stream staged through LDS) with d_model = 5000, so the last k stage of the
+    projection is partial, and a ragged token count: q_lat and q_pe against the
+    oracle's query path."""
+    from oracle import mla_oracle as O
+    cfg = I.small_variant(I.CONFIGS["deepseek_v2_decode"], d_model=5000, seed=2001)
+    _print_case("absorb_wide_ragged_k", tokens=tokens, d_model=cfg.d_model)
+    layer = Hh.make_layer(cfg)
+    x = I.x_rows(cfg, 0, 0, tokens)
+    pos = np.arange(tokens) * 97 % 8192
+    q_lat, q_pe = Hh.absorb(layer, Hh.to_dev(x, cfg.dtype), pos)
+    w = layer.w_host
+    qn, qr = O.query(x, w["w_qc"], w["w_qr"], pos, n_heads=cfg.n_heads, d_nope=cfg.d_nope,
+                     d_rope=cfg.d_rope, theta=cfg.rope_theta)
+    err_lat = Hh.rel_err_rows(Hh.to_host(q_lat), O.absorbed_query(qn, w["w_uk"]))
+    err_pe = Hh.rel_err_rows(Hh.to_host(q_pe), qr)
+    print(f"absorb tokens={tokens}: q_lat={err_lat:.3e} q_pe={err_pe:.3e}")
+    assert err_lat <= Hh.TOL[cfg.dtype] and err_pe <= Hh.TOL[cfg.dtype], (err_lat, err_pe)
+
+
 @pytest.mark.parametrize("n_split", [1, 3, None])
 def test_decode_partials_merge(torch, n_split):
     """mla_decode_partials: the host merges the per-split partials (each split's
