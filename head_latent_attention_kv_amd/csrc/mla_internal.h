@@ -44,6 +44,8 @@ struct SkinnyArgs {
   int64_t sAs;
   const float* ml;
   int ml_heads, n_merge;
+  // token rows split over m_groups workgroups per column tile (0 or 1: one)
+  int m_groups;
 };
 int skinny_splits(int M, int N, int Z, int K);
 void gemm_skinny(SkinnyArgs sa, bool a_f32, bool out_bf16, hipStream_t s);

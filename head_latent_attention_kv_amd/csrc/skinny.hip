@@ -69,20 +69,25 @@ __global__ __launch_bounds__(256, MINB) void skinny_kernel(SkinnyArgs sa) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * 16 * NB;
+  // blockIdx.x = column tile x token group; this workgroup's token rows are
+  // [m0, m0 + 16 MB) of the M rows
+  const int m_groups = max(1, sa.m_groups);
+  const int n0 = (blockIdx.x / m_groups) * 16 * NB;
+  const int m0 = (blockIdx.x % m_groups) * 16 * MB;
+  const int m_last = sa.M - 1 - m0;  // last local row
   const int z = blockIdx.y;
   const int split = blockIdx.z;
   const int k_lo = split * sa.k_per_split;
   const int k_hi = min(sa.K, k_lo + sa.k_per_split);
-  const int64_t a_base = static_cast<int64_t>(z) * sa.sAz;
+  const int64_t a_base = static_cast<int64_t>(z) * sa.sAz + static_cast<int64_t>(m0) * sa.sAm;
   const int64_t b_base = static_cast<int64_t>(z) * sa.sBz;
 
   if constexpr (AK == kAMerge) {
     // w[m][s] = 2^(m_s - M) l_s / Σ_s 2^(m_s - M) l_s, M = max_s m_s, for this
     // workgroup's head z (each split's partial is its normalised o_)
-    if (tid < sa.M) {
+    if (tid < 16 * MB && tid <= m_last) {
       const int ns = min(sa.n_merge, NS);
-      const float* ml = sa.ml + (static_cast<int64_t>(tid) * ns * sa.ml_heads + z) * 2;
+      const float* ml = sa.ml + (static_cast<int64_t>(m0 + tid) * ns * sa.ml_heads + z) * 2;
       float mx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < NS; ++j)
@@ -127,7 +132,7 @@ __global__ __launch_bounds__(256, MINB) void skinny_kernel(SkinnyArgs sa) {
   float wm[MB][AK == kAMerge ? NS : 1];
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
-    const int m = min(16 * i + l16, sa.M - 1);
+    const int m = min(16 * i + l16, m_last);  // local row
     arow[i] = a_base + static_cast<int64_t>(m) * sa.sAm;
     if constexpr (AK == kAMerge) {
 #pragma unroll
@@ -243,7 +248,8 @@ __global__ __launch_bounds__(256, MINB) void skinny_kernel(SkinnyArgs sa) {
         acc[i][j][e] += red[0][i * NB + j][e][lane] + red[1][i * NB + j][e][lane] + red[2][i * NB + j][e][lane];
 
   // lane holds C[m = 16i + 4lg + e][n = n0 + 16j + l16]
-  OutT* C = static_cast<OutT*>(sa.C) + static_cast<int64_t>(split) * sa.sPs + static_cast<int64_t>(z) * sa.sCz;
+  OutT* C = static_cast<OutT*>(sa.C) + static_cast<int64_t>(split) * sa.sPs + static_cast<int64_t>(z) * sa.sCz +
+            static_cast<int64_t>(m0) * sa.sCm;
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -253,7 +259,7 @@ __global__ __launch_bounds__(256, MINB) void skinny_kernel(SkinnyArgs sa) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = 16 * i + 4 * lg + e;
-        if (m < sa.M) Elem<OutT>::store(C, static_cast<int64_t>(m) * sa.sCm + n, acc[i][j][e]);
+        if (m <= m_last) Elem<OutT>::store(C, static_cast<int64_t>(m) * sa.sCm + n, acc[i][j][e]);
       }
     }
 }
@@ -492,7 +498,7 @@ namespace {
 template <int MB, int NB, int AK, int NS, int DEPTH, int MINB>
 void launch_out(const SkinnyArgs& sa, bool out_bf16, hipStream_t s) {
   // every one of the `splits` slices is written (an empty K piece writes zeros)
-  dim3 grid((sa.N + 16 * NB - 1) / (16 * NB), sa.Z, sa.splits);
+  dim3 grid((sa.N + 16 * NB - 1) / (16 * NB) * std::max(1, sa.m_groups), sa.Z, sa.splits);
   if (out_bf16)
     hipLaunchKernelGGL((skinny_kernel<MB, NB, AK, NS, DEPTH, MINB, bf16_t>), grid, dim3(256), 0, s, sa);
   else
@@ -564,6 +570,19 @@ void gemm_skinny_merged(SkinnyArgs sa, int n_merge, bool out_bf16, hipStream_t s
   sa.n_merge = n_merge;
   sa.splits = 1;
   sa.k_per_split = k_per_split(sa.K, 1);
+  if (n_merge > 1 && sa.M > 32 && sa.M <= 64 && sa.N >= 128 && sa.Z * 2 >= 128) {
+    // the merge reads n_merge partial rows per token row: two workgroups per
+    // head take 32 token rows each, so every partial is read once and the
+    // registers freed go to a deeper prefetch over 128 columns
+    sa.m_groups = 2;
+    switch (n_merge) {
+      case 2: launch_out<2, 8, kAMerge, 2, 3, 1>(sa, out_bf16, s); break;
+      case 3: launch_out<2, 8, kAMerge, 3, 2, 1>(sa, out_bf16, s); break;
+      case 4: launch_out<2, 8, kAMerge, 4, 2, 1>(sa, out_bf16, s); break;
+      default: launch_out<2, 8, kAMerge, kMaxMerge, 1, 1>(sa, out_bf16, s); break;
+    }
+    return;
+  }
   launch(sa, n_merge <= 1 ? kAF32 : kAMerge, n_merge, out_bf16, s);
 }
 
