@@ -51,10 +51,7 @@ constexpr int kHeads = 128;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTL = 32;              // rows per tile
-#ifndef MLA_WIDE_STAGES
-#define MLA_WIDE_STAGES 4
-#endif
-constexpr int kStages = MLA_WIDE_STAGES;
+constexpr int kStages = 4;
 constexpr int kRowBytes = kRW * 2;   // 1152
 constexpr int kRowChunks = kRowBytes / 16;           // 72
 constexpr int kTileBytes = kTL * kRowBytes;          // 36864
@@ -75,9 +72,6 @@ constexpr float kSlack = 64.f;
 #ifndef MLA_WIDE_SCORE_LA
 #define MLA_WIDE_SCORE_LA 2  // score k-steps of LDS fragments in flight
 #endif
-#ifndef MLA_WIDE_DMA_SPREAD
-#define MLA_WIDE_DMA_SPREAD 0  // 1: a tile's copies spread over the score k-steps
-#endif
 #ifndef MLA_WIDE_PV_LA
 #define MLA_WIDE_PV_LA 3     // PV column blocks of LDS fragments in flight
 #endif
@@ -91,6 +85,7 @@ static_assert(2 * kDmaPerWave <= kSteps, "one tile copy per odd score k-step");
 static_assert(kTL * kRowChunks <= 2304, "row-of-chunk division by multiplication is exact below 2304");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
@@ -201,16 +196,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
   const int x_odd = ((4 + lg) ^ (l16 >> 1)) & 7;
 
   float m_ref[2] = {-INFINITY, -INFINITY};   // reference max of heads 32w + 16hb + l16 (base 2)
-  float m_lane[2], l_lane[2];
-  bool over = false;                         // some score passed the reference's headroom
+  float m_lane[2], l_lane[2];                // raw score max, bf16 weight sum of the lane
   f32x4 o[kHB][kCB];  // O[heads 16HB + 4lg + i][columns 128w + 16j + l16]
 
-  // Scaled, masked scores of tile tt: s[rb][hb] = rows 16rb + 4lg + i, head
-  // 16hb + l16.  Fragments of k-step ks + 2 are read while the MFMAs of ks run;
-  // the scheduling barriers keep the compiler from hoisting more reads.  The
-  // copies of tile t_issue (if >= 0) go out one per odd k-step, so the memory
-  // pipeline's back-pressure on their issue is spent under the MFMAs.
-  auto score = [&](int tt, f32x4 (&s)[2][2], int t_issue) {
+  // Raw scores q·k of tile tt (unscaled; rows past the split masked to -inf):
+  // s[rb][hb] = rows 16rb + 4lg + i, head 16hb + l16.  Fragments of k-step
+  // ks + 2 are read while the MFMAs of ks run; the scheduling barriers keep
+  // the compiler from hoisting more reads.
+  auto score = [&](int tt, f32x4 (&s)[2][2]) {
     const unsigned char* tb = smem + (tt % kStages) * kTileBytes;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
@@ -239,43 +232,40 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
         fa[ks % kLA][0] = frag(ks + kLA, a_off0);
         fa[ks % kLA][1] = frag(ks + kLA, a_off1);
       }
-#if MLA_WIDE_DMA_SPREAD
-      if ((ks & 1) && (ks >> 1) < kDmaPerWave && t_issue >= 0) issue_op(t_issue, ks >> 1);
-#endif
       __builtin_amdgcn_sched_barrier(0);
     }
     const int valid = min(kTL, l_end - (l_begin + tt * kTL));  // <= 0 past the last tile
+    if (valid < kTL) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
+        for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = s[rb][hb][i] * qk_scale;
-          s[rb][hb][i] = (rb * 16 + lg * 4 + i < valid) ? v : -INFINITY;
-        }
+          for (int i = 0; i < 4; ++i)
+            if (rb * 16 + lg * 4 + i >= valid) s[rb][hb][i] = -INFINITY;
+    }
   };
 
-  // softmax weights of head block hb: P = 2^(s - m_ref) as the bf16 A operand
-  // of the PV product, K order = [rows 4lg + i, then 16 + 4lg + i], stored to
-  // slot [2w + hb][lane] of P exchange buffer pbuf
-  auto softmax = [&](const f32x4 (&s)[2][2], int hb, unsigned char* pbuf) {
-    const float lim = m_ref[hb] + kSlack;
-    uint32_t w[4];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const f32x4 v = s[rb][hb];
-      m_lane[hb] = fmaxf(m_lane[hb], fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-      over = over || (v[0] > lim) || (v[1] > lim) || (v[2] > lim) || (v[3] > lim);
-      const float p0 = __builtin_amdgcn_exp2f(v[0] - m_ref[hb]);
-      const float p1 = __builtin_amdgcn_exp2f(v[1] - m_ref[hb]);
-      const float p2 = __builtin_amdgcn_exp2f(v[2] - m_ref[hb]);
-      const float p3 = __builtin_amdgcn_exp2f(v[3] - m_ref[hb]);
-      w[2 * rb] = pack_bf16x2(p0, p1);
-      w[2 * rb + 1] = pack_bf16x2(p2, p3);
-      // the row sum takes the bf16 weights the PV product uses
-      l_lane[hb] += bf16x2_sum(w[2 * rb]) + bf16x2_sum(w[2 * rb + 1]);
-    }
+  // softmax weights P = 2^(s·scale·log2(e) - m_ref) of rows 16rb + 4lg + (0..3)
+  // of head block hb, packed bf16 into w[2rb], w[2rb + 1]: half of the bf16 A
+  // operand of the PV product, whose K order is [rows 4lg + i, then 16 + 4lg + i].
+  // The row sum takes the bf16 weights the PV product uses (v_dot2 with ones).
+  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+  auto soft_part = [&](const f32x4 (&s)[2][2], int hb, int rb, uint32_t (&w)[4]) {
+    const f32x4 v = s[rb][hb];
+    m_lane[hb] = fmaxf(m_lane[hb], fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+    const float nm = -m_ref[hb];
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(v[0], qk_scale, nm));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(v[1], qk_scale, nm));
+    const float p2 = __builtin_amdgcn_exp2f(fmaf(v[2], qk_scale, nm));
+    const float p3 = __builtin_amdgcn_exp2f(fmaf(v[3], qk_scale, nm));
+    w[2 * rb] = pack_bf16x2(p0, p1);
+    w[2 * rb + 1] = pack_bf16x2(p2, p3);
+    l_lane[hb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[2 * rb]), ones, l_lane[hb], false);
+    l_lane[hb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[2 * rb + 1]), ones, l_lane[hb], false);
+  };
+  // store head block hb's weights to slot [2w + hb][lane] of exchange buffer pbuf
+  auto soft_store = [&](const uint32_t (&w)[4], int hb, unsigned char* pbuf) {
     *reinterpret_cast<uint4*>(pbuf + ((wave * 2 + hb) * 64 + lane) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   };
 
@@ -294,8 +284,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
   };
 
   // PV of tile tt over this wave's columns, P of all heads from exchange buffer
-  // tt % 2; the softmax of the next tile's scores s_next is issued between the
-  // products, into buffer (tt + 1) % 2
+  // tt % 2; the softmax of the next tile's scores s_next is issued in four
+  // pieces between the products, into buffer (tt + 1) % 2
   auto pv_softmax = [&](int tt, const f32x4 (&s_next)[2][2]) {
     const unsigned char* tb = smem + (tt % kStages) * kTileBytes;
     const unsigned char* pb = smem + kPOff + (tt & 1) * kPBytes;
@@ -306,6 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
     for (int hb = 0; hb < kHB; ++hb)
       pf[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pb + (hb * 64 + lane) * 16));
     bf16x8 cf[kLA];
+    uint32_t wn[4];
 #pragma unroll
     for (int p = 0; p < kLA; ++p) cf[p] = cfrag(tb, wave * kCB + p);
 #pragma unroll
@@ -315,8 +306,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
       for (int hb = 0; hb < kHB; ++hb)
         o[hb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[hb], b, o[hb][j], 0, 0, 0);
       if (j + kLA < kCB) cf[j % kLA] = cfrag(tb, wave * kCB + j + kLA);
-      if (j == 1) softmax(s_next, 0, pn);
-      if (j == 4) softmax(s_next, 1, pn);
+      if (j == 1) soft_part(s_next, 0, 0, wn);
+      if (j == 2) { soft_part(s_next, 0, 1, wn); soft_store(wn, 0, pn); }
+      if (j == 4) soft_part(s_next, 1, 0, wn);
+      if (j == 5) { soft_part(s_next, 1, 1, wn); soft_store(wn, 1, pn); }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -328,7 +321,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
       for (int j = 0; j < kCB; ++j) o[hb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_lane[0] = m_lane[1] = -INFINITY;
     l_lane[0] = l_lane[1] = 0.f;
-    over = false;
 
 #pragma unroll
     for (int t = 0; t < kStages - 1; ++t)
@@ -340,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
       wait_tile(0, issued);
       lds_barrier();
       f32x4 s0[2][2];
-      score(0, s0, -1);
+      score(0, s0);
       if (pass == 0) {
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
@@ -348,11 +340,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
                            fmaxf(fmaxf(s0[1][hb][0], s0[1][hb][1]), fmaxf(s0[1][hb][2], s0[1][hb][3])));
           mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
           mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-          m_ref[hb] = mx;
+          m_ref[hb] = mx * qk_scale;
         }
       }
-      softmax(s0, 0, smem + kPOff);
-      softmax(s0, 1, smem + kPOff);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        uint32_t w[4];
+        soft_part(s0, hb, 0, w);
+        soft_part(s0, hb, 1, w);
+        soft_store(w, hb, smem + kPOff);
+      }
     }
 
     // iteration t: scores of tile t+1 (masked to nothing past the last tile),
@@ -362,16 +359,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
       // tile t+1 and the P of tile t visible; PV(t-1) done everywhere: ring
       // buffer (t-1) % 4 and P buffer (t+1) % 2 are free
       lds_barrier();
-      // tile t+3 goes to buffer (t-1) % 4, its copies spread over the score of t+1
-      const int t_issue = t + kStages - 1 < n_tiles ? t + kStages - 1 : -1;
-#if !MLA_WIDE_DMA_SPREAD
-      if (t_issue >= 0) issue_tile(t_issue);
-#endif
+      if (t + kStages - 1 < n_tiles) {  // tile t+3 into buffer (t-1) % 4
+        issue_tile(t + kStages - 1);
+        issued = t + kStages - 1;
+      }
       f32x4 s_next[2][2];
-      score(t + 1, s_next, t_issue);
-      if (t_issue >= 0) issued = t_issue;
+      score(t + 1, s_next);
       pv_softmax(t, s_next);
     }
+    // restart when some score passed its reference's headroom (raw max of the
+    // lane's head times the scale; the scale is positive)
+    const bool over = m_lane[0] * qk_scale > m_ref[0] + kSlack || m_lane[1] * qk_scale > m_ref[1] + kSlack;
     lds_barrier();
     if (lane == 0) flags[wave] = __ballot(over) != 0 ? 1 : 0;
     lds_barrier();
@@ -383,7 +381,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
       float mx = m_lane[hb];
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      m_ref[hb] = mx;
+      m_ref[hb] = mx * qk_scale;
     }
     lds_barrier();  // every wave has read the flags before they are rewritten
   }

@@ -3,7 +3,7 @@ the C ABI, and the oracle on the same inputs.  Test infrastructure only."""
 from __future__ import annotations
 
 import dataclasses
-from typing import Dict, List, Optional
+from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
@@ -91,8 +91,22 @@ def raw_to_dev(a: np.ndarray, dtype: str, device="cuda"):
     return t.to(torch.bfloat16) if dtype == "bf16" else t
 
 
+def key_rows(cfg, b: int, c0: int, c1: int, n: int, x_scale: float = 1.0,
+             key_boost: Optional[Tuple[int, float]] = None) -> np.ndarray:
+    """Unrounded hidden states of rows [c0, c1) of sequence b (length n).  With
+    key_boost = (p0, f), rows at positions p0 <= p < n - 1 are multiplied by f
+    (the query row n - 1 is not), so later keys score far above the first ones."""
+    x = I.x_rows(cfg, b, c0, c1, scale=x_scale, quantized=False)
+    if key_boost is not None:
+        p0, f = key_boost
+        pos = np.arange(c0, c1)
+        x = np.where(((pos >= p0) & (pos < n - 1))[:, None], x * np.float32(f), x).astype(np.float32)
+    return x
+
+
 def build_decode(layer: DeviceLayer, lengths: np.ndarray, x_scale: float = 1.0,
-                 chunk: int = 8192, threads: int = 8) -> DecodeRun:
+                 chunk: int = 8192, threads: int = 8,
+                 key_boost: Optional[Tuple[int, float]] = None) -> DecodeRun:
     """Fill a packed cache for sequences of the given lengths with mla_write_cache,
     absorb each sequence's last token, run mla_decode."""
     import concurrent.futures as cf
@@ -111,7 +125,7 @@ def build_decode(layer: DeviceLayer, lengths: np.ndarray, x_scale: float = 1.0,
 
     def gen(job):
         b, c0, c1 = job
-        return job, I.x_rows(cfg, b, c0, c1, scale=x_scale, quantized=False)
+        return job, key_rows(cfg, b, c0, c1, int(lengths[b]), x_scale, key_boost)
 
     with cf.ThreadPoolExecutor(max_workers=threads) as ex:
         for (b, c0, c1), xb in ex.map(gen, jobs):
@@ -200,6 +214,29 @@ def oracle_decode_rows(cfg, w, x_keys: np.ndarray, x_query: np.ndarray, n: int,
                             np.zeros(1, int), np.zeros(n, int), cfg.softmax_scale)
         out.append(o[0, 0])
     return np.stack(out)
+
+
+def oracle_absorbed_rows(cfg, w, q_lat: np.ndarray, q_pe: np.ndarray, cache_rows: np.ndarray,
+                         head_chunk: int = 16) -> np.ndarray:
+    """Oracle output [H, d_v] of one decode query given the query the kernels see
+    (the GPU's q_lat [H, r] and q_pe [H, d_rope]) and the GPU-written rows: the
+    oracle's attention definition with Q = [q_lat ; q_pe], K = [c ; kr_g(h)] and
+    V = c per head, then W_UV.  For logits so large that the bf16 rounding of the
+    query alone moves the softmax (the oracle's own query is float64)."""
+    from oracle import mla_oracle as O
+    n = cache_rows.shape[0]
+    c, kr = O.split_rows(cache_rows, cfg.rank, cfg.n_groups, cfg.d_rope)
+    g_of_h = O.head_groups(cfg.n_heads, cfg.n_groups)
+    out = np.zeros((cfg.n_heads, cfg.d_v))
+    allowed = np.ones((1, n), bool)
+    for h0 in range(0, cfg.n_heads, head_chunk):
+        hs = np.arange(h0, min(cfg.n_heads, h0 + head_chunk))
+        Q = np.concatenate([q_lat[hs], q_pe[hs]], axis=-1)[None]                      # [1, hc, r + dr]
+        K = np.concatenate([np.repeat(c[:, None, :], len(hs), 1), kr[:, g_of_h[hs], :]], axis=-1)
+        V = np.repeat(c[:, None, :], len(hs), 1)
+        o_lat = O.softmax_attention(Q, K, V, allowed, cfg.softmax_scale)[0]           # [hc, r]
+        out[hs] = np.einsum("hvc,hc->hv", w["w_uv"][hs].astype(np.float64), o_lat)
+    return out
 
 
 def rel_err_rows(got: np.ndarray, ref: np.ndarray) -> float:

@@ -120,6 +120,33 @@ def test_decode_reduced(torch, name, lengths):
         assert v <= Hh.TOL[cfg.dtype], (k, v)
 
 
+@pytest.mark.parametrize("name,lengths", [("deepseek_v2_decode", [700, 2100, 90]),
+                                          ("qwen25_7b_decode", [1500, 333])])
+def test_decode_restart(torch, name, lengths):
+    """Keys from position 40 on are scaled 30x (the query row is not), so the
+    scores of later tiles pass the first tile's reference by 96..224 (log2) in
+    every head, far beyond its 2^64 headroom, and the attention kernels take
+    their second pass with the true maximum.  Logits this large make the bf16
+    rounding of the query itself move the softmax by ~10%, so the reference is
+    the oracle's attention definition on the query and rows the kernel reads."""
+    cfg = I.CONFIGS[name]
+    _print_case("decode_restart", cfg=name, lengths=lengths)
+    boost = (40, 30.0)
+    layer = Hh.make_layer(cfg)
+    run = Hh.build_decode(layer, np.array(lengths), key_boost=boost)
+    got = Hh.to_host(run.out)
+    cache_h = Hh.to_host(run.cache)
+    err = 0.0
+    for b, n in enumerate(run.lengths):
+        n = int(n)
+        rows_gpu = cache_h[run.starts[b]:run.starts[b] + n]
+        ref = Hh.oracle_absorbed_rows(cfg, layer.w_host, Hh.to_host(run.q_lat[b]), Hh.to_host(run.q_pe[b]),
+                                      rows_gpu)
+        err = max(err, Hh.rel_err_rows(got[b], ref))
+    print(f"{name} restart {lengths}: attn={err:.3e}")
+    assert err <= Hh.TOL[cfg.dtype], err
+
+
 @pytest.mark.parametrize("tokens", [37, 64])
 def test_absorb_wide_ragged_k(torch, tokens):
     """mla_absorb at H=128 (24576 projection columns, the column-tiled weight
