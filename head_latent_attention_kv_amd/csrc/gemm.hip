@@ -206,6 +206,137 @@ __global__ __launch_bounds__(256) void gemm_f32_valu(GemmArgs g) {
     static_cast<float*>(g.C)[static_cast<int64_t>(z) * g.sCz + static_cast<int64_t>(m) * g.sCm + n] = acc;
 }
 
+// ---- few-token product with an n-contiguous weight (q_lat = q_nope · W_UK) ----
+// For M <= 64 rows of fp32 A and B[z] = [K][N] bf16 (n contiguous): one
+// workgroup per (z, 256-column slice of N).  A is split once into hi + lo bf16
+// rows in LDS (rows padded by 16 bytes: the 16 rows of a fragment read fall on
+// distinct banks); the [K][256] slice of B goes to LDS with its 32-byte column
+// units XOR-swizzled by f(k) = (k & 3) + 4((k >> 3) & 1), so the eight rows one
+// half-wave of a transposed read touches land on distinct banks.  B fragments
+// come from ds_read_b64_tr_b16 (lane n gets 4 consecutive k of column n); wave w
+// computes columns [64w, 64w + 64) of the slice for all M rows, K in chunks of
+// 128 staged one at a time.
+constexpr int kUkCols = 256;                  // columns per workgroup
+constexpr int kUkK = 128;                     // k per staged chunk
+constexpr int kUkBPitch = kUkCols * 2;        // 512 B per B row (swizzled, unpadded)
+constexpr int kUkAPitch = kUkK * 2 + 16;      // 272 B per A row
+constexpr int kUkLds = kUkK * kUkBPitch + 2 * 64 * kUkAPitch;
+
+typedef short uk_s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uk_s16x4 uk_lds_s16x4;
+
+__device__ __forceinline__ int uk_unit(int k, int u) { return u ^ ((k & 3) + 4 * ((k >> 3) & 1)); }
+
+template <int MB, typename OutT>
+__global__ __launch_bounds__(256) void gemm_uk_kernel(GemmArgs g) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* sB = smem;
+  unsigned char* sAh = smem + kUkK * kUkBPitch;
+  unsigned char* sAl = sAh + 64 * kUkAPitch;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * kUkCols;
+  const int z = blockIdx.y;
+  const float* A = static_cast<const float*>(g.A) + static_cast<int64_t>(z) * g.sAz;
+  const bf16_t* B = static_cast<const bf16_t*>(g.B) + static_cast<int64_t>(z) * g.sBz;
+
+  f32x4 acc[MB][4];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = 0; k0 < g.K; k0 += kUkK) {
+    if (k0 > 0) __syncthreads();  // the previous chunk is consumed
+    // B chunk: rows k0 .. k0+127, 32 chunks of 16 B per row (zero past K or N)
+#pragma unroll
+    for (int i = 0; i < kUkK * 32 / 256; ++i) {
+      const int c = tid + 256 * i;
+      const int kr = c >> 5, ch = c & 31;
+      const int k = k0 + kr, n = n0 + ch * 8;
+      const uint4 v = (k < g.K && n < g.N)
+          ? *reinterpret_cast<const uint4*>(B + static_cast<int64_t>(k) * g.sBo + n)
+          : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(sB + kr * kUkBPitch + (uk_unit(kr, ch >> 1) * 2 + (ch & 1)) * 16) = v;
+    }
+    // A chunk: rows 0..16MB-1, 32 float4 per row, split into hi and lo bf16
+#pragma unroll
+    for (int i = 0; i < MB * 16 * 32 / 256; ++i) {
+      const int c = tid + 256 * i;
+      const int m = c >> 5, kc = (c & 31) * 4;
+      const int k = k0 + kc;
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (m < g.M && k < g.K) a = *reinterpret_cast<const float4*>(A + static_cast<int64_t>(m) * g.sAm + k);
+      const uint32_t h0 = pack_bf16x2(a.x, a.y), h1 = pack_bf16x2(a.z, a.w);
+      const uint32_t l0 = pack_bf16x2(a.x - __uint_as_float(h0 << 16), a.y - __uint_as_float(h0 & 0xFFFF0000u));
+      const uint32_t l1 = pack_bf16x2(a.z - __uint_as_float(h1 << 16), a.w - __uint_as_float(h1 & 0xFFFF0000u));
+      *reinterpret_cast<uint2*>(sAh + m * kUkAPitch + kc * 2) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(sAl + m * kUkAPitch + kc * 2) = make_uint2(l0, l1);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kUkK / 32; ++ks) {
+      bf16x8 ah[MB], al[MB], bf[4];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int off = (i * 16 + l16) * kUkAPitch + (ks * 32 + lg * 8) * 2;
+        ah[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sAh + off));
+        al[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sAl + off));
+      }
+      // lane s of each 16-lane group addresses row base + s/4, columns c0 + 4(s%4)..+3
+      // of its 16-column unit; it receives column c0 + s at rows base..base+3
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int u = wave * 4 + j;  // 16-column unit within the slice (32 B)
+        const int r_lo = ks * 32 + lg * 8 + (l16 >> 2), r_hi = r_lo + 4;
+        const int cb = (l16 & 3) * 8;  // byte offset of columns 4(s%4) within the unit
+        const uk_s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (uk_lds_s16x4*)(sB + r_lo * kUkBPitch + uk_unit(r_lo, u) * 32 + cb));
+        const uk_s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (uk_lds_s16x4*)(sB + r_hi * kUkBPitch + uk_unit(r_hi, u) * 32 + cb));
+        bf[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+    }
+  }
+
+  // lane holds C[m = 16i + 4lg + e][n = n0 + 64w + 16j + l16]
+  OutT* C = static_cast<OutT*>(g.C) + static_cast<int64_t>(z) * g.sCz;
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wave * 64 + j * 16 + l16;
+      if (n >= g.N) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = i * 16 + lg * 4 + e;
+        if (m < g.M) Elem<OutT>::store(C, static_cast<int64_t>(m) * g.sCm + n, acc[i][j][e]);
+      }
+    }
+}
+
+template <int MB>
+void launch_uk(const GemmArgs& g, bool out_bf16, hipStream_t s) {
+  dim3 grid((g.N + kUkCols - 1) / kUkCols, g.Z);
+  if (out_bf16) {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_uk_kernel<MB, bf16_t>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, kUkLds);
+    hipLaunchKernelGGL((gemm_uk_kernel<MB, bf16_t>), grid, dim3(256), kUkLds, s, g);
+  } else {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_uk_kernel<MB, float>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, kUkLds);
+    hipLaunchKernelGGL((gemm_uk_kernel<MB, float>), grid, dim3(256), kUkLds, s, g);
+  }
+}
+
 template <int BM, int BN, bool A_F32, bool B_KN>
 void launch_bf16(const GemmArgs& g, bool out_bf16, hipStream_t s) {
   dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, g.Z);
@@ -234,6 +365,17 @@ void gemm(const GemmArgs& g, int dtype, bool a_f32, bool b_kn, bool out_bf16, hi
     dim3 grid((g.N + 15) / 16, (g.M + 15) / 16, g.Z);
     if (b_kn) hipLaunchKernelGGL(gemm_f32_valu<true>, grid, dim3(256), 0, s, g);
     else hipLaunchKernelGGL(gemm_f32_valu<false>, grid, dim3(256), 0, s, g);
+    return;
+  }
+  if (a_f32 && b_kn && g.M <= 64 && g.K % 32 == 0 && g.N % 8 == 0 && g.sBo % 8 == 0 && g.sAm % 4 == 0 &&
+      g.sAz % 4 == 0) {
+    // few rows against an n-contiguous weight: the transposed-read kernel
+    switch ((g.M + 15) / 16) {
+      case 1: launch_uk<1>(g, out_bf16, s); break;
+      case 2: launch_uk<2>(g, out_bf16, s); break;
+      case 3: launch_uk<3>(g, out_bf16, s); break;
+      default: launch_uk<4>(g, out_bf16, s); break;
+    }
     return;
   }
   // Large problems: 128x128 tiles; otherwise 64x64 for more blocks.
