@@ -249,25 +249,37 @@ __global__ __launch_bounds__(256) void gemm_uk_kernel(GemmArgs g) {
 
   for (int k0 = 0; k0 < g.K; k0 += kUkK) {
     if (k0 > 0) __syncthreads();  // the previous chunk is consumed
-    // B chunk: rows k0 .. k0+127, 32 chunks of 16 B per row (zero past K or N)
+    // B chunk: rows k0 .. k0+127, 32 chunks of 16 B per row; A chunk: rows
+    // 0 .. 16MB-1, 32 float4 per row.  Every load is issued before any store,
+    // from a clamped (valid) address, and zeroed past K, N or M afterwards.
+    constexpr int kBLoads = kUkK * 32 / 256, kALoads = MB * 16 * 32 / 256;
+    uint4 bv[kBLoads];
+    float4 av[kALoads];
 #pragma unroll
-    for (int i = 0; i < kUkK * 32 / 256; ++i) {
+    for (int i = 0; i < kBLoads; ++i) {
+      const int c = tid + 256 * i;
+      const int k = k0 + (c >> 5), n = n0 + (c & 31) * 8;
+      bv[i] = *reinterpret_cast<const uint4*>(B + static_cast<int64_t>(min(k, g.K - 1)) * g.sBo + min(n, g.N - 8));
+    }
+#pragma unroll
+    for (int i = 0; i < kALoads; ++i) {
+      const int c = tid + 256 * i;
+      const int m = c >> 5, k = k0 + (c & 31) * 4;
+      av[i] = *reinterpret_cast<const float4*>(A + static_cast<int64_t>(min(m, g.M - 1)) * g.sAm + min(k, g.K - 4));
+    }
+#pragma unroll
+    for (int i = 0; i < kBLoads; ++i) {
       const int c = tid + 256 * i;
       const int kr = c >> 5, ch = c & 31;
-      const int k = k0 + kr, n = n0 + ch * 8;
-      const uint4 v = (k < g.K && n < g.N)
-          ? *reinterpret_cast<const uint4*>(B + static_cast<int64_t>(k) * g.sBo + n)
-          : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(sB + kr * kUkBPitch + (uk_unit(kr, ch >> 1) * 2 + (ch & 1)) * 16) = v;
+      const bool ok = k0 + kr < g.K && n0 + ch * 8 < g.N;
+      *reinterpret_cast<uint4*>(sB + kr * kUkBPitch + (uk_unit(kr, ch >> 1) * 2 + (ch & 1)) * 16) =
+          ok ? bv[i] : make_uint4(0, 0, 0, 0);
     }
-    // A chunk: rows 0..16MB-1, 32 float4 per row, split into hi and lo bf16
 #pragma unroll
-    for (int i = 0; i < MB * 16 * 32 / 256; ++i) {
+    for (int i = 0; i < kALoads; ++i) {
       const int c = tid + 256 * i;
       const int m = c >> 5, kc = (c & 31) * 4;
-      const int k = k0 + kc;
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (m < g.M && k < g.K) a = *reinterpret_cast<const float4*>(A + static_cast<int64_t>(m) * g.sAm + k);
+      const float4 a = (m < g.M && k0 + kc < g.K) ? av[i] : make_float4(0.f, 0.f, 0.f, 0.f);
       const uint32_t h0 = pack_bf16x2(a.x, a.y), h1 = pack_bf16x2(a.z, a.w);
       const uint32_t l0 = pack_bf16x2(a.x - __uint_as_float(h0 << 16), a.y - __uint_as_float(h0 & 0xFFFF0000u));
       const uint32_t l1 = pack_bf16x2(a.z - __uint_as_float(h1 << 16), a.w - __uint_as_float(h1 & 0xFFFF0000u));

@@ -61,17 +61,22 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// RoPE angle p * theta^(-2j/d) formed in double precision, then reduced to
-// cos/sin.  Long contexts (p ~ 1e5) need the product in double: an fp32 angle
-// at that magnitude is off by ~1e-2 rad.
-__device__ __forceinline__ void rope_cos_sin(int32_t pos, int j, int d_rope, double theta, float* c,
-                                             float* s) {
-  double inv_freq = pow(theta, -2.0 * static_cast<double>(j) / static_cast<double>(d_rope));
-  double ang = static_cast<double>(pos) * inv_freq;
-  double sd, cd;
-  sincos(ang, &sd, &cd);
-  *c = static_cast<float>(cd);
-  *s = static_cast<float>(sd);
+// RoPE angle p·θ^(-2j/d) and its cos/sin.  The frequency is base^j with
+// base = θ^(-2/d) (computed by the host in double), raised by squaring in
+// double; the angle p·base^j is formed and reduced to [-π, π] in double, since
+// an fp32 angle at p ~ 1e5 is off by ~1e-2 rad.  Only the reduced angle goes
+// through fp32 sin/cos (error ~1e-7 for |x| <= π).
+__device__ __forceinline__ void rope_cos_sin(int32_t pos, int j, double base, float* c, float* s) {
+  double f = 1.0, b = base;
+  for (int e = j; e != 0; e >>= 1) {
+    if (e & 1) f *= b;
+    b *= b;
+  }
+  const double ang = static_cast<double>(pos) * f;
+  constexpr double kTwoPi = 6.283185307179586476925;
+  const double k = rint(ang * (1.0 / kTwoPi));
+  const float r = static_cast<float>(fma(-k, kTwoPi, ang));
+  sincosf(r, s, c);
 }
 
 }  // namespace mla

@@ -2,8 +2,9 @@
 //  - cache rows: optional unit-gain RMSNorm over the latent, rotate-half RoPE of
 //    each rotary-key group at the token's position, cast, store to its slot;
 //  - query rotary part: RoPE of q_pe per head.
-// RoPE pairs dims (j, j + d/2), angle p·θ^(-2j/d) formed in double.
+// RoPE pairs dims (j, j + d/2), angle p·θ^(-2j/d) formed and reduced in double.
 #include <algorithm>
+#include <cmath>
 
 #include "mla_device.h"
 #include "mla_internal.h"
@@ -14,7 +15,7 @@ namespace {
 
 constexpr int kMaxHalf = 256;  // rotary pairs per group supported by the shared cos/sin table
 
-template <typename T>
+template <typename T, int kSlices>
 __global__ __launch_bounds__(256) void cache_rows_kernel(const float* __restrict__ proj, int64_t ld,
                                                          int splits, int64_t sps,
                                                          T* __restrict__ cache,
@@ -22,25 +23,33 @@ __global__ __launch_bounds__(256) void cache_rows_kernel(const float* __restrict
                                                          const int32_t* __restrict__ positions,
                                                          int r, int n_groups, int d_rope,
                                                          int latent_rmsnorm, float eps,
-                                                         double theta) {
+                                                         double rope_base) {
   __shared__ float row[1024];  // summed projection row (r + G*d_rope <= 1024)
   __shared__ float cs[kMaxHalf], sn[kMaxHalf];
   __shared__ float red[4];
   const int64_t t = blockIdx.x;
   const int row_w = r + n_groups * d_rope;
   const int half = d_rope / 2;
-  for (int i = threadIdx.x; i < row_w; i += blockDim.x) {
-    // all slices' loads issued before the sum (splits <= 16)
-    float part[16];
+  // every slice load of this thread's (up to four) elements goes out first,
+  // from clamped addresses so no branch splits them (splits <= kSlices)
+  constexpr int kIt = 1024 / 256;
+  float part[kIt][kSlices];
 #pragma unroll
-    for (int p = 0; p < 16; ++p) part[p] = p < splits ? proj[p * sps + t * ld + i] : 0.f;
-    float v = 0.f;
+  for (int it = 0; it < kIt; ++it) {
+    const int i = min(static_cast<int>(threadIdx.x) + 256 * it, row_w - 1);
 #pragma unroll
-    for (int p = 0; p < 16; ++p) v += part[p];
-    row[i] = v;
+    for (int p = 0; p < kSlices; ++p) part[it][p] = proj[min(p, splits - 1) * sps + t * ld + i];
   }
   const int32_t pos = positions[t];
-  for (int j = threadIdx.x; j < half; j += blockDim.x) rope_cos_sin(pos, j, d_rope, theta, &cs[j], &sn[j]);
+  for (int j = threadIdx.x; j < half; j += blockDim.x) rope_cos_sin(pos, j, rope_base, &cs[j], &sn[j]);
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int i = static_cast<int>(threadIdx.x) + 256 * it;
+    float v = 0.f;
+#pragma unroll
+    for (int p = 0; p < kSlices; ++p) v += p < splits ? part[it][p] : 0.f;
+    if (i < row_w) row[i] = v;
+  }
   __syncthreads();
   T* dst = cache + slots[t] * static_cast<int64_t>(row_w);
 
@@ -69,13 +78,10 @@ template <typename T>
 __global__ __launch_bounds__(256) void query_rope_kernel(const float* __restrict__ proj, int64_t ld,
                                                          T* __restrict__ q_pe,
                                                          const int32_t* __restrict__ positions,
-                                                         int n_heads, int d_rope, double theta) {
-  __shared__ float cs[kMaxHalf], sn[kMaxHalf];
+                                                         int n_heads, int d_rope, double rope_base) {
   const int64_t t = blockIdx.x;
   const int half = d_rope / 2;
   const int32_t pos = positions[t];
-  for (int j = threadIdx.x; j < half; j += blockDim.x) rope_cos_sin(pos, j, d_rope, theta, &cs[j], &sn[j]);
-  __syncthreads();
   const float* src = proj + t * ld;
   T* dst = q_pe + t * static_cast<int64_t>(n_heads) * d_rope;
   // blockIdx.y picks a slice of the (head, pair) items so one token's heads
@@ -84,10 +90,13 @@ __global__ __launch_bounds__(256) void query_rope_kernel(const float* __restrict
   const int per = (items + gridDim.y - 1) / gridDim.y;
   const int lo = blockIdx.y * per, hi = min(items, lo + per);
   for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) {
+    // the pair's loads go out before its angle is formed
     const int h = i / half, j = i % half;
     const float a = src[h * d_rope + j], b = src[h * d_rope + j + half];
-    Elem<T>::store(dst, h * d_rope + j, a * cs[j] - b * sn[j]);
-    Elem<T>::store(dst, h * d_rope + j + half, b * cs[j] + a * sn[j]);
+    float c, sn;
+    rope_cos_sin(pos, j, rope_base, &c, &sn);
+    Elem<T>::store(dst, h * d_rope + j, a * c - b * sn);
+    Elem<T>::store(dst, h * d_rope + j + half, b * c + a * sn);
   }
 }
 
@@ -98,29 +107,36 @@ void finalize_cache_rows(int dtype, const float* proj, int64_t ld, int splits, i
                          int64_t n_tokens, int r, int n_groups, int d_rope, int latent_rmsnorm,
                          float eps, double theta, hipStream_t s) {
   if (n_tokens <= 0) return;
+  const double base = std::pow(theta, -2.0 / d_rope);
   dim3 grid(static_cast<unsigned>(n_tokens));
-  if (dtype == kF32)
-    hipLaunchKernelGGL(cache_rows_kernel<float>, grid, dim3(256), 0, s, proj, ld, splits, sps,
-                       static_cast<float*>(cache), slots, positions, r, n_groups, d_rope,
-                       latent_rmsnorm, eps, theta);
-  else
-    hipLaunchKernelGGL(cache_rows_kernel<bf16_t>, grid, dim3(256), 0, s, proj, ld, splits, sps,
-                       static_cast<bf16_t*>(cache), slots, positions, r, n_groups, d_rope,
-                       latent_rmsnorm, eps, theta);
+  auto launch = [&](auto kernel, auto* out) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, proj, ld, splits, sps, out, slots, positions, r,
+                       n_groups, d_rope, latent_rmsnorm, eps, base);
+  };
+  if (dtype == kF32) {
+    float* out = static_cast<float*>(cache);
+    if (splits <= 1) launch(cache_rows_kernel<float, 1>, out);
+    else launch(cache_rows_kernel<float, 16>, out);
+  } else {
+    bf16_t* out = static_cast<bf16_t*>(cache);
+    if (splits <= 1) launch(cache_rows_kernel<bf16_t, 1>, out);
+    else launch(cache_rows_kernel<bf16_t, 16>, out);
+  }
 }
 
 void finalize_query_rope(int dtype, const float* proj, int64_t ld, void* q_pe,
                          const int32_t* positions, int64_t n_tokens, int n_heads, int d_rope,
                          double theta, hipStream_t s) {
   if (n_tokens <= 0) return;
+  const double base = std::pow(theta, -2.0 / d_rope);
   const int items = n_heads * (d_rope / 2);
   dim3 grid(static_cast<unsigned>(n_tokens), static_cast<unsigned>(std::max(1, std::min(16, items / 256))));
   if (dtype == kF32)
     hipLaunchKernelGGL(query_rope_kernel<float>, grid, dim3(256), 0, s, proj, ld,
-                       static_cast<float*>(q_pe), positions, n_heads, d_rope, theta);
+                       static_cast<float*>(q_pe), positions, n_heads, d_rope, base);
   else
     hipLaunchKernelGGL(query_rope_kernel<bf16_t>, grid, dim3(256), 0, s, proj, ld,
-                       static_cast<bf16_t*>(q_pe), positions, n_heads, d_rope, theta);
+                       static_cast<bf16_t*>(q_pe), positions, n_heads, d_rope, base);
 }
 
 }  // namespace mla
