@@ -6,19 +6,21 @@
 // absorption, eqs. (4)-(5)), so one workgroup takes ALL heads of one
 // (sequence, context split): each cache tile crosses HBM -> LDS once per CU.
 //
-// Workgroup = 4 wave64s, one per SIMD, each with the whole 512-entry register
-// file.  Wave w scores heads [32w, 32w+32) (their Qᵀ for the split: 144
-// registers of bf16 MFMA operands) and accumulates latent columns
-// [128w, 128w+128) of O for all 128 heads (256 fp32 registers).  Splitting the
-// PV by columns makes each wave read only its quarter of the transposed C
-// fragments, whose LDS path runs at about half the rate of plain reads; the
-// softmax weights cross between waves through a small LDS buffer instead.
+// Workgroup = 8 wave64s, two per SIMD, so one wave's softmax, LDS waits and
+// copy issue run under the other wave's MFMAs (with one wave per SIMD those
+// latencies were exposed).  Each wave has half a SIMD's register file:
+//   - wave w scores heads [16w, 16w+16): their Qᵀ for the split is 72 registers
+//     of bf16 MFMA operands;
+//   - wave w accumulates latent columns [64w, 64w+64) of O for all 128 heads
+//     (128 fp32 registers).  Splitting the PV by columns makes each wave read
+//     only its eighth of the transposed C fragments; the softmax weights cross
+//     between waves through a small LDS buffer.
 // Tiles of 32 rows:
 //   - copies HBM -> LDS by global_load_lds_dwordx4 into 4 buffers (tiles t and
 //     t+1 in use, t+2 and t+3 in flight), stored without padding; the 16-byte
 //     chunks of a row are XOR-swizzled by (row / 2) within groups of eight, so
 //     the 16 rows one fragment read touches fall on distinct bank groups;
-//   - score: Sᵀ[32 rows x 32 heads], four 16x16 blocks of
+//   - score: Sᵀ[32 rows x 16 heads], two 16x16 blocks of
 //     v_mfma_f32_16x16x32_bf16 over the whole row (K = 576), tile rows as the A
 //     operand from LDS, Qᵀ as the B operand from registers;
 //   - softmax against a per-head reference max of the split (the first tile's
@@ -28,11 +30,10 @@
 //     exchange [head block][lane] (8 KB a tile): a score lane holds rows
 //     4lg..4lg+3 and 16+4lg..16+4lg+3 of its head, and the K order of the PV
 //     product is taken to be exactly that;
-//   - PV: O[128 heads x 128 columns of wave w] += P[128 x 32]·C[32 x 128], the
+//   - PV: O[128 heads x 64 columns of wave w] += P[128 x 32]·C[32 x 64], the
 //     transposed C fragments (ds_read_b64_tr_b16) read at those row bases.
 // Iteration t (one barrier, for the tile ring and the P exchange): score of
-// tile t+1, then PV of tile t with the softmax of tile t+1 (and its store to
-// the exchange) issued between its MFMAs.
+// tile t+1, its softmax and store to the exchange, then the PV of tile t.
 // Output: normalised o_ (part_o null, one split) or the split's (m, l) and
 // its normalised o_ in bf16.
 #include <math.h>
@@ -48,7 +49,7 @@ namespace {
 constexpr int kR = 512;              // latent width
 constexpr int kRW = 576;             // cache row width (r + d_rope, one rotary group)
 constexpr int kHeads = 128;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTL = 32;              // rows per tile
 constexpr int kStages = 4;
@@ -56,11 +57,11 @@ constexpr int kRowBytes = kRW * 2;   // 1152
 constexpr int kRowChunks = kRowBytes / 16;           // 72
 constexpr int kTileBytes = kTL * kRowBytes;          // 36864
 constexpr int kDmaOps = kTileBytes / 1024;           // 36 one-KB copies per tile
-constexpr int kDmaPerWave = kDmaOps / kWaves;        // 9
+constexpr int kDmaMax = (kDmaOps + kWaves - 1) / kWaves;  // 5: waves 0-3 issue 5, waves 4-7 issue 4
 constexpr int kSteps = kRW / 32;                     // 18 score k-steps
-constexpr int kHW = kHeads / kWaves;                 // 32 heads per wave
+constexpr int kHW = kHeads / kWaves;                 // 16 heads per wave in the score
 constexpr int kHB = kHeads / 16;                     // 8 head blocks of the PV
-constexpr int kCB = kR / 16 / kWaves;                // 8 column blocks of 16 per wave
+constexpr int kCB = kR / 16 / kWaves;                // 4 column blocks of 16 per wave
 constexpr int kPBytes = kHB * 64 * 16;               // one tile's softmax weights: 8 KB
 constexpr int kPOff = kStages * kTileBytes;          // P exchange, two buffers
 constexpr int kLdsBytes = kPOff + 2 * kPBytes;       // 160 KB
@@ -69,19 +70,14 @@ constexpr int kLdsBytes = kPOff + 2 * kPBytes;       // 160 KB
 constexpr int kFlagsOff = 1024;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSlack = 64.f;
-#ifndef MLA_WIDE_SCORE_LA
-#define MLA_WIDE_SCORE_LA 2  // score k-steps of LDS fragments in flight
-#endif
-#ifndef MLA_WIDE_PV_LA
-#define MLA_WIDE_PV_LA 3     // PV column blocks of LDS fragments in flight
-#endif
+constexpr int kSLA = 2;                              // score k-steps of fragments in flight
 
-static_assert(kDmaOps % kWaves == 0, "tile copies split evenly over the waves");
+static_assert(kHW == 16, "one 16-head block per wave in the score");
+static_assert(kDmaOps - (kWaves / 2) * kDmaMax == (kWaves / 2) * (kDmaMax - 1), "copies split 5/4 over the waves");
 static_assert(kRowChunks % 8 == 0, "swizzle groups of eight chunks");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-static_assert(kHeads * 4 <= kFlagsOff && kFlagsOff + 64 <= kTileBytes, "xch and flags inside tile slot 0");
-static_assert(3 * kDmaPerWave < 64, "vmcnt range");
-static_assert(2 * kDmaPerWave <= kSteps, "one tile copy per odd score k-step");
+static_assert(kHeads * 4 <= kFlagsOff && kFlagsOff + 4 * kWaves <= kTileBytes, "xch and flags inside tile slot 0");
+static_assert(3 * kDmaMax < 64, "vmcnt range");
 static_assert(kTL * kRowChunks <= 2304, "row-of-chunk division by multiplication is exact below 2304");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -92,10 +88,10 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 // LDS chunk slot of 16-byte chunk c of tile row r (an involution for fixed r).
 __device__ __forceinline__ int swz(int c, int r) { return (c & ~7) | ((c ^ (r >> 1)) & 7); }
 
-
-template <int N>
+// wait until at most N tiles' copies of this wave are in flight (OPS copies per tile)
+template <int N, int OPS>
 __device__ __forceinline__ void wait_tiles_after() {
-  wait_vmcnt<N * kDmaPerWave>();
+  wait_vmcnt<N * OPS>();
 }
 
 __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
@@ -116,6 +112,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
+  const bool five = wave < kDmaOps - kWaves * (kDmaMax - 1);  // this wave issues 5 copies a tile
 
   const int64_t row0 = seq_start[b];
   const int len = seq_len[b];
@@ -125,18 +122,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
   const char* cache_b = reinterpret_cast<const char*>(cache + row0 * kRW);
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)smem));
 
-  // ---- tile copy: wave w issues 1 KB copies j = w + 4i; copy j fills LDS chunks
-  // [64j, 64j + 64) of the tile image.  LDS chunk L (row L / 72, slot L % 72)
-  // holds global chunk swz(slot, row) of the same row, which is L ^ ((row / 2) & 7)
-  // since rows are whole groups of eight chunks.  Rows past the split read a
-  // chunk of its last valid row instead.  The lane index is made opaque so the
-  // few offset instructions are redone per tile rather than held in registers.
-  auto issue_op = [&](int t, int i) {
+  // ---- tile copy: wave w issues 1 KB copies j = w + 8i < 36; copy j fills LDS
+  // chunks [64j, 64j + 64) of the tile image.  LDS chunk L (row L / 72, slot
+  // L % 72) holds global chunk swz(slot, row) of the same row, which is
+  // L ^ ((row / 2) & 7) since rows are whole groups of eight chunks.  Rows past
+  // the split read a chunk of its last valid row instead.  The lane index is
+  // made opaque so the few offset instructions are redone per tile rather than
+  // held in registers.
+  auto issue_op = [&](int t, int j) {
     const int tile_row = l_begin + t * kTL;
     const int valid = min(kTL, l_end - tile_row);
     const char* tbase = cache_b + static_cast<int64_t>(tile_row) * kRowBytes;
     const uint32_t dst = lds0 + (t % kStages) * kTileBytes;
-    const int j = wave + kWaves * i;
     int ln = lane;
     __asm__ volatile("" : "+v"(ln));
     if (valid == kTL) {
@@ -158,22 +155,32 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
   };
   auto issue_tile = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) issue_op(t, i);
+    for (int i = 0; i < kDmaMax; ++i) {
+      const int j = wave + kWaves * i;
+      if (j < kDmaOps) issue_op(t, j);
+    }
   };
   auto wait_tile = [&](int t, int last_issued) {
-    switch (last_issued - t) {
-      case 0: wait_tiles_after<0>(); break;
-      case 1: wait_tiles_after<1>(); break;
-      case 2: wait_tiles_after<2>(); break;
-      default: wait_tiles_after<3>(); break;
+    const int n = last_issued - t;  // tiles issued after t
+    if (five) {
+      switch (n) {
+        case 0: wait_tiles_after<0, kDmaMax>(); break;
+        case 1: wait_tiles_after<1, kDmaMax>(); break;
+        default: wait_tiles_after<2, kDmaMax>(); break;
+      }
+    } else {
+      switch (n) {
+        case 0: wait_tiles_after<0, kDmaMax - 1>(); break;
+        case 1: wait_tiles_after<1, kDmaMax - 1>(); break;
+        default: wait_tiles_after<2, kDmaMax - 1>(); break;
+      }
     }
   };
 
-  // ---- Qᵀ of this wave's heads: B operand, lane = head 16hb + l16, k = 32ks + 8lg + e
-  bf16x8 qf[2][kSteps];
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const int head = wave * kHW + hb * 16 + l16;
+  // ---- Qᵀ of this wave's heads: B operand, lane = head 16w + l16, k = 32ks + 8lg + e
+  bf16x8 qf[kSteps];
+  {
+    const int head = wave * kHW + l16;
 #pragma unroll
     for (int ks = 0; ks < kSteps; ++ks) {
       const int k0 = ks * 32 + lg * 8;
@@ -181,7 +188,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
           ? *reinterpret_cast<const uint4*>(q_lat + (static_cast<int64_t>(b) * kHeads + head) * kR + k0)
           : *reinterpret_cast<const uint4*>(q_pe + (static_cast<int64_t>(b) * kHeads + head) * (kRW - kR) +
                                             (k0 - kR));
-      qf[hb][ks] = __builtin_bit_cast(bf16x8, v);
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
   const float qk_scale = scale * kLog2e;
@@ -195,42 +202,35 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
   const int x_even = (lg ^ (l16 >> 1)) & 7;
   const int x_odd = ((4 + lg) ^ (l16 >> 1)) & 7;
 
-  float m_ref[2] = {-INFINITY, -INFINITY};   // reference max of heads 32w + 16hb + l16 (base 2)
-  float m_lane[2], l_lane[2];                // raw score max, bf16 weight sum of the lane
-  f32x4 o[kHB][kCB];  // O[heads 16HB + 4lg + i][columns 128w + 16j + l16]
+  float m_ref = -INFINITY;   // reference max of head 16w + l16 (base 2)
+  float m_lane, l_lane;      // raw score max, bf16 weight sum of the lane
+  f32x4 o[kHB][kCB];         // O[heads 16hb + 4lg + i][columns 64w + 16j + l16]
 
   // Raw scores q·k of tile tt (unscaled; rows past the split masked to -inf):
-  // s[rb][hb] = rows 16rb + 4lg + i, head 16hb + l16.  Fragments of k-step
-  // ks + 2 are read while the MFMAs of ks run; the scheduling barriers keep
-  // the compiler from hoisting more reads.
-  auto score = [&](int tt, f32x4 (&s)[2][2]) {
+  // s[rb] = rows 16rb + 4lg + i, head 16w + l16.  Fragments of k-step ks + 2 are
+  // read while the MFMAs of ks run; the scheduling barriers keep the compiler
+  // from hoisting more reads.
+  auto score = [&](int tt, f32x4 (&s)[2]) {
     const unsigned char* tb = smem + (tt % kStages) * kTileBytes;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) s[rb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    s[0] = s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto frag = [&](int ks, int off) {
       const int coff = (ks >> 1) * 128 + ((ks & 1) ? x_odd : x_even) * 16;
       return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tb + off + coff));
     };
-    constexpr int kLA = MLA_WIDE_SCORE_LA;  // k-steps of fragments in flight
-    bf16x8 fa[kLA][2];
+    bf16x8 fa[kSLA][2];
 #pragma unroll
-    for (int p = 0; p < kLA; ++p) {
+    for (int p = 0; p < kSLA; ++p) {
       fa[p][0] = frag(p, a_off0);
       fa[p][1] = frag(p, a_off1);
     }
 #pragma unroll
     for (int ks = 0; ks < kSteps; ++ks) {
-      const bf16x8 a0 = fa[ks % kLA][0], a1 = fa[ks % kLA][1];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        s[0][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[hb][ks], s[0][hb], 0, 0, 0);
-        s[1][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[hb][ks], s[1][hb], 0, 0, 0);
-      }
-      if (ks + kLA < kSteps) {
-        fa[ks % kLA][0] = frag(ks + kLA, a_off0);
-        fa[ks % kLA][1] = frag(ks + kLA, a_off1);
+      const bf16x8 a0 = fa[ks % kSLA][0], a1 = fa[ks % kSLA][1];
+      s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s[1], 0, 0, 0);
+      if (ks + kSLA < kSteps) {
+        fa[ks % kSLA][0] = frag(ks + kSLA, a_off0);
+        fa[ks % kSLA][1] = frag(ks + kSLA, a_off1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -239,34 +239,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (rb * 16 + lg * 4 + i >= valid) s[rb][hb][i] = -INFINITY;
+        for (int i = 0; i < 4; ++i)
+          if (rb * 16 + lg * 4 + i >= valid) s[rb][i] = -INFINITY;
     }
   };
 
-  // softmax weights P = 2^(s·scale·log2(e) - m_ref) of rows 16rb + 4lg + (0..3)
-  // of head block hb, packed bf16 into w[2rb], w[2rb + 1]: half of the bf16 A
-  // operand of the PV product, whose K order is [rows 4lg + i, then 16 + 4lg + i].
-  // The row sum takes the bf16 weights the PV product uses (v_dot2 with ones).
+  // softmax weights P = 2^(s·scale·log2(e) - m_ref) of the wave's head block,
+  // packed bf16 as the A operand of the PV product (K order [rows 4lg + i, then
+  // 16 + 4lg + i]) and stored to slot [w][lane] of exchange buffer pbuf.  The
+  // row sum takes the bf16 weights the PV product uses (v_dot2 with ones).
   const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
-  auto soft_part = [&](const f32x4 (&s)[2][2], int hb, int rb, uint32_t (&w)[4]) {
-    const f32x4 v = s[rb][hb];
-    m_lane[hb] = fmaxf(m_lane[hb], fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-    const float nm = -m_ref[hb];
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(v[0], qk_scale, nm));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(v[1], qk_scale, nm));
-    const float p2 = __builtin_amdgcn_exp2f(fmaf(v[2], qk_scale, nm));
-    const float p3 = __builtin_amdgcn_exp2f(fmaf(v[3], qk_scale, nm));
-    w[2 * rb] = pack_bf16x2(p0, p1);
-    w[2 * rb + 1] = pack_bf16x2(p2, p3);
-    l_lane[hb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[2 * rb]), ones, l_lane[hb], false);
-    l_lane[hb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[2 * rb + 1]), ones, l_lane[hb], false);
-  };
-  // store head block hb's weights to slot [2w + hb][lane] of exchange buffer pbuf
-  auto soft_store = [&](const uint32_t (&w)[4], int hb, unsigned char* pbuf) {
-    *reinterpret_cast<uint4*>(pbuf + ((wave * 2 + hb) * 64 + lane) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  auto softmax = [&](const f32x4 (&s)[2], unsigned char* pbuf) {
+    uint32_t w[4];
+    const float nm = -m_ref;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const f32x4 v = s[rb];
+      m_lane = fmaxf(m_lane, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(v[0], qk_scale, nm));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(v[1], qk_scale, nm));
+      const float p2 = __builtin_amdgcn_exp2f(fmaf(v[2], qk_scale, nm));
+      const float p3 = __builtin_amdgcn_exp2f(fmaf(v[3], qk_scale, nm));
+      w[2 * rb] = pack_bf16x2(p0, p1);
+      w[2 * rb + 1] = pack_bf16x2(p2, p3);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      l_lane = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]), ones, l_lane, false);
+    *reinterpret_cast<uint4*>(pbuf + (wave * 64 + lane) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   };
 
   // transposed C fragment of column block nb: lane (l16, lg) gets column
@@ -283,33 +283,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  // PV of tile tt over this wave's columns, P of all heads from exchange buffer
-  // tt % 2; the softmax of the next tile's scores s_next is issued in four
-  // pieces between the products, into buffer (tt + 1) % 2
-  auto pv_softmax = [&](int tt, const f32x4 (&s_next)[2][2]) {
+  // PV of tile tt over this wave's 64 columns, P of all heads from exchange
+  // buffer tt % 2: head block outer, the wave's four C fragments held
+  auto pv = [&](int tt) {
     const unsigned char* tb = smem + (tt % kStages) * kTileBytes;
     const unsigned char* pb = smem + kPOff + (tt & 1) * kPBytes;
-    unsigned char* pn = smem + kPOff + ((tt + 1) & 1) * kPBytes;
-    constexpr int kLA = MLA_WIDE_PV_LA;
-    bf16x8 pf[kHB];
+    bf16x8 cf[kCB];
 #pragma unroll
-    for (int hb = 0; hb < kHB; ++hb)
-      pf[hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pb + (hb * 64 + lane) * 16));
-    bf16x8 cf[kLA];
-    uint32_t wn[4];
+    for (int j = 0; j < kCB; ++j) cf[j] = cfrag(tb, wave * kCB + j);
 #pragma unroll
-    for (int p = 0; p < kLA; ++p) cf[p] = cfrag(tb, wave * kCB + p);
+    for (int hb = 0; hb < kHB; ++hb) {
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pb + (hb * 64 + lane) * 16));
 #pragma unroll
-    for (int j = 0; j < kCB; ++j) {
-      const bf16x8 b = cf[j % kLA];
-#pragma unroll
-      for (int hb = 0; hb < kHB; ++hb)
-        o[hb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[hb], b, o[hb][j], 0, 0, 0);
-      if (j + kLA < kCB) cf[j % kLA] = cfrag(tb, wave * kCB + j + kLA);
-      if (j == 1) soft_part(s_next, 0, 0, wn);
-      if (j == 2) { soft_part(s_next, 0, 1, wn); soft_store(wn, 0, pn); }
-      if (j == 4) soft_part(s_next, 1, 0, wn);
-      if (j == 5) { soft_part(s_next, 1, 1, wn); soft_store(wn, 1, pn); }
+      for (int j = 0; j < kCB; ++j) o[hb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, cf[j], o[hb][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -319,8 +305,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
     for (int hb = 0; hb < kHB; ++hb)
 #pragma unroll
       for (int j = 0; j < kCB; ++j) o[hb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_lane[0] = m_lane[1] = -INFINITY;
-    l_lane[0] = l_lane[1] = 0.f;
+    m_lane = -INFINITY;
+    l_lane = 0.f;
 
 #pragma unroll
     for (int t = 0; t < kStages - 1; ++t)
@@ -331,29 +317,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
       // prologue: tile 0; in the first pass its max sets the reference
       wait_tile(0, issued);
       lds_barrier();
-      f32x4 s0[2][2];
+      f32x4 s0[2];
       score(0, s0);
       if (pass == 0) {
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          float mx = fmaxf(fmaxf(fmaxf(s0[0][hb][0], s0[0][hb][1]), fmaxf(s0[0][hb][2], s0[0][hb][3])),
-                           fmaxf(fmaxf(s0[1][hb][0], s0[1][hb][1]), fmaxf(s0[1][hb][2], s0[1][hb][3])));
-          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-          m_ref[hb] = mx * qk_scale;
-        }
+        float mx = fmaxf(fmaxf(fmaxf(s0[0][0], s0[0][1]), fmaxf(s0[0][2], s0[0][3])),
+                         fmaxf(fmaxf(s0[1][0], s0[1][1]), fmaxf(s0[1][2], s0[1][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        m_ref = mx * qk_scale;
       }
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        uint32_t w[4];
-        soft_part(s0, hb, 0, w);
-        soft_part(s0, hb, 1, w);
-        soft_store(w, hb, smem + kPOff);
-      }
+      softmax(s0, smem + kPOff);
     }
 
     // iteration t: scores of tile t+1 (masked to nothing past the last tile),
-    // then PV of tile t with the softmax of tile t+1 between its MFMAs
+    // their softmax into exchange buffer (t+1) % 2, then the PV of tile t
     for (int t = 0; t < n_tiles; ++t) {
       if (t + 1 < n_tiles) wait_tile(t + 1, issued);
       // tile t+1 and the P of tile t visible; PV(t-1) done everywhere: ring
@@ -363,48 +340,49 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
         issue_tile(t + kStages - 1);
         issued = t + kStages - 1;
       }
-      f32x4 s_next[2][2];
+      f32x4 s_next[2];
       score(t + 1, s_next);
-      pv_softmax(t, s_next);
+      softmax(s_next, smem + kPOff + ((t + 1) & 1) * kPBytes);
+      pv(t);
     }
     // restart when some score passed its reference's headroom (raw max of the
     // lane's head times the scale; the scale is positive)
-    const bool over = m_lane[0] * qk_scale > m_ref[0] + kSlack || m_lane[1] * qk_scale > m_ref[1] + kSlack;
+    const bool over = m_lane * qk_scale > m_ref + kSlack;
     lds_barrier();
     if (lane == 0) flags[wave] = __ballot(over) != 0 ? 1 : 0;
     lds_barrier();
-    const bool scan = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
-    if (!scan) break;
-    // second pass with the split's true max per head
+    int any = 0;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      float mx = m_lane[hb];
+    for (int w = 0; w < kWaves; ++w) any |= flags[w];
+    if (!any) break;
+    // second pass with the split's true max per head
+    {
+      float mx = m_lane;
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      m_ref[hb] = mx * qk_scale;
+      m_ref = mx * qk_scale;
     }
     lds_barrier();  // every wave has read the flags before they are rewritten
   }
 
   // ---- epilogue: l per head -> LDS (the wave's own heads); O normalised or as a partial
   const bool partials = part_o != nullptr;
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    float l = l_lane[hb];
+  {
+    float l = l_lane;
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    const int head = wave * kHW + hb * 16 + l16;
+    const int head = wave * kHW + l16;
     if (lg == 0) {
       xch[head] = l;
       if (partials) {
         const int64_t pidx = (static_cast<int64_t>(b) * n_split + split) * kHeads + head;
-        part_ml[pidx * 2 + 0] = m_ref[hb];
+        part_ml[pidx * 2 + 0] = m_ref;
         part_ml[pidx * 2 + 1] = l;
       }
     }
   }
   lds_barrier();  // the row sums of every head are in LDS
-  // lane holds O[head 16hb + 4lg + i][column 128w + 16j + l16]
+  // lane holds O[head 16hb + 4lg + i][column 64w + 16j + l16]
   const int col0 = wave * kCB * 16 + l16;
 #pragma unroll
   for (int hb = 0; hb < kHB; ++hb)
