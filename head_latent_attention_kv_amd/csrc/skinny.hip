@@ -434,6 +434,194 @@ __global__ __launch_bounds__(256, 1) void skinny_dma_kernel(SkinnyArgs sa) {
 static_assert(4 * 4 * kDmaNB * 4 * 64 * 4 <= DmaStage<256>::kLds && 4 * 4 * kDmaNB * 4 * 64 * 4 <= DmaStage<128>::kLds,
               "reduction buffer inside the ring");
 
+// ---- split merge + W_UV, DMA-staged (32 token rows per workgroup, 128 columns) ----
+// out[m][z][:] = W_UV[z] · Σ_j w[m][j] A_j[m][z][:], with A_j the bf16 split
+// partials and w the softmax-merge weights from (m_j, l_j).  A workgroup takes
+// one head z and 32 token rows; per stage of 128 k it copies the head's 128
+// W_UV rows and the 32 x NS partial rows (256-byte runs) HBM -> LDS with
+// global_load_lds_dwordx4, two stages in flight.  Chunk p of an LDS row holds
+// global chunk p ^ key, key = (row & 15) for W_UV rows and (token & 15) for the
+// partial rows (NS consecutive rows per token), so the 16 rows of one fragment
+// read fall on distinct banks.  Wave w takes k-step w of every stage: it forms
+// the merged A fragment from the NS partial fragments in fp32, splits it into
+// hi + lo bf16, and runs both against the W_UV fragments; the four partial
+// tiles are summed through LDS at the end.
+constexpr int kMgCols = 128;                       // output columns (d_v) per workgroup
+constexpr int kMgRows = 32;                        // token rows per workgroup
+constexpr int kMgKC = 128;                         // k per stage
+constexpr int kMgRun = kMgKC * 2;                  // 256 bytes of a row per stage
+constexpr int kMgStages = 2;
+
+template <int NS>
+struct MergeStage {
+  static constexpr int kWOps = kMgCols * kMgRun / 1024;       // 32 W_UV copies (4 rows each)
+  static constexpr int kAOps = kMgRows * NS * kMgRun / 1024;  // partial copies (4 rows each)
+  static constexpr int kOps = kWOps + kAOps;
+  static constexpr int kOpsPerWave = kOps / 4;
+  static constexpr int kBytes = kOps * 1024;
+  static constexpr int kLds = kMgStages * kBytes;
+  static_assert(NS == 4, "one token's partial rows per copy");
+  static_assert(kOps % 4 == 0 && kLds <= 160 * 1024 - 1024, "LDS budget (merge weights after the ring)");
+  static_assert(kOpsPerWave < 64, "vmcnt range");
+};
+
+template <int NS>
+__global__ __launch_bounds__(256, 1) void merge_uv_kernel(SkinnyArgs sa) {
+  using G = MergeStage<NS>;
+  constexpr int MB = kMgRows / 16, NB = kMgCols / 16;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  float* wmerge = reinterpret_cast<float*>(smem + G::kLds);  // [kMgRows][NS]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int m_groups = max(1, sa.m_groups);
+  const int m0 = (blockIdx.x % m_groups) * kMgRows;
+  const int m_last = sa.M - 1 - m0;  // last local token row
+  const int z = blockIdx.y;
+  const int n_st = (sa.K + kMgKC - 1) / kMgKC;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)smem));
+  const bf16_t* a_head = static_cast<const bf16_t*>(sa.A) + static_cast<int64_t>(z) * sa.sAz;
+  const uint16_t* w_head = sa.B0 + static_cast<int64_t>(z) * sa.sBz;
+
+  // merge weights w[t][j] = 2^(m_j - M) l_j / Σ_j 2^(m_j - M) l_j of token m0 + t
+  if (tid < kMgRows && tid <= m_last) {
+    const float* ml = sa.ml + (static_cast<int64_t>(m0 + tid) * NS * sa.ml_heads + z) * 2;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) mx = fmaxf(mx, ml[j * sa.ml_heads * 2]);
+    float e[NS], den = 0.f;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      e[j] = exp2f(ml[j * sa.ml_heads * 2] - mx) * ml[j * sa.ml_heads * 2 + 1];
+      den += e[j];
+    }
+    const float inv = 1.f / den;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) wmerge[tid * NS + j] = e[j] * inv;
+  }
+
+  // copy o of stage st: 4 rows R = 4o'..4o'+3 of the W_UV region (o < kWOps,
+  // o' = o) or of the partial region (o' = o - kWOps: token o', splits 0..3);
+  // lanes 16q..16q+15 take row 4o'+q, LDS chunks p = lane % 16 in order
+  auto issue = [&](int st) {
+    const int kb = st * kMgKC;
+    const uint32_t dst = lds0 + (st % kMgStages) * G::kBytes;
+    int ln = lane;
+    __asm__ volatile("" : "+v"(ln));
+    const int q = ln >> 4, p = ln & 15;
+#pragma unroll
+    for (int i = 0; i < G::kOpsPerWave; ++i) {
+      const int o = wave + 4 * i;
+      const char* sbase;
+      uint32_t voff;
+      if (o < G::kWOps) {
+        const int n_base = min(4 * o, sa.N - 1), n = min(4 * o + q, sa.N - 1);
+        int kc = kb + 8 * (p ^ ((4 * o + q) & 15));
+        kc = kc < sa.K ? kc : sa.K - 8;
+        sbase = reinterpret_cast<const char*>(w_head + static_cast<int64_t>(n_base) * sa.sBo);
+        voff = static_cast<uint32_t>((n - n_base) * sa.sBo + kc) * 2u;
+      } else {
+        const int t = o - G::kWOps;                   // token row of the copy, splits j = q
+        const int key = t & 15;
+        int kc = kb + 8 * (p ^ key);
+        kc = kc < sa.K ? kc : sa.K - 8;
+        const int m = min(t, m_last);
+        sbase = reinterpret_cast<const char*>(a_head + static_cast<int64_t>(m0 + m) * sa.sAm);
+        voff = static_cast<uint32_t>(q * sa.sAs + kc) * 2u;
+      }
+      global_to_lds16(sbase, voff, __builtin_amdgcn_readfirstlane(dst + o * 1024));
+    }
+  };
+
+  f32x4 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(0);
+  __syncthreads();  // merge weights visible (the copy of stage 0 stays in flight)
+  float wm[MB][NS];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int t = min(16 * i + l16, max(m_last, 0));
+#pragma unroll
+    for (int j = 0; j < NS; ++j) wm[i][j] = wmerge[t * NS + j];
+  }
+  const int c_log = wave * 4 + lg;  // this wave's k-step within the stage, chunk of the lane
+  const int frag_off = (c_log ^ l16) << 4;
+  for (int st = 0; st < n_st; ++st) {
+    if (st + 1 < n_st) {
+      issue(st + 1);  // its buffer was last read in step st - 1, before the previous barrier
+      wait_vmcnt<G::kOpsPerWave>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();  // stage st visible everywhere
+    const unsigned char* sb = smem + (st % kMgStages) * G::kBytes;
+    const bool k_in = st * kMgKC + 8 * c_log < sa.K;
+    bf16x8 ah[MB], al[MB], bf[NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const uint4 v = *reinterpret_cast<const uint4*>(sb + G::kWOps * 1024 + ((16 * i + l16) * NS + j) * kMgRun + frag_off);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          x[2 * qq] = fmaf(wm[i][j], __uint_as_float(u[qq] << 16), x[2 * qq]);
+          x[2 * qq + 1] = fmaf(wm[i][j], __uint_as_float(u[qq] & 0xFFFF0000u), x[2 * qq + 1]);
+        }
+      }
+      if (!k_in) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      }
+      split_hi_lo(x, ah[i], al[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      bf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sb + (16 * j + l16) * kMgRun + frag_off));
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bf[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], bf[j], acc[i][j], 0, 0, 0);
+      }
+    lds_barrier();  // stage st read everywhere before its buffer is refilled
+  }
+
+  // sum the four waves' tiles; wave b % 4 stores block b
+  float* red = reinterpret_cast<float*>(smem);  // [4 waves][MB * NB][4][64]
+  constexpr int kTile = MB * NB * 4 * 64;
+  static_assert(4 * kTile * 4 <= G::kLds, "reduction buffer inside the ring");
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[wave * kTile + ((i * NB + j) * 4 + e) * 64 + lane] = acc[i][j][e];
+  lds_barrier();
+  bf16_t* C = static_cast<bf16_t*>(sa.C) + static_cast<int64_t>(z) * sa.sCz + static_cast<int64_t>(m0) * sa.sCm;
+#pragma unroll
+  for (int bk = 0; bk < MB * NB; ++bk) {
+    if (bk % 4 != wave) continue;
+    const int i = bk / NB, j = bk % NB;
+    const int n = 16 * j + l16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = (bk * 4 + e) * 64 + lane;
+      const float v = red[idx] + red[kTile + idx] + red[2 * kTile + idx] + red[3 * kTile + idx];
+      const int m = 16 * i + 4 * lg + e;
+      if (n < sa.N && m <= m_last) C[static_cast<int64_t>(m) * sa.sCm + n] = f32_to_bf16(v);
+    }
+  }
+}
+
 }  // namespace
 
 namespace {
@@ -570,6 +758,16 @@ void gemm_skinny_merged(SkinnyArgs sa, int n_merge, bool out_bf16, hipStream_t s
   sa.n_merge = n_merge;
   sa.splits = 1;
   sa.k_per_split = k_per_split(sa.K, 1);
+  if (n_merge == 4 && out_bf16 && sa.M > 32 && sa.M <= 64 && sa.N == kMgCols && sa.K % 8 == 0 &&
+      sa.Z * 2 >= 128) {
+    // DMA-staged merge: two workgroups of 32 token rows per head
+    sa.m_groups = 2;
+    constexpr int lds = MergeStage<4>::kLds + kMgRows * 4 * 4;
+    hipFuncSetAttribute(reinterpret_cast<const void*>(merge_uv_kernel<4>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    hipLaunchKernelGGL(merge_uv_kernel<4>, dim3(2, sa.Z), dim3(256), lds, s, sa);
+    return;
+  }
   if (n_merge > 1 && sa.M > 32 && sa.M <= 64 && sa.N >= 128 && sa.Z * 2 >= 128) {
     // the merge reads n_merge partial rows per token row: two workgroups per
     // head take 32 token rows each, so every partial is read once and the
