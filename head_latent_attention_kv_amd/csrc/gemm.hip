@@ -321,18 +321,41 @@ __global__ __launch_bounds__(256) void gemm_uk_kernel(GemmArgs g) {
 
   // lane holds C[m = 16i + 4lg + e][n = n0 + 64w + 16j + l16]
   OutT* C = static_cast<OutT*>(g.C) + static_cast<int64_t>(z) * g.sCz;
+  if constexpr (sizeof(OutT) == 2) {
+    // bf16 out: the tile goes through LDS (over the B slice, once every wave is
+    // done with it) so each lane stores 16 contiguous bytes of one row
+    __syncthreads();
+    bf16_t* tile = reinterpret_cast<bf16_t*>(sB);  // [MB * 16 rows][kUkCols]
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wave * 64 + j * 16 + l16;
-      if (n >= g.N) continue;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = i * 16 + lg * 4 + e;
-        if (m < g.M) Elem<OutT>::store(C, static_cast<int64_t>(m) * g.sCm + n, acc[i][j][e]);
-      }
+        for (int e = 0; e < 4; ++e)
+          tile[(i * 16 + lg * 4 + e) * kUkCols + wave * 64 + j * 16 + l16] = f32_to_bf16(acc[i][j][e]);
+    __syncthreads();
+    constexpr int kChunks = MB * 16 * kUkCols / 8;  // 16-byte chunks of the tile
+#pragma unroll
+    for (int c = tid; c < kChunks; c += 256) {
+      const int m = c / (kUkCols / 8), n = n0 + (c % (kUkCols / 8)) * 8;
+      if (m < g.M && n < g.N)
+        *reinterpret_cast<uint4*>(C + static_cast<int64_t>(m) * g.sCm + n) =
+            *reinterpret_cast<const uint4*>(tile + m * kUkCols + (n - n0));
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wave * 64 + j * 16 + l16;
+        if (n >= g.N) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = i * 16 + lg * 4 + e;
+          if (m < g.M) Elem<OutT>::store(C, static_cast<int64_t>(m) * g.sCm + n, acc[i][j][e]);
+        }
+      }
+  }
 }
 
 template <int MB>
@@ -380,7 +403,7 @@ void gemm(const GemmArgs& g, int dtype, bool a_f32, bool b_kn, bool out_bf16, hi
     return;
   }
   if (a_f32 && b_kn && g.M <= 64 && g.K % 32 == 0 && g.N % 8 == 0 && g.sBo % 8 == 0 && g.sAm % 4 == 0 &&
-      g.sAz % 4 == 0) {
+      g.sAz % 4 == 0 && g.sCm % 8 == 0 && g.sCz % 8 == 0) {
     // few rows against an n-contiguous weight: the transposed-read kernel
     switch ((g.M + 15) / 16) {
       case 1: launch_uk<1>(g, out_bf16, s); break;
