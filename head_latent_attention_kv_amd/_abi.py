@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(PKG, "libmla_amd.so")
 MLA_OK, MLA_EINVAL, MLA_ENOTSUP, MLA_EWORKSPACE, MLA_EHIP = 0, -1, -2, -3, -4
 MLA_F32, MLA_BF16 = 0, 1
 MLA_OP_WRITE_CACHE, MLA_OP_ABSORB, MLA_OP_DECODE, MLA_OP_PREFILL = 0, 1, 2, 3
+MLA_OP_QUERY, MLA_OP_PREFILL_EXPANDED = 4, 5
 
 # Functions declared in include/mla.h, with their ctypes signatures.
 _vp, _sz, _i32, _i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
@@ -39,6 +40,9 @@ SIGNATURES = {
     "mla_decode_splits": (_i32, [_PD, _i32, _i32]),
     "mla_decode_split_rows": (_i32, [_PD, _i32, _i32]),
     "mla_decode_partials": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "mla_query": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "mla_prefill_expanded": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _vp, _vp, _vp, _vp,
+                                            _sz, _vp]),
     "mla_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_version": (ctypes.c_int, []),
 }
@@ -216,6 +220,32 @@ def mla_prefill(dims, q_lat, q_pe, cache, cu_seqlens, max_len, w_uv, out, worksp
         ctypes.byref(dims), _ptr(q_lat, "q_lat", et), _ptr(q_pe, "q_pe", et), _ptr(cache, "cache", et),
         _ptr(cu_seqlens, "cu_seqlens", torch.int64), B, T, int(max_len), _ptr(w_uv, "w_uv", et),
         _ptr(out, "out", et), _ptr(ws, "workspace"), nbytes, _stream(stream)))
+    return out
+
+
+def mla_query(dims, x, w_qc, w_qr, positions, q_nope, q_pe, workspace=None, stream=None):
+    torch = _torch()
+    et = _elem_dtype(dims)
+    T = x.shape[0]
+    ws, nbytes = _workspace(dims, MLA_OP_QUERY, 0, T, 0, workspace, x.device)
+    _check("mla_query", load().mla_query(
+        ctypes.byref(dims), _ptr(x, "x", et), _ptr(w_qc, "w_qc", et), _ptr(w_qr, "w_qr", et),
+        _ptr(positions, "positions", torch.int32), T, _ptr(q_nope, "q_nope", et), _ptr(q_pe, "q_pe", et),
+        _ptr(ws, "workspace"), nbytes, _stream(stream)))
+    return q_nope, q_pe
+
+
+def mla_prefill_expanded(dims, q_nope, q_pe, cache, cu_seqlens, max_len, w_uk, w_uv, out, workspace=None,
+                         stream=None):
+    torch = _torch()
+    et = _elem_dtype(dims)
+    T = q_nope.shape[0]
+    B = cu_seqlens.shape[0] - 1
+    ws, nbytes = _workspace(dims, MLA_OP_PREFILL_EXPANDED, B, T, max_len, workspace, q_nope.device)
+    _check("mla_prefill_expanded", load().mla_prefill_expanded(
+        ctypes.byref(dims), _ptr(q_nope, "q_nope", et), _ptr(q_pe, "q_pe", et), _ptr(cache, "cache", et),
+        _ptr(cu_seqlens, "cu_seqlens", torch.int64), B, T, int(max_len), _ptr(w_uk, "w_uk", et),
+        _ptr(w_uv, "w_uv", et), _ptr(out, "out", et), _ptr(ws, "workspace"), nbytes, _stream(stream)))
     return out
 
 

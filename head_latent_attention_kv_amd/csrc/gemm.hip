@@ -394,6 +394,18 @@ void dispatch_bf16(const GemmArgs& g, bool a_f32, bool b_kn, bool out_bf16, hipS
 
 }  // namespace
 
+void gemm_f16_out(const GemmArgs& g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0 || g.Z <= 0) return;
+  const int64_t tiles128 = static_cast<int64_t>((g.M + 127) / 128) * ((g.N + 127) / 128) * g.Z;
+  if (g.M >= 256 && tiles128 >= 512) {
+    dim3 grid((g.N + 127) / 128, (g.M + 127) / 128, g.Z);
+    hipLaunchKernelGGL((gemm_bf16_mfma<128, 128, false, false, _Float16>), grid, dim3(256), 0, s, g);
+  } else {
+    dim3 grid((g.N + 63) / 64, (g.M + 63) / 64, g.Z);
+    hipLaunchKernelGGL((gemm_bf16_mfma<64, 64, false, false, _Float16>), grid, dim3(256), 0, s, g);
+  }
+}
+
 void gemm(const GemmArgs& g, int dtype, bool a_f32, bool b_kn, bool out_bf16, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.Z <= 0) return;
   if (dtype == kF32) {

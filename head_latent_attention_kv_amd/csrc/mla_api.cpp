@@ -207,6 +207,16 @@ size_t absorb_ws(const mla_dims* d, int64_t n_tokens) {
   return proj_bytes(d, q_cols(d), T, q_width(d));
 }
 
+// Expanded keys and values of the original-order prefill: k_nope [H, T, d_nope]
+// then v [H, T, d_v], fp16.
+size_t expanded_k_bytes(const mla_dims* d, int64_t n_tokens) {
+  return align_up(static_cast<size_t>(std::max<int64_t>(n_tokens, 0)) * d->n_heads * d->d_nope * 2);
+}
+size_t expanded_ws(const mla_dims* d, int64_t n_tokens) {
+  return expanded_k_bytes(d, n_tokens) +
+         align_up(static_cast<size_t>(std::max<int64_t>(n_tokens, 0)) * d->n_heads * d->d_v * 2);
+}
+
 int launch_status() {
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? MLA_OK : MLA_EHIP;
@@ -279,6 +289,8 @@ size_t mla_workspace_size(const mla_dims* dims, int op, int32_t batch, int64_t n
     case MLA_OP_ABSORB: return absorb_ws(dims, n_tokens);
     case MLA_OP_DECODE: return decode_plan(dims, batch, max_len).total();
     case MLA_OP_PREFILL: return prefill_ws(dims, n_tokens);
+    case MLA_OP_QUERY: return absorb_ws(dims, n_tokens);
+    case MLA_OP_PREFILL_EXPANDED: return expanded_ws(dims, n_tokens);
     default: return 0;
   }
 }
@@ -468,6 +480,80 @@ int mla_prefill(const mla_dims* dims, const void* q_lat, const void* q_pe, const
     mla::attend_generic(dims->dtype, sh, q_lat, q_pe, cache, nullptr, nullptr, cu_seqlens, batch,
                         n_tokens, 1, max_len, nullptr, nullptr, o_lat, s);
   apply_w_uv(dims, o_lat, n_tokens, w_uv, out, s);
+  return launch_status();
+}
+
+int mla_query(const mla_dims* dims, const void* x, const void* w_qc, const void* w_qr,
+              const int32_t* positions, int64_t n_tokens, void* q_nope, void* q_pe, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_tokens < 0) return MLA_EINVAL;
+  if (n_tokens == 0) return MLA_OK;
+  if (n_tokens > INT32_MAX) return MLA_ENOTSUP;
+  if (!ptr_ok(x) || !ptr_ok(w_qc) || !ptr_ok(w_qr) || !ptr_ok(positions) || !ptr_ok(q_nope) ||
+      !ptr_ok(q_pe) || !ptr_ok(workspace))
+    return MLA_EINVAL;
+  if (workspace_bytes < absorb_ws(dims, n_tokens)) return MLA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int H = dims->n_heads;
+  const int64_t ld = q_width(dims);
+  float* q = static_cast<float*>(workspace);
+  const Proj p = proj_two(dims, x, w_qc, H * dims->d_nope, w_qr, H * dims->d_rope, q, ld, n_tokens, s);
+  mla::sum_split_slices(q, p.splits, p.sps, static_cast<int>(n_tokens), q_cols(dims), ld, s);
+  mla::finalize_query_rope(dims->dtype, q + static_cast<int64_t>(H) * dims->d_nope, ld, q_pe, positions,
+                           n_tokens, H, dims->d_rope, dims->rope_theta, s);
+  mla::cast_rows(dims->dtype, q, ld, H * dims->d_nope, q_nope, static_cast<int64_t>(H) * dims->d_nope,
+                 n_tokens, s);
+  return launch_status();
+}
+
+int mla_prefill_expanded(const mla_dims* dims, const void* q_nope, const void* q_pe, const void* cache,
+                         const int64_t* cu_seqlens, int32_t batch, int64_t n_tokens, int32_t max_len,
+                         const void* w_uk, const void* w_uv, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || n_tokens < 0) return MLA_EINVAL;
+  if (batch == 0 || n_tokens == 0) return MLA_OK;
+  if (max_len <= 0) return MLA_EINVAL;
+  if (n_tokens > INT32_MAX) return MLA_ENOTSUP;
+  const AttnShape sh = shape_of(dims);
+  if (dims->dtype != MLA_BF16 || !mla::prefill_expanded_supported(sh, dims->d_nope, dims->d_v))
+    return MLA_ENOTSUP;
+  if (!ptr_ok(q_nope) || !ptr_ok(q_pe) || !ptr_ok(cache) || !ptr_ok(cu_seqlens) || !ptr_ok(w_uk) ||
+      !ptr_ok(w_uv) || !ptr_ok(out) || !ptr_ok(workspace))
+    return MLA_EINVAL;
+  if (workspace_bytes < expanded_ws(dims, n_tokens)) return MLA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int H = dims->n_heads;
+  const int T = static_cast<int>(n_tokens);
+  char* ws = static_cast<char*>(workspace);
+  void* k_nope = ws;
+  void* v = ws + expanded_k_bytes(dims, n_tokens);
+  // k_nope[h, t, :] = W_UK[h] · c[t]  and  v[h, t, :] = W_UV[h] · c[t]  (c = cache row t, cols 0..r),
+  // stored in fp16: three more significant bits than bf16 for the two operands
+  // this order rounds and the absorbed one does not
+  auto expand = [&](const void* w, int n, void* dst) {
+    GemmArgs g{};
+    g.A = cache;
+    g.sAz = 0;
+    g.sAm = sh.row_w;
+    g.B = w;
+    g.sBz = static_cast<int64_t>(n) * dims->rank;
+    g.sBo = dims->rank;
+    g.C = dst;
+    g.sCz = static_cast<int64_t>(T) * n;
+    g.sCm = n;
+    g.M = T;
+    g.N = n;
+    g.K = dims->rank;
+    g.Z = H;
+    mla::gemm_f16_out(g, s);
+  };
+  expand(w_uk, dims->d_nope, k_nope);
+  expand(w_uv, dims->d_v, v);
+  mla::prefill_expanded(sh, q_nope, q_pe, k_nope, v, cache, cu_seqlens, batch, n_tokens, out, s);
   return launch_status();
 }
 

@@ -45,6 +45,10 @@ template <> struct Elem<float> {
   __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
   __device__ __forceinline__ static void store(float* p, int64_t i, float v) { p[i] = v; }
 };
+template <> struct Elem<_Float16> {
+  __device__ __forceinline__ static float load(const _Float16* p, int64_t i) { return static_cast<float>(p[i]); }
+  __device__ __forceinline__ static void store(_Float16* p, int64_t i, float v) { p[i] = static_cast<_Float16>(v); }
+};
 template <> struct Elem<bf16_t> {
   __device__ __forceinline__ static float load(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
   __device__ __forceinline__ static void store(bf16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }

@@ -24,6 +24,8 @@ struct GemmArgs {
 // dtype == kF32: fp32 in/out VALU path.  dtype == kBF16: A bf16 (or fp32 if a_f32),
 // B bf16, fp32 accumulate, C fp32 or bf16 (out_bf16).
 void gemm(const GemmArgs& g, int dtype, bool a_f32, bool b_kn, bool out_bf16, hipStream_t s);
+// bf16 A [z][m][k], bf16 B [z][n][k] -> fp16 C (fp32 accumulate).
+void gemm_f16_out(const GemmArgs& g, hipStream_t s);
 
 // Weight-streaming GEMM for M <= 64 rows: C[z][m][n] = Σ_k A[z][m][k]·W[z][n][k]
 // with W rows n < N0 from B0 and n >= N0 from B1 (row n - N0), bf16 weights.
@@ -67,6 +69,10 @@ void finalize_query_rope(int dtype, const float* proj, int64_t ld, void* q_pe,
                          const int32_t* positions, int64_t n_tokens, int n_heads, int d_rope,
                          double theta, hipStream_t s);
 
+// dst[row, 0:n_cols] = src[row, 0:n_cols] (fp32 -> dtype), rows strided.
+void cast_rows(int dtype, const float* src, int64_t ld_src, int n_cols, void* dst, int64_t ld_dst,
+               int64_t n_rows, hipStream_t s);
+
 // Shape of one attention call, as the kernels see it.
 struct AttnShape {
   int H, G, r, d_rope, row_w;  // row_w = r + G*d_rope
@@ -109,5 +115,13 @@ bool prefill_mfma_supported(const AttnShape& sh);
 void prefill_mfma(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
                   const int64_t* cu, int batch, int64_t n_tokens, int max_len, float* o_out,
                   hipStream_t s);
+
+// bf16 MFMA causal prefill in the original order (see prefill_expanded.hip):
+// k_nope [H, T, d_nope] and v [H, T, d_v] already expanded (fp16), rotary keys
+// from the cache rows, output [T, H, d_v] bf16.
+bool prefill_expanded_supported(const AttnShape& sh, int d_nope, int d_v);
+void prefill_expanded(const AttnShape& sh, const void* q_nope, const void* q_pe, const void* k_nope,
+                      const void* v, const void* cache, const int64_t* cu, int batch, int64_t n_tokens,
+                      void* out, hipStream_t s);
 
 }  // namespace mla

@@ -100,7 +100,32 @@ __global__ __launch_bounds__(256) void query_rope_kernel(const float* __restrict
   }
 }
 
+// dst[row, c] = src[row, c] for c < n_cols, cast to T (the q_nope columns of the
+// fp32 query projection).
+template <typename T>
+__global__ __launch_bounds__(256) void cast_rows_kernel(const float* __restrict__ src, int64_t ld_src,
+                                                        int n_cols, T* __restrict__ dst, int64_t ld_dst,
+                                                        int64_t n_rows) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= n_cols) return;
+  for (int64_t row = blockIdx.y; row < n_rows; row += gridDim.y)
+    Elem<T>::store(dst, row * ld_dst + c, src[row * ld_src + c]);
+}
+
 }  // namespace
+
+void cast_rows(int dtype, const float* src, int64_t ld_src, int n_cols, void* dst, int64_t ld_dst,
+               int64_t n_rows, hipStream_t s) {
+  if (n_rows <= 0 || n_cols <= 0) return;
+  dim3 grid(static_cast<unsigned>((n_cols + 255) / 256),
+            static_cast<unsigned>(std::min<int64_t>(n_rows, 65535)));
+  if (dtype == kF32)
+    hipLaunchKernelGGL(cast_rows_kernel<float>, grid, dim3(256), 0, s, src, ld_src, n_cols,
+                       static_cast<float*>(dst), ld_dst, n_rows);
+  else
+    hipLaunchKernelGGL(cast_rows_kernel<bf16_t>, grid, dim3(256), 0, s, src, ld_src, n_cols,
+                       static_cast<bf16_t*>(dst), ld_dst, n_rows);
+}
 
 void finalize_cache_rows(int dtype, const float* proj, int64_t ld, int splits, int64_t sps,
                          void* cache, const int64_t* slots, const int32_t* positions,

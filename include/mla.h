@@ -64,7 +64,9 @@ typedef enum mla_op {
   MLA_OP_WRITE_CACHE = 0,
   MLA_OP_ABSORB = 1,
   MLA_OP_DECODE = 2,
-  MLA_OP_PREFILL = 3
+  MLA_OP_PREFILL = 3,
+  MLA_OP_QUERY = 4,
+  MLA_OP_PREFILL_EXPANDED = 5
 } mla_op;
 
 /* Layer dimensions and hyper-parameters shared by all calls. */
@@ -186,6 +188,43 @@ int mla_prefill(const mla_dims* dims, const void* q_lat, const void* q_pe, const
                 const int64_t* cu_seqlens, int32_t batch, int64_t n_tokens, int32_t max_len,
                 const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/* Query side without absorption (the input of the original-order prefill).
+ *   q_nope[t,h] = x[t]·W_QC[h*d_nope : +d_nope]ᵀ
+ *   q_pe[t,h]   = RoPE(x[t]·W_QR[h*d_rope : +d_rope]ᵀ, positions[t])
+ * Source: MLA principle page, split of the query into q_nope / q_pe and the
+ * rotation of q_pe; MLAfication page, q_c_proj / q_r_proj.
+ *   x device [n_tokens, d_model]; w_qc device [H*d_nope, d_model];
+ *   w_qr device [H*d_rope, d_model]; positions device int32 [n_tokens]
+ *   q_nope device out [n_tokens, H, d_nope]; q_pe device out [n_tokens, H, d_rope]
+ *   workspace device, >= mla_workspace_size(dims, MLA_OP_QUERY, 0, n_tokens, 0) bytes
+ * n_tokens == 0 is a no-op. */
+int mla_query(const mla_dims* dims, const void* x, const void* w_qc, const void* w_qr,
+              const int32_t* positions, int64_t n_tokens, void* q_nope, void* q_pe, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* Causal prefill in the original (non-absorbed) order, same sequences and
+ * result as mla_prefill.  The cached latents are first up-projected per head,
+ *   k_nope[h,l] = W_UK[h]·c[l],   v[h,l] = W_UV[h]·c[l],
+ * and token t then attends to rows cu_seqlens[b] .. t with
+ *   s[h,l] = scale·(q_nope[t,h]·k_nope[h,l] + q_pe[t,h]·kr[l, g(h)])
+ *   out[t,h,:] = Σ_l softmax_l(s)[h,l]·v[h,l]
+ * For a long prompt this order costs 2(d_nope + d_rope) + 2 d_v flops per
+ * (query, key, head) against 2(r + d_rope) + 2r for the absorbed one.
+ * Source: MLA principle page, section "原始顺序" eqs. (1)-(2) (v = W_UV·c, then
+ * o = P·v) and the up-projection kv_b_proj split into W_UK / W_UV; causal SDPA
+ * of the nanowhale MLA page.
+ *   q_nope device [n_tokens, H, d_nope]; q_pe device [n_tokens, H, d_rope] (mla_query)
+ *   cache, cu_seqlens, batch, n_tokens, max_len: as mla_prefill
+ *   w_uk device [H, d_nope, r]; w_uv device [H, d_v, r]; out device out [n_tokens, H, d_v]
+ *   workspace device, >= mla_workspace_size(dims, MLA_OP_PREFILL_EXPANDED, batch, n_tokens,
+ *   max_len) bytes: it holds k_nope and v in bf16 (2·n_tokens·H·(d_nope + d_v) bytes)
+ * Compiled for bf16 with d_nope = d_v = 128 and d_rope = 64; other layers get
+ * MLA_ENOTSUP (mla_prefill covers them).  batch == 0 or n_tokens == 0 is a no-op. */
+int mla_prefill_expanded(const mla_dims* dims, const void* q_nope, const void* q_pe, const void* cache,
+                         const int64_t* cu_seqlens, int32_t batch, int64_t n_tokens, int32_t max_len,
+                         const void* w_uk, const void* w_uv, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* Human-readable text for a status code (static storage). */
 const char* mla_strerror(int status);

@@ -72,6 +72,47 @@ def absorb(layer: DeviceLayer, x_dev, positions: np.ndarray):
     return q_lat, q_pe
 
 
+def query(layer: DeviceLayer, x_dev, positions: np.ndarray):
+    """mla_query: q_nope [T, H, d_nope] and q_pe [T, H, d_rope] without absorption."""
+    import head_latent_attention_kv_amd as M
+    torch = torch_mod()
+    cfg = layer.cfg
+    T = x_dev.shape[0]
+    q_nope = torch.empty((T, cfg.n_heads, cfg.d_nope), dtype=elem_dtype(cfg), device=x_dev.device)
+    q_pe = torch.empty((T, cfg.n_heads, cfg.d_rope), dtype=elem_dtype(cfg), device=x_dev.device)
+    pos = torch.from_numpy(positions.astype(np.int32)).to(x_dev.device)
+    M.mla_query(layer.dims, x_dev, layer.w_dev["w_qc"], layer.w_dev["w_qr"], pos, q_nope, q_pe)
+    return q_nope, q_pe
+
+
+def prefill_expanded(layer: DeviceLayer, q_nope, q_pe, cache, lengths):
+    """mla_prefill_expanded over packed sequences of the given lengths; returns the
+    output and the workspace (k_nope [H, T, d_nope] then v [H, T, d_v], fp16)."""
+    import head_latent_attention_kv_amd as M
+    torch = torch_mod()
+    cfg = layer.cfg
+    T = q_nope.shape[0]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int64, device="cuda")
+    need = M.mla_workspace_size(layer.dims, M.MLA_OP_PREFILL_EXPANDED, len(lengths), T, int(max(lengths)))
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, cfg.n_heads, cfg.d_v), dtype=elem_dtype(cfg), device="cuda")
+    M.mla_prefill_expanded(layer.dims, q_nope, q_pe, cache, cu, int(max(lengths)), layer.w_dev["w_uk"],
+                           layer.w_dev["w_uv"], out, workspace=ws)
+    return out, ws
+
+
+def expanded_kv(layer: DeviceLayer, ws, T: int):
+    """The fp16 k_nope [H, T, d_nope] and v [H, T, d_v] an mla_prefill_expanded call
+    left in its workspace, as host arrays."""
+    torch = torch_mod()
+    cfg = layer.cfg
+    nk = cfg.n_heads * T * cfg.d_nope
+    k_bytes = (nk * 2 + 255) // 256 * 256
+    k = ws[:nk * 2].view(torch.float16).view(cfg.n_heads, T, cfg.d_nope)
+    v = ws[k_bytes:k_bytes + cfg.n_heads * T * cfg.d_v * 2].view(torch.float16).view(cfg.n_heads, T, cfg.d_v)
+    return to_host(k), to_host(v)
+
+
 @dataclasses.dataclass
 class DecodeRun:
     lengths: np.ndarray

@@ -112,3 +112,29 @@ def test_workspace_sizes_cover_the_plan():
     assert lib.mla_workspace_size(ctypes.byref(d), abi.MLA_OP_WRITE_CACHE, 0, 1000, 0) >= 1000 * 576 * 4
     assert lib.mla_workspace_size(ctypes.byref(d), abi.MLA_OP_ABSORB, 0, 64, 0) >= 64 * 128 * 192 * 4
     assert lib.mla_workspace_size(ctypes.byref(d), 99, 1, 1, 1) == 0
+
+
+def test_original_order_prefill_entry_points():
+    """mla_query / mla_prefill_expanded: argument checks, shapes without a
+    compiled kernel, and the workspace that holds the expanded keys and values."""
+    abi, lib = _lib()
+    null = None
+    d = abi.dims_of(I.CONFIGS["long_prefill_131k"])
+    T = 131072
+    ws = lib.mla_workspace_size(ctypes.byref(d), abi.MLA_OP_PREFILL_EXPANDED, 1, T, T)
+    assert ws >= T * 16 * (128 + 128) * 2
+    assert lib.mla_workspace_size(ctypes.byref(d), abi.MLA_OP_QUERY, 0, 64, 0) >= 64 * 16 * 192 * 4
+    assert lib.mla_query(ctypes.byref(d), null, null, null, null, 3, null, null, null, 0, null) == abi.MLA_EINVAL
+    assert lib.mla_query(ctypes.byref(d), null, null, null, null, 0, null, null, null, 0, null) == abi.MLA_OK
+    assert lib.mla_query(ctypes.byref(d), null, null, null, null, -1, null, null, null, 0, null) == abi.MLA_EINVAL
+    pe = lib.mla_prefill_expanded
+    assert pe(ctypes.byref(d), null, null, null, null, 1, 10, 10, null, null, null, null, 0, null) == abi.MLA_EINVAL
+    assert pe(ctypes.byref(d), null, null, null, null, 0, 10, 10, null, null, null, null, 0, null) == abi.MLA_OK
+    assert pe(ctypes.byref(d), null, null, null, null, 1, 10, 0, null, null, null, null, 0, null) == abi.MLA_EINVAL
+    # aligned stand-in pointers that are never dereferenced: the workspace check fails first
+    p = 0x10000
+    assert pe(ctypes.byref(d), p, p, p, p, 1, 10, 10, p, p, p, p, 16, null) == abi.MLA_EWORKSPACE
+    # shapes without a compiled kernel: fp32 layers, other rotary or value widths
+    for cfg in ("tiny_f32", "qwen25_7b_decode", "qwen3_30b_ragged_decode"):
+        dd = abi.dims_of(I.CONFIGS[cfg])
+        assert pe(ctypes.byref(dd), p, p, p, p, 1, 10, 10, p, p, p, p, 1 << 40, null) == abi.MLA_ENOTSUP, cfg

@@ -297,11 +297,128 @@ def test_prefill_full_size_sampled(torch):
     ref_chain = O.mla_attention(qn[sel], qr[sel], c_o, kr_o, w["w_uk"], w["w_uv"], sub, np.arange(L),
                                 np.zeros(len(sub), int), zeros_k, cfg.softmax_scale, head_chunk=1)
     err_chain = Hh.rel_err_rows(got[sel], ref_chain)
+    # the same prefill in the original order, checked against the same references
+    xd = Hh.to_dev(run.x_q, cfg.dtype)
+    q_nope, q_pe_e = Hh.query(layer, xd, np.arange(L))
+    del xd
+    out_e, ws_e = Hh.prefill_expanded(layer, q_nope, q_pe_e, run.cache, [L])
+    torch.cuda.synchronize()
+    got_e = Hh.to_host(out_e[torch.from_numpy(rows).cuda()])
+    del ws_e, out_e
+    err_e = Hh.rel_err_rows(got_e, ref)
+    err_e_chain = Hh.rel_err_rows(got_e[sel], ref_chain)
     print(f"prefill {L}: attn={err_attn:.3e} chain={err_chain:.3e} write={err_write:.3e} "
-          f"q_lat={err_qlat:.3e} q_pe={err_qpe:.3e}")
+          f"q_lat={err_qlat:.3e} q_pe={err_qpe:.3e}; original order attn={err_e:.3e} chain={err_e_chain:.3e}")
     for name, v in (("attn", err_attn), ("chain", err_chain), ("write", err_write), ("q_lat", err_qlat),
-                    ("q_pe", err_qpe)):
+                    ("q_pe", err_qpe), ("expanded attn", err_e), ("expanded chain", err_e_chain)):
         assert v <= Hh.TOL[cfg.dtype], (name, v)
+
+
+# ----------------------------------------------------------------------------
+# prefill in the original order (expanded k_nope / v), long-prefill layer dims
+# ----------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "long_prefill_131k"])
+def test_query_matches_oracle(torch, name):
+    from oracle import mla_oracle as O
+    cfg = I.CONFIGS[name]
+    T = 300
+    _print_case("query", cfg=name, T=T)
+    layer = Hh.make_layer(cfg)
+    x = I.x_rows(cfg, 0, 0, T)
+    pos = np.random.default_rng(7).integers(0, 100000, T)
+    q_nope, q_pe = Hh.query(layer, Hh.to_dev(x, cfg.dtype), pos)
+    torch.cuda.synchronize()
+    qn, qr = O.query(x, layer.w_host["w_qc"], layer.w_host["w_qr"], pos, n_heads=cfg.n_heads,
+                     d_nope=cfg.d_nope, d_rope=cfg.d_rope, theta=cfg.rope_theta)
+    e_n = Hh.rel_err_rows(Hh.to_host(q_nope), qn)
+    e_r = Hh.rel_err_rows(Hh.to_host(q_pe), qr)
+    print(f"{name} query: q_nope {e_n:.3e} q_pe {e_r:.3e}")
+    assert e_n <= Hh.TOL[cfg.dtype] and e_r <= Hh.TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("lengths", [[700, 1, 333], [256], [1], [300, 257, 513, 40]])
+def test_prefill_expanded_ragged(torch, lengths):
+    """Ragged batches (workgroups of 256 queries spanning sequence ends, a ragged
+    last tile, one-token sequences) against the oracle's whole chain; the
+    expanded k_nope / v the call leaves in its workspace against the oracle's
+    expansion of the GPU-written latents; and the same call in the absorbed
+    order (mla_prefill) against the same oracle."""
+    import head_latent_attention_kv_amd as M
+    from oracle import mla_oracle as O
+    cfg = I.CONFIGS["long_prefill_131k"]
+    _print_case("prefill_expanded", lengths=lengths)
+    layer = Hh.make_layer(cfg)
+    T = sum(lengths)
+    x = np.concatenate([I.x_rows(cfg, b, 0, n) for b, n in enumerate(lengths)])
+    pos = np.concatenate([np.arange(n) for n in lengths])
+    seg = np.concatenate([np.full(n, b) for b, n in enumerate(lengths)])
+    cache = torch.empty((T, cfg.row_width), dtype=torch.bfloat16, device="cuda")
+    xd = Hh.to_dev(x, cfg.dtype)
+    Hh.write_cache(layer, xd, pos, np.arange(T), cache)
+    q_nope, q_pe = Hh.query(layer, xd, pos)
+    out, ws = Hh.prefill_expanded(layer, q_nope, q_pe, cache, lengths)
+    q_lat, q_pe_a = Hh.absorb(layer, xd, pos)
+    out_abs = torch.empty_like(out)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int64, device="cuda")
+    M.mla_prefill(layer.dims, q_lat, q_pe_a, cache, cu, max(lengths), layer.w_dev["w_uv"], out_abs)
+    torch.cuda.synchronize()
+    w = layer.w_host
+    ref = O.mla_layer(x, x, w, k_pos=pos, q_pos=pos, k_seg=seg, q_seg=seg, n_heads=cfg.n_heads,
+                      n_groups=cfg.n_groups, d_nope=cfg.d_nope, d_rope=cfg.d_rope,
+                      theta=cfg.rope_theta, scale=cfg.softmax_scale, head_chunk=4)
+    err = Hh.rel_err_rows(Hh.to_host(out), ref)
+    err_abs = Hh.rel_err_rows(Hh.to_host(out_abs), ref)
+    c, _ = O.split_rows(Hh.to_host(cache), cfg.rank, cfg.n_groups, cfg.d_rope)
+    kn_ref, v_ref = O.expand_kv(c, w["w_uk"], w["w_uv"])          # [T, H, d]
+    kn, v = Hh.expanded_kv(layer, ws, T)                             # [H, T, d]
+    err_k = Hh.rel_err_rows(kn.transpose(1, 0, 2), kn_ref)
+    err_v = Hh.rel_err_rows(v.transpose(1, 0, 2), v_ref)
+    print(f"prefill expanded {lengths}: chain {err:.3e} (absorbed {err_abs:.3e}) k_nope {err_k:.3e} "
+          f"v {err_v:.3e}")
+    for nm, e in (("chain", err), ("absorbed", err_abs), ("k_nope", err_k), ("v", err_v)):
+        assert e <= Hh.TOL["bf16"], (nm, e)
+
+
+def test_prefill_expanded_restart(torch):
+    """Hidden states from position 100 on are scaled 8x, so their queries and
+    keys score ~64x higher against each other than against the first rows: the
+    later tiles pass each query's first-tile reference by far more than the
+    kernel's 2^15 headroom and the workgroups take their second pass with the
+    true maximum.  At such logits the bf16 rounding of any operand moves the
+    softmax, so the reference is the oracle's attention definition on exactly
+    the operands the kernel reads: the GPU's q_nope / q_pe, the expanded
+    k_nope / v from the workspace and the rotary keys of the GPU cache."""
+    from oracle import mla_oracle as O
+    cfg = I.CONFIGS["long_prefill_131k"]
+    lengths = [600, 300]
+    _print_case("prefill_expanded_restart", lengths=lengths)
+    layer = Hh.make_layer(cfg)
+    T = sum(lengths)
+    xs = []
+    for b, n in enumerate(lengths):
+        xb = I.x_rows(cfg, b, 0, n, quantized=False)
+        xb[100:] *= np.float32(8.0)
+        xs.append(I.quantize(xb, cfg.dtype))
+    x = np.concatenate(xs)
+    pos = np.concatenate([np.arange(n) for n in lengths])
+    seg = np.concatenate([np.full(n, b) for b, n in enumerate(lengths)])
+    cache = torch.empty((T, cfg.row_width), dtype=torch.bfloat16, device="cuda")
+    xd = Hh.to_dev(x, cfg.dtype)
+    Hh.write_cache(layer, xd, pos, np.arange(T), cache)
+    q_nope, q_pe = Hh.query(layer, xd, pos)
+    out, ws = Hh.prefill_expanded(layer, q_nope, q_pe, cache, lengths)
+    torch.cuda.synchronize()
+    kn, v = Hh.expanded_kv(layer, ws, T)
+    _, kr = O.split_rows(Hh.to_host(cache), cfg.rank, cfg.n_groups, cfg.d_rope)
+    Q = np.concatenate([Hh.to_host(q_nope), Hh.to_host(q_pe)], axis=-1)          # [T, H, 192]
+    K = np.concatenate([kn.transpose(1, 0, 2), np.repeat(kr, cfg.n_heads, 1)], axis=-1)
+    allowed = (seg[:, None] == seg[None, :]) & (pos[None, :] <= pos[:, None])
+    ref = O.softmax_attention(Q, K, v.transpose(1, 0, 2), allowed, cfg.softmax_scale)
+    err = Hh.rel_err_rows(Hh.to_host(out), ref)
+    print(f"prefill expanded restart {lengths}: attn {err:.3e}")
+    assert err <= Hh.TOL["bf16"], err
 
 
 # ----------------------------------------------------------------------------
