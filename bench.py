@@ -176,6 +176,13 @@ def prefill_alg_flops(cfg, L: int) -> int:
     return pairs * cfg.n_heads * (2 * cfg.row_width + 2 * cfg.rank)
 
 
+def prefill_orig_alg_flops(cfg, L: int) -> int:
+    """The same attention in the original order: per (query, key <= query, head)
+    2(d_nope + d_rope) for the score and 2 d_v for P·v."""
+    pairs = L * (L + 1) // 2
+    return pairs * cfg.n_heads * (2 * (cfg.d_nope + cfg.d_rope) + 2 * cfg.d_v)
+
+
 def bench_prefill(args, torch, M, I, Hh, cfg):
     """Long causal prefill: one step = mla_write_cache + mla_absorb + mla_prefill over
     the whole sequence (x resident in HBM); the attention kernel is timed alone
@@ -199,6 +206,9 @@ def bench_prefill(args, torch, M, I, Hh, cfg):
     ws_w = torch.empty(M.mla_workspace_size(dims, M.MLA_OP_WRITE_CACHE, 0, L, 0), dtype=torch.uint8, device="cuda")
     ws_a = torch.empty(M.mla_workspace_size(dims, M.MLA_OP_ABSORB, 0, L, 0), dtype=torch.uint8, device="cuda")
     ws_p = torch.empty(M.mla_workspace_size(dims, M.MLA_OP_PREFILL, 1, L, L), dtype=torch.uint8, device="cuda")
+    q_nope = torch.empty((L, cfg.n_heads, cfg.d_nope), dtype=et, device="cuda")
+    ws_e = torch.empty(M.mla_workspace_size(dims, M.MLA_OP_PREFILL_EXPANDED, 1, L, L), dtype=torch.uint8,
+                       device="cuda")
     wd = layer.w_dev
     setup_s = time.perf_counter() - t_setup
 
@@ -209,6 +219,15 @@ def bench_prefill(args, torch, M, I, Hh, cfg):
 
     def attention():
         M.mla_prefill(dims, q_lat, q_pe, cache, cu, L, wd["w_uv"], out, workspace=ws_p)
+
+    # the same prefill in the original order (k_nope and v expanded once per row)
+    def step_orig():
+        M.mla_write_cache(dims, x, wd["w_dkv"], wd["w_kr"], pos, slots, cache, workspace=ws_w)
+        M.mla_query(dims, x, wd["w_qc"], wd["w_qr"], pos, q_nope, q_pe, workspace=ws_a)
+        M.mla_prefill_expanded(dims, q_nope, q_pe, cache, cu, L, wd["w_uk"], wd["w_uv"], out, workspace=ws_e)
+
+    def attention_orig():
+        M.mla_prefill_expanded(dims, q_nope, q_pe, cache, cu, L, wd["w_uk"], wd["w_uv"], out, workspace=ws_e)
 
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -233,6 +252,13 @@ def bench_prefill(args, torch, M, I, Hh, cfg):
     print(f"[bench] prefill {L}: step {ms_step:.2f} ms, mla_prefill {ms_attn:.2f} ms "
           f"({tflops:.0f} TFLOP/s on the attention) (setup {setup_s:.1f} s)", file=sys.stderr, flush=True)
     assert torch.isfinite(out.float()).all(), "non-finite prefill output"
+    ms_step_o = timed(step_orig, steps, warm)
+    ms_attn_o = timed(attention_orig, steps, warm)
+    flops_o = prefill_orig_alg_flops(cfg, L)
+    tflops_o = flops_o / (ms_attn_o * 1e-3) / 1e12
+    print(f"[bench] original order: step {ms_step_o:.2f} ms, mla_prefill_expanded {ms_attn_o:.2f} ms "
+          f"({tflops_o:.0f} TFLOP/s)", file=sys.stderr, flush=True)
+    assert torch.isfinite(out.float()).all(), "non-finite original-order prefill output"
     line = {
         "metric": "MLA absorbed causal prefill tokens/s + % of MFMA roofline, H=16 r=256 L=131072",
         "value": round(L / (ms_step * 1e-3), 1),
@@ -253,6 +279,13 @@ def bench_prefill(args, torch, M, I, Hh, cfg):
                      "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
                      "alg_flops_per_launch": flops, "ms_per_launch": round(ms_attn, 3)},
+        "original_order": {
+            "step": "mla_write_cache + mla_query + mla_prefill_expanded",
+            "tokens_per_s": round(L / (ms_step_o * 1e-3), 1), "ms_per_step": round(ms_step_o, 3),
+            "kernel": "mla_prefill_expanded (K/V expansion + attention)",
+            "achieved": round(tflops_o, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+            "frac": round(tflops_o / MFMA_BF16_PEAK_TFS, 4), "alg_flops_per_launch": flops_o,
+            "ms_per_launch": round(ms_attn_o, 3)},
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)

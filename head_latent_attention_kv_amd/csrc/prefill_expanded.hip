@@ -19,9 +19,10 @@
 // The rotary part of the score stays bf16; both parts accumulate into one
 // fp32 tile.  fp16 bounds |k_nope|, |v| and |q_nope| to 65504.
 //
-// Workgroup = 4 wave64s on 256 consecutive query tokens of one head; each wave
-// owns 64 queries (two 32-wide MFMA column blocks), so every K or V fragment
-// read from LDS feeds two MFMAs.  Per 32-key tile:
+// Workgroup = W wave64s on 256 consecutive query tokens of one head; each wave
+// owns 256/W queries (8/W 32-wide MFMA column blocks): with W = 4 every K or V
+// fragment read from LDS feeds two MFMAs, with W = 8 two waves share each SIMD
+// and hide each other's LDS and softmax latencies.  Per 32-key tile:
 //   - Sᵀ[32 keys x 64 queries] = K·Qᵀ with v_mfma_f32_32x32x16_bf16: key rows
 //     as the A operand from LDS, Qᵀ as the B operand held in registers.  In
 //     this orientation a lane owns one query column, so the row max is a
@@ -39,7 +40,7 @@
 // The score of tile t+1 is issued before the softmax and PV of tile t, so the
 // matrix cores stay busy while the softmax runs.
 // Tiles stream HBM -> LDS with global_load_lds_dwordx4 through a 4-stage ring;
-// each tile's 20 one-KB copies are split evenly over the four waves.
+// each tile's 20 one-KB copies are spread over the waves.
 #include <math.h>
 
 #include <algorithm>
@@ -48,16 +49,17 @@
 #include "mla_device.h"
 #include "mla_internal.h"
 
+#ifndef MLA_PREFILL_FA_WAVES
+#define MLA_PREFILL_FA_WAVES 8  // waves per workgroup (4: one per SIMD, 8: two per SIMD)
+#endif
+
 namespace mla {
 
 namespace {
 
 constexpr int kDN = 128;            // d_nope (key/query dims without position)
 constexpr int kDV = 128;            // d_v
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kQW = 64;             // queries per wave
-constexpr int kBM = kQW * kWaves;   // queries per workgroup
+constexpr int kBM = 256;            // queries per workgroup
 constexpr int kBN = 32;             // keys per tile
 constexpr int kStages = 4;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -82,10 +84,7 @@ struct FShape {
   static constexpr int kKnOps = kKnBytes / 1024;
   static constexpr int kKrOps = kKrBytes / 1024;
   static constexpr int kVOps = kVBytes / 1024;
-  static_assert(kKnOps % kWaves == 0 && kKrOps % kWaves == 0 && kVOps % kWaves == 0,
-                "copies split evenly over the waves");
-  static constexpr int kOpsPerWave = (kKnOps + kKrOps + kVOps) / kWaves;
-  static_assert(3 * kOpsPerWave < 64, "vmcnt range");
+  static constexpr int kOps = kKnOps + kKrOps + kVOps;
   static constexpr int kKrChunks = DR / 8;          // 16-byte chunks of a rotary row
   static constexpr int kKrRowsPer256 = 16 / kKrChunks;
   static constexpr int kKS = (kDN + DR) / 16;       // score k-steps
@@ -132,13 +131,19 @@ __device__ __forceinline__ void wait_tiles_after() {
   wait_vmcnt<N * PerWave>();
 }
 
-template <int DR>
-__global__ __launch_bounds__(kThreads, 1) void prefill_fa_kernel(
+template <int DR, int W>
+__global__ __launch_bounds__(64 * W, 1) void prefill_fa_kernel(
     const bf16_t* __restrict__ q_nope, const bf16_t* __restrict__ q_pe,
     const _Float16* __restrict__ k_nope, const _Float16* __restrict__ v,
     const bf16_t* __restrict__ cache, const int64_t* __restrict__ cu, int batch, int n_tokens,
     int n_heads, int heads_per_group, int row_w, int r, float scale, bf16_t* __restrict__ out) {
   using S = FShape<DR>;
+  constexpr int kQB = 8 / W;          // 32-query column blocks per wave
+  constexpr int kQW = 32 * kQB;       // queries per wave
+  static_assert(W * kQW == kBM && S::kKnOps % W == 0 && S::kVOps % W == 0, "wave split");
+  // tile copies per wave: the first kOps % W waves take one more
+  constexpr int kOpsHi = (S::kOps + W - 1) / W, kOpsLo = S::kOps / W;
+  static_assert(3 * kOpsHi < 64, "vmcnt range");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   const int tid = threadIdx.x;
@@ -168,10 +173,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fa_kernel(
   const int qwl = min(qw0 + kQW - 1, n_tokens - 1);
   const int start_last = wave_on ? seq_start(qwl) : k_lo;
 
-  // ---- this lane's two queries (columns l32 of the two 32-query blocks)
-  int qv[2], qst[2];
+  // ---- this lane's queries (column l32 of each 32-query block)
+  int qv[kQB], qst[kQB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < kQB; ++qb) {
     qv[qb] = qw0 + 32 * qb + l32;
     qst[qb] = seq_start(min(qv[qb], n_tokens - 1));
   }
@@ -180,10 +185,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fa_kernel(
   // no-position part converted to fp16 (exact for bf16 values of moderate range)
   constexpr int kKN = kDN / 16;       // k-steps of the no-position part
   constexpr int kKR = S::kKS - kKN;   // k-steps of the rotary part
-  f16x8 qn[2][kKN];
-  bf16x8 qr[2][kKR];
+  f16x8 qn[kQB][kKN];
+  bf16x8 qr[kQB][kKR];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < kQB; ++qb) {
     const int64_t qrow = static_cast<int64_t>(min(qv[qb], n_tokens - 1)) * n_heads + head;
 #pragma unroll
     for (int ks = 0; ks < kKN; ++ks) {
@@ -215,8 +220,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fa_kernel(
     const char* v_t = v_head + static_cast<int64_t>(kt0) * (kDV * 2);
     const char* kr_t = kr_col + static_cast<int64_t>(kt0) * row_bytes;
 #pragma unroll
-    for (int i = 0; i < S::kKnOps / kWaves; ++i) {
-      const int j = wave + kWaves * i;
+    for (int i = 0; i < S::kKnOps / W; ++i) {
+      const int j = wave + W * i;
       const int L = j * 64 + ln;
       const int row = L >> 4, p = L & 15;
       const int rr = min(row, valid - 1);
@@ -224,29 +229,37 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fa_kernel(
                       __builtin_amdgcn_readfirstlane(dst + j * 1024));
     }
 #pragma unroll
-    for (int i = 0; i < S::kKrOps / kWaves; ++i) {
-      const int j = wave + kWaves * i;
-      const int L = j * 64 + ln;
-      const int row = L / S::kKrChunks, p = L % S::kKrChunks;
-      const int rr = min(row, valid - 1);
-      global_to_lds16(kr_t, static_cast<uint32_t>(rr * row_bytes + ((p ^ kr_key<DR>(row)) << 4)),
-                      __builtin_amdgcn_readfirstlane(dst + S::kKrOff + j * 1024));
-    }
-#pragma unroll
-    for (int i = 0; i < S::kVOps / kWaves; ++i) {
-      const int j = wave + kWaves * i;
+    for (int i = 0; i < S::kVOps / W; ++i) {
+      const int j = wave + W * i;
       const int L = j * 64 + ln;
       const int row = L >> 4, p = L & 15;
       const int rr = min(row, valid - 1);
       global_to_lds16(v_t, static_cast<uint32_t>(rr * (kDV * 2) + ((p ^ v_key(row)) << 4)),
                       __builtin_amdgcn_readfirstlane(dst + S::kVOff + j * 1024));
     }
+#pragma unroll
+    for (int i = 0; i < (S::kKrOps + W - 1) / W; ++i) {
+      const int j = wave + W * i;
+      if (j < S::kKrOps) {
+        const int L = j * 64 + ln;
+        const int row = L / S::kKrChunks, p = L % S::kKrChunks;
+        const int rr = min(row, valid - 1);
+        global_to_lds16(kr_t, static_cast<uint32_t>(rr * row_bytes + ((p ^ kr_key<DR>(row)) << 4)),
+                        __builtin_amdgcn_readfirstlane(dst + S::kKrOff + j * 1024));
+      }
+    }
   };
+  const bool ops_hi = wave < S::kOps % W || S::kOps % W == 0;
   auto wait_tile = [&](int tt, int last_issued) {
-    switch (last_issued - tt) {
-      case 0: wait_tiles_after<0, S::kOpsPerWave>(); break;
-      case 1: wait_tiles_after<1, S::kOpsPerWave>(); break;
-      default: wait_tiles_after<2, S::kOpsPerWave>(); break;
+    const int d = last_issued - tt;
+    if (ops_hi) {
+      if (d == 0) wait_tiles_after<0, kOpsHi>();
+      else if (d == 1) wait_tiles_after<1, kOpsHi>();
+      else wait_tiles_after<2, kOpsHi>();
+    } else {
+      if (d == 0) wait_tiles_after<0, kOpsLo>();
+      else if (d == 1) wait_tiles_after<1, kOpsLo>();
+      else wait_tiles_after<2, kOpsLo>();
     }
   };
 
@@ -279,10 +292,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fa_kernel(
   };
 
   // Sᵀ[qb][i]: key 8(i/4) + 4hh + (i%4) of the tile, query qv[qb]
-  auto score = [&](const unsigned char* st, f32x16 (&sc)[2]) {
+  auto score = [&](const unsigned char* st, f32x16 (&sc)[kQB]) {
     const f32x16 z = {};
-    sc[0] = z;
-    sc[1] = z;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) sc[qb] = z;
     uint4 kf[2];
     kf[0] = kfrag(st, 0);
 #pragma unroll
@@ -290,18 +303,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fa_kernel(
       if (ks + 1 < S::kKS) kf[(ks + 1) & 1] = kfrag(st, ks + 1);
       if (ks < kKN) {
         const f16x8 a = __builtin_bit_cast(f16x8, kf[ks & 1]);
-        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qn[0][ks], sc[0], 0, 0, 0);
-        sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qn[1][ks], sc[1], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qn[qb][ks], sc[qb], 0, 0, 0);
       } else {
         const bf16x8 a = __builtin_bit_cast(bf16x8, kf[ks & 1]);
-        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[0][ks - kKN], sc[0], 0, 0, 0);
-        sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[1][ks - kKN], sc[1], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[qb][ks - kKN], sc[qb], 0, 0, 0);
       }
     }
   };
-  auto mask = [&](f32x16 (&sc)[2], int kt0) {
+  auto mask = [&](f32x16 (&sc)[kQB], int kt0) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kt0 + 8 * (i >> 2) + 4 * hh + (i & 3);
@@ -309,18 +324,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fa_kernel(
       }
   };
 
-  float m_ref[2] = {kNoMax, kNoMax};  // reference per query (base 2), equal in both lane halves
-  float m_lane[2], l_run[2];
+  float m_ref[kQB];  // reference per query (base 2), equal in both lane halves
+  float m_lane[kQB], l_run[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) m_ref[qb] = kNoMax;
   bool over;
-  f32x16 o[2][4];
+  f32x16 o[kQB][4];
   const f16x2 ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};  // row sum of the fp16 weights
 
   // max of the tile's scores per query; the reference is set at the query's
   // first tile with a valid key
-  auto tile_max = [&](const f32x16 (&sc)[2]) {
-    float lmax[2];
+  auto tile_max = [&](const f32x16 (&sc)[kQB]) {
+    float lmax[kQB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < kQB; ++qb) {
       const f32x16 s = sc[qb];
       float mx = s[0];
 #pragma unroll
@@ -329,17 +346,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fa_kernel(
       m_lane[qb] = fmaxf(m_lane[qb], mx);
     }
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < kQB; ++qb) {
       const float m = swap_max(lmax[qb]) * qk;
       m_ref[qb] = (m_ref[qb] == kNoMax && m != -INFINITY) ? m : m_ref[qb];
+      over = over || (lmax[qb] * qk > m_ref[qb] + kSlack);
     }
-    over = over || (lmax[0] * qk > m_ref[0] + kSlack) || (lmax[1] * qk > m_ref[1] + kSlack);
   };
   // w[qb][k]: fp16 pair (p_2k, p_2k+1) of query block qb
-  uint32_t w[2][8];
-  auto weights = [&](const f32x16 (&sc)[2]) {
+  uint32_t w[kQB][8];
+  auto weights = [&](const f32x16 (&sc)[kQB]) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < kQB; ++qb) {
       const f32x16 s = sc[qb];
       const float neg = -m_ref[qb];
       float acc = l_run[qb];
@@ -355,9 +372,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fa_kernel(
     }
   };
   auto pv = [&](const unsigned char* st) {
-    f16x8 pb[2][2];
+    f16x8 pb[kQB][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
         pb[qb][s2] = __builtin_bit_cast(
@@ -367,15 +384,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fa_kernel(
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const f16x8 a = vfrag(st, db, s2);
-        o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[0][s2], o[0][db], 0, 0, 0);
-        o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[1][s2], o[1][db], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[qb][s2], o[qb][db], 0, 0, 0);
       }
   };
 
   int* flags = reinterpret_cast<int*>(smem + S::kFlagsOff);
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < kQB; ++qb) {
       m_lane[qb] = -INFINITY;
       l_run[qb] = 0.f;
 #pragma unroll
@@ -383,20 +401,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fa_kernel(
     }
     over = false;
 
-    // ---- iteration t computes S(t + 1) beside the softmax and PV of tile t
+    auto tile_scores = [&](int t, f32x16 (&sc)[kQB]) { score(smem + (t % kStages) * S::kStageBytes, sc); };
+    // Every active wave takes every tile of the workgroup's range: tiles outside
+    // its own queries' ranges are masked out (a few tiles per workgroup).
+    // Iteration t issues the scores of tile t+1 before the softmax and PV of
+    // tile t, so the matrix core has work while the softmax runs.
 #pragma unroll
     for (int tt = 0; tt < kStages - 1; ++tt)
       if (tt < n_tiles) issue_tile(tt);
     int issued = min(kStages - 1, n_tiles) - 1;
     wait_tile(0, issued);
     lds_barrier();
-
-    f32x16 sa[2], sb[2];
-    if (wave_on) score(smem, sa);
-
-    // Every active wave takes every tile of the workgroup's range: tiles outside
-    // its own queries' ranges are masked out (a few tiles per workgroup).
-    auto iter = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    f32x16 sa[kQB], sb[kQB];
+    if (wave_on) tile_scores(0, sa);
+    auto iter = [&](int t, f32x16 (&cur)[kQB], f32x16 (&nxt)[kQB]) {
       if (t + 1 < n_tiles) wait_tile(t + 1, issued);
       lds_barrier();  // tile t+1 landed everywhere; tile t-1's buffer is free
       if (t + kStages - 1 < n_tiles) {
@@ -404,14 +422,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fa_kernel(
         issued = t + kStages - 1;
       }
       if (!wave_on) return;
-      const unsigned char* st_cur = smem + (t % kStages) * S::kStageBytes;
-      const unsigned char* st_nxt = smem + ((t + 1) % kStages) * S::kStageBytes;
       const int kt0 = k_lo + t * kBN;
       if (kt0 + kBN - 1 > qw0 || kt0 < start_last) mask(cur, kt0);
       tile_max(cur);
-      score(st_nxt, nxt);  // past the last tile this reads a stale buffer; unused
+      tile_scores(t + 1, nxt);  // past the last tile this reads a stale buffer; unused
       weights(cur);
-      pv(st_cur);
+      pv(smem + (t % kStages) * S::kStageBytes);
     };
     for (int t = 0; t < n_tiles; t += 2) {
       iter(t, sa, sb);
@@ -423,11 +439,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fa_kernel(
     lds_barrier();
     int any = 0;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) any |= flags[i];
+    for (int i = 0; i < W; ++i) any |= flags[i];
     if (any == 0) break;
     // second pass with each query's true max
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < kQB; ++qb) {
       const float m = swap_max(m_lane[qb]) * qk;
       m_ref[qb] = m == -INFINITY ? kNoMax : m;
     }
@@ -437,7 +453,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fa_kernel(
   // ---- epilogue: Oᵀ[qb][db][i] is dim 32db + 8(i/4) + 4hh + (i%4) of query qv[qb]
   if (!wave_on) return;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < kQB; ++qb) {
     if (qv[qb] >= n_tokens) continue;
     const float l = swap_sum(l_run[qb]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -454,16 +470,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fa_kernel(
   }
 }
 
-template <int DR>
+template <int DR, int W>
 void launch_fa(const AttnShape& sh, const void* q_nope, const void* q_pe, const void* k_nope,
                const void* v, const void* cache, const int64_t* cu, int batch, int n_tokens,
                void* out, hipStream_t s) {
   using S = FShape<DR>;
-  auto kern = prefill_fa_kernel<DR>;
+  auto kern = prefill_fa_kernel<DR, W>;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                       S::kLdsBytes);
   const int n_qt = (n_tokens + kBM - 1) / kBM;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(n_qt), static_cast<unsigned>(sh.H)), dim3(kThreads),
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(n_qt), static_cast<unsigned>(sh.H)), dim3(64 * W),
                      S::kLdsBytes, s, static_cast<const bf16_t*>(q_nope), static_cast<const bf16_t*>(q_pe),
                      static_cast<const _Float16*>(k_nope), static_cast<const _Float16*>(v),
                      static_cast<const bf16_t*>(cache), cu, batch, n_tokens, sh.H, sh.H / sh.G, sh.row_w,
@@ -481,7 +497,7 @@ void prefill_expanded(const AttnShape& sh, const void* q_nope, const void* q_pe,
                       const void* v, const void* cache, const int64_t* cu, int batch, int64_t n_tokens,
                       void* out, hipStream_t s) {
   if (n_tokens <= 0 || batch <= 0) return;
-  launch_fa<64>(sh, q_nope, q_pe, k_nope, v, cache, cu, batch, static_cast<int>(n_tokens), out, s);
+  launch_fa<64, MLA_PREFILL_FA_WAVES>(sh, q_nope, q_pe, k_nope, v, cache, cu, batch, static_cast<int>(n_tokens), out, s);
 }
 
 }  // namespace mla
