@@ -70,6 +70,11 @@ def quantize(a: np.ndarray, dtype: str) -> np.ndarray:
 
 # tensor ids for the seed sequence
 T_X, T_WDKV, T_WKR, T_WQC, T_WQR, T_WUK, T_WUV, T_LEN, T_SAMPLE = range(9)
+T_WQA, T_QGAIN, T_WQB, T_WO = range(9, 13)
+
+# Query down-projection width of the low-rank query path: DeepSeek-V2 factors its
+# 5120 -> 24576 query map through 1536 dims (MLA principle page, section 'steps').
+Q_LORA_RANK = 1536
 
 X_BLOCK = 1024  # x is drawn in independent blocks of this many tokens per sequence
 
@@ -191,6 +196,26 @@ def weights(cfg: MLAConfig) -> Dict[str, np.ndarray]:
         fan_in = cfg.rank if k in ("w_uk", "w_uv") else cfg.d_model
         out[k] = draw_normal(cfg.seed, ids[k], (0,), shp, 1.0 / math.sqrt(fan_in), cfg.dtype)
     return out
+
+
+def lowrank_query_weights(cfg: MLAConfig, q_rank: int = Q_LORA_RANK) -> Dict[str, np.ndarray]:
+    """The low-rank query path's weights: W_QA [q_rank, d_model] ~ N(0, 1/d_model),
+    the RMSNorm gain [q_rank] ~ 1 + N(0, 0.1^2), and W_QB [H·(d_nope + d_rope), q_rank]
+    ~ N(0, 1/q_rank), its rows head-major with each head's d_nope rows first."""
+    H = cfg.n_heads
+    gain = draw_normal(cfg.seed, T_QGAIN, (0,), (q_rank,), 0.1, "f32") + np.float32(1.0)
+    return {
+        "w_qa": draw_normal(cfg.seed, T_WQA, (0,), (q_rank, cfg.d_model), 1.0 / math.sqrt(cfg.d_model), cfg.dtype),
+        "q_gain": quantize(gain, cfg.dtype),
+        "w_qb": draw_normal(cfg.seed, T_WQB, (0,), (H * (cfg.d_nope + cfg.d_rope), q_rank),
+                            1.0 / math.sqrt(q_rank), cfg.dtype),
+    }
+
+
+def output_weight(cfg: MLAConfig) -> np.ndarray:
+    """W_o [d_model, H·d_v] ~ N(0, 1/(H·d_v)): the output projection after W_UV."""
+    k = cfg.n_heads * cfg.d_v
+    return draw_normal(cfg.seed, T_WO, (0,), (cfg.d_model, k), 1.0 / math.sqrt(k), cfg.dtype)
 
 
 def x_rows(cfg: MLAConfig, seq: int, start: int, stop: int, scale: float = 1.0,

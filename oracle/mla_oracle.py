@@ -34,6 +34,9 @@ named by their title / subject; equation numbers are the pages' own.
   KV projection).
 * Page "MLA 在 nanowhale-100m 中的实现原理", §"高效注意力计算实现": causal
   scaled-dot-product attention with an explicit scale (SDPA with is_causal).
+* Beyond the attention itself (``lowrank_query``, ``output_projection``): the
+  MLA principle page's low-rank query q_b_proj(q_a_layernorm(q_a_proj(x))) of its
+  §"步骤", and its output projection o_proj, eqs. (3)/(6).
 
 Readings taken where the pages are silent (each is listed in the design doc):
 rotate-half RoPE pairing (j, j + d_r/2) with θ_j = θ^(-2j/d_r) and the angle
@@ -149,6 +152,21 @@ def absorbed_query(qn, w_uk) -> np.ndarray:
     return np.einsum("hdc,thd->thc", _f64(w_uk), _f64(qn))
 
 
+def lowrank_query(x, w_qa, q_gain, w_qb, pos, *, n_heads, d_nope, d_rope, theta, eps):
+    """The low-rank query path, page "MLA 原理" §"步骤" (the report's eqs. (37)-(40)):
+    q = q_b_proj(q_a_layernorm(q_a_proj(x))), viewed as [H, d_nope + d_rope] per
+    token and split into q_nope (first d_nope) and q_pe (last d_rope); q_pe is then
+    rotated like the full-rank q_pe.  Same structure on the nanowhale page
+    (wq_a, q_norm = RMSNorm over the q rank, wq_b).
+    W_QA [q_rank, d_model]; q_gain [q_rank] (None: unit gain); W_QB [H·(d_nope+d_rope), q_rank].
+    Returns (qn [T, H, d_nope], qr [T, H, d_rope])."""
+    cq = rmsnorm(_f64(x) @ _f64(w_qa).T, eps)
+    if q_gain is not None:
+        cq = cq * _f64(q_gain)
+    q = (cq @ _f64(w_qb).T).reshape(-1, n_heads, d_nope + d_rope)
+    return q[..., :d_nope], rope(q[..., d_nope:], pos, theta)
+
+
 # ----------------------------------------------------------------------------
 # non-absorbed attention
 # ----------------------------------------------------------------------------
@@ -231,6 +249,14 @@ def mla_layer(x_keys, x_queries, w, *, k_pos, q_pos, k_seg, q_seg, n_heads, n_gr
                    d_rope=d_rope, theta=theta)
     return mla_attention(qn, qr, c, kr, w["w_uk"], w["w_uv"], q_pos, k_pos, q_seg, k_seg,
                          scale, head_chunk=head_chunk)
+
+
+def output_projection(o, w_o) -> np.ndarray:
+    """u[t,:] = Σ_h Σ_e o[t,h,e]·W_o[:, h·d_v + e]: page "MLA 原理", eqs. (3)/(6)
+    (einsum 'hdD,bhqd->bqD' of W_o with the per-head outputs), after W_UV.
+    o [T, H, d_v]; W_o stored [d_model, H·d_v] (o_proj, [H·d_v -> hidden])."""
+    o = _f64(o)
+    return o.reshape(o.shape[0], -1) @ _f64(w_o).T
 
 
 def max_rel_err(got, ref) -> float:

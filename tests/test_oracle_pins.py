@@ -416,6 +416,8 @@ def test_p7_page_facts_and_workload_shapes():
     assert c3.n_heads * (c3.d_nope + c3.d_rope) == f("deepseek_v2_q_b_proj_out")
     assert c3.n_heads * c3.d_v == f("deepseek_v2_o_proj_in")
     assert c3.d_model == f("deepseek_v2_hidden")
+    from mla_inputs import Q_LORA_RANK
+    assert Q_LORA_RANK == f("deepseek_v2_q_down_rank")  # the low-rank query's middle width
     # Qwen3-30B-A3B delta: rank 512, 8 rotary dims per KV head
     c4 = CONFIGS["qwen3_30b_ragged_decode"]
     assert c4.rank == f("qwen3_30b_latent_rank") and c4.d_rope == f("qwen3_30b_rope_dims_per_kv_head")
@@ -424,3 +426,114 @@ def test_p7_page_facts_and_workload_shapes():
     assert (c5.rank, c5.d_model, c5.n_heads) == (f("zebra_kv_lora_rank"), f("zebra_hidden"), f("zebra_heads"))
     nw = f("nanowhale_head_dim_split")
     assert nw["head_dim"] == nw["qk_rope_head_dim"] + nw["nope_head_dim"]
+
+
+# ----------------------------------------------------------------------------
+# P8: low-rank query path and output projection (beyond the attention)
+# ----------------------------------------------------------------------------
+
+
+def _lowrank_layer(rng, d_model, q_rank, H, d_nope, d_r, gain=True):
+    return {
+        "w_qa": rng.standard_normal((q_rank, d_model)) / math.sqrt(d_model),
+        "q_gain": 1.0 + 0.1 * rng.standard_normal(q_rank) if gain else None,
+        "w_qb": rng.standard_normal((H * (d_nope + d_r), q_rank)) / math.sqrt(q_rank),
+    }
+
+
+def test_p8_lowrank_query_brute_force():
+    """Scalar loops: down-projection, RMSNorm with gain, up-projection, per-head
+    split [q_nope ; q_pe] (no-position part first), then the rotation of q_pe
+    (d_r = 2: the single pair turns by p radians)."""
+    rng = np.random.default_rng(80)
+    d_model, q_rank, H, d_nope, d_r, eps = 6, 4, 2, 3, 2, 1e-6
+    w = _lowrank_layer(rng, d_model, q_rank, H, d_nope, d_r)
+    x = rng.standard_normal((3, d_model))
+    pos = np.array([0, 1, 5])
+    qn, qr = O.lowrank_query(x, w["w_qa"], w["q_gain"], w["w_qb"], pos, n_heads=H, d_nope=d_nope,
+                             d_rope=d_r, theta=10000.0, eps=eps)
+    for t in range(3):
+        cq = [sum(x[t][k] * w["w_qa"][i][k] for k in range(d_model)) for i in range(q_rank)]
+        ms = sum(v * v for v in cq) / q_rank
+        cqn = [cq[i] / math.sqrt(ms + eps) * w["q_gain"][i] for i in range(q_rank)]
+        q = [sum(cqn[i] * w["w_qb"][j][i] for i in range(q_rank)) for j in range(H * (d_nope + d_r))]
+        for h in range(H):
+            base = h * (d_nope + d_r)
+            for d in range(d_nope):
+                assert abs(qn[t, h, d] - q[base + d]) < 1e-12
+            y0, y1 = q[base + d_nope], q[base + d_nope + 1]
+            a = float(pos[t])
+            assert abs(qr[t, h, 0] - (y0 * math.cos(a) - y1 * math.sin(a))) < 1e-12
+            assert abs(qr[t, h, 1] - (y1 * math.cos(a) + y0 * math.sin(a))) < 1e-12
+
+
+def test_p8_lowrank_query_library_and_invariants():
+    """torch's float64 rms_norm with weight, then the linear maps; RMSNorm makes the
+    query invariant to the scale of x (eps = 0); with q_rank = d_model, W_QA = I,
+    unit gain and eps = 0 the path is the full-rank query of rmsnorm(x) whose
+    W_QC / W_QR are W_QB's per-head no-position / rotary rows."""
+    rng = np.random.default_rng(81)
+    d_model, q_rank, H, d_nope, d_r = 12, 8, 3, 4, 4
+    w = _lowrank_layer(rng, d_model, q_rank, H, d_nope, d_r)
+    x = rng.standard_normal((5, d_model))
+    pos = np.zeros(5, int)
+    qn, qr = O.lowrank_query(x, w["w_qa"], w["q_gain"], w["w_qb"], pos, n_heads=H, d_nope=d_nope,
+                             d_rope=d_r, theta=10000.0, eps=1e-6)
+    tx = torch.from_numpy(x)
+    cq = torch.nn.functional.rms_norm(tx @ torch.from_numpy(w["w_qa"]).T, (q_rank,),
+                                      weight=torch.from_numpy(w["q_gain"]), eps=1e-6)
+    q = (cq @ torch.from_numpy(w["w_qb"]).T).view(5, H, d_nope + d_r).numpy()
+    np.testing.assert_allclose(qn, q[..., :d_nope], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(qr, q[..., d_nope:], rtol=1e-12, atol=1e-14)   # p = 0: no rotation
+    pos = np.array([0, 3, 17, 100, 4095])
+    a = O.lowrank_query(x, w["w_qa"], w["q_gain"], w["w_qb"], pos, n_heads=H, d_nope=d_nope, d_rope=d_r,
+                        theta=10000.0, eps=0.0)
+    b = O.lowrank_query(7.3 * x, w["w_qa"], w["q_gain"], w["w_qb"], pos, n_heads=H, d_nope=d_nope,
+                        d_rope=d_r, theta=10000.0, eps=0.0)
+    np.testing.assert_allclose(a[0], b[0], rtol=1e-12)
+    np.testing.assert_allclose(a[1], b[1], rtol=1e-12)
+    # reduction to the full-rank query
+    wf = _lowrank_layer(rng, d_model, d_model, H, d_nope, d_r, gain=False)
+    wf["w_qa"] = np.eye(d_model)
+    qn_l, qr_l = O.lowrank_query(x, wf["w_qa"], None, wf["w_qb"], pos, n_heads=H, d_nope=d_nope,
+                                 d_rope=d_r, theta=10000.0, eps=0.0)
+    rows = wf["w_qb"].reshape(H, d_nope + d_r, d_model)
+    w_qc = rows[:, :d_nope].reshape(H * d_nope, d_model)
+    w_qr = rows[:, d_nope:].reshape(H * d_r, d_model)
+    qn_f, qr_f = O.query(O.rmsnorm(x, 0.0), w_qc, w_qr, pos, n_heads=H, d_nope=d_nope, d_rope=d_r,
+                         theta=10000.0)
+    np.testing.assert_allclose(qn_l, qn_f, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(qr_l, qr_f, rtol=1e-12, atol=1e-14)
+
+
+def test_p8_output_projection_brute_and_page_chain():
+    """Scalar loops of u[D] = Σ_h Σ_e o[h,e]·W_o[D, h·d_v + e]; and the page's combined
+    form of eqs. (1)-(3), einsum('hdc,blc,bqhl,hdD->bhD', W_UV, c, P, W_o), with P the
+    softmax of explicit scores, equals output_projection(mla_attention(...))."""
+    rng = np.random.default_rng(82)
+    T, H, d_v, D = 3, 2, 3, 5
+    o = rng.standard_normal((T, H, d_v))
+    w_o = rng.standard_normal((D, H * d_v))
+    u = O.output_projection(o, w_o)
+    for t in range(T):
+        for dd in range(D):
+            ref = sum(o[t][h][e] * w_o[dd][h * d_v + e] for h in range(H) for e in range(d_v))
+            assert abs(u[t, dd] - ref) < 1e-12
+    # combined page form for the last query of one causal sequence
+    d_model, r, d_r, d_nope, G, L = 10, 6, 4, 3, 1, 7
+    w = _rand_layer(rng, d_model, H, G, r, d_r, d_nope, d_v)
+    x = rng.standard_normal((L, d_model))
+    seg, pos = _ragged([L])
+    scale = 1.0 / math.sqrt(d_nope + d_r)
+    o_all = _run(x, w, seg, pos, H=H, G=G, d_nope=d_nope, d_r=d_r, theta=10000.0, scale=scale)
+    u_or = O.output_projection(o_all, w_o)[-1]
+    c = x @ w["w_dkv"].T
+    kn = np.einsum("hdc,lc->lhd", w["w_uk"], c)
+    kr = O.rope((x @ w["w_kr"].T).reshape(L, G, d_r), pos, 10000.0)
+    qn = (x[-1] @ w["w_qc"].T).reshape(H, d_nope)
+    qr = O.rope((x[-1] @ w["w_qr"].T).reshape(1, H, d_r), pos[-1:], 10000.0)[0]
+    s = scale * (np.einsum("hd,lhd->hl", qn, kn) + np.einsum("hd,ld->hl", qr, kr[:, 0]))
+    P = np.exp(s - s.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    u_page = np.einsum("hdc,lc,hl,hdD->D", w["w_uv"], c, P, w_o.T.reshape(H, d_v, D))
+    np.testing.assert_allclose(u_or, u_page, rtol=1e-11, atol=1e-12)
