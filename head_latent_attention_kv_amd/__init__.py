@@ -11,14 +11,17 @@ its calls:
     mla_decode_partials — the decode attention's per-split softmax partials
     mla_query        — q_nope = x·W_QCᵀ, q_pe = RoPE(x·W_QRᵀ) (no absorption)
     mla_prefill_expanded — causal prefill in the original order (k_nope, v expanded)
+    mla_absorb_lowrank / mla_query_lowrank — the low-rank query path (W_QA, RMSNorm, W_QB)
+    mla_output       — the output projection W_o after W_UV
 
 Build the library with ``python -m head_latent_attention_kv_amd.build``.
 """
 from ._abi import (  # noqa: F401
     MLA_BF16, MLA_EHIP, MLA_EINVAL, MLA_ENOTSUP, MLA_EWORKSPACE, MLA_F32, MLA_OK, MLA_OP_ABSORB,
-    MLA_OP_DECODE, MLA_OP_PREFILL, MLA_OP_PREFILL_EXPANDED, MLA_OP_QUERY, MLA_OP_WRITE_CACHE, MlaDims,
-    MlaError, dims_of, load, make_dims, mla_absorb, mla_decode, mla_decode_partials, mla_decode_split_rows,
-    mla_decode_splits, mla_prefill, mla_prefill_expanded, mla_query, mla_workspace_size, mla_write_cache,
+    MLA_OP_DECODE, MLA_OP_OUTPUT, MLA_OP_PREFILL, MLA_OP_PREFILL_EXPANDED, MLA_OP_QUERY, MLA_OP_WRITE_CACHE,
+    MlaDims, MlaError, dims_of, load, make_dims, mla_absorb, mla_absorb_lowrank, mla_decode,
+    mla_decode_partials, mla_decode_split_rows, mla_decode_splits, mla_lowrank_workspace_size, mla_output,
+    mla_prefill, mla_prefill_expanded, mla_query, mla_query_lowrank, mla_workspace_size, mla_write_cache,
     strerror,
 )
 
@@ -26,4 +29,5 @@ __all__ = [
     "MlaDims", "MlaError", "dims_of", "load", "make_dims", "mla_absorb", "mla_decode",
     "mla_decode_partials", "mla_decode_split_rows", "mla_decode_splits", "mla_prefill",
     "mla_prefill_expanded", "mla_query", "mla_workspace_size", "mla_write_cache", "strerror",
+    "mla_absorb_lowrank", "mla_query_lowrank", "mla_lowrank_workspace_size", "mla_output",
 ]

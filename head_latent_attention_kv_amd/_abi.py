@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(PKG, "libmla_amd.so")
 MLA_OK, MLA_EINVAL, MLA_ENOTSUP, MLA_EWORKSPACE, MLA_EHIP = 0, -1, -2, -3, -4
 MLA_F32, MLA_BF16 = 0, 1
 MLA_OP_WRITE_CACHE, MLA_OP_ABSORB, MLA_OP_DECODE, MLA_OP_PREFILL = 0, 1, 2, 3
-MLA_OP_QUERY, MLA_OP_PREFILL_EXPANDED = 4, 5
+MLA_OP_QUERY, MLA_OP_PREFILL_EXPANDED, MLA_OP_OUTPUT = 4, 5, 6
 
 # Functions declared in include/mla.h, with their ctypes signatures.
 _vp, _sz, _i32, _i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
@@ -43,6 +43,11 @@ SIGNATURES = {
     "mla_query": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "mla_prefill_expanded": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _vp, _vp, _vp, _vp,
                                             _sz, _vp]),
+    "mla_lowrank_workspace_size": (_sz, [_PD, _i32, _i64]),
+    "mla_absorb_lowrank": (ctypes.c_int, [_PD, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz,
+                                          _vp]),
+    "mla_query_lowrank": (ctypes.c_int, [_PD, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "mla_output": (ctypes.c_int, [_PD, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "mla_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_version": (ctypes.c_int, []),
 }
@@ -246,6 +251,56 @@ def mla_prefill_expanded(dims, q_nope, q_pe, cache, cu_seqlens, max_len, w_uk, w
         ctypes.byref(dims), _ptr(q_nope, "q_nope", et), _ptr(q_pe, "q_pe", et), _ptr(cache, "cache", et),
         _ptr(cu_seqlens, "cu_seqlens", torch.int64), B, T, int(max_len), _ptr(w_uk, "w_uk", et),
         _ptr(w_uv, "w_uv", et), _ptr(out, "out", et), _ptr(ws, "workspace"), nbytes, _stream(stream)))
+    return out
+
+
+def mla_lowrank_workspace_size(dims, q_rank: int, n_tokens: int) -> int:
+    return int(load().mla_lowrank_workspace_size(ctypes.byref(dims), int(q_rank), int(n_tokens)))
+
+
+def _lowrank_ws(dims, q_rank, T, workspace, device):
+    if workspace is None:
+        torch = _torch()
+        need = mla_lowrank_workspace_size(dims, q_rank, T)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def mla_absorb_lowrank(dims, q_rank, x, w_qa, q_gain, w_qb, w_uk, positions, q_lat, q_pe, workspace=None,
+                       stream=None):
+    torch = _torch()
+    et = _elem_dtype(dims)
+    T = x.shape[0]
+    ws, nbytes = _lowrank_ws(dims, q_rank, T, workspace, x.device)
+    gain = None if q_gain is None else _ptr(q_gain, "q_gain", et)
+    _check("mla_absorb_lowrank", load().mla_absorb_lowrank(
+        ctypes.byref(dims), int(q_rank), _ptr(x, "x", et), _ptr(w_qa, "w_qa", et), gain, _ptr(w_qb, "w_qb", et),
+        _ptr(w_uk, "w_uk", et), _ptr(positions, "positions", torch.int32), T, _ptr(q_lat, "q_lat", et),
+        _ptr(q_pe, "q_pe", et), _ptr(ws, "workspace"), nbytes, _stream(stream)))
+    return q_lat, q_pe
+
+
+def mla_query_lowrank(dims, q_rank, x, w_qa, q_gain, w_qb, positions, q_nope, q_pe, workspace=None,
+                      stream=None):
+    torch = _torch()
+    et = _elem_dtype(dims)
+    T = x.shape[0]
+    ws, nbytes = _lowrank_ws(dims, q_rank, T, workspace, x.device)
+    gain = None if q_gain is None else _ptr(q_gain, "q_gain", et)
+    _check("mla_query_lowrank", load().mla_query_lowrank(
+        ctypes.byref(dims), int(q_rank), _ptr(x, "x", et), _ptr(w_qa, "w_qa", et), gain, _ptr(w_qb, "w_qb", et),
+        _ptr(positions, "positions", torch.int32), T, _ptr(q_nope, "q_nope", et), _ptr(q_pe, "q_pe", et),
+        _ptr(ws, "workspace"), nbytes, _stream(stream)))
+    return q_nope, q_pe
+
+
+def mla_output(dims, attn, w_o, out, workspace=None, stream=None):
+    et = _elem_dtype(dims)
+    T = attn.shape[0]
+    ws, nbytes = _workspace(dims, MLA_OP_OUTPUT, 0, T, 0, workspace, attn.device)
+    _check("mla_output", load().mla_output(
+        ctypes.byref(dims), _ptr(attn, "attn", et), _ptr(w_o, "w_o", et), T, _ptr(out, "out", et),
+        _ptr(ws, "workspace"), nbytes, _stream(stream)))
     return out
 
 

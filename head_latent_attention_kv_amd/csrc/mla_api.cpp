@@ -129,18 +129,26 @@ struct Proj {
   int64_t sps;
 };
 
-Proj proj_plan(const mla_dims* d, int n, int64_t n_tokens, int64_t ldc) {
+Proj proj_plan_k(const mla_dims* d, int n, int k, int64_t n_tokens, int64_t ldc) {
   Proj p{1, 0};
   if (skinny_ok(d, n_tokens)) {
-    p.splits = mla::skinny_splits(static_cast<int>(n_tokens), n, 1, d->d_model);
+    p.splits = mla::skinny_splits(static_cast<int>(n_tokens), n, 1, k);
     p.sps = static_cast<int64_t>(align_up(static_cast<size_t>(n_tokens) * ldc * sizeof(float)) / sizeof(float));
   }
   return p;
 }
 
-size_t proj_bytes(const mla_dims* d, int n, int64_t n_tokens, int64_t ldc) {
-  const Proj p = proj_plan(d, n, n_tokens, ldc);
+Proj proj_plan(const mla_dims* d, int n, int64_t n_tokens, int64_t ldc) {
+  return proj_plan_k(d, n, d->d_model, n_tokens, ldc);
+}
+
+size_t proj_bytes_k(const mla_dims* d, int n, int k, int64_t n_tokens, int64_t ldc) {
+  const Proj p = proj_plan_k(d, n, k, n_tokens, ldc);
   return static_cast<size_t>(p.splits) * align_up(static_cast<size_t>(n_tokens) * ldc * sizeof(float));
+}
+
+size_t proj_bytes(const mla_dims* d, int n, int64_t n_tokens, int64_t ldc) {
+  return proj_bytes_k(d, n, d->d_model, n_tokens, ldc);
 }
 
 GemmArgs proj_args(const mla_dims* d, const void* x, const void* w, int n, float* c, int64_t ldc,
@@ -157,6 +165,44 @@ GemmArgs proj_args(const mla_dims* d, const void* x, const void* w, int n, float
   g.K = d->d_model;
   g.Z = 1;
   return g;
+}
+
+// C (fp32, row stride ldc) = A [T, k] (row stride lda, layer dtype) · Wᵀ, W [n, k].
+// Few bf16 tokens: the weight-streaming kernel, leaving `splits` K slices.
+Proj proj_one(const mla_dims* d, const void* a, int64_t lda, int k, const void* w, int n, float* c,
+              int64_t ldc, int64_t n_tokens, hipStream_t s) {
+  const Proj p = proj_plan_k(d, n, k, n_tokens, ldc);
+  if (skinny_ok(d, n_tokens)) {
+    mla::SkinnyArgs sa{};
+    sa.A = a;
+    sa.sAm = lda;
+    sa.B0 = sa.B1 = static_cast<const uint16_t*>(w);
+    sa.N0 = n;
+    sa.sBo = k;
+    sa.C = c;
+    sa.sCm = ldc;
+    sa.sPs = p.sps;
+    sa.M = static_cast<int>(n_tokens);
+    sa.N = n;
+    sa.K = k;
+    sa.Z = 1;
+    sa.splits = p.splits;
+    mla::gemm_skinny(sa, /*a_f32=*/false, /*out_bf16=*/false, s);
+  } else {
+    GemmArgs g{};
+    g.A = a;
+    g.sAm = lda;
+    g.B = w;
+    g.sBo = k;
+    g.C = c;
+    g.sCm = ldc;
+    g.M = static_cast<int>(n_tokens);
+    g.N = n;
+    g.K = k;
+    g.Z = 1;
+    mla::gemm(g, d->dtype, false, false, false, s);
+  }
+  return p;
 }
 
 Proj proj_two(const mla_dims* d, const void* x, const void* w0, int n0, const void* w1, int n1,
@@ -215,6 +261,29 @@ size_t expanded_k_bytes(const mla_dims* d, int64_t n_tokens) {
 size_t expanded_ws(const mla_dims* d, int64_t n_tokens) {
   return expanded_k_bytes(d, n_tokens) +
          align_up(static_cast<size_t>(std::max<int64_t>(n_tokens, 0)) * d->n_heads * d->d_v * 2);
+}
+
+// Low-rank query path: [x·W_QAᵀ fp32 slices][normalised rows, layer dtype][q fp32 slices]
+int64_t lowrank_ld(int32_t q_rank) { return (static_cast<int64_t>(q_rank) + 7) / 8 * 8; }
+struct LowrankWs {
+  size_t cq, cqn, q;
+  size_t total() const { return cq + cqn + q; }
+};
+LowrankWs lowrank_ws(const mla_dims* d, int32_t q_rank, int64_t n_tokens) {
+  const int64_t T = std::max<int64_t>(n_tokens, 0);
+  LowrankWs w{};
+  w.cq = proj_bytes_k(d, q_rank, d->d_model, T, lowrank_ld(q_rank));
+  w.cqn = align_up(static_cast<size_t>(T) * q_rank * (d->dtype == MLA_F32 ? 4 : 2));
+  w.q = proj_bytes_k(d, q_cols(d), q_rank, T, q_width(d));
+  return w;
+}
+
+// Output projection: fp32 slices of the few-token weight-streaming product
+int64_t out_width(const mla_dims* d) { return (static_cast<int64_t>(d->d_model) + 7) / 8 * 8; }
+size_t output_ws(const mla_dims* d, int64_t n_tokens) {
+  const int64_t T = std::max<int64_t>(n_tokens, 0);
+  if (!skinny_ok(d, T)) return 0;
+  return proj_bytes_k(d, d->d_model, d->n_heads * d->d_v, T, out_width(d));
 }
 
 int launch_status() {
@@ -291,6 +360,7 @@ size_t mla_workspace_size(const mla_dims* dims, int op, int32_t batch, int64_t n
     case MLA_OP_PREFILL: return prefill_ws(dims, n_tokens);
     case MLA_OP_QUERY: return absorb_ws(dims, n_tokens);
     case MLA_OP_PREFILL_EXPANDED: return expanded_ws(dims, n_tokens);
+    case MLA_OP_OUTPUT: return output_ws(dims, n_tokens);
     default: return 0;
   }
 }
@@ -337,8 +407,8 @@ int mla_absorb(const mla_dims* dims, const void* x, const void* w_qc, const void
   float* q = static_cast<float*>(workspace);
   const Proj p = proj_two(dims, x, w_qc, H * dims->d_nope, w_qr, H * dims->d_rope, q, ld, n_tokens, s);
   mla::sum_split_slices(q, p.splits, p.sps, static_cast<int>(n_tokens), q_cols(dims), ld, s);
-  mla::finalize_query_rope(dims->dtype, q + static_cast<int64_t>(H) * dims->d_nope, ld, q_pe, positions,
-                           n_tokens, H, dims->d_rope, dims->rope_theta, s);
+  mla::finalize_query_rope(dims->dtype, q + static_cast<int64_t>(H) * dims->d_nope, ld, dims->d_rope, q_pe,
+                           positions, n_tokens, H, dims->d_rope, dims->rope_theta, s);
   // q_lat[t,h,:] = Σ_d q_nope[t,h,d] W_UK[h,d,:]   (batched over heads)
   GemmArgs a{};
   a.A = q;
@@ -501,10 +571,9 @@ int mla_query(const mla_dims* dims, const void* x, const void* w_qc, const void*
   float* q = static_cast<float*>(workspace);
   const Proj p = proj_two(dims, x, w_qc, H * dims->d_nope, w_qr, H * dims->d_rope, q, ld, n_tokens, s);
   mla::sum_split_slices(q, p.splits, p.sps, static_cast<int>(n_tokens), q_cols(dims), ld, s);
-  mla::finalize_query_rope(dims->dtype, q + static_cast<int64_t>(H) * dims->d_nope, ld, q_pe, positions,
-                           n_tokens, H, dims->d_rope, dims->rope_theta, s);
-  mla::cast_rows(dims->dtype, q, ld, H * dims->d_nope, q_nope, static_cast<int64_t>(H) * dims->d_nope,
-                 n_tokens, s);
+  mla::finalize_query_rope(dims->dtype, q + static_cast<int64_t>(H) * dims->d_nope, ld, dims->d_rope, q_pe,
+                           positions, n_tokens, H, dims->d_rope, dims->rope_theta, s);
+  mla::cast_heads(dims->dtype, q, ld, dims->d_nope, H, dims->d_nope, q_nope, n_tokens, s);
   return launch_status();
 }
 
@@ -554,6 +623,143 @@ int mla_prefill_expanded(const mla_dims* dims, const void* q_nope, const void* q
   expand(w_uk, dims->d_nope, k_nope);
   expand(w_uv, dims->d_v, v);
   mla::prefill_expanded(sh, q_nope, q_pe, k_nope, v, cache, cu_seqlens, batch, n_tokens, out, s);
+  return launch_status();
+}
+
+size_t mla_lowrank_workspace_size(const mla_dims* dims, int32_t q_rank, int64_t n_tokens) {
+  if (check_dims(dims) != MLA_OK || q_rank <= 0) return 0;
+  return lowrank_ws(dims, q_rank, n_tokens).total();
+}
+
+namespace {
+
+// Shared front of the low-rank query calls: q = RMSNorm(x·W_QAᵀ)·gain · W_QBᵀ into
+// the fp32 rows of the workspace ([H, d_nope + d_rope] per token), q_pe rotated.
+// Returns the fp32 rows (row stride q_width) or nullptr after an argument error in *st.
+float* lowrank_front(const mla_dims* dims, int32_t q_rank, const void* x, const void* w_qa,
+                     const void* q_gain, const void* w_qb, const int32_t* positions, int64_t n_tokens,
+                     void* q_pe, void* workspace, size_t workspace_bytes, hipStream_t s, int* st) {
+  *st = check_dims(dims);
+  if (*st != MLA_OK) return nullptr;
+  if (q_rank <= 0 || n_tokens < 0) {
+    *st = MLA_EINVAL;
+    return nullptr;
+  }
+  if (q_rank % 8 != 0 || !mla::norm_rows_supported(q_rank) || n_tokens > INT32_MAX) {
+    *st = MLA_ENOTSUP;
+    return nullptr;
+  }
+  if (n_tokens == 0) return nullptr;
+  if (!ptr_ok(x) || !ptr_ok(w_qa) || (q_gain != nullptr && !ptr_ok(q_gain)) || !ptr_ok(w_qb) ||
+      !ptr_ok(positions) || !ptr_ok(q_pe) || !ptr_ok(workspace)) {
+    *st = MLA_EINVAL;
+    return nullptr;
+  }
+  const LowrankWs w = lowrank_ws(dims, q_rank, n_tokens);
+  if (workspace_bytes < w.total()) {
+    *st = MLA_EWORKSPACE;
+    return nullptr;
+  }
+  char* base = static_cast<char*>(workspace);
+  float* cq = reinterpret_cast<float*>(base);
+  void* cqn = base + w.cq;
+  float* q = reinterpret_cast<float*>(base + w.cq + w.cqn);
+  const int64_t ldq = lowrank_ld(q_rank);
+  const Proj p1 = proj_one(dims, x, dims->d_model, dims->d_model, w_qa, q_rank, cq, ldq, n_tokens, s);
+  mla::norm_rows(dims->dtype, cq, ldq, p1.splits, p1.sps, q_rank, q_gain, dims->rms_eps, cqn, q_rank,
+                 n_tokens, s);
+  const int64_t ld = q_width(dims);
+  const Proj p2 = proj_one(dims, cqn, q_rank, q_rank, w_qb, q_cols(dims), q, ld, n_tokens, s);
+  mla::sum_split_slices(q, p2.splits, p2.sps, static_cast<int>(n_tokens), q_cols(dims), ld, s);
+  const int hw = dims->d_nope + dims->d_rope;
+  mla::finalize_query_rope(dims->dtype, q + dims->d_nope, ld, hw, q_pe, positions, n_tokens, dims->n_heads,
+                           dims->d_rope, dims->rope_theta, s);
+  return q;
+}
+
+}  // namespace
+
+int mla_absorb_lowrank(const mla_dims* dims, int32_t q_rank, const void* x, const void* w_qa,
+                       const void* q_gain, const void* w_qb, const void* w_uk, const int32_t* positions,
+                       int64_t n_tokens, void* q_lat, void* q_pe, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  const int st0 = check_dims(dims);
+  if (st0 != MLA_OK) return st0;
+  if (n_tokens > 0 && (!ptr_ok(w_uk) || !ptr_ok(q_lat))) return MLA_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int st = MLA_OK;
+  float* q = lowrank_front(dims, q_rank, x, w_qa, q_gain, w_qb, positions, n_tokens, q_pe, workspace,
+                           workspace_bytes, s, &st);
+  if (q == nullptr) return st;
+  const int H = dims->n_heads;
+  GemmArgs a{};
+  a.A = q;
+  a.sAz = dims->d_nope + dims->d_rope;
+  a.sAm = q_width(dims);
+  a.B = w_uk;
+  a.sBz = static_cast<int64_t>(dims->d_nope) * dims->rank;
+  a.sBo = dims->rank;
+  a.C = q_lat;
+  a.sCz = dims->rank;
+  a.sCm = static_cast<int64_t>(H) * dims->rank;
+  a.M = static_cast<int>(n_tokens);
+  a.N = dims->rank;
+  a.K = dims->d_nope;
+  a.Z = H;
+  mla::gemm(a, dims->dtype, /*a_f32=*/true, /*b_kn=*/true, dims->dtype == MLA_BF16, s);
+  return launch_status();
+}
+
+int mla_query_lowrank(const mla_dims* dims, int32_t q_rank, const void* x, const void* w_qa,
+                      const void* q_gain, const void* w_qb, const int32_t* positions, int64_t n_tokens,
+                      void* q_nope, void* q_pe, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st0 = check_dims(dims);
+  if (st0 != MLA_OK) return st0;
+  if (n_tokens > 0 && !ptr_ok(q_nope)) return MLA_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int st = MLA_OK;
+  float* q = lowrank_front(dims, q_rank, x, w_qa, q_gain, w_qb, positions, n_tokens, q_pe, workspace,
+                           workspace_bytes, s, &st);
+  if (q == nullptr) return st;
+  mla::cast_heads(dims->dtype, q, q_width(dims), dims->d_nope + dims->d_rope, dims->n_heads, dims->d_nope,
+                  q_nope, n_tokens, s);
+  return launch_status();
+}
+
+int mla_output(const mla_dims* dims, const void* attn, const void* w_o, int64_t n_tokens, void* out,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_tokens < 0) return MLA_EINVAL;
+  if (n_tokens == 0) return MLA_OK;
+  if (n_tokens > INT32_MAX) return MLA_ENOTSUP;
+  const int K = dims->n_heads * dims->d_v;
+  if (dims->dtype == MLA_BF16 && K % 8 != 0) return MLA_ENOTSUP;
+  const size_t need = output_ws(dims, n_tokens);
+  if (!ptr_ok(attn) || !ptr_ok(w_o) || !ptr_ok(out) || (need > 0 && !ptr_ok(workspace))) return MLA_EINVAL;
+  if (workspace_bytes < need) return MLA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (need > 0) {
+    // few tokens: stream W_o once, K slices in fp32, then sum and cast
+    float* c = static_cast<float*>(workspace);
+    const int64_t ld = out_width(dims);
+    const Proj p = proj_one(dims, attn, K, K, w_o, dims->d_model, c, ld, n_tokens, s);
+    mla::sum_split_slices(c, p.splits, p.sps, static_cast<int>(n_tokens), dims->d_model, ld, s);
+    mla::cast_heads(dims->dtype, c, ld, 0, 1, dims->d_model, out, n_tokens, s);
+  } else {
+    GemmArgs g{};
+    g.A = attn;
+    g.sAm = K;
+    g.B = w_o;
+    g.sBo = K;
+    g.C = out;
+    g.sCm = dims->d_model;
+    g.M = static_cast<int>(n_tokens);
+    g.N = dims->d_model;
+    g.K = K;
+    g.Z = 1;
+    mla::gemm(g, dims->dtype, /*a_f32=*/false, /*b_kn=*/false, /*out_bf16=*/dims->dtype == MLA_BF16, s);
+  }
   return launch_status();
 }
 

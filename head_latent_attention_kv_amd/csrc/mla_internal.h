@@ -64,14 +64,19 @@ void finalize_cache_rows(int dtype, const float* proj, int64_t ld, int splits, i
                          int64_t n_tokens, int r, int n_groups, int d_rope, int latent_rmsnorm,
                          float eps, double theta, hipStream_t s);
 
-// q_pe[t,h,:] = RoPE(proj[t*ld + h*d_rope : +d_rope], positions[t]), cast to dtype.
-void finalize_query_rope(int dtype, const float* proj, int64_t ld, void* q_pe,
+// q_pe[t,h,:] = RoPE(proj[t*ld + h*hstride : +d_rope], positions[t]), cast to dtype.
+void finalize_query_rope(int dtype, const float* proj, int64_t ld, int hstride, void* q_pe,
                          const int32_t* positions, int64_t n_tokens, int n_heads, int d_rope,
                          double theta, hipStream_t s);
 
-// dst[row, 0:n_cols] = src[row, 0:n_cols] (fp32 -> dtype), rows strided.
-void cast_rows(int dtype, const float* src, int64_t ld_src, int n_cols, void* dst, int64_t ld_dst,
-               int64_t n_rows, hipStream_t s);
+// dst[t, h, 0:n] = src[t*ld + h*hstride : +n] (fp32 -> dtype), dst dense [n_rows, n_heads, n].
+void cast_heads(int dtype, const float* src, int64_t ld, int hstride, int n_heads, int n, void* dst,
+                int64_t n_rows, hipStream_t s);
+
+// out[t, :n] = RMSNorm(Σ_p proj[p*sps + t*ld + :n]) * gain (gain may be null: unit), in dtype.
+bool norm_rows_supported(int n);
+void norm_rows(int dtype, const float* proj, int64_t ld, int splits, int64_t sps, int n, const void* gain,
+               float eps, void* out, int64_t ld_out, int64_t n_rows, hipStream_t s);
 
 // Shape of one attention call, as the kernels see it.
 struct AttnShape {

@@ -1,7 +1,10 @@
 // Row epilogues of the projection GEMMs:
 //  - cache rows: optional unit-gain RMSNorm over the latent, rotate-half RoPE of
 //    each rotary-key group at the token's position, cast, store to its slot;
-//  - query rotary part: RoPE of q_pe per head.
+//  - query rotary part: RoPE of q_pe per head;
+//  - normalised rows: sum of K-split slices, RMSNorm with a gain, cast (the
+//    low-rank query's q_a_layernorm);
+//  - per-head casts of fp32 projection columns.
 // RoPE pairs dims (j, j + d/2), angle p·θ^(-2j/d) formed and reduced in double.
 #include <algorithm>
 #include <cmath>
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(256) void cache_rows_kernel(const float* __restrict
 
 template <typename T>
 __global__ __launch_bounds__(256) void query_rope_kernel(const float* __restrict__ proj, int64_t ld,
-                                                         T* __restrict__ q_pe,
+                                                         int hstride, T* __restrict__ q_pe,
                                                          const int32_t* __restrict__ positions,
                                                          int n_heads, int d_rope, double rope_base) {
   const int64_t t = blockIdx.x;
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(256) void query_rope_kernel(const float* __restrict
   for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) {
     // the pair's loads go out before its angle is formed
     const int h = i / half, j = i % half;
-    const float a = src[h * d_rope + j], b = src[h * d_rope + j + half];
+    const float a = src[h * hstride + j], b = src[h * hstride + j + half];
     float c, sn;
     rope_cos_sin(pos, j, rope_base, &c, &sn);
     Elem<T>::store(dst, h * d_rope + j, a * c - b * sn);
@@ -100,31 +103,74 @@ __global__ __launch_bounds__(256) void query_rope_kernel(const float* __restrict
   }
 }
 
-// dst[row, c] = src[row, c] for c < n_cols, cast to T (the q_nope columns of the
-// fp32 query projection).
+// dst[t, h*n + c] = src[t*ld + h*hstride + c] for c < n, cast to T (per-head
+// columns of an fp32 projection, e.g. q_nope out of [q_nope ; q_pe] head rows).
 template <typename T>
-__global__ __launch_bounds__(256) void cast_rows_kernel(const float* __restrict__ src, int64_t ld_src,
-                                                        int n_cols, T* __restrict__ dst, int64_t ld_dst,
-                                                        int64_t n_rows) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= n_cols) return;
-  for (int64_t row = blockIdx.y; row < n_rows; row += gridDim.y)
-    Elem<T>::store(dst, row * ld_dst + c, src[row * ld_src + c]);
+__global__ __launch_bounds__(256) void cast_heads_kernel(const float* __restrict__ src, int64_t ld,
+                                                         int hstride, int n_heads, int n,
+                                                         T* __restrict__ dst, int64_t n_rows) {
+  const int i = blockIdx.x * 256 + threadIdx.x;  // column of the output row
+  if (i >= n_heads * n) return;
+  const int h = i / n, c = i - h * n;
+  for (int64_t t = blockIdx.y; t < n_rows; t += gridDim.y)
+    Elem<T>::store(dst, t * n_heads * n + i, src[t * ld + static_cast<int64_t>(h) * hstride + c]);
+}
+
+// out[t, i] = v[i] / sqrt(mean(v^2) + eps) * gain[i], v = the sum of `splits`
+// fp32 slices of row t (n <= kNormMax); gain == nullptr: unit gain.
+constexpr int kNormMax = 4096;
+template <typename T>
+__global__ __launch_bounds__(256) void norm_rows_kernel(const float* __restrict__ proj, int64_t ld,
+                                                        int splits, int64_t sps, int n,
+                                                        const T* __restrict__ gain, float eps,
+                                                        T* __restrict__ out, int64_t ld_out) {
+  __shared__ float row[kNormMax];
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    float v = 0.f;
+    for (int p = 0; p < splits; ++p) v += proj[p * sps + t * ld + i];
+    row[i] = v;
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / static_cast<float>(n) + eps);
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const float g = gain != nullptr ? Elem<T>::load(gain, i) : 1.f;
+    Elem<T>::store(out, t * ld_out + i, row[i] * inv * g);
+  }
 }
 
 }  // namespace
 
-void cast_rows(int dtype, const float* src, int64_t ld_src, int n_cols, void* dst, int64_t ld_dst,
-               int64_t n_rows, hipStream_t s) {
-  if (n_rows <= 0 || n_cols <= 0) return;
-  dim3 grid(static_cast<unsigned>((n_cols + 255) / 256),
+void cast_heads(int dtype, const float* src, int64_t ld, int hstride, int n_heads, int n, void* dst,
+                int64_t n_rows, hipStream_t s) {
+  if (n_rows <= 0 || n <= 0 || n_heads <= 0) return;
+  dim3 grid(static_cast<unsigned>((n_heads * n + 255) / 256),
             static_cast<unsigned>(std::min<int64_t>(n_rows, 65535)));
   if (dtype == kF32)
-    hipLaunchKernelGGL(cast_rows_kernel<float>, grid, dim3(256), 0, s, src, ld_src, n_cols,
-                       static_cast<float*>(dst), ld_dst, n_rows);
+    hipLaunchKernelGGL(cast_heads_kernel<float>, grid, dim3(256), 0, s, src, ld, hstride, n_heads, n,
+                       static_cast<float*>(dst), n_rows);
   else
-    hipLaunchKernelGGL(cast_rows_kernel<bf16_t>, grid, dim3(256), 0, s, src, ld_src, n_cols,
-                       static_cast<bf16_t*>(dst), ld_dst, n_rows);
+    hipLaunchKernelGGL(cast_heads_kernel<bf16_t>, grid, dim3(256), 0, s, src, ld, hstride, n_heads, n,
+                       static_cast<bf16_t*>(dst), n_rows);
+}
+
+bool norm_rows_supported(int n) { return n > 0 && n <= kNormMax; }
+
+void norm_rows(int dtype, const float* proj, int64_t ld, int splits, int64_t sps, int n, const void* gain,
+               float eps, void* out, int64_t ld_out, int64_t n_rows, hipStream_t s) {
+  if (n_rows <= 0) return;
+  dim3 grid(static_cast<unsigned>(n_rows));
+  if (dtype == kF32)
+    hipLaunchKernelGGL(norm_rows_kernel<float>, grid, dim3(256), 0, s, proj, ld, splits, sps, n,
+                       static_cast<const float*>(gain), eps, static_cast<float*>(out), ld_out);
+  else
+    hipLaunchKernelGGL(norm_rows_kernel<bf16_t>, grid, dim3(256), 0, s, proj, ld, splits, sps, n,
+                       static_cast<const bf16_t*>(gain), eps, static_cast<bf16_t*>(out), ld_out);
 }
 
 void finalize_cache_rows(int dtype, const float* proj, int64_t ld, int splits, int64_t sps,
@@ -149,7 +195,7 @@ void finalize_cache_rows(int dtype, const float* proj, int64_t ld, int splits, i
   }
 }
 
-void finalize_query_rope(int dtype, const float* proj, int64_t ld, void* q_pe,
+void finalize_query_rope(int dtype, const float* proj, int64_t ld, int hstride, void* q_pe,
                          const int32_t* positions, int64_t n_tokens, int n_heads, int d_rope,
                          double theta, hipStream_t s) {
   if (n_tokens <= 0) return;
@@ -157,10 +203,10 @@ void finalize_query_rope(int dtype, const float* proj, int64_t ld, void* q_pe,
   const int items = n_heads * (d_rope / 2);
   dim3 grid(static_cast<unsigned>(n_tokens), static_cast<unsigned>(std::max(1, std::min(16, items / 256))));
   if (dtype == kF32)
-    hipLaunchKernelGGL(query_rope_kernel<float>, grid, dim3(256), 0, s, proj, ld,
+    hipLaunchKernelGGL(query_rope_kernel<float>, grid, dim3(256), 0, s, proj, ld, hstride,
                        static_cast<float*>(q_pe), positions, n_heads, d_rope, base);
   else
-    hipLaunchKernelGGL(query_rope_kernel<bf16_t>, grid, dim3(256), 0, s, proj, ld,
+    hipLaunchKernelGGL(query_rope_kernel<bf16_t>, grid, dim3(256), 0, s, proj, ld, hstride,
                        static_cast<bf16_t*>(q_pe), positions, n_heads, d_rope, base);
 }
 

@@ -66,7 +66,8 @@ typedef enum mla_op {
   MLA_OP_DECODE = 2,
   MLA_OP_PREFILL = 3,
   MLA_OP_QUERY = 4,
-  MLA_OP_PREFILL_EXPANDED = 5
+  MLA_OP_PREFILL_EXPANDED = 5,
+  MLA_OP_OUTPUT = 6
 } mla_op;
 
 /* Layer dimensions and hyper-parameters shared by all calls. */
@@ -225,6 +226,45 @@ int mla_prefill_expanded(const mla_dims* dims, const void* q_nope, const void* q
                          const int64_t* cu_seqlens, int32_t batch, int64_t n_tokens, int32_t max_len,
                          const void* w_uk, const void* w_uv, void* out, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Low-rank query path (DeepSeek-V2's query factorisation), with or without the
+ * W_UK absorption:
+ *   c_q        = RMSNorm(x[t]·W_QAᵀ) * q_gain      (eps = dims->rms_eps; over q_rank values)
+ *   q[t,h,:]   = c_q·W_QB[h*(d_nope+d_rope) : +(d_nope+d_rope)]ᵀ = [q_nope ; q_pe_raw]
+ *   q_pe[t,h]  = RoPE(q_pe_raw, positions[t])
+ *   q_lat[t,h,:] = Σ_d q_nope[t,h,d]·W_UK[h,d,:]    (mla_absorb_lowrank)
+ * c_q is rounded to the layer's element type between the two projections.
+ * Source: MLA principle page, section "步骤": q = q_b_proj(q_a_layernorm(q_a_proj(x)))
+ * (5120 -> 1536 -> 24576 = 128 heads x 192), viewed per head and split into q_nope /
+ * q_pe; the nanowhale MLA page's wq_a / q_norm / wq_b.
+ *   q_rank: width of the middle (multiple of 8, at most 4096)
+ *   x device [n_tokens, d_model]; w_qa device [q_rank, d_model]
+ *   q_gain device [q_rank] or NULL (unit gain); w_qb device [H*(d_nope+d_rope), q_rank],
+ *     rows head-major with each head's d_nope rows before its d_rope rows
+ *   w_uk device [H, d_nope, r]; positions device int32 [n_tokens]
+ *   q_lat device out [n_tokens, H, r] or q_nope device out [n_tokens, H, d_nope];
+ *   q_pe device out [n_tokens, H, d_rope]
+ *   workspace device, >= mla_lowrank_workspace_size(dims, q_rank, n_tokens) bytes
+ * n_tokens == 0 is a no-op. */
+size_t mla_lowrank_workspace_size(const mla_dims* dims, int32_t q_rank, int64_t n_tokens);
+int mla_absorb_lowrank(const mla_dims* dims, int32_t q_rank, const void* x, const void* w_qa,
+                       const void* q_gain, const void* w_qb, const void* w_uk, const int32_t* positions,
+                       int64_t n_tokens, void* q_lat, void* q_pe, void* workspace, size_t workspace_bytes,
+                       void* stream);
+int mla_query_lowrank(const mla_dims* dims, int32_t q_rank, const void* x, const void* w_qa,
+                      const void* q_gain, const void* w_qb, const int32_t* positions, int64_t n_tokens,
+                      void* q_nope, void* q_pe, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Output projection after W_UV:  u[t,:] = Σ_h Σ_e attn[t,h,e]·W_o[:, h*d_v + e].
+ * Source: MLA principle page, eqs. (3)/(6) (einsum 'hdD,bhqd->bqD' of W_o with the
+ * per-head outputs) and o_proj of size [num_heads * v_head_dim -> hidden].
+ *   attn device [n_tokens, H, d_v] (the output of mla_decode / mla_prefill)
+ *   w_o device [d_model, H*d_v];  out device out [n_tokens, d_model]
+ *   workspace device, >= mla_workspace_size(dims, MLA_OP_OUTPUT, 0, n_tokens, 0) bytes
+ *   (0 for many tokens: then workspace may be NULL)
+ * n_tokens == 0 is a no-op. */
+int mla_output(const mla_dims* dims, const void* attn, const void* w_o, int64_t n_tokens, void* out,
+               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable text for a status code (static storage). */
 const char* mla_strerror(int status);

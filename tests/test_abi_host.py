@@ -138,3 +138,30 @@ def test_original_order_prefill_entry_points():
     for cfg in ("tiny_f32", "qwen25_7b_decode", "qwen3_30b_ragged_decode"):
         dd = abi.dims_of(I.CONFIGS[cfg])
         assert pe(ctypes.byref(dd), p, p, p, p, 1, 10, 10, p, p, p, p, 1 << 40, null) == abi.MLA_ENOTSUP, cfg
+
+
+def test_lowrank_query_and_output_entry_points():
+    abi, lib = _lib()
+    null = None
+    d = abi.dims_of(I.CONFIGS["deepseek_v2_decode"])
+    ws = lib.mla_lowrank_workspace_size(ctypes.byref(d), 1536, 64)
+    assert ws >= 64 * (1536 * 4 + 1536 * 2 + 128 * 192 * 4)
+    assert lib.mla_lowrank_workspace_size(ctypes.byref(d), 0, 64) == 0
+    assert lib.mla_lowrank_workspace_size(None, 1536, 64) == 0
+    a = lib.mla_absorb_lowrank
+    assert a(ctypes.byref(d), 1536, null, null, null, null, null, null, 0, null, null, null, 0, null) == abi.MLA_OK
+    assert a(ctypes.byref(d), 1536, null, null, null, null, null, null, 4, null, null, null, 0, null) == abi.MLA_EINVAL
+    p = 0x10000
+    assert a(ctypes.byref(d), 0, p, p, null, p, p, p, 4, p, p, p, 1 << 40, null) == abi.MLA_EINVAL
+    assert a(ctypes.byref(d), 100, p, p, null, p, p, p, 4, p, p, p, 1 << 40, null) == abi.MLA_ENOTSUP  # q_rank % 8
+    assert a(ctypes.byref(d), 8192, p, p, null, p, p, p, 4, p, p, p, 1 << 40, null) == abi.MLA_ENOTSUP  # > 4096
+    assert a(ctypes.byref(d), 1536, p, p, null, p, p, p, 4, p, p, p, 16, null) == abi.MLA_EWORKSPACE
+    assert a(ctypes.byref(d), 1536, p, p, 0x10001, p, p, p, 4, p, p, p, 1 << 40, null) == abi.MLA_EINVAL
+    q = lib.mla_query_lowrank
+    assert q(ctypes.byref(d), 1536, p, p, null, p, p, 4, null, p, p, 1 << 40, null) == abi.MLA_EINVAL
+    o = lib.mla_output
+    assert lib.mla_workspace_size(ctypes.byref(d), abi.MLA_OP_OUTPUT, 0, 64, 0) >= 64 * 5120 * 4
+    assert lib.mla_workspace_size(ctypes.byref(d), abi.MLA_OP_OUTPUT, 0, 5000, 0) == 0  # tiled GEMM, no scratch
+    assert o(ctypes.byref(d), null, null, 0, null, null, 0, null) == abi.MLA_OK
+    assert o(ctypes.byref(d), null, null, 4, null, null, 0, null) == abi.MLA_EINVAL
+    assert o(ctypes.byref(d), p, p, 4, p, p, 16, null) == abi.MLA_EWORKSPACE

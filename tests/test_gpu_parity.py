@@ -422,6 +422,67 @@ def test_prefill_expanded_restart(torch):
 
 
 # ----------------------------------------------------------------------------
+# beyond the attention: the low-rank query path and the output projection
+# ----------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("name,T,q_rank", [("deepseek_v2_decode", 64, I.Q_LORA_RANK),
+                                           ("deepseek_v2_decode", 300, I.Q_LORA_RANK),
+                                           ("tiny_f32", 37, 96)])
+def test_lowrank_query_matches_oracle(torch, name, T, q_rank):
+    """mla_absorb_lowrank and mla_query_lowrank against the oracle's low-rank query
+    (few tokens: weight-streaming projections; many: tiled GEMMs)."""
+    import head_latent_attention_kv_amd as M
+    from oracle import mla_oracle as O
+    cfg = I.CONFIGS[name]
+    _print_case("lowrank_query", cfg=name, T=T, q_rank=q_rank)
+    layer = Hh.make_layer(cfg)
+    lw = I.lowrank_query_weights(cfg, q_rank)
+    lwd = {k: Hh.to_dev(v, cfg.dtype) for k, v in lw.items()}
+    x = I.x_rows(cfg, 3, 0, T)
+    pos = np.random.default_rng(11).integers(0, 50000, T)
+    et = Hh.elem_dtype(cfg)
+    xd = Hh.to_dev(x, cfg.dtype)
+    posd = torch.from_numpy(pos.astype(np.int32)).cuda()
+    q_lat = torch.empty((T, cfg.n_heads, cfg.rank), dtype=et, device="cuda")
+    q_pe = torch.empty((T, cfg.n_heads, cfg.d_rope), dtype=et, device="cuda")
+    q_nope = torch.empty((T, cfg.n_heads, cfg.d_nope), dtype=et, device="cuda")
+    q_pe2 = torch.empty_like(q_pe)
+    M.mla_absorb_lowrank(layer.dims, q_rank, xd, lwd["w_qa"], lwd["q_gain"], lwd["w_qb"], layer.w_dev["w_uk"],
+                         posd, q_lat, q_pe)
+    M.mla_query_lowrank(layer.dims, q_rank, xd, lwd["w_qa"], lwd["q_gain"], lwd["w_qb"], posd, q_nope, q_pe2)
+    torch.cuda.synchronize()
+    qn, qr = O.lowrank_query(x, lw["w_qa"], lw["q_gain"], lw["w_qb"], pos, n_heads=cfg.n_heads,
+                             d_nope=cfg.d_nope, d_rope=cfg.d_rope, theta=cfg.rope_theta, eps=cfg.rms_eps)
+    errs = {"q_lat": Hh.rel_err_rows(Hh.to_host(q_lat), O.absorbed_query(qn, layer.w_host["w_uk"])),
+            "q_pe": Hh.rel_err_rows(Hh.to_host(q_pe), qr),
+            "q_nope": Hh.rel_err_rows(Hh.to_host(q_nope), qn),
+            "q_pe (query call)": Hh.rel_err_rows(Hh.to_host(q_pe2), qr)}
+    print(f"{name} lowrank T={T}: " + " ".join(f"{k}={v:.3e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= Hh.TOL[cfg.dtype], (k, v)
+
+
+@pytest.mark.parametrize("name,T", [("deepseek_v2_decode", 64), ("deepseek_v2_decode", 300),
+                                    ("long_prefill_131k", 1000), ("tiny_f32", 17)])
+def test_output_projection_matches_oracle(torch, name, T):
+    """mla_output (u = o·W_oᵀ over all heads) against the oracle's eq. (3)/(6) product."""
+    import head_latent_attention_kv_amd as M
+    from oracle import mla_oracle as O
+    cfg = I.CONFIGS[name]
+    _print_case("output_projection", cfg=name, T=T)
+    layer = Hh.make_layer(cfg)
+    w_o = I.output_weight(cfg)
+    o = I.draw_normal(cfg.seed, 40, (T,), (T, cfg.n_heads, cfg.d_v), 1.0, cfg.dtype)
+    out = torch.empty((T, cfg.d_model), dtype=Hh.elem_dtype(cfg), device="cuda")
+    M.mla_output(layer.dims, Hh.to_dev(o, cfg.dtype), Hh.to_dev(w_o, cfg.dtype), out)
+    torch.cuda.synchronize()
+    err = Hh.rel_err_rows(Hh.to_host(out), O.output_projection(o, w_o))
+    print(f"{name} output projection T={T}: {err:.3e}")
+    assert err <= Hh.TOL[cfg.dtype], err
+
+
+# ----------------------------------------------------------------------------
 # ABI behaviour on the device
 # ----------------------------------------------------------------------------
 
