@@ -403,6 +403,58 @@ def main():
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all(), "non-finite decode output"
 
+    # beyond the attention: the low-rank query path (DeepSeek-V2's 1536-wide query
+    # factorisation) in place of [W_QC | W_QR], and the output projection W_o
+    q_rank = I.Q_LORA_RANK
+    lw = {k: Hh.to_dev(v, cfg.dtype) for k, v in I.lowrank_query_weights(cfg, q_rank).items()}
+    w_o = Hh.to_dev(I.output_weight(cfg), cfg.dtype)
+    u = torch.empty((B, cfg.d_model), dtype=et, device="cuda")
+    ws_l = torch.empty(max(256, M.mla_lowrank_workspace_size(dims, q_rank, B)), dtype=torch.uint8, device="cuda")
+    ws_o = torch.empty(max(256, M.mla_workspace_size(dims, M.MLA_OP_OUTPUT, 0, B, 0)), dtype=torch.uint8,
+                       device="cuda")
+
+    def lowrank_only(i):
+        M.mla_absorb_lowrank(dims, q_rank, x_new_d, lw["w_qa"], lw["q_gain"], lw["w_qb"], wd["w_uk"], pos_new,
+                             q_lat, q_pe, workspace=ws_l)
+
+    def output_only(i):
+        M.mla_output(dims, out, w_o, u, workspace=ws_o)
+
+    def layer_step(i):
+        c = caches[i % n_copies]
+        M.mla_write_cache(dims, x_new_d, wd["w_dkv"], wd["w_kr"], pos_new, slots_new, c, workspace=ws_w)
+        lowrank_only(i)
+        M.mla_decode(dims, q_lat, q_pe, c, seq_start, seq_len, max_len, wd["w_uv"], out, workspace=ws_d)
+        output_only(i)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_lr, ms_out, ms_layer = timed(lowrank_only), timed(output_only), timed(layer_step)
+    assert torch.isfinite(u.float()).all(), "non-finite output projection"
+    lr_bytes = 2 * (q_rank * cfg.d_model + cfg.n_heads * (cfg.d_nope + cfg.d_rope) * q_rank +
+                    cfg.n_heads * cfg.d_nope * cfg.rank + q_rank)
+    wo_bytes = 2 * cfg.d_model * cfg.n_heads * cfg.d_v
+    print(f"[bench] low-rank query {ms_lr * 1e3:.1f} us, output projection {ms_out * 1e3:.1f} us, "
+          f"layer step {ms_layer * 1e3:.1f} us", file=sys.stderr, flush=True)
+    beyond = {
+        "lowrank_query": {"call": "mla_absorb_lowrank", "q_rank": q_rank, "us": round(ms_lr * 1e3, 2),
+                          "weight_bytes": lr_bytes,
+                          "hbm_frac": round(lr_bytes / (ms_lr * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "output_projection": {"call": "mla_output", "us": round(ms_out * 1e3, 2), "weight_bytes": wo_bytes,
+                              "hbm_frac": round(wo_bytes / (ms_out * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "layer_step": {"step": "mla_write_cache + mla_absorb_lowrank + mla_decode + mla_output",
+                       "us": round(ms_layer * 1e3, 2), "tokens_per_s": round(B / (ms_layer * 1e-3), 1)},
+    }
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, I, lengths)
@@ -439,6 +491,7 @@ def main():
                         "alg_flops": decode_alg_flops(cfg, lengths),
                         "hbm_frac": round(decode_alg_bytes(cfg, lengths) / (ms_dec * 1e-3) / 1e9
                                           / HBM_PEAK_GBS, 4)},
+        "beyond_attention": beyond,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

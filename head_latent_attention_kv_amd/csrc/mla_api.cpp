@@ -744,8 +744,7 @@ int mla_output(const mla_dims* dims, const void* attn, const void* w_o, int64_t 
     float* c = static_cast<float*>(workspace);
     const int64_t ld = out_width(dims);
     const Proj p = proj_one(dims, attn, K, K, w_o, dims->d_model, c, ld, n_tokens, s);
-    mla::sum_split_slices(c, p.splits, p.sps, static_cast<int>(n_tokens), dims->d_model, ld, s);
-    mla::cast_heads(dims->dtype, c, ld, 0, 1, dims->d_model, out, n_tokens, s);
+    mla::sum_cast_slices(dims->dtype, c, p.splits, p.sps, static_cast<int>(n_tokens), dims->d_model, ld, out, s);
   } else {
     GemmArgs g{};
     g.A = attn;

@@ -52,6 +52,9 @@ struct SkinnyArgs {
 int skinny_splits(int M, int N, int Z, int K);
 void gemm_skinny(SkinnyArgs sa, bool a_f32, bool out_bf16, hipStream_t s);
 void sum_split_slices(float* c, int splits, int64_t sps, int M, int N, int64_t ldc, hipStream_t s);
+// out[m, n] (dense [M, N], dtype) = Σ_p c[p*sps + m*ldc + n]
+void sum_cast_slices(int dtype, const float* c, int splits, int64_t sps, int M, int N, int64_t ldc, void* out,
+                     hipStream_t s);
 // fp32 A merged from n_merge <= skinny_max_merge() split-softmax partials, one K piece
 int skinny_max_merge();
 void gemm_skinny_merged(SkinnyArgs sa, int n_merge, bool out_bf16, hipStream_t s);

@@ -117,30 +117,51 @@ __global__ __launch_bounds__(256) void cast_heads_kernel(const float* __restrict
 }
 
 // out[t, i] = v[i] / sqrt(mean(v^2) + eps) * gain[i], v = the sum of `splits`
-// fp32 slices of row t (n <= kNormMax); gain == nullptr: unit gain.
-constexpr int kNormMax = 4096;
+// fp32 slices of row t (n <= kNormMax, splits <= kNormSlices); gain == nullptr:
+// unit gain.  1024 threads per row; each thread's slice loads go out before any
+// sum (clamped addresses, no branch between them).
+constexpr int kNormThreads = 1024;
+constexpr int kNormPer = 4;  // elements per thread
+constexpr int kNormMax = kNormThreads * kNormPer;
+constexpr int kNormSlices = 16;
 template <typename T>
-__global__ __launch_bounds__(256) void norm_rows_kernel(const float* __restrict__ proj, int64_t ld,
-                                                        int splits, int64_t sps, int n,
-                                                        const T* __restrict__ gain, float eps,
-                                                        T* __restrict__ out, int64_t ld_out) {
-  __shared__ float row[kNormMax];
-  __shared__ float red[4];
+__global__ __launch_bounds__(kNormThreads) void norm_rows_kernel(const float* __restrict__ proj, int64_t ld,
+                                                                 int splits, int64_t sps, int n,
+                                                                 const T* __restrict__ gain, float eps,
+                                                                 T* __restrict__ out, int64_t ld_out) {
+  __shared__ float red[kNormThreads / 64];
   const int64_t t = blockIdx.x;
+  float part[kNormPer][kNormSlices];
+#pragma unroll
+  for (int e = 0; e < kNormPer; ++e) {
+    const int i = min(static_cast<int>(threadIdx.x) + kNormThreads * e, n - 1);
+#pragma unroll
+    for (int p = 0; p < kNormSlices; ++p) part[e][p] = proj[min(p, splits - 1) * sps + t * ld + i];
+  }
+  float v[kNormPer];
   float ss = 0.f;
-  for (int i = threadIdx.x; i < n; i += 256) {
-    float v = 0.f;
-    for (int p = 0; p < splits; ++p) v += proj[p * sps + t * ld + i];
-    row[i] = v;
-    ss = fmaf(v, v, ss);
+#pragma unroll
+  for (int e = 0; e < kNormPer; ++e) {
+    float a = 0.f;
+#pragma unroll
+    for (int p = 0; p < kNormSlices; ++p) a += p < splits ? part[e][p] : 0.f;
+    v[e] = a;
+    if (static_cast<int>(threadIdx.x) + kNormThreads * e < n) ss = fmaf(a, a, ss);
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / static_cast<float>(n) + eps);
-  for (int i = threadIdx.x; i < n; i += 256) {
-    const float g = gain != nullptr ? Elem<T>::load(gain, i) : 1.f;
-    Elem<T>::store(out, t * ld_out + i, row[i] * inv * g);
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kNormThreads / 64; ++w) tot += red[w];
+  const float inv = 1.0f / sqrtf(tot / static_cast<float>(n) + eps);
+#pragma unroll
+  for (int e = 0; e < kNormPer; ++e) {
+    const int i = static_cast<int>(threadIdx.x) + kNormThreads * e;
+    if (i < n) {
+      const float g = gain != nullptr ? Elem<T>::load(gain, i) : 1.f;
+      Elem<T>::store(out, t * ld_out + i, v[e] * inv * g);
+    }
   }
 }
 
@@ -166,10 +187,10 @@ void norm_rows(int dtype, const float* proj, int64_t ld, int splits, int64_t sps
   if (n_rows <= 0) return;
   dim3 grid(static_cast<unsigned>(n_rows));
   if (dtype == kF32)
-    hipLaunchKernelGGL(norm_rows_kernel<float>, grid, dim3(256), 0, s, proj, ld, splits, sps, n,
+    hipLaunchKernelGGL(norm_rows_kernel<float>, grid, dim3(kNormThreads), 0, s, proj, ld, splits, sps, n,
                        static_cast<const float*>(gain), eps, static_cast<float*>(out), ld_out);
   else
-    hipLaunchKernelGGL(norm_rows_kernel<bf16_t>, grid, dim3(256), 0, s, proj, ld, splits, sps, n,
+    hipLaunchKernelGGL(norm_rows_kernel<bf16_t>, grid, dim3(kNormThreads), 0, s, proj, ld, splits, sps, n,
                        static_cast<const bf16_t*>(gain), eps, static_cast<bf16_t*>(out), ld_out);
 }
 

@@ -654,24 +654,55 @@ namespace {
 //           K splits supply the parallelism);
 //  else   = 64 columns, two per CU (up to 32 token rows).
 enum class Bf16Variant { kWide, kNarrow, kBase };
-Bf16Variant bf16_variant(int M, int N, int Z) {
+Bf16Variant bf16_variant(int M, int N, int Z, int K) {
   if (M <= 32) return Bf16Variant::kBase;
-  return (N + 16 * kWideNB - 1) / (16 * kWideNB) * Z >= 128 ? Bf16Variant::kWide : Bf16Variant::kNarrow;
+  // wide (96-column) tiles when they, or they times the K splits a long K allows,
+  // fill the chip: a 5120-column output of K = 16384 runs 54 tiles x 5 splits
+  const int tiles = (N + 16 * kWideNB - 1) / (16 * kWideNB) * Z;
+  const int max_splits = std::max(1, std::min(16, K / 256));
+  return tiles >= 128 || tiles * max_splits >= 256 ? Bf16Variant::kWide : Bf16Variant::kNarrow;
 }
 }  // namespace
 
 int skinny_splits(int M, int N, int Z, int K) {
-  // enough workgroups to fill every slot (one or two per compute unit, as the
-  // bf16 launch picks), at least 256 k per split and at most 16 slices; the
-  // value returned is the number of K pieces the kernel uses
-  const Bf16Variant v = bf16_variant(M, N, Z);
+  // workgroups to fill the slots (one or two per compute unit, as the bf16
+  // launch picks), at least 256 k per split and at most 16 slices; the value
+  // returned is the number of K pieces the kernel uses
+  const Bf16Variant v = bf16_variant(M, N, Z, K);
   const int cols = v == Bf16Variant::kWide ? 16 * kWideNB : v == Bf16Variant::kNarrow ? 32 : 64;
   const int slots = v == Bf16Variant::kWide ? 256 : 512;
   const int tiles = (N + cols - 1) / cols * Z;
-  int splits = (slots + tiles - 1) / tiles;
+  // as many K pieces as keep the grid within one wave of workgroup slots (a
+  // second, partly filled wave would take as long as the first)
+  int splits = std::max(1, slots / tiles);
   splits = std::max(1, std::min({splits, std::max(1, K / 256), 16}));
   const int kps = k_per_split(K, splits);
   return (K + kps - 1) / kps;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void sum_cast_kernel(const float* __restrict__ c, int splits, int64_t sps,
+                                                       int M, int N, int64_t ldc, T* __restrict__ out) {
+  const int64_t total = static_cast<int64_t>(M) * N;
+  for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < total; i += gridDim.x * 256LL) {
+    const int64_t m = i / N, n = i - m * N;
+    float v = 0.f;
+    for (int p = 0; p < splits; ++p) v += c[p * sps + m * ldc + n];
+    Elem<T>::store(out, i, v);
+  }
+}
+
+void sum_cast_slices(int dtype, const float* c, int splits, int64_t sps, int M, int N, int64_t ldc, void* out,
+                     hipStream_t s) {
+  if (M <= 0 || N <= 0) return;
+  const int64_t total = static_cast<int64_t>(M) * N;
+  const int blocks = static_cast<int>(std::min<int64_t>(4096, (total + 255) / 256));
+  if (dtype == kF32)
+    hipLaunchKernelGGL(sum_cast_kernel<float>, dim3(blocks), dim3(256), 0, s, c, splits, sps, M, N, ldc,
+                       static_cast<float*>(out));
+  else
+    hipLaunchKernelGGL(sum_cast_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, c, splits, sps, M, N, ldc,
+                       static_cast<bf16_t*>(out));
 }
 
 void sum_split_slices(float* c, int splits, int64_t sps, int M, int N, int64_t ldc, hipStream_t s) {
@@ -714,7 +745,7 @@ void launch_dma(const SkinnyArgs& sa, bool out_bf16, hipStream_t s) {
 template <int MB>
 void launch_kind(const SkinnyArgs& sa, int kind, int ns, bool out_bf16, hipStream_t s) {
   if (kind == kABf16) {
-    const Bf16Variant v = bf16_variant(sa.M, sa.N, sa.Z);
+    const Bf16Variant v = bf16_variant(sa.M, sa.N, sa.Z, sa.K);
     if constexpr (MB >= 3) {
       if (v == Bf16Variant::kWide && sa.N0 % 4 == 0) launch_dma<MB>(sa, out_bf16, s);
       else if (v == Bf16Variant::kWide) launch_out<MB, kWideNB, kABf16, 1, 3, 1>(sa, out_bf16, s);
