@@ -71,6 +71,7 @@ def quantize(a: np.ndarray, dtype: str) -> np.ndarray:
 # tensor ids for the seed sequence
 T_X, T_WDKV, T_WKR, T_WQC, T_WQR, T_WUK, T_WUV, T_LEN, T_SAMPLE = range(9)
 T_WQA, T_QGAIN, T_WQB, T_WO = range(9, 13)
+T_V4 = 13  # base id of the DeepSeek-V4 variant's tensors (13 .. 20)
 
 # Query down-projection width of the low-rank query path: DeepSeek-V2 factors its
 # 5120 -> 24576 query map through 1536 dims (MLA principle page, section 'steps').
@@ -216,6 +217,63 @@ def output_weight(cfg: MLAConfig) -> np.ndarray:
     """W_o [d_model, H·d_v] ~ N(0, 1/(H·d_v)): the output projection after W_UV."""
     k = cfg.n_heads * cfg.d_v
     return draw_normal(cfg.seed, T_WO, (0,), (cfg.d_model, k), 1.0 / math.sqrt(k), cfg.dtype)
+
+
+@dataclasses.dataclass(frozen=True)
+class V4Config:
+    """The DeepSeek-V4 / nanowhale MLA variant (nanowhale MLA page): one KV head of
+    head_dim values (its last d_rope rotary) shared by all query heads as key and
+    value, a low-rank query, an attention sink, grouped low-rank output."""
+    name: str
+    seed: int
+    d_model: int
+    n_heads: int
+    head_dim: int
+    d_rope: int
+    q_rank: int
+    o_groups: int
+    o_rank: int
+    dtype: str
+    batch: int
+    context: int
+    rms_eps: float = 1e-6
+    rope_theta: float = 10000.0
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+# nanowhale-100m's attention (page: hidden 320, 8 query heads, one KV head,
+# q_lora_rank 160, head_dim 512 = 448 + 64 rotary, o_groups 8, o_lora_rank 1024,
+# context 2048), decoded for 256 sequences at full context.
+V4_CONFIGS: Dict[str, V4Config] = {
+    "nanowhale_v4_decode": V4Config(
+        name="nanowhale_v4_decode", seed=1006, d_model=320, n_heads=8, head_dim=512, d_rope=64,
+        q_rank=160, o_groups=8, o_rank=1024, dtype="bf16", batch=256, context=2048),
+}
+
+
+def v4_weights(cfg: V4Config) -> Dict[str, np.ndarray]:
+    """W_KV [head_dim, d_model], kv_gain [head_dim], W_QA [q_rank, d_model], q_gain
+    [q_rank], W_QB [H·head_dim, q_rank], W_OA [o_groups·o_rank, H·head_dim/o_groups],
+    W_OB [d_model, o_groups·o_rank] ~ N(0, 1/fan_in); gains ~ 1 + N(0, 0.1^2);
+    sink [H] ~ N(0, 1) (fp32)."""
+    H, D = cfg.n_heads, cfg.head_dim
+    gdim = H * D // cfg.o_groups
+    sd = lambda k: 1.0 / math.sqrt(k)  # noqa: E731
+    g = lambda i, n: quantize(draw_normal(cfg.seed, T_V4 + i, (0,), (n,), 0.1, "f32") + np.float32(1.0), cfg.dtype)  # noqa: E731
+    return {
+        "w_kv": draw_normal(cfg.seed, T_V4, (0,), (D, cfg.d_model), sd(cfg.d_model), cfg.dtype),
+        "kv_gain": g(1, D),
+        "w_qa": draw_normal(cfg.seed, T_V4 + 2, (0,), (cfg.q_rank, cfg.d_model), sd(cfg.d_model), cfg.dtype),
+        "q_gain": g(3, cfg.q_rank),
+        "w_qb": draw_normal(cfg.seed, T_V4 + 4, (0,), (H * D, cfg.q_rank), sd(cfg.q_rank), cfg.dtype),
+        "w_oa": draw_normal(cfg.seed, T_V4 + 5, (0,), (cfg.o_groups * cfg.o_rank, gdim), sd(gdim), cfg.dtype),
+        "w_ob": draw_normal(cfg.seed, T_V4 + 6, (0,), (cfg.d_model, cfg.o_groups * cfg.o_rank),
+                            sd(cfg.o_groups * cfg.o_rank), cfg.dtype),
+        "sink": draw_normal(cfg.seed, T_V4 + 7, (0,), (H,), 1.0, "f32"),
+    }
 
 
 def x_rows(cfg: MLAConfig, seq: int, start: int, stop: int, scale: float = 1.0,

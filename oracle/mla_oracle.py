@@ -37,6 +37,10 @@ named by their title / subject; equation numbers are the pages' own.
 * Beyond the attention itself (``lowrank_query``, ``output_projection``): the
   MLA principle page's low-rank query q_b_proj(q_a_layernorm(q_a_proj(x))) of its
   §"步骤", and its output projection o_proj, eqs. (3)/(6).
+* The nanowhale page's DeepSeek-V4 variant (``v4_*``): one normalised KV head
+  used as both key and value, the complex-form RoPE on its last dims with the
+  inverse rotation of the output, an attention sink, and the grouped low-rank
+  output projection.
 
 Readings taken where the pages are silent (each is listed in the design doc):
 rotate-half RoPE pairing (j, j + d_r/2) with θ_j = θ^(-2j/d_r) and the angle
@@ -257,6 +261,84 @@ def output_projection(o, w_o) -> np.ndarray:
     o [T, H, d_v]; W_o stored [d_model, H·d_v] (o_proj, [H·d_v -> hidden])."""
     o = _f64(o)
     return o.reshape(o.shape[0], -1) @ _f64(w_o).T
+
+
+# ----------------------------------------------------------------------------
+# DeepSeek-V4 / nanowhale variant: one latent head serves as both K and V
+# (page "MLA 在 nanowhale-100m 中的实现原理")
+# ----------------------------------------------------------------------------
+
+
+def rope_interleaved(y, pos, theta: float = 10000.0, inv_freq=None) -> np.ndarray:
+    """The nanowhale page's apply_rotary_emb(x, freqs_cis) (§"RoPE位置编码的优化应用"):
+    dims (2j, 2j+1) are the complex number y[2j] + i·y[2j+1], multiplied by
+    e^{i·p·f_j} with f_j = θ^(-2j/d) or a given inverse-frequency table (a
+    context-extension rescaling such as YaRN supplies its own table).  A negative
+    position rotates back (the page's inverse rotation of the output)."""
+    y = _f64(y)
+    d = y.shape[-1]
+    f = _f64(inv_freq) if inv_freq is not None else float(theta) ** (-2.0 * np.arange(d // 2, dtype=F64) / d)
+    ang = _f64(pos)[..., None] * f
+    while ang.ndim < y.ndim:
+        ang = np.expand_dims(ang, axis=-2)
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = y[..., 0::2], y[..., 1::2]
+    out = np.empty_like(y)
+    out[..., 0::2] = a * c - b * s
+    out[..., 1::2] = b * c + a * s
+    return out
+
+
+def v4_cache_rows(x, w_kv, kv_gain, pos, *, d_rope, eps, theta=10000.0, inv_freq=None) -> np.ndarray:
+    """kv = kv_norm(x·W_KVᵀ) (RMSNorm with gain over head_dim, §"单KV头多查询头设计"),
+    then the last d_rope dims rotated by the token's position (§"RoPE位置编码的优化应用").
+    W_KV [head_dim, d_model]; returns the cached rows [T, head_dim]."""
+    kv = rmsnorm(_f64(x) @ _f64(w_kv).T, eps) * _f64(kv_gain)
+    kv[:, -d_rope:] = rope_interleaved(kv[:, -d_rope:], pos, theta, inv_freq)
+    return kv
+
+
+def v4_query(x, w_qa, q_gain, w_qb, pos, *, n_heads, head_dim, d_rope, eps, theta=10000.0,
+             inv_freq=None) -> np.ndarray:
+    """q = wq_b(q_norm(wq_a(x))) viewed [H, head_dim] (§"低秩查询投影机制"), its last
+    d_rope dims rotated by the token's position.  Returns [T, H, head_dim]."""
+    c = rmsnorm(_f64(x) @ _f64(w_qa).T, eps) * _f64(q_gain)
+    q = (c @ _f64(w_qb).T).reshape(-1, n_heads, head_dim)
+    q[..., -d_rope:] = rope_interleaved(q[..., -d_rope:], pos, theta, inv_freq)
+    return q
+
+
+def v4_attention(q, kv, sink, q_pos, k_pos, q_seg, k_seg, scale, *, d_rope, theta=10000.0,
+                 inv_freq=None) -> np.ndarray:
+    """Multi-query attention with K = V = the cached row (§"高效注意力计算实现": SDPA of
+    q against kv_expanded for both keys and values, causal), a per-head attention
+    sink (a learned logit that joins each softmax's normalisation and carries no
+    value), and the inverse rotation of the output's last d_rope dims by the
+    query's position (§"RoPE位置编码的优化应用": rotation before and after attention).
+    q [T, H, D]; kv [S, D]; sink [H]; returns [T, H, D]."""
+    q, kv, sink = _f64(q), _f64(kv), _f64(sink)
+    allowed = (_f64(q_seg)[:, None] == _f64(k_seg)[None, :]) & (_f64(k_pos)[None, :] <= _f64(q_pos)[:, None])
+    a = scale * np.einsum("thd,sd->hts", q, kv)
+    a = np.where(allowed[None], a, -np.inf)
+    m = np.maximum(a.max(axis=-1), sink[:, None])                  # [H, T]
+    e = np.exp(a - m[..., None])
+    den = e.sum(axis=-1) + np.exp(sink[:, None] - m)
+    o = np.einsum("hts,sd->thd", e, kv) / den.T[..., None]
+    o[..., -d_rope:] = rope_interleaved(o[..., -d_rope:], -_f64(q_pos)[:, None], theta, inv_freq)
+    return o
+
+
+def v4_output(o, w_oa, w_ob, o_groups: int) -> np.ndarray:
+    """Grouped low-rank output projection (§"分组低秩输出投影"): the H·D outputs are cut
+    into o_groups groups, group g is projected by its own [o_rank, H·D/o_groups] block
+    of W_OA (rows g·o_rank ...), and the concatenated o_groups·o_rank values by W_OB
+    [d_model, o_groups·o_rank]."""
+    o = _f64(o)
+    T = o.shape[0]
+    og = o.reshape(T, o_groups, -1)
+    w = _f64(w_oa).reshape(o_groups, -1, og.shape[-1])
+    a = np.einsum("tgd,grd->tgr", og, w).reshape(T, -1)
+    return a @ _f64(w_ob).T
 
 
 def max_rel_err(got, ref) -> float:

@@ -537,3 +537,134 @@ def test_p8_output_projection_brute_and_page_chain():
     P /= P.sum(axis=1, keepdims=True)
     u_page = np.einsum("hdc,lc,hl,hdD->D", w["w_uv"], c, P, w_o.T.reshape(H, d_v, D))
     np.testing.assert_allclose(u_or, u_page, rtol=1e-11, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# P9: the DeepSeek-V4 / nanowhale variant
+# ----------------------------------------------------------------------------
+
+
+def test_p9_rope_interleaved_complex_form_and_inverse():
+    """Pairs (2j, 2j+1) times e^{i p f_j} (cmath), p = 0 identity, rotation by -p
+    undoes p, and a given frequency table equal to θ^(-2j/d) gives the same result."""
+    rng = np.random.default_rng(90)
+    y = rng.standard_normal(8)
+    p = 37.0
+    got = O.rope_interleaved(y, p, 10000.0)
+    for j in range(4):
+        z = complex(y[2 * j], y[2 * j + 1]) * cmath.exp(1j * p * 10000.0 ** (-2.0 * j / 8))
+        assert abs(got[2 * j] - z.real) < 1e-12 and abs(got[2 * j + 1] - z.imag) < 1e-12
+    np.testing.assert_allclose(O.rope_interleaved(y, 0.0), y, rtol=0, atol=0)
+    np.testing.assert_allclose(O.rope_interleaved(got, -p), y, rtol=1e-12, atol=1e-12)
+    table = 10000.0 ** (-2.0 * np.arange(4) / 8)
+    np.testing.assert_allclose(O.rope_interleaved(y, p, inv_freq=table), got, rtol=1e-14, atol=1e-14)
+
+
+def _v4_small(rng, T=5, D=6, dr=2, H=2):
+    q = rng.standard_normal((T, H, D))
+    kv = rng.standard_normal((T, D))
+    return q, kv
+
+
+def test_p9_v4_attention_brute_force_and_library():
+    """Scalar loops (sink in the denominator, K = V = the row, inverse rotation of
+    the output's rotary pair by the query position); with sink = -inf the
+    no-position dims equal torch's float64 SDPA of the expanded single head."""
+    rng = np.random.default_rng(91)
+    T, D, dr, H = 5, 6, 2, 2
+    q, kv = _v4_small(rng, T, D, dr, H)
+    sink = np.array([0.3, -1.2])
+    pos = np.arange(T)
+    seg = np.zeros(T, int)
+    scale = 0.7
+    got = O.v4_attention(q, kv, sink, pos, pos, seg, seg, scale, d_rope=dr)
+    for t in range(T):
+        for h in range(H):
+            s = [scale * sum(q[t, h, d] * kv[u, d] for d in range(D)) for u in range(t + 1)]
+            m = max(max(s), sink[h])
+            e = [math.exp(v - m) for v in s]
+            den = sum(e) + math.exp(sink[h] - m)
+            o = [sum(e[u] * kv[u, d] for u in range(t + 1)) / den for d in range(D)]
+            z = complex(o[D - 2], o[D - 1]) * cmath.exp(-1j * t * 1.0)   # f_0 = 1 for the single pair
+            ref = o[:D - 2] + [z.real, z.imag]
+            for d in range(D):
+                assert abs(got[t, h, d] - ref[d]) < 1e-12
+    no_sink = O.v4_attention(q, kv, np.full(H, -np.inf), pos, pos, seg, seg, scale, d_rope=dr)
+    Q = torch.from_numpy(q).permute(1, 0, 2)[None]
+    K = torch.from_numpy(np.repeat(kv[:, None], H, 1)).permute(1, 0, 2)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, K, is_causal=True, scale=scale)[0]
+    np.testing.assert_allclose(no_sink[..., :D - dr], ref.permute(1, 0, 2).numpy()[..., :D - dr],
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_p9_v4_attention_closed_form_and_relative_positions():
+    """One key: o = kv_0·e^s / (e^s + e^sink) on the no-position dims.  Rotating q and
+    kv by their positions, then the output back by the query's, makes the output
+    depend on relative positions only: shifting every position changes nothing."""
+    rng = np.random.default_rng(92)
+    D, dr, H = 8, 4, 3
+    q = rng.standard_normal((1, H, D))
+    kv = rng.standard_normal((1, D))
+    sink = rng.standard_normal(H)
+    o = O.v4_attention(q, kv, sink, [0], [0], [0], [0], 0.5, d_rope=dr)
+    for h in range(H):
+        s = 0.5 * float(q[0, h] @ kv[0])
+        w = math.exp(s) / (math.exp(s) + math.exp(sink[h]))
+        np.testing.assert_allclose(o[0, h, :D - dr], w * kv[0, :D - dr], rtol=1e-13)
+    # relative positions: rows built from position-free parts, rotated at p and p + 1000
+    T = 6
+    qa = rng.standard_normal((T, H, D))
+    ka = rng.standard_normal((T, D))
+    seg = np.zeros(T, int)
+    outs = []
+    for shift in (0, 1000):
+        pos = np.arange(T) + shift
+        qq, kk = qa.copy(), ka.copy()
+        qq[..., -dr:] = O.rope_interleaved(qa[..., -dr:], pos[:, None], 10000.0)
+        kk[:, -dr:] = O.rope_interleaved(ka[:, -dr:], pos, 10000.0)
+        outs.append(O.v4_attention(qq, kk, sink, pos, pos, seg, seg, 0.4, d_rope=dr))
+    np.testing.assert_allclose(outs[0], outs[1], rtol=1e-9, atol=1e-11)
+
+
+def test_p9_v4_projections_brute_force():
+    """Cache rows (RMSNorm with gain, rotary tail), queries (low-rank, per-head rotary
+    tail) and the grouped output projection against scalar loops; one output group
+    is two plain products."""
+    rng = np.random.default_rng(93)
+    d_model, D, dr, H, qr, G, R = 5, 4, 2, 2, 3, 2, 3
+    x = rng.standard_normal((3, d_model))
+    pos = np.array([0, 2, 9])
+    w_kv = rng.standard_normal((D, d_model))
+    g_kv = 1 + 0.1 * rng.standard_normal(D)
+    rows = O.v4_cache_rows(x, w_kv, g_kv, pos, d_rope=dr, eps=1e-6)
+    for t in range(3):
+        v = [sum(x[t, k] * w_kv[i, k] for k in range(d_model)) for i in range(D)]
+        inv = 1 / math.sqrt(sum(a * a for a in v) / D + 1e-6)
+        v = [v[i] * inv * g_kv[i] for i in range(D)]
+        z = complex(v[2], v[3]) * cmath.exp(1j * pos[t])
+        ref = v[:2] + [z.real, z.imag]
+        np.testing.assert_allclose(rows[t], ref, rtol=1e-12, atol=1e-13)
+    w_qa = rng.standard_normal((qr, d_model))
+    g_q = 1 + 0.1 * rng.standard_normal(qr)
+    w_qb = rng.standard_normal((H * D, qr))
+    q = O.v4_query(x, w_qa, g_q, w_qb, pos, n_heads=H, head_dim=D, d_rope=dr, eps=1e-6)
+    for t in range(3):
+        c = [sum(x[t, k] * w_qa[i, k] for k in range(d_model)) for i in range(qr)]
+        inv = 1 / math.sqrt(sum(a * a for a in c) / qr + 1e-6)
+        c = [c[i] * inv * g_q[i] for i in range(qr)]
+        for h in range(H):
+            v = [sum(c[i] * w_qb[h * D + d, i] for i in range(qr)) for d in range(D)]
+            z = complex(v[2], v[3]) * cmath.exp(1j * pos[t])
+            np.testing.assert_allclose(q[t, h], v[:2] + [z.real, z.imag], rtol=1e-12, atol=1e-13)
+    o = rng.standard_normal((3, H, D))
+    gdim = H * D // G
+    w_oa = rng.standard_normal((G * R, gdim))
+    w_ob = rng.standard_normal((d_model, G * R))
+    u = O.v4_output(o, w_oa, w_ob, G)
+    flat = o.reshape(3, -1)
+    for t in range(3):
+        a = [sum(flat[t, g * gdim + d] * w_oa[g * R + r, d] for d in range(gdim)) for g in range(G) for r in range(R)]
+        for j in range(d_model):
+            assert abs(u[t, j] - sum(a[i] * w_ob[j, i] for i in range(G * R))) < 1e-11
+    w1 = rng.standard_normal((R, H * D))
+    np.testing.assert_allclose(O.v4_output(o, w1, w_ob[:, :R], 1), (flat @ w1.T) @ w_ob[:, :R].T, rtol=1e-12)
