@@ -13,10 +13,15 @@ its calls:
     mla_prefill_expanded — causal prefill in the original order (k_nope, v expanded)
     mla_absorb_lowrank / mla_query_lowrank — the low-rank query path (W_QA, RMSNorm, W_QB)
     mla_output       — the output projection W_o after W_UV
+    mla_v4_*         — the DeepSeek-V4 / nanowhale variant (one KV head as key and value,
+                       attention sink, inverse rotation of the output, grouped output)
 
 Build the library with ``python -m head_latent_attention_kv_amd.build``.
 """
 from ._abi import (  # noqa: F401
+    MLA_V4_OP_DECODE, MLA_V4_OP_OUTPUT, MLA_V4_OP_PREFILL, MLA_V4_OP_QUERY, MLA_V4_OP_WRITE_CACHE, MlaV4Dims,
+    mla_v4_decode, mla_v4_output, mla_v4_prefill, mla_v4_query, mla_v4_workspace_size, mla_v4_write_cache,
+    v4_dims_of,
     MLA_BF16, MLA_EHIP, MLA_EINVAL, MLA_ENOTSUP, MLA_EWORKSPACE, MLA_F32, MLA_OK, MLA_OP_ABSORB,
     MLA_OP_DECODE, MLA_OP_OUTPUT, MLA_OP_PREFILL, MLA_OP_PREFILL_EXPANDED, MLA_OP_QUERY, MLA_OP_WRITE_CACHE,
     MlaDims, MlaError, dims_of, load, make_dims, mla_absorb, mla_absorb_lowrank, mla_decode,
@@ -30,4 +35,6 @@ __all__ = [
     "mla_decode_partials", "mla_decode_split_rows", "mla_decode_splits", "mla_prefill",
     "mla_prefill_expanded", "mla_query", "mla_workspace_size", "mla_write_cache", "strerror",
     "mla_absorb_lowrank", "mla_query_lowrank", "mla_lowrank_workspace_size", "mla_output",
+    "MlaV4Dims", "v4_dims_of", "mla_v4_write_cache", "mla_v4_query", "mla_v4_decode", "mla_v4_prefill",
+    "mla_v4_output", "mla_v4_workspace_size",
 ]

@@ -29,7 +29,19 @@ class MlaDims(ctypes.Structure):
     ]
 
 
+class MlaV4Dims(ctypes.Structure):
+    _fields_ = [
+        ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("d_rope", ctypes.c_int32), ("q_rank", ctypes.c_int32), ("o_groups", ctypes.c_int32),
+        ("o_rank", ctypes.c_int32), ("dtype", ctypes.c_int32), ("rms_eps", ctypes.c_float),
+        ("softmax_scale", ctypes.c_float), ("rope_theta", ctypes.c_double),
+    ]
+
+
+MLA_V4_OP_WRITE_CACHE, MLA_V4_OP_QUERY, MLA_V4_OP_DECODE, MLA_V4_OP_PREFILL, MLA_V4_OP_OUTPUT = range(5)
+
 _PD = ctypes.POINTER(MlaDims)
+_P4 = ctypes.POINTER(MlaV4Dims)
 SIGNATURES = {
     "mla_workspace_size": (_sz, [_PD, ctypes.c_int, _i32, _i64, _i32]),
     "mla_check_dims": (ctypes.c_int, [_PD]),
@@ -48,6 +60,13 @@ SIGNATURES = {
                                           _vp]),
     "mla_query_lowrank": (ctypes.c_int, [_PD, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "mla_output": (ctypes.c_int, [_PD, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "mla_v4_check_dims": (ctypes.c_int, [_P4]),
+    "mla_v4_workspace_size": (_sz, [_P4, ctypes.c_int, _i32, _i64, _i32]),
+    "mla_v4_write_cache": (ctypes.c_int, [_P4, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "mla_v4_query": (ctypes.c_int, [_P4, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "mla_v4_decode": (ctypes.c_int, [_P4, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mla_v4_prefill": (ctypes.c_int, [_P4, _vp, _vp, _vp, _i32, _i64, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mla_v4_output": (ctypes.c_int, [_P4, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "mla_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_version": (ctypes.c_int, []),
 }
@@ -301,6 +320,95 @@ def mla_output(dims, attn, w_o, out, workspace=None, stream=None):
     _check("mla_output", load().mla_output(
         ctypes.byref(dims), _ptr(attn, "attn", et), _ptr(w_o, "w_o", et), T, _ptr(out, "out", et),
         _ptr(ws, "workspace"), nbytes, _stream(stream)))
+    return out
+
+
+# ---- DeepSeek-V4 / nanowhale variant ----------------------------------------------
+
+
+def v4_dims_of(cfg) -> MlaV4Dims:
+    return MlaV4Dims(cfg.d_model, cfg.n_heads, cfg.head_dim, cfg.d_rope, cfg.q_rank, cfg.o_groups, cfg.o_rank,
+                     MLA_F32 if cfg.dtype == "f32" else MLA_BF16, cfg.rms_eps, 0.0, cfg.rope_theta)
+
+
+def mla_v4_workspace_size(dims: MlaV4Dims, op: int, batch: int = 0, n_tokens: int = 0, max_len: int = 0) -> int:
+    return int(load().mla_v4_workspace_size(ctypes.byref(dims), op, batch, n_tokens, max_len))
+
+
+def _v4_ws(dims, op, batch, n_tokens, max_len, workspace, device):
+    if workspace is None:
+        torch = _torch()
+        need = mla_v4_workspace_size(dims, op, batch, n_tokens, max_len)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _v4_et(dims):
+    torch = _torch()
+    return torch.float32 if dims.dtype == MLA_F32 else torch.bfloat16
+
+
+def mla_v4_write_cache(dims, x, w_kv, kv_gain, positions, slots, cache, rope_freqs=None, workspace=None,
+                       stream=None):
+    torch = _torch()
+    et = _v4_et(dims)
+    T = x.shape[0]
+    ws, nbytes = _v4_ws(dims, MLA_V4_OP_WRITE_CACHE, 0, T, 0, workspace, x.device)
+    _check("mla_v4_write_cache", load().mla_v4_write_cache(
+        ctypes.byref(dims), _ptr(x, "x", et), _ptr(w_kv, "w_kv", et), _ptr(kv_gain, "kv_gain", et),
+        _ptr(positions, "positions", torch.int32), _ptr(slots, "slots", torch.int64), T, _ptr(cache, "cache", et),
+        cache.shape[0], _ptr(rope_freqs, "rope_freqs", torch.float64), _ptr(ws, "workspace"), nbytes,
+        _stream(stream)))
+    return cache
+
+
+def mla_v4_query(dims, x, w_qa, q_gain, w_qb, positions, q, rope_freqs=None, workspace=None, stream=None):
+    torch = _torch()
+    et = _v4_et(dims)
+    T = x.shape[0]
+    ws, nbytes = _v4_ws(dims, MLA_V4_OP_QUERY, 0, T, 0, workspace, x.device)
+    _check("mla_v4_query", load().mla_v4_query(
+        ctypes.byref(dims), _ptr(x, "x", et), _ptr(w_qa, "w_qa", et), _ptr(q_gain, "q_gain", et),
+        _ptr(w_qb, "w_qb", et), _ptr(positions, "positions", torch.int32), T,
+        _ptr(rope_freqs, "rope_freqs", torch.float64), _ptr(q, "q", et), _ptr(ws, "workspace"), nbytes,
+        _stream(stream)))
+    return q
+
+
+def mla_v4_decode(dims, q, cache, seq_start, seq_len, max_len, sink, out, rope_freqs=None, workspace=None,
+                  stream=None):
+    torch = _torch()
+    et = _v4_et(dims)
+    B = q.shape[0]
+    ws, nbytes = _v4_ws(dims, MLA_V4_OP_DECODE, B, 0, max_len, workspace, q.device)
+    _check("mla_v4_decode", load().mla_v4_decode(
+        ctypes.byref(dims), _ptr(q, "q", et), _ptr(cache, "cache", et), _ptr(seq_start, "seq_start", torch.int64),
+        _ptr(seq_len, "seq_len", torch.int32), B, int(max_len), _ptr(sink, "sink", torch.float32),
+        _ptr(rope_freqs, "rope_freqs", torch.float64), _ptr(out, "out", et), _ptr(ws, "workspace"), nbytes,
+        _stream(stream)))
+    return out
+
+
+def mla_v4_prefill(dims, q, cache, cu_seqlens, max_len, sink, out, rope_freqs=None, workspace=None, stream=None):
+    torch = _torch()
+    et = _v4_et(dims)
+    T = q.shape[0]
+    B = cu_seqlens.shape[0] - 1
+    ws, nbytes = _v4_ws(dims, MLA_V4_OP_PREFILL, B, T, max_len, workspace, q.device)
+    _check("mla_v4_prefill", load().mla_v4_prefill(
+        ctypes.byref(dims), _ptr(q, "q", et), _ptr(cache, "cache", et), _ptr(cu_seqlens, "cu_seqlens", torch.int64),
+        B, T, int(max_len), _ptr(sink, "sink", torch.float32), _ptr(rope_freqs, "rope_freqs", torch.float64),
+        _ptr(out, "out", et), _ptr(ws, "workspace"), nbytes, _stream(stream)))
+    return out
+
+
+def mla_v4_output(dims, attn, w_oa, w_ob, out, workspace=None, stream=None):
+    et = _v4_et(dims)
+    T = attn.shape[0]
+    ws, nbytes = _v4_ws(dims, MLA_V4_OP_OUTPUT, 0, T, 0, workspace, attn.device)
+    _check("mla_v4_output", load().mla_v4_output(
+        ctypes.byref(dims), _ptr(attn, "attn", et), _ptr(w_oa, "w_oa", et), _ptr(w_ob, "w_ob", et), T,
+        _ptr(out, "out", et), _ptr(ws, "workspace"), nbytes, _stream(stream)))
     return out
 
 

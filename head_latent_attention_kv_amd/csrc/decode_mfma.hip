@@ -427,7 +427,8 @@ void launch(const AttnShape& sh, const void* q_lat, const void* q_pe, const void
 #define MLA_DECODE_SHAPES(X)                                                                  \
   X(512, 576, 4, 2, 4, 113, 128) /* H = 128, G = 1, d_rope = 64 (DeepSeek-V2)          */ \
   X(512, 544, 2, 1, 4, 17, 32)   /* H = 32, G = 4, d_rope = 8 (Qwen3-30B-A3B MLA delta) */ \
-  X(128, 160, 2, 1, 3, 17, 32)   /* H = 28, G = 4, d_rope = 8 (Qwen2.5-7B MLA delta)    */
+  X(128, 160, 2, 1, 3, 17, 32)   /* H = 28, G = 4, d_rope = 8 (Qwen2.5-7B MLA delta)    */ \
+  X(512, 512, 1, 1, 4, 1, 16)    /* one 512-wide KV head as key and value (DeepSeek-V4)  */
 
 }  // namespace
 

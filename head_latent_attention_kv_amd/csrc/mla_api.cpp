@@ -763,3 +763,319 @@ int mla_output(const mla_dims* dims, const void* attn, const void* w_o, int64_t 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// DeepSeek-V4 variant
+// ---------------------------------------------------------------------------
+namespace {
+
+int v4_check(const mla_v4_dims* d) {
+  if (!d) return MLA_EINVAL;
+  if (d->d_model <= 0 || d->n_heads <= 0 || d->head_dim <= 0 || d->d_rope < 0 || d->q_rank <= 0 ||
+      d->o_groups <= 0 || d->o_rank <= 0)
+    return MLA_EINVAL;
+  if (d->d_rope % 2 != 0 || d->d_rope > d->head_dim) return MLA_EINVAL;
+  if ((static_cast<int64_t>(d->n_heads) * d->head_dim) % d->o_groups != 0) return MLA_EINVAL;
+  if (d->dtype != MLA_F32 && d->dtype != MLA_BF16) return MLA_EINVAL;
+  if (!(d->rms_eps >= 0.f) || !isfinite(d->rms_eps)) return MLA_EINVAL;
+  if (isnan(d->softmax_scale) || isinf(d->softmax_scale)) return MLA_EINVAL;
+  if (!(d->rope_theta > 0.0) || !isfinite(d->rope_theta)) return MLA_EINVAL;
+  const int64_t gdim = static_cast<int64_t>(d->n_heads) * d->head_dim / d->o_groups;
+  if (d->dtype != MLA_BF16 || d->head_dim > 512 || d->head_dim % 16 != 0 || d->d_model % 8 != 0 ||
+      d->q_rank % 8 != 0 || !mla::norm_rows_supported(d->q_rank) || d->o_rank % 8 != 0 || gdim % 8 != 0 ||
+      !mla::v4_rows_supported(d->head_dim, d->d_rope))
+    return MLA_ENOTSUP;
+  return MLA_OK;
+}
+
+// The projection helpers above only look at the element type.
+mla_dims v4_shadow(const mla_v4_dims* d) {
+  mla_dims s{};
+  s.d_model = d->d_model;
+  s.dtype = d->dtype;
+  return s;
+}
+
+AttnShape v4_shape(const mla_v4_dims* d) {
+  AttnShape s;
+  s.H = d->n_heads;
+  s.G = 1;
+  s.r = d->head_dim;
+  s.d_rope = 0;  // the rotary dims are inside the row
+  s.row_w = d->head_dim;
+  s.scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf(static_cast<float>(d->head_dim));
+  return s;
+}
+
+struct V4Decode {
+  bool mfma;
+  int n_split, split_len;
+  size_t part_o, part_ml;
+};
+
+V4Decode v4_decode_plan(const mla_v4_dims* d, int32_t batch, int32_t max_len) {
+  V4Decode p{};
+  const AttnShape sh = v4_shape(d);
+  p.mfma = mla::decode_mfma_supported(sh);
+  const int64_t B = std::max<int32_t>(batch, 0);
+  const int L = std::max<int32_t>(max_len, 1);
+  const int64_t per = p.mfma ? B : B * ((sh.H + mla::generic_head_block() - 1) / mla::generic_head_block());
+  const int64_t target = p.mfma ? mla::decode_mfma_blocks_per_cu(sh) * kCUs : 2 * kCUs;
+  int64_t ns = per > 0 ? (target + per - 1) / per : 1;
+  ns = std::max<int64_t>(1, std::min<int64_t>(ns, std::max<int64_t>(1, L / 256)));
+  p.split_len = split_rows(L, ns);
+  p.n_split = (L + p.split_len - 1) / p.split_len;
+  p.part_o = align_up(static_cast<size_t>(B) * p.n_split * sh.H * d->head_dim * 2);
+  p.part_ml = align_up(static_cast<size_t>(B) * p.n_split * sh.H * 2 * sizeof(float));
+  return p;
+}
+
+struct V4Query {
+  size_t cq, cqn, q;
+  size_t total() const { return cq + cqn + q; }
+};
+V4Query v4_query_ws(const mla_v4_dims* d, int64_t T) {
+  const mla_dims sh = v4_shadow(d);
+  V4Query w{};
+  w.cq = proj_bytes_k(&sh, d->q_rank, d->d_model, T, lowrank_ld(d->q_rank));
+  w.cqn = align_up(static_cast<size_t>(T) * d->q_rank * 2);
+  w.q = proj_bytes_k(&sh, d->n_heads * d->head_dim, d->q_rank, T, static_cast<int64_t>(d->n_heads) * d->head_dim);
+  return w;
+}
+
+struct V4Out {
+  int splits_a;
+  int64_t sps_a;
+  size_t a_slices, a, u;
+  size_t total() const { return a_slices + a + u; }
+};
+V4Out v4_out_ws(const mla_v4_dims* d, int64_t T) {
+  const mla_dims sh = v4_shadow(d);
+  V4Out w{};
+  const int gr = d->o_groups * d->o_rank;
+  w.a = align_up(static_cast<size_t>(T) * gr * 2);
+  if (skinny_ok(&sh, T)) {
+    const int gdim = d->n_heads * d->head_dim / d->o_groups;
+    w.splits_a = mla::skinny_splits(static_cast<int>(T), d->o_rank, d->o_groups, gdim);
+    w.sps_a = static_cast<int64_t>(align_up(static_cast<size_t>(T) * gr * sizeof(float)) / sizeof(float));
+    w.a_slices = static_cast<size_t>(w.splits_a) * w.sps_a * sizeof(float);
+    w.u = proj_bytes_k(&sh, d->d_model, gr, T, out_width(&sh));
+  }
+  return w;
+}
+
+size_t v4_ws(const mla_v4_dims* d, int op, int32_t batch, int64_t n_tokens, int32_t max_len) {
+  const mla_dims sh = v4_shadow(d);
+  const int64_t T = std::max<int64_t>(n_tokens, 0);
+  switch (op) {
+    case MLA_V4_OP_WRITE_CACHE: return proj_bytes_k(&sh, d->head_dim, d->d_model, T, d->head_dim);
+    case MLA_V4_OP_QUERY: return v4_query_ws(d, T).total();
+    case MLA_V4_OP_DECODE: {
+      const V4Decode p = v4_decode_plan(d, batch, max_len);
+      return p.part_o + p.part_ml;
+    }
+    case MLA_V4_OP_PREFILL:
+      return align_up(static_cast<size_t>(T) * d->n_heads * d->head_dim * 2) +
+             align_up(static_cast<size_t>(T) * d->n_heads * 2 * sizeof(float));
+    case MLA_V4_OP_OUTPUT: return v4_out_ws(d, T).total();
+    default: return 0;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_v4_check_dims(const mla_v4_dims* dims) { return v4_check(dims); }
+
+size_t mla_v4_workspace_size(const mla_v4_dims* dims, int op, int32_t batch, int64_t n_tokens,
+                             int32_t max_len) {
+  if (v4_check(dims) != MLA_OK) return 0;
+  return v4_ws(dims, op, batch, n_tokens, max_len);
+}
+
+int mla_v4_write_cache(const mla_v4_dims* dims, const void* x, const void* w_kv, const void* kv_gain,
+                       const int32_t* positions, const int64_t* slots, int64_t n_tokens, void* cache,
+                       int64_t cache_rows, const double* rope_freqs, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int st = v4_check(dims);
+  if (st != MLA_OK) return st;
+  if (n_tokens < 0 || cache_rows < 0) return MLA_EINVAL;
+  if (n_tokens == 0) return MLA_OK;
+  if (n_tokens > INT32_MAX) return MLA_ENOTSUP;
+  if (!ptr_ok(x) || !ptr_ok(w_kv) || !ptr_ok(kv_gain) || !ptr_ok(positions) || !ptr_ok(slots) ||
+      !ptr_ok(cache) || !ptr_ok(workspace) || (rope_freqs != nullptr && !ptr_ok(rope_freqs)))
+    return MLA_EINVAL;
+  if (workspace_bytes < v4_ws(dims, MLA_V4_OP_WRITE_CACHE, 0, n_tokens, 0)) return MLA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const mla_dims sh = v4_shadow(dims);
+  float* proj = static_cast<float*>(workspace);
+  const int D = dims->head_dim;
+  const Proj p = proj_one(&sh, x, dims->d_model, dims->d_model, w_kv, D, proj, D, n_tokens, s);
+  mla::v4_rows(dims->dtype, proj, D, p.splits, p.sps, 1, D, dims->d_rope, /*norm=*/1, kv_gain, dims->rms_eps,
+               positions, slots, dims->rope_theta, rope_freqs, cache, n_tokens, s);
+  return launch_status();
+}
+
+int mla_v4_query(const mla_v4_dims* dims, const void* x, const void* w_qa, const void* q_gain,
+                 const void* w_qb, const int32_t* positions, int64_t n_tokens, const double* rope_freqs,
+                 void* q, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = v4_check(dims);
+  if (st != MLA_OK) return st;
+  if (n_tokens < 0) return MLA_EINVAL;
+  if (n_tokens == 0) return MLA_OK;
+  if (n_tokens > INT32_MAX) return MLA_ENOTSUP;
+  if (!ptr_ok(x) || !ptr_ok(w_qa) || !ptr_ok(q_gain) || !ptr_ok(w_qb) || !ptr_ok(positions) || !ptr_ok(q) ||
+      !ptr_ok(workspace) || (rope_freqs != nullptr && !ptr_ok(rope_freqs)))
+    return MLA_EINVAL;
+  const V4Query w = v4_query_ws(dims, n_tokens);
+  if (workspace_bytes < w.total()) return MLA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const mla_dims sh = v4_shadow(dims);
+  char* base = static_cast<char*>(workspace);
+  float* cq = reinterpret_cast<float*>(base);
+  void* cqn = base + w.cq;
+  float* qp = reinterpret_cast<float*>(base + w.cq + w.cqn);
+  const int64_t ldq = lowrank_ld(dims->q_rank);
+  const Proj p1 = proj_one(&sh, x, dims->d_model, dims->d_model, w_qa, dims->q_rank, cq, ldq, n_tokens, s);
+  mla::norm_rows(dims->dtype, cq, ldq, p1.splits, p1.sps, dims->q_rank, q_gain, dims->rms_eps, cqn,
+                 dims->q_rank, n_tokens, s);
+  const int HD = dims->n_heads * dims->head_dim;
+  const Proj p2 = proj_one(&sh, cqn, dims->q_rank, dims->q_rank, w_qb, HD, qp, HD, n_tokens, s);
+  mla::v4_rows(dims->dtype, qp, HD, p2.splits, p2.sps, dims->n_heads, dims->head_dim, dims->d_rope, /*norm=*/0,
+               nullptr, 0.f, positions, nullptr, dims->rope_theta, rope_freqs, q, n_tokens, s);
+  return launch_status();
+}
+
+int mla_v4_decode(const mla_v4_dims* dims, const void* q, const void* cache, const int64_t* seq_start,
+                  const int32_t* seq_len, int32_t batch, int32_t max_len, const float* sink,
+                  const double* rope_freqs, void* out, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  int st = v4_check(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0) return MLA_EINVAL;
+  if (batch == 0) return MLA_OK;
+  if (max_len <= 0) return MLA_EINVAL;
+  if (!ptr_ok(q) || !ptr_ok(cache) || !ptr_ok(seq_start) || !ptr_ok(seq_len) || !ptr_ok(sink) || !ptr_ok(out) ||
+      !ptr_ok(workspace) || (rope_freqs != nullptr && !ptr_ok(rope_freqs)))
+    return MLA_EINVAL;
+  const V4Decode p = v4_decode_plan(dims, batch, max_len);
+  if (workspace_bytes < p.part_o + p.part_ml) return MLA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const AttnShape sh = v4_shape(dims);
+  char* base = static_cast<char*>(workspace);
+  void* part_o = base;
+  float* part_ml = reinterpret_cast<float*>(base + p.part_o);
+  if (p.mfma)
+    mla::decode_mfma(sh, q, nullptr, cache, seq_start, seq_len, batch, p.n_split, p.split_len, part_o, part_ml,
+                     nullptr, s);
+  else
+    mla::attend_generic(dims->dtype, sh, q, nullptr, cache, seq_start, seq_len, nullptr, batch, batch,
+                        p.n_split, p.split_len, part_o, part_ml, nullptr, s);
+  mla::v4_merge(dims->dtype, part_o, part_ml, batch, p.n_split, sh.H, dims->head_dim, dims->d_rope, sink,
+                seq_len, nullptr, batch, dims->rope_theta, rope_freqs, out, s);
+  return launch_status();
+}
+
+int mla_v4_prefill(const mla_v4_dims* dims, const void* q, const void* cache, const int64_t* cu_seqlens,
+                   int32_t batch, int64_t n_tokens, int32_t max_len, const float* sink,
+                   const double* rope_freqs, void* out, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  int st = v4_check(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || n_tokens < 0) return MLA_EINVAL;
+  if (batch == 0 || n_tokens == 0) return MLA_OK;
+  if (max_len <= 0) return MLA_EINVAL;
+  if (n_tokens > INT32_MAX) return MLA_ENOTSUP;
+  if (!ptr_ok(q) || !ptr_ok(cache) || !ptr_ok(cu_seqlens) || !ptr_ok(sink) || !ptr_ok(out) ||
+      !ptr_ok(workspace) || (rope_freqs != nullptr && !ptr_ok(rope_freqs)))
+    return MLA_EINVAL;
+  if (workspace_bytes < v4_ws(dims, MLA_V4_OP_PREFILL, batch, n_tokens, max_len)) return MLA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const AttnShape sh = v4_shape(dims);
+  char* base = static_cast<char*>(workspace);
+  void* part_o = base;
+  float* part_ml = reinterpret_cast<float*>(
+      base + align_up(static_cast<size_t>(n_tokens) * dims->n_heads * dims->head_dim * 2));
+  mla::attend_generic(dims->dtype, sh, q, nullptr, cache, nullptr, nullptr, cu_seqlens, batch, n_tokens, 1,
+                      max_len, part_o, part_ml, nullptr, s);
+  mla::v4_merge(dims->dtype, part_o, part_ml, n_tokens, 1, sh.H, dims->head_dim, dims->d_rope, sink, nullptr,
+                cu_seqlens, batch, dims->rope_theta, rope_freqs, out, s);
+  return launch_status();
+}
+
+int mla_v4_output(const mla_v4_dims* dims, const void* attn, const void* w_oa, const void* w_ob,
+                  int64_t n_tokens, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = v4_check(dims);
+  if (st != MLA_OK) return st;
+  if (n_tokens < 0) return MLA_EINVAL;
+  if (n_tokens == 0) return MLA_OK;
+  if (n_tokens > INT32_MAX) return MLA_ENOTSUP;
+  if (!ptr_ok(attn) || !ptr_ok(w_oa) || !ptr_ok(w_ob) || !ptr_ok(out) || !ptr_ok(workspace)) return MLA_EINVAL;
+  const V4Out w = v4_out_ws(dims, n_tokens);
+  if (workspace_bytes < w.total()) return MLA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const mla_dims sh = v4_shadow(dims);
+  const int G = dims->o_groups, R = dims->o_rank, HD = dims->n_heads * dims->head_dim, gdim = HD / G;
+  const int T = static_cast<int>(n_tokens);
+  char* base = static_cast<char*>(workspace);
+  float* a_sl = reinterpret_cast<float*>(base);
+  void* a = base + w.a_slices;
+  float* u_sl = reinterpret_cast<float*>(base + w.a_slices + w.a);
+  if (w.a_slices > 0) {
+    // few tokens: each group's W_OA block streamed once, K slices in fp32
+    mla::SkinnyArgs sa{};
+    sa.A = attn;
+    sa.sAz = gdim;
+    sa.sAm = HD;
+    sa.B0 = sa.B1 = static_cast<const uint16_t*>(w_oa);
+    sa.N0 = R;
+    sa.sBz = static_cast<int64_t>(R) * gdim;
+    sa.sBo = gdim;
+    sa.C = a_sl;
+    sa.sCz = R;
+    sa.sCm = static_cast<int64_t>(G) * R;
+    sa.sPs = w.sps_a;
+    sa.M = T;
+    sa.N = R;
+    sa.K = gdim;
+    sa.Z = G;
+    sa.splits = w.splits_a;
+    mla::gemm_skinny(sa, /*a_f32=*/false, /*out_bf16=*/false, s);
+    mla::sum_cast_slices(dims->dtype, a_sl, w.splits_a, w.sps_a, T, G * R, static_cast<int64_t>(G) * R, a, s);
+    const int64_t ld = out_width(&sh);
+    const Proj p = proj_one(&sh, a, G * R, G * R, w_ob, dims->d_model, u_sl, ld, n_tokens, s);
+    mla::sum_cast_slices(dims->dtype, u_sl, p.splits, p.sps, T, dims->d_model, ld, out, s);
+  } else {
+    GemmArgs g{};
+    g.A = attn;
+    g.sAz = gdim;
+    g.sAm = HD;
+    g.B = w_oa;
+    g.sBz = static_cast<int64_t>(R) * gdim;
+    g.sBo = gdim;
+    g.C = a;
+    g.sCz = R;
+    g.sCm = static_cast<int64_t>(G) * R;
+    g.M = T;
+    g.N = R;
+    g.K = gdim;
+    g.Z = G;
+    mla::gemm(g, dims->dtype, false, false, /*out_bf16=*/true, s);
+    GemmArgs g2{};
+    g2.A = a;
+    g2.sAm = static_cast<int64_t>(G) * R;
+    g2.B = w_ob;
+    g2.sBo = static_cast<int64_t>(G) * R;
+    g2.C = out;
+    g2.sCm = dims->d_model;
+    g2.M = T;
+    g2.N = dims->d_model;
+    g2.K = G * R;
+    g2.Z = 1;
+    mla::gemm(g2, dims->dtype, false, false, /*out_bf16=*/true, s);
+  }
+  return launch_status();
+}
+
+}  // extern "C"

@@ -70,17 +70,26 @@ __device__ __forceinline__ float wave_sum(float v) {
 // double; the angle p·base^j is formed and reduced to [-π, π] in double, since
 // an fp32 angle at p ~ 1e5 is off by ~1e-2 rad.  Only the reduced angle goes
 // through fp32 sin/cos (error ~1e-7 for |x| <= π).
-__device__ __forceinline__ void rope_cos_sin(int32_t pos, int j, double base, float* c, float* s) {
+__device__ __forceinline__ void angle_cos_sin(double ang, float* c, float* s) {
+  constexpr double kTwoPi = 6.283185307179586476925;
+  const double k = rint(ang * (1.0 / kTwoPi));
+  const float r = static_cast<float>(fma(-k, kTwoPi, ang));
+  sincosf(r, s, c);
+}
+
+// Frequency of rotary pair j: base^j (base = θ^(-2/d)), or freqs[j] from a table.
+__device__ __forceinline__ double rope_freq(int j, double base, const double* freqs) {
+  if (freqs != nullptr) return freqs[j];
   double f = 1.0, b = base;
   for (int e = j; e != 0; e >>= 1) {
     if (e & 1) f *= b;
     b *= b;
   }
-  const double ang = static_cast<double>(pos) * f;
-  constexpr double kTwoPi = 6.283185307179586476925;
-  const double k = rint(ang * (1.0 / kTwoPi));
-  const float r = static_cast<float>(fma(-k, kTwoPi, ang));
-  sincosf(r, s, c);
+  return f;
+}
+
+__device__ __forceinline__ void rope_cos_sin(int32_t pos, int j, double base, float* c, float* s) {
+  angle_cos_sin(static_cast<double>(pos) * rope_freq(j, base, nullptr), c, s);
 }
 
 }  // namespace mla

@@ -132,4 +132,18 @@ void prefill_expanded(const AttnShape& sh, const void* q_nope, const void* q_pe,
                       const void* v, const void* cache, const int64_t* cu, int batch, int64_t n_tokens,
                       void* out, hipStream_t s);
 
+// DeepSeek-V4 variant (v4.hip).  Rows of width D from fp32 projections (K-slice
+// sum): optional RMSNorm (norm != 0) with gain (null: unit), complex-form RoPE of the last
+// d_rope dims at positions[t]; row r = (t = r / heads, h = r % heads) reads
+// proj[t*ld + h*D], writes out[(slots ? slots[t] : r) * D].
+bool v4_rows_supported(int D, int d_rope);
+void v4_rows(int dtype, const float* proj, int64_t ld, int splits, int64_t sps, int heads, int D, int d_rope,
+             int norm, const void* gain, float eps, const int32_t* positions, const int64_t* slots, double theta,
+             const double* freqs, void* out, int64_t n_tokens, hipStream_t s);
+// Split merge with the attention sink, then the inverse rotation of the last
+// d_rope dims by the query position (decode: seq_len[q] - 1; prefill: offset in cu).
+void v4_merge(int dtype, const void* part_o, const float* part_ml, int64_t n_q, int n_split, int H, int D,
+              int d_rope, const float* sink, const int32_t* seq_len, const int64_t* cu, int batch, double theta,
+              const double* freqs, void* out, hipStream_t s);
+
 }  // namespace mla

@@ -266,6 +266,91 @@ int mla_query_lowrank(const mla_dims* dims, int32_t q_rank, const void* x, const
 int mla_output(const mla_dims* dims, const void* attn, const void* w_o, int64_t n_tokens, void* out,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------------
+ * DeepSeek-V4 / nanowhale variant (nanowhale MLA page).  One KV head of head_dim
+ * values, kv = kv_norm(x·W_KVᵀ) (RMSNorm with gain), its last d_rope dims rotated
+ * in the page's complex form (apply_rotary_emb: pairs (2i, 2i+1) turned by
+ * p·f_i, f_i = theta^(-2i/d_rope) or a caller's table), is cached per token and
+ * used by every query head as both key and value:
+ *   q[t,h]   = (RMSNorm(x[t]·W_QAᵀ)·q_gain)·W_QB[h*D : +D]ᵀ, last d_rope dims rotated
+ *   s[h,l]   = scale·q[t,h]·kv[l]                  (scale <= 0: 1/sqrt(head_dim))
+ *   o[t,h,:] = Σ_l e^(s_l) kv[l] / (Σ_l e^(s_l) + e^(sink[h])),
+ *              then its last d_rope dims rotated back by the query's position
+ *   u[t]     = W_OB · concat_g(W_OA[g]·o_g[t])      (o_g: group g of the H·D outputs)
+ * Sources: nanowhale MLA page, sections on the single KV head (wkv, kv_norm), the
+ * low-rank query (wq_a, q_norm, wq_b), the partial RoPE with rotation before and
+ * after attention, the SDPA over kv for keys and values with attn_sink, and the
+ * grouped low-rank output (wo_a, wo_b).
+ * rope_freqs: device float64 [d_rope/2] inverse frequencies, or NULL for
+ * theta^(-2i/d_rope); a context-extension rescaling passes its own table.
+ * Compiled for bf16 with head_dim <= 512 (multiple of 16); the MFMA decode
+ * kernel takes head_dim 512 with up to 16 heads, other shapes run the generic
+ * kernel.
+ * ------------------------------------------------------------------------------ */
+typedef struct mla_v4_dims {
+  int32_t d_model;      /* hidden size */
+  int32_t n_heads;      /* H query heads, all reading the one KV head */
+  int32_t head_dim;     /* D: KV row width and per-head query width */
+  int32_t d_rope;       /* rotary dims at the end of the row (even, <= D) */
+  int32_t q_rank;       /* low-rank query width (multiple of 8, <= 4096) */
+  int32_t o_groups;     /* output groups; (H*D) % o_groups == 0 */
+  int32_t o_rank;       /* per-group output rank */
+  int32_t dtype;        /* MLA_BF16 */
+  float rms_eps;        /* eps of kv_norm and q_norm */
+  float softmax_scale;  /* <= 0: 1/sqrt(head_dim) */
+  double rope_theta;
+} mla_v4_dims;
+
+typedef enum mla_v4_op {
+  MLA_V4_OP_WRITE_CACHE = 0,
+  MLA_V4_OP_QUERY = 1,
+  MLA_V4_OP_DECODE = 2,
+  MLA_V4_OP_PREFILL = 3,
+  MLA_V4_OP_OUTPUT = 4
+} mla_v4_op;
+
+int mla_v4_check_dims(const mla_v4_dims* dims);
+size_t mla_v4_workspace_size(const mla_v4_dims* dims, int op, int32_t batch, int64_t n_tokens,
+                             int32_t max_len);
+
+/* cache[slots[t], :] = rotated kv_norm(x[t]·W_KVᵀ)·kv_gain.
+ *   x device [n_tokens, d_model]; w_kv device [D, d_model]; kv_gain device [D]
+ *   positions device int32 [n_tokens]; slots device int64 [n_tokens], distinct, < cache_rows
+ *   cache device [cache_rows, D] */
+int mla_v4_write_cache(const mla_v4_dims* dims, const void* x, const void* w_kv, const void* kv_gain,
+                       const int32_t* positions, const int64_t* slots, int64_t n_tokens, void* cache,
+                       int64_t cache_rows, const double* rope_freqs, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* q[t,h,:] as above.  w_qa device [q_rank, d_model]; q_gain device [q_rank];
+ * w_qb device [H*D, q_rank]; q device out [n_tokens, H, D]. */
+int mla_v4_query(const mla_v4_dims* dims, const void* x, const void* w_qa, const void* q_gain,
+                 const void* w_qb, const int32_t* positions, int64_t n_tokens, const double* rope_freqs,
+                 void* q, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Decode: one query per sequence (at position seq_len[b]-1, its own row already
+ * cached) over rows seq_start[b] .. seq_start[b]+seq_len[b]-1.
+ *   q device [batch, H, D]; sink device fp32 [H]; out device out [batch, H, D] */
+int mla_v4_decode(const mla_v4_dims* dims, const void* q, const void* cache, const int64_t* seq_start,
+                  const int32_t* seq_len, int32_t batch, int32_t max_len, const float* sink,
+                  const double* rope_freqs, void* out, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/* Causal prefill over packed sequences (as mla_prefill: token t's row is cache row t,
+ * it attends rows cu_seqlens[b] .. t, its position is t - cu_seqlens[b]).
+ *   q device [n_tokens, H, D]; out device out [n_tokens, H, D] */
+int mla_v4_prefill(const mla_v4_dims* dims, const void* q, const void* cache, const int64_t* cu_seqlens,
+                   int32_t batch, int64_t n_tokens, int32_t max_len, const float* sink,
+                   const double* rope_freqs, void* out, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* u = grouped low-rank output projection of attn [n_tokens, H, D].
+ *   w_oa device [o_groups*o_rank, H*D/o_groups] (group g: rows g*o_rank ..)
+ *   w_ob device [d_model, o_groups*o_rank]; out device out [n_tokens, d_model]
+ * The o_groups*o_rank intermediate is rounded to the layer's element type. */
+int mla_v4_output(const mla_v4_dims* dims, const void* attn, const void* w_oa, const void* w_ob,
+                  int64_t n_tokens, void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* mla_strerror(int status);
 

@@ -165,3 +165,36 @@ def test_lowrank_query_and_output_entry_points():
     assert o(ctypes.byref(d), null, null, 0, null, null, 0, null) == abi.MLA_OK
     assert o(ctypes.byref(d), null, null, 4, null, null, 0, null) == abi.MLA_EINVAL
     assert o(ctypes.byref(d), p, p, 4, p, p, 16, null) == abi.MLA_EWORKSPACE
+
+
+def test_v4_entry_points_validate_arguments():
+    abi, lib = _lib()
+    null = None
+    cfg = I.V4_CONFIGS["nanowhale_v4_decode"]
+    d = abi.v4_dims_of(cfg)
+    assert ctypes.sizeof(abi.MlaV4Dims) == 48
+    assert lib.mla_v4_check_dims(ctypes.byref(d)) == abi.MLA_OK
+    bad = abi.v4_dims_of(cfg)
+    bad.d_rope = 7
+    assert lib.mla_v4_check_dims(ctypes.byref(bad)) == abi.MLA_EINVAL
+    bad = abi.v4_dims_of(cfg)
+    bad.o_groups = 3   # H*D not divisible
+    assert lib.mla_v4_check_dims(ctypes.byref(bad)) == abi.MLA_EINVAL
+    bad = abi.v4_dims_of(cfg)
+    bad.head_dim = 1024
+    assert lib.mla_v4_check_dims(ctypes.byref(bad)) == abi.MLA_ENOTSUP
+    bad = abi.v4_dims_of(cfg)
+    bad.dtype = abi.MLA_F32
+    assert lib.mla_v4_check_dims(ctypes.byref(bad)) == abi.MLA_ENOTSUP
+    B, L = 256, 2048
+    assert lib.mla_v4_workspace_size(ctypes.byref(d), abi.MLA_V4_OP_DECODE, B, 0, L) >= B * 8 * 512 * 2
+    assert lib.mla_v4_workspace_size(ctypes.byref(d), abi.MLA_V4_OP_OUTPUT, 0, 64, 0) >= 64 * 8 * 1024 * 2
+    p = 0x10000
+    assert lib.mla_v4_decode(ctypes.byref(d), null, null, null, null, 0, L, null, null, null, null, 0, null) == abi.MLA_OK
+    assert lib.mla_v4_decode(ctypes.byref(d), p, p, p, p, 4, L, null, null, p, p, 1 << 40, null) == abi.MLA_EINVAL
+    assert lib.mla_v4_decode(ctypes.byref(d), p, p, p, p, 4, L, p, 0x10001, p, p, 1 << 40, null) == abi.MLA_EINVAL
+    assert lib.mla_v4_decode(ctypes.byref(d), p, p, p, p, 4, L, p, null, p, p, 16, null) == abi.MLA_EWORKSPACE
+    assert lib.mla_v4_prefill(ctypes.byref(d), p, p, p, 1, 10, 0, p, null, p, p, 1 << 40, null) == abi.MLA_EINVAL
+    assert lib.mla_v4_query(ctypes.byref(d), p, p, null, p, p, 4, null, p, p, 1 << 40, null) == abi.MLA_EINVAL
+    assert lib.mla_v4_output(ctypes.byref(d), p, p, p, 4, p, p, 16, null) == abi.MLA_EWORKSPACE
+    assert lib.mla_v4_write_cache(ctypes.byref(d), p, p, p, p, p, 4, p, 10, null, p, 16, null) == abi.MLA_EWORKSPACE

@@ -483,6 +483,117 @@ def test_output_projection_matches_oracle(torch, name, T):
 
 
 # ----------------------------------------------------------------------------
+# the DeepSeek-V4 / nanowhale variant
+# ----------------------------------------------------------------------------
+
+
+def _v4_setup(torch, cfg):
+    import head_latent_attention_kv_amd as M
+    w = I.v4_weights(cfg)
+    wd = {k: (torch.from_numpy(v).cuda() if k == "sink" else Hh.to_dev(v, cfg.dtype)) for k, v in w.items()}
+    return M.v4_dims_of(cfg), w, wd
+
+
+def _v4_table(cfg):
+    """A context-extension style frequency table: the lower half of the rotary
+    frequencies divided by 32 (the Zebra page's YaRN factor), the rest unchanged."""
+    f = cfg.rope_theta ** (-2.0 * np.arange(cfg.d_rope // 2) / cfg.d_rope)
+    f[cfg.d_rope // 4:] /= 32.0
+    return f
+
+
+@pytest.mark.parametrize("lengths", [[700, 2048, 33, 1, 1500, 257]])
+def test_v4_decode_chain(torch, lengths):
+    """Cache rows, queries, decode with the sink and the inverse rotation, and the
+    grouped output projection, against the oracle's V4 chain (nanowhale shape)."""
+    import head_latent_attention_kv_amd as M
+    from oracle import mla_oracle as O
+    cfg = I.V4_CONFIGS["nanowhale_v4_decode"]
+    _print_case("v4_decode", lengths=lengths)
+    dims, w, wd = _v4_setup(torch, cfg)
+    D, H = cfg.head_dim, cfg.n_heads
+    lengths = np.array(lengths)
+    starts = np.concatenate([[0], np.cumsum(lengths)[:-1]])
+    rows = int(lengths.sum())
+    cache = torch.empty((rows, D), dtype=torch.bfloat16, device="cuda")
+    xs = [I.x_rows(cfg, b, 0, int(n)) for b, n in enumerate(lengths)]
+    for b, n in enumerate(lengths):
+        pos = torch.arange(int(n), dtype=torch.int32, device="cuda")
+        slots = torch.arange(int(n), dtype=torch.int64, device="cuda") + int(starts[b])
+        M.mla_v4_write_cache(dims, Hh.to_dev(xs[b], cfg.dtype), wd["w_kv"], wd["kv_gain"], pos, slots, cache)
+    xq = np.stack([x[-1] for x in xs])
+    q = torch.empty((len(lengths), H, D), dtype=torch.bfloat16, device="cuda")
+    M.mla_v4_query(dims, Hh.to_dev(xq, cfg.dtype), wd["w_qa"], wd["q_gain"], wd["w_qb"],
+                   torch.from_numpy((lengths - 1).astype(np.int32)).cuda(), q)
+    out = torch.empty_like(q)
+    M.mla_v4_decode(dims, q, cache, torch.from_numpy(starts.astype(np.int64)).cuda(),
+                    torch.from_numpy(lengths.astype(np.int32)).cuda(), int(lengths.max()), wd["sink"], out)
+    u = torch.empty((len(lengths), cfg.d_model), dtype=torch.bfloat16, device="cuda")
+    M.mla_v4_output(dims, out, wd["w_oa"], wd["w_ob"], u)
+    torch.cuda.synchronize()
+    got, got_u = Hh.to_host(out), Hh.to_host(u)
+    errs = []
+    ref_all = []
+    for b, n in enumerate(lengths):
+        n = int(n)
+        kv = O.v4_cache_rows(xs[b], w["w_kv"], w["kv_gain"], np.arange(n), d_rope=cfg.d_rope, eps=cfg.rms_eps)
+        qr = O.v4_query(xs[b][-1:], w["w_qa"], w["q_gain"], w["w_qb"], [n - 1], n_heads=H, head_dim=D,
+                        d_rope=cfg.d_rope, eps=cfg.rms_eps)
+        ref = O.v4_attention(qr, kv, w["sink"], [n - 1], np.arange(n), [0], np.zeros(n, int),
+                             cfg.softmax_scale, d_rope=cfg.d_rope)[0]
+        ref_all.append(ref)
+        errs.append(Hh.rel_err_rows(got[b], ref))
+    err = max(errs)
+    err_u = Hh.rel_err_rows(got_u, O.v4_output(got, w["w_oa"], w["w_ob"], cfg.o_groups))
+    err_uc = Hh.rel_err_rows(got_u, O.v4_output(np.stack(ref_all), w["w_oa"], w["w_ob"], cfg.o_groups))
+    print(f"v4 decode {list(lengths)}: attn chain {err:.3e}; output on gpu attn {err_u:.3e}, chain {err_uc:.3e}")
+    assert err <= Hh.TOL["bf16"] and err_u <= Hh.TOL["bf16"] and err_uc <= Hh.TOL["bf16"]
+
+
+@pytest.mark.parametrize("table", [False, True])
+def test_v4_prefill_ragged(torch, table):
+    """Causal V4 prefill over a ragged batch (with the default rotary frequencies and
+    with a caller's table), and the grouped output projection of many tokens."""
+    import head_latent_attention_kv_amd as M
+    from oracle import mla_oracle as O
+    cfg = I.V4_CONFIGS["nanowhale_v4_decode"]
+    lengths = [300, 1, 77]
+    _print_case("v4_prefill", lengths=lengths, table=table)
+    dims, w, wd = _v4_setup(torch, cfg)
+    D, H = cfg.head_dim, cfg.n_heads
+    f = _v4_table(cfg) if table else None
+    fd = torch.from_numpy(f).cuda() if table else None
+    T = sum(lengths)
+    x = np.concatenate([I.x_rows(cfg, 10 + b, 0, n) for b, n in enumerate(lengths)])
+    pos = np.concatenate([np.arange(n) for n in lengths])
+    seg = np.concatenate([np.full(n, b) for b, n in enumerate(lengths)])
+    xd = Hh.to_dev(x, cfg.dtype)
+    posd = torch.from_numpy(pos.astype(np.int32)).cuda()
+    cache = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    M.mla_v4_write_cache(dims, xd, wd["w_kv"], wd["kv_gain"], posd, torch.arange(T, device="cuda"), cache,
+                         rope_freqs=fd)
+    q = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    M.mla_v4_query(dims, xd, wd["w_qa"], wd["q_gain"], wd["w_qb"], posd, q, rope_freqs=fd)
+    out = torch.empty_like(q)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int64, device="cuda")
+    M.mla_v4_prefill(dims, q, cache, cu, max(lengths), wd["sink"], out, rope_freqs=fd)
+    u = torch.empty((T, cfg.d_model), dtype=torch.bfloat16, device="cuda")
+    M.mla_v4_output(dims, out, wd["w_oa"], wd["w_ob"], u)
+    torch.cuda.synchronize()
+    kv = O.v4_cache_rows(x, w["w_kv"], w["kv_gain"], pos, d_rope=cfg.d_rope, eps=cfg.rms_eps, inv_freq=f)
+    qr = O.v4_query(x, w["w_qa"], w["q_gain"], w["w_qb"], pos, n_heads=H, head_dim=D, d_rope=cfg.d_rope,
+                    eps=cfg.rms_eps, inv_freq=f)
+    ref = O.v4_attention(qr, kv, w["sink"], pos, pos, seg, seg, cfg.softmax_scale, d_rope=cfg.d_rope, inv_freq=f)
+    got = Hh.to_host(out)
+    err = Hh.rel_err_rows(got, ref)
+    err_kv = Hh.rel_err_rows(Hh.to_host(cache), kv)
+    err_u = Hh.rel_err_rows(Hh.to_host(u), O.v4_output(got, w["w_oa"], w["w_ob"], cfg.o_groups))
+    print(f"v4 prefill {lengths} table={table}: attn chain {err:.3e}, cache rows {err_kv:.3e}, output {err_u:.3e}")
+    for nm, e in (("attn", err), ("cache", err_kv), ("output", err_u)):
+        assert e <= Hh.TOL["bf16"], (nm, e)
+
+
+# ----------------------------------------------------------------------------
 # ABI behaviour on the device
 # ----------------------------------------------------------------------------
 
