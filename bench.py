@@ -183,6 +183,123 @@ def prefill_orig_alg_flops(cfg, L: int) -> int:
     return pairs * cfg.n_heads * (2 * (cfg.d_nope + cfg.d_rope) + 2 * cfg.d_v)
 
 
+def bench_v4(args, torch, M, I, Hh, cfg):
+    """DeepSeek-V4-variant decode at the nanowhale shape: one step = mla_v4_write_cache
+    (the new token of each sequence) + mla_v4_query + mla_v4_decode + mla_v4_output
+    over `batch` sequences of `context` cached rows (one 512-wide KV head)."""
+    import numpy as np
+    from oracle import mla_oracle as O
+    B, L, D, H = cfg.batch, cfg.context, cfg.head_dim, cfg.n_heads
+    dims = M.v4_dims_of(cfg)
+    t_setup = time.perf_counter()
+    w = I.v4_weights(cfg)
+    wd = {k: (torch.from_numpy(v).cuda() if k == "sink" else Hh.to_dev(v, cfg.dtype)) for k, v in w.items()}
+    starts = np.arange(B, dtype=np.int64) * L
+    cache0 = torch.empty((B * L, D), dtype=torch.bfloat16, device="cuda")
+    ws_w = torch.empty(M.mla_v4_workspace_size(dims, M.MLA_V4_OP_WRITE_CACHE, 0, L, 0), dtype=torch.uint8,
+                       device="cuda")
+    threads = args.threads or min(16, host_threads())
+
+    def gen(b):
+        return b, I.x_rows(cfg, b, 0, L - 1, quantized=False)
+
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        for b, xb in ex.map(gen, range(B)):
+            xd = torch.from_numpy(xb).cuda().to(torch.bfloat16)
+            pos = torch.arange(L - 1, dtype=torch.int32, device="cuda")
+            M.mla_v4_write_cache(dims, xd, wd["w_kv"], wd["kv_gain"], pos,
+                                 pos.to(torch.int64) + int(starts[b]), cache0, workspace=ws_w)
+    torch.cuda.synchronize()
+    cache_bytes = cache0.numel() * 2
+    n_copies = max(2, math.ceil(512e6 / cache_bytes) + 1)
+    caches = [cache0] + [cache0.clone() for _ in range(n_copies - 1)]
+    x_new = Hh.to_dev(np.stack([I.x_rows(cfg, b, L - 1, L)[0] for b in range(B)]), cfg.dtype)
+    pos_new = torch.full((B,), L - 1, dtype=torch.int32, device="cuda")
+    slots_new = torch.from_numpy(starts + L - 1).cuda()
+    seq_start = torch.from_numpy(starts).cuda()
+    seq_len = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    q = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    u = torch.empty((B, cfg.d_model), dtype=torch.bfloat16, device="cuda")
+    ws = {op: torch.empty(max(256, M.mla_v4_workspace_size(dims, op, B, B, L)), dtype=torch.uint8, device="cuda")
+          for op in (M.MLA_V4_OP_WRITE_CACHE, M.MLA_V4_OP_QUERY, M.MLA_V4_OP_DECODE, M.MLA_V4_OP_OUTPUT)}
+    setup_s = time.perf_counter() - t_setup
+
+    def step(i):
+        c = caches[i % n_copies]
+        M.mla_v4_write_cache(dims, x_new, wd["w_kv"], wd["kv_gain"], pos_new, slots_new, c,
+                             workspace=ws[M.MLA_V4_OP_WRITE_CACHE])
+        M.mla_v4_query(dims, x_new, wd["w_qa"], wd["q_gain"], wd["w_qb"], pos_new, q,
+                       workspace=ws[M.MLA_V4_OP_QUERY])
+        M.mla_v4_decode(dims, q, c, seq_start, seq_len, L, wd["sink"], out, workspace=ws[M.MLA_V4_OP_DECODE])
+        M.mla_v4_output(dims, out, wd["w_oa"], wd["w_ob"], u, workspace=ws[M.MLA_V4_OP_OUTPUT])
+
+    def decode_only(i):
+        M.mla_v4_decode(dims, q, caches[i % n_copies], seq_start, seq_len, L, wd["sink"], out,
+                        workspace=ws[M.MLA_V4_OP_DECODE])
+
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_step, ms_dec = timed(step), timed(decode_only)
+    assert torch.isfinite(u.float()).all(), "non-finite V4 output"
+    dec_bytes = B * L * D * 2 + 2 * B * H * D * 2
+    dec_flops = B * L * H * 4 * D
+    gbs = dec_bytes / (ms_dec * 1e-3) / 1e9
+    print(f"[bench] v4 decode: step {ms_step * 1e3:.1f} us, mla_v4_decode {ms_dec * 1e3:.1f} us "
+          f"({gbs:.0f} GB/s algorithmic) (setup {setup_s:.1f} s)", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle on 32 of the sequences: cache rows, query, attention (float64)
+        n_s = 32
+        t0 = time.perf_counter()
+        for b in range(n_s):
+            xb = I.x_rows(cfg, b, 0, L)
+            kv = O.v4_cache_rows(xb, w["w_kv"], w["kv_gain"], np.arange(L), d_rope=cfg.d_rope, eps=cfg.rms_eps)
+            qq = O.v4_query(xb[-1:], w["w_qa"], w["q_gain"], w["w_qb"], [L - 1], n_heads=H, head_dim=D,
+                            d_rope=cfg.d_rope, eps=cfg.rms_eps)
+            O.v4_attention(qq, kv, w["sink"], [L - 1], np.arange(L), [0], np.zeros(L, int), cfg.softmax_scale,
+                           d_rope=cfg.d_rope)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(n_s / dt, 3), "unit": "tokens/s", "cores": host_threads(), "kind": "oracle",
+               "sample": f"{n_s} of {B} sequences: float64 oracle (cache rows of {L} tokens, query, "
+                         f"V4 attention) = {n_s} decode tokens, {dt:.2f} s"}
+    line = {
+        "metric": "MLA V4-variant decode tokens/s + % of HBM roofline (one 512-wide KV head, nanowhale shape)",
+        "value": round(B / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded x ~ N(0,1), weights ~ N(0,1/fan_in), gains 1 + N(0, 0.01), sink N(0,1)",
+        "config": {"workload": cfg.name, "batch": B, "context": L, "heads": H, "head_dim": D, "d_rope": cfg.d_rope,
+                   "d_model": cfg.d_model, "q_rank": cfg.q_rank, "o_groups": cfg.o_groups, "o_rank": cfg.o_rank,
+                   "step": "mla_v4_write_cache + mla_v4_query + mla_v4_decode + mla_v4_output"},
+        "roofline": {"bound": "hbm", "kernel": "mla_v4_decode (decode_mfma_kernel<512, 512> + sink/rotation merge)",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "alg_bytes_per_launch": dec_bytes,
+                     "alg_flops_per_launch": dec_flops, "us_per_launch": round(ms_dec * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def bench_prefill(args, torch, M, I, Hh, cfg):
     """Long causal prefill: one step = mla_write_cache + mla_absorb + mla_prefill over
     the whole sequence (x resident in HBM); the attention kernel is timed alone
@@ -306,6 +423,8 @@ def main():
 
     M.load()
     torch.cuda.set_device(0)
+    if args.workload in I.V4_CONFIGS:
+        return bench_v4(args, torch, M, I, Hh, I.V4_CONFIGS[args.workload])
     cfg = I.CONFIGS[args.workload]
     if cfg.mode == "prefill":
         return bench_prefill(args, torch, M, I, Hh, cfg)

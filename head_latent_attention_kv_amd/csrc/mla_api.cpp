@@ -846,9 +846,11 @@ V4Query v4_query_ws(const mla_v4_dims* d, int64_t T) {
 struct V4Out {
   int splits_a;
   int64_t sps_a;
+  bool u_chunks;  // W_OB streamed per chunk of <= 64 tokens (few output tiles)
   size_t a_slices, a, u;
   size_t total() const { return a_slices + a + u; }
 };
+constexpr int kTokChunk = 64;
 V4Out v4_out_ws(const mla_v4_dims* d, int64_t T) {
   const mla_dims sh = v4_shadow(d);
   V4Out w{};
@@ -859,8 +861,12 @@ V4Out v4_out_ws(const mla_v4_dims* d, int64_t T) {
     w.splits_a = mla::skinny_splits(static_cast<int>(T), d->o_rank, d->o_groups, gdim);
     w.sps_a = static_cast<int64_t>(align_up(static_cast<size_t>(T) * gr * sizeof(float)) / sizeof(float));
     w.a_slices = static_cast<size_t>(w.splits_a) * w.sps_a * sizeof(float);
-    w.u = proj_bytes_k(&sh, d->d_model, gr, T, out_width(&sh));
   }
+  // a d_model-wide output over K = o_groups·o_rank: the tiled GEMM has too few
+  // workgroups unless T is large; stream W_OB once per chunk of 64 tokens instead
+  const int64_t tiles = (T + 63) / 64 * ((d->d_model + 63) / 64);
+  w.u_chunks = d->dtype == MLA_BF16 && T > 0 && tiles < 128;
+  if (w.u_chunks) w.u = proj_bytes_k(&sh, d->d_model, gr, std::min<int64_t>(T, kTokChunk), out_width(&sh));
   return w;
 }
 
@@ -1043,9 +1049,6 @@ int mla_v4_output(const mla_v4_dims* dims, const void* attn, const void* w_oa, c
     sa.splits = w.splits_a;
     mla::gemm_skinny(sa, /*a_f32=*/false, /*out_bf16=*/false, s);
     mla::sum_cast_slices(dims->dtype, a_sl, w.splits_a, w.sps_a, T, G * R, static_cast<int64_t>(G) * R, a, s);
-    const int64_t ld = out_width(&sh);
-    const Proj p = proj_one(&sh, a, G * R, G * R, w_ob, dims->d_model, u_sl, ld, n_tokens, s);
-    mla::sum_cast_slices(dims->dtype, u_sl, p.splits, p.sps, T, dims->d_model, ld, out, s);
   } else {
     GemmArgs g{};
     g.A = attn;
@@ -1062,6 +1065,17 @@ int mla_v4_output(const mla_v4_dims* dims, const void* attn, const void* w_oa, c
     g.K = gdim;
     g.Z = G;
     mla::gemm(g, dims->dtype, false, false, /*out_bf16=*/true, s);
+  }
+  if (w.u_chunks) {
+    const int64_t ld = out_width(&sh);
+    for (int t0 = 0; t0 < T; t0 += kTokChunk) {
+      const int n = std::min(kTokChunk, T - t0);
+      const Proj p = proj_one(&sh, static_cast<const char*>(a) + static_cast<int64_t>(t0) * G * R * 2, G * R,
+                              G * R, w_ob, dims->d_model, u_sl, ld, n, s);
+      mla::sum_cast_slices(dims->dtype, u_sl, p.splits, p.sps, n, dims->d_model, ld,
+                           static_cast<char*>(out) + static_cast<int64_t>(t0) * dims->d_model * 2, s);
+    }
+  } else {
     GemmArgs g2{};
     g2.A = a;
     g2.sAm = static_cast<int64_t>(G) * R;
