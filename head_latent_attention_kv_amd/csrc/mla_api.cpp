@@ -846,11 +846,11 @@ V4Query v4_query_ws(const mla_v4_dims* d, int64_t T) {
 struct V4Out {
   int splits_a;
   int64_t sps_a;
-  bool u_chunks;  // W_OB streamed per chunk of <= 64 tokens (few output tiles)
+  int u_splits;   // K pieces of the W_OB product run as one batched GEMM (few output tiles)
+  int64_t u_sps;
   size_t a_slices, a, u;
   size_t total() const { return a_slices + a + u; }
 };
-constexpr int kTokChunk = 64;
 V4Out v4_out_ws(const mla_v4_dims* d, int64_t T) {
   const mla_dims sh = v4_shadow(d);
   V4Out w{};
@@ -862,11 +862,17 @@ V4Out v4_out_ws(const mla_v4_dims* d, int64_t T) {
     w.sps_a = static_cast<int64_t>(align_up(static_cast<size_t>(T) * gr * sizeof(float)) / sizeof(float));
     w.a_slices = static_cast<size_t>(w.splits_a) * w.sps_a * sizeof(float);
   }
-  // a d_model-wide output over K = o_groups·o_rank: the tiled GEMM has too few
-  // workgroups unless T is large; stream W_OB once per chunk of 64 tokens instead
+  // W_OB: d_model outputs over K = o_groups·o_rank.  With few 64x64 output tiles
+  // the K range is cut into pieces that run as the batch index of one GEMM
+  // (fp32 slices, summed after), so the grid fills the chip.
   const int64_t tiles = (T + 63) / 64 * ((d->d_model + 63) / 64);
-  w.u_chunks = d->dtype == MLA_BF16 && T > 0 && tiles < 128;
-  if (w.u_chunks) w.u = proj_bytes_k(&sh, d->d_model, gr, std::min<int64_t>(T, kTokChunk), out_width(&sh));
+  int sp = 1;
+  while (sp < 16 && tiles * sp < 256 && gr % (2 * sp * 32) == 0) sp *= 2;
+  w.u_splits = sp;
+  if (sp > 1) {
+    w.u_sps = static_cast<int64_t>(align_up(static_cast<size_t>(T) * d->d_model * sizeof(float)) / sizeof(float));
+    w.u = static_cast<size_t>(sp) * w.u_sps * sizeof(float);
+  }
   return w;
 }
 
@@ -1066,15 +1072,24 @@ int mla_v4_output(const mla_v4_dims* dims, const void* attn, const void* w_oa, c
     g.Z = G;
     mla::gemm(g, dims->dtype, false, false, /*out_bf16=*/true, s);
   }
-  if (w.u_chunks) {
-    const int64_t ld = out_width(&sh);
-    for (int t0 = 0; t0 < T; t0 += kTokChunk) {
-      const int n = std::min(kTokChunk, T - t0);
-      const Proj p = proj_one(&sh, static_cast<const char*>(a) + static_cast<int64_t>(t0) * G * R * 2, G * R,
-                              G * R, w_ob, dims->d_model, u_sl, ld, n, s);
-      mla::sum_cast_slices(dims->dtype, u_sl, p.splits, p.sps, n, dims->d_model, ld,
-                           static_cast<char*>(out) + static_cast<int64_t>(t0) * dims->d_model * 2, s);
-    }
+  if (w.u_splits > 1) {
+    const int kc = G * R / w.u_splits;
+    GemmArgs g2{};
+    g2.A = a;
+    g2.sAz = kc;  // piece z reads columns [z·kc, (z+1)·kc) of a and of W_OB
+    g2.sAm = static_cast<int64_t>(G) * R;
+    g2.B = w_ob;
+    g2.sBz = kc;
+    g2.sBo = static_cast<int64_t>(G) * R;
+    g2.C = u_sl;
+    g2.sCz = w.u_sps;
+    g2.sCm = dims->d_model;
+    g2.M = T;
+    g2.N = dims->d_model;
+    g2.K = kc;
+    g2.Z = w.u_splits;
+    mla::gemm(g2, dims->dtype, false, false, /*out_bf16=*/false, s);
+    mla::sum_cast_slices(dims->dtype, u_sl, w.u_splits, w.u_sps, T, dims->d_model, dims->d_model, out, s);
   } else {
     GemmArgs g2{};
     g2.A = a;
