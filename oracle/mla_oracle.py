@@ -37,6 +37,10 @@ named by their title / subject; equation numbers are the pages' own.
 * Beyond the attention itself (``lowrank_query``, ``output_projection``): the
   MLA principle page's low-rank query q_b_proj(q_a_layernorm(q_a_proj(x))) of its
   §"步骤", and its output projection o_proj, eqs. (3)/(6).
+* Page "zebra_qwen3_7MLA21GDN": the context window extended 32 times with YaRN
+  (factor 32.0 over a 32K pretraining window); YaRN changes only the rotary
+  frequencies (``yarn_inv_freq``, from the YaRN paper), which every rotating
+  function here accepts as ``inv_freq``.
 * The nanowhale page's DeepSeek-V4 variant (``v4_*``): one normalised KV head
   used as both key and value, the complex-form RoPE on its last dims with the
   inverse rotation of the output, an attention sink, and the grouped low-rank
@@ -67,28 +71,60 @@ def _f64(a) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 
-def rope_angles(pos, d_rope: int, theta: float) -> np.ndarray:
-    """Angles p·θ_j, θ_j = θ^(-2j/d_rope), j < d_rope/2, in float64; shape [..., d_rope/2]."""
+def rope_angles(pos, d_rope: int, theta: float, inv_freq=None) -> np.ndarray:
+    """Angles p·θ_j, θ_j = θ^(-2j/d_rope), j < d_rope/2, in float64; shape [..., d_rope/2].
+    ``inv_freq`` [d_rope/2], when given, replaces θ_j (a rescaled table such as YaRN's)."""
     if d_rope % 2:
         raise ValueError("rotary width must be even")
     half = d_rope // 2
-    j = np.arange(half, dtype=F64)
-    inv_freq = float(theta) ** (-2.0 * j / d_rope)
+    if inv_freq is None:
+        j = np.arange(half, dtype=F64)
+        inv_freq = float(theta) ** (-2.0 * j / d_rope)
+    inv_freq = _f64(inv_freq)
+    if inv_freq.shape != (half,):
+        raise ValueError("inverse-frequency table must hold d_rope/2 values")
     return _f64(pos)[..., None] * inv_freq
 
 
-def rope(y, pos, theta: float) -> np.ndarray:
+def yarn_inv_freq(d_rope: int, theta: float, factor: float, original_window: float,
+                  alpha: float = 1.0, beta: float = 32.0) -> np.ndarray:
+    """YaRN's rescaled inverse frequencies (Peng et al., "YaRN: Efficient Context
+    Window Extension of Large Language Models", the "NTK-by-parts" interpolation
+    that YaRN keeps).  Pair j turns at θ_j = θ^(-2j/d_rope), i.e. with wavelength
+    λ_j = 2π/θ_j; r_j = original_window/λ_j counts its turns over the pretraining
+    window.  A ramp γ(r) is 0 below α, 1 above β and linear between; the new
+    frequency is (1 − γ)·θ_j/factor + γ·θ_j: slow pairs are interpolated by the
+    factor, fast pairs keep their frequency.  The Zebra hybrid page extends a
+    32K window 32 times this way; α = 1 and β = 32 are the paper's values."""
+    if d_rope % 2 or factor <= 0 or original_window <= 0 or not beta > alpha:
+        raise ValueError("bad YaRN parameters")
+    j = np.arange(d_rope // 2, dtype=F64)
+    base = float(theta) ** (-2.0 * j / d_rope)
+    r = float(original_window) * base / (2.0 * np.pi)
+    gamma = np.clip((r - alpha) / (beta - alpha), 0.0, 1.0)
+    return (1.0 - gamma) * base / float(factor) + gamma * base
+
+
+def yarn_logit_scale(factor: float) -> float:
+    """YaRN's attention temperature: logits are multiplied by (0.1·ln(factor) + 1)²
+    (the paper applies √(1/t) = 0.1·ln s + 1 to both q and k); a caller folds it
+    into the softmax scale."""
+    m = 0.1 * np.log(float(factor)) + 1.0 if factor > 1 else 1.0
+    return float(m * m)
+
+
+def rope(y, pos, theta: float, inv_freq=None) -> np.ndarray:
     """Rotate-half RoPE of the last axis of ``y`` (width d_r) by position ``pos``.
 
     Dims j and j + d_r/2 form a pair rotated by angle p·θ_j:
       y'[j]        = y[j]·cos − y[j+half]·sin
       y'[j+half]   = y[j+half]·cos + y[j]·sin
-    ``pos`` broadcasts against y's leading axes.
+    ``pos`` broadcasts against y's leading axes.  ``inv_freq`` replaces θ_j.
     """
     y = _f64(y)
     d = y.shape[-1]
     half = d // 2
-    ang = rope_angles(pos, d, theta)
+    ang = rope_angles(pos, d, theta, inv_freq)
     # broadcast angles over any middle axes (e.g. heads) of y
     while ang.ndim < y.ndim:
         ang = np.expand_dims(ang, axis=-2)
@@ -114,17 +150,17 @@ def latent(x, w_dkv, latent_rmsnorm: bool = False, eps: float = 1e-6) -> np.ndar
     return rmsnorm(c, eps) if latent_rmsnorm else c
 
 
-def rotary_key(x, w_kr, pos, n_groups: int, d_rope: int, theta: float) -> np.ndarray:
+def rotary_key(x, w_kr, pos, n_groups: int, d_rope: int, theta: float, inv_freq=None) -> np.ndarray:
     """kr[t, g] = RoPE(x[t] · W_KR[g·d_r:(g+1)·d_r]ᵀ, p[t]). Shape [T, G, d_r]."""
     raw = (_f64(x) @ _f64(w_kr).T).reshape(-1, n_groups, d_rope)
-    return rope(raw, pos, theta)
+    return rope(raw, pos, theta, inv_freq)
 
 
 def cache_rows(x, w_dkv, w_kr, pos, *, n_groups, d_rope, theta, latent_rmsnorm=False,
-               eps=1e-6) -> np.ndarray:
+               eps=1e-6, inv_freq=None) -> np.ndarray:
     """One cache row per token: [c (r) ; kr_0 ; ... ; kr_{G-1}] (width r + G·d_r)."""
     c = latent(x, w_dkv, latent_rmsnorm, eps)
-    kr = rotary_key(x, w_kr, pos, n_groups, d_rope, theta)
+    kr = rotary_key(x, w_kr, pos, n_groups, d_rope, theta, inv_freq)
     return np.concatenate([c, kr.reshape(kr.shape[0], -1)], axis=1)
 
 
@@ -139,11 +175,11 @@ def split_rows(rows, rank: int, n_groups: int, d_rope: int):
 # ----------------------------------------------------------------------------
 
 
-def query(x, w_qc, w_qr, pos, *, n_heads, d_nope, d_rope, theta):
+def query(x, w_qc, w_qr, pos, *, n_heads, d_nope, d_rope, theta, inv_freq=None):
     """qn[t,h] = x[t]·W_QC[h·d_nope:(h+1)·d_nope]ᵀ; qr[t,h] = RoPE(x[t]·W_QR[h·d_r:…]ᵀ, p[t])."""
     x = _f64(x)
     qn = (x @ _f64(w_qc).T).reshape(-1, n_heads, d_nope)
-    qr = rope((x @ _f64(w_qr).T).reshape(-1, n_heads, d_rope), pos, theta)
+    qr = rope((x @ _f64(w_qr).T).reshape(-1, n_heads, d_rope), pos, theta, inv_freq)
     return qn, qr
 
 
@@ -156,7 +192,7 @@ def absorbed_query(qn, w_uk) -> np.ndarray:
     return np.einsum("hdc,thd->thc", _f64(w_uk), _f64(qn))
 
 
-def lowrank_query(x, w_qa, q_gain, w_qb, pos, *, n_heads, d_nope, d_rope, theta, eps):
+def lowrank_query(x, w_qa, q_gain, w_qb, pos, *, n_heads, d_nope, d_rope, theta, eps, inv_freq=None):
     """The low-rank query path, page "MLA 原理" §"步骤" (the report's eqs. (37)-(40)):
     q = q_b_proj(q_a_layernorm(q_a_proj(x))), viewed as [H, d_nope + d_rope] per
     token and split into q_nope (first d_nope) and q_pe (last d_rope); q_pe is then
@@ -168,7 +204,7 @@ def lowrank_query(x, w_qa, q_gain, w_qb, pos, *, n_heads, d_nope, d_rope, theta,
     if q_gain is not None:
         cq = cq * _f64(q_gain)
     q = (cq @ _f64(w_qb).T).reshape(-1, n_heads, d_nope + d_rope)
-    return q[..., :d_nope], rope(q[..., d_nope:], pos, theta)
+    return q[..., :d_nope], rope(q[..., d_nope:], pos, theta, inv_freq)
 
 
 # ----------------------------------------------------------------------------
@@ -241,16 +277,16 @@ def mla_attention(qn, qr, c, kr, w_uk, w_uv, q_pos, k_pos, q_seg, k_seg, scale, 
 
 def mla_layer(x_keys, x_queries, w, *, k_pos, q_pos, k_seg, q_seg, n_heads, n_groups,
               d_nope, d_rope, theta, scale, latent_rmsnorm=False, eps=1e-6,
-              head_chunk=None) -> np.ndarray:
+              head_chunk=None, inv_freq=None) -> np.ndarray:
     """End-to-end chain: cache rows from x_keys, queries from x_queries, attention output.
 
     ``w`` holds w_dkv, w_kr, w_qc, w_qr, w_uk, w_uv (float arrays)."""
     r = w["w_dkv"].shape[0]
     rows = cache_rows(x_keys, w["w_dkv"], w["w_kr"], k_pos, n_groups=n_groups, d_rope=d_rope,
-                      theta=theta, latent_rmsnorm=latent_rmsnorm, eps=eps)
+                      theta=theta, latent_rmsnorm=latent_rmsnorm, eps=eps, inv_freq=inv_freq)
     c, kr = split_rows(rows, r, n_groups, d_rope)
     qn, qr = query(x_queries, w["w_qc"], w["w_qr"], q_pos, n_heads=n_heads, d_nope=d_nope,
-                   d_rope=d_rope, theta=theta)
+                   d_rope=d_rope, theta=theta, inv_freq=inv_freq)
     return mla_attention(qn, qr, c, kr, w["w_uk"], w["w_uv"], q_pos, k_pos, q_seg, k_seg,
                          scale, head_chunk=head_chunk)
 

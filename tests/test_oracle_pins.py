@@ -668,3 +668,83 @@ def test_p9_v4_projections_brute_force():
             assert abs(u[t, j] - sum(a[i] * w_ob[j, i] for i in range(G * R))) < 1e-11
     w1 = rng.standard_normal((R, H * D))
     np.testing.assert_allclose(O.v4_output(o, w1, w_ob[:, :R], 1), (flat @ w1.T) @ w_ob[:, :R].T, rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# P10: YaRN-rescaled rotary frequencies (Zebra hybrid page: factor 32 over a 32K
+# window; the interpolation itself from the YaRN paper)
+# ----------------------------------------------------------------------------
+
+
+def test_p10_yarn_table_ends_and_midpoint():
+    """θ = 16, d_rope = 8 gives θ_j = 2^-j; a window of 2π·16 turns pair j 16·2^-j
+    times over it.  With the ramp on [4, 12]: pair 0 (16 turns) keeps its
+    frequency, pair 3 (2 turns) is divided by the factor, and pair 1 (8 turns, the
+    ramp's midpoint) gets the mean of the two."""
+    s = 5.0
+    f = O.yarn_inv_freq(8, 16.0, s, 2 * math.pi * 16, alpha=4.0, beta=12.0)
+    assert f[0] == 1.0
+    assert abs(f[3] - 0.125 / s) < 1e-16
+    assert abs(f[1] - 0.5 * (0.5 / s + 0.5)) < 1e-15
+    # factor 1 changes nothing, at the pages' shape (64 rotary dims, 32K window)
+    plain = 10000.0 ** (-2.0 * np.arange(32) / 64)
+    np.testing.assert_allclose(O.yarn_inv_freq(64, 10000.0, 1.0, 32768.0), plain, rtol=1e-15, atol=0)
+
+
+def test_p10_yarn_table_bounds_and_order():
+    """Every rescaled frequency lies in [θ_j/s, θ_j] and they fall with j; at the
+    Zebra page's factor 32 over 32768 tokens the fastest pair is untouched and the
+    slowest (fewer than one turn over the window) is interpolated fully."""
+    s = 32.0
+    f = O.yarn_inv_freq(64, 10000.0, s, 32768.0)
+    plain = 10000.0 ** (-2.0 * np.arange(32) / 64)
+    assert np.all(f <= plain * (1 + 1e-15)) and np.all(f >= plain / s * (1 - 1e-15))
+    assert np.all(np.diff(f) < 0)
+    assert f[0] == plain[0]
+    assert abs(f[-1] - plain[-1] / s) < 1e-18
+    assert np.any((f > plain / s * 1.01) & (f < plain * 0.99))    # some pairs on the ramp
+
+
+def test_p10_yarn_interpolated_pairs_stretch_positions():
+    """On the fully interpolated pairs, position s·p with the YaRN table turns exactly
+    as p did with the original frequencies; on the untouched pairs nothing changes."""
+    d, s, W = 64, 32.0, 32768.0
+    f = O.yarn_inv_freq(d, 10000.0, s, W)
+    plain = 10000.0 ** (-2.0 * np.arange(d // 2) / d)
+    slow = np.isclose(f, plain / s, rtol=1e-14, atol=0)
+    fast = f == plain
+    assert slow.sum() >= 2 and fast.sum() >= 2
+    rng = np.random.default_rng(100)
+    y = rng.standard_normal(d)
+    p = 1234.0
+    got = O.rope(y, s * p, 10000.0, inv_freq=f)
+    ref = O.rope(y, p, 10000.0)
+    idx = np.nonzero(slow)[0]
+    np.testing.assert_allclose(got[idx], ref[idx], rtol=1e-9, atol=1e-9)
+    np.testing.assert_allclose(got[idx + d // 2], ref[idx + d // 2], rtol=1e-9, atol=1e-9)
+    same = O.rope(y, p, 10000.0, inv_freq=f)
+    jdx = np.nonzero(fast)[0]
+    np.testing.assert_allclose(same[jdx], ref[jdx], rtol=0, atol=1e-15)
+
+
+def test_p10_table_rope_keeps_rotation_properties():
+    """With any frequency table the rotation keeps the norm and scores depend only on
+    relative positions; the default table reproduces the untabled rotation."""
+    rng = np.random.default_rng(101)
+    d = 16
+    f = O.yarn_inv_freq(d, 10000.0, 32.0, 4096.0)
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    a = O.rope(q, 1_000_000.0, 10000.0, inv_freq=f) @ O.rope(k, 999_000.0, 10000.0, inv_freq=f)
+    b = O.rope(q, 1000.0, 10000.0, inv_freq=f) @ O.rope(k, 0.0, 10000.0, inv_freq=f)
+    assert abs(a - b) < 1e-9
+    assert abs(np.linalg.norm(O.rope(q, 777.0, 10000.0, inv_freq=f)) - np.linalg.norm(q)) < 1e-12
+    plain = 10000.0 ** (-2.0 * np.arange(d // 2) / d)
+    np.testing.assert_allclose(O.rope(q, 77.0, 10000.0, inv_freq=plain), O.rope(q, 77.0, 10000.0),
+                               rtol=0, atol=1e-15)
+
+
+def test_p10_yarn_logit_scale():
+    """The temperature's closed forms: factor 1 leaves the logits; factor e^10 gives
+    √(1/t) = 2, so logits are multiplied by 4."""
+    assert O.yarn_logit_scale(1.0) == 1.0
+    assert abs(O.yarn_logit_scale(math.exp(10.0)) - 4.0) < 1e-12
