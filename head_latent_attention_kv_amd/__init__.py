@@ -13,6 +13,7 @@ its calls:
     mla_prefill_expanded — causal prefill in the original order (k_nope, v expanded)
     mla_absorb_lowrank / mla_query_lowrank — the low-rank query path (W_QA, RMSNorm, W_QB)
     mla_output       — the output projection W_o after W_UV
+    mla_rope_yarn_table — YaRN's rescaled rotary frequencies, for mla_dims.rope_freqs
     mla_v4_*         — the DeepSeek-V4 / nanowhale variant (one KV head as key and value,
                        attention sink, inverse rotation of the output, grouped output)
 
@@ -26,7 +27,8 @@ from ._abi import (  # noqa: F401
     MLA_OP_DECODE, MLA_OP_OUTPUT, MLA_OP_PREFILL, MLA_OP_PREFILL_EXPANDED, MLA_OP_QUERY, MLA_OP_WRITE_CACHE,
     MlaDims, MlaError, dims_of, load, make_dims, mla_absorb, mla_absorb_lowrank, mla_decode,
     mla_decode_partials, mla_decode_split_rows, mla_decode_splits, mla_lowrank_workspace_size, mla_output,
-    mla_prefill, mla_prefill_expanded, mla_query, mla_query_lowrank, mla_workspace_size, mla_write_cache,
+    mla_prefill, mla_prefill_expanded, mla_query, mla_query_lowrank, mla_rope_yarn_table, mla_workspace_size,
+    mla_write_cache,
     strerror,
 )
 

@@ -25,7 +25,7 @@ class MlaDims(ctypes.Structure):
         ("rank", ctypes.c_int32), ("d_rope", ctypes.c_int32), ("d_nope", ctypes.c_int32),
         ("d_v", ctypes.c_int32), ("dtype", ctypes.c_int32), ("latent_rmsnorm", ctypes.c_int32),
         ("rms_eps", ctypes.c_float), ("softmax_scale", ctypes.c_float),
-        ("rope_theta", ctypes.c_double),
+        ("rope_theta", ctypes.c_double), ("rope_freqs", ctypes.c_void_p),
     ]
 
 
@@ -45,6 +45,8 @@ _P4 = ctypes.POINTER(MlaV4Dims)
 SIGNATURES = {
     "mla_workspace_size": (_sz, [_PD, ctypes.c_int, _i32, _i64, _i32]),
     "mla_check_dims": (ctypes.c_int, [_PD]),
+    "mla_rope_yarn_table": (ctypes.c_int, [_i32, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                           ctypes.c_double, ctypes.c_double, ctypes.POINTER(ctypes.c_double)]),
     "mla_write_cache": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
     "mla_absorb": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "mla_decode": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
@@ -104,18 +106,40 @@ def strerror(status: int) -> str:
 
 
 def make_dims(*, d_model, n_heads, n_groups, rank, d_rope, d_nope, d_v, dtype, latent_rmsnorm=False,
-              rms_eps=1e-6, softmax_scale=0.0, rope_theta=10000.0) -> MlaDims:
+              rms_eps=1e-6, softmax_scale=0.0, rope_theta=10000.0, rope_freqs=None) -> MlaDims:
+    """rope_freqs: a contiguous float64 device tensor of d_rope/2 inverse frequencies
+    (e.g. from mla_rope_yarn_table), or None for rope_theta.  The dims object keeps
+    a reference to it, so it lives as long as the dims do."""
     dt = {"f32": MLA_F32, "bf16": MLA_BF16}.get(dtype, dtype)
-    return MlaDims(d_model, n_heads, n_groups, rank, d_rope, d_nope, d_v, int(dt), int(bool(latent_rmsnorm)),
-                   float(rms_eps), float(softmax_scale), float(rope_theta))
+    ptr = None
+    if rope_freqs is not None:
+        if getattr(rope_freqs, "dtype", None) is None or str(rope_freqs.dtype) != "torch.float64" \
+                or not rope_freqs.is_contiguous() or rope_freqs.numel() != d_rope // 2:
+            raise ValueError("rope_freqs must be a contiguous float64 tensor of d_rope/2 values")
+        ptr = rope_freqs.data_ptr()
+    d = MlaDims(d_model, n_heads, n_groups, rank, d_rope, d_nope, d_v, int(dt), int(bool(latent_rmsnorm)),
+                float(rms_eps), float(softmax_scale), float(rope_theta), ptr)
+    d._rope_freqs_ref = rope_freqs
+    return d
 
 
-def dims_of(cfg) -> MlaDims:
+def mla_rope_yarn_table(d_rope: int, theta: float, factor: float, original_window: float,
+                        alpha: float = 1.0, beta: float = 32.0) -> list:
+    """YaRN's rescaled inverse frequencies (d_rope/2 values, host), from the library."""
+    out = (ctypes.c_double * max(1, d_rope // 2))()
+    st = load().mla_rope_yarn_table(int(d_rope), float(theta), float(factor), float(original_window),
+                                    float(alpha), float(beta), out)
+    if st != MLA_OK:
+        raise MlaError("mla_rope_yarn_table", st)
+    return list(out)[: d_rope // 2]
+
+
+def dims_of(cfg, rope_freqs=None) -> MlaDims:
     """mla_dims for a workload description with the usual field names."""
     return make_dims(d_model=cfg.d_model, n_heads=cfg.n_heads, n_groups=cfg.n_groups, rank=cfg.rank,
                      d_rope=cfg.d_rope, d_nope=cfg.d_nope, d_v=cfg.d_v, dtype=cfg.dtype,
                      latent_rmsnorm=cfg.latent_rmsnorm, rms_eps=cfg.rms_eps,
-                     softmax_scale=cfg.softmax_scale, rope_theta=cfg.rope_theta)
+                     softmax_scale=cfg.softmax_scale, rope_theta=cfg.rope_theta, rope_freqs=rope_freqs)
 
 
 # ----------------------------------------------------------------------------

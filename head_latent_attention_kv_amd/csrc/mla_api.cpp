@@ -37,6 +37,7 @@ int check_dims(const mla_dims* d) {
   if (!(d->rms_eps >= 0.f) || !isfinite(d->rms_eps)) return MLA_EINVAL;
   if (isnan(d->softmax_scale) || isinf(d->softmax_scale)) return MLA_EINVAL;
   if (!(d->rope_theta > 0.0) || !isfinite(d->rope_theta)) return MLA_EINVAL;
+  if (d->rope_freqs != nullptr && !aligned16(d->rope_freqs)) return MLA_EINVAL;
   // limits of the compiled kernels
   if (d->rank > kMaxRank || d->rank % 16 != 0) return MLA_ENOTSUP;
   if (d->dtype == MLA_BF16 && (d->d_model % 8 != 0 || d->d_nope % 8 != 0)) return MLA_ENOTSUP;
@@ -335,7 +336,7 @@ void apply_w_uv(const mla_dims* d, const float* o_lat, int64_t n_q, const void* 
 
 extern "C" {
 
-int mla_version(void) { return 100; }
+int mla_version(void) { return 101; }
 
 const char* mla_strerror(int status) {
   switch (status) {
@@ -349,6 +350,23 @@ const char* mla_strerror(int status) {
 }
 
 int mla_check_dims(const mla_dims* dims) { return check_dims(dims); }
+
+int mla_rope_yarn_table(int32_t d_rope, double theta, double factor, double original_window, double alpha,
+                        double beta, double* out) {
+  if (out == nullptr || d_rope <= 0 || d_rope % 2 != 0) return MLA_EINVAL;
+  if (!(theta > 0.0) || !(factor > 0.0) || !(original_window > 0.0) || !(beta > alpha) ||
+      !std::isfinite(theta) || !std::isfinite(factor) || !std::isfinite(original_window) || !std::isfinite(alpha) ||
+      !std::isfinite(beta))
+    return MLA_EINVAL;
+  constexpr double kTwoPi = 6.283185307179586476925;
+  for (int j = 0; j < d_rope / 2; ++j) {
+    const double f = std::pow(theta, -2.0 * j / d_rope);
+    const double turns = original_window * f / kTwoPi;  // turns of the pair over the original window
+    const double g = std::min(1.0, std::max(0.0, (turns - alpha) / (beta - alpha)));
+    out[j] = (1.0 - g) * f / factor + g * f;
+  }
+  return MLA_OK;
+}
 
 size_t mla_workspace_size(const mla_dims* dims, int op, int32_t batch, int64_t n_tokens,
                           int32_t max_len) {
@@ -384,7 +402,7 @@ int mla_write_cache(const mla_dims* dims, const void* x, const void* w_dkv, cons
                           row_w, n_tokens, s);
   mla::finalize_cache_rows(dims->dtype, proj, row_w, p.splits, p.sps, cache, slots, positions,
                            n_tokens, dims->rank, dims->n_groups, dims->d_rope, dims->latent_rmsnorm,
-                           dims->rms_eps, dims->rope_theta, s);
+                           dims->rms_eps, dims->rope_theta, dims->rope_freqs, s);
   return launch_status();
 }
 
@@ -408,7 +426,7 @@ int mla_absorb(const mla_dims* dims, const void* x, const void* w_qc, const void
   const Proj p = proj_two(dims, x, w_qc, H * dims->d_nope, w_qr, H * dims->d_rope, q, ld, n_tokens, s);
   mla::sum_split_slices(q, p.splits, p.sps, static_cast<int>(n_tokens), q_cols(dims), ld, s);
   mla::finalize_query_rope(dims->dtype, q + static_cast<int64_t>(H) * dims->d_nope, ld, dims->d_rope, q_pe,
-                           positions, n_tokens, H, dims->d_rope, dims->rope_theta, s);
+                           positions, n_tokens, H, dims->d_rope, dims->rope_theta, dims->rope_freqs, s);
   // q_lat[t,h,:] = Σ_d q_nope[t,h,d] W_UK[h,d,:]   (batched over heads)
   GemmArgs a{};
   a.A = q;
@@ -572,7 +590,7 @@ int mla_query(const mla_dims* dims, const void* x, const void* w_qc, const void*
   const Proj p = proj_two(dims, x, w_qc, H * dims->d_nope, w_qr, H * dims->d_rope, q, ld, n_tokens, s);
   mla::sum_split_slices(q, p.splits, p.sps, static_cast<int>(n_tokens), q_cols(dims), ld, s);
   mla::finalize_query_rope(dims->dtype, q + static_cast<int64_t>(H) * dims->d_nope, ld, dims->d_rope, q_pe,
-                           positions, n_tokens, H, dims->d_rope, dims->rope_theta, s);
+                           positions, n_tokens, H, dims->d_rope, dims->rope_theta, dims->rope_freqs, s);
   mla::cast_heads(dims->dtype, q, ld, dims->d_nope, H, dims->d_nope, q_nope, n_tokens, s);
   return launch_status();
 }
@@ -673,7 +691,7 @@ float* lowrank_front(const mla_dims* dims, int32_t q_rank, const void* x, const 
   mla::sum_split_slices(q, p2.splits, p2.sps, static_cast<int>(n_tokens), q_cols(dims), ld, s);
   const int hw = dims->d_nope + dims->d_rope;
   mla::finalize_query_rope(dims->dtype, q + dims->d_nope, ld, hw, q_pe, positions, n_tokens, dims->n_heads,
-                           dims->d_rope, dims->rope_theta, s);
+                           dims->d_rope, dims->rope_theta, dims->rope_freqs, s);
   return q;
 }
 

@@ -88,8 +88,9 @@ __device__ __forceinline__ double rope_freq(int j, double base, const double* fr
   return f;
 }
 
-__device__ __forceinline__ void rope_cos_sin(int32_t pos, int j, double base, float* c, float* s) {
-  angle_cos_sin(static_cast<double>(pos) * rope_freq(j, base, nullptr), c, s);
+__device__ __forceinline__ void rope_cos_sin(int32_t pos, int j, double base, const double* freqs, float* c,
+                                             float* s) {
+  angle_cos_sin(static_cast<double>(pos) * rope_freq(j, base, freqs), c, s);
 }
 
 }  // namespace mla

@@ -62,15 +62,16 @@ void gemm_skinny_merged(SkinnyArgs sa, int n_merge, bool out_bf16, hipStream_t s
 // Cache rows from the fp32 projections in `proj` ([T, r + G*d_rope], row stride ld):
 // optional RMSNorm over the latent, RoPE on each rotary-key group, cast, scatter to slots.
 // `proj` holds `splits` partial slices (slice stride `sps` floats) that are summed first.
+// `freqs` (device, d_rope/2 doubles) replaces theta^(-2j/d_rope) when not null.
 void finalize_cache_rows(int dtype, const float* proj, int64_t ld, int splits, int64_t sps,
                          void* cache, const int64_t* slots, const int32_t* positions,
                          int64_t n_tokens, int r, int n_groups, int d_rope, int latent_rmsnorm,
-                         float eps, double theta, hipStream_t s);
+                         float eps, double theta, const double* freqs, hipStream_t s);
 
 // q_pe[t,h,:] = RoPE(proj[t*ld + h*hstride : +d_rope], positions[t]), cast to dtype.
 void finalize_query_rope(int dtype, const float* proj, int64_t ld, int hstride, void* q_pe,
                          const int32_t* positions, int64_t n_tokens, int n_heads, int d_rope,
-                         double theta, hipStream_t s);
+                         double theta, const double* freqs, hipStream_t s);
 
 // dst[t, h, 0:n] = src[t*ld + h*hstride : +n] (fp32 -> dtype), dst dense [n_rows, n_heads, n].
 void cast_heads(int dtype, const float* src, int64_t ld, int hstride, int n_heads, int n, void* dst,

@@ -26,7 +26,8 @@ __global__ __launch_bounds__(256) void cache_rows_kernel(const float* __restrict
                                                          const int32_t* __restrict__ positions,
                                                          int r, int n_groups, int d_rope,
                                                          int latent_rmsnorm, float eps,
-                                                         double rope_base) {
+                                                         double rope_base,
+                                                         const double* __restrict__ freqs) {
   __shared__ float row[1024];  // summed projection row (r + G*d_rope <= 1024)
   __shared__ float cs[kMaxHalf], sn[kMaxHalf];
   __shared__ float red[4];
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(256) void cache_rows_kernel(const float* __restrict
     for (int p = 0; p < kSlices; ++p) part[it][p] = proj[min(p, splits - 1) * sps + t * ld + i];
   }
   const int32_t pos = positions[t];
-  for (int j = threadIdx.x; j < half; j += blockDim.x) rope_cos_sin(pos, j, rope_base, &cs[j], &sn[j]);
+  for (int j = threadIdx.x; j < half; j += blockDim.x) rope_cos_sin(pos, j, rope_base, freqs, &cs[j], &sn[j]);
 #pragma unroll
   for (int it = 0; it < kIt; ++it) {
     const int i = static_cast<int>(threadIdx.x) + 256 * it;
@@ -81,7 +82,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void query_rope_kernel(const float* __restrict__ proj, int64_t ld,
                                                          int hstride, T* __restrict__ q_pe,
                                                          const int32_t* __restrict__ positions,
-                                                         int n_heads, int d_rope, double rope_base) {
+                                                         int n_heads, int d_rope, double rope_base,
+                                                         const double* __restrict__ freqs) {
   const int64_t t = blockIdx.x;
   const int half = d_rope / 2;
   const int32_t pos = positions[t];
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(256) void query_rope_kernel(const float* __restrict
     const int h = i / half, j = i % half;
     const float a = src[h * hstride + j], b = src[h * hstride + j + half];
     float c, sn;
-    rope_cos_sin(pos, j, rope_base, &c, &sn);
+    rope_cos_sin(pos, j, rope_base, freqs, &c, &sn);
     Elem<T>::store(dst, h * d_rope + j, a * c - b * sn);
     Elem<T>::store(dst, h * d_rope + j + half, b * c + a * sn);
   }
@@ -197,13 +199,13 @@ void norm_rows(int dtype, const float* proj, int64_t ld, int splits, int64_t sps
 void finalize_cache_rows(int dtype, const float* proj, int64_t ld, int splits, int64_t sps,
                          void* cache, const int64_t* slots, const int32_t* positions,
                          int64_t n_tokens, int r, int n_groups, int d_rope, int latent_rmsnorm,
-                         float eps, double theta, hipStream_t s) {
+                         float eps, double theta, const double* freqs, hipStream_t s) {
   if (n_tokens <= 0) return;
   const double base = std::pow(theta, -2.0 / d_rope);
   dim3 grid(static_cast<unsigned>(n_tokens));
   auto launch = [&](auto kernel, auto* out) {
     hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, proj, ld, splits, sps, out, slots, positions, r,
-                       n_groups, d_rope, latent_rmsnorm, eps, base);
+                       n_groups, d_rope, latent_rmsnorm, eps, base, freqs);
   };
   if (dtype == kF32) {
     float* out = static_cast<float*>(cache);
@@ -218,17 +220,17 @@ void finalize_cache_rows(int dtype, const float* proj, int64_t ld, int splits, i
 
 void finalize_query_rope(int dtype, const float* proj, int64_t ld, int hstride, void* q_pe,
                          const int32_t* positions, int64_t n_tokens, int n_heads, int d_rope,
-                         double theta, hipStream_t s) {
+                         double theta, const double* freqs, hipStream_t s) {
   if (n_tokens <= 0) return;
   const double base = std::pow(theta, -2.0 / d_rope);
   const int items = n_heads * (d_rope / 2);
   dim3 grid(static_cast<unsigned>(n_tokens), static_cast<unsigned>(std::max(1, std::min(16, items / 256))));
   if (dtype == kF32)
     hipLaunchKernelGGL(query_rope_kernel<float>, grid, dim3(256), 0, s, proj, ld, hstride,
-                       static_cast<float*>(q_pe), positions, n_heads, d_rope, base);
+                       static_cast<float*>(q_pe), positions, n_heads, d_rope, base, freqs);
   else
     hipLaunchKernelGGL(query_rope_kernel<bf16_t>, grid, dim3(256), 0, s, proj, ld, hstride,
-                       static_cast<bf16_t*>(q_pe), positions, n_heads, d_rope, base);
+                       static_cast<bf16_t*>(q_pe), positions, n_heads, d_rope, base, freqs);
 }
 
 }  // namespace mla

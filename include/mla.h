@@ -84,7 +84,28 @@ typedef struct mla_dims {
   float rms_eps;          /* RMSNorm epsilon (unit gain) */
   float softmax_scale;    /* applied to the whole score; <= 0 selects 1/sqrt(d_nope + d_rope) */
   double rope_theta;      /* RoPE base; pair (j, j + d_rope/2) turns by p * theta^(-2j/d_rope) */
+  /* Device float64 [d_rope/2]: the inverse frequency of each rotary pair, used in
+   * place of theta^(-2j/d_rope) by every call that rotates (cache write, absorb,
+   * query and their low-rank forms); NULL selects theta.  A context extension
+   * such as YaRN (Zebra hybrid page: factor 32 over a 32K window) changes only
+   * this table; mla_rope_yarn_table() fills one.  Borrowed: it must stay valid
+   * until the calls that read it have run on their stream.  Key and query rows
+   * must be rotated with the same table. */
+  const double* rope_freqs;
 } mla_dims;
+
+/* YaRN's rescaled inverse frequencies (Peng et al., YaRN: Efficient Context
+ * Window Extension of Large Language Models, the per-pair interpolation it keeps),
+ * written to host memory out[0 .. d_rope/2):
+ *   f_j = theta^(-2j/d_rope); r_j = original_window * f_j / (2 pi) (turns of pair j
+ *   over the pretraining window); g = clamp((r_j - alpha) / (beta - alpha), 0, 1);
+ *   out[j] = (1 - g) * f_j / factor + g * f_j.
+ * The paper uses alpha = 1, beta = 32.  Its attention temperature, logits times
+ * (0.1 ln(factor) + 1)^2, belongs in softmax_scale.  Host only, no HIP call.
+ * MLA_EINVAL for an odd or non-positive d_rope, factor or window <= 0,
+ * beta <= alpha, or a null out. */
+int mla_rope_yarn_table(int32_t d_rope, double theta, double factor, double original_window, double alpha,
+                        double beta, double* out);
 
 /* Bytes of scratch an operation needs for the given sizes (0 if none).
  * op: mla_op.  batch: sequences (decode/prefill).  n_tokens: tokens in the call.

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
         assert n in abi.SIGNATURES, n
     assert lib.mla_version() >= 100
-    assert ctypes.sizeof(abi.MlaDims) == 56
+    assert ctypes.sizeof(abi.MlaDims) == 64
 
 
 def test_dims_validation_codes():
@@ -198,3 +198,33 @@ def test_v4_entry_points_validate_arguments():
     assert lib.mla_v4_query(ctypes.byref(d), p, p, null, p, p, 4, null, p, p, 1 << 40, null) == abi.MLA_EINVAL
     assert lib.mla_v4_output(ctypes.byref(d), p, p, p, 4, p, p, 16, null) == abi.MLA_EWORKSPACE
     assert lib.mla_v4_write_cache(ctypes.byref(d), p, p, p, p, p, 4, p, 10, null, p, 16, null) == abi.MLA_EWORKSPACE
+
+
+def test_yarn_table_and_frequency_pointer():
+    """mla_rope_yarn_table (host code of the library) against the oracle's own YaRN
+    table at the Zebra page's factor 32 over a 32K window; its argument checks; and
+    mla_dims.rope_freqs: accepted when null or 16-byte aligned, rejected otherwise
+    (checked on the host, nothing is dereferenced)."""
+    import numpy as np
+    from oracle import mla_oracle as O
+    abi, lib = _lib()
+    for d_rope, theta, s, win in ((64, 10000.0, 32.0, 32768.0), (8, 10000.0, 32.0, 32768.0),
+                                  (64, 1e6, 4.0, 4096.0), (16, 10000.0, 1.0, 2048.0)):
+        got = np.array(abi.mla_rope_yarn_table(d_rope, theta, s, win))
+        np.testing.assert_allclose(got, O.yarn_inv_freq(d_rope, theta, s, win), rtol=1e-14, atol=0)
+    out = (ctypes.c_double * 32)()
+    f = lib.mla_rope_yarn_table
+    assert f(64, 10000.0, 32.0, 32768.0, 1.0, 32.0, out) == abi.MLA_OK
+    assert f(63, 10000.0, 32.0, 32768.0, 1.0, 32.0, out) == abi.MLA_EINVAL
+    assert f(64, 10000.0, 0.0, 32768.0, 1.0, 32.0, out) == abi.MLA_EINVAL
+    assert f(64, 10000.0, 32.0, 32768.0, 32.0, 1.0, out) == abi.MLA_EINVAL
+    assert f(64, 10000.0, 32.0, 32768.0, 1.0, 32.0, None) == abi.MLA_EINVAL
+    d = abi.dims_of(I.CONFIGS["long_prefill_131k"])
+    assert d.rope_freqs is None and lib.mla_check_dims(ctypes.byref(d)) == abi.MLA_OK
+    d.rope_freqs = 0x10000
+    assert lib.mla_check_dims(ctypes.byref(d)) == abi.MLA_OK
+    d.rope_freqs = 0x10008
+    assert lib.mla_check_dims(ctypes.byref(d)) == abi.MLA_EINVAL
+    with pytest.raises(ValueError):
+        import torch
+        abi.dims_of(I.CONFIGS["long_prefill_131k"], rope_freqs=torch.zeros(31, dtype=torch.float64))

@@ -381,6 +381,59 @@ def test_prefill_expanded_ragged(torch, lengths):
         assert e <= Hh.TOL["bf16"], (nm, e)
 
 
+def test_yarn_table_at_million_positions(torch):
+    """The Zebra page's YaRN extension (factor 32 over a 32K window) at positions near
+    2^20: a frequency table from mla_rope_yarn_table in mla_dims.rope_freqs drives
+    the cache write and the query rotation; the rotary keys, the absorbed prefill
+    and the original-order prefill are checked against the oracle run with its own
+    YaRN table."""
+    import head_latent_attention_kv_amd as M
+    from oracle import mla_oracle as O
+    cfg = I.CONFIGS["long_prefill_131k"]
+    lengths = [300, 45]
+    starts = [1_048_576 - 300, 700_001]
+    _print_case("yarn_table", lengths=lengths, starts=starts)
+    table = torch.tensor(M.mla_rope_yarn_table(cfg.d_rope, cfg.rope_theta, 32.0, 32768.0),
+                         dtype=torch.float64, device="cuda")
+    layer = Hh.make_layer(cfg)
+    layer.dims = M.dims_of(cfg, rope_freqs=table)
+    inv = O.yarn_inv_freq(cfg.d_rope, cfg.rope_theta, 32.0, 32768.0)
+    T = sum(lengths)
+    x = np.concatenate([I.x_rows(cfg, b, 0, n) for b, n in enumerate(lengths)])
+    pos = np.concatenate([np.arange(n) + p0 for n, p0 in zip(lengths, starts)])
+    seg = np.concatenate([np.full(n, b) for b, n in enumerate(lengths)])
+    cache = torch.empty((T, cfg.row_width), dtype=torch.bfloat16, device="cuda")
+    xd = Hh.to_dev(x, cfg.dtype)
+    Hh.write_cache(layer, xd, pos, np.arange(T), cache)
+    q_lat, q_pe = Hh.absorb(layer, xd, pos)
+    out_abs = torch.empty((T, cfg.n_heads, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int64, device="cuda")
+    M.mla_prefill(layer.dims, q_lat, q_pe, cache, cu, max(lengths), layer.w_dev["w_uv"], out_abs)
+    q_nope, q_pe2 = Hh.query(layer, xd, pos)
+    out, _ = Hh.prefill_expanded(layer, q_nope, q_pe2, cache, lengths)
+    torch.cuda.synchronize()
+    w = layer.w_host
+    rows = O.cache_rows(x, w["w_dkv"], w["w_kr"], pos, n_groups=cfg.n_groups, d_rope=cfg.d_rope,
+                        theta=cfg.rope_theta, inv_freq=inv)
+    _, kr_ref = O.split_rows(rows, cfg.rank, cfg.n_groups, cfg.d_rope)
+    _, kr = O.split_rows(Hh.to_host(cache), cfg.rank, cfg.n_groups, cfg.d_rope)
+    _, qr_ref = O.query(x, w["w_qc"], w["w_qr"], pos, n_heads=cfg.n_heads, d_nope=cfg.d_nope,
+                        d_rope=cfg.d_rope, theta=cfg.rope_theta, inv_freq=inv)
+    ref = O.mla_layer(x, x, w, k_pos=pos, q_pos=pos, k_seg=seg, q_seg=seg, n_heads=cfg.n_heads,
+                      n_groups=cfg.n_groups, d_nope=cfg.d_nope, d_rope=cfg.d_rope,
+                      theta=cfg.rope_theta, scale=cfg.softmax_scale, head_chunk=4, inv_freq=inv)
+    errs = {"kr": Hh.rel_err_rows(kr, kr_ref), "q_pe": Hh.rel_err_rows(Hh.to_host(q_pe2), qr_ref),
+            "absorbed": Hh.rel_err_rows(Hh.to_host(out_abs), ref), "expanded": Hh.rel_err_rows(Hh.to_host(out), ref)}
+    # without the table the rotation differs: the check above sees the table
+    plain = O.cache_rows(x, w["w_dkv"], w["w_kr"], pos, n_groups=cfg.n_groups, d_rope=cfg.d_rope,
+                         theta=cfg.rope_theta)
+    errs_plain = Hh.rel_err_rows(kr, O.split_rows(plain, cfg.rank, cfg.n_groups, cfg.d_rope)[1])
+    print("yarn table:", {k: f"{v:.3e}" for k, v in errs.items()}, f"(vs plain theta {errs_plain:.2e})")
+    for nm, e in errs.items():
+        assert e <= Hh.TOL["bf16"], (nm, e)
+    assert errs_plain > 0.1
+
+
 def test_prefill_expanded_restart(torch):
     """Hidden states from position 100 on are scaled 8x, so their queries and
     keys score ~64x higher against each other than against the first rows: the
