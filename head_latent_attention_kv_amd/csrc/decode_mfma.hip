@@ -326,8 +326,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
         if (unit) m_ref = fmaxf(xch[hloc], xch[S::kHeads + hloc]);
       }
       if (unit) {
-        const bool over = emit_p(0, sv);
-        if (lane == 0) flag_lds[wave] = __ballot(over) != 0 ? 1 : 0;
+        const bool over = __ballot(emit_p(0, sv)) != 0;  // every lane votes
+        if (lane == 0) flag_lds[wave] = over ? 1 : 0;
       }
     }
 
@@ -350,13 +350,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
       // scan, P may be out of range; the accumulators are then discarded.
       if constexpr (kAllUnits) {
         const f32x4 sv = score_and_pv(t + 1, t);
-        const bool over = emit_p(t + 1, sv);
-        if (lane == 0) flag_lds[((t + 1) & 1) * kWaves + wave] = __ballot(over) != 0 ? 1 : 0;
+        const bool over = __ballot(emit_p(t + 1, sv)) != 0;
+        if (lane == 0) flag_lds[((t + 1) & 1) * kWaves + wave] = over ? 1 : 0;
       } else {
         if (unit) {
           const f32x4 sv = score(t + 1);
-          const bool over = emit_p(t + 1, sv);
-          if (lane == 0) flag_lds[((t + 1) & 1) * kWaves + wave] = __ballot(over) != 0 ? 1 : 0;
+          const bool over = __ballot(emit_p(t + 1, sv)) != 0;
+          if (lane == 0) flag_lds[((t + 1) & 1) * kWaves + wave] = over ? 1 : 0;
         }
         pv(t);
       }

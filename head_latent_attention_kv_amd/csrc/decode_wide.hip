@@ -347,9 +347,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
     }
     // restart when some score passed its reference's headroom (raw max of the
     // lane's head times the scale; the scale is positive)
-    const bool over = m_lane * qk_scale > m_ref + kSlack;
+    const bool over = __ballot(m_lane * qk_scale > m_ref + kSlack) != 0;  // every lane votes
     lds_barrier();
-    if (lane == 0) flags[wave] = __ballot(over) != 0 ? 1 : 0;
+    if (lane == 0) flags[wave] = over ? 1 : 0;
     lds_barrier();
     int any = 0;
 #pragma unroll

@@ -261,7 +261,8 @@ size_t expanded_k_bytes(const mla_dims* d, int64_t n_tokens) {
 }
 size_t expanded_ws(const mla_dims* d, int64_t n_tokens) {
   return expanded_k_bytes(d, n_tokens) +
-         align_up(static_cast<size_t>(std::max<int64_t>(n_tokens, 0)) * d->n_heads * d->d_v * 2);
+         align_up(static_cast<size_t>(mla::prefill_expanded_vt_cols(std::max<int64_t>(n_tokens, 0))) *
+                  d->n_heads * d->d_v * 2);
 }
 
 // Low-rank query path: [x·W_QAᵀ fp32 slices][normalised rows, layer dtype][q fp32 slices]
@@ -604,7 +605,7 @@ int mla_prefill_expanded(const mla_dims* dims, const void* q_nope, const void* q
   if (batch < 0 || n_tokens < 0) return MLA_EINVAL;
   if (batch == 0 || n_tokens == 0) return MLA_OK;
   if (max_len <= 0) return MLA_EINVAL;
-  if (n_tokens > INT32_MAX) return MLA_ENOTSUP;
+  if (n_tokens > mla::kPrefillExpandedMaxTokens) return MLA_ENOTSUP;
   const AttnShape sh = shape_of(dims);
   if (dims->dtype != MLA_BF16 || !mla::prefill_expanded_supported(sh, dims->d_nope, dims->d_v))
     return MLA_ENOTSUP;
@@ -618,28 +619,42 @@ int mla_prefill_expanded(const mla_dims* dims, const void* q_nope, const void* q
   char* ws = static_cast<char*>(workspace);
   void* k_nope = ws;
   void* v = ws + expanded_k_bytes(dims, n_tokens);
-  // k_nope[h, t, :] = W_UK[h] · c[t]  and  v[h, t, :] = W_UV[h] · c[t]  (c = cache row t, cols 0..r),
+  // k_nope[h, t, :] = W_UK[h] · c[t]  and  vᵀ[h, :, t] = W_UV[h] · c[t]  (c = cache row t, cols 0..r),
   // stored in fp16: three more significant bits than bf16 for the two operands
-  // this order rounds and the absorbed one does not
-  auto expand = [&](const void* w, int n, void* dst) {
-    GemmArgs g{};
-    g.A = cache;
-    g.sAz = 0;
-    g.sAm = sh.row_w;
-    g.B = w;
-    g.sBz = static_cast<int64_t>(n) * dims->rank;
-    g.sBo = dims->rank;
-    g.C = dst;
-    g.sCz = static_cast<int64_t>(T) * n;
-    g.sCm = n;
-    g.M = T;
-    g.N = n;
-    g.K = dims->rank;
-    g.Z = H;
-    mla::gemm_f16_out(g, s);
-  };
-  expand(w_uk, dims->d_nope, k_nope);
-  expand(w_uv, dims->d_v, v);
+  // this order rounds and the absorbed one does not.  v is kept transposed
+  // (rows of T_pad keys, the pad zero) for the attention kernel's PV operand.
+  GemmArgs g{};
+  g.A = cache;
+  g.sAz = 0;
+  g.sAm = sh.row_w;
+  g.B = w_uk;
+  g.sBz = static_cast<int64_t>(dims->d_nope) * dims->rank;
+  g.sBo = dims->rank;
+  g.C = k_nope;
+  g.sCz = static_cast<int64_t>(T) * dims->d_nope;
+  g.sCm = dims->d_nope;
+  g.M = T;
+  g.N = dims->d_nope;
+  g.K = dims->rank;
+  g.Z = H;
+  mla::gemm_f16_out(g, s);
+  const int64_t t_pad = mla::prefill_expanded_vt_cols(T);
+  GemmArgs gv{};
+  gv.A = w_uv;
+  gv.sAz = static_cast<int64_t>(dims->d_v) * dims->rank;
+  gv.sAm = dims->rank;
+  gv.B = cache;
+  gv.sBz = 0;
+  gv.sBo = sh.row_w;
+  gv.C = v;
+  gv.sCz = static_cast<int64_t>(dims->d_v) * t_pad;
+  gv.sCm = t_pad;
+  gv.M = dims->d_v;
+  gv.N = T;
+  gv.K = dims->rank;
+  gv.Z = H;
+  mla::gemm_f16_out(gv, s);
+  mla::prefill_expanded_vt_pad(v, static_cast<int64_t>(H) * dims->d_v, T, s);
   mla::prefill_expanded(sh, q_nope, q_pe, k_nope, v, cache, cu_seqlens, batch, n_tokens, out, s);
   return launch_status();
 }

@@ -128,6 +128,12 @@ void prefill_mfma(const AttnShape& sh, const void* q_lat, const void* q_pe, cons
 // bf16 MFMA causal prefill in the original order (see prefill_expanded.hip):
 // k_nope [H, T, d_nope] and v [H, T, d_v] already expanded (fp16), rotary keys
 // from the cache rows, output [T, H, d_v] bf16.
+// Columns of the transposed value rows vᵀ [H, d_v, cols]: n_tokens rounded up to 32.
+int64_t prefill_expanded_vt_cols(int64_t n_tokens);
+// Largest n_tokens the kernel addresses (128 vᵀ rows of one head within 32-bit offsets).
+constexpr int64_t kPrefillExpandedMaxTokens = 16 * 1024 * 1024 - 32;
+// Zero the pad columns [n_tokens, cols) of `rows` vᵀ rows (fp16).
+void prefill_expanded_vt_pad(void* vt, int64_t rows, int64_t n_tokens, hipStream_t s);
 bool prefill_expanded_supported(const AttnShape& sh, int d_nope, int d_v);
 void prefill_expanded(const AttnShape& sh, const void* q_nope, const void* q_pe, const void* k_nope,
                       const void* v, const void* cache, const int64_t* cu, int batch, int64_t n_tokens,

@@ -10,9 +10,10 @@
 // Causal rule (nanowhale page, SDPA with is_causal): token t attends to the
 // rows cu[b] .. t of its own sequence.
 //
-// Inputs: k_nope [H, T, 128] and v [H, T, 128] in fp16 (expanded by the
-// caller), the rotary keys straight from the bf16 latent cache rows, q_nope
-// [T, H, 128] and q_pe [T, H, DR] in bf16.  Output [T, H, 128] bf16.
+// Inputs: k_nope [H, T, 128] and vᵀ [H, 128, T_pad] in fp16 (expanded by the
+// caller; T_pad = T rounded up to 32, the pad columns zero), the rotary keys
+// straight from the bf16 latent cache rows, q_nope [T, H, 128] and q_pe
+// [T, H, DR] in bf16.  Output [T, H, 128] bf16.
 // Precision: this order rounds two intermediates the absorbed order does not
 // (the expanded keys and values), so they, q_nope and the weights P are fp16
 // inside the kernel (11 significant bits against bf16's 8, same MFMA rate).
@@ -26,17 +27,20 @@
 //   - Sᵀ[32 keys x 64 queries] = K·Qᵀ with v_mfma_f32_32x32x16_bf16: key rows
 //     as the A operand from LDS, Qᵀ as the B operand held in registers.  In
 //     this orientation a lane owns one query column, so the row max is a
-//     lane-local max and the softmax needs no cross-lane traffic;
+//     lane-local max and the softmax needs no cross-lane traffic.  The A
+//     operand's rows are a permutation of the tile's keys chosen so that each
+//     lane's 16 accumulator values are 16 consecutive keys;
 //   - softmax against one reference per query (base 2): the max of the first
-//     tile in which the query has a valid key, with 2^15 of headroom (P is
-//     fp16).  A pass
-//     in which some later score passes the headroom is redone with each
-//     query's true max, so O is never rescaled and stays in the matrix
-//     accumulators for the whole pass;
+//     tile in which the query has a valid key.  No running max is kept: a
+//     weight past fp16's range (a later score about 16 or more above the
+//     reference, in log2 units) turns the row sum into inf, and such a pass is
+//     redone after a max-only scan with each query's true max.  O is never
+//     rescaled and stays in the matrix accumulators for the whole pass;
 //   - Oᵀ[128 dims x 64 queries] += Vᵀ·Pᵀ: the fp16 weights go straight from the
-//     score registers into the B operand (the product's K order is the order
-//     in which a lane holds its keys); Vᵀ fragments are transposed reads
-//     (ds_read_b64_tr_b16) of the V tile at the matching key rows.
+//     score registers into the B operand, so each lane contributes 8
+//     consecutive keys per MFMA, and a Vᵀ fragment is one 16-byte read of a
+//     vᵀ row (the V tile is staged transposed, [128 dims][32 keys]).
+// Key tiles are aligned to 32 keys, so every vᵀ chunk is 16-byte aligned.
 // The score of tile t+1 is issued before the softmax and PV of tile t, so the
 // matrix cores stay busy while the softmax runs.
 // Tiles stream HBM -> LDS with global_load_lds_dwordx4 through a 4-stage ring;
@@ -44,6 +48,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "lds_dma.h"
 #include "mla_device.h"
@@ -52,6 +57,7 @@
 #ifndef MLA_PREFILL_FA_WAVES
 #define MLA_PREFILL_FA_WAVES 8  // waves per workgroup (4: one per SIMD, 8: two per SIMD)
 #endif
+
 
 namespace mla {
 
@@ -63,18 +69,15 @@ constexpr int kBM = 256;            // queries per workgroup
 constexpr int kBN = 32;             // keys per tile
 constexpr int kStages = 4;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kSlack = 15.f;      // headroom (base 2) of the reference: P <= 2^15 fits fp16
 constexpr float kNoMax = -1e30f;    // reference before a query's first valid key
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 template <int DR>
 struct FShape {
-  static_assert(DR % 16 == 0 && DR >= 64 && DR <= 128, "rotary width");
+  static_assert(DR == 64, "rotary width (the chunk keys assume 128-byte rotary rows)");
   static constexpr int kKnBytes = kBN * kDN * 2;
   static constexpr int kKrBytes = kBN * DR * 2;
   static constexpr int kVBytes = kBN * kDV * 2;
@@ -86,23 +89,29 @@ struct FShape {
   static constexpr int kVOps = kVBytes / 1024;
   static constexpr int kOps = kKnOps + kKrOps + kVOps;
   static constexpr int kKrChunks = DR / 8;          // 16-byte chunks of a rotary row
-  static constexpr int kKrRowsPer256 = 16 / kKrChunks;
   static constexpr int kKS = (kDN + DR) / 16;       // score k-steps
   static constexpr int kFlagsOff = kStages * kStageBytes;
   static constexpr int kLdsBytes = kFlagsOff + 64;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
-// XOR keys of the 16-byte chunk slots.  A fragment read of 16 key rows at one
-// chunk (k_nope, rotary key) and a transposed read of 4 V rows x 2 chunks then
-// land on distinct banks.
-__device__ __forceinline__ int kn_key(int row) { return row & 15; }
-template <int DR>
-__device__ __forceinline__ int kr_key(int row) {
-  using S = FShape<DR>;
-  return (row / S::kKrRowsPer256) & (S::kKrChunks - 1);
+// Score row r of the A operand holds key kperm(r) of the tile: the accumulator
+// rows 8a + 4h + b that lane half h holds (a, b < 4) are keys 16h + 4a + b.
+__device__ __forceinline__ int kperm(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
+
+// XOR keys of the 16-byte chunk slots, so that the 16 (or 8) lanes a fragment
+// read serves at once land on distinct banks.  Lanes 16g .. 16g+15 of a score
+// read take key rows with bits {0, 1, 2, 4} varying (bit 3 = g); lanes 16g ..
+// 16g+15 of a vᵀ read take dim rows 16g' .. 16g'+15.
+__device__ __forceinline__ int kn_key(int row) {  // 256-byte rows: a 4-bit key
+  return (row & 3) | ((row >> 2) & 4) | ((row << 1) & 8);
 }
-__device__ __forceinline__ int v_key(int row) { return 4 * (row & 3); }
+__device__ __forceinline__ int kr_key(int row) {  // 128-byte rows: a 3-bit key
+  return ((row >> 1) & 1) | (((row >> 4) & 1) << 1) | (((row ^ (row >> 2)) & 1) << 2);
+}
+__device__ __forceinline__ int v_key(int row) {   // 64-byte rows: a 2-bit key
+  return (((row >> 2) ^ (row >> 1)) & 1) | ((((row >> 3) ^ (row >> 1)) & 1) << 1);
+}
 
 __device__ __forceinline__ float swap_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -136,7 +145,7 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_fa_kernel(
     const bf16_t* __restrict__ q_nope, const bf16_t* __restrict__ q_pe,
     const _Float16* __restrict__ k_nope, const _Float16* __restrict__ v,
     const bf16_t* __restrict__ cache, const int64_t* __restrict__ cu, int batch, int n_tokens,
-    int n_heads, int heads_per_group, int row_w, int r, float scale, bf16_t* __restrict__ out) {
+    int t_pad, int n_heads, int heads_per_group, int row_w, int r, float scale, bf16_t* __restrict__ out) {
   using S = FShape<DR>;
   constexpr int kQB = 8 / W;          // 32-query column blocks per wave
   constexpr int kQW = 32 * kQB;       // queries per wave
@@ -165,8 +174,9 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_fa_kernel(
     return static_cast<int>(cu[lo]);
   };
 
-  // ---- key range of the workgroup and of this wave (tiles of kBN rows from k_lo)
-  const int k_lo = seq_start(q0);
+  // ---- key range of the workgroup and of this wave (tiles of kBN rows from k_lo,
+  // aligned down to a multiple of kBN; keys before the sequence are masked)
+  const int k_lo = seq_start(q0) & ~(kBN - 1);
   const int k_hi = min(q0 + kBM - 1, n_tokens - 1);
   const int n_tiles = (k_hi - k_lo + kBN) / kBN;
   const bool wave_on = qw0 < n_tokens;
@@ -202,52 +212,69 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_fa_kernel(
   wait_vmcnt<0>();  // queries and sequence bounds landed before any tile copy is in flight
 
   // ---- tile copies.  LDS chunk slot p of a row holds global chunk p ^ key(row);
-  // rows past k_hi repeat row k_hi (finite values, masked out).
+  // key rows past k_hi repeat row k_hi, and vᵀ columns past T are the zero pad
+  // (finite values, masked out).
   const char* kn_head = reinterpret_cast<const char*>(k_nope + static_cast<int64_t>(head) * n_tokens * kDN);
-  const char* v_head = reinterpret_cast<const char*>(v + static_cast<int64_t>(head) * n_tokens * kDV);
+  const char* v_head = reinterpret_cast<const char*>(v + static_cast<int64_t>(head) * kDV * t_pad);
+  const uint32_t vt_row = static_cast<uint32_t>(t_pad) * 2;  // 128 rows of it fit 32 bits (host check)
   const char* kr_col = reinterpret_cast<const char*>(cache) +
                        static_cast<int64_t>(r + (head / heads_per_group) * DR) * 2;
   const int row_bytes = row_w * 2;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)smem));
 
+  // Per-lane source offsets of this wave's copies, computed once: row clamping
+  // (rows past k_hi repeat row k_hi) changes them only in a ragged last tile.
+  constexpr int kKnW = S::kKnOps / W, kVW = S::kVOps / W, kKrW = (S::kKrOps + W - 1) / W;
+  auto dma_offsets = [&](int valid, uint32_t (&okn)[kKnW], uint32_t (&ov)[kVW], uint32_t (&okr)[kKrW]) {
+    int ln = lane;
+    __asm__ volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < kKnW; ++i) {
+      const int L = (wave + W * i) * 64 + ln;
+      const int row = L >> 4, p = L & 15;
+      okn[i] = static_cast<uint32_t>(min(row, valid - 1) * (kDN * 2) + ((p ^ kn_key(row)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < kVW; ++i) {  // vᵀ: 128 dim rows of 64 bytes (32 keys)
+      const int L = (wave + W * i) * 64 + ln;
+      const int row = L >> 2, p = L & 3;
+      ov[i] = static_cast<uint32_t>(row) * vt_row + static_cast<uint32_t>((p ^ v_key(row)) << 4);
+    }
+#pragma unroll
+    for (int i = 0; i < kKrW; ++i) {
+      const int L = (wave + W * i) * 64 + ln;
+      const int row = L / S::kKrChunks, p = L % S::kKrChunks;
+      okr[i] = static_cast<uint32_t>(min(row, valid - 1) * row_bytes + ((p ^ kr_key(row)) << 4));
+    }
+  };
+  uint32_t full_kn[kKnW], full_v[kVW], full_kr[kKrW];
+  dma_offsets(kBN, full_kn, full_v, full_kr);
+
   auto issue_tile = [&](int tt) {
     const int kt0 = k_lo + tt * kBN;
     const int valid = min(kBN, k_hi + 1 - kt0);
     const uint32_t dst = lds0 + (tt % kStages) * S::kStageBytes;
-    int ln = lane;
-    __asm__ volatile("" : "+v"(ln));
     const char* kn_t = kn_head + static_cast<int64_t>(kt0) * (kDN * 2);
-    const char* v_t = v_head + static_cast<int64_t>(kt0) * (kDV * 2);
+    const char* v_t = v_head + static_cast<int64_t>(kt0) * 2;
     const char* kr_t = kr_col + static_cast<int64_t>(kt0) * row_bytes;
+    uint32_t okn[kKnW], ov[kVW], okr[kKrW];
 #pragma unroll
-    for (int i = 0; i < S::kKnOps / W; ++i) {
-      const int j = wave + W * i;
-      const int L = j * 64 + ln;
-      const int row = L >> 4, p = L & 15;
-      const int rr = min(row, valid - 1);
-      global_to_lds16(kn_t, static_cast<uint32_t>(rr * (kDN * 2) + ((p ^ kn_key(row)) << 4)),
-                      __builtin_amdgcn_readfirstlane(dst + j * 1024));
-    }
+    for (int i = 0; i < kKnW; ++i) okn[i] = full_kn[i];
 #pragma unroll
-    for (int i = 0; i < S::kVOps / W; ++i) {
-      const int j = wave + W * i;
-      const int L = j * 64 + ln;
-      const int row = L >> 4, p = L & 15;
-      const int rr = min(row, valid - 1);
-      global_to_lds16(v_t, static_cast<uint32_t>(rr * (kDV * 2) + ((p ^ v_key(row)) << 4)),
-                      __builtin_amdgcn_readfirstlane(dst + S::kVOff + j * 1024));
-    }
+    for (int i = 0; i < kVW; ++i) ov[i] = full_v[i];
 #pragma unroll
-    for (int i = 0; i < (S::kKrOps + W - 1) / W; ++i) {
-      const int j = wave + W * i;
-      if (j < S::kKrOps) {
-        const int L = j * 64 + ln;
-        const int row = L / S::kKrChunks, p = L % S::kKrChunks;
-        const int rr = min(row, valid - 1);
-        global_to_lds16(kr_t, static_cast<uint32_t>(rr * row_bytes + ((p ^ kr_key<DR>(row)) << 4)),
-                        __builtin_amdgcn_readfirstlane(dst + S::kKrOff + j * 1024));
-      }
-    }
+    for (int i = 0; i < kKrW; ++i) okr[i] = full_kr[i];
+    if (valid < kBN) dma_offsets(valid, okn, ov, okr);  // uniform branch, last tile only
+#pragma unroll
+    for (int i = 0; i < kKnW; ++i)
+      global_to_lds16(kn_t, okn[i], __builtin_amdgcn_readfirstlane(dst + (wave + W * i) * 1024));
+#pragma unroll
+    for (int i = 0; i < kVW; ++i)
+      global_to_lds16(v_t, ov[i], __builtin_amdgcn_readfirstlane(dst + S::kVOff + (wave + W * i) * 1024));
+#pragma unroll
+    for (int i = 0; i < kKrW; ++i)
+      if (wave + W * i < S::kKrOps)
+        global_to_lds16(kr_t, okr[i], __builtin_amdgcn_readfirstlane(dst + S::kKrOff + (wave + W * i) * 1024));
   };
   const bool ops_hi = wave < S::kOps % W || S::kOps % W == 0;
   auto wait_tile = [&](int tt, int last_issued) {
@@ -264,50 +291,45 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_fa_kernel(
   };
 
   // ---- fragment addressing (byte offsets inside a stage)
-  // K: lane reads key row l32, dims 16ks + 8hh .. +7
-  const int kn_base = l32 * (kDN * 2);
-  const int kn_x = kn_key(l32);
-  const int kr_base = S::kKrOff + l32 * (DR * 2);
-  const int kr_x = kr_key<DR>(l32);
+  // K: lane reads key row kperm(l32), dims 16ks + 8hh .. +7
+  const int krow = kperm(l32);
+  const int kn_base = krow * (kDN * 2);
+  const int kn_x = kn_key(krow);
+  const int kr_base = S::kKrOff + krow * (DR * 2);
+  const int kr_x = kr_key(krow);
   auto kfrag = [&](const unsigned char* st, int ks) {
     int off;
     if (ks < kDN / 16) off = kn_base + (((2 * ks + hh) ^ kn_x) << 4);
     else off = kr_base + (((2 * (ks - kDN / 16) + hh) ^ kr_x) << 4);
     return *reinterpret_cast<const uint4*>(st + off);
   };
-  // Vᵀ: lane (group g = lane / 16, s = lane % 16) addresses row 4hh + s/4 (+ 16 ks2,
-  // + 8 for the second read), dims 32db + 16(g & 1) + 4(s & 3); it receives dim
-  // 32db + l32 at 4 consecutive key rows.
-  const int vs = lane & 15;
-  const int v_row = 4 * hh + (vs >> 2);
-  const int v_x = v_key(v_row);
-  const int v_chunk = 2 * ((lane >> 4) & 1) + ((vs & 3) >> 1);
-  const int v_sub = 8 * (vs & 1);
-  auto vfrag = [&](const unsigned char* st, int db, int ks2) {
-    const int col = ((((4 * db) + v_chunk) ^ v_x) << 4) + v_sub;
-    const unsigned char* plo = st + S::kVOff + (16 * ks2 + v_row) * (kDV * 2) + col;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(plo));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(plo + 8 * (kDV * 2)));
-    return __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  // Vᵀ: lane reads dim row 32db + l32 at keys 16hh + 8s2 .. +7 (chunk 2hh + s2);
+  // the row's key depends on l32 only (32db keeps bits 0..3)
+  const int v_x = v_key(l32);
+  auto vfrag = [&](const unsigned char* st, int db, int s2) {
+    const int off = S::kVOff + (32 * db + l32) * (kBN * 2) + (((2 * hh + s2) ^ v_x) << 4);
+    return *reinterpret_cast<const f16x8*>(st + off);
   };
 
-  // Sᵀ[qb][i]: key 8(i/4) + 4hh + (i%4) of the tile, query qv[qb]
+  // Sᵀ[qb][i]: key 16hh + i of the tile, query qv[qb]
   auto score = [&](const unsigned char* st, f32x16 (&sc)[kQB]) {
     const f32x16 z = {};
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) sc[qb] = z;
-    uint4 kf[2];
-    kf[0] = kfrag(st, 0);
+    constexpr int kPF = 2;  // K fragments in flight
+    uint4 kf[kPF];
+#pragma unroll
+    for (int i = 0; i < kPF - 1; ++i) kf[i] = kfrag(st, i);
 #pragma unroll
     for (int ks = 0; ks < S::kKS; ++ks) {
-      if (ks + 1 < S::kKS) kf[(ks + 1) & 1] = kfrag(st, ks + 1);
+      if (ks + kPF - 1 < S::kKS) kf[(ks + kPF - 1) % kPF] = kfrag(st, ks + kPF - 1);
       if (ks < kKN) {
-        const f16x8 a = __builtin_bit_cast(f16x8, kf[ks & 1]);
+        const f16x8 a = __builtin_bit_cast(f16x8, kf[ks % kPF]);
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb)
           sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qn[qb][ks], sc[qb], 0, 0, 0);
       } else {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, kf[ks & 1]);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, kf[ks % kPF]);
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb)
           sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[qb][ks - kKN], sc[qb], 0, 0, 0);
@@ -319,7 +341,7 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_fa_kernel(
     for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = kt0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        const int key = kt0 + 16 * hh + i;
         sc[qb][i] = (key >= qst[qb] && key <= qv[qb]) ? sc[qb][i] : -INFINITY;
       }
   };
@@ -328,29 +350,33 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_fa_kernel(
   float m_lane[kQB], l_run[kQB];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) m_ref[qb] = kNoMax;
-  bool over;
   f32x16 o[kQB][4];
   const f16x2 ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};  // row sum of the fp16 weights
 
-  // max of the tile's scores per query; the reference is set at the query's
-  // first tile with a valid key
-  auto tile_max = [&](const f32x16 (&sc)[kQB]) {
-    float lmax[kQB];
+  auto lane_max = [&](const f32x16& s) {
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    return mx;
+  };
+  // The reference of a query is set at its first tile with a valid key.
+  auto set_ref = [&](const f32x16 (&sc)[kQB]) {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
-      const f32x16 s = sc[qb];
-      float mx = s[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-      lmax[qb] = mx;
-      m_lane[qb] = fmaxf(m_lane[qb], mx);
-    }
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const float m = swap_max(lmax[qb]) * qk;
+      const float m = swap_max(lane_max(sc[qb])) * qk;
       m_ref[qb] = (m_ref[qb] == kNoMax && m != -INFINITY) ? m : m_ref[qb];
-      over = over || (lmax[qb] * qk > m_ref[qb] + kSlack);
     }
+  };
+  auto ref_missing = [&]() {
+    bool miss = false;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) miss = miss || m_ref[qb] == kNoMax;
+    return __builtin_amdgcn_ballot_w64(miss) != 0;
+  };
+  // running max of the scores (the rare max-only pass)
+  auto scan_max = [&](const f32x16 (&sc)[kQB]) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) m_lane[qb] = fmaxf(m_lane[qb], lane_max(sc[qb]));
   };
   // w[qb][k]: fp16 pair (p_2k, p_2k+1) of query block qb
   uint32_t w[kQB][8];
@@ -390,22 +416,20 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_fa_kernel(
       }
   };
 
+  // Passes: 0 weighs every tile against the first-tile reference.  A weight
+  // past fp16's range (a later score more than ~2^16 above the reference)
+  // turns the row sum into inf; then pass 1 scans the true max of every
+  // query and pass 2 weighs again against it.  All waves take the same passes.
   int* flags = reinterpret_cast<int*>(smem + S::kFlagsOff);
-  for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      m_lane[qb] = -INFINITY;
-      l_run[qb] = 0.f;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[qb][db] = f32x16{};
-    }
-    over = false;
-
-    auto tile_scores = [&](int t, f32x16 (&sc)[kQB]) { score(smem + (t % kStages) * S::kStageBytes, sc); };
-    // Every active wave takes every tile of the workgroup's range: tiles outside
-    // its own queries' ranges are masked out (a few tiles per workgroup).
-    // Iteration t issues the scores of tile t+1 before the softmax and PV of
-    // tile t, so the matrix core has work while the softmax runs.
+  auto tile_scores = [&](int t, f32x16 (&sc)[kQB]) { score(smem + (t % kStages) * S::kStageBytes, sc); };
+  // One pass over the workgroup's tiles: weights and PV, or (kScan) the running
+  // max only.  Every active wave takes every tile of the workgroup's range:
+  // tiles outside its own queries' ranges are masked out (a few tiles per
+  // workgroup).  Iteration t issues the scores of tile t+1 before the softmax
+  // and PV of tile t, so the matrix core has work while the softmax runs.
+  auto run_pass = [&](auto scan_c) {
+    constexpr bool kScan = decltype(scan_c)::value;
+    bool need_ref = !kScan && ref_missing();
 #pragma unroll
     for (int tt = 0; tt < kStages - 1; ++tt)
       if (tt < n_tiles) issue_tile(tt);
@@ -424,30 +448,61 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_fa_kernel(
       if (!wave_on) return;
       const int kt0 = k_lo + t * kBN;
       if (kt0 + kBN - 1 > qw0 || kt0 < start_last) mask(cur, kt0);
-      tile_max(cur);
-      tile_scores(t + 1, nxt);  // past the last tile this reads a stale buffer; unused
-      weights(cur);
-      pv(smem + (t % kStages) * S::kStageBytes);
+      if constexpr (kScan) {
+        scan_max(cur);
+        tile_scores(t + 1, nxt);
+      } else {
+        if (need_ref) {  // uniform; only until every query of the wave has met a valid key
+          set_ref(cur);
+          need_ref = ref_missing();
+        }
+        tile_scores(t + 1, nxt);  // past the last tile this reads a stale buffer; unused
+        weights(cur);
+        pv(smem + (t % kStages) * S::kStageBytes);
+      }
     };
     for (int t = 0; t < n_tiles; t += 2) {
       iter(t, sa, sb);
       if (t + 1 < n_tiles) iter(t + 1, sb, sa);
     }
+    lds_barrier();  // every wave is done with the ring before another pass refills it
+  };
 
-    lds_barrier();
-    if (lane == 0) flags[wave] = __builtin_amdgcn_ballot_w64(over) != 0 ? 1 : 0;
-    lds_barrier();
-    int any = 0;
+  // Pass 0 weighs every tile against the first-tile reference.  A weight past
+  // fp16's range (a later score about 16 or more above the reference, log2
+  // units) turns the row sum into inf; then a max-only pass finds every
+  // query's true max and a last pass weighs again against it.  All waves take
+  // the same passes.
+  auto reset = [&]() {
 #pragma unroll
-    for (int i = 0; i < W; ++i) any |= flags[i];
-    if (any == 0) break;
-    // second pass with each query's true max
+    for (int qb = 0; qb < kQB; ++qb) {
+      m_lane[qb] = -INFINITY;
+      l_run[qb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[qb][db] = f32x16{};
+    }
+  };
+  reset();
+  run_pass(std::false_type{});
+  bool over = false;
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) over = over || !(l_run[qb] <= 3.0e38f);
+  const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;  // every lane votes
+  if (lane == 0) flags[wave] = wave_on && wave_over ? 1 : 0;
+  lds_barrier();
+  int any = 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) any |= flags[i];
+  if (any != 0) {
+    reset();
+    run_pass(std::true_type{});
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       const float m = swap_max(m_lane[qb]) * qk;
       m_ref[qb] = m == -INFINITY ? kNoMax : m;
     }
-    lds_barrier();  // flags read everywhere before they are rewritten
+    reset();
+    run_pass(std::false_type{});
   }
 
   // ---- epilogue: Oᵀ[qb][db][i] is dim 32db + 8(i/4) + 4hh + (i%4) of query qv[qb]
@@ -474,6 +529,7 @@ template <int DR, int W>
 void launch_fa(const AttnShape& sh, const void* q_nope, const void* q_pe, const void* k_nope,
                const void* v, const void* cache, const int64_t* cu, int batch, int n_tokens,
                void* out, hipStream_t s) {
+  const int t_pad = static_cast<int>(prefill_expanded_vt_cols(n_tokens));
   using S = FShape<DR>;
   auto kern = prefill_fa_kernel<DR, W>;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -482,11 +538,29 @@ void launch_fa(const AttnShape& sh, const void* q_nope, const void* q_pe, const 
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(n_qt), static_cast<unsigned>(sh.H)), dim3(64 * W),
                      S::kLdsBytes, s, static_cast<const bf16_t*>(q_nope), static_cast<const bf16_t*>(q_pe),
                      static_cast<const _Float16*>(k_nope), static_cast<const _Float16*>(v),
-                     static_cast<const bf16_t*>(cache), cu, batch, n_tokens, sh.H, sh.H / sh.G, sh.row_w,
+                     static_cast<const bf16_t*>(cache), cu, batch, n_tokens, t_pad, sh.H, sh.H / sh.G, sh.row_w,
                      sh.r, sh.scale, static_cast<bf16_t*>(out));
 }
 
 }  // namespace
+
+int64_t prefill_expanded_vt_cols(int64_t n_tokens) { return (n_tokens + kBN - 1) / kBN * kBN; }
+
+namespace {
+__global__ __launch_bounds__(256) void vt_pad_kernel(_Float16* __restrict__ vt, int64_t rows, int64_t cols,
+                                                     int64_t n_tokens) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (row >= rows) return;
+  for (int64_t c = n_tokens; c < cols; ++c) vt[row * cols + c] = static_cast<_Float16>(0.f);
+}
+}  // namespace
+
+void prefill_expanded_vt_pad(void* vt, int64_t rows, int64_t n_tokens, hipStream_t s) {
+  const int64_t cols = prefill_expanded_vt_cols(n_tokens);
+  if (cols == n_tokens || rows <= 0) return;
+  hipLaunchKernelGGL(vt_pad_kernel, dim3(static_cast<unsigned>((rows + 255) / 256)), dim3(256), 0, s,
+                     static_cast<_Float16*>(vt), rows, cols, n_tokens);
+}
 
 bool prefill_expanded_supported(const AttnShape& sh, int d_nope, int d_v) {
   return d_nope == kDN && d_v == kDV && sh.d_rope == 64 && sh.H % sh.G == 0 && sh.H <= 65535 &&

@@ -272,8 +272,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    const bool wave_over = __ballot(over) != 0;  // every lane votes
     lds_barrier();
-    if (lane == 0) flags[wave] = __ballot(over) != 0 ? 1 : 0;
+    if (lane == 0) flags[wave] = wave_over ? 1 : 0;
     lds_barrier();
     int any = 0;
 #pragma unroll

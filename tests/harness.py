@@ -103,14 +103,19 @@ def prefill_expanded(layer: DeviceLayer, q_nope, q_pe, cache, lengths):
 
 def expanded_kv(layer: DeviceLayer, ws, T: int):
     """The fp16 k_nope [H, T, d_nope] and v [H, T, d_v] an mla_prefill_expanded call
-    left in its workspace, as host arrays."""
+    left in its workspace, as host arrays.  The workspace holds k_nope [H, T, d_nope]
+    and then vᵀ [H, d_v, T_pad] (T rounded up to 32, the pad columns zero); the pad
+    is checked to be zero here."""
     torch = torch_mod()
     cfg = layer.cfg
     nk = cfg.n_heads * T * cfg.d_nope
     k_bytes = (nk * 2 + 255) // 256 * 256
+    t_pad = (T + 31) // 32 * 32
     k = ws[:nk * 2].view(torch.float16).view(cfg.n_heads, T, cfg.d_nope)
-    v = ws[k_bytes:k_bytes + cfg.n_heads * T * cfg.d_v * 2].view(torch.float16).view(cfg.n_heads, T, cfg.d_v)
-    return to_host(k), to_host(v)
+    vt = ws[k_bytes:k_bytes + cfg.n_heads * cfg.d_v * t_pad * 2].view(torch.float16)
+    vt = to_host(vt.view(cfg.n_heads, cfg.d_v, t_pad))
+    assert not vt[:, :, T:].any(), "vᵀ pad columns not zero"
+    return to_host(k), np.ascontiguousarray(vt[:, :, :T].transpose(0, 2, 1))
 
 
 @dataclasses.dataclass

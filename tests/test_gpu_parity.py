@@ -474,6 +474,108 @@ def test_prefill_expanded_restart(torch):
     assert err <= Hh.TOL["bf16"], err
 
 
+def _quiet(t, sel, factor=0.02):
+    """Scale the rows of t picked by the boolean index sel (a host mask over the
+    leading axes it names) by factor, in t's own dtype."""
+    torch = Hh.torch_mod()
+    m = torch.ones(sel.shape, dtype=torch.float32)
+    m[torch.from_numpy(sel)] = factor
+    while m.dim() < t.dim():
+        m = m.unsqueeze(-1)
+    return (t.float() * m.to(t.device)).to(t.dtype).contiguous()
+
+
+@pytest.mark.parametrize("name,lengths", [("deepseek_v2_decode", [700, 2100, 90]),
+                                          ("qwen25_7b_decode", [1500, 333])])
+def test_decode_restart_one_head(torch, name, lengths):
+    """As the decode restart test, but every head's query except head 5 is scaled
+    down 50x, so only head 5's scores pass the reference's headroom.  The lanes
+    that see it are not the first lane of their wave, so this checks that the
+    restart vote covers every lane."""
+    import head_latent_attention_kv_amd as M
+    cfg = I.CONFIGS[name]
+    _print_case("decode_restart_one_head", cfg=name, lengths=lengths)
+    layer = Hh.make_layer(cfg)
+    run = Hh.build_decode(layer, np.array(lengths), key_boost=(40, 30.0))
+    quiet = np.ones((len(lengths), cfg.n_heads), bool)
+    quiet[:, 5] = False
+    q_lat, q_pe = _quiet(run.q_lat, quiet), _quiet(run.q_pe, quiet)
+    out = torch.empty_like(run.out)
+    M.mla_decode(layer.dims, q_lat, q_pe, run.cache, torch.from_numpy(run.starts).cuda(),
+                 torch.from_numpy(run.lengths.astype(np.int32)).cuda(), int(max(lengths)),
+                 layer.w_dev["w_uv"], out)
+    torch.cuda.synchronize()
+    got, cache_h = Hh.to_host(out), Hh.to_host(run.cache)
+    ql, qp = Hh.to_host(q_lat), Hh.to_host(q_pe)
+    err = 0.0
+    for b, n in enumerate(run.lengths):
+        rows_gpu = cache_h[run.starts[b]:run.starts[b] + int(n)]
+        ref = Hh.oracle_absorbed_rows(cfg, layer.w_host, ql[b], qp[b], rows_gpu)
+        err = max(err, Hh.rel_err_rows(got[b], ref))
+    print(f"{name} restart, head 5 only {lengths}: attn={err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= Hh.TOL[cfg.dtype], err
+
+
+@pytest.mark.parametrize("order", ["expanded", "absorbed"])
+def test_prefill_restart_not_first_lane(torch, order):
+    """Hidden states from position 100 on are scaled 12x, so later tiles pass the
+    first-tile reference of most queries by far more than either kernel's
+    headroom; the queries the first lane of each wave holds are scaled down 50x
+    (tokens t % 32 == 0 in the original order, head 0 in the absorbed order), so
+    the restart must come from the other lanes' votes.  Reference: the oracle's
+    attention definition on the operands the kernel reads."""
+    import head_latent_attention_kv_amd as M
+    from oracle import mla_oracle as O
+    cfg = I.CONFIGS["long_prefill_131k"]
+    lengths = [600, 300]
+    _print_case("prefill_restart_not_first_lane", order=order, lengths=lengths)
+    layer = Hh.make_layer(cfg)
+    T = sum(lengths)
+    xs = []
+    for b, n in enumerate(lengths):
+        xb = I.x_rows(cfg, b, 0, n, quantized=False)
+        xb[100:] *= np.float32(12.0)
+        xs.append(I.quantize(xb, cfg.dtype))
+    x = np.concatenate(xs)
+    pos = np.concatenate([np.arange(n) for n in lengths])
+    seg = np.concatenate([np.full(n, b) for b, n in enumerate(lengths)])
+    cache = torch.empty((T, cfg.row_width), dtype=torch.bfloat16, device="cuda")
+    xd = Hh.to_dev(x, cfg.dtype)
+    Hh.write_cache(layer, xd, pos, np.arange(T), cache)
+    allowed = (seg[:, None] == seg[None, :]) & (pos[None, :] <= pos[:, None])
+    c, kr = O.split_rows(Hh.to_host(cache), cfg.rank, cfg.n_groups, cfg.d_rope)
+    if order == "expanded":
+        q_nope, q_pe = Hh.query(layer, xd, pos)
+        quiet = np.zeros((T, cfg.n_heads), bool)
+        quiet[np.arange(T) % 32 == 0] = True
+        q_nope, q_pe = _quiet(q_nope, quiet), _quiet(q_pe, quiet)
+        out, ws = Hh.prefill_expanded(layer, q_nope, q_pe, cache, lengths)
+        torch.cuda.synchronize()
+        kn, v = Hh.expanded_kv(layer, ws, T)
+        Q = np.concatenate([Hh.to_host(q_nope), Hh.to_host(q_pe)], axis=-1)
+        K = np.concatenate([kn.transpose(1, 0, 2), np.repeat(kr, cfg.n_heads, 1)], axis=-1)
+        ref = O.softmax_attention(Q, K, v.transpose(1, 0, 2), allowed, cfg.softmax_scale)
+    else:
+        q_lat, q_pe = Hh.absorb(layer, xd, pos)
+        quiet = np.zeros((T, cfg.n_heads), bool)
+        quiet[:, 0] = True
+        q_lat, q_pe = _quiet(q_lat, quiet), _quiet(q_pe, quiet)
+        out = torch.empty((T, cfg.n_heads, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int64, device="cuda")
+        M.mla_prefill(layer.dims, q_lat, q_pe, cache, cu, max(lengths), layer.w_dev["w_uv"], out)
+        torch.cuda.synchronize()
+        Q = np.concatenate([Hh.to_host(q_lat), Hh.to_host(q_pe)], axis=-1)               # [T, H, r + dr]
+        K = np.concatenate([c, kr[:, 0]], axis=-1)[:, None, :].repeat(cfg.n_heads, 1)
+        o_lat = O.softmax_attention(Q, K, np.repeat(c[:, None, :], cfg.n_heads, 1), allowed, cfg.softmax_scale)
+        ref = np.einsum("hvc,thc->thv", layer.w_host["w_uv"].astype(np.float64), o_lat)
+    got = Hh.to_host(out)
+    err = Hh.rel_err_rows(got, ref)
+    print(f"prefill restart, first lanes quiet ({order}): attn {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= Hh.TOL["bf16"], err
+
+
 # ----------------------------------------------------------------------------
 # beyond the attention: the low-rank query path and the output projection
 # ----------------------------------------------------------------------------
