@@ -564,7 +564,7 @@ int mla_prefill(const mla_dims* dims, const void* q_lat, const void* q_pe, const
   AttnShape sh = shape_of(dims);
   float* o_lat = static_cast<float*>(workspace);
   if (dims->dtype == MLA_BF16 && mla::prefill_mfma_supported(sh))
-    mla::prefill_mfma(sh, q_lat, q_pe, cache, cu_seqlens, batch, n_tokens, max_len, o_lat, s);
+    mla::prefill_mfma(sh, q_lat, q_pe, cache, cu_seqlens, batch, n_tokens, max_len, o_lat, nullptr, nullptr, s);
   else
     mla::attend_generic(dims->dtype, sh, q_lat, q_pe, cache, nullptr, nullptr, cu_seqlens, batch,
                         n_tokens, 1, max_len, nullptr, nullptr, o_lat, s);
@@ -1042,8 +1042,11 @@ int mla_v4_prefill(const mla_v4_dims* dims, const void* q, const void* cache, co
   void* part_o = base;
   float* part_ml = reinterpret_cast<float*>(
       base + align_up(static_cast<size_t>(n_tokens) * dims->n_heads * dims->head_dim * 2));
-  mla::attend_generic(dims->dtype, sh, q, nullptr, cache, nullptr, nullptr, cu_seqlens, batch, n_tokens, 1,
-                      max_len, part_o, part_ml, nullptr, s);
+  if (dims->dtype == MLA_BF16 && mla::prefill_mfma_supported(sh))
+    mla::prefill_mfma(sh, q, nullptr, cache, cu_seqlens, batch, n_tokens, max_len, nullptr, part_o, part_ml, s);
+  else
+    mla::attend_generic(dims->dtype, sh, q, nullptr, cache, nullptr, nullptr, cu_seqlens, batch, n_tokens, 1,
+                        max_len, part_o, part_ml, nullptr, s);
   mla::v4_merge(dims->dtype, part_o, part_ml, n_tokens, 1, sh.H, dims->head_dim, dims->d_rope, sink, nullptr,
                 cu_seqlens, batch, dims->rope_theta, rope_freqs, out, s);
   return launch_status();

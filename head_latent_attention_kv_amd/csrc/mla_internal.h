@@ -121,9 +121,12 @@ void decode_mfma(const AttnShape& sh, const void* q_lat, const void* q_pe, const
 
 // bf16 MFMA causal prefill kernel for the shapes it supports (see prefill_mfma.hip).
 bool prefill_mfma_supported(const AttnShape& sh);
+// Output: normalised o_ fp32 [T, H, r] in o_out, or (part_o non-null) bf16 o_ in
+// part_o [T, H, r] with (reference max, row sum) per (token, head) in part_ml
+// [T, H, 2] (base 2), a one-split state for the merge that adds a sink.
 void prefill_mfma(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
                   const int64_t* cu, int batch, int64_t n_tokens, int max_len, float* o_out,
-                  hipStream_t s);
+                  void* part_o, float* part_ml, hipStream_t s);
 
 // bf16 MFMA causal prefill in the original order (see prefill_expanded.hip):
 // k_nope [H, T, d_nope] and v [H, T, d_v] already expanded (fp16), rotary keys

@@ -24,7 +24,16 @@
 //     a lane holds its keys), C read transposed from the tile with
 //     ds_read_b64_tr_b16 at the matching row bases.
 // Blocks of later tokens (longer key ranges) are dispatched first.
-// Output: normalised o_ [n_tokens, H, r] fp32.
+// Output: normalised o_ [n_tokens, H, r] fp32; or, as a one-split softmax state
+// for a caller that still folds in more terms (the V4 variant's attention
+// sink), o_ in bf16 with its (reference, row sum) pair per (token, head).
+// With H < 16 heads (H dividing 16) the 16 MFMA columns of a wave are 16/H
+// consecutive tokens times H heads, each lane masking for its own column's
+// token, and a workgroup covers 8·16/H tokens.  The V4
+// variant (nanowhale page: one KV head of 512 dims used as key and value) runs
+// the same kernel with r = row width = 512 and no separate rotary key; there
+// the weights enter PV as a bf16 hi + lo pair (two MFMAs), since bf16 weights
+// against the bf16 rows that are both key and value leave too little margin.
 #include <math.h>
 
 #include <algorithm>
@@ -54,7 +63,7 @@ __device__ __forceinline__ int swz(int c, int r) { return (c & ~7) | ((c ^ (r >>
 
 template <int R, int RW>
 struct PShape {
-  static_assert(R % 16 == 0 && RW % 32 == 0 && RW > R, "row layout");
+  static_assert(R % 16 == 0 && RW % 32 == 0 && RW >= R, "row layout");
   static constexpr int kRowBytes = RW * 2;
   static constexpr int kRowChunks = kRowBytes / 16;
   static_assert(kRowChunks % 8 == 0, "swizzle groups of eight chunks");
@@ -65,6 +74,8 @@ struct PShape {
   static_assert(3 * kDmaPerWave < 64, "vmcnt range");
   static constexpr int kSteps = RW / 32;     // score k-steps
   static constexpr int kNB = R / 16;         // PV column blocks
+  static constexpr bool kSplitP = RW == R;   // K = V rows: weights as hi + lo bf16
+  static constexpr int kLA = kSplitP ? 2 : 3;  // C fragments in flight
   static constexpr int kLdsBytes = kStages * kTileBytes + 64;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
@@ -78,7 +89,8 @@ template <int R, int RW>
 __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
     const bf16_t* __restrict__ q_lat, const bf16_t* __restrict__ q_pe,
     const bf16_t* __restrict__ cache, const int64_t* __restrict__ cu, int batch, int64_t n_tokens,
-    int n_groups, int d_rope, float scale, float* __restrict__ o_out) {
+    int n_heads, int n_groups, int d_rope, float scale, float* __restrict__ o_out,
+    bf16_t* __restrict__ part_o, float* __restrict__ part_ml) {
   using S = PShape<R, RW>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   int64_t* range = reinterpret_cast<int64_t*>(smem + kStages * S::kTileBytes);  // [2][kWaves/2] scratch
@@ -89,12 +101,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
 
-  // ---- this wave's token and its key rows [seq_lo, t]
-  const int64_t n_blocks = (n_tokens + kWaves - 1) / kWaves;
+  // ---- MFMA column l16 of this wave is (token t, head hc): token slot l16 / H
+  // of the wave's 16/H tokens.  Its key rows are [seq_lo, t].
+  const int tpw = kHeads / n_heads;
+  const int64_t block_tokens = static_cast<int64_t>(kWaves) * tpw;
+  const int64_t n_blocks = (n_tokens + block_tokens - 1) / block_tokens;
   const int64_t block = n_blocks - 1 - blockIdx.x;  // longest key ranges first
-  const int64_t t = block * kWaves + wave;
+  const int64_t wave_t0 = block * block_tokens + static_cast<int64_t>(wave) * tpw;
+  const int hc = l16 % n_heads;
+  const int64_t t = wave_t0 + l16 / n_heads;
   const bool active = t < n_tokens;
-  int64_t seq_lo = 0;
+  const int64_t last_t = min(block * block_tokens + block_tokens - 1, n_tokens - 1);
+  int64_t seq_lo = last_t;
   if (active) {
     int lo = 0, hi = batch;  // largest b with cu[b] <= t
     while (hi - lo > 1) {
@@ -105,8 +123,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
     seq_lo = cu[lo];
   }
   // the workgroup's key range: union of its tokens' ranges
-  const int64_t last_t = min(block * kWaves + kWaves - 1, n_tokens - 1);
-  if (lane == 0) range[wave] = active ? seq_lo : last_t;
+  int64_t wave_lo = seq_lo;
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) wave_lo = min(wave_lo, static_cast<int64_t>(__shfl_xor(wave_lo, d, 64)));
+  if (lane == 0) range[wave] = wave_lo;
   __syncthreads();
   int64_t k_lo = range[0];
 #pragma unroll
@@ -144,20 +164,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
     }
   };
 
-  // ---- Qᵀ of the token: B operand, lane = head l16, k = 32ks + 8lg + e
-  const int tq = active ? static_cast<int>(t) : 0;
-  const int per_group = kHeads / n_groups;
+  // ---- Qᵀ of the columns: B operand, lane = column l16, k = 32ks + 8lg + e
+  const int64_t tq = active ? t : 0;
+  const int per_group = n_heads / n_groups;
   bf16x8 qf[S::kSteps];
 #pragma unroll
   for (int ks = 0; ks < S::kSteps; ++ks) {
     const int k0 = ks * 32 + lg * 8;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (k0 < R) {
-      v = *reinterpret_cast<const uint4*>(q_lat + (static_cast<int64_t>(tq) * kHeads + l16) * R + k0);
+      v = *reinterpret_cast<const uint4*>(q_lat + (tq * n_heads + hc) * R + k0);
     } else {
       const int g = (k0 - R) / d_rope, j0 = (k0 - R) - g * d_rope;
-      if (g == l16 / per_group)
-        v = *reinterpret_cast<const uint4*>(q_pe + (static_cast<int64_t>(tq) * kHeads + l16) * d_rope + j0);
+      if (g == hc / per_group)
+        v = *reinterpret_cast<const uint4*>(q_pe + (tq * n_heads + hc) * d_rope + j0);
     }
     qf[ks] = __builtin_bit_cast(bf16x8, v);
   }
@@ -236,7 +256,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
         if (m_ref == -INFINITY) m_ref = tmax;  // first tile with a valid key of this head
       }
       const float lim = m_ref + kSlack;
-      uint32_t w[4];
+      uint32_t w[4], wl[4];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const f32x4 v = s[rb];
@@ -249,8 +269,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
         w[2 * rb + 1] = pack_bf16x2(p[2], p[3]);
         // the row sum takes the bf16 weights the PV product uses
         l_lane += bf16x2_sum(w[2 * rb]) + bf16x2_sum(w[2 * rb + 1]);
+        if constexpr (S::kSplitP) {
+          const float h0 = __uint_as_float(w[2 * rb] << 16), h1 = __uint_as_float(w[2 * rb] & 0xFFFF0000u);
+          const float h2 = __uint_as_float(w[2 * rb + 1] << 16), h3 = __uint_as_float(w[2 * rb + 1] & 0xFFFF0000u);
+          wl[2 * rb] = pack_bf16x2(p[0] - h0, p[1] - h1);
+          wl[2 * rb + 1] = pack_bf16x2(p[2] - h2, p[3] - h3);
+          l_lane += bf16x2_sum(wl[2 * rb]) + bf16x2_sum(wl[2 * rb + 1]);
+        }
       }
       const bf16x8 pa = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+      const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(wl[0], wl[1], wl[2], wl[3]));
+      (void)pl;
 
       // PV: O[head][16nb + col] += P[head][keys]·C[keys][cols], K order as held
       auto cfrag = [&](int nb) {
@@ -261,13 +290,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(phi));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      constexpr int kLA = 3;
+      constexpr int kLA = S::kLA;
       bf16x8 cf[kLA];
 #pragma unroll
       for (int q = 0; q < kLA; ++q) cf[q] = cfrag(q);
 #pragma unroll
       for (int nb = 0; nb < S::kNB; ++nb) {
         o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, cf[nb % kLA], o[nb], 0, 0, 0);
+        if constexpr (S::kSplitP) o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, cf[nb % kLA], o[nb], 0, 0, 0);
         if (nb + kLA < S::kNB) cf[nb % kLA] = cfrag(nb + kLA);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -286,43 +316,60 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
     lds_barrier();  // flags read everywhere before they are rewritten
   }
 
-  // ---- epilogue: l per head (lanes with l16 = head), O[head 4lg + i][16nb + l16]
+  // ---- epilogue: l per column (lanes with l16 = column), O[column 4lg + i][16nb + l16]
   float l = l_lane;
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  if (!active) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int h = lg * 4 + i;
-    const float inv = 1.f / __shfl(l, h, 64);
-    float* dst = o_out + (t * kHeads + h) * R + l16;
+    const int c = lg * 4 + i;
+    const float lh = __shfl(l, c, 64);
+    const float mh = __shfl(m_ref, c, 64);
+    const int64_t tc = wave_t0 + c / n_heads;
+    if (tc >= n_tokens) continue;
+    const float inv = 1.f / lh;
+    const int64_t row = tc * n_heads + c % n_heads;
+    if (part_o != nullptr) {
+      bf16_t* dst = part_o + row * R + l16;
 #pragma unroll
-    for (int nb = 0; nb < S::kNB; ++nb) dst[nb * 16] = o[nb][i] * inv;
+      for (int nb = 0; nb < S::kNB; ++nb) dst[nb * 16] = f32_to_bf16(o[nb][i] * inv);
+      if (l16 == 0) {
+        part_ml[row * 2] = mh;
+        part_ml[row * 2 + 1] = lh;
+      }
+    } else {
+      float* dst = o_out + row * R + l16;
+#pragma unroll
+      for (int nb = 0; nb < S::kNB; ++nb) dst[nb * 16] = o[nb][i] * inv;
+    }
   }
 }
 
 template <int R, int RW>
 void launch(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
-            const int64_t* cu, int batch, int64_t n_tokens, float* o_out, hipStream_t s) {
+            const int64_t* cu, int batch, int64_t n_tokens, float* o_out, void* part_o, float* part_ml,
+            hipStream_t s) {
   using S = PShape<R, RW>;
   auto kern = prefill_mfma_kernel<R, RW>;
   hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                       S::kLdsBytes);
-  const int64_t n_blocks = (n_tokens + kWaves - 1) / kWaves;
+  const int64_t block_tokens = static_cast<int64_t>(kWaves) * (kHeads / sh.H);
+  const int64_t n_blocks = (n_tokens + block_tokens - 1) / block_tokens;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(n_blocks)), dim3(kThreads), S::kLdsBytes, s,
                      static_cast<const bf16_t*>(q_lat), static_cast<const bf16_t*>(q_pe),
-                     static_cast<const bf16_t*>(cache), cu, batch, n_tokens, sh.G, sh.d_rope, sh.scale,
-                     o_out);
+                     static_cast<const bf16_t*>(cache), cu, batch, n_tokens, sh.H, sh.G, sh.d_rope, sh.scale,
+                     o_out, static_cast<bf16_t*>(part_o), part_ml);
 }
 
-// Compiled shapes: (latent r, row width r + G*d_rope) with H = 16 query heads.
-#define MLA_PREFILL_SHAPES(X) \
-  X(256, 320) /* r = 256, one 64-wide rotary key (Zebra MLA layers) */
+// Compiled shapes: (latent r, row width r + G*d_rope) with up to 16 query heads.
+#define MLA_PREFILL_SHAPES(X)                                                   \
+  X(256, 320) /* r = 256, one 64-wide rotary key (Zebra MLA layers)          */ \
+  X(512, 512) /* one 512-wide KV head as key and value (DeepSeek-V4 variant) */
 
 }  // namespace
 
 bool prefill_mfma_supported(const AttnShape& sh) {
-  if (sh.H != kHeads || sh.d_rope % 8 != 0 || sh.H % sh.G != 0) return false;
+  if (sh.H < 1 || kHeads % sh.H != 0 || sh.d_rope % 8 != 0 || sh.H % sh.G != 0) return false;
 #define MLA_MATCH(R_, RW_) \
   if (sh.r == R_ && sh.row_w == RW_) return true;
   MLA_PREFILL_SHAPES(MLA_MATCH)
@@ -332,12 +379,12 @@ bool prefill_mfma_supported(const AttnShape& sh) {
 
 void prefill_mfma(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
                   const int64_t* cu, int batch, int64_t n_tokens, int max_len, float* o_out,
-                  hipStream_t s) {
+                  void* part_o, float* part_ml, hipStream_t s) {
   (void)max_len;
   if (n_tokens <= 0 || batch <= 0) return;
 #define MLA_LAUNCH(R_, RW_)                                                          \
   if (sh.r == R_ && sh.row_w == RW_) {                                               \
-    launch<R_, RW_>(sh, q_lat, q_pe, cache, cu, batch, n_tokens, o_out, s);          \
+    launch<R_, RW_>(sh, q_lat, q_pe, cache, cu, batch, n_tokens, o_out, part_o, part_ml, s); \
     return;                                                                          \
   }
   MLA_PREFILL_SHAPES(MLA_LAUNCH)
