@@ -254,11 +254,33 @@ def bench_v4(args, torch, M, I, Hh, cfg):
 
     ms_step, ms_dec = timed(step), timed(decode_only)
     assert torch.isfinite(u.float()).all(), "non-finite V4 output"
+    # causal prefill of the first pf_b sequences (their queries from mla_v4_query)
+    pf_b = min(32, B)
+    x_pf = Hh.to_dev(np.concatenate([I.x_rows(cfg, b, 0, L) for b in range(pf_b)]), cfg.dtype)
+    pos_pf = torch.arange(L, dtype=torch.int32, device="cuda").repeat(pf_b)
+    q_pf = torch.empty((pf_b * L, H, D), dtype=torch.bfloat16, device="cuda")
+    M.mla_v4_query(dims, x_pf, wd["w_qa"], wd["q_gain"], wd["w_qb"], pos_pf, q_pf)
+    cu_pf = torch.arange(0, pf_b * L + 1, L, dtype=torch.int64, device="cuda")
+    out_pf = torch.empty_like(q_pf)
+    ws_pf = torch.empty(max(256, M.mla_v4_workspace_size(dims, M.MLA_V4_OP_PREFILL, pf_b, pf_b * L, L)),
+                        dtype=torch.uint8, device="cuda")
+
+    def prefill_only(i):
+        M.mla_v4_prefill(dims, q_pf, caches[0], cu_pf, L, wd["sink"], out_pf, workspace=ws_pf)
+
+    steps_keep = args.steps
+    args.steps = max(3, min(10, args.steps))
+    ms_pf = timed(prefill_only)
+    args.steps = steps_keep
+    assert torch.isfinite(out_pf.float()).all(), "non-finite V4 prefill output"
+    pf_flops = pf_b * L * (L + 1) / 2 * H * 4 * D
+    pf_tfs = pf_flops / (ms_pf * 1e-3) / 1e12
     dec_bytes = B * L * D * 2 + 2 * B * H * D * 2
     dec_flops = B * L * H * 4 * D
     gbs = dec_bytes / (ms_dec * 1e-3) / 1e9
     print(f"[bench] v4 decode: step {ms_step * 1e3:.1f} us, mla_v4_decode {ms_dec * 1e3:.1f} us "
-          f"({gbs:.0f} GB/s algorithmic) (setup {setup_s:.1f} s)", file=sys.stderr, flush=True)
+          f"({gbs:.0f} GB/s algorithmic); mla_v4_prefill {pf_b}x{L}: {ms_pf:.2f} ms ({pf_tfs:.0f} TFLOP/s) "
+          f"(setup {setup_s:.1f} s)", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         # the oracle on 32 of the sequences: cache rows, query, attention (float64)
@@ -295,6 +317,12 @@ def bench_v4(args, torch, M, I, Hh, cfg):
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "alg_bytes_per_launch": dec_bytes,
                      "alg_flops_per_launch": dec_flops, "us_per_launch": round(ms_dec * 1e3, 2)},
+        "prefill": {"call": "mla_v4_prefill", "sequences": pf_b, "tokens_per_sequence": L,
+                    "ms_per_call": round(ms_pf, 4), "tokens_per_s": round(pf_b * L / (ms_pf * 1e-3), 1),
+                    "alg_flops_per_call": pf_flops, "achieved_tflops": round(pf_tfs, 1),
+                    "mfma_bf16_peak_tflops": MFMA_BF16_PEAK_TFS, "frac": round(pf_tfs / MFMA_BF16_PEAK_TFS, 4),
+                    "note": "8 heads fill the 16 MFMA columns as 2 tokens x 8 heads; the PV takes the "
+                            "weights as a bf16 hi + lo pair (2 MFMAs), not counted in the algorithmic flops"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -71,6 +71,32 @@ __global__ __launch_bounds__(256) void v4_rows_kernel(const float* __restrict__ 
   }
 }
 
+// Eight consecutive values (16-byte aligned for bf16) as float, and back.
+__device__ __forceinline__ void load8(const bf16_t* p, float (&v)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = p[i];
+}
+__device__ __forceinline__ void store8(bf16_t* p, const float (&v)[8]) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                            pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+}
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = v[i];
+}
+
+// Workgroups (query, y): each thread merges 8 consecutive values of the
+// query's [H, D] output (16-byte loads of every split's part), so the pass
+// streams at memory speed for one split (prefill) as for several (decode).
 template <typename T>
 __global__ __launch_bounds__(256) void v4_merge_kernel(const T* __restrict__ part_o, const float* __restrict__ part_ml,
                                                        int n_split, int H, int D, int d_rope,
@@ -79,7 +105,6 @@ __global__ __launch_bounds__(256) void v4_merge_kernel(const T* __restrict__ par
                                                        const int64_t* __restrict__ cu, int batch, double base,
                                                        const double* __restrict__ freqs, T* __restrict__ out) {
   const int64_t q = blockIdx.x;
-  const int h = blockIdx.y;
   // the query's own position: the last row of its sequence (decode), or its
   // offset in its sequence (prefill)
   int32_t pos;
@@ -94,38 +119,42 @@ __global__ __launch_bounds__(256) void v4_merge_kernel(const T* __restrict__ par
     }
     pos = static_cast<int32_t>(q - cu[lo]);
   }
-  // softmax states are base 2 (u = s·log2 e): the sink joins as 2^(sink·log2 e - M)
-  const float su = sink[h] * kLog2e;
-  float mx = su;
-  for (int j = 0; j < n_split; ++j) mx = fmaxf(mx, part_ml[((q * n_split + j) * H + h) * 2]);
-  float den = exp2f(su - mx);
-  for (int j = 0; j < n_split; ++j) {
-    const float* ml = part_ml + ((q * n_split + j) * H + h) * 2;
-    den += ml[1] > 0.f ? exp2f(ml[0] - mx) * ml[1] : 0.f;
-  }
-  const float inv = 1.f / den;
-  T* dst = out + (q * H + h) * static_cast<int64_t>(D);
   const int n_plain = D - d_rope;
-  for (int k = threadIdx.x; k < D / 2; k += 256) {
-    const int i = 2 * k;
-    float a = 0.f, b = 0.f;
+  const int per_q = H * D;
+  for (int e0 = (blockIdx.y * 256 + threadIdx.x) * 8; e0 < per_q; e0 += gridDim.y * 256 * 8) {
+    const int h = e0 / D, c0 = e0 - h * D;
+    // softmax states are base 2 (u = s·log2 e): the sink joins as 2^(sink·log2 e - M)
+    const float su = sink[h] * kLog2e;
+    float mx = su;
+    for (int j = 0; j < n_split; ++j) mx = fmaxf(mx, part_ml[((q * n_split + j) * H + h) * 2]);
+    float den = exp2f(su - mx);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < n_split; ++j) {
       const int64_t pidx = (q * n_split + j) * H + h;
-      const float w = part_ml[pidx * 2 + 1] > 0.f ? exp2f(part_ml[pidx * 2] - mx) * part_ml[pidx * 2 + 1] : 0.f;
-      a = fmaf(w, Elem<T>::load(part_o, pidx * D + i), a);
-      b = fmaf(w, Elem<T>::load(part_o, pidx * D + i + 1), b);
+      const float l = part_ml[pidx * 2 + 1];
+      const float w = l > 0.f ? exp2f(part_ml[pidx * 2] - mx) * l : 0.f;
+      den += w;
+      float v[8];
+      load8(part_o + pidx * D + c0, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
     }
-    a *= inv;
-    b *= inv;
-    if (i >= n_plain) {
-      float c, sn;
-      angle_cos_sin(-static_cast<double>(pos) * rope_freq((i - n_plain) / 2, base, freqs), &c, &sn);
-      const float a2 = a * c - b * sn, b2 = b * c + a * sn;
-      a = a2;
-      b = b2;
+    const float inv = 1.f / den;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float a = acc[2 * k] * inv, b = acc[2 * k + 1] * inv;
+      const int col = c0 + 2 * k;
+      if (col >= n_plain) {
+        float c, sn;
+        angle_cos_sin(-static_cast<double>(pos) * rope_freq((col - n_plain) / 2, base, freqs), &c, &sn);
+        const float a2 = a * c - b * sn, b2 = b * c + a * sn;
+        a = a2;
+        b = b2;
+      }
+      acc[2 * k] = a;
+      acc[2 * k + 1] = b;
     }
-    Elem<T>::store(dst, i, a);
-    Elem<T>::store(dst, i + 1, b);
+    store8(out + q * static_cast<int64_t>(per_q) + e0, acc);
   }
 }
 
@@ -156,7 +185,9 @@ void v4_merge(int dtype, const void* part_o, const float* part_ml, int64_t n_q, 
               const double* freqs, void* out, hipStream_t s) {
   if (n_q <= 0) return;
   const double base = d_rope > 0 ? std::pow(theta, -2.0 / d_rope) : 1.0;
-  dim3 grid(static_cast<unsigned>(n_q), static_cast<unsigned>(H));
+  // 2048 values per workgroup, or fewer pieces when the queries alone fill the chip
+  const int pieces = (H * D + 2047) / 2048;
+  dim3 grid(static_cast<unsigned>(n_q), static_cast<unsigned>(n_q >= 4096 ? 1 : pieces));
   if (dtype == kF32)
     hipLaunchKernelGGL(v4_merge_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(part_o), part_ml,
                        n_split, H, D, d_rope, sink, seq_len, cu, batch, base, freqs, static_cast<float*>(out));
