@@ -140,11 +140,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
 
   // ---- tile copy: copy j fills LDS chunks [64j, 64j + 64); chunk L holds global
   // chunk L ^ ((row / 2) & 7) of row L / kRowChunks; rows past k_hi read row k_hi
-  auto issue_tile = [&](int tt) {
-    const int64_t tile_row = k_lo + static_cast<int64_t>(tt) * kTL;
-    const int valid = static_cast<int>(min<int64_t>(kTL, k_hi + 1 - tile_row));
-    const char* tbase = cache_c + tile_row * S::kRowBytes;
-    const uint32_t dst = lds0 + (tt % kStages) * S::kTileBytes;
+  // per-lane source offsets of this wave's copies: with a row of chunks that
+  // is no power of two (a real divide), computed once for a full tile and
+  // again only for a ragged last tile; otherwise per tile (shifts, no
+  // registers held)
+  auto dma_offsets = [&](int valid, uint32_t (&off)[S::kDmaPerWave]) {
     int ln = lane;
     __asm__ volatile("" : "+v"(ln));
 #pragma unroll
@@ -153,7 +153,38 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
       const int L = j * 64 + ln;
       const int r = L / S::kRowChunks;
       const int g = r < valid ? (L ^ ((r >> 1) & 7)) : (valid - 1) * S::kRowChunks + (L & 7);
-      global_to_lds16(tbase, static_cast<uint32_t>(g * 16), __builtin_amdgcn_readfirstlane(dst + j * 1024));
+      off[i] = static_cast<uint32_t>(g * 16);
+    }
+  };
+  constexpr bool kHoist = (S::kRowChunks & (S::kRowChunks - 1)) != 0;
+  uint32_t full_off[S::kDmaPerWave];
+  if constexpr (kHoist) dma_offsets(kTL, full_off);
+  auto issue_tile = [&](int tt) {
+    const int64_t tile_row = k_lo + static_cast<int64_t>(tt) * kTL;
+    const int valid = static_cast<int>(min<int64_t>(kTL, k_hi + 1 - tile_row));
+    const char* tbase = cache_c + tile_row * S::kRowBytes;
+    const uint32_t dst = lds0 + (tt % kStages) * S::kTileBytes;
+    if constexpr (kHoist) {
+      uint32_t off[S::kDmaPerWave];
+#pragma unroll
+      for (int i = 0; i < S::kDmaPerWave; ++i) off[i] = full_off[i];
+      if (valid < kTL) dma_offsets(valid, off);  // uniform branch, last tile only
+#pragma unroll
+      for (int i = 0; i < S::kDmaPerWave; ++i) {
+        const int j = min(wave + kWaves * i, S::kDmaOps - 1);
+        global_to_lds16(tbase, off[i], __builtin_amdgcn_readfirstlane(dst + j * 1024));
+      }
+    } else {
+      int ln = lane;
+      __asm__ volatile("" : "+v"(ln));
+#pragma unroll
+      for (int i = 0; i < S::kDmaPerWave; ++i) {
+        const int j = min(wave + kWaves * i, S::kDmaOps - 1);  // duplicates of the last copy are benign
+        const int L = j * 64 + ln;
+        const int r = L / S::kRowChunks;
+        const int g = r < valid ? (L ^ ((r >> 1) & 7)) : (valid - 1) * S::kRowChunks + (L & 7);
+        global_to_lds16(tbase, static_cast<uint32_t>(g * 16), __builtin_amdgcn_readfirstlane(dst + j * 1024));
+      }
     }
   };
   auto wait_tile = [&](int tt, int last_issued) {
