@@ -411,7 +411,7 @@ void launch(const AttnShape& sh, const void* q_lat, const void* q_pe, const void
             void* part_o, float* part_ml, float* o_out, hipStream_t s) {
   using S = Shape<R, RW, NHB, NHH, STAGES>;
   auto kern = decode_mfma_kernel<R, RW, NHB, NHH, STAGES>;
-  hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                       S::kLdsBytes);
   const int pairs = batch * n_split;
   const int grid = NHH == 1 ? pairs : (pairs + 7) / 8 * 8 * NHH;

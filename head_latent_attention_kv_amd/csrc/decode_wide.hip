@@ -413,7 +413,7 @@ void decode_wide(const AttnShape& sh, const void* q_lat, const void* q_pe, const
                  const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split,
                  int split_len, void* part_o, float* part_ml, float* o_out, hipStream_t s) {
   if (batch <= 0) return;
-  hipFuncSetAttribute(reinterpret_cast<const void*>(decode_wide_kernel),
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(decode_wide_kernel),
                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   hipLaunchKernelGGL(decode_wide_kernel, dim3(batch * n_split), dim3(kThreads), kLdsBytes, s,
                      static_cast<const bf16_t*>(q_lat), static_cast<const bf16_t*>(q_pe),

@@ -362,11 +362,11 @@ template <int MB>
 void launch_uk(const GemmArgs& g, bool out_bf16, hipStream_t s) {
   dim3 grid((g.N + kUkCols - 1) / kUkCols, g.Z);
   if (out_bf16) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_uk_kernel<MB, bf16_t>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_uk_kernel<MB, bf16_t>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, kUkLds);
     hipLaunchKernelGGL((gemm_uk_kernel<MB, bf16_t>), grid, dim3(256), kUkLds, s, g);
   } else {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_uk_kernel<MB, float>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_uk_kernel<MB, float>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, kUkLds);
     hipLaunchKernelGGL((gemm_uk_kernel<MB, float>), grid, dim3(256), kUkLds, s, g);
   }

@@ -1063,7 +1063,6 @@ int mla_v4_output(const mla_v4_dims* dims, const void* attn, const void* w_oa, c
   const V4Out w = v4_out_ws(dims, n_tokens);
   if (workspace_bytes < w.total()) return MLA_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const mla_dims sh = v4_shadow(dims);
   const int G = dims->o_groups, R = dims->o_rank, HD = dims->n_heads * dims->head_dim, gdim = HD / G;
   const int T = static_cast<int>(n_tokens);
   char* base = static_cast<char*>(workspace);

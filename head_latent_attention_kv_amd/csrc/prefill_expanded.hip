@@ -54,15 +54,13 @@
 #include "mla_device.h"
 #include "mla_internal.h"
 
-#ifndef MLA_PREFILL_FA_WAVES
-#define MLA_PREFILL_FA_WAVES 8  // waves per workgroup (4: one per SIMD, 8: two per SIMD)
-#endif
 
 
 namespace mla {
 
 namespace {
 
+constexpr int kWavesFA = 8;         // waves per workgroup: two per SIMD (4, one per SIMD, is slower)
 constexpr int kDN = 128;            // d_nope (key/query dims without position)
 constexpr int kDV = 128;            // d_v
 constexpr int kBM = 256;            // queries per workgroup
@@ -571,7 +569,7 @@ void prefill_expanded(const AttnShape& sh, const void* q_nope, const void* q_pe,
                       const void* v, const void* cache, const int64_t* cu, int batch, int64_t n_tokens,
                       void* out, hipStream_t s) {
   if (n_tokens <= 0 || batch <= 0) return;
-  launch_fa<64, MLA_PREFILL_FA_WAVES>(sh, q_nope, q_pe, k_nope, v, cache, cu, batch, static_cast<int>(n_tokens), out, s);
+  launch_fa<64, kWavesFA>(sh, q_nope, q_pe, k_nope, v, cache, cu, batch, static_cast<int>(n_tokens), out, s);
 }
 
 }  // namespace mla

@@ -382,7 +382,7 @@ void launch(const AttnShape& sh, const void* q_lat, const void* q_pe, const void
             hipStream_t s) {
   using S = PShape<R, RW>;
   auto kern = prefill_mfma_kernel<R, RW>;
-  hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                       S::kLdsBytes);
   const int64_t block_tokens = static_cast<int64_t>(kWaves) * (kHeads / sh.H);
   const int64_t n_blocks = (n_tokens + block_tokens - 1) / block_tokens;

@@ -724,19 +724,16 @@ void launch_out(const SkinnyArgs& sa, bool out_bf16, hipStream_t s) {
     hipLaunchKernelGGL((skinny_kernel<MB, NB, AK, NS, DEPTH, MINB, float>), grid, dim3(256), 0, s, sa);
 }
 
-#ifndef MLA_SKINNY_DMA_KC
-#define MLA_SKINNY_DMA_KC 128
-#endif
-template <int MB, int KC = MLA_SKINNY_DMA_KC>
+template <int MB, int KC = 128>
 void launch_dma(const SkinnyArgs& sa, bool out_bf16, hipStream_t s) {
   dim3 grid((sa.N + kDmaCols - 1) / kDmaCols, sa.Z, sa.splits);
   constexpr int lds = DmaStage<KC>::kLds;
   if (out_bf16) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_dma_kernel<MB, KC, bf16_t>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_dma_kernel<MB, KC, bf16_t>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     hipLaunchKernelGGL((skinny_dma_kernel<MB, KC, bf16_t>), grid, dim3(256), lds, s, sa);
   } else {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_dma_kernel<MB, KC, float>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_dma_kernel<MB, KC, float>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     hipLaunchKernelGGL((skinny_dma_kernel<MB, KC, float>), grid, dim3(256), lds, s, sa);
   }
@@ -794,7 +791,7 @@ void gemm_skinny_merged(SkinnyArgs sa, int n_merge, bool out_bf16, hipStream_t s
     // DMA-staged merge: two workgroups of 32 token rows per head
     sa.m_groups = 2;
     constexpr int lds = MergeStage<4>::kLds + kMgRows * 4 * 4;
-    hipFuncSetAttribute(reinterpret_cast<const void*>(merge_uv_kernel<4>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(merge_uv_kernel<4>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     hipLaunchKernelGGL(merge_uv_kernel<4>, dim3(2, sa.Z), dim3(256), lds, s, sa);
     return;
