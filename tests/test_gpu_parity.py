@@ -705,6 +705,74 @@ def test_v4_decode_chain(torch, lengths):
     assert err <= Hh.TOL["bf16"] and err_u <= Hh.TOL["bf16"] and err_uc <= Hh.TOL["bf16"]
 
 
+def test_v4_full_size_sampled(torch):
+    """The V4 bench's configuration: 256 sequences of 2048 cached rows decoded in one
+    call (and the grouped output), and the causal prefill of the first 32 of them,
+    checked on sampled sequences and query rows against the oracle's V4 chain."""
+    import head_latent_attention_kv_amd as M
+    from oracle import mla_oracle as O
+    cfg = I.V4_CONFIGS["nanowhale_v4_decode"]
+    B, L, D, H = cfg.batch, cfg.context, cfg.head_dim, cfg.n_heads
+    _print_case("v4_full_size", batch=B, context=L)
+    dims, w, wd = _v4_setup(torch, cfg)
+    cache = torch.empty((B * L, D), dtype=torch.bfloat16, device="cuda")
+    pos = torch.arange(L, dtype=torch.int32, device="cuda")
+    xq = np.zeros((B, cfg.d_model), np.float32)
+    seqs = [0, 97, 255]
+    pf_b = 32
+    xs = {}
+    x_pf = []
+    for b in range(B):
+        xb = I.x_rows(cfg, b, 0, L)
+        xq[b] = xb[-1]
+        if b in seqs or b in (0, pf_b - 1):
+            xs[b] = xb
+        if b < pf_b:
+            x_pf.append(xb)
+        M.mla_v4_write_cache(dims, Hh.to_dev(xb, cfg.dtype), wd["w_kv"], wd["kv_gain"], pos,
+                             torch.arange(L, dtype=torch.int64, device="cuda") + b * L, cache)
+    starts = torch.arange(0, B * L, L, dtype=torch.int64, device="cuda")
+    q = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    M.mla_v4_query(dims, Hh.to_dev(xq, cfg.dtype), wd["w_qa"], wd["q_gain"], wd["w_qb"],
+                   torch.full((B,), L - 1, dtype=torch.int32, device="cuda"), q)
+    out = torch.empty_like(q)
+    M.mla_v4_decode(dims, q, cache, starts, torch.full((B,), L, dtype=torch.int32, device="cuda"), L,
+                    wd["sink"], out)
+    u = torch.empty((B, cfg.d_model), dtype=torch.bfloat16, device="cuda")
+    M.mla_v4_output(dims, out, wd["w_oa"], wd["w_ob"], u)
+    # prefill of the first pf_b sequences, in one call
+    q_pf = torch.empty((pf_b * L, H, D), dtype=torch.bfloat16, device="cuda")
+    M.mla_v4_query(dims, Hh.to_dev(np.concatenate(x_pf), cfg.dtype), wd["w_qa"], wd["q_gain"], wd["w_qb"],
+                   pos.repeat(pf_b), q_pf)
+    out_pf = torch.empty_like(q_pf)
+    M.mla_v4_prefill(dims, q_pf, cache, torch.arange(0, pf_b * L + 1, L, dtype=torch.int64, device="cuda"), L,
+                     wd["sink"], out_pf)
+    torch.cuda.synchronize()
+    got, got_u = Hh.to_host(out), Hh.to_host(u)
+    errs = {}
+    kv_of = {}
+    for b in sorted(xs):
+        kv_of[b] = O.v4_cache_rows(xs[b], w["w_kv"], w["kv_gain"], np.arange(L), d_rope=cfg.d_rope, eps=cfg.rms_eps)
+    for b in seqs:
+        qr = O.v4_query(xs[b][-1:], w["w_qa"], w["q_gain"], w["w_qb"], [L - 1], n_heads=H, head_dim=D,
+                        d_rope=cfg.d_rope, eps=cfg.rms_eps)
+        ref = O.v4_attention(qr, kv_of[b], w["sink"], [L - 1], np.arange(L), [0], np.zeros(L, int),
+                             cfg.softmax_scale, d_rope=cfg.d_rope)
+        errs[f"decode seq {b}"] = Hh.rel_err_rows(got[b], ref[0])
+        errs[f"output seq {b}"] = Hh.rel_err_rows(got_u[b:b + 1], O.v4_output(ref, w["w_oa"], w["w_ob"], cfg.o_groups))
+    for b, rows in ((0, [0, 1, 1023, L - 1]), (pf_b - 1, [5, L - 1])):
+        rows = np.array(rows)
+        qr = O.v4_query(xs[b][rows], w["w_qa"], w["q_gain"], w["w_qb"], rows, n_heads=H, head_dim=D,
+                        d_rope=cfg.d_rope, eps=cfg.rms_eps)
+        ref = O.v4_attention(qr, kv_of[b], w["sink"], rows, np.arange(L), np.zeros(len(rows), int),
+                             np.zeros(L, int), cfg.softmax_scale, d_rope=cfg.d_rope)
+        got_pf = Hh.to_host(out_pf[torch.from_numpy(b * L + rows).cuda()])
+        errs[f"prefill seq {b} rows {list(rows)}"] = Hh.rel_err_rows(got_pf, ref)
+    print("v4 full size:", {k: f"{v:.3e}" for k, v in errs.items()})
+    for k, e in errs.items():
+        assert e <= Hh.TOL["bf16"], (k, e)
+
+
 @pytest.mark.parametrize("table", [False, True])
 def test_v4_prefill_ragged(torch, table):
     """Causal V4 prefill over a ragged batch (with the default rotary frequencies and
