@@ -304,9 +304,9 @@ int mla_output(const mla_dims* dims, const void* attn, const void* w_o, int64_t 
  * grouped low-rank output (wo_a, wo_b).
  * rope_freqs: device float64 [d_rope/2] inverse frequencies, or NULL for
  * theta^(-2i/d_rope); a context-extension rescaling passes its own table.
- * Compiled for bf16 with head_dim <= 512 (multiple of 16); the MFMA decode
- * kernel takes head_dim 512 with up to 16 heads, other shapes run the generic
- * kernel.
+ * Compiled for bf16 with head_dim <= 512 (multiple of 16).  head_dim 512 runs
+ * on MFMA kernels: decode with up to 16 heads, prefill with a head count that
+ * divides 16; other shapes run the generic kernel.
  * ------------------------------------------------------------------------------ */
 typedef struct mla_v4_dims {
   int32_t d_model;      /* hidden size */
