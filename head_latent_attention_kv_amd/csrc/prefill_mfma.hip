@@ -15,10 +15,12 @@
 //     v_mfma_f32_16x16x32_bf16 over the whole row (K = r + G·d_rope), key rows
 //     as the A operand from LDS, the token's Qᵀ as the B operand in registers
 //     (q_lat, the head's rotary-group q_pe, zero elsewhere);
-//   - causal / sequence mask, softmax against a per-head reference: the max of
-//     the first tile where the head has a valid key, base 2, 2^64 of headroom; a
-//     pass in which some later score passes the headroom is redone with the
-//     true max, so O is never rescaled;
+//   - causal / sequence mask (only on tiles that cross a column's sequence
+//     start or its own token), softmax against a per-column reference: the max
+//     of the first tile where the column has a valid key, base 2.  No running
+//     max is kept: a pass whose weights pass 2^64 (seen in the row sums) is
+//     redone after a max-only scan with each column's true max, so O is never
+//     rescaled;
 //   - PV: O[16 heads x r] += P[16 x 32]·C[32 x r], P straight from the softmax
 //     registers as the A operand (the product's K order is the order in which
 //     a lane holds its keys), C read transposed from the tile with
@@ -37,6 +39,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "lds_dma.h"
 #include "mla_device.h"
@@ -52,7 +55,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTL = 32;             // key rows per tile
 constexpr int kStages = 4;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kSlack = 64.f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -221,17 +223,44 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
   const int r_lo = lg * 4 + (l16 >> 2), r_hi = 16 + r_lo;
   const int c_sub = (l16 & 1) * 8, c_half = (l16 & 3) >> 1;
 
-  float m_ref = -INFINITY;   // reference max of head l16 (base 2); set at its first valid key
+  // Softmax state of column l16 (base 2): the reference is the max of the
+  // column's first tile with a valid key; no running max is kept.  A pass in
+  // which a weight passes 2^64 (its row sum then exceeds 2^64, or is inf/NaN)
+  // is redone after a max-only scan with each column's true max.
+  constexpr float kNoRef = -1e30f;   // reference before a column's first valid key
+  float m_ref = kNoRef;
   float m_lane = -INFINITY, l_lane = 0.f;
-  bool over = false;
   f32x4 o[S::kNB];
 
-  for (int pass = 0; pass < 2; ++pass) {
+  // the wave's tiles need the mask only where they cross a column's sequence
+  // start or its own token (or some column is past the last token)
+  int64_t lo_max = active ? seq_lo : INT64_MAX;
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) lo_max = max(lo_max, static_cast<int64_t>(__shfl_xor(lo_max, d, 64)));
+  const bool all_active = __builtin_amdgcn_ballot_w64(!active) == 0;
+  auto needs_mask = [&](int64_t row0) { return !all_active || row0 < lo_max || row0 + kTL - 1 > wave_t0; };
+  auto mask = [&](f32x4 (&s)[2], int64_t row0) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t kr = row0 + rb * 16 + lg * 4 + i;
+        s[rb][i] = (active && kr >= seq_lo && kr <= t) ? s[rb][i] : -INFINITY;
+      }
+  };
+  auto raw_max = [&](const f32x4 (&s)[2]) {
+    return fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                 fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  };
+  auto ref_missing = [&]() { return __builtin_amdgcn_ballot_w64(active && m_ref == kNoRef) != 0; };
+
+  auto run_pass = [&](auto scan_c) {
+    constexpr bool kScan = decltype(scan_c)::value;
 #pragma unroll
     for (int nb = 0; nb < S::kNB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_lane = -INFINITY;
     l_lane = 0.f;
-    over = false;
+    bool need_ref = !kScan && ref_missing();
 
 #pragma unroll
     for (int tt = 0; tt < kStages - 1; ++tt)
@@ -247,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
       }
       const unsigned char* tb = smem + (tt % kStages) * S::kTileBytes;
 
-      // score: s[rb] = keys 16rb + 4lg + i of head l16
+      // score: s[rb] = keys 16rb + 4lg + i of column l16
       f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       auto frag = [&](int ks, int off) {
         const int coff = (ks >> 1) * 128 + ((ks & 1) ? x_odd : x_even) * 16;
@@ -269,33 +298,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      // mask (this token's sequence rows up to itself), reference, weights
+      // mask (each column's sequence rows up to its token), reference, weights
       const int64_t row0 = k_lo + static_cast<int64_t>(tt) * kTL;
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t kr = row0 + rb * 16 + lg * 4 + i;
-          const float v = s[rb][i] * qk_scale;
-          s[rb][i] = (active && kr >= seq_lo && kr <= t) ? v : -INFINITY;
-          tmax = fmaxf(tmax, s[rb][i]);
-        }
-      if (pass == 0) {
+      if (needs_mask(row0)) mask(s, row0);
+      if constexpr (kScan) {
+        m_lane = fmaxf(m_lane, raw_max(s));
+        continue;
+      }
+      if (need_ref) {  // uniform; only until every column has met a valid key
+        float tmax = raw_max(s);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        if (m_ref == -INFINITY) m_ref = tmax;  // first tile with a valid key of this head
+        if (m_ref == kNoRef && tmax != -INFINITY) m_ref = tmax * qk_scale;
+        need_ref = ref_missing();
       }
-      const float lim = m_ref + kSlack;
+      const float neg = -m_ref;
       uint32_t w[4], wl[4];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const f32x4 v = s[rb];
-        m_lane = fmaxf(m_lane, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-        over = over || (v[0] > lim) || (v[1] > lim) || (v[2] > lim) || (v[3] > lim);
         float p[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = v[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(v[i] - m_ref);
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], qk_scale, neg));
         w[2 * rb] = pack_bf16x2(p[0], p[1]);
         w[2 * rb + 1] = pack_bf16x2(p[2], p[3]);
         // the row sum takes the bf16 weights the PV product uses
@@ -312,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
       const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(wl[0], wl[1], wl[2], wl[3]));
       (void)pl;
 
-      // PV: O[head][16nb + col] += P[head][keys]·C[keys][cols], K order as held
+      // PV: O[column][16nb + col] += P[column][keys]·C[keys][cols], K order as held
       auto cfrag = [&](int nb) {
         const int chunk = nb * 2 + c_half;
         const unsigned char* plo = tb + r_lo * S::kRowBytes + swz(chunk, r_lo) * 16 + c_sub;
@@ -333,18 +357,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    const bool wave_over = __ballot(over) != 0;  // every lane votes
-    lds_barrier();
+    lds_barrier();  // every wave is done with the ring before another pass refills it
+  };
+
+  for (int pass = 0;; ++pass) {  // one weighing pass, or (rarely) two with a scan between
+    run_pass(std::false_type{});
+    if (pass == 1) break;
+    const bool wave_over = __builtin_amdgcn_ballot_w64(!(l_lane <= 1.8e19f)) != 0;  // 2^64; every lane votes
     if (lane == 0) flags[wave] = wave_over ? 1 : 0;
     lds_barrier();
     int any = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) any |= flags[w];
     if (any == 0) break;
-    // second pass with each head's true max
+    run_pass(std::true_type{});
     float mx = fmaxf(m_lane, __shfl_xor(m_lane, 16, 64));
-    m_ref = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    lds_barrier();  // flags read everywhere before they are rewritten
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    m_ref = mx == -INFINITY ? kNoRef : mx * qk_scale;
   }
 
   // ---- epilogue: l per column (lanes with l16 = column), O[column 4lg + i][16nb + l16]
