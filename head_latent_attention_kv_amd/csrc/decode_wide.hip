@@ -24,8 +24,9 @@
 //     v_mfma_f32_16x16x32_bf16 over the whole row (K = 576), tile rows as the A
 //     operand from LDS, Qᵀ as the B operand from registers;
 //   - softmax against a per-head reference max of the split (the first tile's
-//     max, base 2, with 2^64 of headroom); a split whose later scores pass the
-//     headroom is redone with its true max, so O is never rescaled;
+//     max, base 2, with 2^64 of headroom; no running max is kept); a split
+//     whose weights pass the headroom (seen in the row sums) is redone after a
+//     max-only scan with its true max, so O is never rescaled;
 //   - softmax weights P as bf16 MFMA A fragments into a double-buffered LDS
 //     exchange [head block][lane] (8 KB a tile): a score lane holds rows
 //     4lg..4lg+3 and 16+4lg..16+4lg+3 of its head, and the K order of the PV
@@ -69,7 +70,6 @@ constexpr int kLdsBytes = kPOff + 2 * kPBytes;       // 160 KB
 // per head (xch) and the restart flags
 constexpr int kFlagsOff = 1024;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kSlack = 64.f;
 constexpr int kSLA = 2;                              // score k-steps of fragments in flight
 
 static_assert(kHW == 16, "one 16-head block per wave in the score");
@@ -255,7 +255,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const f32x4 v = s[rb];
-      m_lane = fmaxf(m_lane, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
       const float p0 = __builtin_amdgcn_exp2f(fmaf(v[0], qk_scale, nm));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(v[1], qk_scale, nm));
       const float p2 = __builtin_amdgcn_exp2f(fmaf(v[2], qk_scale, nm));
@@ -300,7 +299,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
     }
   };
 
-  for (int pass = 0; pass < 2; ++pass) {
+  auto tile_max = [&](const f32x4 (&s)[2]) {
+    return fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                 fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  };
+  // One pass over the split: weights and PV against m_ref (set from tile 0 in
+  // the first pass), or (kScan) the running max of the raw scores only.
+  auto run_pass = [&](auto scan_c, bool set_ref) {
+    constexpr bool kScan = decltype(scan_c)::value;
 #pragma unroll
     for (int hb = 0; hb < kHB; ++hb)
 #pragma unroll
@@ -319,14 +325,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
       lds_barrier();
       f32x4 s0[2];
       score(0, s0);
-      if (pass == 0) {
-        float mx = fmaxf(fmaxf(fmaxf(s0[0][0], s0[0][1]), fmaxf(s0[0][2], s0[0][3])),
-                         fmaxf(fmaxf(s0[1][0], s0[1][1]), fmaxf(s0[1][2], s0[1][3])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        m_ref = mx * qk_scale;
+      if constexpr (kScan) {
+        m_lane = tile_max(s0);
+      } else {
+        if (set_ref) {
+          float mx = tile_max(s0);
+          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          m_ref = mx * qk_scale;
+        }
+        softmax(s0, smem + kPOff);
       }
-      softmax(s0, smem + kPOff);
     }
 
     // iteration t: scores of tile t+1 (masked to nothing past the last tile),
@@ -342,27 +351,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
       }
       f32x4 s_next[2];
       score(t + 1, s_next);
-      softmax(s_next, smem + kPOff + ((t + 1) & 1) * kPBytes);
-      pv(t);
+      if constexpr (kScan) {
+        m_lane = fmaxf(m_lane, tile_max(s_next));
+      } else {
+        softmax(s_next, smem + kPOff + ((t + 1) & 1) * kPBytes);
+        pv(t);
+      }
     }
-    // restart when some score passed its reference's headroom (raw max of the
-    // lane's head times the scale; the scale is positive)
-    const bool over = __ballot(m_lane * qk_scale > m_ref + kSlack) != 0;  // every lane votes
-    lds_barrier();
+    lds_barrier();  // every wave is done with the ring and the P buffers
+  };
+
+  // A pass whose weights passed the reference's 2^64 headroom (seen in the row
+  // sums: above 2^64, or inf/NaN) is redone after a max-only scan with the
+  // split's true max per head; every lane votes.
+  for (int pass = 0;; ++pass) {
+    run_pass(std::false_type{}, pass == 0);
+    if (pass == 1) break;
+    const bool over = __ballot(!(l_lane <= 1.8e19f)) != 0;
     if (lane == 0) flags[wave] = over ? 1 : 0;
     lds_barrier();
     int any = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) any |= flags[w];
     if (!any) break;
-    // second pass with the split's true max per head
-    {
-      float mx = m_lane;
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      m_ref = mx * qk_scale;
-    }
-    lds_barrier();  // every wave has read the flags before they are rewritten
+    run_pass(std::true_type{}, false);
+    float mx = m_lane;
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    m_ref = mx * qk_scale;
   }
 
   // ---- epilogue: l per head -> LDS (the wave's own heads); O normalised or as a partial
