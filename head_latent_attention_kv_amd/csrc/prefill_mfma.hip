@@ -6,12 +6,13 @@
 // attention with K = [c ; kr] and V = c.  Causal rule (nanowhale page, SDPA
 // with is_causal): token t attends to the rows cu[b] .. t of its sequence.
 //
-// Workgroup = 8 wave64s on 8 consecutive query tokens; wave w takes token
-// 8k + w with its H = 16 heads as the MFMA N dimension.  The workgroup streams
+// Workgroup = 8 wave64s; each wave's 16 MFMA columns are (token, head) pairs
+// (one token with its H = 16 heads, or 16/H tokens of H heads; see below).
+// The workgroup streams
 // the union of its tokens' key ranges in 32-row tiles through a 4-buffer LDS
 // ring (global_load_lds_dwordx4; 16-byte chunks XOR-swizzled by row / 2 within
 // groups of eight so fragment reads spread over the banks).  Per tile and wave:
-//   - score Sᵀ[32 keys x 16 heads]: two 16x16 blocks of
+//   - score Sᵀ[32 keys x 16 columns]: two 16x16 blocks of
 //     v_mfma_f32_16x16x32_bf16 over the whole row (K = r + G·d_rope), key rows
 //     as the A operand from LDS, the token's Qᵀ as the B operand in registers
 //     (q_lat, the head's rotary-group q_pe, zero elsewhere);
@@ -21,7 +22,7 @@
 //     max is kept: a pass whose weights pass 2^64 (seen in the row sums) is
 //     redone after a max-only scan with each column's true max, so O is never
 //     rescaled;
-//   - PV: O[16 heads x r] += P[16 x 32]·C[32 x r], P straight from the softmax
+//   - PV: O[16 columns x r] += P[16 x 32]·C[32 x r], P straight from the softmax
 //     registers as the A operand (the product's K order is the order in which
 //     a lane holds its keys), C read transposed from the tile with
 //     ds_read_b64_tr_b16 at the matching row bases.
