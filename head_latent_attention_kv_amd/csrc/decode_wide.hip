@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
   const int x_odd = ((4 + lg) ^ (l16 >> 1)) & 7;
 
   float m_ref = -INFINITY;   // reference max of head 16w + l16 (base 2)
-  float m_lane, l_lane;      // raw score max (max-only scan), bf16 weight sum of the lane
+  float m_lane, l_lane;      // raw score max, bf16 weight sum of the lane
   f32x4 o[kHB][kCB];         // O[heads 16hb + 4lg + i][columns 64w + 16j + l16]
 
   // Raw scores q·k of tile tt (unscaled; rows past the split masked to -inf):
