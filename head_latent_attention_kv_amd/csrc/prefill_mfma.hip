@@ -58,6 +58,7 @@ constexpr int kStages = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
@@ -229,6 +230,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
   // which a weight passes 2^64 (its row sum then exceeds 2^64, or is inf/NaN)
   // is redone after a max-only scan with each column's true max.
   constexpr float kNoRef = -1e30f;   // reference before a column's first valid key
+  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);  // row sums by v_dot2
   float m_ref = kNoRef;
   float m_lane = -INFINITY, l_lane = 0.f;
   f32x4 o[S::kNB];
@@ -324,13 +326,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
         w[2 * rb] = pack_bf16x2(p[0], p[1]);
         w[2 * rb + 1] = pack_bf16x2(p[2], p[3]);
         // the row sum takes the bf16 weights the PV product uses
-        l_lane += bf16x2_sum(w[2 * rb]) + bf16x2_sum(w[2 * rb + 1]);
+        l_lane = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[2 * rb]), ones, l_lane, false);
+        l_lane = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[2 * rb + 1]), ones, l_lane, false);
         if constexpr (S::kSplitP) {
           const float h0 = __uint_as_float(w[2 * rb] << 16), h1 = __uint_as_float(w[2 * rb] & 0xFFFF0000u);
           const float h2 = __uint_as_float(w[2 * rb + 1] << 16), h3 = __uint_as_float(w[2 * rb + 1] & 0xFFFF0000u);
           wl[2 * rb] = pack_bf16x2(p[0] - h0, p[1] - h1);
           wl[2 * rb + 1] = pack_bf16x2(p[2] - h2, p[3] - h3);
-          l_lane += bf16x2_sum(wl[2 * rb]) + bf16x2_sum(wl[2 * rb + 1]);
+          l_lane = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wl[2 * rb]), ones, l_lane, false);
+          l_lane = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wl[2 * rb + 1]), ones, l_lane, false);
         }
       }
       const bf16x8 pa = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
