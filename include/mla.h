@@ -75,8 +75,9 @@ typedef struct mla_dims {
   int32_t d_model;        /* hidden size of x */
   int32_t n_heads;        /* H, query heads */
   int32_t n_groups;       /* G, rotary-key groups; head h uses group h / (H/G) */
-  int32_t rank;           /* r, latent width (multiple of 16) */
-  int32_t d_rope;         /* rotary dims per query head and per key group (even) */
+  int32_t rank;           /* r, latent width (multiple of 16, at most 512) */
+  int32_t d_rope;         /* rotary dims per query head and per key group (even, at most
+                             512; r + G*d_rope at most 1024) */
   int32_t d_nope;         /* non-rotary query/key dims per head */
   int32_t d_v;            /* value dims per head */
   int32_t dtype;          /* mla_dtype */

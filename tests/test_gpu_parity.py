@@ -120,6 +120,53 @@ def test_decode_reduced(torch, name, lengths):
         assert v <= Hh.TOL[cfg.dtype], (k, v)
 
 
+# The widest cache row the library takes (the largest rank, 512, and four
+# 128-wide rotary keys: r + G·d_rope = 1024, the cache-row epilogue's limit),
+# with latent RMSNorm: no MFMA instance covers it, so decode and prefill run
+# the generic attention kernel.
+WIDE_ROW = I.MLAConfig(name="wide_row_edge", seed=1101, d_model=512, n_heads=8, n_groups=4, rank=512,
+                       d_rope=128, d_nope=64, d_v=64, dtype="bf16", mode="prefill+decode", batch=3,
+                       latent_rmsnorm=True)
+
+
+def test_widest_cache_row_decode_and_prefill(torch):
+    """The largest row width (1024 values: r = 512 and four 128-wide rotary keys) with
+    one-token, ragged and tile-spanning sequences, decode and causal prefill, against
+    the oracle's whole chain."""
+    import head_latent_attention_kv_amd as M
+    from oracle import mla_oracle as O
+    cfg = WIDE_ROW
+    lengths = [1, 333, 70]
+    _print_case("widest_row", lengths=lengths)
+    layer = Hh.make_layer(cfg)
+    T = sum(lengths)
+    x = np.concatenate([I.x_rows(cfg, b, 0, n) for b, n in enumerate(lengths)])
+    pos = np.concatenate([np.arange(n) for n in lengths])
+    seg = np.concatenate([np.full(n, b) for b, n in enumerate(lengths)])
+    cache = torch.empty((T, cfg.row_width), dtype=torch.bfloat16, device="cuda")
+    xd = Hh.to_dev(x, cfg.dtype)
+    Hh.write_cache(layer, xd, pos, np.arange(T), cache)
+    q_lat, q_pe = Hh.absorb(layer, xd, pos)
+    out = torch.empty((T, cfg.n_heads, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int64, device="cuda")
+    M.mla_prefill(layer.dims, q_lat, q_pe, cache, cu, max(lengths), layer.w_dev["w_uv"], out)
+    # decode: the last token of each sequence against its rows
+    last = np.cumsum(lengths) - 1
+    out_d = torch.empty((len(lengths), cfg.n_heads, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+    M.mla_decode(layer.dims, q_lat[torch.from_numpy(last).cuda()].contiguous(),
+                 q_pe[torch.from_numpy(last).cuda()].contiguous(), cache,
+                 torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)[:-1]]).astype(np.int64)).cuda(),
+                 torch.tensor(lengths, dtype=torch.int32, device="cuda"), max(lengths), layer.w_dev["w_uv"], out_d)
+    torch.cuda.synchronize()
+    ref = O.mla_layer(x, x, layer.w_host, k_pos=pos, q_pos=pos, k_seg=seg, q_seg=seg, n_heads=cfg.n_heads,
+                      n_groups=cfg.n_groups, d_nope=cfg.d_nope, d_rope=cfg.d_rope, theta=cfg.rope_theta,
+                      scale=cfg.softmax_scale, latent_rmsnorm=True, eps=cfg.rms_eps)
+    err_p = Hh.rel_err_rows(Hh.to_host(out), ref)
+    err_d = Hh.rel_err_rows(Hh.to_host(out_d), ref[last])
+    print(f"widest row {lengths}: prefill {err_p:.3e}, decode {err_d:.3e}")
+    assert err_p <= Hh.TOL["bf16"] and err_d <= Hh.TOL["bf16"]
+
+
 @pytest.mark.parametrize("name,lengths", [("deepseek_v2_decode", [700, 2100, 90]),
                                           ("qwen25_7b_decode", [1500, 333])])
 def test_decode_restart(torch, name, lengths):
