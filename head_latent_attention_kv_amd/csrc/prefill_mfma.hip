@@ -6,7 +6,9 @@
 // attention with K = [c ; kr] and V = c.  Causal rule (nanowhale page, SDPA
 // with is_causal): token t attends to the rows cu[b] .. t of its sequence.
 //
-// Workgroup = 8 wave64s; each wave's 16 MFMA columns are (token, head) pairs
+// Workgroup = 4 wave64s when two workgroups' rings fit in a CU's LDS (two per
+// CU, each with its own barriers), else 8; each wave's 16 MFMA columns are
+// (token, head) pairs
 // (one token with its H = 16 heads, or 16/H tokens of H heads; see below).
 // The workgroup streams
 // the union of its tokens' key ranges in 32-row tiles through a 4-buffer LDS
@@ -51,8 +53,6 @@ namespace mla {
 namespace {
 
 constexpr int kHeads = 16;          // query heads per token (one MFMA N block)
-constexpr int kWaves = 8;           // query tokens per workgroup
-constexpr int kThreads = 64 * kWaves;
 constexpr int kTL = 32;             // key rows per tile
 constexpr int kStages = 4;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -74,13 +74,22 @@ struct PShape {
   static constexpr int kTileBytes = kTL * kRowBytes;
   static_assert(kTileBytes % 1024 == 0, "whole 1 KB copies");
   static constexpr int kDmaOps = kTileBytes / 1024;
+  // the setup scratch and the restart flags alias the start of the ring, which
+  // is idle at those moments
+  static constexpr int kLdsBytes = kStages * kTileBytes;
+  // two waves per SIMD: two workgroups of 4 waves per CU when two rings fit in
+  // its 160 KB of LDS (they then keep separate barriers and overlap each
+  // other's MFMA and softmax phases), else one of 8
+  static constexpr int kBlocksPerCU = 2 * kLdsBytes <= 160 * 1024 ? 2 : 1;
+  static constexpr int kWaves = 8 / kBlocksPerCU;
+  static constexpr int kThreads = 64 * kWaves;
   static constexpr int kDmaPerWave = (kDmaOps + kWaves - 1) / kWaves;
   static_assert(3 * kDmaPerWave < 64, "vmcnt range");
   static constexpr int kSteps = RW / 32;     // score k-steps
   static constexpr int kNB = R / 16;         // PV column blocks
   static constexpr bool kSplitP = RW == R;   // K = V rows: weights as hi + lo bf16
   static constexpr int kLA = kSplitP ? 2 : 3;  // C fragments in flight
-  static constexpr int kLdsBytes = kStages * kTileBytes + 64;
+  static_assert(kTileBytes >= 8 * kWaves, "scratch in the ring");
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
@@ -90,15 +99,15 @@ __device__ __forceinline__ void wait_tiles_after() {
 }
 
 template <int R, int RW>
-__global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
+__global__ __launch_bounds__((PShape<R, RW>::kThreads), (PShape<R, RW>::kBlocksPerCU)) void prefill_mfma_kernel(
     const bf16_t* __restrict__ q_lat, const bf16_t* __restrict__ q_pe,
     const bf16_t* __restrict__ cache, const int64_t* __restrict__ cu, int batch, int64_t n_tokens,
     int n_heads, int n_groups, int d_rope, float scale, float* __restrict__ o_out,
     bf16_t* __restrict__ part_o, float* __restrict__ part_ml) {
   using S = PShape<R, RW>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  int64_t* range = reinterpret_cast<int64_t*>(smem + kStages * S::kTileBytes);  // [2][kWaves/2] scratch
-  int* flags = reinterpret_cast<int*>(range);                                    // reused after setup
+  int64_t* range = reinterpret_cast<int64_t*>(smem);  // [S::kWaves] setup scratch (ring not yet in use)
+  int* flags = reinterpret_cast<int*>(smem);          // restart flags (ring idle between passes)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -108,7 +117,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
   // ---- MFMA column l16 of this wave is (token t, head hc): token slot l16 / H
   // of the wave's 16/H tokens.  Its key rows are [seq_lo, t].
   const int tpw = kHeads / n_heads;
-  const int64_t block_tokens = static_cast<int64_t>(kWaves) * tpw;
+  const int64_t block_tokens = static_cast<int64_t>(S::kWaves) * tpw;
   const int64_t n_blocks = (n_tokens + block_tokens - 1) / block_tokens;
   const int64_t block = n_blocks - 1 - blockIdx.x;  // longest key ranges first
   const int64_t wave_t0 = block * block_tokens + static_cast<int64_t>(wave) * tpw;
@@ -134,7 +143,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
   __syncthreads();
   int64_t k_lo = range[0];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) k_lo = min(k_lo, range[w]);
+  for (int w = 1; w < S::kWaves; ++w) k_lo = min(k_lo, range[w]);
   const int64_t k_hi = last_t;
   const int n_tiles = static_cast<int>((k_hi - k_lo + kTL) / kTL);
   __syncthreads();  // range[] read everywhere before it is reused as flags
@@ -153,7 +162,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
     __asm__ volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < S::kDmaPerWave; ++i) {
-      const int j = min(wave + kWaves * i, S::kDmaOps - 1);  // duplicates of the last copy are benign
+      const int j = min(wave + S::kWaves * i, S::kDmaOps - 1);  // duplicates of the last copy are benign
       const int L = j * 64 + ln;
       const int r = L / S::kRowChunks;
       const int g = r < valid ? (L ^ ((r >> 1) & 7)) : (valid - 1) * S::kRowChunks + (L & 7);
@@ -175,7 +184,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
       if (valid < kTL) dma_offsets(valid, off);  // uniform branch, last tile only
 #pragma unroll
       for (int i = 0; i < S::kDmaPerWave; ++i) {
-        const int j = min(wave + kWaves * i, S::kDmaOps - 1);
+        const int j = min(wave + S::kWaves * i, S::kDmaOps - 1);
         global_to_lds16(tbase, off[i], __builtin_amdgcn_readfirstlane(dst + j * 1024));
       }
     } else {
@@ -183,7 +192,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
       __asm__ volatile("" : "+v"(ln));
 #pragma unroll
       for (int i = 0; i < S::kDmaPerWave; ++i) {
-        const int j = min(wave + kWaves * i, S::kDmaOps - 1);  // duplicates of the last copy are benign
+        const int j = min(wave + S::kWaves * i, S::kDmaOps - 1);  // duplicates of the last copy are benign
         const int L = j * 64 + ln;
         const int r = L / S::kRowChunks;
         const int g = r < valid ? (L ^ ((r >> 1) & 7)) : (valid - 1) * S::kRowChunks + (L & 7);
@@ -373,8 +382,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(
     lds_barrier();
     int any = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) any |= flags[w];
+    for (int w = 0; w < S::kWaves; ++w) any |= flags[w];
     if (any == 0) break;
+    lds_barrier();  // the flags are read everywhere before the scan refills the ring
     run_pass(std::true_type{});
     float mx = fmaxf(m_lane, __shfl_xor(m_lane, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -418,9 +428,9 @@ void launch(const AttnShape& sh, const void* q_lat, const void* q_pe, const void
   auto kern = prefill_mfma_kernel<R, RW>;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                       S::kLdsBytes);
-  const int64_t block_tokens = static_cast<int64_t>(kWaves) * (kHeads / sh.H);
+  const int64_t block_tokens = static_cast<int64_t>(S::kWaves) * (kHeads / sh.H);
   const int64_t n_blocks = (n_tokens + block_tokens - 1) / block_tokens;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(n_blocks)), dim3(kThreads), S::kLdsBytes, s,
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(n_blocks)), dim3(S::kThreads), S::kLdsBytes, s,
                      static_cast<const bf16_t*>(q_lat), static_cast<const bf16_t*>(q_pe),
                      static_cast<const bf16_t*>(cache), cu, batch, n_tokens, sh.H, sh.G, sh.d_rope, sh.scale,
                      o_out, static_cast<bf16_t*>(part_o), part_ml);
