@@ -60,10 +60,13 @@ namespace mla {
 
 namespace {
 
-constexpr int kWavesFA = 8;         // waves per workgroup: two per SIMD (4, one per SIMD, is slower)
+// waves per workgroup and 32-query blocks per wave: 8 x 1, one workgroup of
+// 256 queries per CU (two workgroups of 4 x 1 per CU, with separate barriers,
+// and 4 x 2 with one wave per SIMD are both slower)
+constexpr int kWavesFA = 8;
+constexpr int kQBFA = 1;
 constexpr int kDN = 128;            // d_nope (key/query dims without position)
 constexpr int kDV = 128;            // d_v
-constexpr int kBM = 256;            // queries per workgroup
 constexpr int kBN = 32;             // keys per tile
 constexpr int kStages = 4;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -88,8 +91,8 @@ struct FShape {
   static constexpr int kOps = kKnOps + kKrOps + kVOps;
   static constexpr int kKrChunks = DR / 8;          // 16-byte chunks of a rotary row
   static constexpr int kKS = (kDN + DR) / 16;       // score k-steps
-  static constexpr int kFlagsOff = kStages * kStageBytes;
-  static constexpr int kLdsBytes = kFlagsOff + 64;
+  // the restart flags alias the start of the ring (idle between passes)
+  static constexpr int kLdsBytes = kStages * kStageBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
@@ -138,16 +141,17 @@ __device__ __forceinline__ void wait_tiles_after() {
   wait_vmcnt<N * PerWave>();
 }
 
-template <int DR, int W>
-__global__ __launch_bounds__(64 * W, 1) void prefill_fa_kernel(
+template <int DR, int W, int QB>
+__global__ __launch_bounds__(64 * W, 8 / W) void prefill_fa_kernel(
     const bf16_t* __restrict__ q_nope, const bf16_t* __restrict__ q_pe,
     const _Float16* __restrict__ k_nope, const _Float16* __restrict__ v,
     const bf16_t* __restrict__ cache, const int64_t* __restrict__ cu, int batch, int n_tokens,
     int t_pad, int n_heads, int heads_per_group, int row_w, int r, float scale, bf16_t* __restrict__ out) {
   using S = FShape<DR>;
-  constexpr int kQB = 8 / W;          // 32-query column blocks per wave
+  constexpr int kQB = QB;             // 32-query column blocks per wave
   constexpr int kQW = 32 * kQB;       // queries per wave
-  static_assert(W * kQW == kBM && S::kKnOps % W == 0 && S::kVOps % W == 0, "wave split");
+  constexpr int kBM = W * kQW;        // queries per workgroup
+  static_assert(S::kKnOps % W == 0 && S::kVOps % W == 0, "wave split");
   // tile copies per wave: the first kOps % W waves take one more
   constexpr int kOpsHi = (S::kOps + W - 1) / W, kOpsLo = S::kOps / W;
   static_assert(3 * kOpsHi < 64, "vmcnt range");
@@ -418,7 +422,7 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_fa_kernel(
   // past fp16's range (a later score more than ~2^16 above the reference)
   // turns the row sum into inf; then pass 1 scans the true max of every
   // query and pass 2 weighs again against it.  All waves take the same passes.
-  int* flags = reinterpret_cast<int*>(smem + S::kFlagsOff);
+  int* flags = reinterpret_cast<int*>(smem);  // restart flags, in the idle ring between passes
   auto tile_scores = [&](int t, f32x16 (&sc)[kQB]) { score(smem + (t % kStages) * S::kStageBytes, sc); };
   // One pass over the workgroup's tiles: weights and PV, or (kScan) the running
   // max only.  Every active wave takes every tile of the workgroup's range:
@@ -492,6 +496,7 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_fa_kernel(
 #pragma unroll
   for (int i = 0; i < W; ++i) any |= flags[i];
   if (any != 0) {
+    lds_barrier();  // the flags are read everywhere before the scan refills the ring
     reset();
     run_pass(std::true_type{});
 #pragma unroll
@@ -523,13 +528,14 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_fa_kernel(
   }
 }
 
-template <int DR, int W>
+template <int DR, int W, int QB>
 void launch_fa(const AttnShape& sh, const void* q_nope, const void* q_pe, const void* k_nope,
                const void* v, const void* cache, const int64_t* cu, int batch, int n_tokens,
                void* out, hipStream_t s) {
   const int t_pad = static_cast<int>(prefill_expanded_vt_cols(n_tokens));
   using S = FShape<DR>;
-  auto kern = prefill_fa_kernel<DR, W>;
+  auto kern = prefill_fa_kernel<DR, W, QB>;
+  constexpr int kBM = W * 32 * QB;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                       S::kLdsBytes);
   const int n_qt = (n_tokens + kBM - 1) / kBM;
@@ -569,7 +575,7 @@ void prefill_expanded(const AttnShape& sh, const void* q_nope, const void* q_pe,
                       const void* v, const void* cache, const int64_t* cu, int batch, int64_t n_tokens,
                       void* out, hipStream_t s) {
   if (n_tokens <= 0 || batch <= 0) return;
-  launch_fa<64, kWavesFA>(sh, q_nope, q_pe, k_nope, v, cache, cu, batch, static_cast<int>(n_tokens), out, s);
+  launch_fa<64, kWavesFA, kQBFA>(sh, q_nope, q_pe, k_nope, v, cache, cu, batch, static_cast<int>(n_tokens), out, s);
 }
 
 }  // namespace mla
