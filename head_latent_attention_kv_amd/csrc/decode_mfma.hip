@@ -29,6 +29,8 @@
 // normalised o_ in bf16.
 #include <math.h>
 
+#include <cmath>
+
 #include <algorithm>
 
 #include "lds_dma.h"
@@ -71,7 +73,7 @@ struct Shape {
   static constexpr int kNC = R / kWaves;                        // PV columns per wave
   static constexpr int kNB = kNC / 16;
   static constexpr int kPBytes = kHeads * kPP;                  // one P buffer
-  static constexpr int kRedBytes = 2 * kHeads * 4 + 2 * kWaves * 4;  // exchange array + flags
+  static constexpr int kRedBytes = 3 * kHeads * 4 + 2 * kWaves * 4;  // exchange array, flags, max per head
   static constexpr int kLdsBytes = STAGES * kBufBytes + 2 * kPBytes + kRedBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
   static_assert(STAGES >= 3 && STAGES <= 4, "tiles t, t+1 resident and 1-2 copies in flight");
@@ -88,13 +90,15 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
     const bf16_t* __restrict__ cache, const int64_t* __restrict__ seq_start,
     const int32_t* __restrict__ seq_len, int batch, int H, int G, int d_rope, float scale,
     int n_split, int split_len, bf16_t* __restrict__ part_o, float* __restrict__ part_ml,
-    float* __restrict__ o_out) {
+    float* __restrict__ o_out, bf16_t* __restrict__ v4_out, const float* __restrict__ sink,
+    double rope_base, const double* __restrict__ freqs, int tail) {
   using S = Shape<R, RW, NHB, NHH, STAGES>;
   constexpr int kBufBytes = S::kBufBytes;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   unsigned char* pbuf = smem + STAGES * kBufBytes;                        // P [2][kHeads][kPP]
   float* xch = reinterpret_cast<float*>(pbuf + 2 * S::kPBytes);           // [2][kHeads]
   int* flag_lds = reinterpret_cast<int*>(xch + 2 * S::kHeads);            // [2][kWaves]
+  float* m_lds = reinterpret_cast<float*>(flag_lds + 2 * kWaves);          // [kHeads] (V4 epilogue)
 
   // ---- which (sequence, split, head group) this workgroup computes
   int pair, hh;
@@ -377,7 +381,40 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
   if (unit && lg == 0) xch[mb_s * S::kHeads + hloc] = l;
+  if (v4_out != nullptr && unit && mb_s == 0 && lg == 0) m_lds[hloc] = m_ref;
   lds_barrier();
+  if (v4_out != nullptr) {
+    // the DeepSeek-V4 variant with one split: the head's attention sink joins
+    // the denominator and the last `tail` columns are rotated back by the
+    // query's position; adjacent columns (a rotary pair) sit in adjacent lanes
+    const int32_t pos = seq_len[b] - 1;
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hl = hb * 16 + lg * 4 + i;
+        const int h = head0 + hl;
+        const bool ok = h < H;
+        const float lh = xch[hl] + xch[S::kHeads + hl];
+        const float inv = ok ? 1.f / (lh + exp2f(sink[ok ? h : 0] * kLog2e - m_lds[hl])) : 0.f;
+#pragma unroll
+        for (int nb = 0; nb < S::kNB; ++nb) {
+          const int col = c0 + nb * 16 + l16;
+          float v = o[hb][nb][i] * inv;
+          if (c0 + nb * 16 + 16 > R - tail) {  // uniform: the block holds rotary columns
+            const float other = __shfl_xor(v, 1, 64);
+            if (col >= R - tail) {
+              float cs, sn;
+              angle_cos_sin(-static_cast<double>(pos) * rope_freq((col - (R - tail)) / 2, rope_base, freqs), &cs,
+                            &sn);
+              v = (l16 & 1) == 0 ? v * cs - other * sn : v * cs + other * sn;
+            }
+          }
+          if (ok) v4_out[(static_cast<int64_t>(b) * H + h) * R + col] = f32_to_bf16(v);
+        }
+      }
+    return;
+  }
   const bool partials = part_o != nullptr;
   if (unit && mb_s == 0 && lg == 0 && partials && head < H) {
     const int64_t pidx = (static_cast<int64_t>(b) * n_split + split) * H + head;
@@ -408,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
 template <int R, int RW, int NHB, int NHH, int STAGES>
 void launch(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
             const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split, int split_len,
-            void* part_o, float* part_ml, float* o_out, hipStream_t s) {
+            void* part_o, float* part_ml, float* o_out, const V4Epilogue* v4, hipStream_t s) {
   using S = Shape<R, RW, NHB, NHH, STAGES>;
   auto kern = decode_mfma_kernel<R, RW, NHB, NHH, STAGES>;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -419,7 +456,9 @@ void launch(const AttnShape& sh, const void* q_lat, const void* q_pe, const void
                      static_cast<const bf16_t*>(q_lat), static_cast<const bf16_t*>(q_pe),
                      static_cast<const bf16_t*>(cache), seq_start, seq_len, batch, sh.H, sh.G,
                      sh.d_rope, sh.scale, n_split, split_len, static_cast<bf16_t*>(part_o), part_ml,
-                     o_out);
+                     o_out, v4 ? static_cast<bf16_t*>(v4->out) : nullptr, v4 ? v4->sink : nullptr,
+                     v4 ? std::pow(v4->theta, -2.0 / v4->d_rope) : 0.0, v4 ? v4->freqs : nullptr,
+                     v4 ? v4->d_rope : 0);
 }
 
 // Compiled shapes: (latent r, row width r + G*d_rope, 16-head blocks per workgroup,
@@ -462,12 +501,13 @@ int decode_mfma_blocks_per_cu(const AttnShape& sh) {
 
 void decode_mfma(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
                  const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split,
-                 int split_len, void* part_o, float* part_ml, float* o_out, hipStream_t s) {
+                 int split_len, void* part_o, float* part_ml, float* o_out, hipStream_t s,
+                 const V4Epilogue* v4) {
   if (batch <= 0) return;
 #define MLA_LAUNCH(R_, RW_, NHB_, NHH_, ST_, HLO_, HHI_)                                          \
   if (sh.r == R_ && sh.row_w == RW_ && sh.H >= HLO_ && sh.H <= HHI_) {                           \
     launch<R_, RW_, NHB_, NHH_, ST_>(sh, q_lat, q_pe, cache, seq_start, seq_len, batch, n_split, \
-                                     split_len, part_o, part_ml, o_out, s);                      \
+                                     split_len, part_o, part_ml, o_out, v4, s);                  \
     return;                                                                                      \
   }
   MLA_DECODE_SHAPES(MLA_LAUNCH)

@@ -1011,6 +1011,13 @@ int mla_v4_decode(const mla_v4_dims* dims, const void* q, const void* cache, con
   char* base = static_cast<char*>(workspace);
   void* part_o = base;
   float* part_ml = reinterpret_cast<float*>(base + p.part_o);
+  if (p.mfma && p.n_split == 1) {
+    // one split: the kernel applies the sink and the inverse rotation itself
+    const mla::V4Epilogue epi{out, sink, dims->rope_theta, rope_freqs, dims->d_rope};
+    mla::decode_mfma(sh, q, nullptr, cache, seq_start, seq_len, batch, 1, p.split_len, nullptr, nullptr, nullptr,
+                     s, &epi);
+    return launch_status();
+  }
   if (p.mfma)
     mla::decode_mfma(sh, q, nullptr, cache, seq_start, seq_len, batch, p.n_split, p.split_len, part_o, part_ml,
                      nullptr, s);

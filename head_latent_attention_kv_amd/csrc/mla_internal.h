@@ -115,9 +115,23 @@ void decode_wide(const AttnShape& sh, const void* q_lat, const void* q_pe, const
 bool decode_mfma_supported(const AttnShape& sh);
 int decode_mfma_blocks_per_cu(const AttnShape& sh);  // workgroups one CU holds (LDS-limited)
 int decode_mfma_head_groups(const AttnShape& sh);    // workgroups that share one sequence split
+struct V4Epilogue;
+// v4 (non-null: one split, a 16-head instance) writes the DeepSeek-V4 output
+// directly (sink in the denominator, inverse rotation of the tail).
 void decode_mfma(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
                  const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split,
-                 int split_len, void* part_o, float* part_ml, float* o_out, hipStream_t s);
+                 int split_len, void* part_o, float* part_ml, float* o_out, hipStream_t s,
+                 const V4Epilogue* v4 = nullptr);
+// The V4 variant's epilogue: the sink [H] (fp32 logits) joins each softmax's
+// denominator and the last d_rope dims of the output are rotated back by the
+// query's position (inverse frequencies from freqs, or theta).
+struct V4Epilogue {
+  void* out;  // bf16 [batch, H, r]
+  const float* sink;
+  double theta;
+  const double* freqs;
+  int d_rope;
+};
 
 // bf16 MFMA causal prefill kernel for the shapes it supports (see prefill_mfma.hip).
 bool prefill_mfma_supported(const AttnShape& sh);
