@@ -475,9 +475,15 @@ __global__ __launch_bounds__(256, 1) void merge_uv_kernel(SkinnyArgs sa) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
   const int m_groups = max(1, sa.m_groups);
-  const int m0 = (blockIdx.x % m_groups) * kMgRows;
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id.  When the
+  // grid divides evenly the ids are renumbered so that the token groups of one
+  // head share an XCD: the head's W_UV rows then cross HBM into one L2.
+  int wg = blockIdx.x + gridDim.x * blockIdx.y;
+  const int n_wg = gridDim.x * gridDim.y;
+  if (n_wg % (8 * gridDim.x) == 0) wg = (wg % 8) * (n_wg / 8) + wg / 8;
+  const int m0 = (wg % gridDim.x % m_groups) * kMgRows;
   const int m_last = sa.M - 1 - m0;  // last local token row
-  const int z = blockIdx.y;
+  const int z = wg / gridDim.x;
   const int n_st = (sa.K + kMgKC - 1) / kMgKC;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)smem));
   const bf16_t* a_head = static_cast<const bf16_t*>(sa.A) + static_cast<int64_t>(z) * sa.sAz;
