@@ -191,6 +191,11 @@ size_t smem_bytes(const AttnShape& sh) {
 
 int generic_head_block() { return kHB; }
 
+bool attend_generic_fits(int dtype, const AttnShape& sh) {
+  const size_t b = dtype == kF32 ? smem_bytes<float>(sh) : smem_bytes<bf16_t>(sh);
+  return b <= 160 * 1024;
+}
+
 void attend_generic(int dtype, const AttnShape& sh, const void* q_lat, const void* q_pe,
                     const void* cache, const int64_t* seq_start, const int32_t* seq_len,
                     const int64_t* cu, int batch, int64_t n_q, int n_split, int split_len,
@@ -199,12 +204,16 @@ void attend_generic(int dtype, const AttnShape& sh, const void* q_lat, const voi
   dim3 grid(static_cast<unsigned>(n_q), (sh.H + kHB - 1) / kHB, n_split);
   if (dtype == kF32) {
     size_t smem = smem_bytes<float>(sh);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(attend_generic_kernel<float>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
     hipLaunchKernelGGL(attend_generic_kernel<float>, grid, dim3(256), smem, s,
                        static_cast<const float*>(q_lat), static_cast<const float*>(q_pe),
                        static_cast<const float*>(cache), seq_start, seq_len, cu, batch, sh, n_split,
                        split_len, static_cast<float*>(part_o), part_ml, o_out);
   } else {
     size_t smem = smem_bytes<bf16_t>(sh);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(attend_generic_kernel<bf16_t>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
     hipLaunchKernelGGL(attend_generic_kernel<bf16_t>, grid, dim3(256), smem, s,
                        static_cast<const bf16_t*>(q_lat), static_cast<const bf16_t*>(q_pe),
                        static_cast<const bf16_t*>(cache), seq_start, seq_len, cu, batch, sh,

@@ -374,6 +374,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) any |= flags[w];
     if (!any) break;
+    // every wave has read the flags before the scan's first copies refill the
+    // ring slot that holds them
+    lds_barrier();
     run_pass(std::true_type{}, false);
     float mx = m_lane;
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));

@@ -25,6 +25,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
 
+AttnShape shape_of(const mla_dims* d);
+
 int check_dims(const mla_dims* d) {
   if (!d) return MLA_EINVAL;
   if (d->d_model <= 0 || d->n_heads <= 0 || d->n_groups <= 0 || d->rank <= 0 || d->d_rope <= 0 ||
@@ -44,6 +46,9 @@ int check_dims(const mla_dims* d) {
   // the cache-row epilogue holds one projected row (<= 1024 floats) and one
   // cos/sin table (<= 256 pairs) in LDS
   if (d->rank + static_cast<int64_t>(d->n_groups) * d->d_rope > 1024 || d->d_rope > 512) return MLA_ENOTSUP;
+  // fp32 layers attend in the generic kernel, whose staged tile of 32 fp32 rows
+  // must fit the 160 KB of LDS (cache rows up to 1017 values)
+  if (d->dtype == MLA_F32 && !mla::attend_generic_fits(mla::kF32, shape_of(d))) return MLA_ENOTSUP;
   return MLA_OK;
 }
 

@@ -98,6 +98,8 @@ void attend_generic(int dtype, const AttnShape& sh, const void* q_lat, const voi
                     const int64_t* cu, int batch, int64_t n_q, int n_split, int split_len,
                     void* part_o, float* part_ml, float* o_out, hipStream_t s);
 int generic_head_block();
+// whether the generic kernel's LDS tile for this shape and element type fits a CU
+bool attend_generic_fits(int dtype, const AttnShape& sh);
 
 // Log-sum-exp merge of split partials into normalised o_ (fp32 [n_q, H, r]).
 // part_o holds each split's normalised o_ in the layer's element type.

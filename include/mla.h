@@ -77,7 +77,9 @@ typedef struct mla_dims {
   int32_t n_groups;       /* G, rotary-key groups; head h uses group h / (H/G) */
   int32_t rank;           /* r, latent width (multiple of 16, at most 512) */
   int32_t d_rope;         /* rotary dims per query head and per key group (even, at most
-                             512; r + G*d_rope at most 1024) */
+                             512; r + G*d_rope at most 1024 for bf16 and at most 1017
+                             for fp32, whose 32-row attention tile must fit 160 KB of
+                             LDS) */
   int32_t d_nope;         /* non-rotary query/key dims per head */
   int32_t d_v;            /* value dims per head */
   int32_t dtype;          /* mla_dtype */
@@ -241,7 +243,13 @@ int mla_query(const mla_dims* dims, const void* x, const void* w_qc, const void*
  *   cache, cu_seqlens, batch, n_tokens, max_len: as mla_prefill
  *   w_uk device [H, d_nope, r]; w_uv device [H, d_v, r]; out device out [n_tokens, H, d_v]
  *   workspace device, >= mla_workspace_size(dims, MLA_OP_PREFILL_EXPANDED, batch, n_tokens,
- *   max_len) bytes: it holds k_nope and v in bf16 (2·n_tokens·H·(d_nope + d_v) bytes)
+ *   max_len) bytes.  After the call it holds the expanded keys and values in fp16
+ *   (11 significant bits, where bf16 would push the result past 1e-2):
+ *   k_nope [H, n_tokens, d_nope] from byte 0, then, from the next multiple of 256
+ *   bytes, vᵀ [H, d_v, T_pad] with T_pad = n_tokens rounded up to 32 and the pad
+ *   columns zero: 2·H·(n_tokens·d_nope + d_v·T_pad) bytes plus alignment.
+ *   Range: fp16 holds |k_nope|, |v| and |q_nope| up to 65504.  Nothing checks
+ *   this; larger values become inf and the output is then not finite.
  * Compiled for bf16 with d_nope = d_v = 128 and d_rope = 64; other layers get
  * MLA_ENOTSUP (mla_prefill covers them).  batch == 0 or n_tokens == 0 is a no-op. */
 int mla_prefill_expanded(const mla_dims* dims, const void* q_nope, const void* q_pe, const void* cache,

@@ -378,7 +378,12 @@ def v4_output(o, w_oa, w_ob, o_groups: int) -> np.ndarray:
 
 
 def max_rel_err(got, ref) -> float:
-    """max over (token, head) of ‖got − ref‖∞ / ‖ref‖∞ over the last axis."""
+    """max over (token, head) of ‖got − ref‖∞ / ‖ref‖∞ over the last axis.
+
+    The parity metric (per output vector, not per element: an attention output is
+    a weighted mean that crosses zero).  A vector whose reference is all zero is
+    measured by its absolute error; a NaN or inf in ``got`` makes the result NaN
+    or inf, which no bar accepts.  Empty inputs give 0."""
     got, ref = _f64(got), _f64(ref)
     num = np.abs(got - ref).max(axis=-1)
     den = np.abs(ref).max(axis=-1)

@@ -1,5 +1,5 @@
-"""Shared test/bench plumbing: seeded inputs to device tensors, the GPU chain through
-the C ABI, and the oracle on the same inputs.  Test infrastructure only."""
+"""Shared test plumbing: the GPU chain through the C ABI on seeded inputs, and the
+oracle on the same inputs.  Test infrastructure only."""
 from __future__ import annotations
 
 import dataclasses
@@ -8,6 +8,8 @@ from typing import Dict, List, Optional, Tuple
 import numpy as np
 
 import mla_inputs as I
+from mla_inputs.device import device_weights, raw_to_dev, to_dev  # noqa: F401  (used by the tests)
+from oracle import mla_oracle as O
 
 TOL = {"bf16": 1e-2, "f32": 1e-4}  # max relative error per (token, head), over d_v
 
@@ -15,15 +17,6 @@ TOL = {"bf16": 1e-2, "f32": 1e-4}  # max relative error per (token, head), over 
 def torch_mod():
     import torch
     return torch
-
-
-def to_dev(a: np.ndarray, dtype: str, device="cuda"):
-    """float32 array of representable values -> device tensor of the workload dtype."""
-    torch = torch_mod()
-    if dtype == "bf16":
-        bits = I.rne_bf16_bits(a).view(np.int16)
-        return torch.from_numpy(bits).view(torch.bfloat16).to(device)
-    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
 
 
 def to_host(t) -> np.ndarray:
@@ -45,8 +38,8 @@ class DeviceLayer:
 
 def make_layer(cfg: I.MLAConfig, device="cuda") -> DeviceLayer:
     import head_latent_attention_kv_amd as M
-    w = I.weights(cfg)
-    return DeviceLayer(cfg, w, {k: to_dev(v, cfg.dtype, device) for k, v in w.items()}, M.dims_of(cfg))
+    w, wd = device_weights(cfg, device)
+    return DeviceLayer(cfg, w, wd, M.dims_of(cfg))
 
 
 def write_cache(layer: DeviceLayer, x_dev, positions: np.ndarray, slots: np.ndarray, cache,
@@ -127,14 +120,6 @@ class DecodeRun:
     q_pe: object
     out: object
     x_query: np.ndarray  # [B, d_model] float32 (representable values)
-
-
-def raw_to_dev(a: np.ndarray, dtype: str, device="cuda"):
-    """Unrounded float32 draw -> device tensor; bf16 rounding (RNE) happens on the
-    device and gives the same values as mla_inputs.quantize on the host."""
-    torch = torch_mod()
-    t = torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
-    return t.to(torch.bfloat16) if dtype == "bf16" else t
 
 
 def key_rows(cfg, b: int, c0: int, c1: int, n: int, x_scale: float = 1.0,
@@ -285,8 +270,14 @@ def oracle_absorbed_rows(cfg, w, q_lat: np.ndarray, q_pe: np.ndarray, cache_rows
     return out
 
 
-def rel_err_rows(got: np.ndarray, ref: np.ndarray) -> float:
-    num = np.abs(got - ref).max(axis=-1)
-    den = np.abs(ref).max(axis=-1)
-    den = np.where(den == 0, 1.0, den)
-    return float((num / den).max())
+def write_err(cfg, rows_gpu: np.ndarray, rows_ref: np.ndarray) -> float:
+    """Write parity of whole cache rows: the latent c per row and each rotary key
+    kr_g per (row, group), each measured on its own (so neither hides the other)."""
+    c_g, kr_g = O.split_rows(rows_gpu, cfg.rank, cfg.n_groups, cfg.d_rope)
+    c_o, kr_o = O.split_rows(rows_ref, cfg.rank, cfg.n_groups, cfg.d_rope)
+    return max(O.max_rel_err(c_g, c_o), O.max_rel_err(kr_g, kr_o))
+
+
+# the parity metric of every GPU test: the oracle's own max_rel_err (pinned on
+# hand-built values in tests/test_oracle_pins.py), not a second copy of it
+rel_err_rows = O.max_rel_err

@@ -63,11 +63,17 @@ def test_dims_validation_codes():
         (dict(d_model=260), abi.MLA_ENOTSUP),     # bf16 rows must be 16-byte multiples
         (dict(softmax_scale=float("nan")), abi.MLA_EINVAL),
         (dict(rope_theta=-1.0), abi.MLA_EINVAL),
+        # fp32 rows of 1016 values fit the generic kernel's 160 KB LDS tile, 1018 do not
+        (dict(dtype="f32", rank=512, n_groups=1, d_rope=504), abi.MLA_OK),
+        (dict(dtype="f32", rank=512, n_groups=1, d_rope=506), abi.MLA_ENOTSUP),
+        (dict(dtype="f32", rank=512, n_groups=2, d_rope=256), abi.MLA_ENOTSUP),
+        (dict(dtype="bf16", rank=512, n_groups=2, d_rope=256), abi.MLA_OK),
     ]
     for change, want in cases:
         d = abi.make_dims(**{**base, **change})
         assert lib.mla_check_dims(ctypes.byref(d)) == want, change
-        assert lib.mla_workspace_size(ctypes.byref(d), abi.MLA_OP_DECODE, 4, 0, 100) == 0
+        if want != abi.MLA_OK:
+            assert lib.mla_workspace_size(ctypes.byref(d), abi.MLA_OP_DECODE, 4, 0, 100) == 0
 
 
 def test_calls_reject_bad_arguments_before_any_launch():

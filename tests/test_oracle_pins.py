@@ -130,9 +130,9 @@ def _absorbed(x, w, seg, pos, *, H, G, d_nope, d_r, theta, scale, norm=False, ep
                         latent_rmsnorm=norm, eps=eps)
     c, kr = O.split_rows(rows, r, G, d_r)
     qn, qr = O.query(x, w["w_qc"], w["w_qr"], pos, n_heads=H, d_nope=d_nope, d_rope=d_r, theta=theta)
-    q_lat = np.einsum("hdc,bhqd->bhqc", w["w_uk"], qn.transpose(1, 0, 2)[None])[0]  # [H, T, r]
+    q_lat = O.absorbed_query(qn, w["w_uk"])  # [T, H, r]: the function every q_lat check uses
     g = np.arange(H) // (H // G)
-    s_lat = np.einsum("hqc,lc->hql", q_lat, c)
+    s_lat = np.einsum("qhc,lc->hql", q_lat, c)
     s_pe = np.einsum("qhd,lhd->hql", qr, kr[:, g, :])
     a = scale * (s_lat + s_pe)
     allowed = (seg[:, None] == seg[None, :]) & (pos[None, :] <= pos[:, None])
@@ -748,3 +748,89 @@ def test_p10_yarn_logit_scale():
     √(1/t) = 2, so logits are multiplied by 4."""
     assert O.yarn_logit_scale(1.0) == 1.0
     assert abs(O.yarn_logit_scale(math.exp(10.0)) - 4.0) < 1e-12
+
+
+# ----------------------------------------------------------------------------
+# P11: the parity metric and the test harness's absorbed reference
+# ----------------------------------------------------------------------------
+# Every GPU parity claim is a value of O.max_rel_err compared with a bar, so the
+# metric itself is pinned here on hand-built arrays whose answer is worked out by
+# hand: per (token, head), ‖got − ref‖∞ / ‖ref‖∞ over the last axis, then the max.
+
+
+def test_p11_max_rel_err_hand_values():
+    ref = np.zeros((2, 3, 4))
+    got = np.zeros((2, 3, 4))
+    # (0, 0): a large reference; an error of 1 in a zero element gives 1/100
+    ref[0, 0] = [100.0, 0.0, 0.0, 0.0]
+    got[0, 0] = [100.0, 1.0, 0.0, 0.0]
+    # (1, 2): a small reference; an error of 0.01 gives 0.01 / 0.1 = 0.1 (the max)
+    ref[1, 2] = [0.1, -0.1, 0.1, 0.05]
+    got[1, 2] = [0.1, -0.11, 0.1, 0.05]
+    # (0, 1): ratio 0.5 / 20 = 0.025
+    ref[0, 1] = [-20.0, 3.0, 0.0, 1.0]
+    got[0, 1] = [-20.0, 3.0, 0.5, 1.0]
+    # the remaining rows are all-zero references with exact results
+    assert abs(O.max_rel_err(got, ref) - 0.1) < 1e-15
+    # the mean over the rows would be (0.01 + 0.1 + 0.025) / 6, a global
+    # normalisation 0.01 / 100, a per-element ratio infinite: none is 0.1
+    assert O.max_rel_err(got[0], ref[0]) == pytest.approx(0.025, abs=1e-15)
+    assert O.max_rel_err(got[0, 0], ref[0, 0]) == pytest.approx(0.01, abs=1e-15)
+
+
+def test_p11_max_rel_err_axis_and_scale():
+    """Normalised along the last axis only: transposing the two leading axes keeps the
+    value, transposing the last one changes it; a common positive factor cancels."""
+    ref = np.array([[[4.0, 0.0], [0.0, 0.5]]])       # rows (0,0) = [4, 0], (0,1) = [0, 0.5]
+    got = np.array([[[4.0, 0.2], [0.0, 0.5]]])       # row (0,0): 0.2 / 4 = 0.05
+    assert O.max_rel_err(got, ref) == pytest.approx(0.05, abs=1e-15)
+    # along the other axis the rows would be [4, 0] / [0, 0.5]: 0 and 0.2 / 0.5 = 0.4
+    assert O.max_rel_err(got.swapaxes(1, 2), ref.swapaxes(1, 2)) == pytest.approx(0.4, abs=1e-15)
+    assert O.max_rel_err(got.swapaxes(0, 1), ref.swapaxes(0, 1)) == pytest.approx(0.05, abs=1e-15)
+    assert O.max_rel_err(3.5 * got, 3.5 * ref) == pytest.approx(0.05, abs=1e-15)
+
+
+def test_p11_max_rel_err_zero_reference_and_edges():
+    """A row whose reference is all zero is measured by its absolute error; an empty
+    input has no error; a NaN or inf in the result never passes a bar."""
+    ref = np.array([[0.0, 0.0, 0.0], [1.0, 2.0, -2.0]])
+    assert O.max_rel_err(np.array([[0.0, 0.0, 0.0], [1.0, 2.0, -2.0]]), ref) == 0.0
+    assert O.max_rel_err(np.array([[0.0, 0.003, -0.004], [1.0, 2.0, -2.0]]), ref) == pytest.approx(0.004)
+    assert O.max_rel_err(np.zeros((0, 4)), np.zeros((0, 4))) == 0.0
+    for bad in (np.nan, np.inf, -np.inf):
+        got = ref.copy()
+        got[1, 1] = bad
+        e = O.max_rel_err(got, ref)
+        assert not (e <= 1e-2), bad
+
+
+def test_p11_harness_checker_is_the_oracle_metric():
+    """The GPU tests' checker is the oracle's metric, not a second copy of it."""
+    from tests import harness as Hh
+    assert Hh.rel_err_rows is O.max_rel_err
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_p11_harness_absorbed_reference_matches_expanded_oracle(G):
+    """tests/harness.oracle_absorbed_rows (the reference of the restart tests: the
+    query the kernels read, K = [c ; kr], V = c, then W_UV) equals the oracle's
+    non-absorbed decode output when it is given the float64 absorbed query
+    q_lat = O.absorbed_query(q_nope, W_UK) (associativity, eqs. (4)-(5))."""
+    import types
+
+    from tests import harness as Hh
+    rng = np.random.default_rng(40 + G)
+    H, r, d_r, d_nope, d_v, D, n = 8, 24, 6, 5, 7, 16, 13
+    w = _rand_layer(rng, D, H, G, r, d_r, d_nope, d_v)
+    cfg = types.SimpleNamespace(n_heads=H, rank=r, n_groups=G, d_rope=d_r, d_v=d_v, softmax_scale=0.29)
+    x = rng.standard_normal((n, D))
+    pos = np.arange(n) + 5
+    rows = O.cache_rows(x, w["w_dkv"], w["w_kr"], pos, n_groups=G, d_rope=d_r, theta=700.0)
+    qn, qr = O.query(x[-1:], w["w_qc"], w["w_qr"], pos[-1:], n_heads=H, d_nope=d_nope, d_rope=d_r,
+                     theta=700.0)
+    q_lat = O.absorbed_query(qn, w["w_uk"])[0]
+    got = Hh.oracle_absorbed_rows(cfg, w, q_lat, qr[0], rows, head_chunk=3)
+    c, kr = O.split_rows(rows, r, G, d_r)
+    ref = O.mla_attention(qn, qr, c, kr, w["w_uk"], w["w_uv"], pos[-1:], pos, np.zeros(1, int),
+                          np.zeros(n, int), 0.29)[0]
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
