@@ -17,7 +17,10 @@
 //     between waves through a small LDS buffer.
 // Tiles of 32 rows:
 //   - copies HBM -> LDS by global_load_lds_dwordx4 into 4 buffers (tiles t and
-//     t+1 in use, t+2 and t+3 in flight), stored without padding; the 16-byte
+//     t+1 in use, t+2 and t+3 in flight), issued by waves 0-3 only: a copy's
+//     issue stalls while the CU's memory pipeline is full, and with one issuing
+//     wave per SIMD the other wave keeps the SIMD's MFMAs busy meanwhile (the
+//     waves w and w + 4 share a SIMD); stored without padding; the 16-byte
 //     chunks of a row are XOR-swizzled by (row / 2) within groups of eight, so
 //     the 16 rows one fragment read touches fall on distinct bank groups;
 //   - score: Sᵀ[32 rows x 16 heads], two 16x16 blocks of
@@ -58,7 +61,8 @@ constexpr int kRowBytes = kRW * 2;   // 1152
 constexpr int kRowChunks = kRowBytes / 16;           // 72
 constexpr int kTileBytes = kTL * kRowBytes;          // 36864
 constexpr int kDmaOps = kTileBytes / 1024;           // 36 one-KB copies per tile
-constexpr int kDmaMax = (kDmaOps + kWaves - 1) / kWaves;  // 5: waves 0-3 issue 5, waves 4-7 issue 4
+constexpr int kDmaWaves = 4;                          // waves 0-3 issue every copy; 4-7 none
+constexpr int kDmaMax = kDmaOps / kDmaWaves;          // 9
 constexpr int kSteps = kRW / 32;                     // 18 score k-steps
 constexpr int kHW = kHeads / kWaves;                 // 16 heads per wave in the score
 constexpr int kHB = kHeads / 16;                     // 8 head blocks of the PV
@@ -73,7 +77,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kSLA = 2;                              // score k-steps of fragments in flight
 
 static_assert(kHW == 16, "one 16-head block per wave in the score");
-static_assert(kDmaOps - (kWaves / 2) * kDmaMax == (kWaves / 2) * (kDmaMax - 1), "copies split 5/4 over the waves");
+static_assert(kDmaOps == kDmaWaves * kDmaMax, "copies split evenly over the issuing waves");
 static_assert(kRowChunks % 8 == 0, "swizzle groups of eight chunks");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 static_assert(kHeads * 4 <= kFlagsOff && kFlagsOff + 4 * kWaves <= kTileBytes, "xch and flags inside tile slot 0");
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
-  const bool five = wave < kDmaOps - kWaves * (kDmaMax - 1);  // this wave issues 5 copies a tile
+  const bool dma_wave = wave < kDmaWaves;
 
   const int64_t row0 = seq_start[b];
   const int len = seq_len[b];
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
   const char* cache_b = reinterpret_cast<const char*>(cache + row0 * kRW);
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)smem));
 
-  // ---- tile copy: wave w issues 1 KB copies j = w + 8i < 36; copy j fills LDS
+  // ---- tile copy: wave w < 4 issues 1 KB copies j = w + 4i < 36; copy j fills LDS
   // chunks [64j, 64j + 64) of the tile image.  LDS chunk L (row L / 72, slot
   // L % 72) holds global chunk swz(slot, row) of the same row, which is
   // L ^ ((row / 2) & 7) since rows are whole groups of eight chunks.  Rows past
@@ -154,25 +158,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
     }
   };
   auto issue_tile = [&](int t) {
+    if (dma_wave) {
 #pragma unroll
-    for (int i = 0; i < kDmaMax; ++i) {
-      const int j = wave + kWaves * i;
-      if (j < kDmaOps) issue_op(t, j);
+      for (int i = 0; i < kDmaMax; ++i) issue_op(t, wave + kDmaWaves * i);
     }
   };
   auto wait_tile = [&](int t, int last_issued) {
     const int n = last_issued - t;  // tiles issued after t
-    if (five) {
+    if (dma_wave) {
       switch (n) {
         case 0: wait_tiles_after<0, kDmaMax>(); break;
         case 1: wait_tiles_after<1, kDmaMax>(); break;
         default: wait_tiles_after<2, kDmaMax>(); break;
-      }
-    } else {
-      switch (n) {
-        case 0: wait_tiles_after<0, kDmaMax - 1>(); break;
-        case 1: wait_tiles_after<1, kDmaMax - 1>(); break;
-        default: wait_tiles_after<2, kDmaMax - 1>(); break;
       }
     }
   };
@@ -283,18 +280,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
   };
 
   // PV of tile tt over this wave's 64 columns, P of all heads from exchange
-  // buffer tt % 2: head block outer, the wave's four C fragments held
-  auto pv = [&](int tt) {
+  // buffer tt % 2: head block outer, the wave's four C fragments held.
+  // pv_load reads the C fragments and the first P fragment (issued before the
+  // softmax, whose VALU work then covers their latency); pv_mma reads each P
+  // fragment one head block ahead of its MFMAs.
+  auto pfrag = [&](const unsigned char* pb, int hb) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pb + (hb * 64 + lane) * 16));
+  };
+  auto pv_load = [&](int tt, bf16x8 (&cf)[kCB], bf16x8 (&pf)[2]) {
     const unsigned char* tb = smem + (tt % kStages) * kTileBytes;
-    const unsigned char* pb = smem + kPOff + (tt & 1) * kPBytes;
-    bf16x8 cf[kCB];
 #pragma unroll
     for (int j = 0; j < kCB; ++j) cf[j] = cfrag(tb, wave * kCB + j);
+    pf[0] = pfrag(smem + kPOff + (tt & 1) * kPBytes, 0);
+  };
+  auto pv_mma = [&](int tt, const bf16x8 (&cf)[kCB], bf16x8 (&pf)[2]) {
+    const unsigned char* pb = smem + kPOff + (tt & 1) * kPBytes;
 #pragma unroll
     for (int hb = 0; hb < kHB; ++hb) {
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pb + (hb * 64 + lane) * 16));
+      if (hb + 1 < kHB) pf[(hb + 1) & 1] = pfrag(pb, hb + 1);
 #pragma unroll
-      for (int j = 0; j < kCB; ++j) o[hb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, cf[j], o[hb][j], 0, 0, 0);
+      for (int j = 0; j < kCB; ++j)
+        o[hb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[hb & 1], cf[j], o[hb][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -354,8 +360,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
       if constexpr (kScan) {
         m_lane = fmaxf(m_lane, tile_max(s_next));
       } else {
+        bf16x8 cf[kCB], pf[2];
+        pv_load(t, cf, pf);
         softmax(s_next, smem + kPOff + ((t + 1) & 1) * kPBytes);
-        pv(t);
+        pv_mma(t, cf, pf);
       }
     }
     lds_barrier();  // every wave is done with the ring and the P buffers
