@@ -47,8 +47,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps before each timed loop (the shader clock takes ~20 ms of load to settle)")
     ap.add_argument("--workload", default="deepseek_v2_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
@@ -106,8 +107,10 @@ class Timer:
 
 
 def spread(t: dict, scale: float = 1.0, unit: str = "ms") -> dict:
+    """Per-call quantiles from the run with an event between calls (each event
+    record adds a few microseconds to the call it follows)."""
     return {"unit": unit, "median": round(t["median_ms"] * scale, 4), "p10": round(t["p10_ms"] * scale, 4),
-            "p90": round(t["p90_ms"] * scale, 4), "n": t["n"]}
+            "p90": round(t["p90_ms"] * scale, 4), "n": t["n"], "timing": "one event between calls"}
 
 
 def counters(kernel_file: str, summary: str):
@@ -166,10 +169,10 @@ def attention_alg_bytes(cfg, lengths) -> int:
 
 
 def attention_alg_flops(cfg, lengths) -> int:
-    """Score (2(r + G·d_rope) per row and head: the zero-padded query row is one
-    contraction over the whole cache row) and P·c (2r)."""
+    """Score (2(r + d_rope) per row and head: a head reads its own group's rotary
+    key only) and P·c (2r)."""
     rows = int(sum(lengths))
-    return rows * cfg.n_heads * (2 * cfg.row_width + 2 * cfg.rank)
+    return rows * cfg.n_heads * (2 * (cfg.rank + cfg.d_rope) + 2 * cfg.rank)
 
 
 def decode_alg_flops(cfg, lengths) -> int:
@@ -179,9 +182,9 @@ def decode_alg_flops(cfg, lengths) -> int:
 
 def prefill_alg_flops(cfg, L: int) -> int:
     """Causal absorbed attention over one sequence of L tokens: every (query,
-    key <= query, head) pair costs 2(r + G·d_rope) for the score and 2r for P·c."""
+    key <= query, head) pair costs 2(r + d_rope) for the score and 2r for P·c."""
     pairs = L * (L + 1) // 2
-    return pairs * cfg.n_heads * (2 * cfg.row_width + 2 * cfg.rank)
+    return pairs * cfg.n_heads * (2 * (cfg.rank + cfg.d_rope) + 2 * cfg.rank)
 
 
 def prefill_orig_alg_flops(cfg, L: int) -> int:
@@ -353,11 +356,8 @@ def bench_decode(args, torch, M, I, D, cfg):
         M.mla_decode(dims, q_lat, q_pe, caches[i % n_copies], seq_start, seq_len, max_len, wd["w_uv"],
                      out, workspace=ws_d)
 
-    t_step = T.run(step, args.steps)
-    ms_step = t_step["mean_ms"]
-    print(f"[bench] {cfg.name}: {args.steps} steps: {ms_step * 1e3:.1f} us/step (median "
-          f"{t_step['median_ms'] * 1e3:.1f}, p10 {t_step['p10_ms'] * 1e3:.1f}, p90 {t_step['p90_ms'] * 1e3:.1f}) "
-          f"(setup {setup_s:.1f} s, {n_copies} cache copies)", file=sys.stderr, flush=True)
+    # the decode call and the attention kernel first, the whole step (the
+    # headline) last, each after its own warm-up steps
     t_dec = T.run(decode_only, args.steps)
     ms_dec = t_dec["mean_ms"]
 
@@ -373,6 +373,11 @@ def bench_decode(args, torch, M, I, D, cfg):
 
     t_att = T.run(attention_only, args.steps)
     ms_att = t_att["mean_ms"]
+    t_step = T.run(step, args.steps)
+    ms_step = t_step["mean_ms"]
+    print(f"[bench] {cfg.name}: {args.steps} steps: {ms_step * 1e3:.1f} us/step (median "
+          f"{t_step['median_ms'] * 1e3:.1f}, p10 {t_step['p10_ms'] * 1e3:.1f}, p90 {t_step['p90_ms'] * 1e3:.1f}) "
+          f"(setup {setup_s:.1f} s, {n_copies} cache copies)", file=sys.stderr, flush=True)
     alg_bytes = attention_alg_bytes(cfg, lengths)
     alg_flops = attention_alg_flops(cfg, lengths)
     achieved = alg_bytes / (ms_att * 1e-3) / 1e9
@@ -521,6 +526,9 @@ def bench_tiny(args, torch, M, I, D, cfg):
     cu = torch.tensor([0, L], dtype=torch.int64, device="cuda")
     seq_start = torch.zeros(1, dtype=torch.int64, device="cuda")
     seq_lens = [torch.tensor([L + s + 1], dtype=torch.int32, device="cuda") for s in range(S)]
+    # one-element tensors per decode step (the library takes 16-byte aligned pointers)
+    pos_1 = [torch.tensor([L + s], dtype=torch.int32, device="cuda") for s in range(S)]
+    slot_1 = [torch.tensor([L + s], dtype=torch.int64, device="cuda") for s in range(S)]
     ws_w = torch.empty(max(256, M.mla_workspace_size(dims, M.MLA_OP_WRITE_CACHE, 0, L, 0)), dtype=torch.uint8,
                        device="cuda")
     ws_a = torch.empty(max(256, M.mla_workspace_size(dims, M.MLA_OP_ABSORB, 0, L, 0)), dtype=torch.uint8,
@@ -541,9 +549,9 @@ def bench_tiny(args, torch, M, I, D, cfg):
         prefill_only(i)
         for s in range(S):
             p = L + s
-            M.mla_write_cache(dims, x[p:p + 1], wd["w_dkv"], wd["w_kr"], pos[p:p + 1], slots[p:p + 1], cache,
+            M.mla_write_cache(dims, x[p:p + 1], wd["w_dkv"], wd["w_kr"], pos_1[s], slot_1[s], cache,
                               workspace=ws_w)
-            M.mla_absorb(dims, x[p:p + 1], wd["w_qc"], wd["w_qr"], wd["w_uk"], pos[p:p + 1], q_lat[p:p + 1],
+            M.mla_absorb(dims, x[p:p + 1], wd["w_qc"], wd["w_qr"], wd["w_uk"], pos_1[s], q_lat[p:p + 1],
                          q_pe[p:p + 1], workspace=ws_a)
             M.mla_decode(dims, q_lat[p:p + 1], q_pe[p:p + 1], cache, seq_start, seq_lens[s], p + 1, wd["w_uv"],
                          out_dec[s:s + 1], workspace=ws_d)
