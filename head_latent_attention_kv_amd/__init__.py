@@ -7,6 +7,7 @@ its calls:
     mla_write_cache  — c = x·W_DKVᵀ (+RMSNorm), kr = RoPE(x·W_KRᵀ), store [c ; kr]
     mla_absorb       — q_lat = (x·W_QCᵀ)·W_UK per head, q_pe = RoPE(x·W_QRᵀ)
     mla_decode       — one query per sequence against its cached rows
+    mla_decode_noalloc — mla_decode with the library's static scratch (allocates nothing)
     mla_prefill      — causal attention over packed sequences
     mla_decode_partials — the decode attention's per-split softmax partials
     mla_query        — q_nope = x·W_QCᵀ, q_pe = RoPE(x·W_QRᵀ) (no absorption)
@@ -23,7 +24,7 @@ from ._abi import (  # noqa: F401
     MLA_V4_OP_DECODE, MLA_V4_OP_OUTPUT, MLA_V4_OP_PREFILL, MLA_V4_OP_QUERY, MLA_V4_OP_WRITE_CACHE, MlaV4Dims,
     mla_v4_decode, mla_v4_output, mla_v4_prefill, mla_v4_query, mla_v4_workspace_size, mla_v4_write_cache,
     v4_dims_of,
-    MLA_BF16, MLA_EHIP, MLA_EINVAL, MLA_ENOTSUP, MLA_EWORKSPACE, MLA_F32, MLA_OK, MLA_OP_ABSORB,
+    MLA_BF16, MLA_EHIP, MLA_EINVAL, MLA_ESCRATCH, MLA_NOALLOC_SCRATCH_BYTES, mla_decode_noalloc, MLA_ENOTSUP, MLA_EWORKSPACE, MLA_F32, MLA_OK, MLA_OP_ABSORB,
     MLA_OP_DECODE, MLA_OP_OUTPUT, MLA_OP_PREFILL, MLA_OP_PREFILL_EXPANDED, MLA_OP_QUERY, MLA_OP_WRITE_CACHE,
     MlaDims, MlaError, dims_of, load, make_dims, mla_absorb, mla_absorb_lowrank, mla_decode,
     mla_decode_partials, mla_decode_split_rows, mla_decode_splits, mla_lowrank_workspace_size, mla_output,
@@ -34,7 +35,7 @@ from ._abi import (  # noqa: F401
 
 __all__ = [
     "MlaDims", "MlaError", "dims_of", "load", "make_dims", "mla_absorb", "mla_decode",
-    "mla_decode_partials", "mla_decode_split_rows", "mla_decode_splits", "mla_prefill",
+    "mla_decode_partials", "mla_decode_noalloc", "mla_decode_split_rows", "mla_decode_splits", "mla_prefill",
     "mla_prefill_expanded", "mla_query", "mla_workspace_size", "mla_write_cache", "strerror",
     "mla_absorb_lowrank", "mla_query_lowrank", "mla_lowrank_workspace_size", "mla_output",
     "MlaV4Dims", "v4_dims_of", "mla_v4_write_cache", "mla_v4_query", "mla_v4_decode", "mla_v4_prefill",

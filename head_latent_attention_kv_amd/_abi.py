@@ -10,7 +10,8 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmla_amd.so")
 
-MLA_OK, MLA_EINVAL, MLA_ENOTSUP, MLA_EWORKSPACE, MLA_EHIP = 0, -1, -2, -3, -4
+MLA_OK, MLA_EINVAL, MLA_ENOTSUP, MLA_EWORKSPACE, MLA_EHIP, MLA_ESCRATCH = 0, -1, -2, -3, -4, -5
+MLA_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # include/mla.h
 MLA_F32, MLA_BF16 = 0, 1
 MLA_OP_WRITE_CACHE, MLA_OP_ABSORB, MLA_OP_DECODE, MLA_OP_PREFILL = 0, 1, 2, 3
 MLA_OP_QUERY, MLA_OP_PREFILL_EXPANDED, MLA_OP_OUTPUT = 4, 5, 6
@@ -54,6 +55,7 @@ SIGNATURES = {
     "mla_decode_splits": (_i32, [_PD, _i32, _i32]),
     "mla_decode_split_rows": (_i32, [_PD, _i32, _i32]),
     "mla_decode_partials": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "mla_decode_noalloc": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp]),
     "mla_query": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "mla_prefill_expanded": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _vp, _vp, _vp, _vp,
                                             _sz, _vp]),
@@ -228,6 +230,19 @@ def mla_decode(dims, q_lat, q_pe, cache, seq_start, seq_len, max_len, w_uv, out,
         _ptr(seq_start, "seq_start", torch.int64), _ptr(seq_len, "seq_len", torch.int32), B,
         int(max_len), _ptr(w_uv, "w_uv", et), _ptr(out, "out", et), _ptr(ws, "workspace"), nbytes,
         _stream(stream)))
+    return out
+
+
+def mla_decode_noalloc(dims, q_lat, q_pe, cache, seq_start, seq_len, max_len, w_uv, out, stream=None):
+    """mla_decode with the library's static scratch array in place of a workspace:
+    no device memory is allocated on this path."""
+    torch = _torch()
+    et = _elem_dtype(dims)
+    B = q_lat.shape[0]
+    _check("mla_decode_noalloc", load().mla_decode_noalloc(
+        ctypes.byref(dims), _ptr(q_lat, "q_lat", et), _ptr(q_pe, "q_pe", et), _ptr(cache, "cache", et),
+        _ptr(seq_start, "seq_start", torch.int64), _ptr(seq_len, "seq_len", torch.int32), B,
+        int(max_len), _ptr(w_uv, "w_uv", et), _ptr(out, "out", et), _stream(stream)))
     return out
 
 

@@ -351,6 +351,7 @@ const char* mla_strerror(int status) {
     case MLA_ENOTSUP: return "unsupported dimensions";
     case MLA_EWORKSPACE: return "workspace too small";
     case MLA_EHIP: return "HIP runtime error";
+    case MLA_ESCRATCH: return "the call needs more than the static scratch array (MLA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

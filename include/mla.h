@@ -55,7 +55,8 @@ typedef enum mla_status {
   MLA_EINVAL = -1,     /* null/misaligned pointer, bad dimension, H % G != 0, ... */
   MLA_ENOTSUP = -2,    /* a dimension combination the compiled kernels do not cover */
   MLA_EWORKSPACE = -3, /* workspace smaller than mla_workspace_size() */
-  MLA_EHIP = -4        /* the HIP runtime reported an error at launch */
+  MLA_EHIP = -4,       /* the HIP runtime reported an error at launch */
+  MLA_ESCRATCH = -5    /* the call needs more than the library's static scratch array */
 } mla_status;
 
 typedef enum mla_dtype { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
@@ -170,6 +171,25 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_pe, const 
                const int64_t* seq_start, const int32_t* seq_len, int32_t batch, int32_t max_len,
                const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
                void* stream);
+
+/* mla_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The split partials live in a static device array of
+ * MLA_NOALLOC_SCRATCH_BYTES inside the library; every GPU the library runs on
+ * holds its own copy from the first call on that device until the process ends.
+ * The call allocates nothing.  Arguments and results are those of mla_decode;
+ * the current device must be the stream's device.
+ *   MLA_ESCRATCH (before any HIP call) when mla_workspace_size(dims,
+ *   MLA_OP_DECODE, batch, 0, max_len) exceeds MLA_NOALLOC_SCRATCH_BYTES
+ *   (64 MiB covers 64 sequences of 8192 rows at H = 128, r = 512);
+ *   MLA_EHIP if the array's device address cannot be taken.
+ * Every call on a GPU uses that GPU's one array, and the array keeps the last
+ * call's contents: calls that overlap on one GPU (two streams, two threads)
+ * race.  Serialise them. */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int mla_decode_noalloc(const mla_dims* dims, const void* q_lat, const void* q_pe, const void* cache,
+                       const int64_t* seq_start, const int32_t* seq_len, int32_t batch, int32_t max_len,
+                       const void* w_uv, void* out, void* stream);
 
 /* Number of context splits mla_decode uses for this batch (>= 1), or a negative
  * mla_status.  Split j of a sequence covers its rows [j*L, min(n, (j+1)*L)) with

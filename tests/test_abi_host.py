@@ -99,6 +99,28 @@ def test_calls_reject_bad_arguments_before_any_launch():
     assert lib.mla_strerror(abi.MLA_EWORKSPACE) == b"workspace too small"
 
 
+def test_noalloc_decode_refuses_before_any_hip_call():
+    """mla_decode_noalloc checks dims, pointers and the static scratch's size on the
+    host: a refused call makes no HIP call (none is possible here)."""
+    abi, lib = _lib()
+    d = abi.dims_of(I.CONFIGS["deepseek_v2_decode"])
+    f = lib.mla_decode_noalloc
+    p = 1 << 20  # aligned, never dereferenced
+    # 64 sequences x 8192 rows fit the 64 MiB array, 300 sequences (one split, 78.6 MB of fp32 o_) do not
+    assert lib.mla_workspace_size(ctypes.byref(d), abi.MLA_OP_DECODE, 64, 0, 8192) <= abi.MLA_NOALLOC_SCRATCH_BYTES
+    need = lib.mla_workspace_size(ctypes.byref(d), abi.MLA_OP_DECODE, 300, 0, 8192)
+    assert need > abi.MLA_NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(d), p, p, p, p, p, 300, 8192, p, p, None) == abi.MLA_ESCRATCH
+    assert b"static scratch" in lib.mla_strerror(abi.MLA_ESCRATCH)
+    assert f(ctypes.byref(d), None, p, p, p, p, 4, 100, p, p, None) == abi.MLA_EINVAL
+    assert f(ctypes.byref(d), p + 8, p, p, p, p, 4, 100, p, p, None) == abi.MLA_EINVAL
+    assert f(ctypes.byref(d), p, p, p, p, p, -1, 100, p, p, None) == abi.MLA_EINVAL
+    assert f(ctypes.byref(d), p, p, p, p, p, 4, 0, p, p, None) == abi.MLA_EINVAL
+    assert f(ctypes.byref(d), p, p, p, p, p, 0, 100, p, p, None) == abi.MLA_OK
+    bad = abi.make_dims(d_model=256, n_heads=8, n_groups=3, rank=64, d_rope=16, d_nope=32, d_v=32, dtype="bf16")
+    assert f(ctypes.byref(bad), p, p, p, p, p, 4, 100, p, p, None) == abi.MLA_EINVAL
+
+
 def test_decode_split_queries():
     abi, lib = _lib()
     d = abi.dims_of(I.CONFIGS["deepseek_v2_decode"])
