@@ -156,28 +156,92 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(
   }
 }
 
-// o_ = Σ_j 2^(m_j - M) l_j o_j / Σ_j 2^(m_j - M) l_j over the splits j of (query, head)
+// o_ = Σ_j 2^(m_j - M) l_j o_j / Σ_j 2^(m_j - M) l_j over the splits j of (query, head).
+// One workgroup per (query, head): the max and the denominator are block
+// reductions over the splits; the weights w_j = 2^(m_j - M) l_j / den go to
+// LDS 256 at a time, and each thread sums two adjacent columns over the splits
+// with independent loads.  An empty split (m = -inf, l = 0) weighs 0.
+constexpr int kMergeThreads = 256;
+
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float u = __shfl_xor(v, o, 64);
+    v = is_max ? fmaxf(v, u) : v + u;
+  }
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();  // red is free
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  v = red[0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) v = is_max ? fmaxf(v, red[w]) : v + red[w];
+  return v;
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void merge_kernel(AttnShape sh, int n_split, const T* __restrict__ part_o,
-                                                    const float* __restrict__ part_ml,
-                                                    float* __restrict__ o_out) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnShape sh, int n_split,
+                                                              const T* __restrict__ part_o,
+                                                              const float* __restrict__ part_ml,
+                                                              float* __restrict__ o_out) {
+  __shared__ float w_lds[kMergeThreads];
+  __shared__ float red[kMergeThreads / 64];
   const int64_t q = blockIdx.x;
   const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const float* ml0 = part_ml + (q * n_split * sh.H + h) * 2;  // split j at ml0 + 2 j H
   float mx = -INFINITY;
-  for (int j = 0; j < n_split; ++j) mx = fmaxf(mx, part_ml[((q * n_split + j) * sh.H + h) * 2]);
+  for (int j = tid; j < n_split; j += kMergeThreads) mx = fmaxf(mx, ml0[2 * static_cast<int64_t>(j) * sh.H]);
+  mx = block_reduce(mx, true, red);
   float den = 0.f;
-  for (int j = 0; j < n_split; ++j) {
-    const float* ml = part_ml + ((q * n_split + j) * sh.H + h) * 2;
-    den += exp2f(ml[0] - mx) * ml[1];
-  }
-  const float inv = 1.f / den;
-  for (int c = threadIdx.x; c < sh.r; c += blockDim.x) {
-    float num = 0.f;
-    for (int j = 0; j < n_split; ++j) {
-      const int64_t pidx = (q * n_split + j) * sh.H + h;
-      num += exp2f(part_ml[pidx * 2] - mx) * part_ml[pidx * 2 + 1] * Elem<T>::load(part_o, pidx * sh.r + c);
+  if (mx != -INFINITY)
+    for (int j = tid; j < n_split; j += kMergeThreads) {
+      const float* ml = ml0 + 2 * static_cast<int64_t>(j) * sh.H;
+      den += exp2f(ml[0] - mx) * ml[1];
     }
-    o_out[(q * sh.H + h) * sh.r + c] = num * inv;
+  den = block_reduce(den, false, red);
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const T* po = part_o + (q * n_split * sh.H + h) * static_cast<int64_t>(sh.r);  // split j at po + j H r
+  const int64_t js = static_cast<int64_t>(sh.H) * sh.r;
+  // every thread runs every barrier: the column and split loops are uniform,
+  // only the loads and stores are guarded (r is even)
+  for (int c0 = 0; c0 < sh.r; c0 += 2 * kMergeThreads) {
+    const int c = c0 + 2 * tid;
+    const bool active = c < sh.r;
+    float a0 = 0.f, a1 = 0.f;
+    for (int j0 = 0; j0 < n_split; j0 += kMergeThreads) {
+      const int jn = min(kMergeThreads, n_split - j0);
+      __syncthreads();  // the previous chunk's weights are consumed
+      if (tid < jn) {
+        const float* ml = ml0 + 2 * static_cast<int64_t>(j0 + tid) * sh.H;
+        w_lds[tid] = inv > 0.f ? exp2f(ml[0] - mx) * ml[1] * inv : 0.f;
+      }
+      __syncthreads();
+      if (!active) continue;
+      const T* p = po + j0 * js + c;
+      int jj = 0;
+      for (; jj + 4 <= jn; jj += 4) {
+        float x[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          x[u][0] = Elem<T>::load(p, (jj + u) * js);
+          x[u][1] = Elem<T>::load(p, (jj + u) * js + 1);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          a0 = fmaf(w_lds[jj + u], x[u][0], a0);
+          a1 = fmaf(w_lds[jj + u], x[u][1], a1);
+        }
+      }
+      for (; jj < jn; ++jj) {
+        a0 = fmaf(w_lds[jj], Elem<T>::load(p, jj * js), a0);
+        a1 = fmaf(w_lds[jj], Elem<T>::load(p, jj * js + 1), a1);
+      }
+    }
+    if (active) {
+      o_out[(q * sh.H + h) * sh.r + c] = a0;
+      o_out[(q * sh.H + h) * sh.r + c + 1] = a1;
+    }
   }
 }
 
@@ -226,10 +290,10 @@ void merge_splits(int dtype, const AttnShape& sh, int64_t n_q, int n_split, cons
   if (n_q <= 0) return;
   const dim3 grid(static_cast<unsigned>(n_q), sh.H);
   if (dtype == kF32)
-    hipLaunchKernelGGL(merge_kernel<float>, grid, dim3(256), 0, s, sh, n_split,
+    hipLaunchKernelGGL(merge_kernel<float>, grid, dim3(kMergeThreads), 0, s, sh, n_split,
                        static_cast<const float*>(part_o), part_ml, o_out);
   else
-    hipLaunchKernelGGL(merge_kernel<bf16_t>, grid, dim3(256), 0, s, sh, n_split,
+    hipLaunchKernelGGL(merge_kernel<bf16_t>, grid, dim3(kMergeThreads), 0, s, sh, n_split,
                        static_cast<const bf16_t*>(part_o), part_ml, o_out);
 }
 
