@@ -8,7 +8,9 @@ import math
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmla_amd.so")
+# MLA_LIBRARY selects another build of the same library (the debug or the
+# host-sanitizer variant of build.py); the release build by default
+LIB_PATH = os.environ.get("MLA_LIBRARY") or os.path.join(PKG, "libmla_amd.so")
 
 MLA_OK, MLA_EINVAL, MLA_ENOTSUP, MLA_EWORKSPACE, MLA_EHIP, MLA_ESCRATCH = 0, -1, -2, -3, -4, -5
 MLA_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # include/mla.h
@@ -56,6 +58,9 @@ SIGNATURES = {
     "mla_decode_split_rows": (_i32, [_PD, _i32, _i32]),
     "mla_decode_partials": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "mla_decode_noalloc": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp]),
+    "mla_check_decode_rows": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i64]),
+    "mla_check_prefill_rows": (ctypes.c_int, [_vp, _i32, _i64, _i32, _i64]),
+    "mla_check_write_rows": (ctypes.c_int, [_vp, _i64, _i64]),
     "mla_query": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "mla_prefill_expanded": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _vp, _vp, _vp, _vp,
                                             _sz, _vp]),

@@ -402,6 +402,10 @@ int mla_write_cache(const mla_dims* dims, const void* x, const void* w_dkv, cons
       !ptr_ok(cache) || !ptr_ok(workspace))
     return MLA_EINVAL;
   if (workspace_bytes < write_ws(dims, n_tokens)) return MLA_EWORKSPACE;
+  if (mla::kDebugChecks) {
+    const int dc = mla::debug_check_write(slots, n_tokens, cache_rows);
+    if (dc != MLA_OK) return dc;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int row_w = row_width(dims);
   float* proj = static_cast<float*>(workspace);
@@ -467,6 +471,10 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_pe, const 
     return MLA_EINVAL;
   DecodePlan p = decode_plan(dims, batch, max_len);
   if (workspace_bytes < p.total()) return MLA_EWORKSPACE;
+  if (mla::kDebugChecks) {
+    const int dc = mla::debug_check_decode(seq_start, seq_len, batch, max_len);
+    if (dc != MLA_OK) return dc;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   AttnShape sh = shape_of(dims);
   char* ws = static_cast<char*>(workspace);
@@ -538,6 +546,10 @@ int mla_decode_partials(const mla_dims* dims, const void* q_lat, const void* q_p
       !ptr_ok(seq_len) || !ptr_ok(part_o) || !ptr_ok(part_ml))
     return MLA_EINVAL;
   const DecodePlan p = decode_plan(dims, batch, max_len, n_split);
+  if (mla::kDebugChecks) {
+    const int dc = mla::debug_check_decode(seq_start, seq_len, batch, max_len);
+    if (dc != MLA_OK) return dc;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   AttnShape sh = shape_of(dims);
   if (p.wide)
@@ -566,6 +578,10 @@ int mla_prefill(const mla_dims* dims, const void* q_lat, const void* q_pe, const
       !ptr_ok(out) || !ptr_ok(workspace))
     return MLA_EINVAL;
   if (workspace_bytes < prefill_ws(dims, n_tokens)) return MLA_EWORKSPACE;
+  if (mla::kDebugChecks) {
+    const int dc = mla::debug_check_prefill(cu_seqlens, batch, n_tokens, max_len);
+    if (dc != MLA_OK) return dc;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   AttnShape sh = shape_of(dims);
   float* o_lat = static_cast<float*>(workspace);
@@ -619,6 +635,10 @@ int mla_prefill_expanded(const mla_dims* dims, const void* q_nope, const void* q
       !ptr_ok(w_uv) || !ptr_ok(out) || !ptr_ok(workspace))
     return MLA_EINVAL;
   if (workspace_bytes < expanded_ws(dims, n_tokens)) return MLA_EWORKSPACE;
+  if (mla::kDebugChecks) {
+    const int dc = mla::debug_check_prefill(cu_seqlens, batch, n_tokens, max_len);
+    if (dc != MLA_OK) return dc;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int H = dims->n_heads;
   const int T = static_cast<int>(n_tokens);
@@ -958,6 +978,10 @@ int mla_v4_write_cache(const mla_v4_dims* dims, const void* x, const void* w_kv,
       !ptr_ok(cache) || !ptr_ok(workspace) || (rope_freqs != nullptr && !ptr_ok(rope_freqs)))
     return MLA_EINVAL;
   if (workspace_bytes < v4_ws(dims, MLA_V4_OP_WRITE_CACHE, 0, n_tokens, 0)) return MLA_EWORKSPACE;
+  if (mla::kDebugChecks) {
+    const int dc = mla::debug_check_write(slots, n_tokens, cache_rows);
+    if (dc != MLA_OK) return dc;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const mla_dims sh = v4_shadow(dims);
   float* proj = static_cast<float*>(workspace);
@@ -1012,6 +1036,10 @@ int mla_v4_decode(const mla_v4_dims* dims, const void* q, const void* cache, con
     return MLA_EINVAL;
   const V4Decode p = v4_decode_plan(dims, batch, max_len);
   if (workspace_bytes < p.part_o + p.part_ml) return MLA_EWORKSPACE;
+  if (mla::kDebugChecks) {
+    const int dc = mla::debug_check_decode(seq_start, seq_len, batch, max_len);
+    if (dc != MLA_OK) return dc;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const AttnShape sh = v4_shape(dims);
   char* base = static_cast<char*>(workspace);
@@ -1049,6 +1077,10 @@ int mla_v4_prefill(const mla_v4_dims* dims, const void* q, const void* cache, co
       !ptr_ok(workspace) || (rope_freqs != nullptr && !ptr_ok(rope_freqs)))
     return MLA_EINVAL;
   if (workspace_bytes < v4_ws(dims, MLA_V4_OP_PREFILL, batch, n_tokens, max_len)) return MLA_EWORKSPACE;
+  if (mla::kDebugChecks) {
+    const int dc = mla::debug_check_prefill(cu_seqlens, batch, n_tokens, max_len);
+    if (dc != MLA_OK) return dc;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const AttnShape sh = v4_shape(dims);
   char* base = static_cast<char*>(workspace);

@@ -98,6 +98,18 @@ void attend_generic(int dtype, const AttnShape& sh, const void* q_lat, const voi
                     const int64_t* cu, int batch, int64_t n_q, int n_split, int split_len,
                     void* part_o, float* part_ml, float* o_out, hipStream_t s);
 int generic_head_block();
+
+// Range checks of the device index arrays on host copies (checks.cpp): no-ops
+// unless the library is built with MLA_DEBUG_CHECKS, where they copy the
+// arrays to the host (synchronising) and return MLA_EINVAL for a bad one.
+#ifdef MLA_DEBUG_CHECKS
+constexpr bool kDebugChecks = true;
+#else
+constexpr bool kDebugChecks = false;
+#endif
+int debug_check_decode(const int64_t* seq_start, const int32_t* seq_len, int32_t batch, int32_t max_len);
+int debug_check_prefill(const int64_t* cu_seqlens, int32_t batch, int64_t n_tokens, int32_t max_len);
+int debug_check_write(const int64_t* slots, int64_t n_tokens, int64_t cache_rows);
 // whether the generic kernel's LDS tile for this shape and element type fits a CU
 bool attend_generic_fits(int dtype, const AttnShape& sh);
 

@@ -111,6 +111,24 @@ typedef struct mla_dims {
 int mla_rope_yarn_table(int32_t d_rope, double theta, double factor, double original_window, double alpha,
                         double beta, double* out);
 
+/* Range checks of the index arrays the device calls read, on HOST copies the
+ * caller provides (the calls themselves never read device contents: a bad
+ * length or slot is undefined behaviour there).  For debugging, and used by a
+ * library built with MLA_DEBUG_CHECKS, whose decode, prefill and cache-write
+ * calls copy these arrays to the host (a synchronising copy) and refuse them
+ * with MLA_EINVAL before any launch.  Pass cache_rows = INT64_MAX when the
+ * cache's size is not known.  Return MLA_OK or MLA_EINVAL; no HIP call.
+ *   mla_check_decode_rows:  for every b: 1 <= seq_len[b] <= max_len, seq_start[b] >= 0,
+ *                           seq_start[b] + seq_len[b] <= cache_rows
+ *   mla_check_prefill_rows: cu_seqlens[0] = 0, non-decreasing, cu_seqlens[batch] = n_tokens,
+ *                           every segment at most max_len rows, n_tokens <= cache_rows
+ *   mla_check_write_rows:   every slot in [0, cache_rows), no slot twice */
+int mla_check_decode_rows(const int64_t* seq_start, const int32_t* seq_len, int32_t batch, int32_t max_len,
+                          int64_t cache_rows);
+int mla_check_prefill_rows(const int64_t* cu_seqlens, int32_t batch, int64_t n_tokens, int32_t max_len,
+                           int64_t cache_rows);
+int mla_check_write_rows(const int64_t* slots, int64_t n_tokens, int64_t cache_rows);
+
 /* Bytes of scratch an operation needs for the given sizes (0 if none).
  * op: mla_op.  batch: sequences (decode/prefill).  n_tokens: tokens in the call.
  * max_len: the largest per-sequence context in the call (decode/prefill).

@@ -256,3 +256,39 @@ def test_yarn_table_and_frequency_pointer():
     with pytest.raises(ValueError):
         import torch
         abi.dims_of(I.CONFIGS["long_prefill_131k"], rope_freqs=torch.zeros(31, dtype=torch.float64))
+
+
+def test_host_range_checks_of_index_arrays():
+    """mla_check_*_rows: the range checks a debug build runs on host copies of the
+    index arrays before a launch (the release calls never read them)."""
+    import numpy as np
+    abi, lib = _lib()
+    OK, BAD = abi.MLA_OK, abi.MLA_EINVAL
+
+    def P(a):
+        return a.ctypes.data_as(ctypes.c_void_p)
+
+    big = (1 << 63) - 1
+    ss, sl = np.array([0, 10, 30], np.int64), np.array([10, 20, 5], np.int32)
+    dec = lib.mla_check_decode_rows
+    assert dec(P(ss), P(sl), 3, 20, 35) == OK
+    assert dec(P(ss), P(sl), 3, 20, big) == OK
+    assert dec(P(ss), P(sl), 3, 19, 35) == BAD                      # a length above max_len
+    assert dec(P(ss), P(sl), 3, 20, 34) == BAD                      # rows past the cache
+    assert dec(P(np.array([0, 10, -1], np.int64)), P(sl), 3, 20, 35) == BAD
+    assert dec(P(ss), P(np.array([10, 0, 5], np.int32)), 3, 20, 35) == BAD  # an empty context
+    assert dec(None, None, 0, 20, 35) == OK and dec(None, None, -1, 20, 35) == BAD
+    pre = lib.mla_check_prefill_rows
+    cu = np.array([0, 5, 5, 12], np.int64)
+    assert pre(P(cu), 3, 12, 7, 12) == OK                            # an empty segment is allowed
+    assert pre(P(cu), 3, 12, 6, 12) == BAD                           # a segment of 7 > max_len
+    assert pre(P(cu), 3, 12, 7, 11) == BAD                           # the rows past the cache
+    assert pre(P(cu), 3, 13, 7, 13) == BAD                           # cu[batch] != n_tokens
+    assert pre(P(np.array([1, 5, 5, 12], np.int64)), 3, 12, 7, 12) == BAD
+    assert pre(P(np.array([0, 6, 5, 12], np.int64)), 3, 12, 7, 12) == BAD  # decreasing
+    wr = lib.mla_check_write_rows
+    assert wr(P(np.array([3, 0, 7], np.int64)), 3, 8) == OK
+    assert wr(P(np.array([3, 8], np.int64)), 2, 8) == BAD
+    assert wr(P(np.array([-1], np.int64)), 1, 8) == BAD
+    assert wr(P(np.array([2, 5, 2], np.int64)), 3, 8) == BAD        # one slot written twice
+    assert wr(None, 0, 8) == OK
