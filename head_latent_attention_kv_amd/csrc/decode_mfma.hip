@@ -11,7 +11,8 @@
 // Workgroup = 8 wave64s.  Per 32-row tile (software-pipelined: the iteration
 // that accumulates tile t also scores tile t+1, one barrier per tile):
 //  1. the tile is copied HBM -> LDS with global_load_lds_dwordx4 (no register
-//     staging), STAGES-2 tiles in flight beyond the two being used;
+//     staging; non-temporal when NHH = 1), STAGES-2 tiles in flight beyond
+//     the two being used;
 //  2. score: wave w (< 2·NHB) computes Sᵀ[16 rows x 16 heads] = C·Qᵀ for head
 //     block w % NHB and row block w / NHB with v_mfma_f32_16x16x32_bf16; C (the
 //     tile) is the A operand read from LDS, fetched a few k-steps ahead; Qᵀ is
@@ -145,7 +146,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
       // rows past the sequence (last tile) or past the tile read the last valid row
       const uint32_t voff = r < valid ? static_cast<uint32_t>(r * (RW * 2) + cb)
                                       : static_cast<uint32_t>((valid - 1) * (RW * 2));
-      global_to_lds16(tbase, voff, __builtin_amdgcn_readfirstlane(dst + j * 1024));
+      // with one workgroup per (sequence, split) each tile is read once: non-temporal copy
+      if constexpr (NHH == 1) global_to_lds16_stream(tbase, voff, __builtin_amdgcn_readfirstlane(dst + j * 1024));
+      else global_to_lds16(tbase, voff, __builtin_amdgcn_readfirstlane(dst + j * 1024));
     }
   };
   // wait until tile t has landed, given that the copies of tiles up to `last_issued` were issued

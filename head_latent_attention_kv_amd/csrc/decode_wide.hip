@@ -17,7 +17,8 @@
 //     between waves through a small LDS buffer.
 // Tiles of 32 rows:
 //   - copies HBM -> LDS by global_load_lds_dwordx4 into 4 buffers (tiles t and
-//     t+1 in use, t+2 and t+3 in flight), issued by waves 0-3 only: a copy's
+//     t+1 in use, t+2 and t+3 in flight) with the non-temporal hint (each
+//     tile is read once), issued by waves 0-3 only: a copy's
 //     issue stalls while the CU's memory pipeline is full, and with one issuing
 //     wave per SIMD the other wave keeps the SIMD's MFMAs busy meanwhile (the
 //     waves w and w + 4 share a SIMD); stored without padding; the 16-byte
@@ -148,13 +149,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
       const int bnd = (r0 + 1) * kRowChunks - j * 64;
       const int k0 = ((r0 >> 1) & 7) << 4, k1 = (((r0 + 1) >> 1) & 7) << 4;
       const uint32_t voff = static_cast<uint32_t>((ln * 16) ^ (ln < bnd ? k0 : k1));
-      global_to_lds16(tbase + j * 1024, voff, __builtin_amdgcn_readfirstlane(dst + j * 1024));
+      global_to_lds16_stream(tbase + j * 1024, voff, __builtin_amdgcn_readfirstlane(dst + j * 1024));
     } else {
       // last tile of the split: rows past it read a chunk of its last valid row
       const int L = j * 64 + ln;
       const int r = (L * 1821) >> 17;  // L / 72 for L < 2304
       const int g = r < valid ? (L ^ ((r >> 1) & 7)) : (valid - 1) * kRowChunks + (L & 63);
-      global_to_lds16(tbase, static_cast<uint32_t>(g * 16), __builtin_amdgcn_readfirstlane(dst + j * 1024));
+      global_to_lds16_stream(tbase, static_cast<uint32_t>(g * 16), __builtin_amdgcn_readfirstlane(dst + j * 1024));
     }
   };
   auto issue_tile = [&](int t) {

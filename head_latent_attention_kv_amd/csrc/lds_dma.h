@@ -30,6 +30,19 @@ __device__ __forceinline__ void global_to_lds16(const void* sbase, uint32_t voff
       : "memory", "m0");
 }
 
+// The same copy with the non-temporal hint (nt), for data that one workgroup
+// reads once per launch and that is far larger than the caches (latent cache
+// tiles, projection weights): the caches then keep what is reused instead.
+__device__ __forceinline__ void global_to_lds16_stream(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  __asm__ __volatile__(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1 nt"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_base)
+      : "memory", "m0");
+}
+
 // Workgroup barrier for LDS traffic only: wait for this wave's LDS operations,
 // then s_barrier.  Unlike __syncthreads() it does not wait for outstanding
 // global loads, so tiles prefetched into other LDS buffers stay in flight.

@@ -352,7 +352,10 @@ __global__ __launch_bounds__(256, 1) void skinny_dma_kernel(SkinnyArgs sa) {
         sbase = reinterpret_cast<const char*>(a_mat + static_cast<int64_t>(m_base) * sa.sAm);
         voff = static_cast<uint32_t>((m - m_base) * sa.sAm + kc) * 2u;
       }
-      global_to_lds16(sbase, voff, __builtin_amdgcn_readfirstlane(dst + o * 1024));
+      // weights are read once per launch (non-temporal copy); the token rows
+      // are read by every workgroup and stay cached
+      if (w_op) global_to_lds16_stream(sbase, voff, __builtin_amdgcn_readfirstlane(dst + o * 1024));
+      else global_to_lds16(sbase, voff, __builtin_amdgcn_readfirstlane(dst + o * 1024));
     }
   };
 
