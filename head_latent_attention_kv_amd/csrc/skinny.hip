@@ -268,17 +268,21 @@ __global__ __launch_bounds__(256, MINB) void skinny_kernel(SkinnyArgs sa) {
 // Per-lane fragment loads read 64 bytes of each of 16 weight rows per
 // instruction, which leaves DRAM pages mostly idle (measured: ~4.9 TB/s at
 // best for that pattern against ~6.2 TB/s for runs of 512 bytes and more).
-// Here a workgroup of four waves owns 96 output columns and copies, per stage
-// of 128 k, the tile's 96 weight rows and the 64 token rows (256-byte runs of
-// each row) HBM/L2 -> LDS with global_load_lds_dwordx4, four stages in flight
-// (160 KB; two stages of 256 k measured slower).  16-byte chunk
-// p of LDS row r holds global chunk p ^ (r & 15), so the 16 rows of one MFMA
-// fragment read fall on distinct banks.  Inside a stage wave w takes k-step w
-// (32 k) for all 64 x 96 outputs; the four partial tiles are summed through LDS
-// at the end.  k past the K piece is read from a clamped address and its A
-// fragments are zeroed.
+// Here a workgroup owns 96 output columns and copies, per stage of 128 k, the
+// tile's 96 weight rows and the 64 token rows (256-byte runs of each row)
+// HBM/L2 -> LDS with global_load_lds_dwordx4, four stages in flight (160 KB;
+// two stages of 256 k measured slower).  16-byte chunk p of LDS row r holds
+// global chunk p ^ (r & 15), so the 16 rows of one MFMA fragment read fall on
+// distinct banks.  Eight waves, two per SIMD: waves 4-7 issue every copy and
+// compute nothing, so the stalls of a copy's issue (the CU's memory pipeline
+// is full most of the time) never hold up the matrix work; inside a stage
+// compute wave w < 4 takes k-step w (32 k) for all 64 x 96 outputs, and the four
+// partial tiles are summed through LDS at the end.  k past the K piece is read
+// from a clamped address and its A fragments are zeroed.
 constexpr int kDmaCols = 96;                         // 6 column blocks
 constexpr int kDmaNB = kDmaCols / 16;
+constexpr int kDmaWaves = 8;                         // 4 compute + 4 copy waves
+constexpr int kDmaThreads = 64 * kDmaWaves;
 constexpr int kDmaLdsMax = 160 * 1024;
 
 // stage geometry for KC k per stage (KC = 128: four stages; 256: two)
@@ -300,12 +304,13 @@ struct DmaStage {
 };
 
 template <int MB, int KC, typename OutT>
-__global__ __launch_bounds__(256, 1) void skinny_dma_kernel(SkinnyArgs sa) {
+__global__ __launch_bounds__(kDmaThreads, 1) void skinny_dma_kernel(SkinnyArgs sa) {
   using G = DmaStage<KC>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
+  const bool copy_wave = wave >= 4;  // waves w and w + 4 share a SIMD
   const int n0 = blockIdx.x * kDmaCols;
   const int z = blockIdx.y;
   const int split = blockIdx.z;
@@ -320,8 +325,9 @@ __global__ __launch_bounds__(256, 1) void skinny_dma_kernel(SkinnyArgs sa) {
   // weight tile (o < kWOps, o' = o) or of the token rows (o' = o - kWOps); the
   // lanes of row R·o'+q fill its LDS chunks p in order.  The rows of a weight
   // copy come from one matrix (B0 rows [0, N0), B1 the rest; N0 is a multiple
-  // of 4 and of R).
+  // of 4 and of R).  Copy wave 4 + c issues copies o = c + 4i.
   auto issue = [&](int st) {
+    if (!copy_wave) return;
     const int kb = k_lo + st * KC;
     const uint32_t dst = lds0 + (st % G::kStages) * G::kBytes;
     int ln = lane;
@@ -330,7 +336,7 @@ __global__ __launch_bounds__(256, 1) void skinny_dma_kernel(SkinnyArgs sa) {
     const int q = ln / kLanesPerRow, p = ln % kLanesPerRow;
 #pragma unroll
     for (int i = 0; i < G::kOpsPerWave; ++i) {
-      const int o = wave + 4 * i;
+      const int o = (wave - 4) + 4 * i;
       const bool w_op = o < G::kWOps;
       const int o2 = w_op ? o : o - G::kWOps;
       const int key = (o2 * G::kRowsPerOp + q) & 15;
@@ -373,16 +379,19 @@ __global__ __launch_bounds__(256, 1) void skinny_dma_kernel(SkinnyArgs sa) {
   int issued = min(G::kStages - 1, n_st) - 1;
 
   for (int st = 0; st < n_st; ++st) {
-    switch (issued - st) {
-      case 0: wait_vmcnt<0>(); break;
-      case 1: wait_vmcnt<G::kOpsPerWave>(); break;
-      default: wait_vmcnt<2 * G::kOpsPerWave>(); break;
+    if (copy_wave) {
+      switch (issued - st) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<G::kOpsPerWave>(); break;
+        default: wait_vmcnt<2 * G::kOpsPerWave>(); break;
+      }
     }
     lds_barrier();  // stage st visible; stage st-1 read everywhere: its buffer is free
     if (st + G::kStages - 1 < n_st) {
       issue(st + G::kStages - 1);
       issued = st + G::kStages - 1;
     }
+    if (copy_wave) continue;
     const unsigned char* sb = smem + (st % G::kStages) * G::kBytes;
 #pragma unroll
     for (int q = 0; q < G::kStepsPerWave; ++q) {
@@ -406,11 +415,12 @@ __global__ __launch_bounds__(256, 1) void skinny_dma_kernel(SkinnyArgs sa) {
     }
   }
 
-  // sum the four waves' tiles: each wave writes its partial tile, then sums a
-  // quarter of the tile over the four copies and stores it
+  // sum the four compute waves' tiles: each writes its partial tile, then every
+  // wave sums an eighth of the tile over the four copies and stores it
   lds_barrier();  // every stage read; no copy in flight
-  float* red = reinterpret_cast<float*>(smem);  // [4 waves][MB * kDmaNB][4][64]
+  float* red = reinterpret_cast<float*>(smem);  // [4 compute waves][MB * kDmaNB][4][64]
   constexpr int kTile = MB * kDmaNB * 4 * 64;
+  if (!copy_wave)
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -419,10 +429,10 @@ __global__ __launch_bounds__(256, 1) void skinny_dma_kernel(SkinnyArgs sa) {
       for (int e = 0; e < 4; ++e) red[wave * kTile + ((i * kDmaNB + j) * 4 + e) * 64 + lane] = acc[i][j][e];
   lds_barrier();
   OutT* C = static_cast<OutT*>(sa.C) + static_cast<int64_t>(split) * sa.sPs + static_cast<int64_t>(z) * sa.sCz;
-  // blocks (i, j) = b handled by wave b % 4; lane holds C[m = 16i + 4lg + e][n = n0 + 16j + l16]
+  // blocks (i, j) = b handled by wave b % 8; lane holds C[m = 16i + 4lg + e][n = n0 + 16j + l16]
 #pragma unroll
   for (int b = 0; b < MB * kDmaNB; ++b) {
-    if (b % 4 != wave) continue;
+    if (b % kDmaWaves != wave) continue;
     const int i = b / kDmaNB, j = b % kDmaNB;
     const int n = n0 + 16 * j + l16;
 #pragma unroll
@@ -740,11 +750,11 @@ void launch_dma(const SkinnyArgs& sa, bool out_bf16, hipStream_t s) {
   if (out_bf16) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_dma_kernel<MB, KC, bf16_t>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    hipLaunchKernelGGL((skinny_dma_kernel<MB, KC, bf16_t>), grid, dim3(256), lds, s, sa);
+    hipLaunchKernelGGL((skinny_dma_kernel<MB, KC, bf16_t>), grid, dim3(kDmaThreads), lds, s, sa);
   } else {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_dma_kernel<MB, KC, float>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    hipLaunchKernelGGL((skinny_dma_kernel<MB, KC, float>), grid, dim3(256), lds, s, sa);
+    hipLaunchKernelGGL((skinny_dma_kernel<MB, KC, float>), grid, dim3(kDmaThreads), lds, s, sa);
   }
 }
 
