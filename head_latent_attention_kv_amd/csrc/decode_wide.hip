@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    const int valid = min(kTL, l_end - (l_begin + tt * kTL));  // <= 0 past the last tile
+    const int valid = min(kTL, l_end - (l_begin + tt * kTL));  // < kTL only in the last tile
     if (valid < kTL) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
@@ -345,8 +345,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
       }
     }
 
-    // iteration t: scores of tile t+1 (masked to nothing past the last tile),
-    // their softmax into exchange buffer (t+1) % 2, then the PV of tile t
+    // iteration t: scores of tile t+1, their softmax into exchange buffer
+    // (t+1) % 2, then the PV of tile t
     for (int t = 0; t < n_tiles; ++t) {
       if (t + 1 < n_tiles) wait_tile(t + 1, issued);
       // tile t+1 and the P of tile t visible; PV(t-1) done everywhere: ring
@@ -356,14 +356,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_wide_kernel(
         issue_tile(t + kStages - 1);
         issued = t + kStages - 1;
       }
+      // the last iteration has no next tile: PV only
+      const bool next = t + 1 < n_tiles;
       f32x4 s_next[2];
-      score(t + 1, s_next);
+      if (next) score(t + 1, s_next);
       if constexpr (kScan) {
-        m_lane = fmaxf(m_lane, tile_max(s_next));
+        if (next) m_lane = fmaxf(m_lane, tile_max(s_next));
       } else {
         bf16x8 cf[kCB], pf[2];
         pv_load(t, cf, pf);
-        softmax(s_next, smem + kPOff + ((t + 1) & 1) * kPBytes);
+        if (next) softmax(s_next, smem + kPOff + ((t + 1) & 1) * kPBytes);
         pv_mma(t, cf, pf);
       }
     }
