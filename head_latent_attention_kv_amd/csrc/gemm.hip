@@ -178,6 +178,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma(GemmArgs g) {
     }
 }
 
+// Row n of the fp32 B[z][n][k] operand, from B or (columns n >= N0) from B1.
+__device__ __forceinline__ const float* f32_b_row(const GemmArgs& g, int z, int n) {
+  const bool second = g.B1 != nullptr && n >= g.N0;
+  const float* base = static_cast<const float*>(second ? g.B1 : g.B) + static_cast<int64_t>(z) * g.sBz;
+  return base + static_cast<int64_t>(second ? n - g.N0 : n) * g.sBo;
+}
+
 // fp32 VALU GEMM: 16x16 outputs per 256-thread block, k staged by 16.
 template <bool B_KN>
 __global__ __launch_bounds__(256) void gemm_f32_valu(GemmArgs g) {
@@ -195,7 +202,7 @@ __global__ __launch_bounds__(256) void gemm_f32_valu(GemmArgs g) {
     int bn = blockIdx.x * 16 + ty, bk = k0 + tx;
     float bv = 0.f;
     if (bn < g.N && bk < g.K)
-      bv = B_KN ? B[static_cast<int64_t>(bk) * g.sBo + bn] : B[static_cast<int64_t>(bn) * g.sBo + bk];
+      bv = B_KN ? B[static_cast<int64_t>(bk) * g.sBo + bn] : f32_b_row(g, z, bn)[bk];
     sB[ty][tx] = bv;
     __syncthreads();
 #pragma unroll
@@ -204,6 +211,68 @@ __global__ __launch_bounds__(256) void gemm_f32_valu(GemmArgs g) {
   }
   if (m < g.M && n < g.N)
     static_cast<float*>(g.C)[static_cast<int64_t>(z) * g.sCz + static_cast<int64_t>(m) * g.sCm + n] = acc;
+}
+
+// fp32 product of a few rows (M <= kSmallM): one launch of latency, no k
+// staging.  B [n][k]: each wave computes four output columns for all rows, its
+// lanes striding k (coalesced rows of A and B), then a shuffle sum per output.
+// B [k][n]: each thread computes one column over k, the wave's loads of a B row
+// coalesced.
+constexpr int kSmallM = 4;
+
+template <bool B_KN>
+__global__ __launch_bounds__(256) void gemm_f32_small(GemmArgs g) {
+  const int z = blockIdx.z;
+  const float* A = static_cast<const float*>(g.A) + static_cast<int64_t>(z) * g.sAz;
+  float* C = static_cast<float*>(g.C) + static_cast<int64_t>(z) * g.sCz;
+  if constexpr (!B_KN) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nb = (blockIdx.x * 4 + wave) * 4;  // the wave's first column
+    const float* brow[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) brow[c] = f32_b_row(g, z, min(nb + c, g.N - 1));
+    float acc[4][kSmallM];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int m = 0; m < kSmallM; ++m) acc[c][m] = 0.f;
+    for (int k = lane; k < g.K; k += 64) {
+      float a[kSmallM];
+#pragma unroll
+      for (int m = 0; m < kSmallM; ++m) a[m] = m < g.M ? A[static_cast<int64_t>(m) * g.sAm + k] : 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float w = brow[c][k];
+#pragma unroll
+        for (int m = 0; m < kSmallM; ++m) acc[c][m] = fmaf(a[m], w, acc[c][m]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int m = 0; m < kSmallM; ++m) {
+        float v = acc[c][m];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+        if (lane == 0 && m < g.M && nb + c < g.N) C[static_cast<int64_t>(m) * g.sCm + nb + c] = v;
+      }
+  } else {
+    const int n = blockIdx.x * 256 + threadIdx.x;
+    if (n >= g.N) return;
+    const float* B = static_cast<const float*>(g.B) + static_cast<int64_t>(z) * g.sBz;
+    float acc[kSmallM];
+#pragma unroll
+    for (int m = 0; m < kSmallM; ++m) acc[m] = 0.f;
+    for (int k = 0; k < g.K; ++k) {
+      const float b = B[static_cast<int64_t>(k) * g.sBo + n];
+#pragma unroll
+      for (int m = 0; m < kSmallM; ++m)
+        if (m < g.M) acc[m] = fmaf(A[static_cast<int64_t>(m) * g.sAm + k], b, acc[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < kSmallM; ++m)
+      if (m < g.M) C[static_cast<int64_t>(m) * g.sCm + n] = acc[m];
+  }
 }
 
 // ---- few-token product with an n-contiguous weight (q_lat = q_nope · W_UK) ----
@@ -409,6 +478,12 @@ void gemm_f16_out(const GemmArgs& g, hipStream_t s) {
 void gemm(const GemmArgs& g, int dtype, bool a_f32, bool b_kn, bool out_bf16, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.Z <= 0) return;
   if (dtype == kF32) {
+    if (g.M <= kSmallM) {
+      const dim3 grid(b_kn ? (g.N + 255) / 256 : (g.N + 15) / 16, 1, g.Z);
+      if (b_kn) hipLaunchKernelGGL(gemm_f32_small<true>, grid, dim3(256), 0, s, g);
+      else hipLaunchKernelGGL(gemm_f32_small<false>, grid, dim3(256), 0, s, g);
+      return;
+    }
     dim3 grid((g.N + 15) / 16, (g.M + 15) / 16, g.Z);
     if (b_kn) hipLaunchKernelGGL(gemm_f32_valu<true>, grid, dim3(256), 0, s, g);
     else hipLaunchKernelGGL(gemm_f32_valu<false>, grid, dim3(256), 0, s, g);

@@ -79,9 +79,9 @@ struct DecodePlan {
   size_t total() const { return part_o_bytes + part_ml_bytes + o_bytes; }
 };
 
-int split_rows(int L, int64_t ns) {
+int split_rows(int L, int64_t ns, int unit = 64) {
   int split_len = static_cast<int>((L + ns - 1) / ns);
-  return (split_len + 63) / 64 * 64;
+  return (split_len + unit - 1) / unit * unit;
 }
 
 DecodePlan decode_plan(const mla_dims* d, int32_t batch, int32_t max_len, int32_t force_splits = 0) {
@@ -104,13 +104,17 @@ DecodePlan decode_plan(const mla_dims* d, int32_t batch, int32_t max_len, int32_
                : B * ((sh.H + mla::generic_head_block() - 1) / mla::generic_head_block());
   // Fill the 256 compute units of an MI355X once (the MFMA kernel's LDS
   // footprint allows one workgroup per CU at the large shapes), keeping
-  // splits >= 256 rows.
+  // splits >= 256 rows (multiples of 64) for the MFMA kernels and >= 32 rows
+  // (one tile) for the generic one, whose workgroups walk their rows serially:
+  // a short context with few head blocks (the fp32 layer) would otherwise run
+  // as a single workgroup.
+  const bool generic = !p.wide && !p.mfma;
   const int64_t target =
       p.wide ? kCUs : p.mfma ? mla::decode_mfma_blocks_per_cu(sh) * kCUs : 2 * kCUs;
   int64_t ns = per_split > 0 ? (target + per_split - 1) / per_split : 1;
-  const int64_t max_ns = std::max<int64_t>(1, L / 256);
+  const int64_t max_ns = std::max<int64_t>(1, L / (generic ? 32 : 256));
   ns = std::max<int64_t>(1, std::min<int64_t>(ns, max_ns));
-  const int split_len = split_rows(L, ns);
+  const int split_len = split_rows(L, ns, generic ? 32 : 64);
   ns = (L + split_len - 1) / split_len;
   p.n_split = static_cast<int>(ns);
   p.split_len = split_len;
@@ -231,6 +235,12 @@ Proj proj_two(const mla_dims* d, const void* x, const void* w0, int n0, const vo
     sa.Z = 1;
     sa.splits = p.splits;
     mla::gemm_skinny(sa, /*a_f32=*/false, /*out_bf16=*/false, s);
+  } else if (d->dtype == MLA_F32) {
+    // the fp32 GEMM takes both weights in one launch
+    GemmArgs g = proj_args(d, x, w0, n0 + n1, c, ldc, n_tokens);
+    g.B1 = w1;
+    g.N0 = n0;
+    mla::gemm(g, d->dtype, false, false, false, s);
   } else {
     mla::gemm(proj_args(d, x, w0, n0, c, ldc, n_tokens), d->dtype, false, false, false, s);
     mla::gemm(proj_args(d, x, w1, n1, c + n0, ldc, n_tokens), d->dtype, false, false, false, s);

@@ -19,6 +19,10 @@ struct GemmArgs {
   void* C;
   int64_t sCz, sCm;  // C[z][m][n]: n contiguous
   int M, N, K, Z;
+  // fp32 path with B[z][n][k] only: columns n >= N0 come from row n - N0 of B1
+  // (two projections of one input in one launch); B1 null: every column from B
+  const void* B1;
+  int N0;
 };
 
 // dtype == kF32: fp32 in/out VALU path.  dtype == kBF16: A bf16 (or fp32 if a_f32),
