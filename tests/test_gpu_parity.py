@@ -85,6 +85,8 @@ DECODE_CASES = [
     ("qwen25_7b_decode", [1, 65, 511, 1000]),
     ("deepseek_v2_decode", [1, 300, 2048]),
     ("qwen3_30b_ragged_decode", [1024, 1537]),
+    # the generic kernel's plan: one-tile splits, splits past a short sequence empty
+    ("tiny_f32", [1, 31, 32, 33, 65, 300]),
 ]
 
 
