@@ -269,9 +269,9 @@ __global__ __launch_bounds__(256, MINB) void skinny_kernel(SkinnyArgs sa) {
 // instruction, which leaves DRAM pages mostly idle (measured: ~4.9 TB/s at
 // best for that pattern against ~6.2 TB/s for runs of 512 bytes and more).
 // Here a workgroup owns 96 output columns and copies, per stage of 128 k, the
-// tile's 96 weight rows and the 64 token rows (256-byte runs of each row)
-// HBM/L2 -> LDS with global_load_lds_dwordx4, four stages in flight (160 KB;
-// two stages of 256 k measured slower).  16-byte chunk p of LDS row r holds
+// tile's 96 weight rows and its 16·MB token rows (256-byte runs of each row)
+// HBM/L2 -> LDS with global_load_lds_dwordx4: four stages in flight at 64 token
+// rows, five at 16 or 32 (160 KB; two stages of 256 k measured slower).  16-byte chunk p of LDS row r holds
 // global chunk p ^ (r & 15), so the 16 rows of one MFMA fragment read fall on
 // distinct banks.  Eight waves, two per SIMD: waves 4-7 issue every copy and
 // compute nothing, so the stalls of a copy's issue (the CU's memory pipeline
@@ -285,13 +285,14 @@ constexpr int kDmaWaves = 8;                         // 4 compute + 4 copy waves
 constexpr int kDmaThreads = 64 * kDmaWaves;
 constexpr int kDmaLdsMax = 160 * 1024;
 
-// stage geometry for KC k per stage (KC = 128: four stages; 256: two)
-template <int KC>
+// stage geometry for KC k per stage and AR staged token rows (16 per row block
+// of the MFMA tile; KC = 128: four stages at 64 rows, five at 16 or 32)
+template <int KC, int AR>
 struct DmaStage {
   static constexpr int kRun = KC * 2;                    // bytes of a row per stage
   static constexpr int kRowsPerOp = 1024 / kRun;         // rows per 1 KB copy
   static constexpr int kWOps = kDmaCols * kRun / 1024;   // weight copies per stage
-  static constexpr int kAOps = 64 * kRun / 1024;         // token-row copies per stage
+  static constexpr int kAOps = AR * kRun / 1024;         // token-row copies per stage
   static constexpr int kOps = kWOps + kAOps;
   static constexpr int kOpsPerWave = kOps / 4;
   static constexpr int kBytes = kOps * 1024;
@@ -299,13 +300,13 @@ struct DmaStage {
   static constexpr int kLds = kStages * kBytes;
   static constexpr int kStepsPerWave = KC / 4 / kKS;     // k-steps of one wave per stage
   static_assert(kOps % 4 == 0, "copies split evenly over the waves");
-  static_assert(kOpsPerWave * (kStages - 1) < 64, "vmcnt range");
+  static_assert(kOpsPerWave * (kStages - 1) < 64 && kStages <= 5, "vmcnt range");
   static_assert(kStepsPerWave >= 1 && kRun / 16 <= 16 * 2, "swizzle covers a row's chunks");
 };
 
 template <int MB, int KC, typename OutT>
 __global__ __launch_bounds__(kDmaThreads, 1) void skinny_dma_kernel(SkinnyArgs sa) {
-  using G = DmaStage<KC>;
+  using G = DmaStage<KC, 16 * MB>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -380,10 +381,11 @@ __global__ __launch_bounds__(kDmaThreads, 1) void skinny_dma_kernel(SkinnyArgs s
 
   for (int st = 0; st < n_st; ++st) {
     if (copy_wave) {
-      switch (issued - st) {
+      switch (issued - st) {  // stages issued after st
         case 0: wait_vmcnt<0>(); break;
         case 1: wait_vmcnt<G::kOpsPerWave>(); break;
-        default: wait_vmcnt<2 * G::kOpsPerWave>(); break;
+        case 2: wait_vmcnt<2 * G::kOpsPerWave>(); break;
+        default: wait_vmcnt<3 * G::kOpsPerWave>(); break;
       }
     }
     lds_barrier();  // stage st visible; stage st-1 read everywhere: its buffer is free
@@ -420,6 +422,7 @@ __global__ __launch_bounds__(kDmaThreads, 1) void skinny_dma_kernel(SkinnyArgs s
   lds_barrier();  // every stage read; no copy in flight
   float* red = reinterpret_cast<float*>(smem);  // [4 compute waves][MB * kDmaNB][4][64]
   constexpr int kTile = MB * kDmaNB * 4 * 64;
+  static_assert(4 * kTile * 4 <= G::kLds, "reduction buffer inside the ring");
   if (!copy_wave)
 #pragma unroll
   for (int i = 0; i < MB; ++i)
@@ -444,8 +447,6 @@ __global__ __launch_bounds__(kDmaThreads, 1) void skinny_dma_kernel(SkinnyArgs s
     }
   }
 }
-static_assert(4 * 4 * kDmaNB * 4 * 64 * 4 <= DmaStage<256>::kLds && 4 * 4 * kDmaNB * 4 * 64 * 4 <= DmaStage<128>::kLds,
-              "reduction buffer inside the ring");
 
 // ---- split merge + W_UV, DMA-staged (32 token rows per workgroup, 128 columns) ----
 // out[m][z][:] = W_UV[z] · Σ_j w[m][j] A_j[m][z][:], with A_j the bf16 split
@@ -674,12 +675,12 @@ namespace {
 //  else   = 64 columns, two per CU (up to 32 token rows).
 enum class Bf16Variant { kWide, kNarrow, kBase };
 Bf16Variant bf16_variant(int M, int N, int Z, int K) {
-  if (M <= 32) return Bf16Variant::kBase;
   // wide (96-column) tiles when they, or they times the K splits a long K allows,
   // fill the chip: a 5120-column output of K = 16384 runs 54 tiles x 5 splits
   const int tiles = (N + 16 * kWideNB - 1) / (16 * kWideNB) * Z;
   const int max_splits = std::max(1, std::min(16, K / 256));
-  return tiles >= 128 || tiles * max_splits >= 256 ? Bf16Variant::kWide : Bf16Variant::kNarrow;
+  if (tiles >= 128 || tiles * max_splits >= 256) return Bf16Variant::kWide;
+  return M <= 32 ? Bf16Variant::kBase : Bf16Variant::kNarrow;
 }
 }  // namespace
 
@@ -746,7 +747,7 @@ void launch_out(const SkinnyArgs& sa, bool out_bf16, hipStream_t s) {
 template <int MB, int KC = 128>
 void launch_dma(const SkinnyArgs& sa, bool out_bf16, hipStream_t s) {
   dim3 grid((sa.N + kDmaCols - 1) / kDmaCols, sa.Z, sa.splits);
-  constexpr int lds = DmaStage<KC>::kLds;
+  constexpr int lds = DmaStage<KC, 16 * MB>::kLds;
   if (out_bf16) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_dma_kernel<MB, KC, bf16_t>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -762,13 +763,10 @@ template <int MB>
 void launch_kind(const SkinnyArgs& sa, int kind, int ns, bool out_bf16, hipStream_t s) {
   if (kind == kABf16) {
     const Bf16Variant v = bf16_variant(sa.M, sa.N, sa.Z, sa.K);
-    if constexpr (MB >= 3) {
-      if (v == Bf16Variant::kWide && sa.N0 % 4 == 0) launch_dma<MB>(sa, out_bf16, s);
-      else if (v == Bf16Variant::kWide) launch_out<MB, kWideNB, kABf16, 1, 3, 1>(sa, out_bf16, s);
-      else launch_out<MB, 2, kABf16, 1, 4, 2>(sa, out_bf16, s);
-    } else {
-      launch_out<MB, 4, kABf16, 1, 3, 2>(sa, out_bf16, s);
-    }
+    if (v == Bf16Variant::kWide && sa.N0 % 4 == 0) launch_dma<MB>(sa, out_bf16, s);
+    else if (v == Bf16Variant::kWide) launch_out<MB, kWideNB, kABf16, 1, 3, 1>(sa, out_bf16, s);
+    else if constexpr (MB >= 3) launch_out<MB, 2, kABf16, 1, 4, 2>(sa, out_bf16, s);  // narrow (M > 32)
+    else launch_out<MB, 4, kABf16, 1, 3, 2>(sa, out_bf16, s);                         // base (M <= 32)
   } else if (kind == kAF32 || ns <= 1) {
     launch_out<MB, 4, kAF32, 1, 2, 1>(sa, out_bf16, s);
   } else {
