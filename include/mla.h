@@ -25,6 +25,9 @@
  *    device; the caller allocates and owns every buffer, including workspaces.
  *    The library allocates nothing, frees nothing and never synchronises: all
  *    work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *    (A library built with MLA_DEBUG_CHECKS synchronises to copy index arrays
+ *    to the host; mla_decode_noalloc's static scratch array is the one piece of
+ *    device memory the library itself holds.)
  *  - Tensors are dense row-major.  Element type of x, weights, cache, q_lat,
  *    q_pe and out is dims->dtype (MLA_F32 or MLA_BF16); positions are int32,
  *    cache slots / sequence starts are int64, lengths are int32.
