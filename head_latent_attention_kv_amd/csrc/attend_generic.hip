@@ -160,7 +160,10 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(
 // One workgroup per (query, head): the max and the denominator are block
 // reductions over the splits; the weights w_j = 2^(m_j - M) l_j / den go to
 // LDS 256 at a time, and each thread sums two adjacent columns over the splits
-// with independent loads.  An empty split (m = -inf, l = 0) weighs 0.
+// with independent loads.  An empty split (m = -inf, l = 0) weighs 0.  The
+// splits of query q are the partial-state items q·n_split .. q·n_split +
+// n_split - 1, or, with ragged_items > 0, the items the device plan over
+// seq_len gives q (each wave recomputes that plan, as the attention kernel did).
 constexpr int kMergeThreads = 256;
 
 __device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
@@ -183,13 +186,21 @@ template <typename T>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnShape sh, int n_split,
                                                               const T* __restrict__ part_o,
                                                               const float* __restrict__ part_ml,
-                                                              float* __restrict__ o_out) {
+                                                              float* __restrict__ o_out,
+                                                              const int32_t* __restrict__ seq_len,
+                                                              int ragged_items) {
   __shared__ float w_lds[kMergeThreads];
   __shared__ float red[kMergeThreads / 64];
   const int64_t q = blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
-  const float* ml0 = part_ml + (q * n_split * sh.H + h) * 2;  // split j at ml0 + 2 j H
+  int64_t first = q * n_split;  // first partial-state item of query q
+  if (ragged_items > 0) {
+    const RaggedLane rl = ragged_plan(seq_len, static_cast<int>(gridDim.x), ragged_items);
+    first = __builtin_amdgcn_readfirstlane(__shfl(rl.first, static_cast<int>(q), kWave));
+    n_split = __builtin_amdgcn_readfirstlane(__shfl(rl.count, static_cast<int>(q), kWave));
+  }
+  const float* ml0 = part_ml + (first * sh.H + h) * 2;  // split j at ml0 + 2 j H
   float mx = -INFINITY;
   for (int j = tid; j < n_split; j += kMergeThreads) mx = fmaxf(mx, ml0[2 * static_cast<int64_t>(j) * sh.H]);
   mx = block_reduce(mx, true, red);
@@ -201,7 +212,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnShape sh, int 
     }
   den = block_reduce(den, false, red);
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  const T* po = part_o + (q * n_split * sh.H + h) * static_cast<int64_t>(sh.r);  // split j at po + j H r
+  const T* po = part_o + (first * sh.H + h) * static_cast<int64_t>(sh.r);  // split j at po + j H r
   const int64_t js = static_cast<int64_t>(sh.H) * sh.r;
   // every thread runs every barrier: the column and split loops are uniform,
   // only the loads and stores are guarded (r is even)
@@ -286,15 +297,15 @@ void attend_generic(int dtype, const AttnShape& sh, const void* q_lat, const voi
 }
 
 void merge_splits(int dtype, const AttnShape& sh, int64_t n_q, int n_split, const void* part_o,
-                  const float* part_ml, float* o_out, hipStream_t s) {
+                  const float* part_ml, float* o_out, hipStream_t s, const int32_t* seq_len, int ragged_items) {
   if (n_q <= 0) return;
   const dim3 grid(static_cast<unsigned>(n_q), sh.H);
   if (dtype == kF32)
     hipLaunchKernelGGL(merge_kernel<float>, grid, dim3(kMergeThreads), 0, s, sh, n_split,
-                       static_cast<const float*>(part_o), part_ml, o_out);
+                       static_cast<const float*>(part_o), part_ml, o_out, seq_len, ragged_items);
   else
     hipLaunchKernelGGL(merge_kernel<bf16_t>, grid, dim3(kMergeThreads), 0, s, sh, n_split,
-                       static_cast<const bf16_t*>(part_o), part_ml, o_out);
+                       static_cast<const bf16_t*>(part_o), part_ml, o_out, seq_len, ragged_items);
 }
 
 }  // namespace mla

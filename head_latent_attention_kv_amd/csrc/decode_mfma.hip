@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
     const int32_t* __restrict__ seq_len, int batch, int H, int G, int d_rope, float scale,
     int n_split, int split_len, bf16_t* __restrict__ part_o, float* __restrict__ part_ml,
     float* __restrict__ o_out, bf16_t* __restrict__ v4_out, const float* __restrict__ sink,
-    double rope_base, const double* __restrict__ freqs, int tail) {
+    double rope_base, const double* __restrict__ freqs, int tail, int ragged_items) {
   using S = Shape<R, RW, NHB, NHH, STAGES>;
   constexpr int kBufBytes = S::kBufBytes;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -112,9 +112,35 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
     hh = rem / 8;
     pair = q * 8 + rem % 8;
   }
-  if (pair >= batch * n_split) return;
-  const int split = pair % n_split;
-  const int b = pair / n_split;
+  int split, b, len;
+  int64_t slot;  // index of this (sequence, split) in the partial states
+  int64_t row0;
+  if (ragged_items > 0) {
+    // plan made here from the lengths (NHH = 1): workgroup i takes item i;
+    // every wave finds the same item, and a workgroup without one leaves.
+    // Lane k loads sequence k's start beside its length, so neither waits on
+    // the plan.
+    const int64_t start_lane = (threadIdx.x & (kWave - 1)) < batch ? seq_start[threadIdx.x & (kWave - 1)] : 0;
+    const RaggedLane rl = ragged_plan(seq_len, batch, ragged_items);
+    const int item = blockIdx.x;
+    const bool mine = (threadIdx.x & (kWave - 1)) < batch && item >= rl.first && item < rl.first + rl.count;
+    const uint64_t owner = __ballot(mine);
+    if (owner == 0) return;
+    // uniform values, kept in scalar registers
+    b = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<unsigned long long>(owner)) - 1);
+    split = __builtin_amdgcn_readfirstlane(item - __shfl(rl.first, b, kWave));
+    split_len = __builtin_amdgcn_readfirstlane(rl.split_len);
+    len = __builtin_amdgcn_readfirstlane(__shfl(rl.len, b, kWave));
+    row0 = uniform_i64(__shfl(static_cast<long long>(start_lane), b, kWave));
+    slot = item;
+  } else {
+    if (pair >= batch * n_split) return;
+    split = pair % n_split;
+    b = pair / n_split;
+    slot = static_cast<int64_t>(b) * n_split + split;
+    row0 = seq_start[b];
+    len = seq_len[b];
+  }
   const int head0 = hh * S::kHeads;
 
   const int tid = threadIdx.x;
@@ -122,8 +148,6 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
 
-  const int64_t row0 = seq_start[b];
-  const int len = seq_len[b];
   const int l_begin = split * split_len;
   const int l_end = min(len, l_begin + split_len);
   const int n_tiles = l_end > l_begin ? (l_end - l_begin + kTL - 1) / kTL : 0;
@@ -420,7 +444,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
   }
   const bool partials = part_o != nullptr;
   if (unit && mb_s == 0 && lg == 0 && partials && head < H) {
-    const int64_t pidx = (static_cast<int64_t>(b) * n_split + split) * H + head;
+    const int64_t pidx = slot * H + head;
     part_ml[pidx * 2 + 0] = m_ref;
     part_ml[pidx * 2 + 1] = xch[hloc] + xch[S::kHeads + hloc];
   }
@@ -438,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
 #pragma unroll
         for (int nb = 0; nb < S::kNB; ++nb) dst[nb * 16] = o[hb][nb][i] * inv;
       } else {
-        bf16_t* dst = part_o + ((static_cast<int64_t>(b) * n_split + split) * H + h) * R + c0 + l16;
+        bf16_t* dst = part_o + (slot * H + h) * R + c0 + l16;
 #pragma unroll
         for (int nb = 0; nb < S::kNB; ++nb) dst[nb * 16] = f32_to_bf16(o[hb][nb][i] * inv);
       }
@@ -448,20 +472,20 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
 template <int R, int RW, int NHB, int NHH, int STAGES>
 void launch(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
             const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split, int split_len,
-            void* part_o, float* part_ml, float* o_out, const V4Epilogue* v4, hipStream_t s) {
+            void* part_o, float* part_ml, float* o_out, const V4Epilogue* v4, hipStream_t s, int ragged_items) {
   using S = Shape<R, RW, NHB, NHH, STAGES>;
   auto kern = decode_mfma_kernel<R, RW, NHB, NHH, STAGES>;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                       S::kLdsBytes);
   const int pairs = batch * n_split;
-  const int grid = NHH == 1 ? pairs : (pairs + 7) / 8 * 8 * NHH;
+  const int grid = ragged_items > 0 ? ragged_items : NHH == 1 ? pairs : (pairs + 7) / 8 * 8 * NHH;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), S::kLdsBytes, s,
                      static_cast<const bf16_t*>(q_lat), static_cast<const bf16_t*>(q_pe),
                      static_cast<const bf16_t*>(cache), seq_start, seq_len, batch, sh.H, sh.G,
                      sh.d_rope, sh.scale, n_split, split_len, static_cast<bf16_t*>(part_o), part_ml,
                      o_out, v4 ? static_cast<bf16_t*>(v4->out) : nullptr, v4 ? v4->sink : nullptr,
                      v4 ? std::pow(v4->theta, -2.0 / v4->d_rope) : 0.0, v4 ? v4->freqs : nullptr,
-                     v4 ? v4->d_rope : 0);
+                     v4 ? v4->d_rope : 0, NHH == 1 ? ragged_items : 0);
 }
 
 // Compiled shapes: (latent r, row width r + G*d_rope, 16-head blocks per workgroup,
@@ -505,12 +529,12 @@ int decode_mfma_blocks_per_cu(const AttnShape& sh) {
 void decode_mfma(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
                  const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split,
                  int split_len, void* part_o, float* part_ml, float* o_out, hipStream_t s,
-                 const V4Epilogue* v4) {
+                 const V4Epilogue* v4, int ragged_items) {
   if (batch <= 0) return;
 #define MLA_LAUNCH(R_, RW_, NHB_, NHH_, ST_, HLO_, HHI_)                                          \
   if (sh.r == R_ && sh.row_w == RW_ && sh.H >= HLO_ && sh.H <= HHI_) {                           \
     launch<R_, RW_, NHB_, NHH_, ST_>(sh, q_lat, q_pe, cache, seq_start, seq_len, batch, n_split, \
-                                     split_len, part_o, part_ml, o_out, v4, s);                  \
+                                     split_len, part_o, part_ml, o_out, v4, s, ragged_items);    \
     return;                                                                                      \
   }
   MLA_DECODE_SHAPES(MLA_LAUNCH)

@@ -75,6 +75,9 @@ struct DecodePlan {
   bool mfma;
   int n_split;
   int split_len;
+  // > 0: the MFMA kernel makes the split plan on the device from the lengths,
+  // over this many workgroups (partial states indexed by item); 0: the plan above
+  int ragged_items;
   size_t part_o_bytes, part_ml_bytes, o_bytes;
   size_t total() const { return part_o_bytes + part_ml_bytes + o_bytes; }
 };
@@ -84,7 +87,8 @@ int split_rows(int L, int64_t ns, int unit = 64) {
   return (split_len + unit - 1) / unit * unit;
 }
 
-DecodePlan decode_plan(const mla_dims* d, int32_t batch, int32_t max_len, int32_t force_splits = 0) {
+DecodePlan decode_plan(const mla_dims* d, int32_t batch, int32_t max_len, int32_t force_splits = 0,
+                       bool allow_ragged = true) {
   DecodePlan p{};
   AttnShape sh = shape_of(d);
   p.wide = d->dtype == MLA_BF16 && mla::decode_wide_supported(sh);
@@ -118,11 +122,20 @@ DecodePlan decode_plan(const mla_dims* d, int32_t batch, int32_t max_len, int32_
   ns = (L + split_len - 1) / split_len;
   p.n_split = static_cast<int>(ns);
   p.split_len = split_len;
+  // A plan made here knows only the longest length, so a ragged batch leaves
+  // most of the shorter sequences' splits empty.  Where the MFMA kernel takes a
+  // whole split per workgroup and the merge is a separate kernel anyway (more
+  // splits than the merge folded into W_UV takes), let the kernel plan over the
+  // same number of workgroups from the lengths themselves (at most 64 of them).
+  if (allow_ragged && p.mfma && mla::decode_mfma_head_groups(sh) == 1 && B <= 64 &&
+      p.n_split > mla::skinny_max_merge())
+    p.ragged_items = static_cast<int>(B) * p.n_split;
   p.o_bytes = align_up(static_cast<size_t>(B) * sh.H * sh.r * sizeof(float));
-  if (p.n_split > 1) {
+  const int64_t items = p.ragged_items > 0 ? p.ragged_items : (p.n_split > 1 ? B * p.n_split : 0);
+  if (items > 0) {
     const size_t elem = d->dtype == MLA_F32 ? sizeof(float) : 2;  // partials in the layer's type
-    p.part_o_bytes = align_up(static_cast<size_t>(B) * p.n_split * sh.H * sh.r * elem);
-    p.part_ml_bytes = align_up(static_cast<size_t>(B) * p.n_split * sh.H * 2 * sizeof(float));
+    p.part_o_bytes = align_up(static_cast<size_t>(items) * sh.H * sh.r * elem);
+    p.part_ml_bytes = align_up(static_cast<size_t>(items) * sh.H * 2 * sizeof(float));
   }
   return p;
 }
@@ -489,17 +502,23 @@ int mla_decode(const mla_dims* dims, const void* q_lat, const void* q_pe, const 
   AttnShape sh = shape_of(dims);
   char* ws = static_cast<char*>(workspace);
   float* o_lat = reinterpret_cast<float*>(ws);
-  void* part_o = p.n_split > 1 ? static_cast<void*>(ws + p.o_bytes) : nullptr;
-  float* part_ml = p.n_split > 1 ? reinterpret_cast<float*>(ws + p.o_bytes + p.part_o_bytes) : nullptr;
+  const bool parts = p.ragged_items > 0 || p.n_split > 1;
+  void* part_o = parts ? static_cast<void*>(ws + p.o_bytes) : nullptr;
+  float* part_ml = parts ? reinterpret_cast<float*>(ws + p.o_bytes + p.part_o_bytes) : nullptr;
   if (p.wide)
     mla::decode_wide(sh, q_lat, q_pe, cache, seq_start, seq_len, batch, p.n_split, p.split_len,
                      part_o, part_ml, o_lat, s);
   else if (p.mfma)
     mla::decode_mfma(sh, q_lat, q_pe, cache, seq_start, seq_len, batch, p.n_split, p.split_len,
-                     part_o, part_ml, o_lat, s);
+                     part_o, part_ml, o_lat, s, nullptr, p.ragged_items);
   else
     mla::attend_generic(dims->dtype, sh, q_lat, q_pe, cache, seq_start, seq_len, nullptr, batch,
                         batch, p.n_split, p.split_len, part_o, part_ml, o_lat, s);
+  if (p.ragged_items > 0) {
+    mla::merge_splits(dims->dtype, sh, batch, p.n_split, part_o, part_ml, o_lat, s, seq_len, p.ragged_items);
+    apply_w_uv(dims, o_lat, batch, w_uv, out, s);
+    return launch_status();
+  }
   if (p.n_split > 1 && skinny_ok(dims, batch) && p.n_split <= mla::skinny_max_merge()) {
     // split merge folded into the W_UV operand load:
     //   out[b,h,:] = W_UV[h] · Σ_j w_j(b,h) part_o[b,j,h,:]
@@ -533,14 +552,14 @@ int32_t mla_decode_splits(const mla_dims* dims, int32_t batch, int32_t max_len) 
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (batch < 0 || max_len <= 0) return MLA_EINVAL;
-  return decode_plan(dims, batch, max_len).n_split;
+  return decode_plan(dims, batch, max_len, 0, /*allow_ragged=*/false).n_split;
 }
 
 int32_t mla_decode_split_rows(const mla_dims* dims, int32_t batch, int32_t max_len) {
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (batch < 0 || max_len <= 0) return MLA_EINVAL;
-  return decode_plan(dims, batch, max_len).split_len;
+  return decode_plan(dims, batch, max_len, 0, /*allow_ragged=*/false).split_len;
 }
 
 int mla_decode_partials(const mla_dims* dims, const void* q_lat, const void* q_pe,

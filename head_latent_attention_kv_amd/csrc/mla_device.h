@@ -93,4 +93,79 @@ __device__ __forceinline__ void rope_cos_sin(int32_t pos, int j, double base, co
   angle_cos_sin(static_cast<double>(pos) * rope_freq(j, base, freqs), c, s);
 }
 
+// ---- Split plan of a ragged decode batch (at most kWave sequences), made on the
+// device from the lengths so that the work spreads over n_items workgroups
+// whatever the lengths.  Every split of every sequence has split_len rows, the
+// smallest multiple of 64 with sum_b ceil(len_b / split_len) <= n_items; the
+// items (sequence, split) are numbered sequence after sequence.  Called by a
+// whole wave; lane b holds sequence b (lanes >= batch hold nothing), and every
+// lane gets the same split_len.  Requires batch < n_items.
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// A value the same in every lane, as a scalar (both 32-bit halves read from the
+// first active lane).
+__device__ __forceinline__ int64_t uniform_i64(long long v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v)));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+struct RaggedLane {
+  int split_len;
+  int len;    // this lane's sequence length (0 for lanes >= batch)
+  int first;  // first item of this lane's sequence
+  int count;  // items of this lane's sequence (0 for lanes >= batch)
+};
+
+__device__ inline RaggedLane ragged_plan(const int32_t* __restrict__ seq_len, int batch, int n_items) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int len = lane < batch ? max(seq_len[lane], 0) : 0;
+  const int total = wave_sum_int(len);
+  {
+    // all lengths equal: n_items / batch splits each (what a plan made on the
+    // host gives), no search
+    int mn = lane < batch ? len : INT_MAX, mx = len;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      mn = min(mn, __shfl_xor(mn, o, kWave));
+      mx = max(mx, __shfl_xor(mx, o, kWave));
+    }
+    if (mn == mx) {
+      const int per = n_items / batch;
+      RaggedLane r;
+      r.split_len = max(64, ((mx + per - 1) / per + 63) / 64 * 64);
+      r.len = len;
+      r.count = (len + r.split_len - 1) / r.split_len;
+      r.first = lane * ((mx + r.split_len - 1) / r.split_len);
+      return r;
+    }
+  }
+  // split_len = 64k: k_lo cannot fit fewer items than total / n_items; k_hi
+  // always fits (at most one partial split per sequence beyond total / 64k)
+  int k_lo = max(1, (total + 64 * n_items - 1) / (64 * n_items));
+  int k_hi = max(k_lo, (total + 64 * (n_items - batch) - 1) / (64 * (n_items - batch)));
+  while (k_lo < k_hi) {
+    const int mid = (k_lo + k_hi) >> 1;
+    const int items = wave_sum_int((len + 64 * mid - 1) / (64 * mid));
+    if (items <= n_items) k_hi = mid;
+    else k_lo = mid + 1;
+  }
+  RaggedLane r;
+  r.split_len = 64 * k_hi;
+  r.len = len;
+  r.count = (len + r.split_len - 1) / r.split_len;
+  int incl = r.count;  // inclusive prefix sum over the lanes
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int v = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += v;
+  }
+  r.first = incl - r.count;
+  return r;
+}
+
 }  // namespace mla

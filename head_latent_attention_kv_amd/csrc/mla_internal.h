@@ -118,9 +118,12 @@ int debug_check_write(const int64_t* slots, int64_t n_tokens, int64_t cache_rows
 bool attend_generic_fits(int dtype, const AttnShape& sh);
 
 // Log-sum-exp merge of split partials into normalised o_ (fp32 [n_q, H, r]).
-// part_o holds each split's normalised o_ in the layer's element type.
+// part_o holds each split's normalised o_ in the layer's element type, query q's
+// splits at items q·n_split ..; with ragged_items > 0 the items of the device
+// plan over seq_len (ragged_plan in mla_device.h) instead.
 void merge_splits(int dtype, const AttnShape& sh, int64_t n_q, int n_split, const void* part_o,
-                  const float* part_ml, float* o_out, hipStream_t s);
+                  const float* part_ml, float* o_out, hipStream_t s, const int32_t* seq_len = nullptr,
+                  int ragged_items = 0);
 
 // bf16 MFMA decode kernel for the shapes it supports (see decode_mfma.hip).
 // All 128 heads of a (sequence, split) per workgroup, for H = 128, G = 1,
@@ -136,10 +139,14 @@ int decode_mfma_head_groups(const AttnShape& sh);    // workgroups that share on
 struct V4Epilogue;
 // v4 (non-null: one split, a 16-head instance) writes the DeepSeek-V4 output
 // directly (sink in the denominator, inverse rotation of the tail).
+// ragged_items > 0 (shapes with one workgroup per split; at most 64 sequences,
+// fewer than ragged_items): the grid is ragged_items workgroups and the split
+// plan is made on the device from seq_len (ragged_plan); n_split and split_len
+// are then unused and the partials are indexed by item.
 void decode_mfma(const AttnShape& sh, const void* q_lat, const void* q_pe, const void* cache,
                  const int64_t* seq_start, const int32_t* seq_len, int batch, int n_split,
                  int split_len, void* part_o, float* part_ml, float* o_out, hipStream_t s,
-                 const V4Epilogue* v4 = nullptr);
+                 const V4Epilogue* v4 = nullptr, int ragged_items = 0);
 // The V4 variant's epilogue: the sink [H] (fp32 logits) joins each softmax's
 // denominator and the last d_rope dims of the output are rotated back by the
 // query's position (inverse frequencies from freqs, or theta).

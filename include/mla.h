@@ -212,9 +212,16 @@ int mla_decode_noalloc(const mla_dims* dims, const void* q_lat, const void* q_pe
                        const int64_t* seq_start, const int32_t* seq_len, int32_t batch, int32_t max_len,
                        const void* w_uv, void* out, void* stream);
 
-/* Number of context splits mla_decode uses for this batch (>= 1), or a negative
- * mla_status.  Split j of a sequence covers its rows [j*L, min(n, (j+1)*L)) with
- * L = mla_decode_split_rows(dims, batch, max_len); trailing splits may be empty. */
+/* The split plan made from the batch and the longest length: the number of
+ * context splits per sequence (>= 1), or a negative mla_status.  Split j of a
+ * sequence covers its rows [j*L, min(n, (j+1)*L)) with
+ * L = mla_decode_split_rows(dims, batch, max_len); trailing splits may be empty.
+ * mla_decode uses this plan, except where the MFMA kernel takes whole splits of
+ * at most 64 sequences and this plan has more splits than the merge folded into
+ * W_UV takes: there the kernel re-plans on the device from the actual lengths
+ * (equal-sized splits spread over the same number of workgroups), so a ragged
+ * batch does not leave most of the shorter sequences' workgroups empty.  The
+ * workspace mla_workspace_size reports covers either plan. */
 int32_t mla_decode_splits(const mla_dims* dims, int32_t batch, int32_t max_len);
 int32_t mla_decode_split_rows(const mla_dims* dims, int32_t batch, int32_t max_len);
 

@@ -122,7 +122,8 @@ def test_tiny_f32_run_in_a_graph(torch):
 
 
 @pytest.mark.parametrize("name,lengths", [("deepseek_v2_decode", [1, 300, 2048, 4100]),
-                                          ("qwen3_30b_ragged_decode", [33, 1537])])
+                                          ("qwen3_30b_ragged_decode", [33, 1537]),
+                                          ("qwen3_30b_ragged_decode", [1, 40, 3000, 9000, 20000])])
 def test_decode_step_in_a_graph(torch, name, lengths):
     """One bf16 decode step (write the batch's new rows, absorb, decode) as a graph."""
     import head_latent_attention_kv_amd as M

@@ -85,6 +85,9 @@ DECODE_CASES = [
     ("qwen25_7b_decode", [1, 65, 511, 1000]),
     ("deepseek_v2_decode", [1, 300, 2048]),
     ("qwen3_30b_ragged_decode", [1024, 1537]),
+    # more splits than the merge folded into W_UV takes: the split plan is made
+    # on the device from these lengths (sequences of 1 and 40 rows get one split)
+    ("qwen3_30b_ragged_decode", [1, 40, 3000, 9000, 20000]),
     # the generic kernel's plan: one-tile splits, splits past a short sequence empty
     ("tiny_f32", [1, 31, 32, 33, 65, 300]),
 ]
