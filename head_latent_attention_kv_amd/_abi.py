@@ -69,6 +69,10 @@ SIGNATURES = {
                                           _vp]),
     "mla_query_lowrank": (ctypes.c_int, [_PD, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "mla_output": (ctypes.c_int, [_PD, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "mla_tiled_weight_bytes": (_sz, [_i64, _i64]),
+    "mla_tile_weights": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i64, _vp, _sz, _vp]),
+    "mla_absorb_tiled": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "mla_output_tiled": (ctypes.c_int, [_PD, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "mla_v4_check_dims": (ctypes.c_int, [_P4]),
     "mla_v4_workspace_size": (_sz, [_P4, ctypes.c_int, _i32, _i64, _i32]),
     "mla_v4_write_cache": (ctypes.c_int, [_P4, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _sz, _vp]),
@@ -363,6 +367,48 @@ def mla_output(dims, attn, w_o, out, workspace=None, stream=None):
     ws, nbytes = _workspace(dims, MLA_OP_OUTPUT, 0, T, 0, workspace, attn.device)
     _check("mla_output", load().mla_output(
         ctypes.byref(dims), _ptr(attn, "attn", et), _ptr(w_o, "w_o", et), T, _ptr(out, "out", et),
+        _ptr(ws, "workspace"), nbytes, _stream(stream)))
+    return out
+
+
+def mla_tiled_weight_bytes(n_rows: int, k: int) -> int:
+    return int(load().mla_tiled_weight_bytes(n_rows, k))
+
+
+def mla_tile_weights(w0, w1=None, out=None, stream=None):
+    """[w0 ; w1] (bf16 [n, k] each) in the library's tiled layout, as a uint8 tensor."""
+    torch = _torch()
+    n0, k = w0.shape
+    n1 = 0 if w1 is None else w1.shape[0]
+    if w1 is not None and w1.shape[1] != k:
+        raise ValueError("w0 and w1 must have the same row length")
+    need = mla_tiled_weight_bytes(n0 + n1, k)
+    if out is None:
+        out = torch.empty(need, dtype=torch.uint8, device=w0.device)
+    _check("mla_tile_weights", load().mla_tile_weights(
+        _ptr(w0, "w0", torch.bfloat16), n0, _ptr(w1, "w1", torch.bfloat16), n1, k, _ptr(out, "out"),
+        out.numel() * out.element_size(), _stream(stream)))
+    return out
+
+
+def mla_absorb_tiled(dims, x, w_q_tiled, w_uk, positions, q_lat, q_pe, workspace=None, stream=None):
+    torch = _torch()
+    et = _elem_dtype(dims)
+    T = x.shape[0]
+    ws, nbytes = _workspace(dims, MLA_OP_ABSORB, 0, T, 0, workspace, x.device)
+    _check("mla_absorb_tiled", load().mla_absorb_tiled(
+        ctypes.byref(dims), _ptr(x, "x", et), _ptr(w_q_tiled, "w_q_tiled"), _ptr(w_uk, "w_uk", et),
+        _ptr(positions, "positions", torch.int32), T, _ptr(q_lat, "q_lat", et), _ptr(q_pe, "q_pe", et),
+        _ptr(ws, "workspace"), nbytes, _stream(stream)))
+    return q_lat, q_pe
+
+
+def mla_output_tiled(dims, attn, w_o_tiled, out, workspace=None, stream=None):
+    et = _elem_dtype(dims)
+    T = attn.shape[0]
+    ws, nbytes = _workspace(dims, MLA_OP_OUTPUT, 0, T, 0, workspace, attn.device)
+    _check("mla_output_tiled", load().mla_output_tiled(
+        ctypes.byref(dims), _ptr(attn, "attn", et), _ptr(w_o_tiled, "w_o_tiled"), T, _ptr(out, "out", et),
         _ptr(ws, "workspace"), nbytes, _stream(stream)))
     return out
 

@@ -440,24 +440,15 @@ int mla_write_cache(const mla_dims* dims, const void* x, const void* w_dkv, cons
   return launch_status();
 }
 
-int mla_absorb(const mla_dims* dims, const void* x, const void* w_qc, const void* w_qr,
-               const void* w_uk, const int32_t* positions, int64_t n_tokens, void* q_lat,
-               void* q_pe, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_dims(dims);
-  if (st != MLA_OK) return st;
-  if (n_tokens < 0) return MLA_EINVAL;
-  if (n_tokens == 0) return MLA_OK;
-  if (n_tokens > INT32_MAX) return MLA_ENOTSUP;
-  if (!ptr_ok(x) || !ptr_ok(w_qc) || !ptr_ok(w_qr) || !ptr_ok(w_uk) || !ptr_ok(positions) ||
-      !ptr_ok(q_lat) || !ptr_ok(q_pe) || !ptr_ok(workspace))
-    return MLA_EINVAL;
-  if (workspace_bytes < absorb_ws(dims, n_tokens)) return MLA_EWORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+}  // extern "C"
+
+namespace {
+// The absorption after the query projection: q (fp32 rows [q_nope | q_rope],
+// p.splits K slices) -> q_pe = RoPE(q_rope) and q_lat = q_nope·W_UK per head.
+void absorb_finish(const mla_dims* dims, float* q, const Proj& p, const void* w_uk,
+                   const int32_t* positions, int64_t n_tokens, void* q_lat, void* q_pe, hipStream_t s) {
   const int H = dims->n_heads;
   const int64_t ld = q_width(dims);
-  // one fp32 row per token: [q_nope (H x d_nope) | q_rope (H x d_rope)]
-  float* q = static_cast<float*>(workspace);
-  const Proj p = proj_two(dims, x, w_qc, H * dims->d_nope, w_qr, H * dims->d_rope, q, ld, n_tokens, s);
   mla::sum_split_slices(q, p.splits, p.sps, static_cast<int>(n_tokens), q_cols(dims), ld, s);
   mla::finalize_query_rope(dims->dtype, q + static_cast<int64_t>(H) * dims->d_nope, ld, dims->d_rope, q_pe,
                            positions, n_tokens, H, dims->d_rope, dims->rope_theta, dims->rope_freqs, s);
@@ -477,6 +468,88 @@ int mla_absorb(const mla_dims* dims, const void* x, const void* w_qc, const void
   a.K = dims->d_nope;
   a.Z = H;
   mla::gemm(a, dims->dtype, /*a_f32=*/true, /*b_kn=*/true, dims->dtype == MLA_BF16, s);
+}
+
+// C (fp32, row stride ldc) = A [T, k] (bf16, row stride lda) · Wᵀ with W [n, k] in
+// the tiled layout; the same K-slice plan as proj_one / proj_two (few tokens)
+Proj proj_tiled(const mla_dims* d, const void* a, int64_t lda, int k, const void* w_tiled, int n, float* c,
+                int64_t ldc, int64_t n_tokens, hipStream_t s) {
+  const Proj p = proj_plan_k(d, n, k, n_tokens, ldc);
+  mla::SkinnyArgs sa{};
+  sa.A = a;
+  sa.sAm = lda;
+  sa.Bt = static_cast<const uint16_t*>(w_tiled);
+  sa.N0 = n;
+  sa.C = c;
+  sa.sCm = ldc;
+  sa.sPs = p.sps;
+  sa.M = static_cast<int>(n_tokens);
+  sa.N = n;
+  sa.K = k;
+  sa.Z = 1;
+  sa.splits = p.splits;
+  mla::gemm_skinny_tiled(sa, /*out_bf16=*/false, s);
+  return p;
+}
+}  // namespace
+
+extern "C" {
+
+int mla_absorb(const mla_dims* dims, const void* x, const void* w_qc, const void* w_qr,
+               const void* w_uk, const int32_t* positions, int64_t n_tokens, void* q_lat,
+               void* q_pe, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_tokens < 0) return MLA_EINVAL;
+  if (n_tokens == 0) return MLA_OK;
+  if (n_tokens > INT32_MAX) return MLA_ENOTSUP;
+  if (!ptr_ok(x) || !ptr_ok(w_qc) || !ptr_ok(w_qr) || !ptr_ok(w_uk) || !ptr_ok(positions) ||
+      !ptr_ok(q_lat) || !ptr_ok(q_pe) || !ptr_ok(workspace))
+    return MLA_EINVAL;
+  if (workspace_bytes < absorb_ws(dims, n_tokens)) return MLA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int H = dims->n_heads;
+  const int64_t ld = q_width(dims);
+  // one fp32 row per token: [q_nope (H x d_nope) | q_rope (H x d_rope)]
+  float* q = static_cast<float*>(workspace);
+  const Proj p = proj_two(dims, x, w_qc, H * dims->d_nope, w_qr, H * dims->d_rope, q, ld, n_tokens, s);
+  absorb_finish(dims, q, p, w_uk, positions, n_tokens, q_lat, q_pe, s);
+  return launch_status();
+}
+
+size_t mla_tiled_weight_bytes(int64_t n_rows, int64_t k) {
+  if (n_rows <= 0 || k <= 0) return 0;
+  return static_cast<size_t>(mla::tiled_weight_bytes(n_rows, k));
+}
+
+int mla_tile_weights(const void* w0, int64_t n0, const void* w1, int64_t n1, int64_t k, void* out,
+                     size_t out_bytes, void* stream) {
+  if (n0 < 0 || n1 < 0 || n0 + n1 <= 0 || k <= 0 || k % 8 != 0) return MLA_EINVAL;
+  if (n0 + n1 > INT32_MAX || k > INT32_MAX) return MLA_ENOTSUP;
+  if ((n0 > 0 && !ptr_ok(w0)) || (n1 > 0 && !ptr_ok(w1)) || !ptr_ok(out)) return MLA_EINVAL;
+  if (out_bytes < mla_tiled_weight_bytes(n0 + n1, k)) return MLA_EINVAL;
+  mla::tile_weights(static_cast<const uint16_t*>(w0), n0, static_cast<const uint16_t*>(w1), n1, k,
+                    static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int mla_absorb_tiled(const mla_dims* dims, const void* x, const void* w_q_tiled, const void* w_uk,
+                     const int32_t* positions, int64_t n_tokens, void* q_lat, void* q_pe, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_tokens < 0) return MLA_EINVAL;
+  if (n_tokens == 0) return MLA_OK;
+  if (dims->dtype != MLA_BF16 || n_tokens > 64) return MLA_ENOTSUP;
+  if (!ptr_ok(x) || !ptr_ok(w_q_tiled) || !ptr_ok(w_uk) || !ptr_ok(positions) || !ptr_ok(q_lat) ||
+      !ptr_ok(q_pe) || !ptr_ok(workspace))
+    return MLA_EINVAL;
+  if (workspace_bytes < absorb_ws(dims, n_tokens)) return MLA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* q = static_cast<float*>(workspace);
+  const Proj p = proj_tiled(dims, x, dims->d_model, dims->d_model, w_q_tiled, q_cols(dims), q, q_width(dims),
+                            n_tokens, s);
+  absorb_finish(dims, q, p, w_uk, positions, n_tokens, q_lat, q_pe, s);
   return launch_status();
 }
 
@@ -847,6 +920,25 @@ int mla_output(const mla_dims* dims, const void* attn, const void* w_o, int64_t 
     g.Z = 1;
     mla::gemm(g, dims->dtype, /*a_f32=*/false, /*b_kn=*/false, /*out_bf16=*/dims->dtype == MLA_BF16, s);
   }
+  return launch_status();
+}
+
+int mla_output_tiled(const mla_dims* dims, const void* attn, const void* w_o_tiled, int64_t n_tokens,
+                     void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_tokens < 0) return MLA_EINVAL;
+  if (n_tokens == 0) return MLA_OK;
+  const int K = dims->n_heads * dims->d_v;
+  if (dims->dtype != MLA_BF16 || n_tokens > 64 || K % 8 != 0) return MLA_ENOTSUP;
+  const size_t need = output_ws(dims, n_tokens);
+  if (!ptr_ok(attn) || !ptr_ok(w_o_tiled) || !ptr_ok(out) || !ptr_ok(workspace)) return MLA_EINVAL;
+  if (workspace_bytes < need) return MLA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* c = static_cast<float*>(workspace);
+  const int64_t ld = out_width(dims);
+  const Proj p = proj_tiled(dims, attn, K, K, w_o_tiled, dims->d_model, c, ld, n_tokens, s);
+  mla::sum_cast_slices(dims->dtype, c, p.splits, p.sps, static_cast<int>(n_tokens), dims->d_model, ld, out, s);
   return launch_status();
 }
 

@@ -52,9 +52,24 @@ struct SkinnyArgs {
   int ml_heads, n_merge;
   // token rows split over m_groups workgroups per column tile (0 or 1: one)
   int m_groups;
+  // weights in the tiled streaming layout (gemm_skinny_tiled; B0/B1 unused)
+  const uint16_t* Bt;
 };
 int skinny_splits(int M, int N, int Z, int K);
 void gemm_skinny(SkinnyArgs sa, bool a_f32, bool out_bf16, hipStream_t s);
+// Tiled streaming layout of a weight [W0 (n0 rows) ; W1 (n1 rows)] of row length
+// k: blocks of kTileRows rows x kTileK k (24 KB), tile-major then k-block, each
+// row's 16-byte chunks XOR-swizzled by (row & 15); rows past n0 + n1 and k past
+// k are zero.  gemm_skinny_tiled reads it with one contiguous 1 KB copy per
+// kilobyte of a block.
+constexpr int kTileRows = 96;
+constexpr int kTileK = 128;
+int64_t tiled_weight_bytes(int64_t n_rows, int64_t k);
+void tile_weights(const uint16_t* w0, int64_t n0, const uint16_t* w1, int64_t n1, int64_t k, uint16_t* out,
+                  hipStream_t s);
+// bf16 A (M <= 64) times weights in the tiled layout (sa.Bt; N = n0 + n1 rows,
+// K = k), fp32 or bf16 out with sa.splits K slices as gemm_skinny
+void gemm_skinny_tiled(SkinnyArgs sa, bool out_bf16, hipStream_t s);
 void sum_split_slices(float* c, int splits, int64_t sps, int M, int N, int64_t ldc, hipStream_t s);
 // out[m, n] (dense [M, N], dtype) = Σ_p c[p*sps + m*ldc + n]
 void sum_cast_slices(int dtype, const float* c, int splits, int64_t sps, int M, int N, int64_t ldc, void* out,

@@ -279,7 +279,11 @@ __global__ __launch_bounds__(256, MINB) void skinny_kernel(SkinnyArgs sa) {
 // compute wave w < 4 takes k-step w (32 k) for all 64 x 96 outputs, and the four
 // partial tiles are summed through LDS at the end.  k past the K piece is read
 // from a clamped address and its A fragments are zeroed.
-constexpr int kDmaCols = 96;                         // 6 column blocks
+// With the weights in the tiled layout (sa.Bt) a stage's weight image is one
+// contiguous 24 KB block, already swizzled, so each weight copy reads one
+// contiguous kilobyte: HBM then serves whole DRAM pages instead of 256-byte runs
+// of 96 rows 10 KB apart.
+constexpr int kDmaCols = kTileRows;                  // 6 column blocks
 constexpr int kDmaNB = kDmaCols / 16;
 constexpr int kDmaWaves = 8;                         // 4 compute + 4 copy waves
 constexpr int kDmaThreads = 64 * kDmaWaves;
@@ -299,14 +303,15 @@ struct DmaStage {
   static constexpr int kStages = kDmaLdsMax / kBytes;
   static constexpr int kLds = kStages * kBytes;
   static constexpr int kStepsPerWave = KC / 4 / kKS;     // k-steps of one wave per stage
-  static_assert(kOps % 4 == 0, "copies split evenly over the waves");
+  static_assert(kWOps % 4 == 0 && kAOps % 4 == 0, "copies of each kind split evenly over the copy waves");
   static_assert(kOpsPerWave * (kStages - 1) < 64 && kStages <= 5, "vmcnt range");
   static_assert(kStepsPerWave >= 1 && kRun / 16 <= 16 * 2, "swizzle covers a row's chunks");
 };
 
-template <int MB, int KC, typename OutT>
+template <int MB, int KC, typename OutT, bool TILED>
 __global__ __launch_bounds__(kDmaThreads, 1) void skinny_dma_kernel(SkinnyArgs sa) {
   using G = DmaStage<KC, 16 * MB>;
+  static_assert(KC == kTileK && G::kWOps * 1024 == kTileRows * kTileK * 2, "a stage's weights are one tiled block");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -326,43 +331,57 @@ __global__ __launch_bounds__(kDmaThreads, 1) void skinny_dma_kernel(SkinnyArgs s
   // weight tile (o < kWOps, o' = o) or of the token rows (o' = o - kWOps); the
   // lanes of row R·o'+q fill its LDS chunks p in order.  The rows of a weight
   // copy come from one matrix (B0 rows [0, N0), B1 the rest; N0 is a multiple
-  // of 4 and of R).  Copy wave 4 + c issues copies o = c + 4i.
+  // of 4 and of R).  Copy wave 4 + c issues weight copies o = c + 4i, then
+  // token-row copies o = kWOps + c + 4i, so which kind a copy is never depends
+  // on the wave.  Tiled weights: block (column tile, k block) is the stage's
+  // weight image, copied kilobyte by kilobyte.
+  const char* w_tiled = nullptr;
+  if constexpr (TILED)
+    w_tiled = reinterpret_cast<const char*>(sa.Bt) +
+              (static_cast<int64_t>(blockIdx.x) * ((sa.K + KC - 1) / KC) + k_lo / KC) * (G::kWOps * 1024LL);
   auto issue = [&](int st) {
     if (!copy_wave) return;
+    const int c = wave - 4;
     const int kb = k_lo + st * KC;
     const uint32_t dst = lds0 + (st % G::kStages) * G::kBytes;
     int ln = lane;
     __asm__ volatile("" : "+v"(ln));
     constexpr int kLanesPerRow = G::kRun / 16;
     const int q = ln / kLanesPerRow, p = ln % kLanesPerRow;
+    // k of this lane's chunk in a row whose swizzle key is key (clamped into the K piece)
+    auto k_of = [&](int key) {
+      const int kc = kb + 8 * (p ^ key);
+      return kc < k_hi ? kc : k_hi - 8;
+    };
+    // weights are read once per launch (non-temporal copy); the token rows
+    // are read by every workgroup and stay cached
 #pragma unroll
-    for (int i = 0; i < G::kOpsPerWave; ++i) {
-      const int o = (wave - 4) + 4 * i;
-      const bool w_op = o < G::kWOps;
-      const int o2 = w_op ? o : o - G::kWOps;
-      const int key = (o2 * G::kRowsPerOp + q) & 15;
-      int kc = kb + 8 * (p ^ key);
-      kc = kc < k_hi ? kc : k_hi - 8;
-      const char* sbase;
-      uint32_t voff;
-      if (w_op) {
+    for (int i = 0; i < G::kWOps / 4; ++i) {
+      const int o = c + 4 * i;
+      const uint32_t to = __builtin_amdgcn_readfirstlane(dst + o * 1024);
+      if constexpr (TILED) {
+        global_to_lds16_stream(w_tiled + static_cast<int64_t>(st) * (G::kWOps * 1024) + o * 1024,
+                               static_cast<uint32_t>(ln) * 16u, to);
+      } else {
         // rows past N read row N - 1; the base row keeps every lane offset >= 0
-        const int r_base = min(n0 + o2 * G::kRowsPerOp, sa.N - 1);
-        const int r = min(n0 + o2 * G::kRowsPerOp + q, sa.N - 1);
+        const int r_base = min(n0 + o * G::kRowsPerOp, sa.N - 1);
+        const int r = min(n0 + o * G::kRowsPerOp + q, sa.N - 1);
         const uint16_t* mat = r_base < sa.N0 ? sa.B0 + static_cast<int64_t>(r_base) * sa.sBo
                                              : sa.B1 + static_cast<int64_t>(r_base - sa.N0) * sa.sBo;
-        sbase = reinterpret_cast<const char*>(mat + b_off);
-        voff = static_cast<uint32_t>((r - r_base) * sa.sBo + kc) * 2u;
-      } else {
-        const int m_base = min(o2 * G::kRowsPerOp, sa.M - 1);
-        const int m = min(o2 * G::kRowsPerOp + q, sa.M - 1);
-        sbase = reinterpret_cast<const char*>(a_mat + static_cast<int64_t>(m_base) * sa.sAm);
-        voff = static_cast<uint32_t>((m - m_base) * sa.sAm + kc) * 2u;
+        const int kc = k_of((o * G::kRowsPerOp + q) & 15);
+        global_to_lds16_stream(reinterpret_cast<const char*>(mat + b_off),
+                               static_cast<uint32_t>((r - r_base) * sa.sBo + kc) * 2u, to);
       }
-      // weights are read once per launch (non-temporal copy); the token rows
-      // are read by every workgroup and stay cached
-      if (w_op) global_to_lds16_stream(sbase, voff, __builtin_amdgcn_readfirstlane(dst + o * 1024));
-      else global_to_lds16(sbase, voff, __builtin_amdgcn_readfirstlane(dst + o * 1024));
+    }
+#pragma unroll
+    for (int i = 0; i < G::kAOps / 4; ++i) {
+      const int o2 = c + 4 * i;
+      const int m_base = min(o2 * G::kRowsPerOp, sa.M - 1);
+      const int m = min(o2 * G::kRowsPerOp + q, sa.M - 1);
+      const int kc = k_of((o2 * G::kRowsPerOp + q) & 15);
+      global_to_lds16(reinterpret_cast<const char*>(a_mat + static_cast<int64_t>(m_base) * sa.sAm),
+                      static_cast<uint32_t>((m - m_base) * sa.sAm + kc) * 2u,
+                      __builtin_amdgcn_readfirstlane(dst + (G::kWOps + o2) * 1024));
     }
   };
 
@@ -744,18 +763,26 @@ void launch_out(const SkinnyArgs& sa, bool out_bf16, hipStream_t s) {
     hipLaunchKernelGGL((skinny_kernel<MB, NB, AK, NS, DEPTH, MINB, float>), grid, dim3(256), 0, s, sa);
 }
 
-template <int MB, int KC = 128>
-void launch_dma(const SkinnyArgs& sa, bool out_bf16, hipStream_t s) {
+template <int MB, bool TILED, typename OutT>
+void launch_dma_kernel(const SkinnyArgs& sa, hipStream_t s) {
+  constexpr int KC = kTileK;
   dim3 grid((sa.N + kDmaCols - 1) / kDmaCols, sa.Z, sa.splits);
   constexpr int lds = DmaStage<KC, 16 * MB>::kLds;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_dma_kernel<MB, KC, OutT, TILED>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  hipLaunchKernelGGL((skinny_dma_kernel<MB, KC, OutT, TILED>), grid, dim3(kDmaThreads), lds, s, sa);
+}
+
+// weights in place (B0 / B1), or tiled (sa.Bt)
+template <int MB>
+void launch_dma(const SkinnyArgs& sa, bool out_bf16, hipStream_t s) {
+  const bool tiled = sa.Bt != nullptr;
   if (out_bf16) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_dma_kernel<MB, KC, bf16_t>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    hipLaunchKernelGGL((skinny_dma_kernel<MB, KC, bf16_t>), grid, dim3(kDmaThreads), lds, s, sa);
+    if (tiled) launch_dma_kernel<MB, true, bf16_t>(sa, s);
+    else launch_dma_kernel<MB, false, bf16_t>(sa, s);
   } else {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(skinny_dma_kernel<MB, KC, float>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    hipLaunchKernelGGL((skinny_dma_kernel<MB, KC, float>), grid, dim3(kDmaThreads), lds, s, sa);
+    if (tiled) launch_dma_kernel<MB, true, float>(sa, s);
+    else launch_dma_kernel<MB, false, float>(sa, s);
   }
 }
 
@@ -790,6 +817,56 @@ void launch(const SkinnyArgs& sa, int kind, int ns, bool out_bf16, hipStream_t s
 }
 
 }  // namespace
+
+namespace {
+// out chunk i (16 bytes): slot p = i % 16 of row r of block b = i / (16 kTileRows),
+// b = tile t x k block kb; it holds k = kTileK kb + 8 (p ^ (r & 15)) .. + 7 of
+// weight row kTileRows t + r (zero past the rows or past k)
+__global__ __launch_bounds__(256) void tile_weights_kernel(const uint16_t* __restrict__ w0, int64_t n0,
+                                                           const uint16_t* __restrict__ w1, int64_t n1,
+                                                           int64_t k, int64_t k_blocks,
+                                                           uint4* __restrict__ out, int64_t n_chunks) {
+  for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n_chunks; i += gridDim.x * 256LL) {
+    const int p = static_cast<int>(i & 15);
+    const int64_t rb = i >> 4;
+    const int r = static_cast<int>(rb % kTileRows);
+    const int64_t blk = rb / kTileRows;
+    const int64_t row = (blk / k_blocks) * kTileRows + r;
+    const int64_t kk = (blk % k_blocks) * kTileK + 8 * (p ^ (r & 15));
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (row < n0 + n1 && kk < k) {
+      const uint16_t* src = row < n0 ? w0 + row * k : w1 + (row - n0) * k;
+      v = *reinterpret_cast<const uint4*>(src + kk);
+    }
+    out[i] = v;
+  }
+}
+}  // namespace
+
+int64_t tiled_weight_bytes(int64_t n_rows, int64_t k) {
+  return (n_rows + kTileRows - 1) / kTileRows * ((k + kTileK - 1) / kTileK) * (kTileRows * kTileK * 2);
+}
+
+void tile_weights(const uint16_t* w0, int64_t n0, const uint16_t* w1, int64_t n1, int64_t k, uint16_t* out,
+                  hipStream_t s) {
+  const int64_t n_chunks = tiled_weight_bytes(n0 + n1, k) / 16;
+  if (n_chunks <= 0) return;
+  const int blocks = static_cast<int>(std::min<int64_t>(8192, (n_chunks + 255) / 256));
+  hipLaunchKernelGGL(tile_weights_kernel, dim3(blocks), dim3(256), 0, s, w0, n0, w1, n1, k,
+                     (k + kTileK - 1) / kTileK, reinterpret_cast<uint4*>(out), n_chunks);
+}
+
+void gemm_skinny_tiled(SkinnyArgs sa, bool out_bf16, hipStream_t s) {
+  if (sa.M <= 0 || sa.M > 64 || sa.N <= 0 || sa.Z != 1) return;
+  if (sa.splits < 1) sa.splits = 1;
+  sa.k_per_split = k_per_split(sa.K, sa.splits);
+  switch ((sa.M + 15) / 16) {
+    case 1: launch_dma<1>(sa, out_bf16, s); break;
+    case 2: launch_dma<2>(sa, out_bf16, s); break;
+    case 3: launch_dma<3>(sa, out_bf16, s); break;
+    default: launch_dma<4>(sa, out_bf16, s); break;
+  }
+}
 
 void gemm_skinny(SkinnyArgs sa, bool a_f32, bool out_bf16, hipStream_t s) {
   if (sa.splits < 1) sa.splits = 1;

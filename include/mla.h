@@ -344,6 +344,38 @@ int mla_query_lowrank(const mla_dims* dims, int32_t q_rank, const void* x, const
 int mla_output(const mla_dims* dims, const void* attn, const void* w_o, int64_t n_tokens, void* out,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Tiled weights for few-token steps.  With n_tokens <= 64 a projection is a
+ * stream of its whole weight.  Read in place, 96 rows at a time, the weight
+ * arrives as 256-byte runs of 96 rows that lie 2*in_features bytes apart, which
+ * leaves HBM pages mostly unused.  mla_tile_weights re-lays a weight [W0 ; W1]
+ * once (at load time) so that each block of 96 rows x 128 input features is one
+ * contiguous 24 KB piece: block t*ceil(k/128) + j holds rows [96t, 96t + 96) and
+ * features [128j, 128j + 128), row after row, with the 16-byte chunks of block
+ * row i in the order (chunk ^ (i & 15)); rows past n0 + n1 and features past k
+ * are zero.  Only the *_tiled calls read the result.
+ *   w0 device bf16 [n0, k]; w1 device bf16 [n1, k] (may be NULL when n1 == 0)
+ *   out device, >= mla_tiled_weight_bytes(n0 + n1, k) bytes
+ *   k: multiple of 8.  Sizes or pointers out of range return MLA_EINVAL.
+ * mla_absorb_tiled and mla_output_tiled compute what mla_absorb and mla_output
+ * compute, from
+ *   w_q_tiled = [W_QC ; W_QR] tiled: mla_tile_weights(w_qc, H*d_nope, w_qr, H*d_rope, d_model, ...)
+ *   w_o_tiled = W_o tiled:           mla_tile_weights(w_o, d_model, NULL, 0, H*d_v, ...)
+ * with the workspace of MLA_OP_ABSORB / MLA_OP_OUTPUT, for dims->dtype == MLA_BF16
+ * and 1 <= n_tokens <= 64 (MLA_ENOTSUP otherwise; n_tokens == 0 is a no-op).
+ * Where mla_absorb / mla_output stream the weight with the same kernel (96
+ * output columns per workgroup, as at H = 128 and d_model = 5120) the results
+ * are bit-identical; elsewhere they agree to rounding.
+ * Source: the passages cited at mla_absorb and mla_output; the layout is a
+ * storage choice of this library. */
+size_t mla_tiled_weight_bytes(int64_t n_rows, int64_t k);
+int mla_tile_weights(const void* w0, int64_t n0, const void* w1, int64_t n1, int64_t k, void* out,
+                     size_t out_bytes, void* stream);
+int mla_absorb_tiled(const mla_dims* dims, const void* x, const void* w_q_tiled, const void* w_uk,
+                     const int32_t* positions, int64_t n_tokens, void* q_lat, void* q_pe, void* workspace,
+                     size_t workspace_bytes, void* stream);
+int mla_output_tiled(const mla_dims* dims, const void* attn, const void* w_o_tiled, int64_t n_tokens,
+                     void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------------
  * DeepSeek-V4 / nanowhale variant (nanowhale MLA page).  One KV head of head_dim
  * values, kv = kv_norm(x·W_KVᵀ) (RMSNorm with gain), its last d_rope dims rotated

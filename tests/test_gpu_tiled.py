@@ -1,0 +1,177 @@
+"""The tiled weight layout and the few-token calls that read it.
+
+- mla_tile_weights against a re-layout written here in numpy from the layout's
+  definition (include/mla.h): bit for bit, with row counts and k that leave
+  partial blocks.
+- mla_absorb_tiled and mla_output_tiled against the oracle (q_lat, q_pe and the
+  output projection), and bit for bit against mla_absorb / mla_output where those
+  stream the same weight through the same kernel (H = 128, d_model 5120 or 5000).
+- the argument errors of the new entry points."""
+import numpy as np
+import pytest
+
+import mla_inputs as I
+from tests import harness as Hh
+
+pytestmark = pytest.mark.gpu
+
+ROWS, KB = 96, 128  # block geometry stated in include/mla.h
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch
+    import head_latent_attention_kv_amd as M
+    M.load()
+    assert torch.cuda.is_available()
+    return torch
+
+
+def _tiled_reference(w: np.ndarray) -> np.ndarray:
+    """uint16 [n, k] -> the tiled layout's uint16 stream: block (t, j) = rows
+    [96t, 96t + 96) x features [128j, 128j + 128), row after row, slot p of block
+    row i holding 16-byte chunk p ^ (i & 15) of that row; zero padding."""
+    n, k = w.shape
+    nt, nk = -(-n // ROWS), -(-k // KB)
+    pad = np.zeros((nt * ROWS, nk * KB), np.uint16)
+    pad[:n, :k] = w
+    blocks = pad.reshape(nt, ROWS, nk, KB).transpose(0, 2, 1, 3)  # [t, j, row, k]
+    chunks = blocks.reshape(nt, nk, ROWS, KB // 8, 8)
+    i = np.arange(ROWS)[:, None]
+    p = np.arange(KB // 8)[None, :]
+    return chunks[:, :, i, p ^ (i & 15)].reshape(-1)
+
+
+def _bits(torch, a: np.ndarray):
+    return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("n0,n1,k", [(200, 37, 264), (96, 0, 128), (5, 3, 8)])
+def test_tile_weights_layout(torch, n0, n1, k):
+    import head_latent_attention_kv_amd as M
+    print(f"[case] tile_weights n0={n0} n1={n1} k={k}", flush=True)
+    rng = np.random.default_rng(n0 * 1000 + n1 * 10 + k)
+    w0 = rng.integers(0, 1 << 16, size=(n0, k), dtype=np.uint16)
+    w1 = rng.integers(0, 1 << 16, size=(n1, k), dtype=np.uint16)
+    out = M.mla_tile_weights(_bits(torch, w0), _bits(torch, w1) if n1 else None)
+    torch.cuda.synchronize()
+    assert out.numel() == M.mla_tiled_weight_bytes(n0 + n1, k)
+    got = out.cpu().numpy().view(np.uint16)
+    ref = _tiled_reference(np.concatenate([w0, w1]))
+    assert got.shape == ref.shape
+    assert np.array_equal(got, ref)
+
+
+def _absorb_both(torch, layer, x_dev, pos):
+    import head_latent_attention_kv_amd as M
+    cfg, wd = layer.cfg, layer.w_dev
+    wt = M.mla_tile_weights(wd["w_qc"], wd["w_qr"])
+    T = x_dev.shape[0]
+    et = Hh.elem_dtype(cfg)
+    q_lat = torch.full((T, cfg.n_heads, cfg.rank), 7.0, dtype=et, device="cuda")
+    q_pe = torch.full((T, cfg.n_heads, cfg.d_rope), 7.0, dtype=et, device="cuda")
+    pos_d = torch.from_numpy(pos.astype(np.int32)).cuda()
+    M.mla_absorb_tiled(layer.dims, x_dev, wt, wd["w_uk"], pos_d, q_lat, q_pe)
+    ql_ref, qp_ref = Hh.absorb(layer, x_dev, pos)
+    torch.cuda.synchronize()
+    return q_lat, q_pe, ql_ref, qp_ref
+
+
+@pytest.mark.parametrize("name,d_model,T", [("deepseek_v2_decode", None, 64), ("deepseek_v2_decode", None, 1),
+                                            ("deepseek_v2_decode", 5000, 37), ("qwen25_7b_decode", None, 64),
+                                            ("qwen3_30b_ragged_decode", None, 20)])
+def test_absorb_tiled_matches_oracle(torch, name, d_model, T):
+    from oracle import mla_oracle as O
+    cfg = I.CONFIGS[name] if d_model is None else I.small_variant(I.CONFIGS[name], d_model=d_model, seed=2003)
+    print(f"[case] absorb_tiled {name} d_model={cfg.d_model} T={T}", flush=True)
+    layer = Hh.make_layer(cfg)
+    x = I.x_rows(cfg, 0, 0, T)
+    pos = np.arange(T) * 131 % 8192
+    q_lat, q_pe, ql_ref, qp_ref = _absorb_both(torch, layer, Hh.to_dev(x, cfg.dtype), pos)
+    w = layer.w_host
+    qn, qr = O.query(x, w["w_qc"], w["w_qr"], pos, n_heads=cfg.n_heads, d_nope=cfg.d_nope,
+                     d_rope=cfg.d_rope, theta=cfg.rope_theta)
+    err_lat = Hh.rel_err_rows(Hh.to_host(q_lat), O.absorbed_query(qn, w["w_uk"]))
+    err_pe = Hh.rel_err_rows(Hh.to_host(q_pe), qr)
+    same = torch.equal(q_lat, ql_ref) and torch.equal(q_pe, qp_ref)
+    print(f"absorb_tiled {name} T={T}: q_lat {err_lat:.3e} q_pe {err_pe:.3e}; identical to mla_absorb: {same}")
+    assert err_lat <= Hh.TOL[cfg.dtype] and err_pe <= Hh.TOL[cfg.dtype], (err_lat, err_pe)
+    if cfg.n_heads == 128:
+        # mla_absorb streams [W_QC ; W_QR] with the same kernel and K plan here
+        assert same
+
+
+@pytest.mark.parametrize("name,T", [("deepseek_v2_decode", 64), ("deepseek_v2_decode", 3),
+                                    ("qwen3_30b_ragged_decode", 64)])
+def test_output_tiled_matches_oracle(torch, name, T):
+    import head_latent_attention_kv_amd as M
+    from oracle import mla_oracle as O
+    cfg = I.CONFIGS[name]
+    print(f"[case] output_tiled {name} T={T}", flush=True)
+    layer = Hh.make_layer(cfg)
+    w_o = I.output_weight(cfg)
+    o = I.draw_normal(cfg.seed, 41, (T,), (T, cfg.n_heads, cfg.d_v), 1.0, cfg.dtype)
+    od, wod = Hh.to_dev(o, cfg.dtype), Hh.to_dev(w_o, cfg.dtype)
+    wt = M.mla_tile_weights(wod)
+    out = torch.full((T, cfg.d_model), 7.0, dtype=Hh.elem_dtype(cfg), device="cuda")
+    ref = torch.empty_like(out)
+    M.mla_output_tiled(layer.dims, od, wt, out)
+    M.mla_output(layer.dims, od, wod, ref)
+    torch.cuda.synchronize()
+    err = Hh.rel_err_rows(Hh.to_host(out), O.output_projection(o, w_o))
+    same = torch.equal(out, ref)
+    print(f"output_tiled {name} T={T}: {err:.3e}; identical to mla_output: {same}")
+    assert err <= Hh.TOL[cfg.dtype], err
+    if cfg.n_heads == 128:
+        assert same
+
+
+def test_tiled_argument_errors(torch):
+    import ctypes
+    import head_latent_attention_kv_amd as M
+    from head_latent_attention_kv_amd import _abi
+    lib = M.load()
+    cfg = I.small_variant(I.CONFIGS["deepseek_v2_decode"], d_model=256, n_heads=8, rank=64, d_rope=16,
+                          d_nope=32, d_v=32)
+    print("[case] tiled argument errors", flush=True)
+    layer = Hh.make_layer(cfg)
+    wd = layer.w_dev
+    s = torch.cuda.current_stream().cuda_stream
+    ptr = lambda t: t.data_ptr()
+    w = wd["w_qc"]
+    n_q = cfg.n_heads * (cfg.d_nope + cfg.d_rope)
+    need = M.mla_tiled_weight_bytes(n_q, cfg.d_model)
+    buf = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    # k not a multiple of 8, negative rows, too small an output, null w1 with rows
+    assert lib.mla_tile_weights(ptr(w), 4, None, 0, 12, ptr(buf), need, s) == M.MLA_EINVAL
+    assert lib.mla_tile_weights(ptr(w), -1, None, 0, cfg.d_model, ptr(buf), need, s) == M.MLA_EINVAL
+    assert lib.mla_tile_weights(ptr(wd["w_qc"]), cfg.n_heads * cfg.d_nope, ptr(wd["w_qr"]),
+                                cfg.n_heads * cfg.d_rope, cfg.d_model, ptr(buf), need - 16, s) == M.MLA_EINVAL
+    assert lib.mla_tile_weights(ptr(w), 4, None, 4, cfg.d_model, ptr(buf), need, s) == M.MLA_EINVAL
+    assert M.mla_tiled_weight_bytes(0, 8) == 0
+    assert lib.mla_tile_weights(ptr(wd["w_qc"]), cfg.n_heads * cfg.d_nope, ptr(wd["w_qr"]),
+                                cfg.n_heads * cfg.d_rope, cfg.d_model, ptr(buf), need, s) == M.MLA_OK
+    T = 65
+    x = torch.zeros((T, cfg.d_model), dtype=torch.bfloat16, device="cuda")
+    pos = torch.zeros(T, dtype=torch.int32, device="cuda")
+    q_lat = torch.zeros((T, cfg.n_heads, cfg.rank), dtype=torch.bfloat16, device="cuda")
+    q_pe = torch.zeros((T, cfg.n_heads, cfg.d_rope), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    d = ctypes.byref(layer.dims)
+    ab = lambda n, nb: lib.mla_absorb_tiled(d, ptr(x), ptr(buf), ptr(wd["w_uk"]), ptr(pos), n, ptr(q_lat),
+                                            ptr(q_pe), ptr(ws), nb, s)
+    assert ab(65, ws.numel()) == M.MLA_ENOTSUP          # more than 64 tokens
+    assert ab(0, 0) == M.MLA_OK                          # no-op
+    assert ab(4, 16) == M.MLA_EWORKSPACE
+    assert lib.mla_absorb_tiled(d, ptr(x), None, ptr(wd["w_uk"]), ptr(pos), 4, ptr(q_lat), ptr(q_pe),
+                                ptr(ws), ws.numel(), s) == M.MLA_EINVAL
+    f32 = M.dims_of(I.CONFIGS["tiny_f32"])
+    assert lib.mla_absorb_tiled(ctypes.byref(f32), ptr(x), ptr(buf), ptr(wd["w_uk"]), ptr(pos), 4, ptr(q_lat),
+                                ptr(q_pe), ptr(ws), ws.numel(), s) == M.MLA_ENOTSUP
+    attn = torch.zeros((T, cfg.n_heads, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((T, cfg.d_model), dtype=torch.bfloat16, device="cuda")
+    assert lib.mla_output_tiled(d, ptr(attn), ptr(buf), 65, ptr(out), ptr(ws), ws.numel(), s) == M.MLA_ENOTSUP
+    assert lib.mla_output_tiled(d, ptr(attn), ptr(buf), 4, ptr(out), ptr(ws), 16, s) == M.MLA_EWORKSPACE
+    torch.cuda.synchronize()
+    # the refused calls left their outputs untouched
+    assert not q_lat.any() and not q_pe.any() and not out.any()
