@@ -343,10 +343,26 @@ def bench_decode(args, torch, M, I, D, cfg):
                        device="cuda")
     ws_d = torch.empty(max(256, M.mla_workspace_size(dims, M.MLA_OP_DECODE, B, 0, max_len)), dtype=torch.uint8,
                        device="cuda")
+    # few-token steps read [W_QC ; W_QR] in the tiled layout, made once here
+    tiled = cfg.dtype == "bf16" and B <= 64
+    wq_t = M.mla_tile_weights(wd["w_qc"], wd["w_qr"]) if tiled else None
     setup_s = time.perf_counter() - t_setup
     T = Timer(torch, args.warmup)
 
+    def absorb(i):
+        if tiled:
+            M.mla_absorb_tiled(dims, x_new_d, wq_t, wd["w_uk"], pos_new, q_lat, q_pe, workspace=ws_a)
+        else:
+            M.mla_absorb(dims, x_new_d, wd["w_qc"], wd["w_qr"], wd["w_uk"], pos_new, q_lat, q_pe, workspace=ws_a)
+
     def step(i):
+        c = caches[i % n_copies]
+        M.mla_write_cache(dims, x_new_d, wd["w_dkv"], wd["w_kr"], pos_new, slots_new, c, workspace=ws_w)
+        absorb(i)
+        M.mla_decode(dims, q_lat, q_pe, c, seq_start, seq_len, max_len, wd["w_uv"], out, workspace=ws_d)
+
+    def step_in_place(i):
+        # the same step with the weights read in place (mla_absorb)
         c = caches[i % n_copies]
         M.mla_write_cache(dims, x_new_d, wd["w_dkv"], wd["w_kr"], pos_new, slots_new, c, workspace=ws_w)
         M.mla_absorb(dims, x_new_d, wd["w_qc"], wd["w_qr"], wd["w_uk"], pos_new, q_lat, q_pe, workspace=ws_a)
@@ -376,6 +392,7 @@ def bench_decode(args, torch, M, I, D, cfg):
 
     t_att = T.run(attention_only, args.steps)
     ms_att = t_att["mean_ms"]
+    t_inplace = T.run(step_in_place, args.steps) if tiled else None
     t_step = T.run(step, args.steps)
     ms_step = t_step["mean_ms"]
     print(f"[bench] {cfg.name}: {args.steps} steps: {ms_step * 1e3:.1f} us/step (median "
@@ -422,7 +439,9 @@ def bench_decode(args, torch, M, I, D, cfg):
                    "context_total_rows": int(lengths.sum()), "heads": cfg.n_heads,
                    "kv_groups": cfg.n_groups, "rank": cfg.rank, "d_rope": cfg.d_rope, "d_model": cfg.d_model,
                    "latent_rmsnorm": bool(cfg.latent_rmsnorm), "cache_copies": n_copies,
-                   "step": "mla_write_cache + mla_absorb + mla_decode"},
+                   "step": "mla_write_cache + " + ("mla_absorb_tiled" if tiled else "mla_absorb") + " + mla_decode",
+                   "weights": ("[W_QC ; W_QR] tiled once at setup (mla_tile_weights), the rest in place"
+                               if tiled else "in place")},
         "roofline": {"bound": "hbm", "kernel": f"{kname} (split attention over the latent cache)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -444,6 +463,11 @@ def bench_decode(args, torch, M, I, D, cfg):
                                            / (ms_dec * 1e-3) / 1e9, 1)},
         "cpu_baseline": cpu,
     }
+    if t_inplace is not None:
+        line["step_weights_in_place"] = {"step": "mla_write_cache + mla_absorb + mla_decode",
+                                         "us": round(t_inplace["mean_ms"] * 1e3, 2),
+                                         "us_spread": spread(t_inplace, 1e3, "us"),
+                                         "tokens_per_s": round(B / (t_inplace["mean_ms"] * 1e-3), 1)}
     if beyond is not None:
         line["beyond_attention"] = beyond
     print(json.dumps(line), flush=True)
@@ -468,6 +492,7 @@ def bench_beyond(args, torch, M, I, D, cfg, dims, wd, caches, n_copies, x_new_d,
     q_rank = I.Q_LORA_RANK
     lw = {k: D.to_dev(v, cfg.dtype) for k, v in I.lowrank_query_weights(cfg, q_rank).items()}
     w_o = D.to_dev(I.output_weight(cfg), cfg.dtype)
+    w_o_t = M.mla_tile_weights(w_o)
     u = torch.empty((B, cfg.d_model), dtype=torch.bfloat16, device="cuda")
     ws_l = torch.empty(max(256, M.mla_lowrank_workspace_size(dims, q_rank, B)), dtype=torch.uint8, device="cuda")
     ws_o = torch.empty(max(256, M.mla_workspace_size(dims, M.MLA_OP_OUTPUT, 0, B, 0)), dtype=torch.uint8,
@@ -478,7 +503,7 @@ def bench_beyond(args, torch, M, I, D, cfg, dims, wd, caches, n_copies, x_new_d,
                              q_lat, q_pe, workspace=ws_l)
 
     def output_only(i):
-        M.mla_output(dims, out, w_o, u, workspace=ws_o)
+        M.mla_output_tiled(dims, out, w_o_t, u, workspace=ws_o)
 
     def layer_step(i):
         c = caches[i % n_copies]
@@ -500,9 +525,9 @@ def bench_beyond(args, torch, M, I, D, cfg, dims, wd, caches, n_copies, x_new_d,
         "lowrank_query": {"call": "mla_absorb_lowrank", "q_rank": q_rank, "us": round(ms_lr * 1e3, 2),
                           "weight_bytes": lr_bytes,
                           "hbm_frac": round(lr_bytes / (ms_lr * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "output_projection": {"call": "mla_output", "us": round(ms_out * 1e3, 2), "weight_bytes": wo_bytes,
+        "output_projection": {"call": "mla_output_tiled", "us": round(ms_out * 1e3, 2), "weight_bytes": wo_bytes,
                               "hbm_frac": round(wo_bytes / (ms_out * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "layer_step": {"step": "mla_write_cache + mla_absorb_lowrank + mla_decode + mla_output",
+        "layer_step": {"step": "mla_write_cache + mla_absorb_lowrank + mla_decode + mla_output_tiled",
                        "us": round(ms_layer * 1e3, 2), "us_spread": spread(t_layer, 1e3, "us"),
                        "tokens_per_s": round(B / (ms_layer * 1e-3), 1)},
     }

@@ -494,7 +494,8 @@ struct MergeStage {
   static constexpr int kBytes = kOps * 1024;
   static constexpr int kLds = kMgStages * kBytes;
   static_assert(NS == 4, "one token's partial rows per copy");
-  static_assert(kOps % 4 == 0 && kLds <= 160 * 1024 - 1024, "LDS budget (merge weights after the ring)");
+  static_assert(kWOps % 4 == 0 && kAOps % 4 == 0, "copies of each kind split evenly over the waves");
+  static_assert(kLds <= 160 * 1024 - 1024, "LDS budget (merge weights after the ring)");
   static_assert(kOpsPerWave < 64, "vmcnt range");
 };
 
@@ -541,34 +542,35 @@ __global__ __launch_bounds__(256, 1) void merge_uv_kernel(SkinnyArgs sa) {
 
   // copy o of stage st: 4 rows R = 4o'..4o'+3 of the W_UV region (o < kWOps,
   // o' = o) or of the partial region (o' = o - kWOps: token o', splits 0..3);
-  // lanes 16q..16q+15 take row 4o'+q, LDS chunks p = lane % 16 in order
+  // lanes 16q..16q+15 take row 4o'+q, LDS chunks p = lane % 16 in order.  Wave
+  // w issues the W_UV copies o = w + 4i, then the partial copies o = kWOps + w + 4i.
   auto issue = [&](int st) {
     const int kb = st * kMgKC;
     const uint32_t dst = lds0 + (st % kMgStages) * G::kBytes;
     int ln = lane;
     __asm__ volatile("" : "+v"(ln));
     const int q = ln >> 4, p = ln & 15;
+    auto k_of = [&](int key) {
+      const int kc = kb + 8 * (p ^ key);
+      return kc < sa.K ? kc : sa.K - 8;
+    };
 #pragma unroll
-    for (int i = 0; i < G::kOpsPerWave; ++i) {
+    for (int i = 0; i < G::kWOps / 4; ++i) {
       const int o = wave + 4 * i;
-      const char* sbase;
-      uint32_t voff;
-      if (o < G::kWOps) {
-        const int n_base = min(4 * o, sa.N - 1), n = min(4 * o + q, sa.N - 1);
-        int kc = kb + 8 * (p ^ ((4 * o + q) & 15));
-        kc = kc < sa.K ? kc : sa.K - 8;
-        sbase = reinterpret_cast<const char*>(w_head + static_cast<int64_t>(n_base) * sa.sBo);
-        voff = static_cast<uint32_t>((n - n_base) * sa.sBo + kc) * 2u;
-      } else {
-        const int t = o - G::kWOps;                   // token row of the copy, splits j = q
-        const int key = t & 15;
-        int kc = kb + 8 * (p ^ key);
-        kc = kc < sa.K ? kc : sa.K - 8;
-        const int m = min(t, m_last);
-        sbase = reinterpret_cast<const char*>(a_head + static_cast<int64_t>(m0 + m) * sa.sAm);
-        voff = static_cast<uint32_t>(q * sa.sAs + kc) * 2u;
-      }
-      global_to_lds16(sbase, voff, __builtin_amdgcn_readfirstlane(dst + o * 1024));
+      const int n_base = min(4 * o, sa.N - 1), n = min(4 * o + q, sa.N - 1);
+      const int kc = k_of((4 * o + q) & 15);
+      global_to_lds16(reinterpret_cast<const char*>(w_head + static_cast<int64_t>(n_base) * sa.sBo),
+                      static_cast<uint32_t>((n - n_base) * sa.sBo + kc) * 2u,
+                      __builtin_amdgcn_readfirstlane(dst + o * 1024));
+    }
+#pragma unroll
+    for (int i = 0; i < G::kAOps / 4; ++i) {
+      const int t = wave + 4 * i;  // token row of the copy, splits j = q
+      const int m = min(t, m_last);
+      const int kc = k_of(t & 15);
+      global_to_lds16(reinterpret_cast<const char*>(a_head + static_cast<int64_t>(m0 + m) * sa.sAm),
+                      static_cast<uint32_t>(q * sa.sAs + kc) * 2u,
+                      __builtin_amdgcn_readfirstlane(dst + (G::kWOps + t) * 1024));
     }
   };
 
