@@ -487,20 +487,21 @@ def bench_beyond(args, torch, M, I, D, cfg, dims, wd, caches, n_copies, x_new_d,
                  seq_len, max_len, q_lat, q_pe, out, ws_w, ws_d, T):
     """Beyond the attention at the DeepSeek-V2 shape: the low-rank query path (its
     1536-wide query factorisation) in place of [W_QC | W_QR], and the output
-    projection W_o."""
+    projection W_o, their weights tiled once here."""
     B = q_lat.shape[0]
     q_rank = I.Q_LORA_RANK
     lw = {k: D.to_dev(v, cfg.dtype) for k, v in I.lowrank_query_weights(cfg, q_rank).items()}
     w_o = D.to_dev(I.output_weight(cfg), cfg.dtype)
     w_o_t = M.mla_tile_weights(w_o)
+    wqa_t, wqb_t = M.mla_tile_weights(lw["w_qa"]), M.mla_tile_weights(lw["w_qb"])
     u = torch.empty((B, cfg.d_model), dtype=torch.bfloat16, device="cuda")
     ws_l = torch.empty(max(256, M.mla_lowrank_workspace_size(dims, q_rank, B)), dtype=torch.uint8, device="cuda")
     ws_o = torch.empty(max(256, M.mla_workspace_size(dims, M.MLA_OP_OUTPUT, 0, B, 0)), dtype=torch.uint8,
                        device="cuda")
 
     def lowrank_only(i):
-        M.mla_absorb_lowrank(dims, q_rank, x_new_d, lw["w_qa"], lw["q_gain"], lw["w_qb"], wd["w_uk"], pos_new,
-                             q_lat, q_pe, workspace=ws_l)
+        M.mla_absorb_lowrank_tiled(dims, q_rank, x_new_d, wqa_t, lw["q_gain"], wqb_t, wd["w_uk"], pos_new,
+                                   q_lat, q_pe, workspace=ws_l)
 
     def output_only(i):
         M.mla_output_tiled(dims, out, w_o_t, u, workspace=ws_o)
@@ -522,12 +523,12 @@ def bench_beyond(args, torch, M, I, D, cfg, dims, wd, caches, n_copies, x_new_d,
     print(f"[bench] low-rank query {ms_lr * 1e3:.1f} us, output projection {ms_out * 1e3:.1f} us, "
           f"layer step {ms_layer * 1e3:.1f} us", file=sys.stderr, flush=True)
     return {
-        "lowrank_query": {"call": "mla_absorb_lowrank", "q_rank": q_rank, "us": round(ms_lr * 1e3, 2),
+        "lowrank_query": {"call": "mla_absorb_lowrank_tiled", "q_rank": q_rank, "us": round(ms_lr * 1e3, 2),
                           "weight_bytes": lr_bytes,
                           "hbm_frac": round(lr_bytes / (ms_lr * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "output_projection": {"call": "mla_output_tiled", "us": round(ms_out * 1e3, 2), "weight_bytes": wo_bytes,
                               "hbm_frac": round(wo_bytes / (ms_out * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "layer_step": {"step": "mla_write_cache + mla_absorb_lowrank + mla_decode + mla_output_tiled",
+        "layer_step": {"step": "mla_write_cache + mla_absorb_lowrank_tiled + mla_decode + mla_output_tiled",
                        "us": round(ms_layer * 1e3, 2), "us_spread": spread(t_layer, 1e3, "us"),
                        "tokens_per_s": round(B / (ms_layer * 1e-3), 1)},
     }

@@ -14,8 +14,8 @@ its calls:
     mla_prefill_expanded — causal prefill in the original order (k_nope, v expanded)
     mla_absorb_lowrank / mla_query_lowrank — the low-rank query path (W_QA, RMSNorm, W_QB)
     mla_output       — the output projection W_o after W_UV
-    mla_tile_weights — a weight re-laid once into 24 KB blocks, read by mla_absorb_tiled
-                       and mla_output_tiled (few-token steps)
+    mla_tile_weights — a weight re-laid once into 24 KB blocks, read by mla_absorb_tiled,
+                       mla_absorb_lowrank_tiled and mla_output_tiled (few-token steps)
     mla_rope_yarn_table — YaRN's rescaled rotary frequencies, for mla_dims.rope_freqs
     mla_v4_*         — the DeepSeek-V4 / nanowhale variant (one KV head as key and value,
                        attention sink, inverse rotation of the output, grouped output)
@@ -32,7 +32,7 @@ from ._abi import (  # noqa: F401
     mla_decode_partials, mla_decode_split_rows, mla_decode_splits, mla_lowrank_workspace_size, mla_output,
     mla_prefill, mla_prefill_expanded, mla_query, mla_query_lowrank, mla_rope_yarn_table, mla_workspace_size,
     mla_write_cache,
-    mla_absorb_tiled, mla_output_tiled, mla_tile_weights, mla_tiled_weight_bytes,
+    mla_absorb_tiled, mla_absorb_lowrank_tiled, mla_output_tiled, mla_tile_weights, mla_tiled_weight_bytes,
     strerror,
 )
 
@@ -44,4 +44,5 @@ __all__ = [
     "MlaV4Dims", "v4_dims_of", "mla_v4_write_cache", "mla_v4_query", "mla_v4_decode", "mla_v4_prefill",
     "mla_v4_output", "mla_v4_workspace_size",
     "mla_tile_weights", "mla_tiled_weight_bytes", "mla_absorb_tiled", "mla_output_tiled",
+    "mla_absorb_lowrank_tiled",
 ]

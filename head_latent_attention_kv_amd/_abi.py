@@ -73,6 +73,8 @@ SIGNATURES = {
     "mla_tile_weights": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i64, _vp, _sz, _vp]),
     "mla_absorb_tiled": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "mla_output_tiled": (ctypes.c_int, [_PD, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "mla_absorb_lowrank_tiled": (ctypes.c_int, [_PD, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
+                                                _sz, _vp]),
     "mla_v4_check_dims": (ctypes.c_int, [_P4]),
     "mla_v4_workspace_size": (_sz, [_P4, ctypes.c_int, _i32, _i64, _i32]),
     "mla_v4_write_cache": (ctypes.c_int, [_P4, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _sz, _vp]),
@@ -344,6 +346,20 @@ def mla_absorb_lowrank(dims, q_rank, x, w_qa, q_gain, w_qb, w_uk, positions, q_l
         ctypes.byref(dims), int(q_rank), _ptr(x, "x", et), _ptr(w_qa, "w_qa", et), gain, _ptr(w_qb, "w_qb", et),
         _ptr(w_uk, "w_uk", et), _ptr(positions, "positions", torch.int32), T, _ptr(q_lat, "q_lat", et),
         _ptr(q_pe, "q_pe", et), _ptr(ws, "workspace"), nbytes, _stream(stream)))
+    return q_lat, q_pe
+
+
+def mla_absorb_lowrank_tiled(dims, q_rank, x, w_qa_tiled, q_gain, w_qb_tiled, w_uk, positions, q_lat, q_pe,
+                             workspace=None, stream=None):
+    torch = _torch()
+    et = _elem_dtype(dims)
+    T = x.shape[0]
+    ws, nbytes = _lowrank_ws(dims, q_rank, T, workspace, x.device)
+    gain = None if q_gain is None else _ptr(q_gain, "q_gain", et)
+    _check("mla_absorb_lowrank_tiled", load().mla_absorb_lowrank_tiled(
+        ctypes.byref(dims), int(q_rank), _ptr(x, "x", et), _ptr(w_qa_tiled, "w_qa_tiled"), gain,
+        _ptr(w_qb_tiled, "w_qb_tiled"), _ptr(w_uk, "w_uk", et), _ptr(positions, "positions", torch.int32), T,
+        _ptr(q_lat, "q_lat", et), _ptr(q_pe, "q_pe", et), _ptr(ws, "workspace"), nbytes, _stream(stream)))
     return q_lat, q_pe
 
 

@@ -797,16 +797,19 @@ namespace {
 // Shared front of the low-rank query calls: q = RMSNorm(x·W_QAᵀ)·gain · W_QBᵀ into
 // the fp32 rows of the workspace ([H, d_nope + d_rope] per token), q_pe rotated.
 // Returns the fp32 rows (row stride q_width) or nullptr after an argument error in *st.
+// tiled: W_QA and W_QB in the tiled layout (bf16, at most 64 tokens)
 float* lowrank_front(const mla_dims* dims, int32_t q_rank, const void* x, const void* w_qa,
                      const void* q_gain, const void* w_qb, const int32_t* positions, int64_t n_tokens,
-                     void* q_pe, void* workspace, size_t workspace_bytes, hipStream_t s, int* st) {
+                     void* q_pe, void* workspace, size_t workspace_bytes, hipStream_t s, int* st,
+                     bool tiled = false) {
   *st = check_dims(dims);
   if (*st != MLA_OK) return nullptr;
   if (q_rank <= 0 || n_tokens < 0) {
     *st = MLA_EINVAL;
     return nullptr;
   }
-  if (q_rank % 8 != 0 || !mla::norm_rows_supported(q_rank) || n_tokens > INT32_MAX) {
+  if (q_rank % 8 != 0 || !mla::norm_rows_supported(q_rank) || n_tokens > INT32_MAX ||
+      (tiled && n_tokens > 0 && (dims->dtype != MLA_BF16 || n_tokens > 64))) {
     *st = MLA_ENOTSUP;
     return nullptr;
   }
@@ -826,11 +829,13 @@ float* lowrank_front(const mla_dims* dims, int32_t q_rank, const void* x, const 
   void* cqn = base + w.cq;
   float* q = reinterpret_cast<float*>(base + w.cq + w.cqn);
   const int64_t ldq = lowrank_ld(q_rank);
-  const Proj p1 = proj_one(dims, x, dims->d_model, dims->d_model, w_qa, q_rank, cq, ldq, n_tokens, s);
+  const Proj p1 = tiled ? proj_tiled(dims, x, dims->d_model, dims->d_model, w_qa, q_rank, cq, ldq, n_tokens, s)
+                        : proj_one(dims, x, dims->d_model, dims->d_model, w_qa, q_rank, cq, ldq, n_tokens, s);
   mla::norm_rows(dims->dtype, cq, ldq, p1.splits, p1.sps, q_rank, q_gain, dims->rms_eps, cqn, q_rank,
                  n_tokens, s);
   const int64_t ld = q_width(dims);
-  const Proj p2 = proj_one(dims, cqn, q_rank, q_rank, w_qb, q_cols(dims), q, ld, n_tokens, s);
+  const Proj p2 = tiled ? proj_tiled(dims, cqn, q_rank, q_rank, w_qb, q_cols(dims), q, ld, n_tokens, s)
+                        : proj_one(dims, cqn, q_rank, q_rank, w_qb, q_cols(dims), q, ld, n_tokens, s);
   mla::sum_split_slices(q, p2.splits, p2.sps, static_cast<int>(n_tokens), q_cols(dims), ld, s);
   const int hw = dims->d_nope + dims->d_rope;
   mla::finalize_query_rope(dims->dtype, q + dims->d_nope, ld, hw, q_pe, positions, n_tokens, dims->n_heads,
@@ -838,19 +843,16 @@ float* lowrank_front(const mla_dims* dims, int32_t q_rank, const void* x, const 
   return q;
 }
 
-}  // namespace
-
-int mla_absorb_lowrank(const mla_dims* dims, int32_t q_rank, const void* x, const void* w_qa,
-                       const void* q_gain, const void* w_qb, const void* w_uk, const int32_t* positions,
-                       int64_t n_tokens, void* q_lat, void* q_pe, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+int absorb_lowrank(const mla_dims* dims, int32_t q_rank, const void* x, const void* w_qa, const void* q_gain,
+                   const void* w_qb, const void* w_uk, const int32_t* positions, int64_t n_tokens, void* q_lat,
+                   void* q_pe, void* workspace, size_t workspace_bytes, void* stream, bool tiled) {
   const int st0 = check_dims(dims);
   if (st0 != MLA_OK) return st0;
   if (n_tokens > 0 && (!ptr_ok(w_uk) || !ptr_ok(q_lat))) return MLA_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   int st = MLA_OK;
   float* q = lowrank_front(dims, q_rank, x, w_qa, q_gain, w_qb, positions, n_tokens, q_pe, workspace,
-                           workspace_bytes, s, &st);
+                           workspace_bytes, s, &st, tiled);
   if (q == nullptr) return st;
   const int H = dims->n_heads;
   GemmArgs a{};
@@ -869,6 +871,24 @@ int mla_absorb_lowrank(const mla_dims* dims, int32_t q_rank, const void* x, cons
   a.Z = H;
   mla::gemm(a, dims->dtype, /*a_f32=*/true, /*b_kn=*/true, dims->dtype == MLA_BF16, s);
   return launch_status();
+}
+
+}  // namespace
+
+int mla_absorb_lowrank(const mla_dims* dims, int32_t q_rank, const void* x, const void* w_qa,
+                       const void* q_gain, const void* w_qb, const void* w_uk, const int32_t* positions,
+                       int64_t n_tokens, void* q_lat, void* q_pe, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return absorb_lowrank(dims, q_rank, x, w_qa, q_gain, w_qb, w_uk, positions, n_tokens, q_lat, q_pe, workspace,
+                        workspace_bytes, stream, false);
+}
+
+int mla_absorb_lowrank_tiled(const mla_dims* dims, int32_t q_rank, const void* x, const void* w_qa_tiled,
+                             const void* q_gain, const void* w_qb_tiled, const void* w_uk,
+                             const int32_t* positions, int64_t n_tokens, void* q_lat, void* q_pe,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return absorb_lowrank(dims, q_rank, x, w_qa_tiled, q_gain, w_qb_tiled, w_uk, positions, n_tokens, q_lat, q_pe,
+                        workspace, workspace_bytes, stream, true);
 }
 
 int mla_query_lowrank(const mla_dims* dims, int32_t q_rank, const void* x, const void* w_qa,

@@ -375,6 +375,15 @@ int mla_absorb_tiled(const mla_dims* dims, const void* x, const void* w_q_tiled,
                      size_t workspace_bytes, void* stream);
 int mla_output_tiled(const mla_dims* dims, const void* attn, const void* w_o_tiled, int64_t n_tokens,
                      void* out, void* workspace, size_t workspace_bytes, void* stream);
+/* mla_absorb_lowrank with both low-rank weights tiled:
+ *   w_qa_tiled = mla_tile_weights(w_qa, q_rank, NULL, 0, d_model, ...)
+ *   w_qb_tiled = mla_tile_weights(w_qb, H*(d_nope+d_rope), NULL, 0, q_rank, ...)
+ * workspace as mla_absorb_lowrank (mla_lowrank_workspace_size); bf16, 1 <= n_tokens <= 64
+ * (MLA_ENOTSUP otherwise; n_tokens == 0 is a no-op). */
+int mla_absorb_lowrank_tiled(const mla_dims* dims, int32_t q_rank, const void* x, const void* w_qa_tiled,
+                             const void* q_gain, const void* w_qb_tiled, const void* w_uk,
+                             const int32_t* positions, int64_t n_tokens, void* q_lat, void* q_pe,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------
  * DeepSeek-V4 / nanowhale variant (nanowhale MLA page).  One KV head of head_dim

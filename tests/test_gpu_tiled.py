@@ -3,9 +3,10 @@
 - mla_tile_weights against a re-layout written here in numpy from the layout's
   definition (include/mla.h): bit for bit, with row counts and k that leave
   partial blocks.
-- mla_absorb_tiled and mla_output_tiled against the oracle (q_lat, q_pe and the
-  output projection), and bit for bit against mla_absorb / mla_output where those
-  stream the same weight through the same kernel (H = 128, d_model 5120 or 5000).
+- mla_absorb_tiled, mla_absorb_lowrank_tiled and mla_output_tiled against the
+  oracle (q_lat, q_pe and the output projection), and bit for bit against the
+  in-place calls where those stream the same weight through the same kernel
+  (H = 128, d_model 5120 or 5000).
 - the argument errors of the new entry points."""
 import numpy as np
 import pytest
@@ -124,6 +125,43 @@ def test_output_tiled_matches_oracle(torch, name, T):
     assert err <= Hh.TOL[cfg.dtype], err
     if cfg.n_heads == 128:
         assert same
+
+
+@pytest.mark.parametrize("name,T", [("deepseek_v2_decode", 64), ("deepseek_v2_decode", 5)])
+def test_absorb_lowrank_tiled_matches_oracle(torch, name, T):
+    """mla_absorb_lowrank_tiled (W_QA and W_QB tiled) against the oracle's low-rank
+    query, and bit for bit against mla_absorb_lowrank (the same kernels and plans)."""
+    import head_latent_attention_kv_amd as M
+    from oracle import mla_oracle as O
+    cfg = I.CONFIGS[name]
+    q_rank = I.Q_LORA_RANK
+    print(f"[case] absorb_lowrank_tiled {name} T={T} q_rank={q_rank}", flush=True)
+    layer = Hh.make_layer(cfg)
+    lw = I.lowrank_query_weights(cfg, q_rank)
+    lwd = {k: Hh.to_dev(v, cfg.dtype) for k, v in lw.items()}
+    wqa_t = M.mla_tile_weights(lwd["w_qa"])
+    wqb_t = M.mla_tile_weights(lwd["w_qb"])
+    x = I.x_rows(cfg, 5, 0, T)
+    pos = np.random.default_rng(13).integers(0, 50000, T)
+    et = Hh.elem_dtype(cfg)
+    xd = Hh.to_dev(x, cfg.dtype)
+    posd = torch.from_numpy(pos.astype(np.int32)).cuda()
+    q_lat = torch.full((T, cfg.n_heads, cfg.rank), 7.0, dtype=et, device="cuda")
+    q_pe = torch.full((T, cfg.n_heads, cfg.d_rope), 7.0, dtype=et, device="cuda")
+    ql_ref, qp_ref = torch.empty_like(q_lat), torch.empty_like(q_pe)
+    M.mla_absorb_lowrank_tiled(layer.dims, q_rank, xd, wqa_t, lwd["q_gain"], wqb_t, layer.w_dev["w_uk"], posd,
+                               q_lat, q_pe)
+    M.mla_absorb_lowrank(layer.dims, q_rank, xd, lwd["w_qa"], lwd["q_gain"], lwd["w_qb"], layer.w_dev["w_uk"],
+                         posd, ql_ref, qp_ref)
+    torch.cuda.synchronize()
+    qn, qr = O.lowrank_query(x, lw["w_qa"], lw["q_gain"], lw["w_qb"], pos, n_heads=cfg.n_heads,
+                             d_nope=cfg.d_nope, d_rope=cfg.d_rope, theta=cfg.rope_theta, eps=cfg.rms_eps)
+    err_lat = Hh.rel_err_rows(Hh.to_host(q_lat), O.absorbed_query(qn, layer.w_host["w_uk"]))
+    err_pe = Hh.rel_err_rows(Hh.to_host(q_pe), qr)
+    same = torch.equal(q_lat, ql_ref) and torch.equal(q_pe, qp_ref)
+    print(f"absorb_lowrank_tiled {name} T={T}: q_lat {err_lat:.3e} q_pe {err_pe:.3e}; identical: {same}")
+    assert err_lat <= Hh.TOL[cfg.dtype] and err_pe <= Hh.TOL[cfg.dtype], (err_lat, err_pe)
+    assert same
 
 
 def test_tiled_argument_errors(torch):
