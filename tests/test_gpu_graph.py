@@ -121,14 +121,16 @@ def test_tiny_f32_run_in_a_graph(torch):
     _replay_and_check(torch, g, [cache, q_lat, q_pe, out_pre, out_dec], expected, eager_noise)
 
 
-@pytest.mark.parametrize("name,lengths", [("deepseek_v2_decode", [1, 300, 2048, 4100]),
-                                          ("qwen3_30b_ragged_decode", [33, 1537]),
-                                          ("qwen3_30b_ragged_decode", [1, 40, 3000, 9000, 20000])])
-def test_decode_step_in_a_graph(torch, name, lengths):
-    """One bf16 decode step (write the batch's new rows, absorb, decode) as a graph."""
+@pytest.mark.parametrize("name,lengths,tiled", [("deepseek_v2_decode", [1, 300, 2048, 4100], False),
+                                                ("deepseek_v2_decode", [1, 300, 2048, 4100], True),
+                                                ("qwen3_30b_ragged_decode", [33, 1537], False),
+                                                ("qwen3_30b_ragged_decode", [1, 40, 3000, 9000, 20000], True)])
+def test_decode_step_in_a_graph(torch, name, lengths, tiled):
+    """One bf16 decode step (write the batch's new rows, absorb, decode) as a graph;
+    tiled: the absorption reads [W_QC ; W_QR] tiled (mla_absorb_tiled)."""
     import head_latent_attention_kv_amd as M
     cfg = I.CONFIGS[name]
-    print(f"[case] graph decode step {name} lengths={lengths}", flush=True)
+    print(f"[case] graph decode step {name} lengths={lengths} tiled={tiled}", flush=True)
     layer = Hh.make_layer(cfg)
     lengths = np.asarray(lengths, np.int64)
     run = Hh.build_decode(layer, lengths)
@@ -154,9 +156,14 @@ def test_decode_step_in_a_graph(torch, name, lengths):
     ws_d = torch.empty(max(256, M.mla_workspace_size(dims, M.MLA_OP_DECODE, B, 0, max_len)), dtype=torch.uint8,
                        device="cuda")
 
+    wq_t = M.mla_tile_weights(wd["w_qc"], wd["w_qr"]) if tiled else None
+
     def step():
         M.mla_write_cache(dims, xd, wd["w_dkv"], wd["w_kr"], pos, slots, cache, workspace=ws_w)
-        M.mla_absorb(dims, xd, wd["w_qc"], wd["w_qr"], wd["w_uk"], pos, q_lat, q_pe, workspace=ws_a)
+        if tiled:
+            M.mla_absorb_tiled(dims, xd, wq_t, wd["w_uk"], pos, q_lat, q_pe, workspace=ws_a)
+        else:
+            M.mla_absorb(dims, xd, wd["w_qc"], wd["w_qr"], wd["w_uk"], pos, q_lat, q_pe, workspace=ws_a)
         M.mla_decode(dims, q_lat, q_pe, cache, ss, sl, max_len, wd["w_uv"], out, workspace=ws_d)
 
     step()
