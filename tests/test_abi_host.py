@@ -195,6 +195,47 @@ def test_lowrank_query_and_output_entry_points():
     assert o(ctypes.byref(d), p, p, 4, p, p, 16, null) == abi.MLA_EWORKSPACE
 
 
+def test_tiled_weight_entry_points():
+    """Sizes of the tiled layout (96-row x 128-k blocks of 24 KB) and the argument
+    errors of the tiled calls, all decided before any HIP call."""
+    abi, lib = _lib()
+    null = None
+    p = 0x10000
+    blk = 96 * 128 * 2
+    assert lib.mla_tiled_weight_bytes(24576, 5120) == 256 * 40 * blk == 251658240  # [W_QC ; W_QR] at H = 128
+    assert lib.mla_tiled_weight_bytes(5120, 16384) == 54 * 128 * blk              # W_o
+    assert lib.mla_tiled_weight_bytes(237, 264) == 3 * 3 * blk                     # partial blocks both ways
+    assert lib.mla_tiled_weight_bytes(0, 8) == 0 and lib.mla_tiled_weight_bytes(8, 0) == 0
+    t = lib.mla_tile_weights
+    need = lib.mla_tiled_weight_bytes(200, 264)
+    assert t(p, 200, null, 0, 12, p, 1 << 40, null) == abi.MLA_EINVAL       # k not a multiple of 8
+    assert t(p, -1, null, 0, 264, p, 1 << 40, null) == abi.MLA_EINVAL       # negative rows
+    assert t(p, 0, null, 0, 264, p, 1 << 40, null) == abi.MLA_EINVAL        # no rows
+    assert t(p, 100, null, 100, 264, p, 1 << 40, null) == abi.MLA_EINVAL    # w1 missing for its rows
+    assert t(0x10001, 200, null, 0, 264, p, 1 << 40, null) == abi.MLA_EINVAL  # misaligned w0
+    assert t(p, 200, null, 0, 264, p, need - 16, null) == abi.MLA_EINVAL    # output too small
+    assert t(p, 200, null, 0, 264, null, need, null) == abi.MLA_EINVAL      # no output
+    d = abi.dims_of(I.CONFIGS["deepseek_v2_decode"])
+    f32 = abi.dims_of(I.CONFIGS["tiny_f32"])
+    a = lib.mla_absorb_tiled
+    assert a(ctypes.byref(d), null, null, null, null, 0, null, null, null, 0, null) == abi.MLA_OK  # no-op
+    assert a(ctypes.byref(d), p, p, p, p, 65, p, p, p, 1 << 40, null) == abi.MLA_ENOTSUP        # > 64 tokens
+    assert a(ctypes.byref(f32), p, p, p, p, 4, p, p, p, 1 << 40, null) == abi.MLA_ENOTSUP       # fp32 layer
+    assert a(ctypes.byref(d), p, null, p, p, 4, p, p, p, 1 << 40, null) == abi.MLA_EINVAL
+    assert a(ctypes.byref(d), p, p, p, p, 4, p, p, p, 16, null) == abi.MLA_EWORKSPACE
+    assert a(ctypes.byref(d), p, p, p, p, -1, p, p, p, 1 << 40, null) == abi.MLA_EINVAL
+    o = lib.mla_output_tiled
+    assert o(ctypes.byref(d), p, p, 65, p, p, 1 << 40, null) == abi.MLA_ENOTSUP
+    assert o(ctypes.byref(f32), p, p, 4, p, p, 1 << 40, null) == abi.MLA_ENOTSUP
+    assert o(ctypes.byref(d), p, null, 4, p, p, 1 << 40, null) == abi.MLA_EINVAL
+    assert o(ctypes.byref(d), p, p, 4, p, p, 16, null) == abi.MLA_EWORKSPACE
+    lr = lib.mla_absorb_lowrank_tiled
+    assert lr(ctypes.byref(d), 1536, p, p, null, p, p, p, 65, p, p, p, 1 << 40, null) == abi.MLA_ENOTSUP
+    assert lr(ctypes.byref(f32), 96, p, p, null, p, p, p, 4, p, p, p, 1 << 40, null) == abi.MLA_ENOTSUP
+    assert lr(ctypes.byref(d), 1536, p, p, null, p, p, p, 4, p, p, p, 16, null) == abi.MLA_EWORKSPACE
+    assert lr(ctypes.byref(d), 1536, null, null, null, null, null, null, 0, null, null, null, 0, null) == abi.MLA_OK
+
+
 def test_v4_entry_points_validate_arguments():
     abi, lib = _lib()
     null = None
