@@ -449,9 +449,8 @@ void absorb_finish(const mla_dims* dims, float* q, const Proj& p, const void* w_
                    const int32_t* positions, int64_t n_tokens, void* q_lat, void* q_pe, hipStream_t s) {
   const int H = dims->n_heads;
   const int64_t ld = q_width(dims);
-  mla::sum_split_slices(q, p.splits, p.sps, static_cast<int>(n_tokens), q_cols(dims), ld, s);
-  mla::finalize_query_rope(dims->dtype, q + static_cast<int64_t>(H) * dims->d_nope, ld, dims->d_rope, q_pe,
-                           positions, n_tokens, H, dims->d_rope, dims->rope_theta, dims->rope_freqs, s);
+  mla::finalize_query(dims->dtype, q, ld, p.splits, p.sps, q_cols(dims), H * dims->d_nope, dims->d_rope, q_pe,
+                      positions, n_tokens, H, dims->d_rope, dims->rope_theta, dims->rope_freqs, s);
   // q_lat[t,h,:] = Σ_d q_nope[t,h,d] W_UK[h,d,:]   (batched over heads)
   GemmArgs a{};
   a.A = q;
@@ -713,9 +712,8 @@ int mla_query(const mla_dims* dims, const void* x, const void* w_qc, const void*
   const int64_t ld = q_width(dims);
   float* q = static_cast<float*>(workspace);
   const Proj p = proj_two(dims, x, w_qc, H * dims->d_nope, w_qr, H * dims->d_rope, q, ld, n_tokens, s);
-  mla::sum_split_slices(q, p.splits, p.sps, static_cast<int>(n_tokens), q_cols(dims), ld, s);
-  mla::finalize_query_rope(dims->dtype, q + static_cast<int64_t>(H) * dims->d_nope, ld, dims->d_rope, q_pe,
-                           positions, n_tokens, H, dims->d_rope, dims->rope_theta, dims->rope_freqs, s);
+  mla::finalize_query(dims->dtype, q, ld, p.splits, p.sps, q_cols(dims), H * dims->d_nope, dims->d_rope, q_pe,
+                      positions, n_tokens, H, dims->d_rope, dims->rope_theta, dims->rope_freqs, s);
   mla::cast_heads(dims->dtype, q, ld, dims->d_nope, H, dims->d_nope, q_nope, n_tokens, s);
   return launch_status();
 }
@@ -836,10 +834,9 @@ float* lowrank_front(const mla_dims* dims, int32_t q_rank, const void* x, const 
   const int64_t ld = q_width(dims);
   const Proj p2 = tiled ? proj_tiled(dims, cqn, q_rank, q_rank, w_qb, q_cols(dims), q, ld, n_tokens, s)
                         : proj_one(dims, cqn, q_rank, q_rank, w_qb, q_cols(dims), q, ld, n_tokens, s);
-  mla::sum_split_slices(q, p2.splits, p2.sps, static_cast<int>(n_tokens), q_cols(dims), ld, s);
   const int hw = dims->d_nope + dims->d_rope;
-  mla::finalize_query_rope(dims->dtype, q + dims->d_nope, ld, hw, q_pe, positions, n_tokens, dims->n_heads,
-                           dims->d_rope, dims->rope_theta, dims->rope_freqs, s);
+  mla::finalize_query(dims->dtype, q, ld, p2.splits, p2.sps, q_cols(dims), dims->d_nope, hw, q_pe, positions,
+                      n_tokens, dims->n_heads, dims->d_rope, dims->rope_theta, dims->rope_freqs, s);
   return q;
 }
 

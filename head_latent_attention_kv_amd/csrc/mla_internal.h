@@ -91,6 +91,14 @@ void finalize_cache_rows(int dtype, const float* proj, int64_t ld, int splits, i
 void finalize_query_rope(int dtype, const float* proj, int64_t ld, int hstride, void* q_pe,
                          const int32_t* positions, int64_t n_tokens, int n_heads, int d_rope,
                          double theta, const double* freqs, hipStream_t s);
+// The query projection's rows q [splits][T, ld] (n_cols columns; head h's rotary
+// part at rope_off + h*hstride): the splits summed into slice 0 (every column
+// but the rotary ones) and q_pe = RoPE of the summed rotary part, in one launch;
+// with one slice, finalize_query_rope alone.  Same results as sum_split_slices
+// followed by finalize_query_rope.
+void finalize_query(int dtype, float* q, int64_t ld, int splits, int64_t sps, int n_cols, int rope_off,
+                    int hstride, void* q_pe, const int32_t* positions, int64_t n_tokens, int n_heads,
+                    int d_rope, double theta, const double* freqs, hipStream_t s);
 
 // dst[t, h, 0:n] = src[t*ld + h*hstride : +n] (fp32 -> dtype), dst dense [n_rows, n_heads, n].
 void cast_heads(int dtype, const float* src, int64_t ld, int hstride, int n_heads, int n, void* dst,

@@ -105,6 +105,65 @@ __global__ __launch_bounds__(256) void query_rope_kernel(const float* __restrict
   }
 }
 
+// The query projection's K slices summed and its rotary part rotated in one
+// launch: workgroups y < y_sum sum every other column into slice 0 (in place,
+// in sum_slices_kernel's order), the rest sum and rotate the rotary pairs of head
+// h (columns rope_off + h*hstride + j and + j + d_rope/2) into q_pe, as
+// query_rope_kernel does from summed columns.
+template <typename T>
+__global__ __launch_bounds__(256) void query_sum_rope_kernel(float* __restrict__ q, int64_t ld, int splits,
+                                                             int64_t sps, int n_cols, int rope_off, int hstride,
+                                                             T* __restrict__ q_pe,
+                                                             const int32_t* __restrict__ positions, int n_heads,
+                                                             int d_rope, double rope_base,
+                                                             const double* __restrict__ freqs, int y_sum) {
+  const int64_t t = blockIdx.x;
+  float* row = q + t * ld;
+  const int half = d_rope / 2;
+  if (static_cast<int>(blockIdx.y) < y_sum) {
+    const int per = (n_cols + y_sum - 1) / y_sum;
+    const int lo = blockIdx.y * per, hi = min(n_cols, lo + per);
+    for (int c = lo + threadIdx.x; c < hi; c += blockDim.x) {
+      const int rc = c - rope_off;
+      if (rc >= 0 && rc % hstride < d_rope) continue;  // a rotary column: the other workgroups
+      float part[16];
+#pragma unroll
+      for (int p = 0; p < 16; ++p) part[p] = p < splits ? row[p * sps + c] : 0.f;
+      float v = 0.f;
+#pragma unroll
+      for (int p = 0; p < 16; ++p) v += part[p];
+      row[c] = v;
+    }
+    return;
+  }
+  const int32_t pos = positions[t];
+  T* dst = q_pe + t * static_cast<int64_t>(n_heads) * d_rope;
+  const int items = n_heads * half;
+  const int y_rope = gridDim.y - y_sum;
+  const int per = (items + y_rope - 1) / y_rope;
+  const int lo = (blockIdx.y - y_sum) * per, hi = min(items, lo + per);
+  for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) {
+    const int h = i / half, j = i % half;
+    const int ca = rope_off + h * hstride + j, cb = ca + half;
+    float pa[16], pb[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      pa[p] = p < splits ? row[p * sps + ca] : 0.f;
+      pb[p] = p < splits ? row[p * sps + cb] : 0.f;
+    }
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      a += pa[p];
+      b += pb[p];
+    }
+    float c, sn;
+    rope_cos_sin(pos, j, rope_base, freqs, &c, &sn);
+    Elem<T>::store(dst, h * d_rope + j, a * c - b * sn);
+    Elem<T>::store(dst, h * d_rope + j + half, b * c + a * sn);
+  }
+}
+
 // dst[t, h*n + c] = src[t*ld + h*hstride + c] for c < n, cast to T (per-head
 // columns of an fp32 projection, e.g. q_nope out of [q_nope ; q_pe] head rows).
 template <typename T>
@@ -216,6 +275,27 @@ void finalize_cache_rows(int dtype, const float* proj, int64_t ld, int splits, i
     if (splits <= 1) launch(cache_rows_kernel<bf16_t, 1>, out);
     else launch(cache_rows_kernel<bf16_t, 16>, out);
   }
+}
+
+void finalize_query(int dtype, float* q, int64_t ld, int splits, int64_t sps, int n_cols, int rope_off,
+                    int hstride, void* q_pe, const int32_t* positions, int64_t n_tokens, int n_heads,
+                    int d_rope, double theta, const double* freqs, hipStream_t s) {
+  if (n_tokens <= 0) return;
+  if (splits <= 1) {
+    finalize_query_rope(dtype, q + rope_off, ld, hstride, q_pe, positions, n_tokens, n_heads, d_rope, theta,
+                        freqs, s);
+    return;
+  }
+  const double base = std::pow(theta, -2.0 / d_rope);
+  const int y_sum = std::max(1, std::min(16, n_cols / 256));
+  const int y_rope = std::max(1, std::min(16, n_heads * (d_rope / 2) / 256));
+  dim3 grid(static_cast<unsigned>(n_tokens), static_cast<unsigned>(y_sum + y_rope));
+  if (dtype == kF32)
+    hipLaunchKernelGGL(query_sum_rope_kernel<float>, grid, dim3(256), 0, s, q, ld, splits, sps, n_cols, rope_off,
+                       hstride, static_cast<float*>(q_pe), positions, n_heads, d_rope, base, freqs, y_sum);
+  else
+    hipLaunchKernelGGL(query_sum_rope_kernel<bf16_t>, grid, dim3(256), 0, s, q, ld, splits, sps, n_cols, rope_off,
+                       hstride, static_cast<bf16_t*>(q_pe), positions, n_heads, d_rope, base, freqs, y_sum);
 }
 
 void finalize_query_rope(int dtype, const float* proj, int64_t ld, int hstride, void* q_pe,
