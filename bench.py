@@ -405,6 +405,10 @@ def bench_decode(args, torch, M, I, D, cfg):
     kc = counters(ksrc, f"{kname}_{cfg.name}_counters.txt")
     traffic_b = int(float(kc["hbm_bytes_per_launch"])) if kc and "hbm_bytes_per_launch" in kc else None
     mfma_busy = float(kc["mfma_busy_frac"]) if kc and "mfma_busy_frac" in kc else None
+    # what the busy cycles are divided by (the summaries of short dispatches use the CUs' busy
+    # cycles, since the GRBM window of a dispatch of a few microseconds is mostly profiler overhead)
+    busy_basis = (kc.get("mfma_busy_basis", "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs)")
+                  if mfma_busy is not None else None)
     print(f"[bench] decode call: {ms_dec * 1e3:.1f} us; attention kernel {kname} ({n_split} splits): "
           f"{ms_att * 1e3:.1f} us, {achieved:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
@@ -451,6 +455,7 @@ def bench_decode(args, torch, M, I, D, cfg):
                      "alg_flops_per_launch": alg_flops,
                      "mfma_frac_algorithmic": round(alg_flops / (ms_att * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
                      "mfma_busy_frac_counter": mfma_busy,
+                     "mfma_busy_basis": busy_basis,
                      "us_per_launch": round(ms_att * 1e3, 2),
                      "us_spread": spread(t_att, 1e3, "us"),
                      "n_split": n_split},
