@@ -12,7 +12,7 @@
 // (one token with its H = 16 heads, or 16/H tokens of H heads; see below).
 // The workgroup streams
 // the union of its tokens' key ranges in 32-row tiles through a 4-buffer LDS
-// ring (global_load_lds_dwordx4; 16-byte chunks XOR-swizzled by row / 2 within
+// ring (global_load_lds_dwordx4; 16-byte chunks XOR-swizzled by 2·((row / 2) mod 4) within
 // groups of eight so fragment reads spread over the banks).  Per tile and wave:
 //   - score Sᵀ[32 keys x 16 columns]: two 16x16 blocks of
 //     v_mfma_f32_16x16x32_bf16 over the whole row (K = r + G·d_rope), key rows
@@ -62,8 +62,17 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
+// Swizzle key of tile row r: the 16-byte chunks of a row are XORed within
+// groups of eight by 2·((r / 2) mod 4).  On gfx950 a ds_read_b128 is served
+// 16 lanes at a time, lanes 0-7 with 24-31 (and 8-15 with 16-23, likewise
+// above 32), and a ds_read_b64_tr_b16 32 lanes at a time; with rows whose
+// length is 128 bytes past a multiple of 256, this key keeps both the score's
+// fragment reads (rows l16, chunk 4ks + lg) and the transposed PV reads (rows
+// 4lg + l16/4, a 32-byte pair of chunks each) on distinct banks.  The key
+// (r / 2) mod 8 left every transposed read two-way conflicted.
+__device__ __forceinline__ int row_key(int r) { return ((r >> 1) & 3) << 1; }
 // LDS chunk slot of 16-byte chunk c of tile row r (an involution for fixed r).
-__device__ __forceinline__ int swz(int c, int r) { return (c & ~7) | ((c ^ (r >> 1)) & 7); }
+__device__ __forceinline__ int swz(int c, int r) { return (c & ~7) | ((c ^ row_key(r)) & 7); }
 
 template <int R, int RW>
 struct PShape {
@@ -152,7 +161,7 @@ __global__ __launch_bounds__((PShape<R, RW>::kThreads), (PShape<R, RW>::kBlocksP
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)smem));
 
   // ---- tile copy: copy j fills LDS chunks [64j, 64j + 64); chunk L holds global
-  // chunk L ^ ((row / 2) & 7) of row L / kRowChunks; rows past k_hi read row k_hi
+  // chunk L ^ row_key(row) of row L / kRowChunks; rows past k_hi read row k_hi
   // per-lane source offsets of this wave's copies: with a row of chunks that
   // is no power of two (a real divide), computed once for a full tile and
   // again only for a ragged last tile; otherwise per tile (shifts, no
@@ -165,7 +174,7 @@ __global__ __launch_bounds__((PShape<R, RW>::kThreads), (PShape<R, RW>::kBlocksP
       const int j = min(wave + S::kWaves * i, S::kDmaOps - 1);  // duplicates of the last copy are benign
       const int L = j * 64 + ln;
       const int r = L / S::kRowChunks;
-      const int g = r < valid ? (L ^ ((r >> 1) & 7)) : (valid - 1) * S::kRowChunks + (L & 7);
+      const int g = r < valid ? (L ^ row_key(r)) : (valid - 1) * S::kRowChunks + (L & 7);
       off[i] = static_cast<uint32_t>(g * 16);
     }
   };
@@ -195,7 +204,7 @@ __global__ __launch_bounds__((PShape<R, RW>::kThreads), (PShape<R, RW>::kBlocksP
         const int j = min(wave + S::kWaves * i, S::kDmaOps - 1);  // duplicates of the last copy are benign
         const int L = j * 64 + ln;
         const int r = L / S::kRowChunks;
-        const int g = r < valid ? (L ^ ((r >> 1) & 7)) : (valid - 1) * S::kRowChunks + (L & 7);
+        const int g = r < valid ? (L ^ row_key(r)) : (valid - 1) * S::kRowChunks + (L & 7);
         global_to_lds16(tbase, static_cast<uint32_t>(g * 16), __builtin_amdgcn_readfirstlane(dst + j * 1024));
       }
     }
@@ -229,8 +238,8 @@ __global__ __launch_bounds__((PShape<R, RW>::kThreads), (PShape<R, RW>::kBlocksP
   wait_vmcnt<0>();  // Q landed before any tile copy is in flight
 
   const int a_off0 = l16 * S::kRowBytes, a_off1 = (16 + l16) * S::kRowBytes;
-  const int x_even = (lg ^ (l16 >> 1)) & 7;
-  const int x_odd = ((4 + lg) ^ (l16 >> 1)) & 7;
+  const int x_even = (lg ^ row_key(l16)) & 7;
+  const int x_odd = ((4 + lg) ^ row_key(l16)) & 7;
   const int r_lo = lg * 4 + (l16 >> 2), r_hi = 16 + r_lo;
   const int c_sub = (l16 & 1) * 8, c_half = (l16 & 3) >> 1;
 
