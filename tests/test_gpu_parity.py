@@ -90,13 +90,25 @@ DECODE_CASES = [
     ("qwen3_30b_ragged_decode", [1, 40, 3000, 9000, 20000]),
     # the generic kernel's plan: one-tile splits, splits past a short sequence empty
     ("tiny_f32", [1, 31, 32, 33, 65, 300]),
+    # the 576-wide row with a head count the 128-head kernel does not take: the
+    # generic MFMA kernel, two workgroups of 64 heads per split
+    ("deepseek_v2_h120", [1, 300, 2048]),
 ]
+# reduced variants of the workloads, by the name the cases above use
+DECODE_VARIANTS = {"deepseek_v2_h120": ("deepseek_v2_decode", dict(n_heads=120, d_model=1024))}
+
+
+def _decode_cfg(name):
+    if name in DECODE_VARIANTS:
+        base, changes = DECODE_VARIANTS[name]
+        return I.small_variant(I.CONFIGS[base], **changes)
+    return I.CONFIGS[name]
 
 
 @pytest.mark.parametrize("name,lengths", DECODE_CASES)
 def test_decode_reduced(torch, name, lengths):
     from oracle import mla_oracle as O
-    cfg = I.CONFIGS[name]
+    cfg = _decode_cfg(name)
     _print_case("decode_reduced", cfg=name, lengths=lengths)
     layer = Hh.make_layer(cfg)
     run = Hh.build_decode(layer, np.array(lengths))
